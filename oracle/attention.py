@@ -1,0 +1,46 @@
+"""Hybrid decode attention over the selected compressed entries plus the raw
+window (fp64).
+
+[V4-vLLM] 2.1: keys and values are one shared, RoPE-rotated vector; the
+attention output is rotated back by inverse RoPE so only relative position
+remains.  c128a layers attend to all of their entries; c4a layers to the
+entries the indexer selects ([V4-vLLM] 2.2).  [V4-vLLM] 2.3: every layer also
+attends to an uncompressed sliding window of the most recent tokens (usually
+128).
+
+Readings adopted: the decode query is the last token of the context, at
+position L-1 (the current token is already in the cache); selected entries and
+window tokens enter one softmax, with no de-duplication of tokens that are seen
+both raw and compressed; the logit scale is passed in (1/sqrt(d) in the
+workloads); window = 0 means no window rows.
+"""
+
+import numpy as np
+
+from .rope import rope
+
+
+def attend(q, rows, L: int, scale: float, theta):
+    """q: [H, d] unrotated queries; rows: [R, d] decoded, already-rotated shared
+    K=V rows.  Returns (out [H, d], lse [H], p [H, R]) where
+    out_h = RoPE^-1(sum_r p_hr rows_r, L-1), p_h = softmax(scale * RoPE(q_h, L-1) . rows)."""
+    q = np.asarray(q, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.float64)
+    H, d = q.shape
+    if rows.shape[0] == 0:
+        return np.zeros((H, d)), np.full((H,), -np.inf), np.zeros((H, 0))
+    qt = rope(q, L - 1, theta)
+    logits = scale * (qt @ rows.T)  # [H, R]
+    mx = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - mx)
+    tot = e.sum(axis=1, keepdims=True)
+    p = e / tot
+    o = p @ rows
+    out = rope(o, L - 1, theta, inverse=True)
+    lse = mx[:, 0] + np.log(tot[:, 0])
+    return out, lse, p
+
+
+def window_positions(L: int, window: int) -> np.ndarray:
+    """Token positions of the raw window: [max(0, L-W), L)."""
+    return np.arange(max(0, L - window), L, dtype=np.int64)

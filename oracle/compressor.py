@@ -1,0 +1,81 @@
+"""The compressor: m consecutive token vectors -> one shared K=V entry (fp64).
+
+[V4-vLLM] 2.1: c4a layers fold every few raw tokens, c128a layers every 128,
+into one entry by a learned weighted sum with a positional bias (not a plain
+average); a 1M-token context gives 1,000,000/128 ~= 7,813 c128a entries and
+1,000,000/4 = 250,000 c4a entries.  [V4-vLLM] 3.1.2: compression is not
+one-shot; the part of the context not yet folded is carried as a rolling
+residual whose state is kept like sliding-window KV.  [V4-vLLM] 3.2.1: RoPE is
+applied to the compressed vector before it is inserted into the cache.
+
+Readings adopted:
+* groups are the non-overlapping runs [jm, jm+m) (m = 4 for c4a, 128 for
+  c128a); entry count N = ceil(L/m);
+* the weights are a softmax over the group's slots of (token logit z_t +
+  per-slot bias beta_i);
+* a partial last group (r < m tokens) is an entry whose softmax runs over its r
+  available slots; this is exactly the state a running (max, sum exp, sum w*x)
+  residual holds after r tokens, and equals the full entry once r = m;
+* the entry is rotated at the position of its first token, jm.
+"""
+
+import numpy as np
+
+from .rope import rope
+
+
+def n_entries(L, m):
+    """N = ceil(L/m)."""
+    L = np.asarray(L, dtype=np.int64)
+    return -(-L // m)
+
+
+def group_weights(z, beta, m):
+    """Softmax weights of every group.  z: [T] logits for tokens 0..T-1 of a run
+    that starts at a group boundary; returns w [N, m] with zeros in the slots
+    past the end of a partial last group."""
+    z = np.asarray(z, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    T = z.shape[0]
+    N = int(n_entries(T, m))
+    a = np.full((N, m), -np.inf)
+    a.reshape(-1)[:T] = z
+    a = a + beta[None, :m]
+    valid = np.arange(N * m).reshape(N, m) < T
+    a = np.where(valid, a, -np.inf)
+    amax = a.max(axis=1, keepdims=True)
+    e = np.exp(a - amax)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def compress(x, z, beta, m, theta, pos0=0, chunk_groups=1 << 14):
+    """Entries of a run of tokens.
+
+    x: [T, d] token vectors of positions pos0 .. pos0+T-1 (pos0 a multiple of m),
+    z: [T] logits, beta: [m] slot biases.  Returns e [ceil(T/m), d] fp64, entry j
+    rotated at position pos0 + j*m.  Processed in chunks of groups so that long
+    contexts fit in memory; chunking does not change any value."""
+    x = np.asarray(x, dtype=np.float64)
+    T, d = x.shape
+    assert pos0 % m == 0
+    N = int(n_entries(T, m))
+    out = np.empty((N, d), dtype=np.float64)
+    for g0 in range(0, N, chunk_groups):
+        g1 = min(N, g0 + chunk_groups)
+        t0, t1 = g0 * m, min(T, g1 * m)
+        w = group_weights(z[t0:t1], beta, m)  # [g1-g0, m]
+        xs = np.zeros(((g1 - g0) * m, d))
+        xs[: t1 - t0] = x[t0:t1]
+        c = np.einsum("gi,gid->gd", w, xs.reshape(g1 - g0, m, d))
+        pos = pos0 + m * np.arange(g0, g1, dtype=np.float64)
+        out[g0:g1] = rope(c, pos, theta)
+    return out
+
+
+def window_rows(x_block, first_pos, theta):
+    """Sliding-window rows ([V4-vLLM] 2.3: raw, uncompressed recent tokens, kept in
+    every layer): token t is stored as RoPE(x_t, t).  This is the compressor with
+    m = 1 (one slot, weight 1)."""
+    x_block = np.asarray(x_block, dtype=np.float64)
+    pos = first_pos + np.arange(x_block.shape[0], dtype=np.float64)
+    return rope(x_block, pos, theta)

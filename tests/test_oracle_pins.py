@@ -1,0 +1,414 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test names what it pins: closed forms, brute force written a different
+way, library routines, invariants the pages state, and the pages' worked
+numbers (tests/golden).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, codecs, compressor, indexer, paging, pipeline
+from oracle.rope import rope
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- codecs
+
+
+def test_e4m3_table_anchor_values():
+    # field definition: bias 7, 3 mantissa bits, S.1111.111 = NaN
+    t = codecs.E4M3_TABLE
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x38] == 1.0  # exponent field 7, mantissa 0
+    assert t[0x08] == 2.0 ** -6  # smallest normal
+    assert t[0x01] == 2.0 ** -9  # smallest subnormal
+    assert t[0x07] == 7 * 2.0 ** -9  # largest subnormal
+    assert t[0x00] == 0.0 and np.signbit(t[0x80])
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert np.isfinite(t).sum() == 254
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0)  # monotone in the code
+
+
+def test_e2m1_table():
+    assert list(codecs.E2M1_TABLE[:8]) == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    assert list(codecs.E2M1_TABLE[8:]) == [-0.0, -0.5, -1, -1.5, -2, -3, -4, -6]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_codec_round_trip_every_code(fmt):
+    enc = codecs.e4m3_encode if fmt == "e4m3" else codecs.e2m1_encode
+    tab = codecs.E4M3_TABLE if fmt == "e4m3" else codecs.E2M1_TABLE
+    codes = [c for c in range(len(tab)) if np.isfinite(tab[c])]
+    back = enc(tab[codes].astype(np.float32))
+    assert list(back) == codes
+
+
+def _brute_nearest_even(values, a, max_value):
+    # nearest finite non-negative value by exhaustive search; ties -> even code
+    a = min(abs(a), max_value)
+    best = None
+    for code, v in enumerate(values):
+        dist = abs(v - a)
+        if best is None or dist < best[0] or (dist == best[0] and code % 2 == 0):
+            best = (dist, code)
+    return best[1]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_codec_matches_brute_force_on_midpoints_and_edges(fmt):
+    if fmt == "e4m3":
+        enc, pos, mx, sb = codecs.e4m3_encode, list(codecs.E4M3_TABLE[:0x7F]), 448.0, 7
+    else:
+        enc, pos, mx, sb = codecs.e2m1_encode, list(codecs.E2M1_TABLE[:8]), 6.0, 3
+    probes = []
+    for lo, hi in zip(pos[:-1], pos[1:]):
+        mid = (lo + hi) / 2
+        probes += [lo, mid, np.nextafter(np.float32(mid), np.float32(0)), np.nextafter(np.float32(mid), np.float32(1e9)), hi]
+    probes += [mx * 1.01, mx * 100, 1e30, 0.0]
+    for a in probes:
+        a32 = np.float32(a)
+        want = _brute_nearest_even(pos, float(a32), mx)
+        assert enc(a32) == want, (fmt, a)
+        assert enc(-a32) == want | (1 << sb), (fmt, -a)
+
+
+def test_e4m3_matches_torch_in_range():
+    g = np.random.default_rng(1)
+    x = np.concatenate([
+        g.uniform(-448, 448, 200000), g.normal(0, 1, 200000), g.normal(0, 1e-2, 100000),
+        np.ldexp(g.uniform(-1, 1, 50000), -8),
+    ]).astype(np.float32)
+    ours = codecs.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_matches_torch():
+    g = np.random.default_rng(2)
+    x = g.normal(0, 10, 500000).astype(np.float32)
+    # exact halfway cases in both tie directions
+    n = 20000
+    u = ((g.integers(0, 2, n) << 31) | (g.integers(100, 150, n) << 23) | (g.integers(0, 128, n) << 16) | 0x8000).astype(np.uint32)
+    x = np.concatenate([x, u.view(np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(codecs.bf16_encode(x), ref)
+    assert np.array_equal(codecs.bf16_decode(ref), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).float().double().numpy())
+
+
+# ----------------------------------------------------------------- paging
+
+
+def test_fp8_page_quantization_error_bound_and_scale():
+    g = np.random.default_rng(3)
+    rows = g.normal(0, 0.5, (37, 64)).astype(np.float32)
+    codes, s = paging.quantize_page(rows, "fp8", 64)
+    amax = np.abs(rows).max()
+    assert s == np.float32(amax) / np.float32(448)
+    dec = codecs.e4m3_decode(codes[:37]) * np.float64(s)
+    # E4M3 keeps 3 mantissa bits: relative error <= 2^-4 above the smallest normal,
+    # absolute error <= half the subnormal spacing below it
+    err = np.abs(dec - rows)
+    bound = np.maximum(np.abs(rows) * 2.0 ** -4, 0.5 * 2.0 ** -9 * s) * (1 + 1e-6)
+    assert np.all(err <= bound)
+    assert np.abs(dec).max() == pytest.approx(amax, rel=1e-6)  # the page max maps to 448
+    z, sz = paging.quantize_page(np.zeros((3, 64), np.float32), "fp8", 64)
+    assert sz == 1.0 and not z.any()
+
+
+def test_fp4_key_quantization_block_scales():
+    g = np.random.default_rng(4)
+    rows = g.normal(0, 1, (5, 128)).astype(np.float32)
+    rows[2, 32:64] = 0.0  # an all-zero block: scale code 0, codes 0
+    pool = paging.Pool("fp4", 1, 64, 128)
+    paging.write_run(pool, [0], 0, rows)
+    dec = paging.decode_rows(pool, [0], np.arange(5))
+    blocks = rows.reshape(5, 4, 32)
+    sc = codecs.e4m3_decode(pool.scales[0, :5])
+    for r in range(5):
+        for b in range(4):
+            amax = np.abs(blocks[r, b]).max()
+            if amax == 0:
+                assert sc[r, b] == 0 and not dec[r, 32 * b: 32 * b + 32].any()
+                continue
+            # scale is the E4M3 rounding of amax/6
+            assert sc[r, b] == codecs.E4M3_TABLE[codecs.e4m3_encode(np.float32(amax) / np.float32(6))]
+            # every decoded value is a multiple of the block scale by an E2M1 magnitude
+            ratio = dec[r, 32 * b: 32 * b + 32] / sc[r, b]
+            assert set(np.abs(ratio).tolist()) <= set(codecs.E2M1_TABLE[:8].tolist())
+    # nibble packing: element 2c in the low nibble of byte c
+    lo = pool.codes[0, 0, 0] & 0xF
+    assert codecs.E2M1_TABLE[lo] * sc[0, 0] == dec[0, 0]
+
+
+def test_paged_equals_contiguous_under_permutation_and_aliasing():
+    # the same logical rows through three different tables read back bit-identically
+    g = np.random.default_rng(5)
+    rows = g.normal(0, 1, (300, 32)).astype(np.float32)
+    for dtype in ("fp8", "bf16", "fp4"):
+        outs = []
+        for trial in range(3):
+            pool = paging.Pool(dtype, 10, 64, 32)
+            table = g.permutation(10)[:5] if trial else np.arange(5)
+            paging.write_run(pool, table, 0, rows)
+            outs.append(paging.decode_rows(pool, table, np.arange(300)))
+            outs.append(paging.gather_bytes(pool, table, 300)[0].astype(np.float64))
+        assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[0], outs[4])
+        assert np.array_equal(outs[1], outs[3]) and np.array_equal(outs[1], outs[5])
+    # aliasing: two sequences whose first two blocks name the same pages
+    pool = paging.Pool("fp8", 8, 64, 32)
+    t0 = np.array([5, 6, 0, 1, 2])
+    t1 = np.array([5, 6, 3, 4, 7])
+    paging.write_run(pool, t0, 0, rows)
+    paging.write_run(pool, t1, 0, np.concatenate([rows[:128], rows[128:] * 2]))
+    assert np.array_equal(paging.decode_rows(pool, t0, np.arange(128)), paging.decode_rows(pool, t1, np.arange(128)))
+
+
+# ----------------------------------------------------------------- worked numbers
+
+
+def test_pages_worked_numbers():
+    gold = json.load(open(os.path.join(GOLDEN, "pages_worked_numbers.json")))
+    for e in gold["entry_counts"]:
+        assert int(compressor.n_entries(e["L"], e["m"])) == e["N"], e["cite"]
+    for e in gold["entries_per_block"]:
+        assert paging.entries_per_page(e["m"]) == e["epp"], e["cite"]
+    for e in gold["page_bytes_bf16_5120"]:
+        assert paging.page_bytes(e["m"], 5120, 2) == e["bytes"], e["cite"]
+    for e in gold["layer_bytes_bf16_5120"]:
+        assert e["N"] * 5120 * 2 == e["bytes"], e["cite"]
+    # the ceil(L/m) rule at the 2^20 contexts of the long-context workload
+    assert compressor.n_entries(1 << 20, 4) == 262144 and compressor.n_entries(1 << 20, 128) == 8192
+
+
+# ----------------------------------------------------------------- rope
+
+
+def _rotation_matrix(d, pos, theta):
+    # block-diagonal 2x2 rotations, built entry by entry
+    R = np.zeros((d, d))
+    for i in range(d // 2):
+        ang = pos * theta ** (-2.0 * i / d)
+        c, s = math.cos(ang), math.sin(ang)
+        R[2 * i, 2 * i], R[2 * i, 2 * i + 1] = c, -s
+        R[2 * i + 1, 2 * i], R[2 * i + 1, 2 * i + 1] = s, c
+    return R
+
+
+def test_rope_is_block_rotation_and_inverse():
+    g = np.random.default_rng(6)
+    v = g.normal(size=(16,))
+    for pos in (0, 1, 7, 1000, 1 << 20):
+        R = _rotation_matrix(16, pos, 1e6)
+        assert np.allclose(rope(v, pos, 1e6), R @ v, atol=1e-12)
+        assert np.allclose(rope(rope(v, pos, 1e6), pos, 1e6, inverse=True), v, atol=1e-12)
+    assert np.allclose(rope(rope(v, 3, 1e4), 5, 1e4), rope(v, 8, 1e4), atol=1e-12)
+
+
+# ----------------------------------------------------------------- compressor
+
+
+def test_compressor_mean_pooling_and_identity():
+    g = np.random.default_rng(7)
+    x = g.normal(size=(37, 8))
+    e = compressor.compress(x, np.zeros(37), np.zeros(4), 4, None)
+    assert e.shape == (10, 8)
+    for j in range(10):
+        assert np.allclose(e[j], np.mean(x[4 * j: 4 * j + 4], axis=0), atol=1e-14)
+    # m = 1 is the identity before rotation, and RoPE(x_t, t) with it
+    assert np.allclose(compressor.compress(x, g.normal(size=37), g.normal(size=1), 1, None), x, atol=1e-15)
+    assert np.allclose(compressor.compress(x, g.normal(size=37), g.normal(size=1), 1, 1e4),
+                       compressor.window_rows(x, 0, 1e4), atol=1e-13)
+
+
+def test_compressor_dominant_logit_and_weights_sum_to_one():
+    g = np.random.default_rng(8)
+    x = g.normal(size=(256, 8))
+    z = g.normal(size=256)
+    z[130] = 1e4  # dominates group 1 (tokens 128..255) of m = 128
+    e = compressor.compress(x, z, g.normal(0, 0.1, 128), 128, None)
+    assert np.allclose(e[1], x[130], atol=1e-12)
+    w = compressor.group_weights(g.normal(size=203), g.normal(0, 0.1, 4), 4)
+    assert np.allclose(w.sum(axis=1), 1.0, atol=1e-12)
+    assert (w[-1, 3:] == 0).all()  # partial last group: 203 = 50*4 + 3
+
+
+def test_compressor_partial_group_is_the_running_residual():
+    # the partial group equals a running fold over its tokens (max, sum exp, sum w*x),
+    # i.e. the softmax renormalized over the available slots
+    g = np.random.default_rng(9)
+    x = g.normal(size=(7, 6))
+    z = g.normal(size=7)
+    beta = g.normal(0, 0.1, 4)
+    e = compressor.compress(x, z, beta, 4, None)
+    mx, se, acc = -np.inf, 0.0, np.zeros(6)
+    for i in range(3):
+        a = z[4 + i] + beta[i]
+        nm = max(mx, a)
+        se = se * math.exp(mx - nm) + math.exp(a - nm)
+        acc = acc * math.exp(mx - nm) + math.exp(a - nm) * x[4 + i]
+        mx = nm
+    assert np.allclose(e[1], acc / se, atol=1e-14)
+
+
+def test_incremental_equals_one_shot():
+    # prefill L-1 tokens, then re-fold only the open group with the new token:
+    # the same entries as compressing all L tokens at once
+    g = np.random.default_rng(10)
+    m, L, d = 4, 1031, 8
+    x, z, beta = g.normal(size=(L, d)), g.normal(size=L), g.normal(0, 0.1, m)
+    full = compressor.compress(x, z, beta, m, 1e6)
+    pre = compressor.compress(x[: L - 1], z[: L - 1], beta, m, 1e6)
+    gopen = (L - 1) // m
+    upd = compressor.compress(x[gopen * m: L], z[gopen * m: L], beta, m, 1e6, pos0=gopen * m)
+    inc = np.concatenate([pre[:gopen], upd], axis=0)
+    assert np.array_equal(full, inc)
+
+
+# ----------------------------------------------------------------- indexer
+
+
+def test_indexer_scores_against_loop_and_relu_identity():
+    g = np.random.default_rng(11)
+    q, w, k = g.normal(size=(16, 32)), g.normal(size=16), g.normal(size=(50, 32))
+    s = indexer.scores(q, w, k)
+    for j in range(50):
+        ref = math.fsum(w[h] * max(0.0, math.fsum(q[h, c] * k[j, c] for c in range(32))) for h in range(16))
+        assert s[j] == pytest.approx(ref, abs=1e-11)
+    # relu(x) - relu(-x) = x: the ReLU is present and the key sign enters linearly
+    diff = indexer.scores(q, w, k) - indexer.scores(q, w, -k)
+    assert np.allclose(diff, (k @ q.T) @ w, atol=1e-11)
+    # basis keys pick one coordinate of every head
+    s_basis = indexer.scores(q, w, np.eye(32)[:5])
+    assert np.allclose(s_basis, (np.maximum(q[:, :5], 0) * w[:, None]).sum(axis=0), atol=1e-13)
+
+
+def test_topk_against_stable_argsort_with_ties():
+    g = np.random.default_rng(12)
+    for trial in range(50):
+        N = int(g.integers(1, 60))
+        s = g.integers(0, 6, N).astype(np.float64)  # many ties
+        k = int(g.integers(1, 70))
+        got = indexer.topk(s, k)
+        order = np.argsort(-s, kind="stable")  # stable: equal scores keep index order
+        want = np.sort(order[: min(k, N)])
+        assert np.array_equal(got, want)
+    assert np.array_equal(indexer.topk(np.ones(5), 9), np.arange(5))
+
+
+# ----------------------------------------------------------------- attention
+
+
+def test_attention_reduces_to_sdpa_without_rope():
+    # m = 1, no window, no top-k, rotation switched off: standard single-KV-head attention
+    g = np.random.default_rng(13)
+    H, d, L = 4, 16, 40
+    x, q = g.normal(size=(L, d)), g.normal(size=(H, d))
+    e = compressor.compress(x, g.normal(size=L), g.normal(size=1), 1, None)
+    out, lse, p = attention.attend(q, e, L, 1 / math.sqrt(d), None)
+    kv = torch.from_numpy(x)[None, None]
+    qt = torch.from_numpy(q).reshape(1, H, 1, d)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kv.expand(1, H, L, d), kv.expand(1, H, L, d))
+    assert np.allclose(out, ref[0, :, 0].numpy(), atol=1e-12)
+    assert np.allclose(p.sum(axis=1), 1.0, atol=1e-12)
+    logits = (q @ x.T) / math.sqrt(d)
+    assert np.allclose(lse, np.log(np.exp(logits).sum(axis=1)), atol=1e-12)
+
+
+def test_attention_with_rope_brute_force_rotation_matrices():
+    # out_h = sum_t p_t R(t-(L-1)) x_t with logits q_h^T R(t-(L-1)) x_t
+    g = np.random.default_rng(14)
+    H, d, L, theta = 3, 8, 24, 100.0
+    x, q = g.normal(size=(L, d)), g.normal(size=(H, d))
+    rows = compressor.window_rows(x, 0, theta)
+    out, _, _ = attention.attend(q, rows, L, 0.3, theta)
+    for h in range(H):
+        logit = np.array([q[h] @ _rotation_matrix(d, t - (L - 1), theta) @ x[t] for t in range(L)]) * 0.3
+        p = np.exp(logit - logit.max())
+        p /= p.sum()
+        ref = sum(p[t] * (_rotation_matrix(d, t - (L - 1), theta) @ x[t]) for t in range(L))
+        assert np.allclose(out[h], ref, atol=1e-12)
+
+
+def test_attention_translation_invariance():
+    # shifting every stored position and the query position by the same amount
+    # leaves the output unchanged: only relative position survives
+    g = np.random.default_rng(15)
+    H, d, n = 4, 32, 50
+    x, q = g.normal(size=(n, d)), g.normal(size=(H, d))
+    pos = np.sort(g.choice(5000, n, replace=False))
+    L = int(pos[-1]) + 1
+    ref, _, _ = attention.attend(q, rope(x, pos, 1e6), L, 0.2, 1e6)
+    for shift in (4, 128, 12345 * 4, (1 << 20) - L):
+        got, _, _ = attention.attend(q, rope(x, pos + shift, 1e6), L + shift, 0.2, 1e6)
+        assert np.allclose(got, ref, atol=1e-9)
+    # without the inverse rotation on the output the result would move with the shift
+    qt = rope(q, L - 1, 1e6)
+    assert not np.allclose(qt, rope(q, L - 1 + 128, 1e6), atol=1e-3)
+
+
+def test_attention_empty_rows():
+    out, lse, _ = attention.attend(np.ones((2, 8)), np.zeros((0, 8)), 5, 1.0, 1e6)
+    assert not out.any() and np.all(np.isneginf(lse))
+
+
+# ----------------------------------------------------------------- pipeline
+
+
+def test_window_blocks_and_pipeline_paging_invariance():
+    assert pipeline.window_blocks(300, 128) == [0, 1]
+    assert pipeline.window_blocks(256, 128) == [0]
+    assert pipeline.window_blocks(257, 128) == [0, 1]
+    assert pipeline.window_blocks(100, 0) == []
+    g = np.random.default_rng(16)
+    spec = pipeline.LayerSpec(m=4, d=32, H=4, window=16, topk=20, kv_dtype="fp8", idx_dtype="fp4", d_idx=32)
+    L = 700
+    x, z, beta = g.normal(size=(L, 32)), g.normal(size=L), g.normal(0, 0.1, 4)
+    keys = g.normal(size=(175, 32)).astype(np.float32)
+    q, qi, wi = g.normal(size=(4, 32)), g.normal(size=(16, 32)), g.normal(size=16)
+    results = []
+    for trial in range(3):
+        perm = g.permutation(6) if trial else np.arange(6)
+        wperm = g.permutation(3) if trial else np.arange(3)
+        table, wtable = perm[:3], np.full(3, -1)
+        for i, blk in enumerate(pipeline.window_blocks(L, spec.window)):
+            wtable[blk] = wperm[i]
+        kv, idx, win = paging.Pool("fp8", 6, 64, 32), paging.Pool("fp4", 6, 64, 32), paging.Pool("fp8", 3, 256, 32)
+        pipeline.fill_entries(spec, kv, table, x, z, beta)
+        pipeline.fill_window(spec, win, wtable, x, L)
+        pipeline.fill_index_keys(idx, table, keys)
+        sel, _ = pipeline.select(spec, L, idx, table, qi, wi)
+        results.append(pipeline.attend(spec, L, q, kv, table, win, wtable, sel)[0])
+    assert np.array_equal(results[0], results[1]) and np.array_equal(results[0], results[2])
+
+
+def test_entry_rotated_at_first_token_position():
+    # reading: entry j is rotated at position j*m
+    g = np.random.default_rng(17)
+    x = g.normal(size=(16, 8))
+    e = compressor.compress(x, np.zeros(16), np.zeros(4), 4, 1e4)
+    for j in range(4):
+        assert np.allclose(e[j], _rotation_matrix(8, 4 * j, 1e4) @ np.mean(x[4 * j: 4 * j + 4], axis=0), atol=1e-13)
+
+
+def test_page_and_slot_addressing():
+    # entry e of a sequence lives in physical page table[e // epp], slot e % epp
+    g = np.random.default_rng(18)
+    rows = g.normal(size=(130, 16)).astype(np.float32)
+    table = np.array([4, 1, 3])
+    pool = paging.Pool("bf16", 5, 64, 16)
+    paging.write_run(pool, table, 0, rows)
+    for e in (0, 63, 64, 100, 129):
+        assert np.array_equal(pool.codes[table[e // 64], e % 64], codecs.bf16_encode(rows[e]))
+    # a run that starts at a later page (the open page of a decode update)
+    pool2 = paging.Pool("fp8", 5, 2, 16)
+    paging.write_run(pool2, [0, 2, 4], 2, rows[:3])
+    assert np.array_equal(pool2.codes[2, :2], paging.quantize_page(rows[:2], "fp8", 2)[0])
+    assert np.array_equal(pool2.codes[4, :1], paging.quantize_page(rows[2:3], "fp8", 2)[0][:1])
