@@ -1,0 +1,201 @@
+"""Python binding of libhca: decode attention over hybrid compressed KV caches
+on AMD MI355X (gfx950).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of ``libhca.so``; torch supplies device memory and streams.  The
+functions carry the names of the C entry points (``include/hca.h``), take torch
+tensors, and raise ``HcaError`` on a non-OK status.  Importing works without a
+GPU; calling a function needs the built library and raises if it is missing.
+
+Build the library with ``python -m decode_attention_compressed_amd.build``.
+"""
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhca.so")
+
+BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2
+DTYPES = {"bf16": BF16, "fp8": FP8_E4M3, "fp4": FP4_E2M1}
+STATUS = {0: "HCA_OK", 1: "HCA_ERR_INVALID", 2: "HCA_ERR_UNSUPPORTED", 3: "HCA_ERR_WORKSPACE", 4: "HCA_ERR_HIP"}
+
+#: every symbol the C headers declare (include/hca.h and include/hca_testing.h)
+EXPORTS = (
+    "hca_status_string", "hca_version", "kv_compress", "kv_quantize_page", "indexer_topk_workspace",
+    "indexer_topk", "paged_hybrid_decode_workspace", "paged_hybrid_decode", "kv_gather",
+    "hca_host_e4m3_encode", "hca_host_e2m1_encode", "hca_host_bf16_encode", "hca_probe_decode", "hca_probe_mfma",
+)
+
+
+class HcaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+class CPagedCache(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("num_pages", ctypes.c_int32),
+                ("epp", ctypes.c_int32), ("dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32, _I64, _F32, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libhca.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m decode_attention_compressed_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.hca_status_string.restype = ctypes.c_char_p
+        L.hca_status_string.argtypes = [ctypes.c_int]
+        L.hca_version.restype = ctypes.c_char_p
+        L.kv_compress.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _I64, _P]
+        L.kv_quantize_page.argtypes = [_P, _I64, _P, _P, _I32, _I32, _P, _I32, CPagedCache, _P]
+        L.indexer_topk_workspace.argtypes = [_I32, _I32, _I32, _I32]
+        L.indexer_topk_workspace.restype = _SZ
+        L.indexer_topk.argtypes = [_P, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]
+        L.paged_hybrid_decode_workspace.argtypes = [_I32, _I32, _I32, _I32, _I32, _I32, _I32]
+        L.paged_hybrid_decode_workspace.restype = _SZ
+        L.paged_hybrid_decode.argtypes = [_P, _I32, CPagedCache, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32,
+                                          _I32, _I32, _P, _P, _I32, _F32, _F32, _P, _P, _P, _SZ, _P]
+        L.kv_gather.argtypes = [CPagedCache, _P, _I32, _P, _I32, _I32, _P, _P, _P]
+        L.hca_host_e4m3_encode.argtypes = [_P, _P, _I64]
+        L.hca_host_e2m1_encode.argtypes = [_P, _P, _I64]
+        L.hca_host_bf16_encode.argtypes = [_P, _P, _I64]
+        L.hca_probe_decode.argtypes = [_P, _P, _I32, _I32, _P]
+        L.hca_probe_mfma.argtypes = [_P, _P, _P, _I32, _P]
+        for name in EXPORTS:
+            if name not in ("hca_status_string", "hca_version", "indexer_topk_workspace",
+                            "paged_hybrid_decode_workspace"):
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise HcaError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+@dataclass
+class PagedCache:
+    """One pool of physical pages (a torch tensor of codes, and scales)."""
+
+    codes: torch.Tensor
+    scales: Optional[torch.Tensor]
+    epp: int
+    dim: int
+    dtype: str
+
+    @property
+    def num_pages(self) -> int:
+        return self.codes.shape[0]
+
+    @staticmethod
+    def empty(num_pages: int, epp: int, dim: int, dtype: str, device="cuda") -> "PagedCache":
+        if dtype == "fp8":
+            codes = torch.zeros((num_pages, epp, dim), dtype=torch.uint8, device=device)
+            scales = torch.ones((num_pages,), dtype=torch.float32, device=device)
+        elif dtype == "fp4":
+            codes = torch.zeros((num_pages, epp, dim // 2), dtype=torch.uint8, device=device)
+            scales = torch.zeros((num_pages, epp, dim // 32), dtype=torch.uint8, device=device)
+        else:
+            codes = torch.zeros((num_pages, epp, dim), dtype=torch.int16, device=device)
+            scales = None
+        return PagedCache(codes, scales, epp, dim, dtype)
+
+    def c(self) -> CPagedCache:
+        return CPagedCache(self.codes.data_ptr(), 0 if self.scales is None else self.scales.data_ptr(),
+                           self.num_pages, self.epp, self.dim, DTYPES[self.dtype])
+
+
+def _null_cache() -> CPagedCache:
+    return CPagedCache(0, 0, 0, 0, 0, 0)
+
+
+def version() -> str:
+    return lib().hca_version().decode()
+
+
+def kv_compress(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, out, max_ntok: int, stream=None):
+    """x: bf16 [B, T, d] (or int16 bit patterns); gate_logit f32 [B, T]; pos_bias f32 [m];
+    pos0, ntok int32 [B]; out f32 [B, ceil(T/m), d]."""
+    B, T, d = x.shape
+    _check(lib().kv_compress(_ptr(x), x.stride(0), _ptr(gate_logit), gate_logit.stride(0), _ptr(pos_bias),
+                             _ptr(pos0), _ptr(ntok), B, max_ntok, d, m, rope_theta, _ptr(out), out.stride(0),
+                             _stream(stream)), "kv_compress")
+
+
+def kv_quantize_page(src, e0, ne, max_ne: int, block_table, dst: PagedCache, stream=None):
+    """src f32 [B, rows, dim]; e0, ne int32 [B]; block_table int32 [B, nb]."""
+    B = src.shape[0]
+    _check(lib().kv_quantize_page(_ptr(src), src.stride(0), _ptr(e0), _ptr(ne), B, max_ne, _ptr(block_table),
+                                  block_table.stride(0), dst.c(), _stream(stream)), "kv_quantize_page")
+
+
+def indexer_topk_workspace(B: int, max_seq_len: int, m: int, k: int) -> int:
+    return int(lib().indexer_topk_workspace(B, max_seq_len, m, k))
+
+
+def indexer_topk(q_idx, head_w, idx_keys: PagedCache, block_table, seq_lens, max_seq_len: int, m: int, k: int,
+                 out_idx, out_n, ws, stream=None):
+    """q_idx bf16 [B, HI, dI]; head_w f32 [B, HI]; out_idx int32 [B, k]; out_n int32 [B];
+    ws: uint8 workspace, zero-filled before its first use (left zeroed by every call)."""
+    B, HI, _ = q_idx.shape
+    _check(lib().indexer_topk(_ptr(q_idx), _ptr(head_w), HI, idx_keys.c(), _ptr(block_table),
+                              block_table.stride(0), _ptr(seq_lens), B, max_seq_len, m, k, _ptr(out_idx),
+                              _ptr(out_n), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "indexer_topk")
+
+
+def paged_hybrid_decode_workspace(B: int, H: int, d: int, max_seq_len: int, m: int, window: int, k: int) -> int:
+    """k = 0 when the call will attend to all entries (sel_idx None)."""
+    return int(lib().paged_hybrid_decode_workspace(B, H, d, max_seq_len, m, window, k))
+
+
+def paged_hybrid_decode(q, kv: PagedCache, block_table, win: Optional[PagedCache], win_block_table, seq_lens,
+                        max_seq_len: int, m: int, window: int, sel_idx, sel_n, softmax_scale: float,
+                        rope_theta: float, out, lse, ws, stream=None):
+    """q bf16 [B, H, d]; sel_idx int32 [B, k] or None (all entries); out f32 [B, H, d]; lse f32 [B, H] or None."""
+    B, H, d = q.shape
+    k = 0 if sel_idx is None else sel_idx.shape[1]
+    wc = win.c() if (win is not None and window > 0) else _null_cache()
+    wbt = win_block_table if window > 0 else None
+    _check(lib().paged_hybrid_decode(_ptr(q), H, kv.c(), _ptr(block_table), block_table.stride(0), wc, _ptr(wbt),
+                                     0 if wbt is None else wbt.stride(0), _ptr(seq_lens), B, max_seq_len, m, window,
+                                     _ptr(sel_idx), _ptr(sel_n), k, softmax_scale, rope_theta, _ptr(out), _ptr(lse),
+                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "paged_hybrid_decode")
+
+
+def kv_gather(src: PagedCache, block_table, n_rows, max_rows: int, dst_codes, dst_scales, stream=None):
+    B = n_rows.shape[0]
+    _check(lib().kv_gather(src.c(), _ptr(block_table), block_table.stride(0), _ptr(n_rows), B, max_rows,
+                           _ptr(dst_codes), _ptr(dst_scales), _stream(stream)), "kv_gather")
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled, 256-byte aligned workspace of at least nbytes."""
+    return torch.zeros((max(1, nbytes),), dtype=torch.uint8, device=device)
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

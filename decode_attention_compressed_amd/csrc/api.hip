@@ -1,0 +1,246 @@
+// C ABI of libhca: host-side argument validation, then kernel launches.
+// Nothing here allocates, synchronizes or keeps state between calls.
+#include <math.h>
+#include <string.h>
+
+#include "hca.h"
+#include "hca_common.h"
+#include "hca_internal.h"
+#include "hca_testing.h"
+
+using namespace hca;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool valid_m(int m) { return m >= 1 && m <= 256 && (256 % m) == 0; }
+
+// a pool descriptor that the kernels can index safely
+bool cache_ok(const hca_paged_cache& c) {
+  if (!c.codes || c.num_pages < 1 || c.epp < 1 || c.dim < 8 || (c.dim % 8) != 0) return false;
+  if (256 % c.epp != 0) return false;
+  if (c.dtype != HCA_BF16 && c.dtype != HCA_FP8_E4M3 && c.dtype != HCA_FP4_E2M1) return false;
+  if (c.dtype != HCA_BF16 && !c.scales) return false;
+  if (c.dtype == HCA_FP4_E2M1 && (c.dim % 32) != 0) return false;
+  if (!aligned(c.codes, 16)) return false;
+  return true;
+}
+
+hca_status from_hip(hipError_t e) { return e == hipSuccess ? HCA_OK : HCA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* hca_status_string(hca_status s) {
+  switch (s) {
+    case HCA_OK: return "ok";
+    case HCA_ERR_INVALID: return "invalid argument";
+    case HCA_ERR_UNSUPPORTED: return "unsupported shape or type";
+    case HCA_ERR_WORKSPACE: return "workspace missing or too small";
+    case HCA_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+const char* hca_version(void) { return "hca 0.1.0 gfx950"; }
+
+hca_status kv_compress(const uint16_t* x, int64_t x_stride_b, const float* gate_logit, int64_t z_stride_b,
+                       const float* pos_bias, const int32_t* pos0, const int32_t* ntok, int32_t B, int32_t max_ntok,
+                       int32_t d, int32_t m, float rope_theta, float* out, int64_t out_stride_b, void* stream) {
+  if (B < 0 || max_ntok < 0) return HCA_ERR_INVALID;
+  if (!valid_m(m) || d < 8 || (d % 8) != 0) return HCA_ERR_INVALID;
+  if (d > 2048) return HCA_ERR_UNSUPPORTED;
+  if (!(rope_theta > 0.0f) || !isfinite(rope_theta)) return HCA_ERR_INVALID;
+  if (B == 0 || max_ntok == 0) return HCA_OK;
+  if (!x || !gate_logit || !pos_bias || !pos0 || !ntok || !out) return HCA_ERR_INVALID;
+  if (!aligned(x, 16) || !aligned(out, 16)) return HCA_ERR_INVALID;
+  const int64_t n_out = (max_ntok + m - 1) / m;
+  if (x_stride_b % 8 != 0 || out_stride_b % 4 != 0) return HCA_ERR_INVALID;
+  if (B > 1 && (x_stride_b < (int64_t)max_ntok * d || z_stride_b < max_ntok || out_stride_b < n_out * d))
+    return HCA_ERR_INVALID;
+  CompressArgs a{x, x_stride_b, gate_logit, z_stride_b, pos_bias, pos0, ntok, B, max_ntok, d, m, rope_theta, out,
+                 out_stride_b};
+  return from_hip(launch_compress(a, (hipStream_t)stream));
+}
+
+hca_status kv_quantize_page(const float* src, int64_t src_stride_b, const int32_t* e0, const int32_t* ne, int32_t B,
+                            int32_t max_ne, const int32_t* block_table, int32_t bt_stride, hca_paged_cache dst,
+                            void* stream) {
+  if (B < 0 || max_ne < 0 || bt_stride < 1) return HCA_ERR_INVALID;
+  if (!cache_ok(dst)) return HCA_ERR_INVALID;
+  if (B == 0 || max_ne == 0) return HCA_OK;
+  if (!src || !e0 || !ne || !block_table) return HCA_ERR_INVALID;
+  if (!aligned(src, 16) || src_stride_b % 4 != 0) return HCA_ERR_INVALID;
+  if (B > 1 && src_stride_b < (int64_t)max_ne * dst.dim) return HCA_ERR_INVALID;
+  QuantArgs a{src, src_stride_b, e0, ne, B, max_ne, block_table, bt_stride, dst};
+  return from_hip(launch_quantize(a, (hipStream_t)stream));
+}
+
+size_t indexer_topk_workspace(int32_t B, int32_t max_seq_len, int32_t m, int32_t k) {
+  if (B < 0 || max_seq_len < 0 || !valid_m(m) || k < 1) return 0;
+  return indexer_ws_layout(B, max_seq_len, m, k).total;
+}
+
+hca_status indexer_topk(const uint16_t* q_idx, const float* head_w, int32_t HI, hca_paged_cache idx_keys,
+                        const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens, int32_t B,
+                        int32_t max_seq_len, int32_t m, int32_t k, int32_t* out_idx, int32_t* out_n, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (B < 0 || max_seq_len < 0 || !valid_m(m) || k < 1 || bt_stride < 1) return HCA_ERR_INVALID;
+  if (k > 8192) return HCA_ERR_UNSUPPORTED;
+  if (HI < 1) return HCA_ERR_INVALID;
+  if (HI > 16) return HCA_ERR_UNSUPPORTED;
+  if (!cache_ok(idx_keys) || idx_keys.epp != 256 / m) return HCA_ERR_INVALID;
+  const int di = idx_keys.dim;
+  if (di != 32 && di != 64 && di != 128 && di != 256) return HCA_ERR_UNSUPPORTED;
+  if ((int64_t)bt_stride * 256 < max_seq_len) return HCA_ERR_INVALID;
+  if (B == 0) return HCA_OK;
+  if (!q_idx || !head_w || !block_table || !seq_lens || !out_idx || !out_n) return HCA_ERR_INVALID;
+  if (!aligned(q_idx, 16)) return HCA_ERR_INVALID;
+  const IndexerWs lay = indexer_ws_layout(B, max_seq_len, m, k);
+  if (!ws || ws_bytes < lay.total || !aligned(ws, 256)) return HCA_ERR_WORKSPACE;
+  IndexerArgs a{q_idx, head_w, HI, idx_keys, block_table, bt_stride, seq_lens, B, max_seq_len, m, k, out_idx, out_n,
+                reinterpret_cast<unsigned char*>(ws), lay};
+  return from_hip(launch_indexer(a, (hipStream_t)stream));
+}
+
+size_t paged_hybrid_decode_workspace(int32_t B, int32_t H, int32_t d, int32_t max_seq_len, int32_t m, int32_t window,
+                                     int32_t k) {
+  if (B < 0 || H < 1 || d < 1 || max_seq_len < 0 || !valid_m(m) || window < 0 || k < 0) return 0;
+  return attn_plan(B, H, d, max_seq_len, m, window, k, k > 0).total;
+}
+
+hca_status paged_hybrid_decode(const uint16_t* q, int32_t H, hca_paged_cache kv, const int32_t* block_table,
+                               int32_t bt_stride, hca_paged_cache win, const int32_t* win_block_table,
+                               int32_t wbt_stride, const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t m,
+                               int32_t window, const int32_t* sel_idx, const int32_t* sel_n, int32_t k,
+                               float softmax_scale, float rope_theta, float* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (B < 0 || max_seq_len < 0 || !valid_m(m) || bt_stride < 1) return HCA_ERR_INVALID;
+  if (H < 1) return HCA_ERR_INVALID;
+  if (H > 128) return HCA_ERR_UNSUPPORTED;
+  if (!cache_ok(kv) || kv.epp != 256 / m) return HCA_ERR_INVALID;
+  if (kv.dtype == HCA_FP4_E2M1) return HCA_ERR_UNSUPPORTED;
+  const int d = kv.dim;
+  if (d != 64 && d != 128 && d != 256 && d != 512) return HCA_ERR_UNSUPPORTED;
+  if (window < 0 || window > 256) return HCA_ERR_INVALID;
+  if (window > 0) {
+    if (!cache_ok(win) || win.epp != 256 || win.dim != d || !win_block_table || wbt_stride < 1) return HCA_ERR_INVALID;
+    if (win.dtype == HCA_FP4_E2M1) return HCA_ERR_UNSUPPORTED;
+    if ((int64_t)wbt_stride * 256 < max_seq_len) return HCA_ERR_INVALID;
+  }
+  if ((int64_t)bt_stride * 256 < max_seq_len) return HCA_ERR_INVALID;
+  if (sel_idx && (!sel_n || k < 1)) return HCA_ERR_INVALID;
+  if (!isfinite(softmax_scale) || !(rope_theta > 0.0f) || !isfinite(rope_theta)) return HCA_ERR_INVALID;
+  if (B == 0) return HCA_OK;
+  if (!q || !block_table || !seq_lens || !out) return HCA_ERR_INVALID;
+  if (!aligned(q, 16)) return HCA_ERR_INVALID;
+  const AttnPlan plan = attn_plan(B, H, d, max_seq_len, m, window, sel_idx ? k : 0, sel_idx != nullptr);
+  if (!ws || ws_bytes < plan.total || !aligned(ws, 256)) return HCA_ERR_WORKSPACE;
+  hca_paged_cache w = win;
+  if (window == 0) { w = kv; w.epp = 256; }  // never read
+  AttnArgs a{q, H, kv, block_table, bt_stride, w, window > 0 ? win_block_table : block_table,
+             window > 0 ? wbt_stride : bt_stride, seq_lens, B, max_seq_len, m, window, sel_idx, sel_n,
+             sel_idx ? k : 0, softmax_scale, rope_theta, out, lse, reinterpret_cast<unsigned char*>(ws), plan};
+  return from_hip(launch_attention(a, (hipStream_t)stream));
+}
+
+hca_status kv_gather(hca_paged_cache src, const int32_t* block_table, int32_t bt_stride, const int32_t* n_rows,
+                     int32_t B, int32_t max_rows, void* dst_codes, void* dst_scales, void* stream) {
+  if (B < 0 || max_rows < 0 || bt_stride < 1) return HCA_ERR_INVALID;
+  if (!cache_ok(src)) return HCA_ERR_INVALID;
+  if ((int64_t)bt_stride * src.epp < max_rows) return HCA_ERR_INVALID;
+  if (B == 0 || max_rows == 0) return HCA_OK;
+  if (!block_table || !n_rows || !dst_codes) return HCA_ERR_INVALID;
+  if (src.dtype != HCA_BF16 && !dst_scales) return HCA_ERR_INVALID;
+  if (!aligned(dst_codes, 4)) return HCA_ERR_INVALID;
+  GatherArgs a{src, block_table, bt_stride, n_rows, B, max_rows, dst_codes, dst_scales};
+  return from_hip(launch_gather(a, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------ checking hooks
+hca_status hca_host_e4m3_encode(const float* in, uint8_t* out, int64_t n) {
+  if (!in || !out || n < 0) return HCA_ERR_INVALID;
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode(in[i]);
+  return HCA_OK;
+}
+hca_status hca_host_e2m1_encode(const float* in, uint8_t* out, int64_t n) {
+  if (!in || !out || n < 0) return HCA_ERR_INVALID;
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)e2m1_encode(in[i]);
+  return HCA_OK;
+}
+hca_status hca_host_bf16_encode(const float* in, uint16_t* out, int64_t n) {
+  if (!in || !out || n < 0) return HCA_ERR_INVALID;
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_encode(in[i]);
+  return HCA_OK;
+}
+
+}  // extern "C"
+
+// probes: same conversions / MFMA as the kernels, on known data
+namespace hca {
+
+__global__ void probe_decode_kernel(const uint8_t* codes, float* out, int n, int kind) {
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (i >= n) return;
+  if (kind == 0) {
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(codes + i);
+    const uint32_t w1 = *reinterpret_cast<const uint32_t*>(codes + i + 4);
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+    out[i + 0] = a[0]; out[i + 1] = a[1]; out[i + 2] = b[0]; out[i + 3] = b[1];
+    out[i + 4] = c[0]; out[i + 5] = c[1]; out[i + 6] = d[0]; out[i + 7] = d[1];
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + i / 2);
+    uint32_t r[4];
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3));
+    for (int sel = 0; sel < 4; ++sel) {
+      out[i + 2 * sel] = u2f(r[sel] << 16);
+      out[i + 2 * sel + 1] = u2f(r[sel] & 0xFFFF0000u);
+    }
+  }
+}
+
+__global__ void probe_mfma_kernel(const uint16_t* A, const uint16_t* B, float* D, int kind) {
+  const int l = threadIdx.x;
+  u32x4 ra, rb;
+  uint16_t av[8], bv[8];
+  for (int j = 0; j < 8; ++j) {
+    av[j] = A[(l % 16) * 32 + 8 * (l / 16) + j];
+    bv[j] = B[(8 * (l / 16) + j) * 16 + (l % 16)];
+  }
+  for (int j = 0; j < 4; ++j) {
+    ra[j] = (uint32_t)av[2 * j] | ((uint32_t)av[2 * j + 1] << 16);
+    rb[j] = (uint32_t)bv[2 * j] | ((uint32_t)bv[2 * j + 1] << 16);
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (kind == 0)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ra), __builtin_bit_cast(f16x8, rb), acc, 0, 0, 0);
+  else
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra), __builtin_bit_cast(bf16x8, rb), acc, 0, 0, 0);
+  for (int i = 0; i < 4; ++i) D[(4 * (l / 16) + i) * 16 + (l % 16)] = acc[i];
+}
+
+}  // namespace hca
+
+extern "C" {
+
+hca_status hca_probe_decode(const uint8_t* codes, float* out, int32_t n, int32_t kind, void* stream) {
+  if (!codes || !out || n < 0 || (n % 8) != 0 || (kind != 0 && kind != 1)) return HCA_ERR_INVALID;
+  if (n == 0) return HCA_OK;
+  const int threads = n / 8;
+  hipLaunchKernelGGL(probe_decode_kernel, dim3((threads + 255) / 256), dim3(256), 0, (hipStream_t)stream, codes, out, n,
+                     kind);
+  return from_hip(hipGetLastError());
+}
+
+hca_status hca_probe_mfma(const uint16_t* A, const uint16_t* B, float* D, int32_t kind, void* stream) {
+  if (!A || !B || !D || (kind != 0 && kind != 1)) return HCA_ERR_INVALID;
+  hipLaunchKernelGGL(probe_mfma_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, A, B, D, kind);
+  return from_hip(hipGetLastError());
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// Shared device helpers for the hca kernels (gfx950).
+//
+// Codecs follow the OCP bit-field definitions of E4M3 "FN" and E2M1 and the
+// bfloat16 truncation of binary32 (storage formats of the V4 page, sections
+// 2.1 and 2.2, and the vLLM-0.7.2 page, section 2.2 "fp8_e4m3").  The encoders
+// are written with exact float steps (power-of-two scaling and rintf, which
+// rounds half to even) so that the same source gives the same codes on the
+// host and on the GPU; they are exported to the host for checking.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define HCA_HD __host__ __device__ __forceinline__
+
+namespace hca {
+
+HCA_HD uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+HCA_HD float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// ------------------------------------------------------------------ bf16
+HCA_HD uint16_t bf16_encode(float x) {
+  // round half to even on the 16 dropped bits (inputs are finite)
+  uint32_t u = f2u(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+HCA_HD float bf16_decode(uint16_t h) { return u2f((uint32_t)h << 16); }
+
+// ------------------------------------------------------------------ E4M3 (FN)
+// value = (-1)^s * 2^(e-7) * (1 + m/8) for e > 0, (-1)^s * 2^-6 * m/8 for e = 0;
+// largest finite 448; S.1111.111 is NaN and is never produced.
+HCA_HD uint8_t e4m3_encode(float y) {
+  const uint32_t sign = (f2u(y) >> 24) & 0x80u;
+  float a = fminf(fabsf(y), 448.0f);  // saturate
+  uint32_t code;
+  if (a < 0.015625f) {  // below 2^-6: subnormal grid of step 2^-9 (8 -> smallest normal)
+    code = (uint32_t)rintf(a * 512.0f);
+  } else {
+    int E = (int)((f2u(a) >> 23) & 0xFFu) - 127;  // -6 .. 8
+    uint32_t r = (uint32_t)rintf(ldexpf(a, 3 - E));  // 8 .. 16, half to even
+    if (r == 16u) { r = 8u; E += 1; }
+    code = ((uint32_t)(E + 7) << 3) | (r - 8u);
+  }
+  return (uint8_t)(code | sign);
+}
+HCA_HD float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  const float v = e ? ldexpf(1.0f + 0.125f * (float)m, (int)e - 7) : ldexpf((float)m, -9);
+  return (c & 0x80u) ? -v : v;
+}
+
+// ------------------------------------------------------------------ E2M1
+// magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}; codes 0..7 in that order, bit 3 = sign.
+HCA_HD uint32_t e2m1_encode(float y) {
+  const uint32_t sign = (f2u(y) >> 28) & 0x8u;
+  const float a = fminf(fabsf(y), 6.0f);
+  uint32_t code;
+  if (a < 2.0f) code = (uint32_t)rintf(a * 2.0f);              // step 0.5
+  else if (a < 4.0f) code = 4u + (uint32_t)rintf(a - 2.0f);    // step 1
+  else code = 6u + (uint32_t)rintf((a - 4.0f) * 0.5f);         // step 2
+  return code | sign;
+}
+HCA_HD float e2m1_decode(uint32_t c) {
+  const uint32_t mag = c & 7u;
+  const float v = mag < 4u ? 0.5f * (float)mag : (mag == 4u ? 2.0f : (mag == 5u ? 3.0f : (mag == 6u ? 4.0f : 6.0f)));
+  return (c & 8u) ? -v : v;
+}
+
+// ------------------------------------------------------------------ score keys
+// Monotone map float -> uint32 (larger float, larger key); -0 is folded to +0.
+HCA_HD uint32_t order_key(float s) {
+  const uint32_t u = f2u(s + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace hca
+
+// ------------------------------------------------------------------ device only
+namespace hca {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// RoPE of pair i (dims 2i, 2i+1) at integer position pos: angle pos * theta^(-2i/d),
+// reduced modulo 2*pi in fp64 before the fp32 sine/cosine (positions reach 2^20,
+// where an fp32 angle would be off by ~0.06 rad).
+__device__ __forceinline__ double rope_inv_freq(int i, int d, float theta) {
+  return pow((double)theta, -2.0 * (double)i / (double)d);
+}
+__device__ __forceinline__ void rope_cs(double pos, double inv_freq, float& c, float& s) {
+  const double twopi_hi = 6.283185307179586232;
+  const double twopi_lo = 2.4492935982947064e-16;
+  const double phi = pos * inv_freq;
+  const double k = rint(phi * (1.0 / twopi_hi));
+  double r = fma(-k, twopi_hi, phi);
+  r = fma(-k, twopi_lo, r);
+  sincosf((float)r, &s, &c);
+}
+
+// Wave64 reductions (butterfly through ds_swizzle/DPP via __shfl_xor).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+}  // namespace hca

@@ -1,0 +1,81 @@
+// Internal launchers shared by the kernel sources and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hca.h"
+
+namespace hca {
+
+struct CompressArgs {
+  const uint16_t* x; int64_t xs;
+  const float* z; int64_t zs;
+  const float* beta;
+  const int32_t* pos0; const int32_t* ntok;
+  int B, max_ntok, d, m;
+  float theta;
+  float* out; int64_t os;
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+
+struct QuantArgs {
+  const float* src; int64_t ss;
+  const int32_t* e0; const int32_t* ne;
+  int B, max_ne;
+  const int32_t* bt; int bts;
+  hca_paged_cache dst;
+};
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+
+struct GatherArgs {
+  hca_paged_cache src;
+  const int32_t* bt; int bts;
+  const int32_t* n_rows;
+  int B, max_rows;
+  void* dst_codes; void* dst_scales;
+};
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+
+// indexer workspace layout (all offsets 256-byte aligned)
+struct IndexerWs {
+  size_t scores, hist, cand, bitmap, counters, total;
+  int n_max;  // max entries per sequence
+};
+IndexerWs indexer_ws_layout(int B, int max_seq_len, int m, int k);
+constexpr int kHistBins = 4096;  // top 12 bits of the score key
+
+struct IndexerArgs {
+  const uint16_t* q; const float* w; int HI;
+  hca_paged_cache keys;
+  const int32_t* bt; int bts;
+  const int32_t* lens;
+  int B, max_len, m, k;
+  int32_t* out_idx; int32_t* out_n;
+  unsigned char* ws; IndexerWs lay;
+};
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
+
+// attention workspace: per (sequence, split, head) partial (m, l) and o[d]
+struct AttnPlan {
+  int rows_max;     // upper bound of rows of any sequence
+  int splits;       // splits per sequence
+  int rows_per_split;
+  int head_blocks;  // ceil(H / 64)
+  size_t o_off, ml_off, total;
+};
+AttnPlan attn_plan(int B, int H, int d, int max_seq_len, int m, int window, int k, bool has_sel);
+
+struct AttnArgs {
+  const uint16_t* q; int H;
+  hca_paged_cache kv; const int32_t* bt; int bts;
+  hca_paged_cache win; const int32_t* wbt; int wbts;
+  const int32_t* lens; int B, max_len, m, window;
+  const int32_t* sel; const int32_t* sel_n; int k;
+  float scale, theta;
+  float* out; float* lse;
+  unsigned char* ws; AttnPlan plan;
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+}  // namespace hca

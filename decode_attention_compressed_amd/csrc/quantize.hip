@@ -1,0 +1,192 @@
+// kv_quantize_page and kv_gather: entries <-> physical pages through the block
+// table (V4 page, section 3.1.1: one 256-token logical block, 256/m entries a
+// page; section 3.1.3: page size = block size x compress ratio x bytes per
+// element; sections 2.1/2.2: fp8 main KV, fp8 or fp4 indexer keys;
+// vLLM-0.7.2 page, section 2.1: logical block -> physical page tables).
+//
+// One block per (sequence, page).  fp8 pages need the amax of the whole page
+// before any code can be written: pass 1 streams the page's fp32 rows with
+// 16-byte loads and reduces the max (wave64 butterflies, then LDS), pass 2
+// re-reads the rows (now in L2) and writes the codes with 16-byte stores.
+// fp4 scales are per 32 elements of a row, so four lanes own one block of 32
+// and reduce its amax with two lane swaps.
+#include "hca_common.h"
+#include "hca_internal.h"
+
+namespace hca {
+
+constexpr int kQThreads = 256;
+
+__device__ __forceinline__ bool page_ok(int phys, int num_pages) { return phys >= 0 && phys < num_pages; }
+
+__global__ __launch_bounds__(kQThreads) void quantize_fp8_kernel(QuantArgs a) {
+  const int b = blockIdx.y;
+  const int epp = a.dst.epp, dim = a.dst.dim;
+  const int n = clampi(a.ne[b], 0, a.max_ne);
+  const int E0 = a.e0[b];
+  const int npages = (n + epp - 1) / epp;
+  uint8_t* codes = reinterpret_cast<uint8_t*>(a.dst.codes);
+  float* scales = reinterpret_cast<float*>(a.dst.scales);
+  __shared__ float red_s[kQThreads / 64];
+  for (int pg = blockIdx.x; pg < npages; pg += gridDim.x) {
+    const int lb = E0 / epp + pg;
+    if (lb < 0 || lb >= a.bts) continue;
+    const int phys = a.bt[(int64_t)b * a.bts + lb];
+    if (!page_ok(phys, a.dst.num_pages)) continue;  // uniform over the block
+    const int rows = min(epp, n - pg * epp);
+    const int nv4 = rows * dim / 4;  // valid float4 groups (dim % 4 == 0)
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.src + (int64_t)b * a.ss + (int64_t)pg * epp * dim);
+    float amax = 0.0f;
+    for (int i = threadIdx.x; i < nv4; i += kQThreads) {
+      const f32x4 v = src[i];
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    }
+    amax = wave_max(amax);
+    if ((threadIdx.x & 63) == 0) red_s[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
+    __syncthreads();
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(codes + (int64_t)phys * epp * dim);
+    const int tot4 = epp * dim / 4;
+    for (int i = threadIdx.x; i < tot4; i += kQThreads) {
+      uint32_t word = 0;
+      if (i < nv4) {
+        const f32x4 v = src[i];
+        word = (uint32_t)e4m3_encode(v[0] / s) | ((uint32_t)e4m3_encode(v[1] / s) << 8) |
+               ((uint32_t)e4m3_encode(v[2] / s) << 16) | ((uint32_t)e4m3_encode(v[3] / s) << 24);
+      }
+      dst[i] = word;
+    }
+    if (threadIdx.x == 0) scales[phys] = s;
+  }
+}
+
+__global__ __launch_bounds__(kQThreads) void quantize_fp4_kernel(QuantArgs a) {
+  // four lanes per 32-element block, 8 elements (two float4) each
+  const int b = blockIdx.y;
+  const int epp = a.dst.epp, dim = a.dst.dim;
+  const int n = clampi(a.ne[b], 0, a.max_ne);
+  const int E0 = a.e0[b];
+  const int npages = (n + epp - 1) / epp;
+  const int nblk = dim / 32;
+  uint8_t* codes = reinterpret_cast<uint8_t*>(a.dst.codes);
+  uint8_t* scales = reinterpret_cast<uint8_t*>(a.dst.scales);
+  for (int pg = blockIdx.x; pg < npages; pg += gridDim.x) {
+    const int lb = E0 / epp + pg;
+    if (lb < 0 || lb >= a.bts) continue;
+    const int phys = a.bt[(int64_t)b * a.bts + lb];
+    if (!page_ok(phys, a.dst.num_pages)) continue;
+    const int rows = min(epp, n - pg * epp);
+    const float* src = a.src + (int64_t)b * a.ss + (int64_t)pg * epp * dim;
+    uint8_t* pc = codes + (int64_t)phys * epp * (dim / 2);
+    uint8_t* ps = scales + (int64_t)phys * epp * nblk;
+    const int units = epp * nblk * 4;  // (row, block, quarter); multiple of 64
+    for (int u = threadIdx.x; u < units; u += kQThreads) {
+      const int q = u & 3;
+      const int blk = (u >> 2) % nblk;
+      const int row = (u >> 2) / nblk;
+      float v[8];
+      float amax = 0.0f;
+      if (row < rows) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(src + (int64_t)row * dim + blk * 32 + q * 8);
+        const f32x4 v0 = p[0], v1 = p[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { v[i] = v0[i]; v[4 + i] = v1[i]; }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      const uint32_t sc = row < rows ? e4m3_encode(amax / 6.0f) : 0u;
+      const float sdec = e4m3_decode(sc);
+      uint32_t word = 0;
+      if (sdec > 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= e2m1_encode(v[i] / sdec) << (4 * i);
+      }
+      *reinterpret_cast<uint32_t*>(pc + (int64_t)row * (dim / 2) + blk * 16 + q * 4) = word;
+      if (q == 0) ps[(int64_t)row * nblk + blk] = (uint8_t)sc;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kQThreads) void quantize_bf16_kernel(QuantArgs a) {
+  const int b = blockIdx.y;
+  const int epp = a.dst.epp, dim = a.dst.dim;
+  const int n = clampi(a.ne[b], 0, a.max_ne);
+  const int E0 = a.e0[b];
+  const int npages = (n + epp - 1) / epp;
+  uint16_t* codes = reinterpret_cast<uint16_t*>(a.dst.codes);
+  for (int pg = blockIdx.x; pg < npages; pg += gridDim.x) {
+    const int lb = E0 / epp + pg;
+    if (lb < 0 || lb >= a.bts) continue;
+    const int phys = a.bt[(int64_t)b * a.bts + lb];
+    if (!page_ok(phys, a.dst.num_pages)) continue;
+    const int rows = min(epp, n - pg * epp);
+    const int nv4 = rows * dim / 4;
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.src + (int64_t)b * a.ss + (int64_t)pg * epp * dim);
+    u32x2* dst = reinterpret_cast<u32x2*>(codes + (int64_t)phys * epp * dim);
+    const int tot4 = epp * dim / 4;
+    for (int i = threadIdx.x; i < tot4; i += kQThreads) {
+      u32x2 w = {0u, 0u};
+      if (i < nv4) {
+        const f32x4 v = src[i];
+        w[0] = (uint32_t)bf16_encode(v[0]) | ((uint32_t)bf16_encode(v[1]) << 16);
+        w[1] = (uint32_t)bf16_encode(v[2]) | ((uint32_t)bf16_encode(v[3]) << 16);
+      }
+      dst[i] = w;
+    }
+  }
+}
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
+  const int epp = a.dst.epp;
+  const int pages_max = (a.max_ne + epp - 1) / epp;
+  if (a.B == 0 || pages_max == 0) return hipSuccess;
+  const int gx = pages_max > 8192 ? 8192 : pages_max;
+  const dim3 grid(gx, a.B);
+  switch (a.dst.dtype) {
+    case HCA_FP8_E4M3: hipLaunchKernelGGL(quantize_fp8_kernel, grid, dim3(kQThreads), 0, s, a); break;
+    case HCA_FP4_E2M1: hipLaunchKernelGGL(quantize_fp4_kernel, grid, dim3(kQThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(quantize_bf16_kernel, grid, dim3(kQThreads), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ gather
+__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
+  const int b = blockIdx.y;
+  const int n = clampi(a.n_rows[b], 0, a.max_rows);
+  const int epp = a.src.epp, dim = a.src.dim;
+  const int row_bytes = a.src.dtype == HCA_FP8_E4M3 ? dim : (a.src.dtype == HCA_FP4_E2M1 ? dim / 2 : 2 * dim);
+  const int w4 = row_bytes / 4;  // 32-bit words per row
+  const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.src.codes);
+  uint8_t* dst = reinterpret_cast<uint8_t*>(a.dst_codes);
+  for (int r = blockIdx.x; r < n; r += gridDim.x) {
+    const int phys = a.bt[(int64_t)b * a.bts + r / epp];
+    if (!page_ok(phys, a.src.num_pages)) continue;
+    const int slot = r % epp;
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(codes + ((int64_t)phys * epp + slot) * row_bytes);
+    uint32_t* dp = reinterpret_cast<uint32_t*>(dst + ((int64_t)b * a.max_rows + r) * row_bytes);
+    for (int i = threadIdx.x; i < w4; i += 256) dp[i] = sp[i];
+    if (threadIdx.x == 0 && a.src.dtype == HCA_FP8_E4M3)
+      reinterpret_cast<float*>(a.dst_scales)[(int64_t)b * a.max_rows + r] = reinterpret_cast<const float*>(a.src.scales)[phys];
+    if (a.src.dtype == HCA_FP4_E2M1 && threadIdx.x < dim / 32) {
+      const uint8_t* ss = reinterpret_cast<const uint8_t*>(a.src.scales) + ((int64_t)phys * epp + slot) * (dim / 32);
+      reinterpret_cast<uint8_t*>(a.dst_scales)[((int64_t)b * a.max_rows + r) * (dim / 32) + threadIdx.x] = ss[threadIdx.x];
+    }
+  }
+}
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
+  if (a.B == 0 || a.max_rows == 0) return hipSuccess;
+  const int gx = a.max_rows > 16384 ? 16384 : a.max_rows;
+  hipLaunchKernelGGL(gather_kernel, dim3(gx, a.B), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hca

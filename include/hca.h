@@ -1,0 +1,233 @@
+/*
+ * hca.h -- decode attention over hybrid compressed KV caches, C ABI.
+ *
+ * The method (from "DeepSeek-V4 Serving ... vLLM", wmrh.cn news 47220, and
+ * "vLLM 0.7.2 ... DeepSeek-V4", lpnh.cn news 995630):
+ *   - a compressor folds every m consecutive token vectors (m = 4: c4a layers,
+ *     m = 128: c128a layers) into one shared K=V entry (V4 page, section 2.1);
+ *   - entries are stored in fp8 pages (indexer keys in fp8 or fp4) behind a block
+ *     table whose logical block is 256 raw tokens (V4 page, sections 2.1, 2.2,
+ *     3.1.1, 3.1.3; vLLM-0.7.2 page, section 2.1);
+ *   - for c4a layers an indexer scores the entries and keeps the top k
+ *     (V4 page, section 2.2);
+ *   - the decode query attends to the selected entries plus a raw sliding window
+ *     of recent tokens, with RoPE on the key use of the shared vector and inverse
+ *     RoPE on the output (V4 page, sections 2.1 and 2.3).
+ *
+ * Conventions shared by every entry point
+ *   Memory     every pointer argument is DEVICE memory owned by the caller (for
+ *              example a torch tensor's data pointer), unless it is documented
+ *              as a host value.  The library allocates nothing, keeps no state
+ *              between calls, never synchronizes, and enqueues all work on
+ *              `stream` (a hipStream_t; NULL is the null stream).
+ *   Layout     all arrays are dense row-major C arrays of the shapes given;
+ *              "bf16" arrays hold bfloat16 bit patterns in uint16_t.
+ *   Block      logical block i of a sequence covers raw positions
+ *   tables     [256 i, 256 i + 256) and, in a pool with epp = 256/m entries per
+ *              page, entries [i*epp, (i+1)*epp).  table[b * stride + i] is the
+ *              physical page of block i of sequence b, or -1 if unmapped.  One
+ *              table may serve every compressed pool of every layer; the window
+ *              pool (m = 1, 256 tokens a page) has its own table.  Pages may be
+ *              shared by several sequences (prefix aliasing); shared pages are
+ *              read-only while shared.
+ *   Errors     arguments are validated on the host before anything is
+ *              launched; a failed validation returns the status and launches
+ *              nothing.  Launch failures return HCA_ERR_HIP.  Device-side values
+ *              (lengths, table entries, indices) are not validated; kernels
+ *              clamp lengths to the host bound they are given and skip page ids
+ *              outside [0, num_pages) and indices outside the valid range, so a
+ *              bad value gives a wrong result, never an out-of-bounds access.
+ *   Threads    all functions are reentrant; calls that write the same memory
+ *              must be ordered by the caller (same stream or events).
+ */
+#ifndef HCA_H
+#define HCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HCA_OK = 0,
+  HCA_ERR_INVALID = 1,     /* an argument is out of range or a pointer is NULL */
+  HCA_ERR_UNSUPPORTED = 2, /* valid, but not a shape/type this build handles    */
+  HCA_ERR_WORKSPACE = 3,   /* the workspace is NULL or too small                */
+  HCA_ERR_HIP = 4          /* a HIP launch or runtime call failed               */
+} hca_status;
+
+/* Storage formats (OCP definitions):
+ *   HCA_BF16      bfloat16, round to nearest even from fp32, no scale;
+ *   HCA_FP8_E4M3  E4M3 "FN" (bias 7, max 448, no inf), one fp32 scale per
+ *                 physical page: s = fl32(amax/448) over the page's valid
+ *                 elements (1 when amax = 0), code = E4M3(fl32(x/s)), round to
+ *                 nearest even, saturating at +-448;
+ *   HCA_FP4_E2M1  E2M1 (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6), two per byte
+ *                 (element 2c in the low nibble of byte c), one E4M3 scale per
+ *                 32 consecutive elements of a row: sc = E4M3(fl32(amax32/6)),
+ *                 code = E2M1(fl32(x/sc)), all codes 0 when sc decodes to 0. */
+typedef enum { HCA_BF16 = 0, HCA_FP8_E4M3 = 1, HCA_FP4_E2M1 = 2 } hca_dtype;
+
+/* One paged pool (one KV kind of one layer).
+ *   codes   HCA_FP8_E4M3: uint8  [num_pages][epp][dim]
+ *           HCA_FP4_E2M1: uint8  [num_pages][epp][dim/2]
+ *           HCA_BF16:     uint16 [num_pages][epp][dim]
+ *   scales  HCA_FP8_E4M3: float  [num_pages]
+ *           HCA_FP4_E2M1: uint8  [num_pages][epp][dim/32]   (E4M3 codes)
+ *           HCA_BF16:     unused (may be NULL)
+ *   epp     entries (rows) per page: 256/m; 256 for a window pool. */
+typedef struct {
+  void* codes;
+  void* scales;
+  int32_t num_pages;
+  int32_t epp;
+  int32_t dim;
+  int32_t dtype; /* hca_dtype */
+} hca_paged_cache;
+
+/* Human-readable name of a status (static string). */
+const char* hca_status_string(hca_status s);
+
+/* Library version, e.g. "hca 0.1.0 gfx950". */
+const char* hca_version(void);
+
+/*
+ * kv_compress -- the compressor (V4 page, section 2.1: a learned weighted sum
+ * with positional bias folds every m tokens into one entry; section 3.1.2: the
+ * not-yet-folded tokens are a rolling residual; section 3.2.1: RoPE is applied
+ * before the entry is inserted into the cache).
+ *
+ * For sequence b, tokens t = 0 .. ntok[b]-1 are the raw vectors of positions
+ * pos0[b] + t (pos0[b] a multiple of m).  Entry j (j < ceil(ntok[b]/m)) folds
+ * slots i < r = min(m, ntok[b] - j*m):
+ *     w_i = softmax_i(gate_logit[t] + pos_bias[i]),  t = j*m + i
+ *     c   = sum_i w_i x[t]
+ *     out[b][j] = RoPE(c, pos0[b] + j*m)
+ * A partial group (r < m) is normalized over its r slots, which is the state of
+ * the rolling residual; re-running the call on a decode step's open group
+ * (pos0 = m*floor((L-1)/m), ntok = L - pos0) re-emits the open entry.  With
+ * m = 1 this is the window insert RoPE(x_t, t).  RoPE rotates adjacent pairs
+ * (2i, 2i+1) by angle p * rope_theta^(-2i/d); the angle is reduced in fp64.
+ *
+ *   x          bf16  x[b * x_stride_b + t * d + c]
+ *   gate_logit float gate_logit[b * z_stride_b + t]
+ *   pos_bias   float [m]
+ *   pos0, ntok int32 [B] (device); ntok[b] is clamped to [0, max_ntok]
+ *   max_ntok   host bound on ntok (sizes the grid)
+ *   d          even, 2 <= d, d % 8 == 0;  m in {1, 2, 4, ..., 256}
+ *   out        float out[b * out_stride_b + j * d + c]
+ */
+hca_status kv_compress(const uint16_t* x, int64_t x_stride_b, const float* gate_logit,
+                       int64_t z_stride_b, const float* pos_bias, const int32_t* pos0,
+                       const int32_t* ntok, int32_t B, int32_t max_ntok, int32_t d, int32_t m,
+                       float rope_theta, float* out, int64_t out_stride_b, void* stream);
+
+/*
+ * kv_quantize_page -- quantize entries into their pages (V4 page, sections
+ * 3.1.1 and 3.1.3: one 256-token logical block, page size = block size x
+ * compress ratio x bytes per element; fp8 main KV, fp8/fp4 indexer keys).
+ *
+ * For sequence b, rows i = 0 .. ne[b]-1 of src are entries e0[b] + i
+ * (e0[b] a multiple of dst.epp).  Every page touched is rewritten whole: its
+ * valid rows are the rows of this call that fall in it; slots past them are
+ * zeroed; the fp8 page scale is taken over the valid rows only.  Pages written
+ * by different sequences in one call must be distinct.
+ *
+ *   src        float src[b * src_stride_b + i * dst.dim + c]
+ *   e0, ne     int32 [B] (device); ne[b] clamped to [0, max_ne]
+ *   block_table int32 [B][bt_stride]
+ */
+hca_status kv_quantize_page(const float* src, int64_t src_stride_b, const int32_t* e0,
+                            const int32_t* ne, int32_t B, int32_t max_ne,
+                            const int32_t* block_table, int32_t bt_stride, hca_paged_cache dst,
+                            void* stream);
+
+/*
+ * indexer_topk -- indexer scoring and top-k selection for c4a layers (V4 page,
+ * section 2.2: a separate, smaller indexer KV tells the query which compressed
+ * entries to look in).
+ *
+ * N_b = ceil(seq_lens[b] / m) entries.  For entry j the decoded key k_j
+ * (dim = idx_keys.dim) is scored by
+ *     s_j = sum_h head_w[b][h] * max(0, q_idx[b][h] . k_j),   h < HI
+ * (fp32 accumulation of exact bf16 products).  The k largest scores are kept
+ * (ties: lower index first) and written in ascending index order to
+ * out_idx[b][0 .. n-1], n = min(k, N_b); the rest of the row is -1 and
+ * out_n[b] = n.
+ *
+ *   q_idx      bf16 [B][HI][idx_keys.dim];  head_w float [B][HI]
+ *   HI         1 .. 16;  idx_keys.dim in {32, 64, 128, 256};  epp = 256/m
+ *   seq_lens   int32 [B] (device), clamped to [0, max_seq_len]
+ *   k          1 .. 8192
+ *   ws         workspace of indexer_topk_workspace(...) bytes.  It must be
+ *              zero-filled before its first use; every successful call leaves
+ *              it zero-filled again (re-zero it after a failed call).
+ *              Calls that overlap in time must use different workspaces.
+ */
+size_t indexer_topk_workspace(int32_t B, int32_t max_seq_len, int32_t m, int32_t k);
+hca_status indexer_topk(const uint16_t* q_idx, const float* head_w, int32_t HI,
+                        hca_paged_cache idx_keys, const int32_t* block_table, int32_t bt_stride,
+                        const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t m,
+                        int32_t k, int32_t* out_idx, int32_t* out_n, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * paged_hybrid_decode -- attention of the decode query over the selected
+ * compressed entries plus the raw window (V4 page, section 2.1: shared K=V,
+ * RoPE on the key use, inverse RoPE on the output; c128a attends to all of its
+ * entries; section 2.3: every layer keeps a raw window, usually 128 tokens;
+ * vLLM-0.7.2 page, section 2.3: only window blocks are read).
+ *
+ * For sequence b with L = seq_lens[b], the rows are
+ *   - the entries sel_idx[b][0 .. sel_n[b]-1] (indices outside [0, ceil(L/m))
+ *     are skipped), or all ceil(L/m) entries when sel_idx is NULL, read from
+ *     `kv` through block_table; then
+ *   - the window tokens t in [max(0, L - window), L), read from `win` through
+ *     win_block_table.
+ * Stored rows are already rotated.  With q~_h = RoPE(q[b][h], L-1):
+ *     p = softmax(softmax_scale * q~_h . rows),  o = sum p * rows
+ *     out[b][h] = RoPE^-1(o, L-1),  lse[b][h] = log sum exp(logits)
+ * A sequence with no rows gets out = 0 and lse = -inf.
+ *
+ *   q          bf16 [B][H][kv.dim], unrotated;  H in 1 .. 128
+ *   kv.dim     in {64, 128, 256, 512}; win.dim == kv.dim; win.epp == 256
+ *   kv, win    dtype HCA_FP8_E4M3 or HCA_BF16
+ *   sel_idx    int32 [B][k] or NULL;  sel_n int32 [B] (required with sel_idx)
+ *   window     0 .. 256 (0: no window; win and win_block_table may be NULL)
+ *   out        float [B][H][kv.dim];  lse float [B][H] or NULL
+ *   ws         workspace of paged_hybrid_decode_workspace(...) bytes; its
+ *              contents on entry do not matter.
+ */
+size_t paged_hybrid_decode_workspace(int32_t B, int32_t H, int32_t d, int32_t max_seq_len,
+                                     int32_t m, int32_t window, int32_t k);
+hca_status paged_hybrid_decode(const uint16_t* q, int32_t H, hca_paged_cache kv,
+                               const int32_t* block_table, int32_t bt_stride, hca_paged_cache win,
+                               const int32_t* win_block_table, int32_t wbt_stride,
+                               const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t m,
+                               int32_t window, const int32_t* sel_idx, const int32_t* sel_n,
+                               int32_t k, float softmax_scale, float rope_theta, float* out,
+                               float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kv_gather -- paged -> contiguous copy of rows 0 .. n_rows[b]-1 of every
+ * sequence (vLLM-0.7.2 page, section 2.1: logical blocks map to physical
+ * pages).  A layout check: the bytes must not depend on where pages live.
+ *
+ *   dst_codes  row r of sequence b at dst_codes + (b * max_rows + r) * row_bytes,
+ *              row_bytes = dim (fp8), dim/2 (fp4), 2*dim (bf16)
+ *   dst_scales fp8: float [B][max_rows] (the row's page scale);
+ *              fp4: uint8 [B][max_rows][dim/32]; bf16: unused (may be NULL)
+ *   n_rows     int32 [B] (device), clamped to [0, max_rows]; rows past n_rows[b]
+ *              are left untouched
+ */
+hca_status kv_gather(hca_paged_cache src, const int32_t* block_table, int32_t bt_stride,
+                     const int32_t* n_rows, int32_t B, int32_t max_rows, void* dst_codes,
+                     void* dst_scales, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HCA_H */

@@ -1,0 +1,43 @@
+/*
+ * hca_testing.h -- checking hooks of libhca (not part of the decode path).
+ *
+ * The host hooks run the very encoder functions the kernels use, compiled for
+ * the host, so their rounding can be checked exhaustively on a machine without
+ * a GPU.  The GPU probes run one hardware conversion or one MFMA on known data
+ * so that the lane layouts the kernels rely on can be checked in isolation.
+ * All return HCA_OK or HCA_ERR_INVALID (NULL pointer / bad size / bad kind).
+ */
+#ifndef HCA_TESTING_H
+#define HCA_TESTING_H
+
+#include "hca.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* host: in[n] fp32 -> E4M3 codes (RNE, saturating, sign kept) */
+hca_status hca_host_e4m3_encode(const float* in, uint8_t* out, int64_t n);
+/* host: in[n] fp32 -> E2M1 codes (low 4 bits of each byte) */
+hca_status hca_host_e2m1_encode(const float* in, uint8_t* out, int64_t n);
+/* host: in[n] fp32 -> bfloat16 bit patterns (RNE) */
+hca_status hca_host_bf16_encode(const float* in, uint16_t* out, int64_t n);
+
+/* GPU: decode n codes with the conversions the kernels use.
+ *   kind 0: E4M3 bytes codes[n] -> out[n] (hardware fp8 -> fp32)
+ *   kind 1: E2M1 packed bytes codes[n/2] -> out[n] (hardware fp4 -> bf16)
+ * codes, out: device; n a multiple of 8. */
+hca_status hca_probe_decode(const uint8_t* codes, float* out, int32_t n, int32_t kind, void* stream);
+
+/* GPU: one wave computes D[16][16] = A[16][32] . B[32][16] with one
+ * v_mfma_f32_16x16x32 (kind 0: f16 operands, kind 1: bf16 operands), loading
+ * lane l's operands as A[l%16][8(l/16) .. +8] and B[8(l/16) .. +8][l%16] and
+ * storing its accumulator as D[4(l/16)+i][l%16].  A, B: 16-bit patterns,
+ * row-major; D: fp32 row-major; all device. */
+hca_status hca_probe_mfma(const uint16_t* A, const uint16_t* B, float* D, int32_t kind, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HCA_TESTING_H */

@@ -1,0 +1,171 @@
+"""CPU checks of libhca: it loads, exports every declared symbol, validates
+arguments on the host, and its encoders (the kernels' own source, compiled for
+the host) round exactly like the oracle's codecs."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_attention_compressed_amd as hca
+from oracle import codecs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(hca.LIB_PATH), reason="libhca.so not built")
+
+
+def _declared(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)) - {"defined"}
+
+
+def test_every_declared_symbol_is_exported():
+    L = hca.lib()
+    names = _declared("hca.h") | _declared("hca_testing.h")
+    assert {"kv_compress", "kv_quantize_page", "indexer_topk", "paged_hybrid_decode", "kv_gather"} <= names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(hca.EXPORTS)
+    assert hca.version().startswith("hca ")
+    for s in range(5):
+        assert L.hca_status_string(s)
+
+
+def _host_encode(fn, x, out_dtype):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros(x.shape, dtype=out_dtype)
+    rc = fn(x.ctypes.data_as(ctypes.c_void_p), out.ctypes.data_as(ctypes.c_void_p), x.size)
+    assert rc == 0
+    return out
+
+
+def _probe_values(table, n_random, rng):
+    pos = table[np.isfinite(table) & (table >= 0)]
+    pos = np.unique(pos)
+    mids = (pos[:-1] + pos[1:]) / 2
+    v = np.concatenate([pos, mids]).astype(np.float32)
+    near = np.concatenate([np.nextafter(v, np.float32(np.inf)), np.nextafter(v, np.float32(-np.inf))])
+    extra = np.array([0.0, 1e-30, 1e30, 448.0, 464.0, 480.0, 6.0, 6.5, 7.0, 2.0 ** -10, 2.0 ** -9], np.float32)
+    rnd = np.concatenate([rng.normal(0, 1, n_random), rng.normal(0, 100, n_random // 4),
+                          np.ldexp(rng.uniform(0, 1, n_random // 4), -8)]).astype(np.float32)
+    x = np.concatenate([v, near, extra, rnd])
+    return np.concatenate([x, -x])
+
+
+def test_host_e4m3_encoder_matches_oracle():
+    rng = np.random.default_rng(21)
+    x = _probe_values(codecs.E4M3_TABLE, 2_000_000, rng)
+    # every binary32 pattern with the 12 low mantissa bits clear, over the whole finite range
+    sweep = (np.arange(0, 0x7F800000 >> 12, dtype=np.uint32) << 12).view(np.float32)
+    x = np.concatenate([x, sweep, -sweep])
+    got = _host_encode(hca.lib().hca_host_e4m3_encode, x, np.uint8)
+    assert np.array_equal(got, codecs.e4m3_encode(x))
+
+
+def test_host_e2m1_encoder_matches_oracle():
+    rng = np.random.default_rng(22)
+    x = _probe_values(codecs.E2M1_TABLE, 1_000_000, rng)
+    sweep = (np.arange(0, 0x7F800000 >> 12, dtype=np.uint32) << 12).view(np.float32)
+    x = np.concatenate([x, sweep, -sweep])
+    got = _host_encode(hca.lib().hca_host_e2m1_encode, x, np.uint8)
+    assert np.array_equal(got, codecs.e2m1_encode(x))
+
+
+def test_host_bf16_encoder_matches_oracle():
+    rng = np.random.default_rng(23)
+    x = np.concatenate([rng.normal(0, 10, 1_000_000), rng.normal(0, 1e-3, 100_000)]).astype(np.float32)
+    u = ((rng.integers(0, 2, 50000) << 31) | (rng.integers(1, 250, 50000) << 23) |
+         (rng.integers(0, 128, 50000) << 16) | 0x8000).astype(np.uint32)
+    x = np.concatenate([x, u.view(np.float32)])
+    got = _host_encode(hca.lib().hca_host_bf16_encode, x, np.uint16)
+    assert np.array_equal(got, codecs.bf16_encode(x))
+
+
+# ----------------------------------------------------------------- host validation
+FAKE = ctypes.c_void_p(0x1000)  # any non-null, 256-byte aligned address: nothing is launched on failure
+
+
+def _cache(dtype=1, epp=64, dim=128, pages=4, codes=FAKE, scales=FAKE):
+    return hca.CPagedCache(codes.value if codes else 0, scales.value if scales else 0, pages, epp, dim, dtype)
+
+
+def test_validation_kv_compress():
+    L = hca.lib()
+    ok = dict(x=FAKE, xs=4096 * 8, z=FAKE, zs=4096, beta=FAKE, pos0=FAKE, ntok=FAKE, B=2, mx=4096, d=128, m=4,
+              theta=1e6, out=FAKE, os=1024 * 128)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.kv_compress(a["x"], a["xs"], a["z"], a["zs"], a["beta"], a["pos0"], a["ntok"], a["B"], a["mx"],
+                             a["d"], a["m"], a["theta"], a["out"], a["os"], None)
+
+    assert call(m=3) == 1 and call(m=512) == 1 and call(m=0) == 1
+    assert call(d=12) == 1 and call(d=4096) == 2
+    assert call(theta=0.0) == 1 and call(theta=float("nan")) == 1
+    assert call(x=None) == 1 and call(out=None) == 1 and call(ntok=None) == 1
+    assert call(xs=100) == 1 and call(os=16) == 1
+    assert call(B=-1) == 1
+    assert call(B=0) == 0 and call(mx=0) == 0  # nothing to do, nothing launched
+
+
+def test_validation_quantize_and_gather():
+    L = hca.lib()
+    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(dtype=7), None) == 1
+    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(epp=3), None) == 1
+    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(dtype=2, dim=48), None) == 1
+    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(scales=None), None) == 1
+    assert L.kv_quantize_page(None, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(), None) == 1
+    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 0, _cache(), None) == 1
+    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 0, 64, FAKE, 16, _cache(), None) == 0
+    assert L.kv_gather(_cache(), FAKE, 1, FAKE, 2, 65, FAKE, FAKE, None) == 1  # table too narrow for 65 rows
+    assert L.kv_gather(_cache(), FAKE, 2, FAKE, 2, 65, FAKE, None, None) == 1  # fp8 needs scales out
+    assert L.kv_gather(_cache(), FAKE, 2, FAKE, 0, 65, FAKE, FAKE, None) == 0
+
+
+def test_validation_indexer_and_attention():
+    L = hca.lib()
+    ws_need = L.indexer_topk_workspace(2, 4096, 4, 256)
+    assert ws_need > 0 and L.indexer_topk_workspace(2, 4096, 3, 256) == 0
+
+    def idx(**kw):
+        a = dict(q=FAKE, w=FAKE, HI=16, keys=_cache(dtype=1, epp=64, dim=128), bt=FAKE, bts=16, lens=FAKE, B=2,
+                 L=4096, m=4, k=256, out=FAKE, n=FAKE, ws=FAKE, wsb=ws_need)
+        a.update(kw)
+        return L.indexer_topk(a["q"], a["w"], a["HI"], a["keys"], a["bt"], a["bts"], a["lens"], a["B"], a["L"],
+                              a["m"], a["k"], a["out"], a["n"], a["ws"], a["wsb"], None)
+
+    assert idx(HI=17) == 2 and idx(HI=0) == 1
+    assert idx(k=0) == 1 and idx(k=9000) == 2
+    assert idx(keys=_cache(dtype=1, epp=2, dim=128)) == 1  # epp must be 256/m
+    assert idx(keys=_cache(dtype=1, epp=64, dim=96)) == 2
+    assert idx(bts=15) == 1  # 15*256 < 4096
+    assert idx(wsb=ws_need - 1) == 3 and idx(ws=None) == 3
+    assert idx(out=None) == 1
+    assert idx(B=0) == 0
+
+    ws_att = L.paged_hybrid_decode_workspace(2, 64, 512, 4096, 4, 128, 256)
+    assert ws_att > 0
+
+    def att(**kw):
+        a = dict(q=FAKE, H=64, kv=_cache(dtype=1, epp=64, dim=512), bt=FAKE, bts=16,
+                 win=_cache(dtype=1, epp=256, dim=512), wbt=FAKE, wbts=16, lens=FAKE, B=2, L=4096, m=4, W=128,
+                 sel=FAKE, seln=FAKE, k=256, scale=0.04, theta=1e6, out=FAKE, lse=None, ws=FAKE, wsb=ws_att)
+        a.update(kw)
+        return L.paged_hybrid_decode(a["q"], a["H"], a["kv"], a["bt"], a["bts"], a["win"], a["wbt"], a["wbts"],
+                                     a["lens"], a["B"], a["L"], a["m"], a["W"], a["sel"], a["seln"], a["k"],
+                                     a["scale"], a["theta"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+    assert att(H=129) == 2 and att(H=0) == 1
+    assert att(kv=_cache(dtype=1, epp=64, dim=384)) == 2
+    assert att(kv=_cache(dtype=2, epp=64, dim=512)) == 2
+    assert att(W=300) == 1 and att(win=_cache(dtype=1, epp=64, dim=512)) == 1
+    assert att(win=_cache(dtype=1, epp=256, dim=256)) == 1
+    assert att(seln=None) == 1 and att(k=0) == 1
+    assert att(scale=float("inf")) == 1
+    assert att(wsb=ws_att - 1) == 3
+    assert att(m=5) == 1
+    assert att(B=0) == 0

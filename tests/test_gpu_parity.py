@@ -1,0 +1,334 @@
+"""GPU parity of every entry point against the CPU oracle (needs an MI355X).
+
+Stage-isolated: each kernel gets inputs the oracle built (pages, selections)
+and is compared with the oracle's result for them.  Sizes span several tiles
+and blocks with ragged tails; the full workload sizes are covered in
+test_gpu_workloads.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import codecs, compressor, paging
+from synth import gen
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+hca = pytest.importorskip("decode_attention_compressed_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hca.lib()
+
+
+# ----------------------------------------------------------------- hardware layout probes
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_probe_mfma_16x16x32_layout(kind):
+    H.flush(f"probe mfma kind={kind}")
+    rng = np.random.default_rng(31)
+    A = rng.integers(-4, 5, (16, 32)).astype(np.float32)
+    B = rng.integers(-4, 5, (32, 16)).astype(np.float32)
+    if kind == 0:
+        a16 = torch.from_numpy(A).half().view(torch.int16)
+        b16 = torch.from_numpy(B).half().view(torch.int16)
+    else:
+        a16 = torch.from_numpy(A).bfloat16().view(torch.int16)
+        b16 = torch.from_numpy(B).bfloat16().view(torch.int16)
+    D = torch.zeros((16, 16), dtype=torch.float32, device="cuda")
+    a_d, b_d = a16.cuda(), b16.cuda()
+    assert hca.lib().hca_probe_mfma(a_d.data_ptr(), b_d.data_ptr(), D.data_ptr(), kind, None) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(D.cpu().numpy(), A @ B)
+
+
+def test_probe_hw_decoders_are_exact():
+    H.flush("probe decode fp8/fp4")
+    codes = np.arange(256, dtype=np.uint8)
+    out = torch.zeros(256, dtype=torch.float32, device="cuda")
+    assert hca.lib().hca_probe_decode(H.to_dev(codes).data_ptr(), out.data_ptr(), 256, 0, None) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    finite = np.isfinite(codecs.E4M3_TABLE)
+    assert np.array_equal(got[finite], codecs.E4M3_TABLE[finite])
+    out4 = torch.zeros(512, dtype=torch.float32, device="cuda")
+    assert hca.lib().hca_probe_decode(H.to_dev(codes).data_ptr(), out4.data_ptr(), 512, 1, None) == 0
+    torch.cuda.synchronize()
+    got4 = out4.cpu().numpy().astype(np.float64)
+    want = np.empty(512)
+    want[0::2] = codecs.E2M1_TABLE[codes & 0xF]
+    want[1::2] = codecs.E2M1_TABLE[codes >> 4]
+    assert np.array_equal(got4, want)
+
+
+# ----------------------------------------------------------------- kv_quantize_page
+
+
+@pytest.mark.parametrize("dtype,epp,dim", [("fp8", 64, 512), ("fp8", 2, 512), ("fp8", 256, 128), ("fp4", 64, 128),
+                                           ("bf16", 64, 128), ("fp4", 64, 64), ("fp8", 64, 136)])
+def test_quantize_pages_bit_exact(dtype, epp, dim):
+    H.flush(f"quantize {dtype} epp={epp} dim={dim}")
+    rng = np.random.default_rng(41)
+    lens = np.array([epp * 5 + 7, epp * 3, 1, epp * 2 - 1])
+    B = len(lens)
+    max_ne = int(lens.max())
+    nb = -(-max_ne // epp)
+    perm = rng.permutation(B * nb + 3)
+    table = perm[: B * nb].reshape(B, nb).astype(np.int32)
+    src = (rng.standard_normal((B, max_ne, dim)) * rng.uniform(0.01, 3, (B, 1, 1))).astype(np.float32)
+    src[1, : epp] = 0.0  # an all-zero page: fp8 scale 1, fp4 scale codes 0
+    src[2, 0, :5] = [448 * 3, -1e-9, 0.0, -0.0, 2.0 ** -12]
+    ref = paging.Pool(dtype, B * nb + 3, epp, dim)
+    for b in range(B):
+        paging.write_run(ref, table[b], 0, src[b, : lens[b]])
+    dst = hca.PagedCache.empty(B * nb + 3, epp, dim, dtype)
+    hca.kv_quantize_page(H.to_dev(src), H.to_dev(np.zeros(B, np.int32)), H.to_dev(lens.astype(np.int32)), max_ne,
+                         H.to_dev(table), dst)
+    torch.cuda.synchronize()
+    got = H.download_pool(dst, ref)
+    for b in range(B):
+        for p in range(-(-lens[b] // epp)):
+            phys = table[b, p]
+            nv = min(epp, lens[b] - p * epp)
+            assert np.array_equal(got.codes[phys, :nv], ref.codes[phys, :nv]), (b, p)
+            if dtype == "fp8":
+                assert got.scales[phys] == ref.scales[phys], (b, p)
+            elif dtype == "fp4":
+                assert np.array_equal(got.scales[phys, :nv], ref.scales[phys, :nv]), (b, p)
+
+
+def test_quantize_open_page_run():
+    # a run that starts at a later page (the decode update's open page), e0 > 0
+    H.flush("quantize open page")
+    rng = np.random.default_rng(42)
+    epp, dim = 64, 512
+    table = np.array([[5, 2, 7, 0], [1, 3, 4, 6]], np.int32)
+    rows = rng.standard_normal((2, 40, dim)).astype(np.float32)
+    e0 = np.array([128, 64], np.int32)
+    ne = np.array([40, 17], np.int32)
+    ref = paging.Pool("fp8", 8, epp, dim)
+    for b in range(2):
+        paging.write_run(ref, table[b], int(e0[b]), rows[b, : ne[b]])
+    dst = hca.PagedCache.empty(8, epp, dim, "fp8")
+    hca.kv_quantize_page(H.to_dev(rows), H.to_dev(e0), H.to_dev(ne), 40, H.to_dev(table), dst)
+    got = H.download_pool(dst, ref)
+    assert np.array_equal(got.codes[7, :40], ref.codes[7, :40]) and got.scales[7] == ref.scales[7]
+    assert np.array_equal(got.codes[3, :17], ref.codes[3, :17]) and got.scales[3] == ref.scales[3]
+
+
+# ----------------------------------------------------------------- kv_compress
+
+
+@pytest.mark.parametrize("m,d", [(4, 512), (128, 512), (4, 128), (1, 512), (16, 64), (256, 128)])
+def test_compress_entries(m, d):
+    H.flush(f"compress m={m} d={d}")
+    rng = np.random.default_rng(51)
+    T = [m * 37 + (m // 2 + 1 if m > 1 else 0), 3, m * 9, 1]
+    B = len(T)
+    Tm = max(T)
+    x32 = rng.standard_normal((B, Tm, d)).astype(np.float32)
+    xb = gen.to_bf16_bits(x32)
+    z = rng.standard_normal((B, Tm)).astype(np.float32)
+    beta = (rng.standard_normal(m) * 0.1).astype(np.float32)
+    pos0 = np.array([0, m * 1000, m * 262143, m * 5], np.int32)
+    ntok = np.array(T, np.int32)
+    n_out = -(-Tm // m)
+    out = torch.zeros((B, n_out, d), dtype=torch.float32, device="cuda")
+    hca.kv_compress(H.to_dev(xb.view(np.int16)), H.to_dev(z), H.to_dev(beta), H.to_dev(pos0), H.to_dev(ntok), m, 1e6,
+                    out, Tm)
+    got = out.cpu().numpy()
+    for b in range(B):
+        ref = compressor.compress(codecs.bf16_decode(xb[b, : T[b]]), z[b, : T[b]], beta, m, 1e6, pos0=int(pos0[b]))
+        assert H.rel_err_rows(got[b, : ref.shape[0]], ref) <= H.ENTRY_TOL, b
+
+
+# ----------------------------------------------------------------- indexer_topk
+
+
+def _idx_workload(dtype, d_idx, k, B=3):
+    kind = synth.LayerKind("c4a", 4, k, dtype, d_idx, 16)
+    return synth.Workload(100, f"idx-{dtype}", B, None, 128, 8, 128, "fp8", [kind])
+
+
+@pytest.mark.parametrize("dtype,d_idx,k,lens", [
+    ("fp8", 128, 256, [40000, 4097, 1025]),
+    ("fp4", 128, 2048, [70001, 8193, 9000]),
+    ("bf16", 64, 256, [4096, 1023, 2000]),
+    ("fp8", 64, 300, [1200, 1201, 1199]),  # N = 300 ~ k: k-1, k, k+1 entries
+    ("fp4", 32, 17, [100000, 640, 65]),
+])
+def test_indexer_topk_sets(dtype, d_idx, k, lens):
+    H.flush(f"indexer {dtype} dI={d_idx} k={k} lens={lens}")
+    w = _idx_workload(dtype, d_idx, k, len(lens))
+    sd = H.SeqData(w, 0, lens, build_pools=False)
+    sd.idx = paging.Pool(dtype, sd.num_pages, 64, d_idx)
+    for b in range(sd.B):
+        paging.write_run(sd.idx, sd.table[b], 0, sd.keys[b])
+    margins = sd.enforce_margin()
+    assert min(margins) >= H.MARGIN
+    Lmax = H.max_len(lens)
+    ws = hca.workspace(hca.indexer_topk_workspace(sd.B, Lmax, 4, k))
+    out_idx = torch.full((sd.B, k), -7, dtype=torch.int32, device="cuda")
+    out_n = torch.zeros(sd.B, dtype=torch.int32, device="cuda")
+    keys = H.upload_pool(sd.idx)
+    for rep in range(2):  # the second call checks the workspace was left clean
+        hca.indexer_topk(H.to_dev(sd.qi.view(np.int16)), H.to_dev(sd.wi), keys, H.to_dev(sd.table), H.to_dev(sd.lens),
+                         Lmax, 4, k, out_idx, out_n, ws)
+        torch.cuda.synchronize()
+        got, n = out_idx.cpu().numpy(), out_n.cpu().numpy()
+        for b in range(sd.B):
+            want = sd.oracle_select(b)
+            assert n[b] == len(want), (rep, b)
+            assert np.array_equal(got[b, : n[b]], want), (rep, b)
+            assert (got[b, n[b]:] == -1).all()
+    assert int(ws.sum().item()) == 0  # left zeroed
+
+
+# ----------------------------------------------------------------- paged_hybrid_decode
+
+
+def _attn_workload(kv_dtype, d, Hh, window, kind, B=3):
+    return synth.Workload(101, "attn", B, None, d, Hh, window, kv_dtype, [kind])
+
+
+def _run_attn(sd, sel_list, window, ws=None, table=None, wtable=None, kv=None, win=None):
+    B, d, Hh = sd.B, sd.w.d, sd.w.H
+    Lmax = H.max_len(sd.lens)
+    m = sd.kind.m
+    if sel_list is not None:
+        k = max(1, max(len(s) for s in sel_list))
+        sel = np.full((B, k), -1, np.int32)
+        for b, s in enumerate(sel_list):
+            sel[b, : len(s)] = s
+        sel_n = np.array([len(s) for s in sel_list], np.int32)
+        sel_d, seln_d = H.to_dev(sel), H.to_dev(sel_n)
+    else:
+        k, sel_d, seln_d = 0, None, None
+    if ws is None:
+        ws = hca.workspace(hca.paged_hybrid_decode_workspace(B, Hh, d, Lmax, m, window, k))
+    out = torch.zeros((B, Hh, d), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((B, Hh), dtype=torch.float32, device="cuda")
+    hca.paged_hybrid_decode(H.to_dev(sd.q.view(np.int16)), kv or H.upload_pool(sd.kv),
+                            H.to_dev(sd.table if table is None else table), win or H.upload_pool(sd.win),
+                            H.to_dev(sd.wtable if wtable is None else wtable), H.to_dev(sd.lens), Lmax, m, window,
+                            sel_d, seln_d, H.scale_for(d), sd.w.theta, out, lse, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", [
+    dict(kv="fp8", d=512, H=64, W=128, m=4, topk=256, lens=[9000, 300, 2500]),
+    dict(kv="fp8", d=512, H=64, W=128, m=128, topk=None, lens=[65536, 1000, 20000]),
+    dict(kv="bf16", d=128, H=8, W=128, m=4, topk=256, lens=[4096, 129, 1000]),
+    dict(kv="fp8", d=256, H=96, W=0, m=4, topk=64, lens=[3000, 50, 700]),
+    dict(kv="fp8", d=64, H=20, W=256, m=128, topk=None, lens=[700, 1, 257]),
+    dict(kv="fp8", d=512, H=128, W=128, m=1, topk=None, lens=[100, 33, 1]),
+])
+def test_paged_hybrid_decode(case):
+    H.flush(f"attention {case}")
+    kind = synth.LayerKind("c4a" if case["topk"] else "c128a", case["m"], case["topk"], "fp8" if case["topk"] else None,
+                           128 if case["topk"] else 0)
+    w = _attn_workload(case["kv"], case["d"], case["H"], case["W"], kind, len(case["lens"]))
+    sd = H.SeqData(w, 0, case["lens"])
+    if case["topk"]:
+        # a valid selection per sequence: the oracle's own top-k
+        sel = [sd.oracle_select(b) for b in range(sd.B)]
+    else:
+        sel = None
+    out, lse = _run_attn(sd, sel, case["W"])
+    for b in range(sd.B):
+        s = sel[b] if sel is not None else np.arange(int(compressor.n_entries(int(sd.lens[b]), case["m"])))
+        ref_out, ref_lse, p = sd.oracle_attend(b, s)
+        assert np.allclose(p.sum(axis=1), 1.0)
+        err = H.rel_err_rows(out[b], ref_out)
+        assert err <= H.ATTN_TOL, (b, err)
+        assert np.allclose(lse[b], ref_lse, rtol=0, atol=2e-3), b
+
+
+def test_attention_layout_invariance_bitwise():
+    # the same logical content through relocated pages, and through a table whose
+    # shared-prefix blocks alias one set of pages: outputs must be bit-identical
+    H.flush("attention layout invariance")
+    kind = synth.LayerKind("c4a", 4, 512, "fp8", 128)
+    w = synth.Workload(102, "alias", 2, None, 512, 64, 128, "fp8", [kind], shared_prefix_seqs=2,
+                       shared_prefix_blocks=8)
+    sd = H.SeqData(w, 0, [6000, 4100])
+    assert len(sd.members) == 2 and (sd.table[0, :8] == sd.table[1, :8]).all()
+    sel = [sd.oracle_select(b) for b in range(sd.B)]
+    base_out, base_lse = _run_attn(sd, sel, 128)
+    for b in range(sd.B):
+        ref_out, _, _ = sd.oracle_attend(b, sel[b])
+        assert H.rel_err_rows(base_out[b], ref_out) <= H.ATTN_TOL
+    rng = np.random.default_rng(61)
+    for trial in range(3):
+        # relocate every page of both pools (trial 2 also un-aliases: sequence 1 gets its own copies)
+        extra = 8 if trial == 2 else 0
+        P = sd.num_pages + 5 + extra
+        perm = rng.permutation(P)
+        kv2 = paging.Pool("fp8", P, sd.kv.epp, sd.kv.d)
+        kv2.codes[perm[: sd.num_pages]] = sd.kv.codes
+        kv2.scales[perm[: sd.num_pages]] = sd.kv.scales
+        t2 = np.where(sd.table >= 0, perm[np.maximum(sd.table, 0)], -1).astype(np.int32)
+        if trial == 2:
+            for i in range(8):
+                fresh = perm[sd.num_pages + 5 + i]
+                kv2.codes[fresh] = kv2.codes[t2[1, i]]
+                kv2.scales[fresh] = kv2.scales[t2[1, i]]
+                t2[1, i] = fresh
+        wperm = rng.permutation(sd.num_wpages + 2)
+        win2 = paging.Pool("fp8", sd.num_wpages + 2, 256, sd.win.d)
+        win2.codes[wperm[: sd.num_wpages]] = sd.win.codes[: sd.num_wpages]
+        win2.scales[wperm[: sd.num_wpages]] = sd.win.scales[: sd.num_wpages]
+        wt2 = np.where(sd.wtable >= 0, wperm[np.maximum(sd.wtable, 0)], -1).astype(np.int32)
+        out, lse = _run_attn(sd, sel, 128, table=t2, wtable=wt2, kv=H.upload_pool(kv2), win=H.upload_pool(win2))
+        assert np.array_equal(out, base_out) and np.array_equal(lse, base_lse), trial
+
+
+def test_attention_skips_invalid_indices_and_empty_sequences():
+    H.flush("attention invalid / empty")
+    kind = synth.LayerKind("c4a", 4, 64, "fp8", 128)
+    w = _attn_workload("fp8", 128, 16, 0, kind, 2)
+    sd = H.SeqData(w, 0, [1000, 1])
+    good = np.arange(0, 250, 5)
+    sel = [np.concatenate([good, [-3, 250, 10 ** 6]]), np.zeros(0, np.int64)]
+    out, lse = _run_attn(sd, sel, 0)
+    ref_out, ref_lse, _ = sd.oracle_attend(0, good)
+    assert H.rel_err_rows(out[0], ref_out) <= H.ATTN_TOL
+    assert not out[1].any() and np.all(np.isneginf(lse[1]))
+
+
+# ----------------------------------------------------------------- kv_gather
+
+
+@pytest.mark.parametrize("dtype,epp,dim", [("fp8", 64, 512), ("fp4", 64, 128), ("bf16", 2, 128)])
+def test_gather_bit_exact(dtype, epp, dim):
+    H.flush(f"gather {dtype}")
+    rng = np.random.default_rng(71)
+    B, n = 3, epp * 4 + 3
+    nb = -(-n // epp)
+    table = rng.permutation(B * nb).reshape(B, nb).astype(np.int32)
+    pool = paging.Pool(dtype, B * nb, epp, dim)
+    rows = rng.standard_normal((B, n, dim)).astype(np.float32)
+    for b in range(B):
+        paging.write_run(pool, table[b], 0, rows[b])
+    pc = H.upload_pool(pool)
+    nrows = np.array([n, n - 5, 1], np.int32)
+    rb = {"fp8": dim, "fp4": dim // 2, "bf16": 2 * dim}[dtype]
+    codes = torch.zeros((B, n, rb), dtype=torch.uint8, device="cuda")
+    scales = {"fp8": torch.zeros((B, n), dtype=torch.float32, device="cuda"),
+              "fp4": torch.zeros((B, n, dim // 32), dtype=torch.uint8, device="cuda"), "bf16": None}[dtype]
+    hca.kv_gather(pc, H.to_dev(table), H.to_dev(nrows), n, codes, scales)
+    torch.cuda.synchronize()
+    gc = codes.cpu().numpy()
+    for b in range(B):
+        rc, rs = paging.gather_bytes(pool, table[b], int(nrows[b]))
+        assert np.array_equal(gc[b, : nrows[b]], rc.view(np.uint8).reshape(nrows[b], rb))
+        if dtype != "bf16":
+            assert np.array_equal(scales.cpu().numpy()[b, : nrows[b]], rs)
