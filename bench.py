@@ -1,0 +1,448 @@
+"""Decode-step benchmark of the hybrid compressed-KV decode path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
+
+Workload (default): the 1M-token long-context stack -- batch 4, context 2^20,
+61 layers (30 c4a: m=4, 262,144 entries, indexer top-2048 over fp4 E2M1 keys
+with per-32 E4M3 scales; 31 c128a: m=128, 8,192 entries, all attended), shared
+K=V dim 512 in fp8 E4M3 pages with a per-page fp32 scale, 64 query heads, a
+128-token raw window.  The caches are filled by a prefill pass on the GPU
+(kv_compress + kv_quantize_page over all 2^20 tokens of every layer), timed
+and reported on its own.
+
+A step is one decode step of the whole stack for the batch: per layer the
+decode update (re-fold of the open group and re-quantization of its page, the
+window insert of the new token, the open indexer page), then indexer_topk (c4a)
+and paged_hybrid_decode.  The step is captured once in a HIP graph and
+replayed; `value` is decode tokens/s = B / step time.
+
+Also reported: the roofline of the dominant kernel (the indexer scoring
+kernel: it streams the fp4 keys, ~77% of a step's bytes), measured with HIP
+events around each of its launches; and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=0, help="debug only: first N layers (result is not the workload)")
+    ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated per step (0: auto)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------- algorithmic bytes
+
+
+def layer_bytes(kind, B, L, d, H, W, d_idx=128, h_idx=16):
+    """Algorithmic HBM bytes of one decode step of one layer for the batch: each
+    stored row read once (codes + its share of scales), queries, outputs, block
+    table entries read; intermediate scores and indices are not counted."""
+    m = kind.m
+    N = -(-L // m)
+    epp = 256 // m
+    win = min(W, L)
+    q = H * d * 2
+    out = H * d * 4 + H * 4
+    win_rows = win * d + 4 * (-(-win // 256) + 1)
+    if kind.topk is not None:
+        kk = min(kind.topk, N)
+        idx_row = d_idx // 2 + d_idx // 32 if kind.idx_dtype == "fp4" else d_idx + 4.0 / epp
+        idx = N * idx_row + h_idx * d_idx * 2 + h_idx * 4 + 4 * (-(-N // epp))
+        rows = kk * (d + 4)  # each selected row and its page scale
+        per_seq = idx + rows + win_rows + q + out + 4 * kk
+    else:
+        rows = N * d + 4 * (-(-N // epp))
+        per_seq = rows + win_rows + q + out + 4 * (-(-N // epp))
+    return B * per_seq
+
+
+def score_bytes(kind, B, L, d_idx=128, h_idx=16):
+    m = kind.m
+    N = -(-L // m)
+    epp = 256 // m
+    idx_row = d_idx // 2 + d_idx // 32 if kind.idx_dtype == "fp4" else d_idx + 4.0 / epp
+    return B * (N * idx_row + h_idx * d_idx * 2 + h_idx * 4 + 4 * (-(-N // epp)))
+
+
+def update_bytes(kind, B, d, d_idx=128):
+    """Bytes moved by the decode update of one layer (open group, open page,
+    window page, open indexer page)."""
+    m, epp = kind.m, 256 // kind.m
+    b = m * d * 2 + m * 4 + d * 4  # ring tokens + logits, entry write
+    b += epp * d * 4 + epp * d + 4  # open page: staging read, codes + scale write
+    b += d * 2 + d * 4 + 256 * d * 4 + 256 * d + 4  # window token, its row, window page re-quantization
+    if kind.topk is not None:
+        b += epp * d_idx * 4 + epp * (d_idx // 2 + d_idx // 32)
+    return B * b
+
+
+# ----------------------------------------------------------------- GPU state
+
+
+class Layer:
+    pass
+
+
+def build_state(w, n_layers, torch, hca, gen, log):
+    """Fill every layer's pools with a GPU prefill pass; keep the decode-update
+    state.  Returns (layers, prefill stats)."""
+    B, L, d, H, W = w.B, w.L, w.d, w.H, w.window
+    lens_np = np.full((B,), L, np.int32)
+    table_np, P, wtable_np, PW = gen.block_tables(w, lens_np)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    table, wtable, lens = dev(table_np), dev(wtable_np), dev(lens_np)
+    zeros_b = dev(np.zeros(B, np.int32))
+    layers = []
+    pre_ms, pre_bytes = 0.0, 0.0
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for li in range(n_layers):
+        kind = w.layers[li]
+        m, epp = kind.m, 256 // kind.m
+        N = -(-L // m)
+        lay = Layer()
+        lay.kind, lay.N, lay.epp = kind, N, epp
+        # raw tokens and logits of the whole context (seeded device draws)
+        x = torch.empty((B, L, d), dtype=torch.bfloat16, device="cuda")
+        for b in range(B):
+            x[b] = gen.device_normal((L, d), 1.0, (0, w.cid, li, gen.S_TOK, b), dtype=torch.bfloat16)
+        z = gen.device_normal((B, L), 1.0, (0, w.cid, li, gen.S_LOGIT))
+        beta = dev(gen.slot_bias(w, li, m))
+        ent = torch.empty((B, N, d), dtype=torch.float32, device="cuda")
+        lay.kv = hca.PagedCache.empty(P, epp, d, w.kv_dtype)
+        xi = x.view(torch.int16)
+        torch.cuda.synchronize()
+        ev0.record()
+        hca.kv_compress(xi, z, beta, zeros_b, lens, m, w.theta, ent, L)
+        hca.kv_quantize_page(ent, zeros_b, dev(np.full(B, N, np.int32)), N, table, lay.kv)
+        ev1.record()
+        torch.cuda.synchronize()
+        pre_ms += ev0.elapsed_time(ev1)
+        pre_bytes += B * (L * d * 2 + L * 4 + 2 * N * d * 4 + N * d + 4 * (-(-N // epp)))
+        # decode-update state: open group ring, open page staging
+        g_open = (L - 1) // m
+        lay.ring_x = xi[:, g_open * m: L].contiguous()
+        lay.ring_z = z[:, g_open * m: L].contiguous()
+        lay.beta = beta
+        e_open0 = (g_open // epp) * epp
+        lay.stage = ent[:, e_open0: N].clone()
+        lay.slot = g_open - e_open0
+        lay.pos0 = dev(np.full(B, g_open * m, np.int32))
+        lay.ntok = dev(np.full(B, L - g_open * m, np.int32))
+        lay.e0 = dev(np.full(B, e_open0, np.int32))
+        lay.ne = dev(np.full(B, N - e_open0, np.int32))
+        del ent
+        # window pages: rows of the blocks that overlap [L-W, L)
+        t0 = (max(0, L - W) // 256) * 256
+        nw = L - t0
+        wrows = torch.empty((B, nw, d), dtype=torch.float32, device="cuda")
+        hca.kv_compress(xi[:, t0:], z[:, t0:], dev(np.zeros(1, np.float32)), dev(np.full(B, t0, np.int32)),
+                        dev(np.full(B, nw, np.int32)), 1, w.theta, wrows, nw)
+        lay.win = hca.PagedCache.empty(PW, 256, d, w.kv_dtype)
+        hca.kv_quantize_page(wrows, dev(np.full(B, t0, np.int32)), dev(np.full(B, nw, np.int32)), nw, wtable, lay.win)
+        tw0 = ((L - 1) // 256) * 256
+        lay.wstage = wrows[:, tw0 - t0:].clone()
+        lay.wslot = (L - 1) - tw0
+        lay.x_last = xi[:, L - 1: L].contiguous()
+        lay.z_last = z[:, L - 1: L].contiguous()
+        lay.wpos0 = dev(np.full(B, L - 1, np.int32))
+        lay.one = dev(np.full(B, 1, np.int32))
+        lay.we0 = dev(np.full(B, tw0, np.int32))
+        lay.wne = dev(np.full(B, L - tw0, np.int32))
+        lay.zero1 = dev(np.zeros(1, np.float32))
+        del x, z, wrows
+        # queries
+        lay.q = dev(gen.queries(w, li).view(np.int16))
+        if kind.topk is not None:
+            keys = gen.device_normal((B, N, kind.d_idx), 1.0, (0, w.cid, li, gen.S_IDXK))
+            lay.idx = hca.PagedCache.empty(P, epp, kind.d_idx, kind.idx_dtype)
+            hca.kv_quantize_page(keys, zeros_b, dev(np.full(B, N, np.int32)), N, table, lay.idx)
+            lay.istage = keys[:, e_open0: N].clone()
+            del keys
+            lay.qi = dev(gen.index_queries(w, li, kind.h_idx, kind.d_idx).view(np.int16))
+            lay.wi = dev(gen.index_weights(w, li, kind.h_idx))
+            lay.sel = torch.zeros((B, kind.topk), dtype=torch.int32, device="cuda")
+            lay.sel_n = torch.zeros((B,), dtype=torch.int32, device="cuda")
+        lay.out = torch.zeros((B, H, d), dtype=torch.float32, device="cuda")
+        lay.lse = torch.zeros((B, H), dtype=torch.float32, device="cuda")
+        layers.append(lay)
+        torch.cuda.synchronize()
+        if li % 10 == 0 or li == n_layers - 1:
+            log(f"prefilled layer {li + 1}/{n_layers} ({kind.name})")
+    shared = dict(table=table, wtable=wtable, lens=lens)
+    return layers, shared, dict(ms=pre_ms, bytes=pre_bytes)
+
+
+def decode_step(w, layers, shared, ws_idx, ws_att, hca, update=True, attend=True):
+    L, W = w.L, w.window
+    table, wtable, lens = shared["table"], shared["wtable"], shared["lens"]
+    scale = 1.0 / math.sqrt(w.d)
+    for lay in layers:
+        kind = lay.kind
+        m = kind.m
+        if update:
+            # open group re-fold -> its slot in the open page staging -> re-quantize the open page
+            hca.kv_compress(lay.ring_x, lay.ring_z, lay.beta, lay.pos0, lay.ntok, m, w.theta,
+                            lay.stage[:, lay.slot:], m)
+            hca.kv_quantize_page(lay.stage, lay.e0, lay.ne, lay.stage.shape[1], table, lay.kv)
+            # window insert of the newest token
+            hca.kv_compress(lay.x_last, lay.z_last, lay.zero1, lay.wpos0, lay.one, 1, w.theta,
+                            lay.wstage[:, lay.wslot:], 1)
+            hca.kv_quantize_page(lay.wstage, lay.we0, lay.wne, lay.wstage.shape[1], wtable, lay.win)
+            if kind.topk is not None:
+                hca.kv_quantize_page(lay.istage, lay.e0, lay.ne, lay.istage.shape[1], table, lay.idx)
+        if attend:
+            if kind.topk is not None:
+                hca.indexer_topk(lay.qi, lay.wi, lay.idx, table, lens, L, m, kind.topk, lay.sel, lay.sel_n, ws_idx)
+                hca.paged_hybrid_decode(lay.q, lay.kv, table, lay.win, wtable, lens, L, m, W, lay.sel, lay.sel_n,
+                                        scale, w.theta, lay.out, lay.lse, ws_att[kind.name])
+            else:
+                hca.paged_hybrid_decode(lay.q, lay.kv, table, lay.win, wtable, lens, L, m, W, None, None, scale,
+                                        w.theta, lay.out, lay.lse, ws_att[kind.name])
+
+
+def time_graph(torch, fn, steps, warmup):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # eager warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall, g
+
+
+def time_dominant(torch, hca, w, layers, shared, reps=4):
+    """Average duration of the indexer scoring kernel: events bracket every
+    launch; a GPU sleep first lets all launches queue back to back."""
+    c4a = [l for l in layers if l.kind.topk is not None]
+    if not c4a:
+        return None
+    kind = c4a[0].kind
+    ws = hca.workspace(hca.indexer_topk_workspace(w.B, w.L, kind.m, kind.topk))
+    n = len(c4a) * reps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)
+    i = 0
+    for _ in range(reps):
+        for lay in c4a:
+            evs[i].record()
+            hca.indexer_score(lay.qi, lay.wi, lay.idx, shared["table"], shared["lens"], w.L, kind.m, kind.topk, ws)
+            evs[i + 1].record()
+            i += 2
+    torch.cuda.synchronize()
+    durs = [evs[j].elapsed_time(evs[j + 1]) for j in range(0, 2 * n, 2)]
+    return float(np.mean(durs)), float(np.median(durs)), n
+
+
+# ----------------------------------------------------------------- CPU baseline
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The oracle's decode step (indexer scores + top-k + gather/decode + attention)
+    for ONE sequence of one c4a and one c128a layer, on page contents of the
+    workload's shape (random codes: the oracle's time does not depend on the
+    values); repeated while within budget; scaled to the 61-layer stack."""
+    from oracle import attention, indexer, paging
+    from oracle.rope import rope  # noqa: F401  (the attention path uses it)
+
+    rng = np.random.default_rng(0)
+    L, d, H, W = w.L, w.d, w.H, w.window
+    out = {}
+    kinds = {}
+    for k in w.layers:
+        kinds.setdefault(k.name, k)
+    t_layer = {}
+    reps = {}
+    t_start = time.perf_counter()
+    for name, kind in kinds.items():
+        m, epp = kind.m, 256 // kind.m
+        N = -(-L // m)
+        P = -(-L // 256)
+        table = rng.permutation(P)
+        kv = paging.Pool("fp8", P, epp, d)
+        kv.codes[:] = rng.integers(0, 0x7E, kv.codes.shape, dtype=np.uint8)
+        kv.scales[:] = rng.uniform(1e-3, 1e-2, P).astype(np.float32)
+        win = paging.Pool("fp8", 1, 256, d)
+        win.codes[:] = rng.integers(0, 0x7E, win.codes.shape, dtype=np.uint8)
+        wtable = np.full(P, -1)
+        wtable[(L - 1) // 256] = 0
+        q = rng.standard_normal((H, d))
+        if kind.topk is not None:
+            idx = paging.Pool(kind.idx_dtype, P, epp, kind.d_idx)
+            idx.codes[:] = rng.integers(0, 256, idx.codes.shape, dtype=np.uint8)
+            idx.scales[:] = rng.integers(0x20, 0x40, idx.scales.shape, dtype=np.uint8)
+            qi, wi = rng.standard_normal((kind.h_idx, kind.d_idx)), rng.standard_normal(kind.h_idx)
+        times = []
+        while True:
+            t0 = time.perf_counter()
+            if kind.topk is not None:
+                keys = paging.decode_rows(idx, table, np.arange(N))
+                s = indexer.scores(qi, wi, keys)
+                sel = indexer.topk(s, kind.topk)
+            else:
+                sel = np.arange(N)
+            rows = paging.decode_rows(kv, table, sel)
+            rows = np.concatenate([rows, paging.decode_rows(win, wtable, attention.window_positions(L, W))])
+            attention.attend(q, rows, L, 1.0 / math.sqrt(d), w.theta)
+            times.append(time.perf_counter() - t0)
+            if sum(times) > budget_s / len(kinds) or len(times) >= 200:
+                break
+        t_layer[name] = float(np.median(times))
+        reps[name] = len(times)
+    n_kind = {name: sum(1 for k in w.layers if k.name == name) for name in kinds}
+    t_seq_step = sum(t_layer[nm] * n_kind[nm] for nm in kinds)
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    out = {
+        "value": 1.0 / t_seq_step,
+        "unit": "tokens/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle decode step (indexer scores + top-k + row gather/decode + attention) of one "
+                   f"sequence at L={L} for one c4a layer ({reps.get('c4a', 0)} runs, median "
+                   f"{t_layer.get('c4a', 0):.2f} s) and one c128a layer ({reps.get('c128a', 0)} runs, median "
+                   f"{t_layer.get('c128a', 0):.2f} s), scaled by the stack's {n_kind} layers; the batch's "
+                   f"sequences are independent so batch tokens/s equals per-sequence tokens/s; "
+                   f"wall {time.perf_counter() - t_start:.1f} s"),
+    }
+    return out
+
+
+# ----------------------------------------------------------------- main
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import decode_attention_compressed_amd as hca
+    import synth
+    from synth import gen
+
+    log = lambda s: print(f"[bench] {s}", file=sys.stderr, flush=True)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    hca.lib()
+    w = synth.workload(args.config)
+    if w.L is None:
+        print("bench.py times fixed-length workloads (configs 0, 1, 2, 4)", file=sys.stderr)
+        sys.exit(2)
+    n_layers = len(w.layers) if args.layers <= 0 else min(args.layers, len(w.layers))
+    log(f"workload {w.name}: B={w.B} L={w.L} layers={n_layers}")
+    layers, shared, pre = build_state(w, n_layers, torch, hca, gen, log)
+    # workspaces (one per kind; the indexer one must start zeroed and is left zeroed)
+    kinds = {l.kind.name: l.kind for l in layers}
+    ws_idx = None
+    ws_att = {}
+    for name, kind in kinds.items():
+        if kind.topk is not None:
+            ws_idx = hca.workspace(hca.indexer_topk_workspace(w.B, w.L, kind.m, kind.topk))
+        ws_att[name] = hca.workspace(hca.paged_hybrid_decode_workspace(w.B, w.H, w.d, w.L, kind.m, w.window,
+                                                                       kind.topk or 0))
+    torch.cuda.synchronize()
+    log("capturing decode step")
+    t_step, wall, _g = time_graph(torch, lambda: decode_step(w, layers, shared, ws_idx, ws_att, hca), args.steps,
+                                  args.warmup)
+    log(f"step {t_step:.3f} ms")
+    t_attn, _, _g2 = time_graph(torch, lambda: decode_step(w, layers, shared, ws_idx, ws_att, hca, update=False),
+                                args.steps, args.warmup)
+    t_upd, _, _g3 = time_graph(torch, lambda: decode_step(w, layers, shared, ws_idx, ws_att, hca, attend=False),
+                               args.steps, args.warmup)
+    dom = time_dominant(torch, hca, w, layers, shared)
+    alg = sum(layer_bytes(l.kind, w.B, w.L, w.d, w.H, w.window) for l in layers)
+    upd = sum(update_bytes(l.kind, w.B, w.d) for l in layers)
+    roofline = None
+    if dom is not None:
+        kind = [l.kind for l in layers if l.kind.topk is not None][0]
+        sb = score_bytes(kind, w.B, w.L)
+        achieved = sb / (dom[0] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "score_kernel<fp4,128> (indexer scoring)", "bytes_per_launch": int(sb),
+                    "avg_launch_ms": round(dom[0], 5), "median_launch_ms": round(dom[1], 5), "launches": dom[2]}
+    cpu = None
+    if not args.no_cpu_baseline and n_layers == len(w.layers):
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(w)
+    value = w.B / (t_step * 1e-3)
+    res = {
+        "metric": "decode-attn tokens/sec per GPU (1M-token 61-layer stack)",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 KV / fp4 idx, f16+bf16 MFMA, fp32 acc",
+        "data": "synthetic (seeded N(0,1) tokens, logits, queries, indexer keys; random page permutation)",
+        "config": {"workload": w.name, "batch": w.B, "context": w.L, "layers": n_layers,
+                   "c4a_layers": sum(1 for l in layers if l.kind.name == "c4a"),
+                   "c128a_layers": sum(1 for l in layers if l.kind.name == "c128a"), "d": w.d, "heads": w.H,
+                   "window": w.window, "topk": 2048, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "step_breakdown": {
+            "algorithmic_bytes_per_step": int(alg),
+            "update_bytes_per_step": int(upd),
+            "step_GBps_incl_update": round((alg + upd) / (t_step * 1e-3) / 1e9, 1),
+            "attn_only_ms": round(t_attn, 4),
+            "attn_only_tokens_per_s": round(w.B / (t_attn * 1e-3), 2),
+            "attn_only_GBps": round(alg / (t_attn * 1e-3) / 1e9, 1),
+            "attn_only_frac_of_peak": round(alg / (t_attn * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "update_only_ms": round(t_upd, 4),
+            "wall_s_timed_region": round(wall, 4),
+        },
+        "prefill": {"ms_all_layers": round(pre["ms"], 3), "bytes": int(pre["bytes"]),
+                    "GBps": round(pre["bytes"] / (pre["ms"] * 1e-3) / 1e9, 1) if pre["ms"] > 0 else None,
+                    "what": "kv_compress + kv_quantize_page over the whole context of every layer"},
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -30,6 +30,7 @@ EXPORTS = (
     "hca_status_string", "hca_version", "kv_compress", "kv_quantize_page", "indexer_topk_workspace",
     "indexer_topk", "paged_hybrid_decode_workspace", "paged_hybrid_decode", "kv_gather",
     "hca_host_e4m3_encode", "hca_host_e2m1_encode", "hca_host_bf16_encode", "hca_probe_decode", "hca_probe_mfma",
+    "hca_indexer_score",
 )
 
 
@@ -74,6 +75,7 @@ def lib() -> ctypes.CDLL:
         L.hca_host_bf16_encode.argtypes = [_P, _P, _I64]
         L.hca_probe_decode.argtypes = [_P, _P, _I32, _I32, _P]
         L.hca_probe_mfma.argtypes = [_P, _P, _P, _I32, _P]
+        L.hca_indexer_score.argtypes = [_P, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P]
         for name in EXPORTS:
             if name not in ("hca_status_string", "hca_version", "indexer_topk_workspace",
                             "paged_hybrid_decode_workspace"):
@@ -165,6 +167,15 @@ def indexer_topk(q_idx, head_w, idx_keys: PagedCache, block_table, seq_lens, max
     _check(lib().indexer_topk(_ptr(q_idx), _ptr(head_w), HI, idx_keys.c(), _ptr(block_table),
                               block_table.stride(0), _ptr(seq_lens), B, max_seq_len, m, k, _ptr(out_idx),
                               _ptr(out_n), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "indexer_topk")
+
+
+def indexer_score(q_idx, head_w, idx_keys: PagedCache, block_table, seq_lens, max_seq_len: int, m: int, k: int, ws,
+                  stream=None):
+    """Measurement hook: the scoring kernel of indexer_topk alone (ws reserved for it)."""
+    B, HI, _ = q_idx.shape
+    _check(lib().hca_indexer_score(_ptr(q_idx), _ptr(head_w), HI, idx_keys.c(), _ptr(block_table),
+                                   block_table.stride(0), _ptr(seq_lens), B, max_seq_len, m, k, _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)), "hca_indexer_score")
 
 
 def paged_hybrid_decode_workspace(B: int, H: int, d: int, max_seq_len: int, m: int, window: int, k: int) -> int:

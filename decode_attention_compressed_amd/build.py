@@ -29,6 +29,11 @@ FLAGS = [
 ]
 
 
+# per-source extra flags: the indexer keeps MFMA results in VGPRs (its
+# accumulators are small), saving the AGPR-to-VGPR copies on every tile
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
@@ -42,7 +47,8 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        outs = list(ex.map(lambda so: _run([HIPCC, *FLAGS, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
+        outs = list(ex.map(lambda so: _run([HIPCC, *FLAGS, *EXTRA.get(os.path.basename(so[0]), []), "-c", so[0], "-o", so[1]]),
+                           zip(srcs, objs)))
     if verbose:
         for o in outs:
             if o.strip():

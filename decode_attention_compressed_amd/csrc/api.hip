@@ -82,10 +82,10 @@ size_t indexer_topk_workspace(int32_t B, int32_t max_seq_len, int32_t m, int32_t
   return indexer_ws_layout(B, max_seq_len, m, k).total;
 }
 
-hca_status indexer_topk(const uint16_t* q_idx, const float* head_w, int32_t HI, hca_paged_cache idx_keys,
-                        const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens, int32_t B,
-                        int32_t max_seq_len, int32_t m, int32_t k, int32_t* out_idx, int32_t* out_n, void* ws,
-                        size_t ws_bytes, void* stream) {
+static hca_status indexer_prepare(const uint16_t* q_idx, const float* head_w, int32_t HI, hca_paged_cache idx_keys,
+                                  const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens, int32_t B,
+                                  int32_t max_seq_len, int32_t m, int32_t k, int32_t* out_idx, int32_t* out_n,
+                                  bool need_out, void* ws, size_t ws_bytes, IndexerArgs& a) {
   if (B < 0 || max_seq_len < 0 || !valid_m(m) || k < 1 || bt_stride < 1) return HCA_ERR_INVALID;
   if (k > 8192) return HCA_ERR_UNSUPPORTED;
   if (HI < 1) return HCA_ERR_INVALID;
@@ -95,13 +95,36 @@ hca_status indexer_topk(const uint16_t* q_idx, const float* head_w, int32_t HI, 
   if (di != 32 && di != 64 && di != 128 && di != 256) return HCA_ERR_UNSUPPORTED;
   if ((int64_t)bt_stride * 256 < max_seq_len) return HCA_ERR_INVALID;
   if (B == 0) return HCA_OK;
-  if (!q_idx || !head_w || !block_table || !seq_lens || !out_idx || !out_n) return HCA_ERR_INVALID;
+  if (!q_idx || !head_w || !block_table || !seq_lens) return HCA_ERR_INVALID;
+  if (need_out && (!out_idx || !out_n)) return HCA_ERR_INVALID;
   if (!aligned(q_idx, 16)) return HCA_ERR_INVALID;
   const IndexerWs lay = indexer_ws_layout(B, max_seq_len, m, k);
+  if (lay.n_max > (1 << 21)) return HCA_ERR_UNSUPPORTED;  // more than 2M entries per sequence
   if (!ws || ws_bytes < lay.total || !aligned(ws, 256)) return HCA_ERR_WORKSPACE;
-  IndexerArgs a{q_idx, head_w, HI, idx_keys, block_table, bt_stride, seq_lens, B, max_seq_len, m, k, out_idx, out_n,
-                reinterpret_cast<unsigned char*>(ws), lay};
+  a = IndexerArgs{q_idx, head_w, HI, idx_keys, block_table, bt_stride, seq_lens, B, max_seq_len, m, k, out_idx, out_n,
+                  reinterpret_cast<unsigned char*>(ws), lay};
+  return HCA_OK;
+}
+
+hca_status indexer_topk(const uint16_t* q_idx, const float* head_w, int32_t HI, hca_paged_cache idx_keys,
+                        const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens, int32_t B,
+                        int32_t max_seq_len, int32_t m, int32_t k, int32_t* out_idx, int32_t* out_n, void* ws,
+                        size_t ws_bytes, void* stream) {
+  IndexerArgs a{};
+  const hca_status st = indexer_prepare(q_idx, head_w, HI, idx_keys, block_table, bt_stride, seq_lens, B, max_seq_len,
+                                        m, k, out_idx, out_n, true, ws, ws_bytes, a);
+  if (st != HCA_OK || B == 0) return st;
   return from_hip(launch_indexer(a, (hipStream_t)stream));
+}
+
+hca_status hca_indexer_score(const uint16_t* q_idx, const float* head_w, int32_t HI, hca_paged_cache idx_keys,
+                             const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens, int32_t B,
+                             int32_t max_seq_len, int32_t m, int32_t k, void* ws, size_t ws_bytes, void* stream) {
+  IndexerArgs a{};
+  const hca_status st = indexer_prepare(q_idx, head_w, HI, idx_keys, block_table, bt_stride, seq_lens, B, max_seq_len,
+                                        m, k, nullptr, nullptr, false, ws, ws_bytes, a);
+  if (st != HCA_OK || B == 0) return st;
+  return from_hip(launch_indexer_score(a, (hipStream_t)stream));
 }
 
 size_t paged_hybrid_decode_workspace(int32_t B, int32_t H, int32_t d, int32_t max_seq_len, int32_t m, int32_t window,
@@ -126,7 +149,7 @@ hca_status paged_hybrid_decode(const uint16_t* q, int32_t H, hca_paged_cache kv,
   if (window < 0 || window > 256) return HCA_ERR_INVALID;
   if (window > 0) {
     if (!cache_ok(win) || win.epp != 256 || win.dim != d || !win_block_table || wbt_stride < 1) return HCA_ERR_INVALID;
-    if (win.dtype == HCA_FP4_E2M1) return HCA_ERR_UNSUPPORTED;
+    if (win.dtype != kv.dtype) return HCA_ERR_UNSUPPORTED;  // one row format per launch
     if ((int64_t)wbt_stride * 256 < max_seq_len) return HCA_ERR_INVALID;
   }
   if ((int64_t)bt_stride * 256 < max_seq_len) return HCA_ERR_INVALID;
@@ -136,6 +159,7 @@ hca_status paged_hybrid_decode(const uint16_t* q, int32_t H, hca_paged_cache kv,
   if (!q || !block_table || !seq_lens || !out) return HCA_ERR_INVALID;
   if (!aligned(q, 16)) return HCA_ERR_INVALID;
   const AttnPlan plan = attn_plan(B, H, d, max_seq_len, m, window, sel_idx ? k : 0, sel_idx != nullptr);
+  if (plan.splits > kAttnMaxSplits) return HCA_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < plan.total || !aligned(ws, 256)) return HCA_ERR_WORKSPACE;
   hca_paged_cache w = win;
   if (window == 0) { w = kv; w.epp = 256; }  // never read

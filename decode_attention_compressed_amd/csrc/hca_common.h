@@ -116,4 +116,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// Load through the global address space.  Pointers rebuilt from integers (for
+// example row addresses kept in LDS) are generic; a generic (flat) load also
+// counts against the LDS counter, so every LDS wait would drain it too.
+template <typename T>
+__device__ __forceinline__ T gload(const void* p) {
+  return *(const __attribute__((address_space(1))) T*)(p);
+}
+
 }  // namespace hca

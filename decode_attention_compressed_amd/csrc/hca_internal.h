@@ -39,7 +39,7 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 
 // indexer workspace layout (all offsets 256-byte aligned)
 struct IndexerWs {
-  size_t scores, hist, cand, bitmap, counters, total;
+  size_t scores, hist, cand, bitmap, counters, cand_counts, total;
   int n_max;  // max entries per sequence
 };
 IndexerWs indexer_ws_layout(int B, int max_seq_len, int m, int k);
@@ -55,6 +55,7 @@ struct IndexerArgs {
   unsigned char* ws; IndexerWs lay;
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
+hipError_t launch_indexer_score(const IndexerArgs& a, hipStream_t s);
 
 // attention workspace: per (sequence, split, head) partial (m, l) and o[d]
 struct AttnPlan {
@@ -64,6 +65,7 @@ struct AttnPlan {
   int head_blocks;  // ceil(H / 64)
   size_t o_off, ml_off, total;
 };
+constexpr int kAttnMaxSplits = 4096;  // splits per sequence the combine kernel handles
 AttnPlan attn_plan(int B, int H, int d, int max_seq_len, int m, int window, int k, bool has_sel);
 
 struct AttnArgs {

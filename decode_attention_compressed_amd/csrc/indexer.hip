@@ -28,7 +28,9 @@ namespace hca {
 constexpr int kScoreThreads = 256;
 constexpr int kScoreChunk = 1024;  // entries per score block (256 per wave)
 constexpr int kSelThreads = 256;
-constexpr int kSelChunk = 8192;    // entries per select block (32 per thread)
+constexpr int kSelChunk = 2048;    // entries per select block (8 per thread)
+constexpr int kMaxSelBlocks = 1024;  // select blocks per sequence (N <= 2M entries)
+constexpr int kCandLds = 4096;      // candidates the last block stages in LDS
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -44,6 +46,7 @@ IndexerWs indexer_ws_layout(int B, int max_seq_len, int m, int k) {
   w.cand = off; off = align256(off + (size_t)B * n_pad * sizeof(uint2));
   w.bitmap = off; off = align256(off + (size_t)B * (n_pad / 32) * sizeof(uint32_t));
   w.counters = off; off = align256(off + (size_t)B * 4 * sizeof(uint32_t));
+  w.cand_counts = off; off = align256(off + (size_t)B * (n_pad / kSelChunk) * sizeof(uint32_t));
   w.total = off;
   return w;
 }
@@ -85,142 +88,334 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// The bytes one lane reads for one 16-entry tile, and how they become the MFMA
+// B operand.  Lane (col, g) serves entry `col` of the tile.
+//   bf16 / fp8: lane group g owns the contiguous dims [g*DI/4, (g+1)*DI/4) of the
+//               key (16-byte loads); k-step t uses the 8 dims at +8t.
+//   fp4:        k-step t is scale block t; lane group g reads the 4 bytes holding
+//               dims 32t + 8g .. +8 of it.
+template <int KDT, int DI>
+struct Tile {
+  static constexpr int KS = DI / 32;
+  static constexpr int NW = KDT == HCA_FP4_E2M1 ? KS : (KDT == HCA_FP8_E4M3 ? DI / 16 : DI / 8);
+  uint32_t w[NW];
+  uint32_t sc[(KS + 3) / 4];  // fp4 block-scale codes of the entry
+  float ps;                   // fp8 page scale (0 for a missing row)
+
+  // Branch-free: a dead lane (past N or an unmapped page) reads the pool's first
+  // row and masks the value, so all loads stay in straight-line code and the
+  // compiler can keep the next page's loads in flight while this one is used.
+  __device__ __forceinline__ void load(const uint8_t* row, const uint8_t* srow, float page_scale, bool live, int g) {
+    ps = live ? page_scale : 0.0f;
+    if constexpr (KDT == HCA_FP4_E2M1) {
+#pragma unroll
+      for (int t = 0; t < KS; ++t) w[t] = *reinterpret_cast<const uint32_t*>(row + 16 * t + 4 * g);
+      if constexpr (KS % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < KS / 4; ++i) sc[i] = *reinterpret_cast<const uint32_t*>(srow + 4 * i);
+      } else {
+        sc[0] = 0u;
+#pragma unroll
+        for (int t = 0; t < KS; ++t) sc[0] |= (uint32_t)srow[t] << (8 * t);
+      }
+#pragma unroll
+      for (int i = 0; i < (KS + 3) / 4; ++i) sc[i] = live ? sc[i] : 0u;
+    } else {
+      const uint8_t* lrow = row + g * (NW * 4);
+      if constexpr (NW >= 4) {
+#pragma unroll
+        for (int c = 0; c < NW / 4; ++c) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(lrow + 16 * c);
+          w[4 * c] = v[0]; w[4 * c + 1] = v[1]; w[4 * c + 2] = v[2]; w[4 * c + 3] = v[3];
+        }
+      } else {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(lrow);
+        w[0] = v[0]; w[1] = v[1];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] = live ? w[i] : 0u;
+  }
+
+  // dot products of this lane's 4 heads (rows 4g..4g+3 of the accumulator) with entry col
+  __device__ __forceinline__ f32x4 dots(const bf16x8* qa) const {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (KDT == HCA_FP4_E2M1) {
+      float sfs[4 * ((KS + 3) / 4)];  // exact E4M3 decode of the block scales
+#pragma unroll
+      for (int i = 0; i < (KS + 3) / 4; ++i) {
+        sfs[4 * i + 0] = __builtin_amdgcn_cvt_f32_fp8((int)sc[i], 0);
+        sfs[4 * i + 1] = __builtin_amdgcn_cvt_f32_fp8((int)sc[i], 1);
+        sfs[4 * i + 2] = __builtin_amdgcn_cvt_f32_fp8((int)sc[i], 2);
+        sfs[4 * i + 3] = __builtin_amdgcn_cvt_f32_fp8((int)sc[i], 3);
+      }
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], fp4x8_to_bf16(w[t]), z, 0, 0, 0);
+        const float sf = sfs[t];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(sf, part[i], acc[i]);
+      }
+    } else if constexpr (KDT == HCA_FP8_E4M3) {
+#pragma unroll
+      for (int t = 0; t < KS; ++t)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], fp8x8_to_bf16(w[2 * t], w[2 * t + 1]), acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= ps;
+    } else {
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        const u32x4 v = {w[4 * t], w[4 * t + 1], w[4 * t + 2], w[4 * t + 3]};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], __builtin_bit_cast(bf16x8, v), acc, 0, 0, 0);
+      }
+    }
+    return acc;
+  }
+};
+
+struct ScoreCtx {
+  float wgt[4];
+  float* scores;
+  uint32_t* hist_s;
+  bool want_hist;
+};
+
+// ReLU, head weights, head sum; lanes 0..15 write the scores of the tile
+__device__ __forceinline__ void finish_tile(const ScoreCtx& c, f32x4 acc, int e, bool valid, int g) {
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s = fmaf(c.wgt[i], fmaxf(acc[i], 0.0f), s);
+  s += __shfl_xor(s, 16, 64);
+  s += __shfl_xor(s, 32, 64);
+  if (g == 0 && valid) {
+    c.scores[e] = s;
+    if (c.want_hist) atomicAdd(&c.hist_s[order_key(s) >> 20], 1u);
+  }
+}
+
+template <int KDT, int DI>
+__device__ __forceinline__ void load_query(const IndexerArgs& a, int b, int col, int g, bf16x8* qa, float* wgt) {
+  constexpr int KS = DI / 32;
+  const int h = col;
+  const uint16_t* qrow = a.q + ((int64_t)b * a.HI + (h < a.HI ? h : 0)) * DI;
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    const int c0 = (KDT == HCA_FP4_E2M1) ? (32 * t + 8 * g) : (g * (DI / 4) + 8 * t);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (h < a.HI) v = *reinterpret_cast<const u32x4*>(qrow + c0);
+    qa[t] = __builtin_bit_cast(bf16x8, v);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = 4 * g + i;
+    wgt[i] = hh < a.HI ? a.w[(int64_t)b * a.HI + hh] : 0.0f;
+  }
+}
+
+__device__ __forceinline__ void hist_flush(const IndexerArgs& a, int b, const uint32_t* hist_s) {
+  __syncthreads();
+  uint32_t* gh = reinterpret_cast<uint32_t*>(a.ws + a.lay.hist) + (size_t)b * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) {
+    const uint32_t c = hist_s[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+__device__ __forceinline__ float* score_row(const IndexerArgs& a, int b) {
+  return reinterpret_cast<float*>(a.ws + a.lay.scores) +
+         (size_t)b * ((a.lay.n_max + kSelChunk - 1) / kSelChunk) * kSelChunk;
+}
+
+// Fast path: 64 entries per page (m = 4).  A wave scores whole pages.  The
+// page is uniform over the wave, so its table lookup is a scalar load and it
+// gets a buffer resource of its own whose size is the page's valid bytes: a
+// lane past the last valid entry, or a whole page that is unmapped, reads 0 in
+// hardware, so the loads need no masks, no branches and only 32-bit offsets.
+// Pages are double-buffered (the loads of page i+2 are issued right after page
+// i is consumed), fully unrolled so that the waits count down in order.
+constexpr int kPagesPerScoreBlock = 8;
+constexpr int kPagesPerScoreWave = kPagesPerScoreBlock / 4;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int KDT, int DI>
+struct PageTiles {
+  static constexpr int KS = DI / 32;
+  static constexpr int ROW = KDT == HCA_FP4_E2M1 ? DI / 2 : (KDT == HCA_FP8_E4M3 ? DI : 2 * DI);
+  static constexpr int NW = KDT == HCA_FP4_E2M1 ? KS : (KDT == HCA_FP8_E4M3 ? DI / 16 : DI / 8);
+  uint32_t w[4][NW];
+  uint32_t sc[4][(KS + 3) / 4];
+  float ps;
+
+  __device__ __forceinline__ void load(const IndexerArgs& a, const int32_t* btrow, int p, bool p_ok, int N, int col,
+                                       int g) {
+    const int phys = btrow[p_ok ? p : 0];
+    const bool live = p_ok && phys >= 0 && phys < a.keys.num_pages;
+    const int rows = live ? min(64, N - 64 * p) : 0;
+    const int pg = live ? phys : 0;
+    const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.keys.codes) + (int64_t)pg * 64 * ROW;
+    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(codes, (uint32_t)(rows * ROW));
+    if constexpr (KDT == HCA_FP8_E4M3) ps = reinterpret_cast<const float*>(a.keys.scales)[pg];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int row_off = (16 * tt + col) * ROW;
+      if constexpr (KDT == HCA_FP4_E2M1) {
+#pragma unroll
+        for (int t = 0; t < KS; ++t) w[tt][t] = __builtin_amdgcn_raw_buffer_load_b32(rc, row_off + 16 * t + 4 * g, 0, 0);
+      } else if constexpr (NW >= 4) {
+#pragma unroll
+        for (int c = 0; c < NW / 4; ++c) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, row_off + g * (NW * 4) + 16 * c, 0, 0);
+          w[tt][4 * c] = v[0]; w[tt][4 * c + 1] = v[1]; w[tt][4 * c + 2] = v[2]; w[tt][4 * c + 3] = v[3];
+        }
+      } else {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, row_off + g * 8, 0, 0);
+        w[tt][0] = v[0]; w[tt][1] = v[1];
+      }
+    }
+    if constexpr (KDT == HCA_FP4_E2M1) {
+      const uint8_t* scl = reinterpret_cast<const uint8_t*>(a.keys.scales) + (int64_t)pg * 64 * KS;
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scl, (uint32_t)(rows * KS));
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        if constexpr (KS % 4 == 0) {
+#pragma unroll
+          for (int i = 0; i < KS / 4; ++i) sc[tt][i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (16 * tt + col) * KS + 4 * i, 0, 0);
+        } else {
+          sc[tt][0] = 0u;
+#pragma unroll
+          for (int t = 0; t < KS; ++t)
+            sc[tt][0] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (16 * tt + col) * KS + t, 0, 0) << (8 * t);
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ f32x4 dots(int tt, const bf16x8* qa) const {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (KDT == HCA_FP4_E2M1) {
+      float sfs[4 * ((KS + 3) / 4)];  // exact E4M3 decode of the block scales
+#pragma unroll
+      for (int i = 0; i < (KS + 3) / 4; ++i) {
+        sfs[4 * i + 0] = __builtin_amdgcn_cvt_f32_fp8((int)sc[tt][i], 0);
+        sfs[4 * i + 1] = __builtin_amdgcn_cvt_f32_fp8((int)sc[tt][i], 1);
+        sfs[4 * i + 2] = __builtin_amdgcn_cvt_f32_fp8((int)sc[tt][i], 2);
+        sfs[4 * i + 3] = __builtin_amdgcn_cvt_f32_fp8((int)sc[tt][i], 3);
+      }
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], fp4x8_to_bf16(w[tt][t]), z, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(sfs[t], part[i], acc[i]);
+      }
+    } else if constexpr (KDT == HCA_FP8_E4M3) {
+#pragma unroll
+      for (int t = 0; t < KS; ++t)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], fp8x8_to_bf16(w[tt][2 * t], w[tt][2 * t + 1]), acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= ps;
+    } else {
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        const u32x4 v = {w[tt][4 * t], w[tt][4 * t + 1], w[tt][4 * t + 2], w[tt][4 * t + 3]};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], __builtin_bit_cast(bf16x8, v), acc, 0, 0, 0);
+      }
+    }
+    return acc;
+  }
+};
+
+template <int KDT, int DI>
+__global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(IndexerArgs a) {
+  const int b = blockIdx.y;
+  const int L = clampi(a.lens[b], 0, a.max_len);
+  const int N = (L + a.m - 1) / a.m;
+  const int NP = (N + 63) / 64;
+  const int page0 = blockIdx.x * kPagesPerScoreBlock;
+  if (page0 >= NP) return;
+  __shared__ uint32_t hist_s[kHistBins];
+  ScoreCtx c;
+  c.want_hist = a.k < N;
+  c.hist_s = hist_s;
+  c.scores = score_row(a, b);
+  if (c.want_hist) {
+    for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) hist_s[i] = 0;
+    __syncthreads();
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar page math
+  const int col = lane & 15, g = lane >> 4;
+  bf16x8 qa[DI / 32];
+  load_query<KDT, DI>(a, b, col, g, qa, c.wgt);
+  const int32_t* btrow = a.bt + (int64_t)b * a.bts;
+  const int p_end = min(NP, page0 + kPagesPerScoreBlock);
+  constexpr int PPW = kPagesPerScoreWave;
+  PageTiles<KDT, DI> pa, pb;
+  auto page_of = [&](int i) { return page0 + wave + 4 * i; };
+  auto consume = [&](const PageTiles<KDT, DI>& t, int i) {
+    const int p = page_of(i);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int e = 64 * p + 16 * tt + col;
+      finish_tile(c, t.dots(tt, qa), e, p < p_end && e < N, g);
+    }
+  };
+  pa.load(a, btrow, page_of(0), page_of(0) < p_end, N, col, g);
+  pb.load(a, btrow, page_of(1), page_of(1) < p_end, N, col, g);
+#pragma unroll
+  for (int i = 0; i < PPW; i += 2) {
+    consume(pa, i);
+    if (i + 2 < PPW) pa.load(a, btrow, page_of(i + 2), page_of(i + 2) < p_end, N, col, g);
+    consume(pb, i + 1);
+    if (i + 3 < PPW) pb.load(a, btrow, page_of(i + 3), page_of(i + 3) < p_end, N, col, g);
+  }
+  if (c.want_hist) hist_flush(a, b, hist_s);
+}
+
+// Generic path (any entries-per-page): per-lane table lookups, 16 entries a step.
 template <int KDT, int DI>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs a) {
-  constexpr int KS = DI / 32;  // MFMA k-steps
   const int b = blockIdx.y;
   const int L = clampi(a.lens[b], 0, a.max_len);
   const int N = (L + a.m - 1) / a.m;
   const int chunk0 = blockIdx.x * kScoreChunk;
   if (chunk0 >= N) return;
-  const bool want_hist = a.k < N;
   __shared__ uint32_t hist_s[kHistBins];
-  if (want_hist) {
+  ScoreCtx c;
+  c.want_hist = a.k < N;
+  c.hist_s = hist_s;
+  c.scores = score_row(a, b);
+  if (c.want_hist) {
     for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) hist_s[i] = 0;
     __syncthreads();
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int epp = a.keys.epp;
-
-  // query fragments (heads >= HI are zero) and head weights of the 4 accumulator rows
-  bf16x8 qa[KS];
-  {
-    const int h = col;
-    const uint16_t* qrow = a.q + ((int64_t)b * a.HI + h) * DI;
-#pragma unroll
-    for (int t = 0; t < KS; ++t) {
-      // bf16 / fp8 keys: lane group g owns dims [g*DI/4, (g+1)*DI/4), step t the 8 at +8t
-      // fp4 keys: step t is block t; lane group g owns dims 32t + 8g .. +8
-      const int c0 = (KDT == HCA_FP4_E2M1) ? (32 * t + 8 * g) : (g * (DI / 4) + 8 * t);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (h < a.HI) v = *reinterpret_cast<const u32x4*>(qrow + c0);
-      qa[t] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-  float wgt[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * g + i;
-    wgt[i] = h < a.HI ? a.w[(int64_t)b * a.HI + h] : 0.0f;
-  }
-
+  bf16x8 qa[DI / 32];
+  load_query<KDT, DI>(a, b, col, g, qa, c.wgt);
+  constexpr int row_bytes = KDT == HCA_FP4_E2M1 ? DI / 2 : (KDT == HCA_FP8_E4M3 ? DI : 2 * DI);
   const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.keys.codes);
-  const int row_bytes = DI * KeyBytes<KDT>::per_dim_x2 / 2;
-  float* scores = reinterpret_cast<float*>(a.ws + a.lay.scores) + (size_t)b * ((a.lay.n_max + kSelChunk - 1) / kSelChunk) * kSelChunk;
-
+  const uint8_t* scales = reinterpret_cast<const uint8_t*>(a.keys.scales);
   const int wave0 = chunk0 + wave * (kScoreChunk / 4);
   const int wave1 = min(N, wave0 + kScoreChunk / 4);
   for (int e_base = wave0; e_base < wave1; e_base += 16) {
     const int e = e_base + col;
     const bool valid = e < wave1;
-    int phys = -1, slot = 0;
-    if (valid) {
-      phys = a.bt[(int64_t)b * a.bts + e / epp];
-      slot = e % epp;
-      if (phys >= a.keys.num_pages) phys = -1;
-    }
-    const bool live = phys >= 0;
-    const uint8_t* row = codes + ((int64_t)(live ? phys : 0) * epp + slot) * row_bytes;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (KDT == HCA_FP4_E2M1) {
-      // per-block accumulators, block scales applied in fp32
-      uint32_t sc_raw = 0;
-      if (live) {
-        const uint8_t* srow = reinterpret_cast<const uint8_t*>(a.keys.scales) + ((int64_t)phys * epp + slot) * KS;
-        if constexpr (KS == 4) sc_raw = *reinterpret_cast<const uint32_t*>(srow);
-        else {
-#pragma unroll
-          for (int t = 0; t < KS && t < 4; ++t) sc_raw |= (uint32_t)srow[t] << (8 * t);
-        }
-      }
-      uint32_t kw[KS];
-#pragma unroll
-      for (int t = 0; t < KS; ++t) kw[t] = live ? *reinterpret_cast<const uint32_t*>(row + 16 * t + 4 * g) : 0u;
-#pragma unroll
-      for (int t = 0; t < KS; ++t) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], fp4x8_to_bf16(kw[t]), z, 0, 0, 0);
-        // the accumulator column (entry) of this lane is `col`; its block-t scale:
-        uint32_t sc;
-        if constexpr (KS <= 4) sc = (sc_raw >> (8 * t)) & 0xFFu;
-        else sc = live ? reinterpret_cast<const uint8_t*>(a.keys.scales)[((int64_t)phys * epp + slot) * KS + t] : 0u;
-        const float sf = e4m3_decode(sc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = fmaf(sf, part[i], acc[i]);
-      }
-    } else {
-      constexpr int LB = DI * KeyBytes<KDT>::per_dim_x2 / 8;  // bytes per lane
-      const uint8_t* lrow = row + g * LB;
-      bf16x8 kb[KS];
-      if constexpr (KDT == HCA_FP8_E4M3) {
-        // LB = DI/4 bytes: KS chunks of 8 codes
-#pragma unroll
-        for (int t = 0; t < KS; t += 2) {
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (live) {
-            if (t + 1 < KS) v = *reinterpret_cast<const u32x4*>(lrow + 8 * t);
-            else { u32x2 h2 = *reinterpret_cast<const u32x2*>(lrow + 8 * t); v[0] = h2[0]; v[1] = h2[1]; }
-          }
-          kb[t] = fp8x8_to_bf16(v[0], v[1]);
-          if (t + 1 < KS) kb[t + 1] = fp8x8_to_bf16(v[2], v[3]);
-        }
-      } else {
-        // bf16 keys: LB = DI/2 bytes, KS chunks of 8 values (16 bytes)
-#pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (live) v = *reinterpret_cast<const u32x4*>(lrow + 16 * t);
-          kb[t] = __builtin_bit_cast(bf16x8, v);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < KS; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], kb[t], acc, 0, 0, 0);
-      if constexpr (KDT == HCA_FP8_E4M3) {
-        const float ps = live ? reinterpret_cast<const float*>(a.keys.scales)[phys] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] *= ps;
-      }
-    }
-    // lane holds heads 4g+i of entry `col`: ReLU, weight, sum over heads
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s = fmaf(wgt[i], fmaxf(acc[i], 0.0f), s);
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
-    if (g == 0 && valid) {
-      scores[e] = s;
-      if (want_hist) atomicAdd(&hist_s[order_key(s) >> 20], 1u);
-    }
+    int phys = a.bt[(int64_t)b * a.bts + (valid ? e : wave0) / epp];
+    const int slot = (valid ? e : wave0) % epp;
+    const bool live = valid && phys >= 0 && phys < a.keys.num_pages;
+    const float pscale = KDT == HCA_FP8_E4M3 ? reinterpret_cast<const float*>(a.keys.scales)[live ? phys : 0] : 0.0f;
+    const int64_t r = live ? (int64_t)phys * epp + slot : 0;
+    Tile<KDT, DI> t;
+    t.load(codes + r * row_bytes, scales + r * (DI / 32), pscale, live, g);
+    finish_tile(c, t.dots(qa), e, valid, g);
   }
-  if (want_hist) {
-    __syncthreads();
-    uint32_t* gh = reinterpret_cast<uint32_t*>(a.ws + a.lay.hist) + (size_t)b * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) {
-      const uint32_t c = hist_s[i];
-      if (c) atomicAdd(&gh[i], c);
-    }
-  }
+  if (c.want_hist) hist_flush(a, b, hist_s);
 }
 
 // ------------------------------------------------------------------ select
@@ -258,6 +453,8 @@ __device__ void find_cut(const uint32_t* bins, int nb, uint32_t need, uint32_t* 
   const uint32_t before = block_excl_scan(cnt, tmp, total);
   __shared__ int cut_s;
   __shared__ uint32_t above_s;
+  if (threadIdx.x == 0) { cut_s = 0; above_s = 0; }
+  __syncthreads();
   if (before < need && before + cnt >= need) {
     uint32_t run = before;
     for (int i = 1; i <= per; ++i) {
@@ -295,6 +492,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
   uint2* cand = reinterpret_cast<uint2*>(a.ws + a.lay.cand) + (size_t)b * n_pad;
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(a.ws + a.lay.bitmap) + (size_t)b * (n_pad / 32);
   uint32_t* ctr = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + (size_t)b * 4;  // [0] candidates, [1] ticket
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
   __shared__ uint32_t tmp[kSelThreads / 64];
   __shared__ uint32_t h_s[1024];
@@ -302,23 +500,50 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
   uint32_t above;
   find_cut(hist, kHistBins, (uint32_t)k, tmp, cut, above);
 
-  // chunk pass: 32 consecutive entries per thread, one bitmap word each
-  const int e0 = blockIdx.x * kSelChunk + threadIdx.x * 32;
-  if (e0 < N) {
-    uint32_t bits = 0;
-    for (int i = 0; i < 32; ++i) {
-      const int e = e0 + i;
-      if (e >= N) break;
-      const uint32_t key = order_key(scores[e]);
+  // chunk pass: a wave classifies 64 consecutive entries per step (coalesced);
+  // its ballot is two bitmap words; cut-bin entries become candidates in this
+  // block's own region of the candidate list (positions from an LDS counter, so
+  // no returning global atomic stalls the wave)
+  __shared__ uint32_t nc_s;
+  if (threadIdx.x == 0) nc_s = 0;
+  __syncthreads();
+  uint2* cand_blk = cand + (size_t)blockIdx.x * kSelChunk;
+  const int c0 = blockIdx.x * kSelChunk;
+  const int c1 = min(N, c0 + kSelChunk);
+  constexpr int kUnroll = kSelChunk / 256;  // one round of loads per wave
+  for (int base = c0 + wave * 64 * kUnroll; base < c1; base += 4 * 64 * kUnroll) {
+    float sc[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int e = base + 64 * u + lane;
+      sc[u] = scores[e < c1 ? e : c0];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int e0 = base + 64 * u;
+      if (e0 >= c1) break;
+      const int e = e0 + lane;
+      const bool in = e < c1;
+      const uint32_t key = order_key(sc[u]);
       const int bin = (int)(key >> 20);
-      if (bin > cut) bits |= 1u << i;
-      else if (bin == cut) {
-        const uint32_t pos = atomicAdd(&ctr[0], 1u);
-        cand[pos] = make_uint2(key, (uint32_t)e);
+      const uint64_t selm = __ballot(in && bin > cut);
+      const uint64_t cm = __ballot(in && bin == cut);
+      if (lane == 0) bitmap[e0 >> 5] = (uint32_t)selm;
+      if (lane == 1 && e0 + 32 < N) bitmap[(e0 >> 5) + 1] = (uint32_t)(selm >> 32);
+      if (cm) {
+        uint32_t basepos = 0;
+        if (lane == 0) basepos = atomicAdd(&nc_s, (uint32_t)__popcll(cm));
+        basepos = __shfl(basepos, 0, 64);
+        if (in && bin == cut) {
+          const uint32_t rank = (uint32_t)__popcll(cm & ((1ull << lane) - 1ull));
+          cand_blk[basepos + rank] = make_uint2(key, (uint32_t)e);
+        }
       }
     }
-    bitmap[e0 >> 5] = bits;
   }
+  __syncthreads();
+  uint32_t* ccount = reinterpret_cast<uint32_t*>(a.ws + a.lay.cand_counts) + (size_t)b * (n_pad / kSelChunk);
+  if (threadIdx.x == 0) ccount[blockIdx.x] = nc_s;
   __threadfence();
   __syncthreads();
   __shared__ int last_s;
@@ -327,20 +552,87 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
   if (!last_s) return;
   __threadfence();
 
-  // ---- last block of this sequence: resolve the cut bin
-  const uint32_t nc = __hip_atomic_load(&ctr[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // ---- last block of this sequence: resolve the cut bin.  The candidates of
+  // all G blocks are first staged in LDS (one batched pass), unless there are
+  // too many, in which case the passes below read them from the regions.
+  __shared__ uint32_t pre_s[kMaxSelBlocks + 1];
+  __shared__ uint2 cl_s[kCandLds];
+  {
+    uint32_t v = 0;
+    const int per = (G + kSelThreads - 1) / kSelThreads;  // counts per thread, contiguous
+    uint32_t loc[kMaxSelBlocks / kSelThreads];
+#pragma unroll
+    for (int u = 0; u < kMaxSelBlocks / kSelThreads; ++u) {
+      const int j = threadIdx.x * per + u;
+      loc[u] = (u < per && j < G) ? ccount[j] : 0u;
+      v += loc[u];
+    }
+    uint32_t tot;
+    uint32_t run = block_excl_scan(v, tmp, tot);
+#pragma unroll
+    for (int u = 0; u < kMaxSelBlocks / kSelThreads; ++u) {
+      const int j = threadIdx.x * per + u;
+      if (u < per && j < G) pre_s[j] = run;
+      run += loc[u];
+    }
+    if (threadIdx.x == 0) pre_s[G] = tot;
+    __syncthreads();
+  }
+  const uint32_t nc = pre_s[G];
+  const bool in_lds = nc <= (uint32_t)kCandLds;
+  if (in_lds) {
+    // flat candidate i lives in region j with pre_s[j] <= i < pre_s[j+1]
+    constexpr int U = 8;
+    for (uint32_t i0 = threadIdx.x; i0 < nc; i0 += U * kSelThreads) {
+      uint2 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = i0 + u * kSelThreads;
+        int lo = 0, hi = G - 1;  // last region with pre_s[j] <= i
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (pre_s[mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        v[u] = i < nc ? cand[(size_t)lo * kSelChunk + (i - pre_s[lo])] : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = i0 + u * kSelThreads;
+        if (i < nc) cl_s[i] = v[u];
+      }
+    }
+    __syncthreads();
+  }
+  // visit every candidate: f(key, index)
+  auto for_cands = [&](auto&& f) {
+    if (in_lds) {
+      for (uint32_t i = threadIdx.x; i < nc; i += kSelThreads) {
+        const uint2 cd = cl_s[i];
+        f(cd.x, cd.y);
+      }
+    } else {
+      for (int j = 0; j < G; ++j) {
+        const uint2* cb = cand + (size_t)j * kSelChunk;
+        const uint32_t n = pre_s[j + 1] - pre_s[j];
+        for (uint32_t i = threadIdx.x; i < n; i += kSelThreads) {
+          const uint2 cd = cb[i];
+          f(cd.x, cd.y);
+        }
+      }
+    }
+  };
   uint32_t need = (uint32_t)k - above;  // 1 .. nc
-  uint32_t T = 0xFFFFFFFFu;             // selected: key > T, or key == T and index <= X
-  int X = -1;
-  if (need < nc) {
+  const bool take_all = need >= nc;
+  uint32_t T = 0u;  // when !take_all: selected = key > T, or key == T and index <= X
+  int X = 0x7FFFFFFF;
+  if (!take_all) {
     uint32_t prefix = (uint32_t)cut << 20, mask = 0xFFF00000u;
     for (int shift = 10; shift >= 0; shift -= 10) {
       for (int i = threadIdx.x; i < 1024; i += kSelThreads) h_s[i] = 0;
       __syncthreads();
-      for (uint32_t i = threadIdx.x; i < nc; i += kSelThreads) {
-        const uint32_t key = cand[i].x;
+      for_cands([&](uint32_t key, uint32_t) {
         if ((key & mask) == prefix) atomicAdd(&h_s[(key >> shift) & 1023u], 1u);
-      }
+      });
       __syncthreads();
       int c2;
       uint32_t ab2;
@@ -348,81 +640,130 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
       need -= ab2;
       prefix |= (uint32_t)c2 << shift;
       mask |= 1023u << shift;
-      __syncthreads();
     }
-    T = prefix;  // exact cut key; `need` entries with key == T are still to take
-    // ties at T: keep the `need` lowest indices (binary search on the index bound)
-    int lo = 0, hi = N - 1;
-    while (lo < hi) {
-      const int mid = lo + (hi - lo) / 2;
-      uint32_t c = 0;
-      for (uint32_t i = threadIdx.x; i < nc; i += kSelThreads) {
-        const uint2 cd = cand[i];
-        c += (cd.x == T && (int)cd.y <= mid) ? 1u : 0u;
+    T = prefix;  // exact cut key; `need` of the entries with key == T are taken
+    const uint32_t ties = h_s[T & 1023u];
+    if (need < ties) {
+      // keep the `need` lowest indices among the ties (binary search on the index bound)
+      int lo = 0, hi = N - 1;
+      while (lo < hi) {
+        const int mid = lo + (hi - lo) / 2;
+        uint32_t cnt = 0;
+        for_cands([&](uint32_t key, uint32_t e) { cnt += (key == T && (int)e <= mid) ? 1u : 0u; });
+        uint32_t tot;
+        (void)block_excl_scan(cnt, tmp, tot);
+        if (tot >= need) hi = mid; else lo = mid + 1;
       }
-      uint32_t tot;
-      (void)block_excl_scan(c, tmp, tot);
-      if (tot >= need) hi = mid; else lo = mid + 1;
+      X = lo;
     }
-    X = lo;
   }
-  for (uint32_t i = threadIdx.x; i < nc; i += kSelThreads) {
-    const uint2 cd = cand[i];
-    const bool take = (T == 0xFFFFFFFFu && X < 0) ? true : (cd.x > T || (cd.x == T && (int)cd.y <= X));
-    if (take) atomicOr(&bitmap[cd.y >> 5], 1u << (cd.y & 31));
-  }
+  for_cands([&](uint32_t key, uint32_t e) {
+    if (take_all || key > T || (key == T && (int)e <= X)) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+  });
   __threadfence();
   __syncthreads();
 
-  // ---- ascending compaction of the bitmap; words are zeroed as they are read
+  // ---- ascending compaction: each wave owns a contiguous quarter of the words;
+  // a lane takes 8 consecutive words a round (loads batched), wave prefix sums
+  // of the popcounts give each lane its output position
+  constexpr int WPL = 8;  // words per lane per round
   const int W = (N + 31) / 32;
-  const int per = (W + kSelThreads - 1) / kSelThreads;
-  const int w0 = min(W, threadIdx.x * per), w1 = min(W, w0 + per);
+  const int per_wave = (W + 3) / 4;
+  const int w0 = min(W, wave * per_wave), w1 = min(W, w0 + per_wave);
   uint32_t cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += __popc(__hip_atomic_load(&bitmap[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  uint32_t total;
-  uint32_t off = block_excl_scan(cnt, tmp, total);
-  for (int w = w0; w < w1; ++w) {
-    uint32_t bits = __hip_atomic_load(&bitmap[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bitmap[w] = 0u;
-    while (bits) {
-      const int bit = __ffs(bits) - 1;
-      bits &= bits - 1;
-      if (off < (uint32_t)k) out[off] = w * 32 + bit;
-      ++off;
-    }
+  for (int wb = w0 + lane * WPL; wb < w1; wb += 64 * WPL) {
+    uint32_t v[WPL];
+#pragma unroll
+    for (int u = 0; u < WPL; ++u) v[u] = wb + u < w1 ? bitmap[wb + u] : 0u;
+#pragma unroll
+    for (int u = 0; u < WPL; ++u) cnt += __popc(v[u]);
   }
-  for (int i = (int)total + threadIdx.x; i < k; i += kSelThreads) out[i] = -1;  // only if fewer (not expected)
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+  if (lane == 0) tmp[wave] = cnt;
+  __syncthreads();
+  uint32_t off = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kSelThreads / 64; ++i) {
+    if (i < wave) off += tmp[i];
+    total += tmp[i];
+  }
+  __syncthreads();
+  for (int base = w0; base < w1; base += 64 * WPL) {
+    const int wb = base + lane * WPL;
+    uint32_t v[WPL];
+    uint32_t pc = 0;
+#pragma unroll
+    for (int u = 0; u < WPL; ++u) {
+      v[u] = wb + u < w1 ? bitmap[wb + u] : 0u;
+      pc += __popc(v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < WPL; ++u)
+      if (wb + u < w1) bitmap[wb + u] = 0u;
+    uint32_t incl = pc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    uint32_t pos = off + incl - pc;
+#pragma unroll
+    for (int u = 0; u < WPL; ++u) {
+      uint32_t bits = v[u];
+      while (bits) {
+        const int bit = __ffs(bits) - 1;
+        bits &= bits - 1;
+        if (pos < (uint32_t)k) out[pos] = (wb + u) * 32 + bit;
+        ++pos;
+      }
+    }
+    off += __shfl(incl, 63, 64);
+  }
+  for (int i = (int)total + threadIdx.x; i < k; i += kSelThreads) out[i] = -1;  // fewer than k: not expected
   if (threadIdx.x == 0) a.out_n[b] = (int)min(total, (uint32_t)k);
-  // ---- leave the workspace zeroed
+  // ---- leave the workspace ready for the next call
   for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = 0u;
-  if (threadIdx.x == 0) { ctr[0] = 0u; ctr[1] = 0u; }
+  if (threadIdx.x == 0) ctr[1] = 0u;
+}
+
+template <int KDT, int DI>
+static void launch_score_one(const IndexerArgs& a, hipStream_t s) {
+  if (a.keys.epp == 64) {
+    const int np = (a.lay.n_max + 63) / 64;
+    const dim3 grid((np + kPagesPerScoreBlock - 1) / kPagesPerScoreBlock, a.B);
+    hipLaunchKernelGGL((score_pages_kernel<KDT, DI>), grid, dim3(kScoreThreads), 0, s, a);
+  } else {
+    const dim3 grid((a.lay.n_max + kScoreChunk - 1) / kScoreChunk, a.B);
+    hipLaunchKernelGGL((score_kernel<KDT, DI>), grid, dim3(kScoreThreads), 0, s, a);
+  }
 }
 
 template <int KDT>
-static hipError_t launch_score_dt(const IndexerArgs& a, dim3 grid, hipStream_t s) {
+static hipError_t launch_score_dt(const IndexerArgs& a, hipStream_t s) {
   switch (a.keys.dim) {
-    case 32: hipLaunchKernelGGL((score_kernel<KDT, 32>), grid, dim3(kScoreThreads), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((score_kernel<KDT, 64>), grid, dim3(kScoreThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((score_kernel<KDT, 128>), grid, dim3(kScoreThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((score_kernel<KDT, 256>), grid, dim3(kScoreThreads), 0, s, a); break;
+    case 32: launch_score_one<KDT, 32>(a, s); break;
+    case 64: launch_score_one<KDT, 64>(a, s); break;
+    case 128: launch_score_one<KDT, 128>(a, s); break;
+    default: launch_score_one<KDT, 256>(a, s); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
-  const int n_max = a.lay.n_max;
-  if (a.B == 0) return hipSuccess;
-  if (n_max > 0) {
-    const dim3 grid((n_max + kScoreChunk - 1) / kScoreChunk, a.B);
-    hipError_t e;
-    switch (a.keys.dtype) {
-      case HCA_FP8_E4M3: e = launch_score_dt<HCA_FP8_E4M3>(a, grid, s); break;
-      case HCA_FP4_E2M1: e = launch_score_dt<HCA_FP4_E2M1>(a, grid, s); break;
-      default: e = launch_score_dt<HCA_BF16>(a, grid, s); break;
-    }
-    if (e != hipSuccess) return e;
+hipError_t launch_indexer_score(const IndexerArgs& a, hipStream_t s) {
+  if (a.B == 0 || a.lay.n_max == 0) return hipSuccess;
+  switch (a.keys.dtype) {
+    case HCA_FP8_E4M3: return launch_score_dt<HCA_FP8_E4M3>(a, s);
+    case HCA_FP4_E2M1: return launch_score_dt<HCA_FP4_E2M1>(a, s);
+    default: return launch_score_dt<HCA_BF16>(a, s);
   }
+}
+
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  const hipError_t e = launch_indexer_score(a, s);
+  if (e != hipSuccess) return e;
+  const int n_max = a.lay.n_max;
   const int gsel = n_max > 0 ? (n_max + kSelChunk - 1) / kSelChunk : 1;
   const int gk = (a.k + kSelChunk - 1) / kSelChunk;
   hipLaunchKernelGGL(select_kernel, dim3(gsel > gk ? gsel : gk, a.B), dim3(kSelThreads), 0, s, a);

@@ -19,7 +19,29 @@ constexpr int kQThreads = 256;
 
 __device__ __forceinline__ bool page_ok(int phys, int num_pages) { return phys >= 0 && phys < num_pages; }
 
-__global__ __launch_bounds__(kQThreads) void quantize_fp8_kernel(QuantArgs a) {
+// fp8 pages: the page's fp32 rows are held in registers (up to kF8Regs float4
+// per thread, all loads in flight at once), the amax is reduced over the block,
+// and the codes are written from the registers.  Larger pages take two passes.
+constexpr int kF8Threads = 1024;
+constexpr int kF8Regs = 16;
+
+__device__ __forceinline__ uint32_t encode4_fp8(const f32x4 v, float s) {
+  return (uint32_t)e4m3_encode(v[0] / s) | ((uint32_t)e4m3_encode(v[1] / s) << 8) |
+         ((uint32_t)e4m3_encode(v[2] / s) << 16) | ((uint32_t)e4m3_encode(v[3] / s) << 24);
+}
+
+__device__ __forceinline__ float block_max_1024(float v, float* red) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kF8Threads / 64; ++i) r = fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kF8Threads) void quantize_fp8_kernel(QuantArgs a) {
   const int b = blockIdx.y;
   const int epp = a.dst.epp, dim = a.dst.dim;
   const int n = clampi(a.ne[b], 0, a.max_ne);
@@ -27,7 +49,8 @@ __global__ __launch_bounds__(kQThreads) void quantize_fp8_kernel(QuantArgs a) {
   const int npages = (n + epp - 1) / epp;
   uint8_t* codes = reinterpret_cast<uint8_t*>(a.dst.codes);
   float* scales = reinterpret_cast<float*>(a.dst.scales);
-  __shared__ float red_s[kQThreads / 64];
+  __shared__ float red_s[kF8Threads / 64];
+  const int tot4 = epp * dim / 4;
   for (int pg = blockIdx.x; pg < npages; pg += gridDim.x) {
     const int lb = E0 / epp + pg;
     if (lb < 0 || lb >= a.bts) continue;
@@ -36,29 +59,58 @@ __global__ __launch_bounds__(kQThreads) void quantize_fp8_kernel(QuantArgs a) {
     const int rows = min(epp, n - pg * epp);
     const int nv4 = rows * dim / 4;  // valid float4 groups (dim % 4 == 0)
     const f32x4* src = reinterpret_cast<const f32x4*>(a.src + (int64_t)b * a.ss + (int64_t)pg * epp * dim);
-    float amax = 0.0f;
-    for (int i = threadIdx.x; i < nv4; i += kQThreads) {
-      const f32x4 v = src[i];
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-    }
-    amax = wave_max(amax);
-    if ((threadIdx.x & 63) == 0) red_s[threadIdx.x >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
-    __syncthreads();
-    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
     uint32_t* dst = reinterpret_cast<uint32_t*>(codes + (int64_t)phys * epp * dim);
-    const int tot4 = epp * dim / 4;
-    for (int i = threadIdx.x; i < tot4; i += kQThreads) {
-      uint32_t word = 0;
-      if (i < nv4) {
-        const f32x4 v = src[i];
-        word = (uint32_t)e4m3_encode(v[0] / s) | ((uint32_t)e4m3_encode(v[1] / s) << 8) |
-               ((uint32_t)e4m3_encode(v[2] / s) << 16) | ((uint32_t)e4m3_encode(v[3] / s) << 24);
+    if (tot4 <= kF8Threads * kF8Regs) {
+      f32x4 v[kF8Regs];
+      float amax = 0.0f;
+#pragma unroll
+      for (int r = 0; r < kF8Regs; ++r) {
+        const int i = threadIdx.x + r * kF8Threads;
+        v[r] = i < nv4 ? src[i] : f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      dst[i] = word;
+#pragma unroll
+      for (int r = 0; r < kF8Regs; ++r)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[r][0]), fabsf(v[r][1])), fmaxf(fabsf(v[r][2]), fabsf(v[r][3]))));
+      amax = block_max_1024(amax, red_s);
+      const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+#pragma unroll
+      for (int r = 0; r < kF8Regs; ++r) {
+        const int i = threadIdx.x + r * kF8Threads;
+        if (i < tot4) dst[i] = i < nv4 ? encode4_fp8(v[r], s) : 0u;
+      }
+      if (threadIdx.x == 0) scales[phys] = s;
+    } else {
+      // two passes, 8 loads in flight per thread; the second pass re-reads from L2
+      constexpr int U = 8;
+      float amax = 0.0f;
+      for (int i0 = threadIdx.x; i0 < nv4; i0 += U * kF8Threads) {
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * kF8Threads;
+          v[u] = i < nv4 ? src[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3]))));
+      }
+      amax = block_max_1024(amax, red_s);
+      const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+      for (int i0 = threadIdx.x; i0 < tot4; i0 += U * kF8Threads) {
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * kF8Threads;
+          v[u] = i < nv4 ? src[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * kF8Threads;
+          if (i < tot4) dst[i] = i < nv4 ? encode4_fp8(v[u], s) : 0u;
+        }
+      }
+      if (threadIdx.x == 0) scales[phys] = s;
     }
-    if (threadIdx.x == 0) scales[phys] = s;
   }
 }
 
@@ -150,7 +202,7 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   const int gx = pages_max > 8192 ? 8192 : pages_max;
   const dim3 grid(gx, a.B);
   switch (a.dst.dtype) {
-    case HCA_FP8_E4M3: hipLaunchKernelGGL(quantize_fp8_kernel, grid, dim3(kQThreads), 0, s, a); break;
+    case HCA_FP8_E4M3: hipLaunchKernelGGL(quantize_fp8_kernel, grid, dim3(kF8Threads), 0, s, a); break;
     case HCA_FP4_E2M1: hipLaunchKernelGGL(quantize_fp4_kernel, grid, dim3(kQThreads), 0, s, a); break;
     default: hipLaunchKernelGGL(quantize_bf16_kernel, grid, dim3(kQThreads), 0, s, a); break;
   }

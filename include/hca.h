@@ -160,11 +160,12 @@ hca_status kv_quantize_page(const float* src, int64_t src_stride_b, const int32_
  *   q_idx      bf16 [B][HI][idx_keys.dim];  head_w float [B][HI]
  *   HI         1 .. 16;  idx_keys.dim in {32, 64, 128, 256};  epp = 256/m
  *   seq_lens   int32 [B] (device), clamped to [0, max_seq_len]
- *   k          1 .. 8192
+ *   k          1 .. 8192; at most 2^21 entries per sequence (ceil(max_seq_len/m))
  *   ws         workspace of indexer_topk_workspace(...) bytes.  It must be
  *              zero-filled before its first use; every successful call leaves
- *              it zero-filled again (re-zero it after a failed call).
- *              Calls that overlap in time must use different workspaces.
+ *              its histogram and counters zeroed again, so it can be reused
+ *              as is (re-zero it after a failed call).  Calls that overlap in
+ *              time must use different workspaces.
  */
 size_t indexer_topk_workspace(int32_t B, int32_t max_seq_len, int32_t m, int32_t k);
 hca_status indexer_topk(const uint16_t* q_idx, const float* head_w, int32_t HI,
@@ -193,11 +194,12 @@ hca_status indexer_topk(const uint16_t* q_idx, const float* head_w, int32_t HI,
  *
  *   q          bf16 [B][H][kv.dim], unrotated;  H in 1 .. 128
  *   kv.dim     in {64, 128, 256, 512}; win.dim == kv.dim; win.epp == 256
- *   kv, win    dtype HCA_FP8_E4M3 or HCA_BF16
+ *   kv, win    dtype HCA_FP8_E4M3 or HCA_BF16, the same for both pools
  *   sel_idx    int32 [B][k] or NULL;  sel_n int32 [B] (required with sel_idx)
  *   window     0 .. 256 (0: no window; win and win_block_table may be NULL)
  *   out        float [B][H][kv.dim];  lse float [B][H] or NULL
- *   ws         workspace of paged_hybrid_decode_workspace(...) bytes; its
+ *   ws         workspace of paged_hybrid_decode_workspace(B, H, d, max_seq_len,
+ *              m, window, k) bytes, with k = 0 when sel_idx will be NULL; its
  *              contents on entry do not matter.
  */
 size_t paged_hybrid_decode_workspace(int32_t B, int32_t H, int32_t d, int32_t max_seq_len,

@@ -1,5 +1,6 @@
 /*
- * hca_testing.h -- checking hooks of libhca (not part of the decode path).
+ * hca_testing.h -- checking and measurement hooks of libhca (not part of the
+ * decode path).
  *
  * The host hooks run the very encoder functions the kernels use, compiled for
  * the host, so their rounding can be checked exhaustively on a machine without
@@ -35,6 +36,14 @@ hca_status hca_probe_decode(const uint8_t* codes, float* out, int32_t n, int32_t
  * storing its accumulator as D[4(l/16)+i][l%16].  A, B: 16-bit patterns,
  * row-major; D: fp32 row-major; all device. */
 hca_status hca_probe_mfma(const uint16_t* A, const uint16_t* B, float* D, int32_t kind, void* stream);
+
+/* Measurement: the scoring kernel of indexer_topk alone, same arguments and
+ * launch configuration, no selection.  It accumulates into the workspace's
+ * score histogram, so use a workspace reserved for it (never one that
+ * indexer_topk will use afterwards).  Scores land in the workspace. */
+hca_status hca_indexer_score(const uint16_t* q_idx, const float* head_w, int32_t HI, hca_paged_cache idx_keys,
+                             const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens, int32_t B,
+                             int32_t max_seq_len, int32_t m, int32_t k, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }
