@@ -13,8 +13,10 @@ and reported on its own.
 A step is one decode step of the whole stack for the batch: per layer the
 decode update (re-fold of the open group and re-quantization of its page, the
 window insert of the new token, the open indexer page), then indexer_topk (c4a)
-and paged_hybrid_decode.  The step is captured once in a HIP graph and
-replayed; `value` is decode tokens/s = B / step time.
+and paged_hybrid_decode.  The three update chains are independent and run on
+separate streams that join before the layer's attention; layers stay in
+order.  The step is captured once in a HIP graph and replayed; `value` is
+decode tokens/s = B / step time.
 
 Also reported: the roofline of the dominant kernel (the indexer scoring
 kernel: it streams the fp4 keys, ~77% of a step's bytes), measured with HIP
@@ -187,31 +189,51 @@ def build_state(w, n_layers, torch, hca, gen, log):
         torch.cuda.synchronize()
         if li % 10 == 0 or li == n_layers - 1:
             log(f"prefilled layer {li + 1}/{n_layers} ({kind.name})")
-    shared = dict(table=table, wtable=wtable, lens=lens)
+    # decode-update workspaces (one per side stream) and the side streams (default priority)
+    wq_main = max(hca.kv_quantize_page_workspace(B, l.stage.shape[1], l.kv) for l in layers)
+    wq_win = max(hca.kv_quantize_page_workspace(B, l.wstage.shape[1], l.win) for l in layers)
+    shared = dict(table=table, wtable=wtable, lens=lens, wsq_main=hca.workspace(wq_main),
+                  wsq_win=hca.workspace(wq_win), streams=(torch.cuda.Stream(), torch.cuda.Stream()))
     return layers, shared, dict(ms=pre_ms, bytes=pre_bytes)
 
 
 def decode_step(w, layers, shared, ws_idx, ws_att, hca, update=True, attend=True):
+    """One decode step of the stack.  Per layer, the three independent parts of
+    the update run on their own streams (window insert; open-group re-fold and
+    its page; the open indexer page, then the indexer, on the main stream) and
+    join before the layer's attention, which the next layer waits for."""
+    import torch
     L, W = w.L, w.window
     table, wtable, lens = shared["table"], shared["wtable"], shared["lens"]
+    s_main = torch.cuda.current_stream()
+    s_win, s_fold = shared["streams"]
+    wsq_main, wsq_win = shared["wsq_main"], shared["wsq_win"]
     scale = 1.0 / math.sqrt(w.d)
     for lay in layers:
         kind = lay.kind
         m = kind.m
         if update:
-            # open group re-fold -> its slot in the open page staging -> re-quantize the open page
-            hca.kv_compress(lay.ring_x, lay.ring_z, lay.beta, lay.pos0, lay.ntok, m, w.theta,
-                            lay.stage[:, lay.slot:], m)
-            hca.kv_quantize_page(lay.stage, lay.e0, lay.ne, lay.stage.shape[1], table, lay.kv)
-            # window insert of the newest token
-            hca.kv_compress(lay.x_last, lay.z_last, lay.zero1, lay.wpos0, lay.one, 1, w.theta,
-                            lay.wstage[:, lay.wslot:], 1)
-            hca.kv_quantize_page(lay.wstage, lay.we0, lay.wne, lay.wstage.shape[1], wtable, lay.win)
+            s_win.wait_stream(s_main)
+            s_fold.wait_stream(s_main)
+            with torch.cuda.stream(s_win):
+                # window insert of the newest token, then its page
+                hca.kv_compress(lay.x_last, lay.z_last, lay.zero1, lay.wpos0, lay.one, 1, w.theta,
+                                lay.wstage[:, lay.wslot:], 1)
+                hca.kv_quantize_page(lay.wstage, lay.we0, lay.wne, lay.wstage.shape[1], wtable, lay.win, ws=wsq_win)
+            with torch.cuda.stream(s_fold):
+                # open group re-fold -> its slot in the open page staging -> re-quantize the open page
+                hca.kv_compress(lay.ring_x, lay.ring_z, lay.beta, lay.pos0, lay.ntok, m, w.theta,
+                                lay.stage[:, lay.slot:], m)
+                hca.kv_quantize_page(lay.stage, lay.e0, lay.ne, lay.stage.shape[1], table, lay.kv, ws=wsq_main)
             if kind.topk is not None:
                 hca.kv_quantize_page(lay.istage, lay.e0, lay.ne, lay.istage.shape[1], table, lay.idx)
+        if attend and kind.topk is not None:
+            hca.indexer_topk(lay.qi, lay.wi, lay.idx, table, lens, L, m, kind.topk, lay.sel, lay.sel_n, ws_idx)
+        if update:
+            s_main.wait_stream(s_win)
+            s_main.wait_stream(s_fold)
         if attend:
             if kind.topk is not None:
-                hca.indexer_topk(lay.qi, lay.wi, lay.idx, table, lens, L, m, kind.topk, lay.sel, lay.sel_n, ws_idx)
                 hca.paged_hybrid_decode(lay.q, lay.kv, table, lay.win, wtable, lens, L, m, W, lay.sel, lay.sel_n,
                                         scale, w.theta, lay.out, lay.lse, ws_att[kind.name])
             else:

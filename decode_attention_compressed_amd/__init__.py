@@ -27,7 +27,8 @@ STATUS = {0: "HCA_OK", 1: "HCA_ERR_INVALID", 2: "HCA_ERR_UNSUPPORTED", 3: "HCA_E
 
 #: every symbol the C headers declare (include/hca.h and include/hca_testing.h)
 EXPORTS = (
-    "hca_status_string", "hca_version", "kv_compress", "kv_quantize_page", "indexer_topk_workspace",
+    "hca_status_string", "hca_version", "kv_compress", "kv_quantize_page_workspace", "kv_quantize_page",
+    "indexer_topk_workspace",
     "indexer_topk", "paged_hybrid_decode_workspace", "paged_hybrid_decode", "kv_gather",
     "hca_host_e4m3_encode", "hca_host_e2m1_encode", "hca_host_bf16_encode", "hca_probe_decode", "hca_probe_mfma",
     "hca_indexer_score",
@@ -61,7 +62,9 @@ def lib() -> ctypes.CDLL:
         L.hca_status_string.argtypes = [ctypes.c_int]
         L.hca_version.restype = ctypes.c_char_p
         L.kv_compress.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _I64, _P]
-        L.kv_quantize_page.argtypes = [_P, _I64, _P, _P, _I32, _I32, _P, _I32, CPagedCache, _P]
+        L.kv_quantize_page_workspace.argtypes = [_I32, _I32, CPagedCache]
+        L.kv_quantize_page_workspace.restype = _SZ
+        L.kv_quantize_page.argtypes = [_P, _I64, _P, _P, _I32, _I32, _P, _I32, CPagedCache, _P, _SZ, _P]
         L.indexer_topk_workspace.argtypes = [_I32, _I32, _I32, _I32]
         L.indexer_topk_workspace.restype = _SZ
         L.indexer_topk.argtypes = [_P, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]
@@ -78,7 +81,7 @@ def lib() -> ctypes.CDLL:
         L.hca_indexer_score.argtypes = [_P, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P]
         for name in EXPORTS:
             if name not in ("hca_status_string", "hca_version", "indexer_topk_workspace",
-                            "paged_hybrid_decode_workspace"):
+                            "paged_hybrid_decode_workspace", "kv_quantize_page_workspace"):
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -148,11 +151,17 @@ def kv_compress(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, 
                              _stream(stream)), "kv_compress")
 
 
-def kv_quantize_page(src, e0, ne, max_ne: int, block_table, dst: PagedCache, stream=None):
-    """src f32 [B, rows, dim]; e0, ne int32 [B]; block_table int32 [B, nb]."""
+def kv_quantize_page_workspace(B: int, max_ne: int, dst: PagedCache) -> int:
+    return int(lib().kv_quantize_page_workspace(B, max_ne, dst.c()))
+
+
+def kv_quantize_page(src, e0, ne, max_ne: int, block_table, dst: PagedCache, ws=None, stream=None):
+    """src f32 [B, rows, dim]; e0, ne int32 [B]; block_table int32 [B, nb];
+    ws: None or a uint8 tensor of kv_quantize_page_workspace(...) bytes (fp8 pages split over blocks)."""
     B = src.shape[0]
+    wp, wn = (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
     _check(lib().kv_quantize_page(_ptr(src), src.stride(0), _ptr(e0), _ptr(ne), B, max_ne, _ptr(block_table),
-                                  block_table.stride(0), dst.c(), _stream(stream)), "kv_quantize_page")
+                                  block_table.stride(0), dst.c(), wp, wn, _stream(stream)), "kv_quantize_page")
 
 
 def indexer_topk_workspace(B: int, max_seq_len: int, m: int, k: int) -> int:

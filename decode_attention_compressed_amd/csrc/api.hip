@@ -64,17 +64,28 @@ hca_status kv_compress(const uint16_t* x, int64_t x_stride_b, const float* gate_
   return from_hip(launch_compress(a, (hipStream_t)stream));
 }
 
+size_t kv_quantize_page_workspace(int32_t B, int32_t max_ne, hca_paged_cache dst) {
+  if (B < 0 || max_ne < 0 || !cache_ok(dst)) return 0;
+  return quantize_ws_bytes(B, max_ne, dst);
+}
+
 hca_status kv_quantize_page(const float* src, int64_t src_stride_b, const int32_t* e0, const int32_t* ne, int32_t B,
                             int32_t max_ne, const int32_t* block_table, int32_t bt_stride, hca_paged_cache dst,
-                            void* stream) {
+                            void* ws, size_t ws_bytes, void* stream) {
   if (B < 0 || max_ne < 0 || bt_stride < 1) return HCA_ERR_INVALID;
   if (!cache_ok(dst)) return HCA_ERR_INVALID;
   if (B == 0 || max_ne == 0) return HCA_OK;
   if (!src || !e0 || !ne || !block_table) return HCA_ERR_INVALID;
   if (!aligned(src, 16) || src_stride_b % 4 != 0) return HCA_ERR_INVALID;
   if (B > 1 && src_stride_b < (int64_t)max_ne * dst.dim) return HCA_ERR_INVALID;
+  float* part = nullptr;
+  const size_t need = quantize_ws_bytes(B, max_ne, dst);
+  if (ws != nullptr && need > 0) {
+    if (ws_bytes < need || !aligned(ws, 16)) return HCA_ERR_INVALID;
+    part = static_cast<float*>(ws);
+  }
   QuantArgs a{src, src_stride_b, e0, ne, B, max_ne, block_table, bt_stride, dst};
-  return from_hip(launch_quantize(a, (hipStream_t)stream));
+  return from_hip(launch_quantize(a, part, (hipStream_t)stream));
 }
 
 size_t indexer_topk_workspace(int32_t B, int32_t max_seq_len, int32_t m, int32_t k) {

@@ -6,7 +6,8 @@
 // HBM-bound stream: each thread owns 8 consecutive dims (one 16-byte bf16
 // load per token) so a row of d dims is read by d/8 adjacent lanes in one
 // coalesced sweep.  Small m: a row-group of d/8 threads folds whole entries on
-// its own.  Large m: the 256 threads of a block share one entry, each
+// its own.  Large m: the 256 threads of a block share one entry (or, when
+// there are few entries, as in a decode step, one 64-dim slice of it), each
 // row-group folding a strided subset of its tokens, reduced through LDS.
 #include "hca_common.h"
 #include "hca_internal.h"
@@ -83,11 +84,21 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
     return;
   }
 
-  // large m: one entry per block iteration
+  // large m: a block folds one (entry, dim slice) at a time; its row groups
+  // take strided subsets of the group's tokens and are summed through LDS
+  const int DS = a.ds;                 // dims of a slice (divides d, multiple of 8)
+  const int nsl = a.d / DS;
+  const int TS = DS >> 3;              // threads across the slice
+  const int RS = kCompressThreads / TS;
+  const int ls = threadIdx.x % TS;
+  const int gs = threadIdx.x / TS;
   __shared__ float w_s[256];
   __shared__ float red_s[kCompressThreads];
-  extern __shared__ float acc_s[];                      // [RP][d]
-  for (int j = blockIdx.x; j < N; j += gridDim.x) {
+  extern __shared__ float acc_s[];     // [RS][DS]
+  const uint16_t* xs = a.x + (int64_t)b * a.xs + ls * 8;
+  for (int u = blockIdx.x; u < N * nsl; u += gridDim.x) {
+    const int j = u / nsl;
+    const int base = (u % nsl) * DS;
     const int t0 = j * m;
     const int r = min(m, n - t0);
     // softmax weights of the group's r slots
@@ -110,46 +121,57 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
       __syncthreads();
     }
     const float tot = red_s[0];
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (active) {
-      for (int i = gi; i < r; i += RP) {
+    if (gs < RS) {
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 4
+      for (int i = gs; i < r; i += RS) {
         float v[8];
-        load_bf16x8(xb + (int64_t)(t0 + i) * a.d, v);
+        load_bf16x8(xs + (int64_t)(t0 + i) * a.d + base, v);
         const float wi = w_s[i];
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[c] = fmaf(wi, v[c], acc[c]);
       }
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc_s[gi * a.d + li * 8 + c] = acc[c];
+      for (int c = 0; c < 8; ++c) acc_s[gs * DS + ls * 8 + c] = acc[c];
     }
     __syncthreads();
-    if (active && gi == 0) {
-      for (int g = 1; g < RP; ++g) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] += acc_s[g * a.d + li * 8 + c];
+    // one thread per dim pair of the slice: sum the row groups, normalise, rotate
+    const float inv_tot = 1.0f / tot;
+    const double pos = (double)p0 + (double)t0;
+    for (int t = threadIdx.x; t < DS / 2; t += kCompressThreads) {
+      float e0 = 0.0f, e1 = 0.0f;
+      for (int g = 0; g < RS; ++g) {
+        e0 += acc_s[g * DS + 2 * t];
+        e1 += acc_s[g * DS + 2 * t + 1];
       }
-      const float inv_tot = 1.0f / tot;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] *= inv_tot;
-      rope_store8(ob + (int64_t)j * a.d, acc, (double)p0 + (double)t0, inv);
+      e0 *= inv_tot;
+      e1 *= inv_tot;
+      float c, sn;
+      rope_cs(pos, rope_inv_freq(base / 2 + t, a.d, a.theta), c, sn);
+      float* o = a.out + (int64_t)b * a.os + (int64_t)j * a.d + base + 2 * t;
+      o[0] = e0 * c - e1 * sn;
+      o[1] = e0 * sn + e1 * c;
     }
     __syncthreads();
   }
 }
 
-hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
+hipError_t launch_compress(CompressArgs a, hipStream_t s) {
   const int n_max = (a.max_ntok + a.m - 1) / a.m;
   if (a.B == 0 || n_max == 0) return hipSuccess;
-  const int TD = a.d / 8;
-  const int RP = kCompressThreads / TD;
   int gx;
   size_t shm = 0;
+  a.ds = a.d;
   if (a.m <= kSmallM) {
+    const int RP = kCompressThreads / (a.d / 8);
     gx = (n_max + RP - 1) / RP;
     gx = gx > 2048 ? 2048 : gx;
   } else {
-    gx = n_max > 4096 ? 4096 : n_max;
-    shm = (size_t)RP * a.d * sizeof(float);
+    // few entries (a decode step's open group): cut the dims into 64-wide slices
+    if ((int64_t)n_max * a.B < 512 && a.d % 64 == 0) a.ds = 64;
+    const int64_t units = (int64_t)n_max * (a.d / a.ds);
+    gx = units > 4096 ? 4096 : (int)units;
+    shm = (size_t)(kCompressThreads / (a.ds / 8)) * a.ds * sizeof(float);
   }
   hipLaunchKernelGGL(compress_kernel, dim3(gx, a.B), dim3(kCompressThreads), shm, s, a);
   return hipGetLastError();

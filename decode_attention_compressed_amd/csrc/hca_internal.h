@@ -16,8 +16,9 @@ struct CompressArgs {
   int B, max_ntok, d, m;
   float theta;
   float* out; int64_t os;
+  int ds;  // dims per block slice (set by the launcher)
 };
-hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+hipError_t launch_compress(CompressArgs a, hipStream_t s);
 
 struct QuantArgs {
   const float* src; int64_t ss;
@@ -26,7 +27,9 @@ struct QuantArgs {
   const int32_t* bt; int bts;
   hca_paged_cache dst;
 };
-hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+// ws: NULL (one block per page) or quantize_ws_bytes(...) bytes of chunk partials
+size_t quantize_ws_bytes(int B, int max_ne, const hca_paged_cache& dst);
+hipError_t launch_quantize(const QuantArgs& a, float* ws, hipStream_t s);
 
 struct GatherArgs {
   hca_paged_cache src;

@@ -14,12 +14,13 @@
 // order key of every score lands in a 4096-bin LDS histogram that is added to
 // a per-sequence histogram in the workspace.
 //
-// Select kernel.  Every block re-derives the cut bin from the histogram, marks
+// Select.  Every chunk block re-derives the cut bin from the histogram, marks
 // the scores above it in a bitmap and appends the cut bin's entries as
-// candidates; the last block of a sequence (ticket counter) refines the cut
-// with two 10-bit radix passes over the candidates, breaks exact ties by the
-// lowest index, and compacts the bitmap into ascending indices.  It leaves the
-// histogram, counters and bitmap zeroed for the next call.
+// candidates; one block per sequence then refines the cut with two 10-bit
+// radix passes over the candidates, breaks exact ties by the lowest index and
+// marks the winners, and a last pass compacts the bitmap into ascending
+// indices.  The histogram is left zeroed for the next call; every other part
+// of the workspace is overwritten before it is read.
 #include "hca_common.h"
 #include "hca_internal.h"
 
@@ -469,11 +470,46 @@ __device__ void find_cut(const uint32_t* bins, int nb, uint32_t need, uint32_t* 
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
-  const int b = blockIdx.y;
+// Three launches per call, so that kernel boundaries order the passes (no
+// device-scope fences, which write back and invalidate the whole L2):
+//   select_chunk   (G blocks per sequence) entries whose 12-bit bin is above
+//                  the cut bin go straight into the bitmap; cut-bin entries
+//                  become (key, index) candidates in the block's region;
+//   select_resolve (one block per sequence) exact cut key and index bound
+//                  from the candidates (LDS radix passes), winners OR-ed into
+//                  the bitmap; resets the histogram for the next call;
+//   select_compact (one block per sequence) ascending compaction of the
+//                  bitmap into out_idx.
+// The chunk pass writes every bitmap word below N, so only the histogram has
+// to start at zero.
+struct SelView {
+  int N, G, n_pad;
+  const float* scores;
+  uint32_t* hist;
+  uint2* cand;
+  uint32_t* bitmap;
+  uint32_t* ctr;     // [0] cut bin, [1] count above the cut bin
+  uint32_t* ccount;  // candidates per chunk block
+};
+__device__ __forceinline__ SelView sel_view(const IndexerArgs& a, int b) {
+  SelView v;
   const int L = clampi(a.lens[b], 0, a.max_len);
-  const int N = (L + a.m - 1) / a.m;
-  const int k = a.k;
+  v.N = (L + a.m - 1) / a.m;
+  v.G = (v.N + kSelChunk - 1) / kSelChunk;
+  v.n_pad = ((a.lay.n_max + kSelChunk - 1) / kSelChunk) * kSelChunk;
+  v.scores = reinterpret_cast<const float*>(a.ws + a.lay.scores) + (size_t)b * v.n_pad;
+  v.hist = reinterpret_cast<uint32_t*>(a.ws + a.lay.hist) + (size_t)b * kHistBins;
+  v.cand = reinterpret_cast<uint2*>(a.ws + a.lay.cand) + (size_t)b * v.n_pad;
+  v.bitmap = reinterpret_cast<uint32_t*>(a.ws + a.lay.bitmap) + (size_t)b * (v.n_pad / 32);
+  v.ctr = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + (size_t)b * 4;
+  v.ccount = reinterpret_cast<uint32_t*>(a.ws + a.lay.cand_counts) + (size_t)b * (v.n_pad / kSelChunk);
+  return v;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(IndexerArgs a) {
+  const int b = blockIdx.y;
+  const SelView v = sel_view(a, b);
+  const int N = v.N, k = a.k;
   int32_t* out = a.out_idx + (int64_t)b * k;
   if (N <= k) {  // every entry is kept
     const int lo = blockIdx.x * kSelChunk, hi = min(N, lo + kSelChunk);
@@ -484,30 +520,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
     }
     return;
   }
-  const int G = (N + kSelChunk - 1) / kSelChunk;
-  if ((int)blockIdx.x >= G) return;
-  const int n_pad = ((a.lay.n_max + kSelChunk - 1) / kSelChunk) * kSelChunk;
-  const float* scores = reinterpret_cast<const float*>(a.ws + a.lay.scores) + (size_t)b * n_pad;
-  uint32_t* hist = reinterpret_cast<uint32_t*>(a.ws + a.lay.hist) + (size_t)b * kHistBins;
-  uint2* cand = reinterpret_cast<uint2*>(a.ws + a.lay.cand) + (size_t)b * n_pad;
-  uint32_t* bitmap = reinterpret_cast<uint32_t*>(a.ws + a.lay.bitmap) + (size_t)b * (n_pad / 32);
-  uint32_t* ctr = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + (size_t)b * 4;  // [0] candidates, [1] ticket
+  if ((int)blockIdx.x >= v.G) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-
   __shared__ uint32_t tmp[kSelThreads / 64];
-  __shared__ uint32_t h_s[1024];
   int cut;
   uint32_t above;
-  find_cut(hist, kHistBins, (uint32_t)k, tmp, cut, above);
-
-  // chunk pass: a wave classifies 64 consecutive entries per step (coalesced);
-  // its ballot is two bitmap words; cut-bin entries become candidates in this
-  // block's own region of the candidate list (positions from an LDS counter, so
-  // no returning global atomic stalls the wave)
+  find_cut(v.hist, kHistBins, (uint32_t)k, tmp, cut, above);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    v.ctr[0] = (uint32_t)cut;
+    v.ctr[1] = above;
+  }
+  // a wave classifies 64 consecutive entries per step (coalesced); its ballot
+  // is two bitmap words; cut-bin entries take positions from an LDS counter
+  // (no returning global atomic stalls the wave)
   __shared__ uint32_t nc_s;
   if (threadIdx.x == 0) nc_s = 0;
   __syncthreads();
-  uint2* cand_blk = cand + (size_t)blockIdx.x * kSelChunk;
+  uint2* cand_blk = v.cand + (size_t)blockIdx.x * kSelChunk;
   const int c0 = blockIdx.x * kSelChunk;
   const int c1 = min(N, c0 + kSelChunk);
   constexpr int kUnroll = kSelChunk / 256;  // one round of loads per wave
@@ -516,7 +545,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int e = base + 64 * u + lane;
-      sc[u] = scores[e < c1 ? e : c0];
+      sc[u] = v.scores[e < c1 ? e : c0];
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -528,8 +557,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
       const int bin = (int)(key >> 20);
       const uint64_t selm = __ballot(in && bin > cut);
       const uint64_t cm = __ballot(in && bin == cut);
-      if (lane == 0) bitmap[e0 >> 5] = (uint32_t)selm;
-      if (lane == 1 && e0 + 32 < N) bitmap[(e0 >> 5) + 1] = (uint32_t)(selm >> 32);
+      if (lane == 0) v.bitmap[e0 >> 5] = (uint32_t)selm;
+      if (lane == 1 && e0 + 32 < N) v.bitmap[(e0 >> 5) + 1] = (uint32_t)(selm >> 32);
       if (cm) {
         uint32_t basepos = 0;
         if (lane == 0) basepos = atomicAdd(&nc_s, (uint32_t)__popcll(cm));
@@ -542,33 +571,36 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
     }
   }
   __syncthreads();
-  uint32_t* ccount = reinterpret_cast<uint32_t*>(a.ws + a.lay.cand_counts) + (size_t)b * (n_pad / kSelChunk);
-  if (threadIdx.x == 0) ccount[blockIdx.x] = nc_s;
-  __threadfence();
-  __syncthreads();
-  __shared__ int last_s;
-  if (threadIdx.x == 0) last_s = (atomicAdd(&ctr[1], 1u) == (uint32_t)(G - 1));
-  __syncthreads();
-  if (!last_s) return;
-  __threadfence();
+  if (threadIdx.x == 0) v.ccount[blockIdx.x] = nc_s;
+}
 
-  // ---- last block of this sequence: resolve the cut bin.  The candidates of
-  // all G blocks are first staged in LDS (one batched pass), unless there are
-  // too many, in which case the passes below read them from the regions.
+__global__ __launch_bounds__(kSelThreads) void select_resolve_kernel(IndexerArgs a) {
+  const int b = blockIdx.x;
+  const SelView v = sel_view(a, b);
+  const int N = v.N, G = v.G, k = a.k;
+  // the histogram has been read by every chunk block: clear it for the next call
+  for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) v.hist[i] = 0u;
+  if (N <= k) return;
+  __shared__ uint32_t tmp[kSelThreads / 64];
+  __shared__ uint32_t h_s[1024];
+  const int cut = (int)v.ctr[0];
+  const uint32_t above = v.ctr[1];
+  // the candidates of all G chunk blocks are staged in LDS (one batched pass),
+  // unless there are too many, in which case the passes read their regions
   __shared__ uint32_t pre_s[kMaxSelBlocks + 1];
   __shared__ uint2 cl_s[kCandLds];
   {
-    uint32_t v = 0;
+    uint32_t cv = 0;
     const int per = (G + kSelThreads - 1) / kSelThreads;  // counts per thread, contiguous
     uint32_t loc[kMaxSelBlocks / kSelThreads];
 #pragma unroll
     for (int u = 0; u < kMaxSelBlocks / kSelThreads; ++u) {
       const int j = threadIdx.x * per + u;
-      loc[u] = (u < per && j < G) ? ccount[j] : 0u;
-      v += loc[u];
+      loc[u] = (u < per && j < G) ? v.ccount[j] : 0u;
+      cv += loc[u];
     }
     uint32_t tot;
-    uint32_t run = block_excl_scan(v, tmp, tot);
+    uint32_t run = block_excl_scan(cv, tmp, tot);
 #pragma unroll
     for (int u = 0; u < kMaxSelBlocks / kSelThreads; ++u) {
       const int j = threadIdx.x * per + u;
@@ -584,7 +616,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
     // flat candidate i lives in region j with pre_s[j] <= i < pre_s[j+1]
     constexpr int U = 8;
     for (uint32_t i0 = threadIdx.x; i0 < nc; i0 += U * kSelThreads) {
-      uint2 v[U];
+      uint2 cv[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t i = i0 + u * kSelThreads;
@@ -593,12 +625,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
           const int mid = (lo + hi + 1) >> 1;
           if (pre_s[mid] <= i) lo = mid; else hi = mid - 1;
         }
-        v[u] = i < nc ? cand[(size_t)lo * kSelChunk + (i - pre_s[lo])] : make_uint2(0u, 0u);
+        cv[u] = i < nc ? v.cand[(size_t)lo * kSelChunk + (i - pre_s[lo])] : make_uint2(0u, 0u);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t i = i0 + u * kSelThreads;
-        if (i < nc) cl_s[i] = v[u];
+        if (i < nc) cl_s[i] = cv[u];
       }
     }
     __syncthreads();
@@ -612,7 +644,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
       }
     } else {
       for (int j = 0; j < G; ++j) {
-        const uint2* cb = cand + (size_t)j * kSelChunk;
+        const uint2* cb = v.cand + (size_t)j * kSelChunk;
         const uint32_t n = pre_s[j + 1] - pre_s[j];
         for (uint32_t i = threadIdx.x; i < n; i += kSelThreads) {
           const uint2 cd = cb[i];
@@ -658,25 +690,33 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
     }
   }
   for_cands([&](uint32_t key, uint32_t e) {
-    if (take_all || key > T || (key == T && (int)e <= X)) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+    if (take_all || key > T || (key == T && (int)e <= X)) atomicOr(&v.bitmap[e >> 5], 1u << (e & 31));
   });
-  __threadfence();
-  __syncthreads();
+}
 
-  // ---- ascending compaction: each wave owns a contiguous quarter of the words;
-  // a lane takes 8 consecutive words a round (loads batched), wave prefix sums
-  // of the popcounts give each lane its output position
+__global__ __launch_bounds__(kSelThreads) void select_compact_kernel(IndexerArgs a) {
+  // each wave owns a contiguous quarter of the words; a lane takes 8
+  // consecutive words a round (loads batched), wave prefix sums of the
+  // popcounts give each lane its output position
+  const int b = blockIdx.x;
+  const SelView v = sel_view(a, b);
+  const int N = v.N, k = a.k;
+  if (N <= k) return;
+  int32_t* out = a.out_idx + (int64_t)b * k;
+  uint32_t* bitmap = v.bitmap;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ uint32_t tmp[kSelThreads / 64];
   constexpr int WPL = 8;  // words per lane per round
   const int W = (N + 31) / 32;
   const int per_wave = (W + 3) / 4;
   const int w0 = min(W, wave * per_wave), w1 = min(W, w0 + per_wave);
   uint32_t cnt = 0;
   for (int wb = w0 + lane * WPL; wb < w1; wb += 64 * WPL) {
-    uint32_t v[WPL];
+    uint32_t bw[WPL];
 #pragma unroll
-    for (int u = 0; u < WPL; ++u) v[u] = wb + u < w1 ? bitmap[wb + u] : 0u;
+    for (int u = 0; u < WPL; ++u) bw[u] = wb + u < w1 ? bitmap[wb + u] : 0u;
 #pragma unroll
-    for (int u = 0; u < WPL; ++u) cnt += __popc(v[u]);
+    for (int u = 0; u < WPL; ++u) cnt += __popc(bw[u]);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
@@ -691,16 +731,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
   __syncthreads();
   for (int base = w0; base < w1; base += 64 * WPL) {
     const int wb = base + lane * WPL;
-    uint32_t v[WPL];
+    uint32_t bw[WPL];
     uint32_t pc = 0;
 #pragma unroll
     for (int u = 0; u < WPL; ++u) {
-      v[u] = wb + u < w1 ? bitmap[wb + u] : 0u;
-      pc += __popc(v[u]);
+      bw[u] = wb + u < w1 ? bitmap[wb + u] : 0u;
+      pc += __popc(bw[u]);
     }
-#pragma unroll
-    for (int u = 0; u < WPL; ++u)
-      if (wb + u < w1) bitmap[wb + u] = 0u;
     uint32_t incl = pc;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -710,7 +747,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
     uint32_t pos = off + incl - pc;
 #pragma unroll
     for (int u = 0; u < WPL; ++u) {
-      uint32_t bits = v[u];
+      uint32_t bits = bw[u];
       while (bits) {
         const int bit = __ffs(bits) - 1;
         bits &= bits - 1;
@@ -722,9 +759,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(IndexerArgs a) {
   }
   for (int i = (int)total + threadIdx.x; i < k; i += kSelThreads) out[i] = -1;  // fewer than k: not expected
   if (threadIdx.x == 0) a.out_n[b] = (int)min(total, (uint32_t)k);
-  // ---- leave the workspace ready for the next call
-  for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = 0u;
-  if (threadIdx.x == 0) ctr[1] = 0u;
 }
 
 template <int KDT, int DI>
@@ -766,7 +800,9 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
   const int n_max = a.lay.n_max;
   const int gsel = n_max > 0 ? (n_max + kSelChunk - 1) / kSelChunk : 1;
   const int gk = (a.k + kSelChunk - 1) / kSelChunk;
-  hipLaunchKernelGGL(select_kernel, dim3(gsel > gk ? gsel : gk, a.B), dim3(kSelThreads), 0, s, a);
+  hipLaunchKernelGGL(select_chunk_kernel, dim3(gsel > gk ? gsel : gk, a.B), dim3(kSelThreads), 0, s, a);
+  hipLaunchKernelGGL(select_resolve_kernel, dim3(a.B), dim3(kSelThreads), 0, s, a);
+  hipLaunchKernelGGL(select_compact_kernel, dim3(a.B), dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
 }
 

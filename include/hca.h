@@ -138,11 +138,20 @@ hca_status kv_compress(const uint16_t* x, int64_t x_stride_b, const float* gate_
  *   src        float src[b * src_stride_b + i * dst.dim + c]
  *   e0, ne     int32 [B] (device); ne[b] clamped to [0, max_ne]
  *   block_table int32 [B][bt_stride]
+ *   ws         NULL, or kv_quantize_page_workspace(B, max_ne, dst) bytes of
+ *              device scratch (no initial contents needed).  With a
+ *              workspace an fp8 page is split over several blocks (an amax
+ *              pass then an encode pass), which is what a decode step that
+ *              rewrites one open page per sequence needs; without one, each
+ *              page is done by a single block.  The codes are the same either
+ *              way.  Calls that overlap in time must use different workspaces.
+ *              The size is 0 for fp4 and bf16 pools (ws is then ignored).
  */
+size_t kv_quantize_page_workspace(int32_t B, int32_t max_ne, hca_paged_cache dst);
 hca_status kv_quantize_page(const float* src, int64_t src_stride_b, const int32_t* e0,
                             const int32_t* ne, int32_t B, int32_t max_ne,
                             const int32_t* block_table, int32_t bt_stride, hca_paged_cache dst,
-                            void* stream);
+                            void* ws, size_t ws_bytes, void* stream);
 
 /*
  * indexer_topk -- indexer scoring and top-k selection for c4a layers (V4 page,
@@ -163,9 +172,10 @@ hca_status kv_quantize_page(const float* src, int64_t src_stride_b, const int32_
  *   k          1 .. 8192; at most 2^21 entries per sequence (ceil(max_seq_len/m))
  *   ws         workspace of indexer_topk_workspace(...) bytes.  It must be
  *              zero-filled before its first use; every successful call leaves
- *              its histogram and counters zeroed again, so it can be reused
- *              as is (re-zero it after a failed call).  Calls that overlap in
- *              time must use different workspaces.
+ *              the part that must start at zero (a score histogram) zeroed
+ *              again, so it can be reused as is (re-zero it after a failed
+ *              call).  Calls that overlap in time must use different
+ *              workspaces.
  */
 size_t indexer_topk_workspace(int32_t B, int32_t max_seq_len, int32_t m, int32_t k);
 hca_status indexer_topk(const uint16_t* q_idx, const float* head_w, int32_t HI,

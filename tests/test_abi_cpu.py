@@ -114,13 +114,18 @@ def test_validation_kv_compress():
 
 def test_validation_quantize_and_gather():
     L = hca.lib()
-    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(dtype=7), None) == 1
-    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(epp=3), None) == 1
-    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(dtype=2, dim=48), None) == 1
-    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(scales=None), None) == 1
-    assert L.kv_quantize_page(None, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(), None) == 1
-    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 0, _cache(), None) == 1
-    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 0, 64, FAKE, 16, _cache(), None) == 0
+    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(dtype=7), None, 0, None) == 1
+    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(epp=3), None, 0, None) == 1
+    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(dtype=2, dim=48), None, 0, None) == 1
+    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(scales=None), None, 0, None) == 1
+    assert L.kv_quantize_page(None, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(), None, 0, None) == 1
+    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 0, _cache(), None, 0, None) == 1
+    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 0, 64, FAKE, 16, _cache(), None, 0, None) == 0
+    # a workspace smaller than kv_quantize_page_workspace(...) is rejected before any launch
+    need = L.kv_quantize_page_workspace(2, 64, _cache())
+    assert need > 0 and need % 256 == 0
+    assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(), FAKE, need - 1, None) == 1
+    assert L.kv_quantize_page_workspace(2, 64, _cache(dtype=2, dim=64)) == 0  # fp4: no workspace
     assert L.kv_gather(_cache(), FAKE, 1, FAKE, 2, 65, FAKE, FAKE, None) == 1  # table too narrow for 65 rows
     assert L.kv_gather(_cache(), FAKE, 2, FAKE, 2, 65, FAKE, None, None) == 1  # fp8 needs scales out
     assert L.kv_gather(_cache(), FAKE, 2, FAKE, 0, 65, FAKE, FAKE, None) == 0

@@ -71,10 +71,12 @@ def test_probe_hw_decoders_are_exact():
 # ----------------------------------------------------------------- kv_quantize_page
 
 
+@pytest.mark.parametrize("use_ws", [False, True])
 @pytest.mark.parametrize("dtype,epp,dim", [("fp8", 64, 512), ("fp8", 2, 512), ("fp8", 256, 128), ("fp4", 64, 128),
-                                           ("bf16", 64, 128), ("fp4", 64, 64), ("fp8", 64, 136)])
-def test_quantize_pages_bit_exact(dtype, epp, dim):
-    H.flush(f"quantize {dtype} epp={epp} dim={dim}")
+                                           ("bf16", 64, 128), ("fp4", 64, 64), ("fp8", 64, 136), ("fp8", 256, 512),
+                                           ("fp4", 64, 256)])
+def test_quantize_pages_bit_exact(dtype, epp, dim, use_ws):
+    H.flush(f"quantize {dtype} epp={epp} dim={dim} ws={use_ws}")
     rng = np.random.default_rng(41)
     lens = np.array([epp * 5 + 7, epp * 3, 1, epp * 2 - 1])
     B = len(lens)
@@ -89,8 +91,14 @@ def test_quantize_pages_bit_exact(dtype, epp, dim):
     for b in range(B):
         paging.write_run(ref, table[b], 0, src[b, : lens[b]])
     dst = hca.PagedCache.empty(B * nb + 3, epp, dim, dtype)
+    dst.codes.fill_(0x5A)  # slots past the valid rows must come back zeroed
+    ws = None
+    if use_ws:
+        nws = hca.kv_quantize_page_workspace(B, max_ne, dst)
+        assert (nws > 0) == (dtype == "fp8")
+        ws = torch.full((max(nws, 1),), 0xC3, dtype=torch.uint8, device="cuda")  # no initial contents needed
     hca.kv_quantize_page(H.to_dev(src), H.to_dev(np.zeros(B, np.int32)), H.to_dev(lens.astype(np.int32)), max_ne,
-                         H.to_dev(table), dst)
+                         H.to_dev(table), dst, ws=ws)
     torch.cuda.synchronize()
     got = H.download_pool(dst, ref)
     for b in range(B):
@@ -98,15 +106,17 @@ def test_quantize_pages_bit_exact(dtype, epp, dim):
             phys = table[b, p]
             nv = min(epp, lens[b] - p * epp)
             assert np.array_equal(got.codes[phys, :nv], ref.codes[phys, :nv]), (b, p)
+            assert not got.codes[phys, nv:].any(), (b, p)
             if dtype == "fp8":
                 assert got.scales[phys] == ref.scales[phys], (b, p)
             elif dtype == "fp4":
                 assert np.array_equal(got.scales[phys, :nv], ref.scales[phys, :nv]), (b, p)
 
 
-def test_quantize_open_page_run():
+@pytest.mark.parametrize("use_ws", [False, True])
+def test_quantize_open_page_run(use_ws):
     # a run that starts at a later page (the decode update's open page), e0 > 0
-    H.flush("quantize open page")
+    H.flush(f"quantize open page ws={use_ws}")
     rng = np.random.default_rng(42)
     epp, dim = 64, 512
     table = np.array([[5, 2, 7, 0], [1, 3, 4, 6]], np.int32)
@@ -117,7 +127,8 @@ def test_quantize_open_page_run():
     for b in range(2):
         paging.write_run(ref, table[b], int(e0[b]), rows[b, : ne[b]])
     dst = hca.PagedCache.empty(8, epp, dim, "fp8")
-    hca.kv_quantize_page(H.to_dev(rows), H.to_dev(e0), H.to_dev(ne), 40, H.to_dev(table), dst)
+    ws = hca.workspace(hca.kv_quantize_page_workspace(2, 40, dst)) if use_ws else None
+    hca.kv_quantize_page(H.to_dev(rows), H.to_dev(e0), H.to_dev(ne), 40, H.to_dev(table), dst, ws=ws)
     got = H.download_pool(dst, ref)
     assert np.array_equal(got.codes[7, :40], ref.codes[7, :40]) and got.scales[7] == ref.scales[7]
     assert np.array_equal(got.codes[3, :17], ref.codes[3, :17]) and got.scales[3] == ref.scales[3]
@@ -126,11 +137,15 @@ def test_quantize_open_page_run():
 # ----------------------------------------------------------------- kv_compress
 
 
-@pytest.mark.parametrize("m,d", [(4, 512), (128, 512), (4, 128), (1, 512), (16, 64), (256, 128)])
-def test_compress_entries(m, d):
-    H.flush(f"compress m={m} d={d}")
+# groups0 sets the first sequence's full groups: with few entries (groups0 * 4 < 512)
+# and d % 64 == 0 a large-m fold is cut into 64-dim slices, otherwise a block
+# folds whole entries; (64, 136) has no 64-dim slicing at all.
+@pytest.mark.parametrize("m,d,groups0", [(4, 512, 37), (128, 512, 37), (4, 128, 37), (1, 512, 37), (16, 64, 37),
+                                         (256, 128, 37), (128, 512, 140), (64, 136, 37), (32, 256, 1)])
+def test_compress_entries(m, d, groups0):
+    H.flush(f"compress m={m} d={d} groups0={groups0}")
     rng = np.random.default_rng(51)
-    T = [m * 37 + (m // 2 + 1 if m > 1 else 0), 3, m * 9, 1]
+    T = [m * groups0 + (m // 2 + 1 if m > 1 else 0), 3, m * 9, 1]
     B = len(T)
     Tm = max(T)
     x32 = rng.standard_normal((B, Tm, d)).astype(np.float32)
