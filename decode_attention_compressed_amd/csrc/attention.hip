@@ -5,10 +5,22 @@
 // page, section 2.3: only window blocks are read).
 //
 // Work split: block = (split of the sequence's row list, sequence, 64-head
-// group); wave w owns 16 query heads.  A 32-row tile is gathered through the
-// block table with 16-byte loads (8 lanes cover 128 contiguous bytes of 8
-// rows), decoded ONCE to f16 (fp8 code x page scale, or bf16) and stored in LDS
-// row-major.  Both MFMA contractions are v_mfma_f32_16x16x32_f16:
+// group); wave w owns 16 query heads.  A split is at most kMaxTiles tiles of
+// 32 rows, and the block issues the gathers of ALL its tiles before it waits
+// for any of them (random 512-byte rows cost a full HBM round trip each, so
+// the bytes in flight, not the arithmetic, set the pace); splits are sized so
+// that all blocks are resident at once.  The rows are
+// gathered through the block table with 16-byte loads (8 lanes cover 128
+// contiguous bytes of 8 rows) and written to LDS row-major as f16.
+//
+// fp8 rows are converted without their page scale (every E4M3 value is exact
+// in f16, so no overflow or rounding whatever the scale); the scale is applied
+// per row in fp32: to the logit after the QK product, and to the probability
+// before the PV product as scale/sigma (sigma = the split's largest scale,
+// folded back into the partial output).  The rotated query is multiplied by a
+// power of two per head so that its f16 copy is exact in range.
+//
+// Both MFMA contractions are v_mfma_f32_16x16x32_f16:
 //   S^T[rows x heads] = K[rows x d] . Q~^T          (Q~ in registers)
 //   O[heads x d]     += P[heads x rows] . V[rows x d]
 // The V operand (8 rows of one dim per lane) is read from the same row-major
@@ -33,7 +45,12 @@ constexpr int kAttnThreads = 256;
 constexpr int kTileRows = 32;
 constexpr int kHeadsPerBlock = 64;
 constexpr float kRescaleSlack = 8.0f;
-constexpr int kMaxRowsPerSplit = 256;
+constexpr int kMaxTiles = 8;  // tiles of one split, all in flight at once
+constexpr int kMaxRowsPerSplit = kTileRows * kMaxTiles;
+// A one-tile split keeps two blocks on a CU (<= 256 VGPRs); longer splits hold
+// their tiles in registers and run one block per CU.  Splits are sized so that
+// every block is resident at once: each then pays one HBM round trip.
+constexpr int kCUs = 256;
 constexpr int kMaxSplits = kAttnMaxSplits;
 
 static inline size_t align256a(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -45,17 +62,19 @@ AttnPlan attn_plan(int B, int H, int d, int max_seq_len, int m, int window, int 
   const int win = window < max_seq_len ? window : max_seq_len;
   p.rows_max = ent + win;
   p.head_blocks = (H + kHeadsPerBlock - 1) / kHeadsPerBlock;
-  const int units = (B > 0 ? B : 1) * p.head_blocks;
-  int S = (512 + units - 1) / units;
-  const int tiles = (p.rows_max + kTileRows - 1) / kTileRows;
-  if (S > tiles) S = tiles;
-  if (S < 1) S = 1;
-  int rps = (p.rows_max + S - 1) / S;
-  rps = ((rps + kTileRows - 1) / kTileRows) * kTileRows;
-  if (rps < 64) rps = 64;
-  if (rps > kMaxRowsPerSplit) rps = kMaxRowsPerSplit;
-  p.rows_per_split = rps;
-  p.splits = p.rows_max > 0 ? (p.rows_max + rps - 1) / rps : 1;
+  // one tile per split if two blocks per CU cover the rows, else the fewest
+  // tiles (1..6, or 8) that fit one block per CU
+  const int64_t units = (int64_t)(B > 0 ? B : 1) * p.head_blocks;
+  const int64_t tiles = (p.rows_max + kTileRows - 1) / kTileRows;
+  int64_t tps = 1;
+  if (tiles * units > 2 * kCUs) {
+    tps = (tiles * units + kCUs - 1) / kCUs;
+    tps = tps > 6 ? kMaxTiles : tps;
+  }
+  p.tiles = (int)tps;
+  p.rows_per_split = kTileRows * p.tiles;
+  const int64_t splits = p.rows_max > 0 ? (p.rows_max + p.rows_per_split - 1) / p.rows_per_split : 1;
+  p.splits = (int)(splits > 2 * (int64_t)kMaxSplits ? 2 * (int64_t)kMaxSplits : splits);  // caller rejects > kMaxSplits
   size_t off = 0;
   p.o_off = off; off = align256a(off + (size_t)B * p.splits * H * d * sizeof(float));
   p.ml_off = off; off = align256a(off + (size_t)B * p.splits * H * 2 * sizeof(float));
@@ -63,40 +82,66 @@ AttnPlan attn_plan(int B, int H, int d, int max_seq_len, int m, int window, int 
   return p;
 }
 
-// Address of one row of the sequence's row list (selected entries, then window
-// tokens); 0 when the row is skipped (index outside [0, N) or unmapped page).
-__device__ __forceinline__ uint64_t resolve_row(const AttnArgs& a, int b, int r, int n_sel, int N, int L, int n_win,
-                                                float& scale) {
-  const hca_paged_cache* pool;
-  int phys, slot;
-  scale = 0.0f;
-  if (r < n_sel) {
-    const int e = a.sel ? a.sel[(int64_t)b * a.k + r] : r;
-    if (e < 0 || e >= N) return 0;
-    pool = &a.kv;
-    phys = a.bt[(int64_t)b * a.bts + e / a.kv.epp];
-    slot = e % a.kv.epp;
-  } else {
-    const int t = L - n_win + (r - n_sel);
-    pool = &a.win;
-    phys = a.wbt[(int64_t)b * a.wbts + t / a.win.epp];
-    slot = t % a.win.epp;
-  }
-  if (phys < 0 || phys >= pool->num_pages) return 0;
-  const bool fp8 = pool->dtype == HCA_FP8_E4M3;
-  const uint8_t* p = reinterpret_cast<const uint8_t*>(pool->codes) + ((int64_t)phys * pool->epp + slot) * pool->dim * (fp8 ? 1 : 2);
-  scale = fp8 ? reinterpret_cast<const float*>(pool->scales)[phys] : 1.0f;
-  return reinterpret_cast<uint64_t>(p);
+// LDS-only barrier: orders the block's LDS accesses without waiting for its
+// outstanding global loads (a full __syncthreads also drains those).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+// Address of one row of the sequence's row list (selected entries, then window
+// tokens); 0 when the row is skipped (index outside [0, N) or unmapped page).
+// `sidx` is the row's page in its pool, for the page scale.
+// `e_sel` is the row's selected entry index, loaded by the caller ahead of
+// time (ignored without a selection).
+__device__ __forceinline__ uint64_t resolve_row(const AttnArgs& a, int b, int r, int e_sel, int n_sel, int N, int L,
+                                                int n_win, int row_bytes, bool& in_win, int& sidx) {
+  int phys, slot, np, epp;
+  uint64_t base;
+  if (r < n_sel) {
+    const int e = a.sel ? e_sel : r;
+    if (e < 0 || e >= N) return 0;
+    epp = a.kv.epp;
+    phys = a.bt[(int64_t)b * a.bts + e / epp];
+    slot = e % epp;
+    np = a.kv.num_pages;
+    base = reinterpret_cast<uint64_t>(a.kv.codes);
+    in_win = false;
+  } else {
+    const int t = L - n_win + (r - n_sel);
+    epp = a.win.epp;
+    phys = a.wbt[(int64_t)b * a.wbts + t / epp];
+    slot = t % epp;
+    np = a.win.num_pages;
+    base = reinterpret_cast<uint64_t>(a.win.codes);
+    in_win = true;
+  }
+  if (phys < 0 || phys >= np) return 0;
+  sidx = phys;
+  return base + ((uint64_t)phys * epp + slot) * row_bytes;
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// LDS tile layout.  For D >= 128 a row holds its D halves unpadded and the
+// 16-byte chunk c of row r sits at chunk c ^ swz(r): the 16 rows a QK read
+// touches and the 8 rows x 32 bytes a transposed PV read touches then fall on
+// distinct banks.  D = 64 rows (8 chunks) are padded instead.
+template <int D>
+struct TileLayout {
+  static constexpr bool kSwz = D >= 128;
+  static constexpr int STR = kSwz ? D : D + 16;  // halves per row
+  __device__ static __forceinline__ int swz(int r) { return kSwz ? (((r & 7) << 1) | ((r >> 3) & 1)) : 0; }
+  // half index of chunk c (8 halves) of row r
+  __device__ static __forceinline__ int chunk(int r, int c) { return r * STR + ((c ^ swz(r)) << 3); }
+};
 typedef short s4 __attribute__((ext_vector_type(4)));
 
 // the 4 rows x 16 dims one loader thread gathers per tile (raw bytes).  The
 // gather is unconditional and branch-free: a skipped row, a thread with no
 // chunk, or a tile past the end reads the pool's first row (masked when the
-// tile is decoded), so the next tile's loads stay in flight across this
-// tile's compute.
+// tile is decoded), so no wait is forced before the tile is used.
 template <int KVDT>
 struct RowRaw {
   static constexpr int NV = KVDT == HCA_FP8_E4M3 ? 1 : 2;  // 16-byte loads per row
@@ -113,20 +158,27 @@ struct RowRaw {
   }
 };
 
-template <int D, int KVDT>
-__global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
+template <int D, int KVDT, int TILES>
+__global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_kernel(AttnArgs a) {
   constexpr int KS = D / 32;          // k-steps of the S contraction
   constexpr int NT = D / 16;          // 16-dim tiles of O
-  constexpr int KSTR = D + 16;        // LDS row stride (halves): 4 consecutive rows on disjoint banks
+  using TL = TileLayout<D>;
   constexpr int CHUNKS = D / 16;      // 16-dim chunks per row (load phase)
-  __shared__ _Float16 k_s[kTileRows * KSTR];
+  constexpr int RPS = kTileRows * TILES;
+  constexpr bool kFp8 = KVDT == HCA_FP8_E4M3;
+  __shared__ _Float16 k_s[kTileRows * TL::STR];
   __shared__ float2 cs_s[D / 2];
-  __shared__ uint64_t rowptr_s[kMaxRowsPerSplit];
-  __shared__ float rowscale_s[kMaxRowsPerSplit];
+  __shared__ uint64_t rowptr_s[RPS];
+  __shared__ float ratio_s[RPS];      // page scale / sigma (0 for skipped rows)
+  __shared__ float red_s[kAttnThreads / 64];
 
   const int s = blockIdx.x, b = blockIdx.y, hb = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
+  // the selected entry of this thread's row, loaded before the lengths are known
+  int e_sel = 0;
+  if (a.sel != nullptr && threadIdx.x < RPS)
+    e_sel = gload<int>(a.sel + (int64_t)b * a.k + min(s * a.plan.rows_per_split + (int)threadIdx.x, a.k - 1));
   const int L = clampi(a.lens[b], 0, a.max_len);
   const int N = (L + a.m - 1) / a.m;
   const int n_sel = a.sel ? clampi(a.sel_n[b], 0, a.k) : N;
@@ -145,38 +197,97 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
     return;
   }
 
-  // row addresses of the whole split, and the RoPE table at the query position L-1
-  for (int i = threadIdx.x; i < kMaxRowsPerSplit; i += kAttnThreads) {
-    float sc = 0.0f;
-    uint64_t rp = 0;
-    if (r0 + i < r1) rp = resolve_row(a, b, r0 + i, n_sel, N, L, n_win, sc);
-    rowptr_s[i] = rp;
-    rowscale_s[i] = sc;
+  // ---- query loads (bf16): in flight while the rows are resolved
+  const bool hv = head < H;
+  u32x4 qraw[KS];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)b * H + (hv ? head : H - 1)) * D;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) qraw[t] = gload<u32x4>(qrow + 32 * t + 8 * g);
   }
+
+  // ---- row addresses of the split; page scales are loaded now, used later
+  constexpr int row_bytes = kFp8 ? D : 2 * D;
+  float pscale = 0.0f;
+  if (threadIdx.x < RPS) {
+    const int r = r0 + threadIdx.x;
+    uint64_t rp = 0;
+    bool in_win = false;
+    int sidx = 0;
+    if (r < r1) rp = resolve_row(a, b, r, e_sel, n_sel, N, L, n_win, row_bytes, in_win, sidx);
+    rowptr_s[threadIdx.x] = rp;
+    if constexpr (kFp8) {
+      const float* sc = reinterpret_cast<const float*>(in_win ? a.win.scales : a.kv.scales);
+      pscale = gload<float>(sc + (rp ? sidx : 0));
+      if (rp == 0) pscale = 0.0f;
+    } else {
+      pscale = rp ? 1.0f : 0.0f;
+    }
+  }
+  lds_barrier();
+
+  // ---- every tile's gather, issued before anything waits for one
+  const int q4 = threadIdx.x & 7;
+  const int c16 = threadIdx.x >> 3;
+  const bool loader = c16 < CHUNKS;
+  const uint8_t* safe = reinterpret_cast<const uint8_t*>(a.kv.codes);
+  const int c16e = loader ? c16 : 0;
+  RowRaw<KVDT> raw[TILES];
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) raw[t].gather(rowptr_s, kTileRows * t + 4 * q4, r0 + kTileRows * t < r1, c16e, safe);
+
+  // ---- meanwhile: RoPE table at the query position L-1, sigma, row ratios
   for (int i = threadIdx.x; i < D / 2; i += kAttnThreads) {
     float c, sn;
     rope_cs((double)(L - 1), rope_inv_freq(i, D, a.theta), c, sn);
     cs_s[i] = make_float2(c, sn);
   }
-  __syncthreads();
-
-  // rotated query fragments: lane holds Q~[head][32t + 8g + j], j < 8
-  f16x8 qf[KS];
   {
-    const bool hv = head < H;
-    const uint16_t* qrow = a.q + ((int64_t)b * H + (hv ? head : 0)) * D;
+    const float wm = wave_max(pscale);
+    if (lane == 0) red_s[wave] = wm;
+  }
+  lds_barrier();
+  float sigma = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
+  sigma = sigma > 0.0f ? sigma : 1.0f;
+  if (threadIdx.x < RPS) ratio_s[threadIdx.x] = pscale / sigma;
+
+  // ---- rotated query fragments: lane holds Q~[head][32t + 8g + j] x qs, j < 8,
+  // with qs a power of two that puts the head's largest |value| in [2^13, 2^14)
+  f16x8 qf[KS];
+  float hfac;  // logit = S x ratio x hfac
+  {
+    // pass 1: largest |component| of the rotated head; pass 2: rotate again, scale, round
+    auto rot = [&](int t, int p, float& y0, float& y1) {
+      const float x0 = u2f(qraw[t][p] << 16), x1 = u2f(qraw[t][p] & 0xFFFF0000u);
+      const float2 cs = cs_s[(32 * t + 8 * g) / 2 + p];
+      y0 = x0 * cs.x - x1 * cs.y;
+      y1 = x0 * cs.y + x1 * cs.x;
+    };
+    float amax = 0.0f;
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
-      const int c0 = 32 * t + 8 * g;
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (hv) raw = *reinterpret_cast<const u32x4*>(qrow + c0);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        float y0, y1;
+        rot(t, p, y0, y1);
+        amax = fmaxf(amax, fmaxf(fabsf(y0), fabsf(y1)));
+      }
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    int e = 0;
+    if (amax > 0.0f) (void)frexpf(amax, &e);  // amax < 2^e
+    const float qs = ldexpf(1.0f, min(14 - e, 126));
+    hfac = a.scale * sigma / qs;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
       f16x8 v;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const float x0 = u2f(raw[p] << 16), x1 = u2f(raw[p] & 0xFFFF0000u);
-        const float2 cs = cs_s[c0 / 2 + p];
-        v[2 * p] = (_Float16)(x0 * cs.x - x1 * cs.y);
-        v[2 * p + 1] = (_Float16)(x0 * cs.y + x1 * cs.x);
+        float y0, y1;
+        rot(t, p, y0, y1);
+        v[2 * p] = (_Float16)(y0 * qs);
+        v[2 * p + 1] = (_Float16)(y1 * qs);
       }
       qf[t] = v;
     }
@@ -187,79 +298,74 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
   for (int n = 0; n < NT; ++n) oacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;  // for head `head` (replicated over g)
 
-  // load-phase mapping: quad q4 (rows 4q4..4q4+3 of the tile), 16-dim chunk c16
-  const int q4 = threadIdx.x & 7;
-  const int c16 = threadIdx.x >> 3;
-  const bool loader = c16 < CHUNKS;
-
-  const uint8_t* safe = reinterpret_cast<const uint8_t*>(a.kv.codes);
-  const int c16e = loader ? c16 : 0;
-  RowRaw<KVDT> raw;
-  raw.gather(rowptr_s, 4 * q4, true, c16e, safe);
-
-  for (int tr0 = r0; tr0 < r1; tr0 += kTileRows) {
-    const int lr0 = tr0 - r0;
-    // ---- decode this tile's 32 rows into both LDS copies
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) {
+    const int tr0 = r0 + kTileRows * t;
+    if (tr0 >= r1) break;  // uniform over the block
+    const int lr0 = kTileRows * t;
+    // ---- write this tile's 32 rows to LDS as f16 (skipped rows as zeros)
     if (loader) {
-      f16x8 lo[4], hi[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = rowptr_s[lr0 + 4 * q4 + i] != 0;  // skipped rows decode to zero
-        const float sc = rowscale_s[lr0 + 4 * q4 + i];
+        const bool ok = rowptr_s[lr0 + 4 * q4 + i] != 0;
+        f16x8 lo, hi;
+        const u32x4 z = {0u, 0u, 0u, 0u};
         if constexpr (KVDT == HCA_BF16) {
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          const u32x4 w0 = ok ? raw.w[i][0] : z, w1 = ok ? raw.w[i][1] : z;
+          const u32x4 w0 = ok ? raw[t].w[i][0] : z, w1 = ok ? raw[t].w[i][1] : z;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            lo[i][2 * q] = (_Float16)u2f(w0[q] << 16);
-            lo[i][2 * q + 1] = (_Float16)u2f(w0[q] & 0xFFFF0000u);
-            hi[i][2 * q] = (_Float16)u2f(w1[q] << 16);
-            hi[i][2 * q + 1] = (_Float16)u2f(w1[q] & 0xFFFF0000u);
+            lo[2 * q] = (_Float16)u2f(w0[q] << 16);
+            lo[2 * q + 1] = (_Float16)u2f(w0[q] & 0xFFFF0000u);
+            hi[2 * q] = (_Float16)u2f(w1[q] << 16);
+            hi[2 * q + 1] = (_Float16)u2f(w1[q] & 0xFFFF0000u);
           }
         } else {
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          const u32x4 w = ok ? raw.w[i][0] : z;
+          const u32x4 w = ok ? raw[t].w[i][0] : z;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const f32x2 x = __builtin_amdgcn_cvt_pk_f32_fp8(w[q], false);
-            const f32x2 y = __builtin_amdgcn_cvt_pk_f32_fp8(w[q], true);
-            f16x8& dst = q < 2 ? lo[i] : hi[i];
+            const f16x2 x = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w[q], 1.0f, false);
+            const f16x2 y = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w[q], 1.0f, true);
+            f16x8& dst = q < 2 ? lo : hi;
             const int o = (q & 1) * 4;
-            dst[o + 0] = (_Float16)(x[0] * sc);
-            dst[o + 1] = (_Float16)(x[1] * sc);
-            dst[o + 2] = (_Float16)(y[0] * sc);
-            dst[o + 3] = (_Float16)(y[1] * sc);
+            dst[o + 0] = x[0];
+            dst[o + 1] = x[1];
+            dst[o + 2] = y[0];
+            dst[o + 3] = y[1];
           }
         }
-        *reinterpret_cast<f16x8*>(&k_s[(4 * q4 + i) * KSTR + 16 * c16]) = lo[i];
-        *reinterpret_cast<f16x8*>(&k_s[(4 * q4 + i) * KSTR + 16 * c16 + 8]) = hi[i];
+        *reinterpret_cast<f16x8*>(&k_s[TL::chunk(4 * q4 + i, 2 * c16)]) = lo;
+        *reinterpret_cast<f16x8*>(&k_s[TL::chunk(4 * q4 + i, 2 * c16 + 1)]) = hi;
       }
     }
-    __syncthreads();
-    // ---- next tile's gather is in flight while this tile is computed
-    raw.gather(rowptr_s, lr0 + kTileRows + 4 * q4, tr0 + kTileRows < r1, c16e, safe);
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this tile's compute
+    lds_barrier();
 
-    // ---- S^T = K . Q~^T for the two 16-row halves
-    f32x4 sacc[2];
+    // ---- S^T = K . Q~^T for the two 16-row halves: four independent MFMA
+    // chains (half h, k-step parity); lane reads chunk 4kt + g of row 16h + col
+    f32x4 sacc[2][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      sacc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h) sacc[h][0] = sacc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < KS; ++t) {
-        const f16x8 kf = *reinterpret_cast<const f16x8*>(&k_s[(16 * h + col) * KSTR + 32 * t + 8 * g]);
-        sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[t], sacc[h], 0, 0, 0);
+    for (int kt = 0; kt < KS; ++kt) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f16x8 kf = *reinterpret_cast<const f16x8*>(&k_s[TL::chunk(16 * h + col, 4 * kt + g)]);
+        sacc[h][kt & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[kt], sacc[h][kt & 1], 0, 0, 0);
       }
     }
+    f32x4 sres[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) sres[h] = sacc[h][0] + sacc[h][1];
     // lane: rows 16h + 4g + i, head `head`
-    float x[8];
+    float x[8], rr[8];
     float tmax = -INFINITY;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int lr = lr0 + 16 * h + 4 * g + i;
-        const float v = (tr0 + 16 * h + 4 * g + i < r1 && rowptr_s[lr] != 0) ? sacc[h][i] * a.scale : -INFINITY;
+        const bool ok = tr0 + 16 * h + 4 * g + i < r1 && rowptr_s[lr] != 0;
+        rr[4 * h + i] = ratio_s[lr];
+        const float v = ok ? sres[h][i] * rr[4 * h + i] * hfac : -INFINITY;
         x[4 * h + i] = v;
         tmax = fmaxf(tmax, v);
       }
@@ -270,15 +376,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
     if (__any(need)) {
       const float m_new = need ? tmax : m_run;
       const float alpha = need ? expf(m_run - m_new) : 1.0f;  // exp(-inf) = 0 on the first tile
+      const bool had = m_run != -INFINITY;  // the accumulator holds something to rescale
       l_run *= alpha;
       m_run = m_new;
-      float al[4];
+      if (__any(had)) {
+        float al[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);  // lanes 0..15 hold heads 0..15
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);  // lanes 0..15 hold heads 0..15
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
+        for (int n = 0; n < NT; ++n) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) oacc[n][i] *= al[i];
+          for (int i = 0; i < 4; ++i) oacc[n][i] *= al[i];
+        }
       }
     }
     f16x8 pf;
@@ -287,37 +396,39 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
     for (int j = 0; j < 8; ++j) {
       const float p = x[j] == -INFINITY ? 0.0f : expf(x[j] - m_run);
       psum += p;
-      pf[j] = (_Float16)p;
+      pf[j] = (_Float16)(p * rr[j]);
     }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
     l_run += psum;
 
     // ---- O += P . V  (V operand: two transposing LDS reads of 4 rows each)
-    const _Float16* vbase0 = &k_s[(4 * g + (col >> 2)) * KSTR + 4 * (col & 3)];
-    const _Float16* vbase1 = vbase0 + 16 * KSTR;
+    // lane reads row R (and R + 16) at dims 16n + 4(col & 3): chunk 2n + (col & 3) / 2
+    const int vr = 4 * g + (col >> 2);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const s4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(vbase0 + 16 * n));
-      const s4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(vbase1 + 16 * n));
+      const int vo = TL::chunk(vr, 2 * n + ((col & 3) >> 1)) + 4 * (col & 1);
+      const s4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(&k_s[vo]));
+      const s4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s4*)(&k_s[vo + 16 * TL::STR]));
       const u32x4 vv = {__builtin_bit_cast(u32x2, v0)[0], __builtin_bit_cast(u32x2, v0)[1],
                         __builtin_bit_cast(u32x2, v1)[0], __builtin_bit_cast(u32x2, v1)[1]};
       oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, __builtin_bit_cast(f16x8, vv), oacc[n], 0, 0, 0);
     }
-    __syncthreads();
+    lds_barrier();
   }
 
-  // ---- partials: o (unnormalized, relative to m_run), m, l
+  // ---- partials: o (unnormalized, relative to m_run, sigma folded back), m, l
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = hb * kHeadsPerBlock + wave * 16 + 4 * g + i;
     if (h < H) {
       float* dst = opart + (part + h) * D + col;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) dst[16 * n] = oacc[n][i];
+      for (int n = 0; n < NT; ++n) dst[16 * n] = oacc[n][i] * sigma;
     }
   }
-  if (g == 0 && head < H) ml[part + head] = make_float2(m_run, l_run);
+  if (g == 0 && hv) ml[part + head] = make_float2(m_run, l_run);
 }
 
 // merge the splits of one (sequence, head) in split order, then inverse RoPE at L-1
@@ -393,13 +504,26 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)b * H + h] = M + logf(tot);
 }
 
+template <int D, int KVDT>
+static void launch_split(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(a.plan.splits, a.B, a.plan.head_blocks);
+  switch (a.plan.tiles) {
+    case 1: hipLaunchKernelGGL((attn_split_kernel<D, KVDT, 1>), grid, dim3(kAttnThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_split_kernel<D, KVDT, 2>), grid, dim3(kAttnThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((attn_split_kernel<D, KVDT, 3>), grid, dim3(kAttnThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_split_kernel<D, KVDT, 4>), grid, dim3(kAttnThreads), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((attn_split_kernel<D, KVDT, 5>), grid, dim3(kAttnThreads), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((attn_split_kernel<D, KVDT, 6>), grid, dim3(kAttnThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_split_kernel<D, KVDT, kMaxTiles>), grid, dim3(kAttnThreads), 0, s, a); break;
+  }
+}
+
 template <int D>
 static hipError_t launch_attn_d(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.plan.splits, a.B, a.plan.head_blocks);
   if (a.kv.dtype == HCA_FP8_E4M3)
-    hipLaunchKernelGGL((attn_split_kernel<D, HCA_FP8_E4M3>), grid, dim3(kAttnThreads), 0, s, a);
+    launch_split<D, HCA_FP8_E4M3>(a, s);
   else
-    hipLaunchKernelGGL((attn_split_kernel<D, HCA_BF16>), grid, dim3(kAttnThreads), 0, s, a);
+    launch_split<D, HCA_BF16>(a, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel<D>, dim3(a.H, a.B), dim3(256), 0, s, a);

@@ -65,6 +65,7 @@ struct AttnPlan {
   int rows_max;     // upper bound of rows of any sequence
   int splits;       // splits per sequence
   int rows_per_split;
+  int tiles;        // 32-row tiles per split (all in flight at once)
   int head_blocks;  // ceil(H / 64)
   size_t o_off, ml_off, total;
 };

@@ -47,7 +47,7 @@ IndexerWs indexer_ws_layout(int B, int max_seq_len, int m, int k) {
   w.cand = off; off = align256(off + (size_t)B * n_pad * sizeof(uint2));
   w.bitmap = off; off = align256(off + (size_t)B * (n_pad / 32) * sizeof(uint32_t));
   w.counters = off; off = align256(off + (size_t)B * 4 * sizeof(uint32_t));
-  w.cand_counts = off; off = align256(off + (size_t)B * (n_pad / kSelChunk) * sizeof(uint32_t));
+  w.cand_counts = off; off = align256(off + (size_t)B * 3 * (n_pad / kSelChunk) * sizeof(uint32_t));
   w.total = off;
   return w;
 }
@@ -478,8 +478,9 @@ __device__ void find_cut(const uint32_t* bins, int nb, uint32_t need, uint32_t* 
 //   select_resolve (one block per sequence) exact cut key and index bound
 //                  from the candidates (LDS radix passes), winners OR-ed into
 //                  the bitmap; resets the histogram for the next call;
-//   select_compact (one block per sequence) ascending compaction of the
-//                  bitmap into out_idx.
+//   select_compact (one block per chunk) ascending compaction of the chunk's
+//                  bitmap words into out_idx, at the offset given by the
+//                  kept counts of the chunks before it.
 // The chunk pass writes every bitmap word below N, so only the histogram has
 // to start at zero.
 struct SelView {
@@ -489,7 +490,9 @@ struct SelView {
   uint2* cand;
   uint32_t* bitmap;
   uint32_t* ctr;     // [0] cut bin, [1] count above the cut bin
-  uint32_t* ccount;  // candidates per chunk block
+  uint32_t* ccount;  // per chunk block: candidates
+  uint32_t* above;   // per chunk block: entries above the cut bin
+  uint32_t* wins;    // per chunk block: candidates kept
 };
 __device__ __forceinline__ SelView sel_view(const IndexerArgs& a, int b) {
   SelView v;
@@ -502,7 +505,10 @@ __device__ __forceinline__ SelView sel_view(const IndexerArgs& a, int b) {
   v.cand = reinterpret_cast<uint2*>(a.ws + a.lay.cand) + (size_t)b * v.n_pad;
   v.bitmap = reinterpret_cast<uint32_t*>(a.ws + a.lay.bitmap) + (size_t)b * (v.n_pad / 32);
   v.ctr = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + (size_t)b * 4;
-  v.ccount = reinterpret_cast<uint32_t*>(a.ws + a.lay.cand_counts) + (size_t)b * (v.n_pad / kSelChunk);
+  const int gp = v.n_pad / kSelChunk;
+  v.ccount = reinterpret_cast<uint32_t*>(a.ws + a.lay.cand_counts) + (size_t)b * 3 * gp;
+  v.above = v.ccount + gp;
+  v.wins = v.ccount + 2 * gp;
   return v;
 }
 
@@ -533,9 +539,10 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(IndexerArgs a
   // a wave classifies 64 consecutive entries per step (coalesced); its ballot
   // is two bitmap words; cut-bin entries take positions from an LDS counter
   // (no returning global atomic stalls the wave)
-  __shared__ uint32_t nc_s;
-  if (threadIdx.x == 0) nc_s = 0;
+  __shared__ uint32_t nc_s, na_s;
+  if (threadIdx.x == 0) nc_s = na_s = 0;
   __syncthreads();
+  uint32_t n_above = 0;  // kept-for-sure entries seen by this wave (lane 0)
   uint2* cand_blk = v.cand + (size_t)blockIdx.x * kSelChunk;
   const int c0 = blockIdx.x * kSelChunk;
   const int c1 = min(N, c0 + kSelChunk);
@@ -558,6 +565,7 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(IndexerArgs a
       const uint64_t selm = __ballot(in && bin > cut);
       const uint64_t cm = __ballot(in && bin == cut);
       if (lane == 0) v.bitmap[e0 >> 5] = (uint32_t)selm;
+      n_above += (uint32_t)__popcll(selm);
       if (lane == 1 && e0 + 32 < N) v.bitmap[(e0 >> 5) + 1] = (uint32_t)(selm >> 32);
       if (cm) {
         uint32_t basepos = 0;
@@ -570,8 +578,12 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(IndexerArgs a
       }
     }
   }
+  if (lane == 0) atomicAdd(&na_s, n_above);
   __syncthreads();
-  if (threadIdx.x == 0) v.ccount[blockIdx.x] = nc_s;
+  if (threadIdx.x == 0) {
+    v.ccount[blockIdx.x] = nc_s;
+    v.above[blockIdx.x] = na_s;
+  }
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_resolve_kernel(IndexerArgs a) {
@@ -689,76 +701,63 @@ __global__ __launch_bounds__(kSelThreads) void select_resolve_kernel(IndexerArgs
       X = lo;
     }
   }
+  __shared__ uint32_t wc_s[kMaxSelBlocks];
+  for (int j = threadIdx.x; j < G; j += kSelThreads) wc_s[j] = 0u;
+  __syncthreads();
   for_cands([&](uint32_t key, uint32_t e) {
-    if (take_all || key > T || (key == T && (int)e <= X)) atomicOr(&v.bitmap[e >> 5], 1u << (e & 31));
+    if (take_all || key > T || (key == T && (int)e <= X)) {
+      atomicOr(&v.bitmap[e >> 5], 1u << (e & 31));
+      atomicAdd(&wc_s[e / kSelChunk], 1u);
+    }
   });
+  __syncthreads();
+  for (int j = threadIdx.x; j < G; j += kSelThreads) v.wins[j] = wc_s[j];
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_compact_kernel(IndexerArgs a) {
-  // each wave owns a contiguous quarter of the words; a lane takes 8
-  // consecutive words a round (loads batched), wave prefix sums of the
-  // popcounts give each lane its output position
-  const int b = blockIdx.x;
+  // block j writes the kept entries of chunk j: its output offset is the count
+  // kept by chunks 0 .. j-1 (entries above the cut bin plus winning candidates)
+  const int b = blockIdx.y, j = blockIdx.x;
   const SelView v = sel_view(a, b);
-  const int N = v.N, k = a.k;
-  if (N <= k) return;
+  const int N = v.N, G = v.G, k = a.k;
+  if (N <= k || j >= G) return;
   int32_t* out = a.out_idx + (int64_t)b * k;
-  uint32_t* bitmap = v.bitmap;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ uint32_t tmp[kSelThreads / 64];
-  constexpr int WPL = 8;  // words per lane per round
-  const int W = (N + 31) / 32;
-  const int per_wave = (W + 3) / 4;
-  const int w0 = min(W, wave * per_wave), w1 = min(W, w0 + per_wave);
-  uint32_t cnt = 0;
-  for (int wb = w0 + lane * WPL; wb < w1; wb += 64 * WPL) {
-    uint32_t bw[WPL];
-#pragma unroll
-    for (int u = 0; u < WPL; ++u) bw[u] = wb + u < w1 ? bitmap[wb + u] : 0u;
-#pragma unroll
-    for (int u = 0; u < WPL; ++u) cnt += __popc(bw[u]);
+  uint32_t before = 0, all = 0;
+  for (int i = threadIdx.x; i < G; i += kSelThreads) {
+    const uint32_t c = v.above[i] + v.wins[i];
+    all += c;
+    before += i < j ? c : 0u;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
-  if (lane == 0) tmp[wave] = cnt;
-  __syncthreads();
-  uint32_t off = 0, total = 0;
-#pragma unroll
-  for (int i = 0; i < kSelThreads / 64; ++i) {
-    if (i < wave) off += tmp[i];
-    total += tmp[i];
-  }
-  __syncthreads();
-  for (int base = w0; base < w1; base += 64 * WPL) {
-    const int wb = base + lane * WPL;
-    uint32_t bw[WPL];
-    uint32_t pc = 0;
-#pragma unroll
-    for (int u = 0; u < WPL; ++u) {
-      bw[u] = wb + u < w1 ? bitmap[wb + u] : 0u;
-      pc += __popc(bw[u]);
-    }
+  uint32_t tot_before, total;
+  (void)block_excl_scan(before, tmp, tot_before);
+  (void)block_excl_scan(all, tmp, total);
+  // chunk j holds words [64 j, 64 j + 64) of the bitmap: one word per lane of wave 0
+  if (wave == 0) {
+    const int W = (N + 31) / 32;
+    const int w = j * (kSelChunk / 32) + lane;
+    const uint32_t bits0 = w < W ? v.bitmap[w] : 0u;
+    const uint32_t pc = (uint32_t)__popc(bits0);
     uint32_t incl = pc;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const uint32_t y = __shfl_up(incl, o, 64);
       if (lane >= o) incl += y;
     }
-    uint32_t pos = off + incl - pc;
-#pragma unroll
-    for (int u = 0; u < WPL; ++u) {
-      uint32_t bits = bw[u];
-      while (bits) {
-        const int bit = __ffs(bits) - 1;
-        bits &= bits - 1;
-        if (pos < (uint32_t)k) out[pos] = (wb + u) * 32 + bit;
-        ++pos;
-      }
+    uint32_t pos = tot_before + incl - pc;
+    uint32_t bits = bits0;
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (pos < (uint32_t)k) out[pos] = w * 32 + bit;
+      ++pos;
     }
-    off += __shfl(incl, 63, 64);
   }
-  for (int i = (int)total + threadIdx.x; i < k; i += kSelThreads) out[i] = -1;  // fewer than k: not expected
-  if (threadIdx.x == 0) a.out_n[b] = (int)min(total, (uint32_t)k);
+  if (j == G - 1) {
+    for (int i = (int)total + threadIdx.x; i < k; i += kSelThreads) out[i] = -1;  // fewer than k: not expected
+    if (threadIdx.x == 0) a.out_n[b] = (int)min(total, (uint32_t)k);
+  }
 }
 
 template <int KDT, int DI>
@@ -802,7 +801,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
   const int gk = (a.k + kSelChunk - 1) / kSelChunk;
   hipLaunchKernelGGL(select_chunk_kernel, dim3(gsel > gk ? gsel : gk, a.B), dim3(kSelThreads), 0, s, a);
   hipLaunchKernelGGL(select_resolve_kernel, dim3(a.B), dim3(kSelThreads), 0, s, a);
-  hipLaunchKernelGGL(select_compact_kernel, dim3(a.B), dim3(kSelThreads), 0, s, a);
+  hipLaunchKernelGGL(select_compact_kernel, dim3(gsel, a.B), dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
 }
 
