@@ -21,8 +21,10 @@
 // power of two per head so that its f16 copy is exact in range.
 //
 // Both MFMA contractions are v_mfma_f32_16x16x32_f16:
-//   S^T[rows x heads] = K[rows x d] . Q~^T          (Q~ in registers)
-//   O[heads x d]     += P[heads x rows] . V[rows x d]
+//   S^T[rows x heads] = K[rows x d] . Q~^T          (wave w: its 16 heads, all d)
+//   O[heads x d]     += P[heads x rows] . V[rows x d]  (wave w: all 64 heads, d/4 dims)
+// Each wave's P goes through LDS to the other three, so a V fragment read
+// from LDS feeds four MFMAs instead of one.
 // The V operand (8 rows of one dim per lane) is read from the same row-major
 // copy with ds_read_b64_tr_b16: within each 16-lane group, output lane i gets
 // element i%4 of the 8-byte runs addressed by source lanes i/4, i/4+4, i/4+8,
@@ -30,9 +32,10 @@
 // receives rows R(0..3) at dim i.
 // The S^T accumulator of a lane is exactly its P operand for the PV step when
 // the PV k-slot (g, j) is mapped to row 4g+j (j < 4) / 16+4g+j-4 (j >= 4), so
-// P never leaves registers.  Online softmax keeps a running max per head and
-// rescales the O accumulator only when the tile max exceeds it by more than 8
-// (exp(8) still fits f16 for P), which makes the rescale rare.
+// P is shared lane for lane.  The online softmax works in base 2 (log2(e) is
+// folded into the logit factor, so P = 2^(x - m) is one v_exp_f32); it keeps a
+// running max per head and rescales the O accumulator only when the tile max
+// exceeds it by more than 8 (P <= 2^8 in f16), which makes the rescale rare.
 // Partials (o, m, l) go to the workspace; a combine kernel merges the splits in
 // split order (so the result does not depend on page placement) and applies
 // inverse RoPE at position L-1.
@@ -161,7 +164,7 @@ struct RowRaw {
 template <int D, int KVDT, int TILES>
 __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_kernel(AttnArgs a) {
   constexpr int KS = D / 32;          // k-steps of the S contraction
-  constexpr int NT = D / 16;          // 16-dim tiles of O
+  constexpr int NTW = D / 64;         // 16-dim tiles of O per wave (a quarter of the dims)
   using TL = TileLayout<D>;
   constexpr int CHUNKS = D / 16;      // 16-dim chunks per row (load phase)
   constexpr int RPS = kTileRows * TILES;
@@ -169,8 +172,11 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
   __shared__ _Float16 k_s[kTileRows * TL::STR];
   __shared__ float2 cs_s[D / 2];
   __shared__ uint64_t rowptr_s[RPS];
-  __shared__ float ratio_s[RPS];      // page scale / sigma (0 for skipped rows)
+  __shared__ __attribute__((aligned(16))) float ratio_s[RPS];  // page scale / sigma; -1 marks a skipped row
   __shared__ float red_s[kAttnThreads / 64];
+  __shared__ f16x8 p_s[4][64];        // each wave's P operand, shared for the PV step
+  __shared__ float al_s[4][16];       // rescale factor of each head this tile
+  __shared__ int rs_s[4];             // did the head group rescale this tile
 
   const int s = blockIdx.x, b = blockIdx.y, hb = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -209,6 +215,7 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
   // ---- row addresses of the split; page scales are loaded now, used later
   constexpr int row_bytes = kFp8 ? D : 2 * D;
   float pscale = 0.0f;
+  bool row_ok = false;
   if (threadIdx.x < RPS) {
     const int r = r0 + threadIdx.x;
     uint64_t rp = 0;
@@ -216,6 +223,7 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
     int sidx = 0;
     if (r < r1) rp = resolve_row(a, b, r, e_sel, n_sel, N, L, n_win, row_bytes, in_win, sidx);
     rowptr_s[threadIdx.x] = rp;
+    row_ok = rp != 0;
     if constexpr (kFp8) {
       const float* sc = reinterpret_cast<const float*>(in_win ? a.win.scales : a.kv.scales);
       pscale = gload<float>(sc + (rp ? sidx : 0));
@@ -249,12 +257,12 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
   lds_barrier();
   float sigma = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
   sigma = sigma > 0.0f ? sigma : 1.0f;
-  if (threadIdx.x < RPS) ratio_s[threadIdx.x] = pscale / sigma;
+  if (threadIdx.x < RPS) ratio_s[threadIdx.x] = row_ok ? pscale / sigma : -1.0f;
 
   // ---- rotated query fragments: lane holds Q~[head][32t + 8g + j] x qs, j < 8,
   // with qs a power of two that puts the head's largest |value| in [2^13, 2^14)
   f16x8 qf[KS];
-  float hfac;  // logit = S x ratio x hfac
+  float hfac;  // base-2 logit = S x ratio x hfac
   {
     // pass 1: largest |component| of the rotated head; pass 2: rotate again, scale, round
     auto rot = [&](int t, int p, float& y0, float& y1) {
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
     int e = 0;
     if (amax > 0.0f) (void)frexpf(amax, &e);  // amax < 2^e
     const float qs = ldexpf(1.0f, min(14 - e, 126));
-    hfac = a.scale * sigma / qs;
+    hfac = a.scale * sigma / qs * 1.4426950408889634f;  // logits in base 2: p = 2^(x - m)
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
       f16x8 v;
@@ -293,9 +301,13 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
     }
   }
 
-  f32x4 oacc[NT];
+  // O for all 64 heads (head group hg, rows 4g + i) over this wave's dims
+  // 16 (wave * NTW + n) + col
+  f32x4 oacc[4][NTW];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) oacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int hg = 0; hg < 4; ++hg)
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) oacc[hg][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;  // for head `head` (replicated over g)
 
 #pragma unroll
@@ -305,9 +317,10 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
     const int lr0 = kTileRows * t;
     // ---- write this tile's 32 rows to LDS as f16 (skipped rows as zeros)
     if (loader) {
+      const f32x4 rok = *reinterpret_cast<const f32x4*>(&ratio_s[lr0 + 4 * q4]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = rowptr_s[lr0 + 4 * q4 + i] != 0;
+        const bool ok = rok[i] >= 0.0f;
         f16x8 lo, hi;
         const u32x4 z = {0u, 0u, 0u, 0u};
         if constexpr (KVDT == HCA_BF16) {
@@ -340,17 +353,30 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
     lds_barrier();
 
     // ---- S^T = K . Q~^T for the two 16-row halves: four independent MFMA
-    // chains (half h, k-step parity); lane reads chunk 4kt + g of row 16h + col
+    // chains (half h, k-step parity); lane reads chunk 4kt + g of row 16h + col.
+    // Fragments are read in batches of 8 before their MFMAs issue, so the LDS
+    // latency is paid once per batch rather than once per MFMA.
     f32x4 sacc[2][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) sacc[h][0] = sacc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int KB = KS < 4 ? KS : 4;  // k-steps per batch
 #pragma unroll
-    for (int kt = 0; kt < KS; ++kt) {
+    for (int kb = 0; kb < KS; kb += KB) {
+      f16x8 kf[KB][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const f16x8 kf = *reinterpret_cast<const f16x8*>(&k_s[TL::chunk(16 * h + col, 4 * kt + g)]);
-        sacc[h][kt & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[kt], sacc[h][kt & 1], 0, 0, 0);
+      for (int u = 0; u < KB; ++u) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          kf[u][h] = *reinterpret_cast<const f16x8*>(&k_s[TL::chunk(16 * h + col, 4 * (kb + u) + g)]);
       }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          sacc[h][u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[u][h], qf[kb + u], sacc[h][u & 1], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 0);  // the LDS reads first,
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KB, 0);  // then the MFMAs
     }
     f32x4 sres[2];
 #pragma unroll
@@ -360,12 +386,12 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
     float tmax = -INFINITY;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      const f32x4 rq = *reinterpret_cast<const f32x4*>(&ratio_s[lr0 + 16 * h + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int lr = lr0 + 16 * h + 4 * g + i;
-        const bool ok = tr0 + 16 * h + 4 * g + i < r1 && rowptr_s[lr] != 0;
-        rr[4 * h + i] = ratio_s[lr];
-        const float v = ok ? sres[h][i] * rr[4 * h + i] * hfac : -INFINITY;
+        const bool ok = rq[i] >= 0.0f;  // also false past the end of the split
+        rr[4 * h + i] = ok ? rq[i] : 0.0f;
+        const float v = ok ? sres[h][i] * rq[i] * hfac : -INFINITY;
         x[4 * h + i] = v;
         tmax = fmaxf(tmax, v);
       }
@@ -373,28 +399,20 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const bool need = tmax > m_run + kRescaleSlack;
+    float alpha = 1.0f;
+    bool resc = false;
     if (__any(need)) {
       const float m_new = need ? tmax : m_run;
-      const float alpha = need ? expf(m_run - m_new) : 1.0f;  // exp(-inf) = 0 on the first tile
-      const bool had = m_run != -INFINITY;  // the accumulator holds something to rescale
+      alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // 2^-inf = 0 on the first tile
+      resc = __any(m_run != -INFINITY);           // the accumulators hold something to rescale
       l_run *= alpha;
       m_run = m_new;
-      if (__any(had)) {
-        float al[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);  // lanes 0..15 hold heads 0..15
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[n][i] *= al[i];
-        }
-      }
     }
     f16x8 pf;
     float psum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float p = x[j] == -INFINITY ? 0.0f : expf(x[j] - m_run);
+      const float p = x[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[j] - m_run);
       psum += p;
       pf[j] = (_Float16)(p * rr[j]);
     }
@@ -402,33 +420,70 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
     psum += __shfl_xor(psum, 32, 64);
     l_run += psum;
 
-    // ---- O += P . V  (V operand: two transposing LDS reads of 4 rows each)
-    // lane reads row R (and R + 16) at dims 16n + 4(col & 3): chunk 2n + (col & 3) / 2
-    const int vr = 4 * g + (col >> 2);
+    // ---- share P and the rescale factors: each wave then accumulates O for
+    // all 64 heads over its quarter of the dims, so one V fragment feeds four
+    // MFMAs (one per head group)
+    p_s[wave][lane] = pf;
+    if (g == 0) al_s[wave][col] = alpha;
+    if (lane == 0) rs_s[wave] = resc ? 1 : 0;
+    lds_barrier();
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int vo = TL::chunk(vr, 2 * n + ((col & 3) >> 1)) + 4 * (col & 1);
+    for (int hg = 0; hg < 4; ++hg) {
+      if (__builtin_amdgcn_readfirstlane(rs_s[hg])) {  // the same for every lane
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = al_s[hg][4 * g + i];
+#pragma unroll
+        for (int n = 0; n < NTW; ++n) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[hg][n][i] *= al[i];
+        }
+      }
+    }
+    f16x8 pa[4];
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) pa[hg] = p_s[hg][lane];
+
+    // ---- O += P . V  (V operand: two transposing LDS reads of 4 rows each)
+    // lane reads row R (and R + 16) at dims 16nn + 4(col & 3): chunk 2nn + (col & 3) / 2
+    const int vr = 4 * g + (col >> 2);
+    f16x8 vf[NTW];
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) {
+      const int nn = wave * NTW + n;
+      const int vo = TL::chunk(vr, 2 * nn + ((col & 3) >> 1)) + 4 * (col & 1);
       const s4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(&k_s[vo]));
       const s4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s4*)(&k_s[vo + 16 * TL::STR]));
       const u32x4 vv = {__builtin_bit_cast(u32x2, v0)[0], __builtin_bit_cast(u32x2, v0)[1],
                         __builtin_bit_cast(u32x2, v1)[0], __builtin_bit_cast(u32x2, v1)[1]};
-      oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, __builtin_bit_cast(f16x8, vv), oacc[n], 0, 0, 0);
+      vf[n] = __builtin_bit_cast(f16x8, vv);
     }
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) {
+#pragma unroll
+      for (int hg = 0; hg < 4; ++hg)
+        oacc[hg][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[hg], vf[n], oacc[hg][n], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NTW + 4, 0);  // the LDS reads first,
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NTW, 0);      // then the MFMAs
     lds_barrier();
   }
 
   // ---- partials: o (unnormalized, relative to m_run, sigma folded back), m, l
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = hb * kHeadsPerBlock + wave * 16 + 4 * g + i;
-    if (h < H) {
-      float* dst = opart + (part + h) * D + col;
+  for (int hg = 0; hg < 4; ++hg) {
 #pragma unroll
-      for (int n = 0; n < NT; ++n) dst[16 * n] = oacc[n][i] * sigma;
+    for (int i = 0; i < 4; ++i) {
+      const int h = hb * kHeadsPerBlock + hg * 16 + 4 * g + i;
+      if (h < H) {
+        float* dst = opart + (part + h) * D + 16 * wave * NTW + col;
+#pragma unroll
+        for (int n = 0; n < NTW; ++n) dst[16 * n] = oacc[hg][n][i] * sigma;
+      }
     }
   }
-  if (g == 0 && hv) ml[part + head] = make_float2(m_run, l_run);
+  if (g == 0 && hv) ml[part + head] = make_float2(m_run * 0.6931471805599453f, l_run);  // m back to base e
 }
 
 // merge the splits of one (sequence, head) in split order, then inverse RoPE at L-1
