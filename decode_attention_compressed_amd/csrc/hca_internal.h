@@ -47,6 +47,7 @@ struct IndexerWs {
 };
 IndexerWs indexer_ws_layout(int B, int max_seq_len, int m, int k);
 constexpr int kHistBins = 4096;  // top 12 bits of the score key
+constexpr int kHistCopies = 16;  // per-sequence histogram copies the score blocks spread over
 
 struct IndexerArgs {
   const uint16_t* q; const float* w; int HI;

@@ -12,15 +12,18 @@
 // accumulator and the block scale is applied in fp32 afterwards.  ReLU, the
 // per-head weights and the head sum run on the accumulator lanes, and the
 // order key of every score lands in a 4096-bin LDS histogram that is added to
-// a per-sequence histogram in the workspace.
+// per-sequence histogram copies in the workspace.
 //
-// Select.  Every chunk block re-derives the cut bin from the histogram, marks
+// The score blocks add their LDS histograms to one of several copies in the
+// workspace (spread by block index, so the hot bins are not one queue).
+//
+// Select.  The cut bin comes from the summed copies; every chunk block marks
 // the scores above it in a bitmap and appends the cut bin's entries as
 // candidates; one block per sequence then refines the cut with two 10-bit
 // radix passes over the candidates, breaks exact ties by the lowest index and
 // marks the winners, and a last pass compacts the bitmap into ascending
-// indices.  The histogram is left zeroed for the next call; every other part
-// of the workspace is overwritten before it is read.
+// indices.  The histogram copies are left zeroed for the next call; every
+// other part of the workspace is overwritten before it is read.
 #include "hca_common.h"
 #include "hca_internal.h"
 
@@ -43,7 +46,7 @@ IndexerWs indexer_ws_layout(int B, int max_seq_len, int m, int k) {
   const int n_pad = ((n_max + kSelChunk - 1) / kSelChunk) * kSelChunk;
   size_t off = 0;
   w.scores = off; off = align256(off + (size_t)B * n_pad * sizeof(float));
-  w.hist = off; off = align256(off + (size_t)B * kHistBins * sizeof(uint32_t));
+  w.hist = off; off = align256(off + (size_t)B * kHistCopies * kHistBins * sizeof(uint32_t));
   w.cand = off; off = align256(off + (size_t)B * n_pad * sizeof(uint2));
   w.bitmap = off; off = align256(off + (size_t)B * (n_pad / 32) * sizeof(uint32_t));
   w.counters = off; off = align256(off + (size_t)B * 4 * sizeof(uint32_t));
@@ -214,9 +217,12 @@ __device__ __forceinline__ void load_query(const IndexerArgs& a, int b, int col,
   }
 }
 
+// The block's histogram is added to one of kHistCopies copies (by block index),
+// so that the blocks of a sequence do not all queue on the same hot bins.
 __device__ __forceinline__ void hist_flush(const IndexerArgs& a, int b, const uint32_t* hist_s) {
   __syncthreads();
-  uint32_t* gh = reinterpret_cast<uint32_t*>(a.ws + a.lay.hist) + (size_t)b * kHistBins;
+  uint32_t* gh = reinterpret_cast<uint32_t*>(a.ws + a.lay.hist) +
+                 ((size_t)b * kHistCopies + blockIdx.x % kHistCopies) * kHistBins;
   for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) {
     const uint32_t c = hist_s[i];
     if (c) atomicAdd(&gh[i], c);
@@ -472,15 +478,17 @@ __device__ void find_cut(const uint32_t* bins, int nb, uint32_t need, uint32_t* 
 
 // Three launches per call, so that kernel boundaries order the passes (no
 // device-scope fences, which write back and invalidate the whole L2):
-//   select_chunk   (G blocks per sequence) entries whose 12-bit bin is above
-//                  the cut bin go straight into the bitmap; cut-bin entries
-//                  become (key, index) candidates in the block's region;
+//   select_chunk   (G blocks per sequence) the cut bin from the summed
+//                  histogram copies; entries whose 12-bit bin is above it go
+//                  straight into the bitmap; cut-bin entries become (key,
+//                  index) candidates in the block's region;
 //   select_resolve (one block per sequence) exact cut key and index bound
 //                  from the candidates (LDS radix passes), winners OR-ed into
-//                  the bitmap; resets the histogram for the next call;
+//                  the bitmap;
 //   select_compact (one block per chunk) ascending compaction of the chunk's
 //                  bitmap words into out_idx, at the offset given by the
-//                  kept counts of the chunks before it.
+//                  kept counts of the chunks before it; re-zeroes the
+//                  histogram copies.
 // The chunk pass writes every bitmap word below N, so only the histogram has
 // to start at zero.
 struct SelView {
@@ -501,7 +509,7 @@ __device__ __forceinline__ SelView sel_view(const IndexerArgs& a, int b) {
   v.G = (v.N + kSelChunk - 1) / kSelChunk;
   v.n_pad = ((a.lay.n_max + kSelChunk - 1) / kSelChunk) * kSelChunk;
   v.scores = reinterpret_cast<const float*>(a.ws + a.lay.scores) + (size_t)b * v.n_pad;
-  v.hist = reinterpret_cast<uint32_t*>(a.ws + a.lay.hist) + (size_t)b * kHistBins;
+  v.hist = reinterpret_cast<uint32_t*>(a.ws + a.lay.hist) + (size_t)b * kHistCopies * kHistBins;
   v.cand = reinterpret_cast<uint2*>(a.ws + a.lay.cand) + (size_t)b * v.n_pad;
   v.bitmap = reinterpret_cast<uint32_t*>(a.ws + a.lay.bitmap) + (size_t)b * (v.n_pad / 32);
   v.ctr = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + (size_t)b * 4;
@@ -510,6 +518,41 @@ __device__ __forceinline__ SelView sel_view(const IndexerArgs& a, int b) {
   v.above = v.ccount + gp;
   v.wins = v.ccount + 2 * gp;
   return v;
+}
+
+// The cut bin (where the count from the top reaches `need`) and the count
+// strictly above it, from the histogram copies: the bins are summed 256 at a
+// time from the top, usually once, since the k highest scores sit in the top
+// bins.  Every thread of the block gets the result.
+__device__ void find_cut_copies(const uint32_t* hist, uint32_t need, uint32_t* tmp, int& cut, uint32_t& above) {
+  __shared__ int cut_s;
+  __shared__ uint32_t above_s;
+  uint32_t run = 0;  // entries in the bins already passed
+  for (int top = kHistBins - 1; top >= 0; top -= kSelThreads) {
+    const int bin = top - (int)threadIdx.x;  // descending with the thread index
+    uint32_t c[kHistCopies];
+#pragma unroll
+    for (int r = 0; r < kHistCopies; ++r) c[r] = bin >= 0 ? hist[(size_t)r * kHistBins + bin] : 0u;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int r = 0; r < kHistCopies; ++r) cnt += c[r];
+    uint32_t total;
+    const uint32_t before = run + block_excl_scan(cnt, tmp, total);
+    if (run + total >= need) {  // the cut is in this slice
+      if (before < need && before + cnt >= need) {
+        cut_s = bin;
+        above_s = before;
+      }
+      __syncthreads();
+      cut = cut_s;
+      above = above_s;
+      __syncthreads();
+      return;
+    }
+    run += total;
+  }
+  cut = 0;  // not reached: more than k entries were scored
+  above = run;
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(IndexerArgs a) {
@@ -528,10 +571,21 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(IndexerArgs a
   }
   if ((int)blockIdx.x >= v.G) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // this block's scores are loaded first: they are in flight while the cut is found
+  const int c0 = blockIdx.x * kSelChunk;
+  const int c1 = min(N, c0 + kSelChunk);
+  constexpr int kUnroll = kSelChunk / 256;  // one round of loads per wave
+  const int base0 = c0 + wave * 64 * kUnroll;
+  float sc[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int e = base0 + 64 * u + lane;
+    sc[u] = v.scores[e < c1 ? e : c0];
+  }
   __shared__ uint32_t tmp[kSelThreads / 64];
   int cut;
   uint32_t above;
-  find_cut(v.hist, kHistBins, (uint32_t)k, tmp, cut, above);
+  find_cut_copies(v.hist, (uint32_t)k, tmp, cut, above);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     v.ctr[0] = (uint32_t)cut;
     v.ctr[1] = above;
@@ -544,16 +598,8 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(IndexerArgs a
   __syncthreads();
   uint32_t n_above = 0;  // kept-for-sure entries seen by this wave (lane 0)
   uint2* cand_blk = v.cand + (size_t)blockIdx.x * kSelChunk;
-  const int c0 = blockIdx.x * kSelChunk;
-  const int c1 = min(N, c0 + kSelChunk);
-  constexpr int kUnroll = kSelChunk / 256;  // one round of loads per wave
-  for (int base = c0 + wave * 64 * kUnroll; base < c1; base += 4 * 64 * kUnroll) {
-    float sc[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int e = base + 64 * u + lane;
-      sc[u] = v.scores[e < c1 ? e : c0];
-    }
+  {
+    const int base = base0;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int e0 = base + 64 * u;
@@ -590,8 +636,6 @@ __global__ __launch_bounds__(kSelThreads) void select_resolve_kernel(IndexerArgs
   const int b = blockIdx.x;
   const SelView v = sel_view(a, b);
   const int N = v.N, G = v.G, k = a.k;
-  // the histogram has been read by every chunk block: clear it for the next call
-  for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) v.hist[i] = 0u;
   if (N <= k) return;
   __shared__ uint32_t tmp[kSelThreads / 64];
   __shared__ uint32_t h_s[1024];
@@ -757,6 +801,13 @@ __global__ __launch_bounds__(kSelThreads) void select_compact_kernel(IndexerArgs
   if (j == G - 1) {
     for (int i = (int)total + threadIdx.x; i < k; i += kSelThreads) out[i] = -1;  // fewer than k: not expected
     if (threadIdx.x == 0) a.out_n[b] = (int)min(total, (uint32_t)k);
+  }
+  // leave the histogram copies zeroed for the next call: each block a slice
+  {
+    constexpr int kWords4 = kHistCopies * kHistBins / 4;
+    const int per = (kWords4 + G - 1) / G;
+    u32x4* h4 = reinterpret_cast<u32x4*>(v.hist);
+    for (int i = j * per + threadIdx.x; i < min(kWords4, (j + 1) * per); i += kSelThreads) h4[i] = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
