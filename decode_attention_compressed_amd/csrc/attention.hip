@@ -486,68 +486,92 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
   if (g == 0 && hv) ml[part + head] = make_float2(m_run * 0.6931471805599453f, l_run);  // m back to base e
 }
 
-// merge the splits of one (sequence, head) in split order, then inverse RoPE at L-1
+// Merge the splits of one (sequence, head), then inverse RoPE at L-1.  The
+// threads form SG split groups; a group's lanes cover the D dims with 16-byte
+// loads and the group takes every SG-th split.  All partial loads of a round
+// (up to kCombU splits per thread) are issued together with the (m, l) loads
+// of the splits, so a round costs one memory round trip; the groups' sums meet
+// in LDS in a fixed order.
+constexpr int kCombThreads = 256;
+constexpr int kCombU = 36;
+
 template <int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) {
+  constexpr int TPG = D / 4;                  // threads per split group (one float4 each)
+  constexpr int SG = kCombThreads / TPG;      // split groups: 2 (D=512) .. 16 (D=64)
   const int h = blockIdx.x, b = blockIdx.y;
   const int H = a.H;
+  const int grp = threadIdx.x / TPG, li = threadIdx.x % TPG;
   const int L = clampi(a.lens[b], 0, a.max_len);
   const int N = (L + a.m - 1) / a.m;
   const int n_sel = a.sel ? clampi(a.sel_n[b], 0, a.k) : N;
   const int rows_b = n_sel + min(a.window, L);
   const int S = min(a.plan.splits, (rows_b + a.plan.rows_per_split - 1) / a.plan.rows_per_split);
-  const float2* ml = reinterpret_cast<const float2*>(a.ws + a.plan.ml_off);
-  const float* opart = reinterpret_cast<const float*>(a.ws + a.plan.o_off);
+  const float2* ml = reinterpret_cast<const float2*>(a.ws + a.plan.ml_off) + (size_t)b * a.plan.splits * H + h;
+  const f32x4* opart =
+      reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.ws + a.plan.o_off) + ((size_t)b * a.plan.splits * H + h) * D) + li;
+  const size_t ostride = (size_t)H * D / 4;  // f32x4 between consecutive splits
   __shared__ float w_s[kMaxSplits];
-  __shared__ float red_s[256];
-  // split weights exp(m_s - M): max and sum over splits, in split order
-  float mloc = -INFINITY;
-  for (int s = threadIdx.x; s < S; s += 256) mloc = fmaxf(mloc, ml[((size_t)b * a.plan.splits + s) * H + h].x);
-  red_s[threadIdx.x] = mloc;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red_s[threadIdx.x] = fmaxf(red_s[threadIdx.x], red_s[threadIdx.x + o]);
-    __syncthreads();
+  __shared__ float red_s[kCombThreads / 64];
+  __shared__ f32x4 acc_s[SG][TPG];
+
+  // first round of partial loads, issued before anything else waits
+  f32x4 o[kCombU];
+#pragma unroll
+  for (int u = 0; u < kCombU; ++u) {
+    const int s = grp + SG * u;
+    o[u] = opart[(size_t)(s < S ? s : 0) * ostride];
   }
-  const float M = red_s[0];
+  // split maxima -> M; weights w_s = exp(m_s - M) (0 for empty splits); tot = sum w_s l_s
+  float mloc = -INFINITY;
+  for (int s = threadIdx.x; s < S; s += kCombThreads) mloc = fmaxf(mloc, ml[(size_t)s * H].x);
+  mloc = wave_max(mloc);
+  if ((threadIdx.x & 63) == 0) red_s[threadIdx.x >> 6] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
   __syncthreads();
   float* out = a.out + ((int64_t)b * H + h) * D;
   if (M == -INFINITY) {
-    for (int c = threadIdx.x; c < D; c += 256) out[c] = 0.0f;
+    for (int c = threadIdx.x; c < D; c += kCombThreads) out[c] = 0.0f;
     if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)b * H + h] = -INFINITY;
     return;
   }
-  for (int s = threadIdx.x; s < S; s += 256) {
-    const float2 v = ml[((size_t)b * a.plan.splits + s) * H + h];
-    w_s[s] = v.y > 0.0f ? expf(v.x - M) : 0.0f;
+  float tloc = 0.0f;
+  for (int s = threadIdx.x; s < S; s += kCombThreads) {
+    const float2 v = ml[(size_t)s * H];
+    const float w = v.y > 0.0f ? expf(v.x - M) : 0.0f;
+    w_s[s] = w;
+    tloc += w * v.y;
   }
+  tloc = wave_sum(tloc);
+  if ((threadIdx.x & 63) == 0) red_s[threadIdx.x >> 6] = tloc;
   __syncthreads();
-  float tot = 0.0f;
-  for (int s = 0; s < S; ++s) tot += w_s[s] * ml[((size_t)b * a.plan.splits + s) * H + h].y;
-  const float inv_tot = 1.0f / tot;
-  for (int pi = threadIdx.x; pi < D / 2; pi += 256) {
-    float o0 = 0.0f, o1 = 0.0f;
-    int s = 0;
-    constexpr int U = 8;  // split partials loaded per round
-    for (; s + U <= S; s += U) {
-      float2 o[U];
+  const float tot = (red_s[0] + red_s[1]) + (red_s[2] + red_s[3]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = grp;; s0 += SG * kCombU) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        o[u] = *reinterpret_cast<const float2*>(opart + (((size_t)b * a.plan.splits + s + u) * H + h) * D + 2 * pi);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float w = w_s[s + u];
-        o0 = fmaf(w, o[u].x, o0);
-        o1 = fmaf(w, o[u].y, o1);
-      }
+    for (int u = 0; u < kCombU; ++u) {
+      const int s = s0 + SG * u;
+      const float w = s < S ? w_s[s] : 0.0f;
+      acc += w * o[u];
     }
-    for (; s < S; ++s) {
-      const float w = w_s[s];
-      if (w > 0.0f) {
-        const float2 o = *reinterpret_cast<const float2*>(opart + (((size_t)b * a.plan.splits + s) * H + h) * D + 2 * pi);
-        o0 = fmaf(w, o.x, o0);
-        o1 = fmaf(w, o.y, o1);
-      }
+    if (s0 + SG * kCombU >= S) break;
+#pragma unroll
+    for (int u = 0; u < kCombU; ++u) {  // next round (more than SG * kCombU splits)
+      const int s = s0 + SG * (kCombU + u);
+      o[u] = opart[(size_t)(s < S ? s : 0) * ostride];
+    }
+  }
+  acc_s[grp][li] = acc;
+  __syncthreads();
+  const float inv_tot = 1.0f / tot;
+  for (int pi = threadIdx.x; pi < D / 2; pi += kCombThreads) {
+    float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+    for (int gq = 0; gq < SG; ++gq) {
+      const float* ag = reinterpret_cast<const float*>(acc_s[gq]);
+      o0 += ag[2 * pi];
+      o1 += ag[2 * pi + 1];
     }
     o0 *= inv_tot;
     o1 *= inv_tot;
