@@ -248,6 +248,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// 4x4 transpose across the four 16-lane rows of a wave: with r[c] holding
+// element (row, c) in every lane of row `row`, afterwards r[c] holds element
+// (c, row).  Two v_permlane32_swap (off-diagonal 2x2 blocks of rows), then two
+// v_permlane16_swap (within the blocks).
+__device__ __forceinline__ void row_transpose4(uint32_t& r0, uint32_t& r1, uint32_t& r2, uint32_t& r3) {
+  auto a = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  r0 = c[0];
+  r1 = c[1];
+  r2 = d[0];
+  r3 = d[1];
+}
+
 template <int KDT, int DI>
 struct PageTiles {
   static constexpr int KS = DI / 32;
@@ -256,6 +271,13 @@ struct PageTiles {
   uint32_t w[4][NW];
   uint32_t sc[4][(KS + 3) / 4];
   float ps;
+
+  // fp4 pages are read with one 16-byte load per lane per 16 bytes of a row:
+  // lane l takes entry l of the page (raw[] below); prepare() then moves the
+  // bytes into the MFMA operand layout with row transposes.
+  static constexpr int SW = (KS + 3) / 4;  // block-scale words per entry (fp4)
+  uint32_t raw[KDT == HCA_FP4_E2M1 ? 4 * KS : 1];
+  uint32_t rsc[KDT == HCA_FP4_E2M1 ? SW : 1];
 
   __device__ __forceinline__ void load(const IndexerArgs& a, const int32_t* btrow, int p, bool p_ok, int N, int col,
                                        int g) {
@@ -266,13 +288,29 @@ struct PageTiles {
     const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.keys.codes) + (int64_t)pg * 64 * ROW;
     const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(codes, (uint32_t)(rows * ROW));
     if constexpr (KDT == HCA_FP8_E4M3) ps = reinterpret_cast<const float*>(a.keys.scales)[pg];
+    if constexpr (KDT == HCA_FP4_E2M1) {
+      const int lane = 16 * g + col;
+#pragma unroll
+      for (int c = 0; c < KS; ++c) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * ROW + 16 * c, 0, 0);
+        raw[4 * c] = v[0]; raw[4 * c + 1] = v[1]; raw[4 * c + 2] = v[2]; raw[4 * c + 3] = v[3];
+      }
+      const uint8_t* scl = reinterpret_cast<const uint8_t*>(a.keys.scales) + (int64_t)pg * 64 * KS;
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scl, (uint32_t)(rows * KS));
+      if constexpr (KS % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < SW; ++i) rsc[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * KS + 4 * i, 0, 0);
+      } else if constexpr (KS == 2) {
+        rsc[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, lane * KS, 0, 0);
+      } else {
+        rsc[0] = __builtin_amdgcn_raw_buffer_load_b8(rs, lane * KS, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       const int row_off = (16 * tt + col) * ROW;
-      if constexpr (KDT == HCA_FP4_E2M1) {
-#pragma unroll
-        for (int t = 0; t < KS; ++t) w[tt][t] = __builtin_amdgcn_raw_buffer_load_b32(rc, row_off + 16 * t + 4 * g, 0, 0);
-      } else if constexpr (NW >= 4) {
+      if constexpr (NW >= 4) {
 #pragma unroll
         for (int c = 0; c < NW / 4; ++c) {
           const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, row_off + g * (NW * 4) + 16 * c, 0, 0);
@@ -283,20 +321,23 @@ struct PageTiles {
         w[tt][0] = v[0]; w[tt][1] = v[1];
       }
     }
+  }
+
+  // fp4: lane (col, g) of tile tt, k-step t needs dword 4t + g of entry 16tt + col,
+  // which row tt holds in lane col: one row transpose per k-step (and per scale word)
+  __device__ __forceinline__ void prepare() {
     if constexpr (KDT == HCA_FP4_E2M1) {
-      const uint8_t* scl = reinterpret_cast<const uint8_t*>(a.keys.scales) + (int64_t)pg * 64 * KS;
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scl, (uint32_t)(rows * KS));
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        if constexpr (KS % 4 == 0) {
+      for (int t = 0; t < KS; ++t) {
+        uint32_t r0 = raw[4 * t], r1 = raw[4 * t + 1], r2 = raw[4 * t + 2], r3 = raw[4 * t + 3];
+        row_transpose4(r0, r1, r2, r3);
+        w[0][t] = r0; w[1][t] = r1; w[2][t] = r2; w[3][t] = r3;
+      }
 #pragma unroll
-          for (int i = 0; i < KS / 4; ++i) sc[tt][i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (16 * tt + col) * KS + 4 * i, 0, 0);
-        } else {
-          sc[tt][0] = 0u;
-#pragma unroll
-          for (int t = 0; t < KS; ++t)
-            sc[tt][0] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (16 * tt + col) * KS + t, 0, 0) << (8 * t);
-        }
+      for (int i = 0; i < SW; ++i) {
+        uint32_t r0 = rsc[i], r1 = rsc[i], r2 = rsc[i], r3 = rsc[i];
+        row_transpose4(r0, r1, r2, r3);
+        sc[0][i] = r0; sc[1][i] = r1; sc[2][i] = r2; sc[3][i] = r3;
       }
     }
   }
@@ -363,7 +404,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(IndexerArgs 
   constexpr int PPW = kPagesPerScoreWave;
   PageTiles<KDT, DI> pa, pb;
   auto page_of = [&](int i) { return page0 + wave + 4 * i; };
-  auto consume = [&](const PageTiles<KDT, DI>& t, int i) {
+  auto consume = [&](PageTiles<KDT, DI>& t, int i) {
+    t.prepare();
     const int p = page_of(i);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {

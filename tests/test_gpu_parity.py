@@ -178,6 +178,8 @@ def _idx_workload(dtype, d_idx, k, B=3):
     ("bf16", 64, 256, [4096, 1023, 2000]),
     ("fp8", 64, 300, [1200, 1201, 1199]),  # N = 300 ~ k: k-1, k, k+1 entries
     ("fp4", 32, 17, [100000, 640, 65]),
+    ("fp4", 64, 500, [30000, 257, 64]),     # two scale blocks per key
+    ("fp4", 256, 1000, [20000, 4096, 100]),  # eight scale blocks per key
 ])
 def test_indexer_topk_sets(dtype, d_idx, k, lens):
     H.flush(f"indexer {dtype} dI={d_idx} k={k} lens={lens}")
