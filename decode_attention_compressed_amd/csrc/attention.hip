@@ -97,16 +97,17 @@ __device__ __forceinline__ void lds_barrier() {
 // tokens); 0 when the row is skipped (index outside [0, N) or unmapped page).
 // `sidx` is the row's page in its pool, for the page scale.
 // `e_sel` is the row's selected entry index, loaded by the caller ahead of
-// time (ignored without a selection).
-__device__ __forceinline__ uint64_t resolve_row(const AttnArgs& a, int b, int r, int e_sel, int n_sel, int N, int L,
-                                                int n_win, int row_bytes, bool& in_win, int& sidx) {
+// time (ignored without a selection); without a selection `phys_pre` is the
+// page of entry r, also loaded ahead of time.
+__device__ __forceinline__ uint64_t resolve_row(const AttnArgs& a, int b, int r, int e_sel, int phys_pre, int n_sel,
+                                                int N, int L, int n_win, int row_bytes, bool& in_win, int& sidx) {
   int phys, slot, np, epp;
   uint64_t base;
   if (r < n_sel) {
     const int e = a.sel ? e_sel : r;
     if (e < 0 || e >= N) return 0;
     epp = a.kv.epp;
-    phys = a.bt[(int64_t)b * a.bts + e / epp];
+    phys = a.sel ? a.bt[(int64_t)b * a.bts + e / epp] : phys_pre;
     slot = e % epp;
     np = a.kv.num_pages;
     base = reinterpret_cast<uint64_t>(a.kv.codes);
@@ -181,10 +182,16 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
   const int s = blockIdx.x, b = blockIdx.y, hb = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
-  // the selected entry of this thread's row, loaded before the lengths are known
-  int e_sel = 0;
-  if (a.sel != nullptr && threadIdx.x < RPS)
-    e_sel = gload<int>(a.sel + (int64_t)b * a.k + min(s * a.plan.rows_per_split + (int)threadIdx.x, a.k - 1));
+  // loaded before the lengths are known: the selected entry of this thread's
+  // row, or (no selection: row r is entry r) the page of that entry
+  int e_sel = 0, phys_pre = 0;
+  if (threadIdx.x < RPS) {
+    const int r = s * a.plan.rows_per_split + (int)threadIdx.x;
+    if (a.sel != nullptr)
+      e_sel = gload<int>(a.sel + (int64_t)b * a.k + min(r, a.k - 1));
+    else
+      phys_pre = gload<int>(a.bt + (int64_t)b * a.bts + min(r / a.kv.epp, a.bts - 1));
+  }
   const int L = clampi(a.lens[b], 0, a.max_len);
   const int N = (L + a.m - 1) / a.m;
   const int n_sel = a.sel ? clampi(a.sel_n[b], 0, a.k) : N;
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
     uint64_t rp = 0;
     bool in_win = false;
     int sidx = 0;
-    if (r < r1) rp = resolve_row(a, b, r, e_sel, n_sel, N, L, n_win, row_bytes, in_win, sidx);
+    if (r < r1) rp = resolve_row(a, b, r, e_sel, phys_pre, n_sel, N, L, n_win, row_bytes, in_win, sidx);
     rowptr_s[threadIdx.x] = rp;
     row_ok = rp != 0;
     if constexpr (kFp8) {

@@ -329,11 +329,11 @@ hipError_t launch_quantize(const QuantArgs& a, float* ws, hipStream_t s) {
   if (a.B == 0 || pages_max == 0) return hipSuccess;
   switch (a.dst.dtype) {
     case HCA_FP8_E4M3: {
-      if (ws == nullptr) {
+      const ChunkGeom g = chunk_geom(epp, a.dst.dim);
+      if (ws == nullptr || g.C == 1) {  // a page that fits one chunk needs no split
         const int gx = pages_max > 8192 ? 8192 : pages_max;
         hipLaunchKernelGGL(quantize_fp8_kernel, dim3(gx, a.B), dim3(kF8Threads), 0, s, a);
       } else {
-        const ChunkGeom g = chunk_geom(epp, a.dst.dim);
         const int64_t units = (int64_t)pages_max * g.C;
         const dim3 grid(units > 16384 ? 16384 : (int)units, a.B);
         hipLaunchKernelGGL(amax_fp8_kernel, grid, dim3(kQThreads), 0, s, a, ws, pages_max);
