@@ -180,6 +180,7 @@ def _idx_workload(dtype, d_idx, k, B=3):
     ("fp4", 32, 17, [100000, 640, 65]),
     ("fp4", 64, 500, [30000, 257, 64]),     # two scale blocks per key
     ("fp4", 256, 1000, [20000, 4096, 100]),  # eight scale blocks per key
+    ("fp8", 32, 300, [2200000, 3000]),      # 550,000 entries: past the LDS bitmap, separate compaction
 ])
 def test_indexer_topk_sets(dtype, d_idx, k, lens):
     H.flush(f"indexer {dtype} dI={d_idx} k={k} lens={lens}")
