@@ -19,10 +19,9 @@
 //
 // Select.  The cut bin comes from the summed copies; every chunk block marks
 // the scores above it in a bitmap and appends the cut bin's entries as
-// candidates; one block per sequence then refines the cut with two 10-bit
-// radix passes over the candidates, breaks exact ties by the lowest index and
-// marks the winners, and a last pass compacts the bitmap into ascending
-// indices.  The histogram copies are left zeroed for the next call; every
+// candidates; then every compaction block refines the cut with two 10-bit
+// radix passes over the candidates, breaks exact ties by the lowest index, and
+// writes its chunk's kept indices in ascending order.  The histogram copies are left zeroed for the next call; every
 // other part of the workspace is overwritten before it is read.
 #include "hca_common.h"
 #include "hca_internal.h"
@@ -50,7 +49,7 @@ IndexerWs indexer_ws_layout(int B, int max_seq_len, int m, int k) {
   w.cand = off; off = align256(off + (size_t)B * n_pad * sizeof(uint2));
   w.bitmap = off; off = align256(off + (size_t)B * (n_pad / 32) * sizeof(uint32_t));
   w.counters = off; off = align256(off + (size_t)B * 4 * sizeof(uint32_t));
-  w.cand_counts = off; off = align256(off + (size_t)B * 3 * (n_pad / kSelChunk) * sizeof(uint32_t));
+  w.cand_counts = off; off = align256(off + (size_t)B * 2 * (n_pad / kSelChunk) * sizeof(uint32_t));
   w.total = off;
   return w;
 }
@@ -518,19 +517,17 @@ __device__ void find_cut(const uint32_t* bins, int nb, uint32_t need, uint32_t* 
   __syncthreads();
 }
 
-// Three launches per call, so that kernel boundaries order the passes (no
-// device-scope fences, which write back and invalidate the whole L2):
+// Two launches after the score pass, so that kernel boundaries order the
+// passes (no device-scope fences, which write back and invalidate the whole L2):
 //   select_chunk   (G blocks per sequence) the cut bin from the summed
 //                  histogram copies; entries whose 12-bit bin is above it go
 //                  straight into the bitmap; cut-bin entries become (key,
 //                  index) candidates in the block's region;
-//   select_resolve (one block per sequence) exact cut key and index bound
-//                  from the candidates (LDS radix passes), winners OR-ed into
-//                  the bitmap;
-//   select_compact (one block per chunk) ascending compaction of the chunk's
-//                  bitmap words into out_idx, at the offset given by the
-//                  kept counts of the chunks before it; re-zeroes the
-//                  histogram copies.
+//   select_compact (one block per chunk) every block resolves the exact cut
+//                  from all candidates (LDS radix passes, ties by index),
+//                  takes its output offset from the kept counts of the
+//                  chunks before it, and compacts its 64 bitmap words plus
+//                  its winning candidates; re-zeroes the histogram copies.
 // The chunk pass writes every bitmap word below N, so only the histogram has
 // to start at zero.
 struct SelView {
@@ -542,7 +539,6 @@ struct SelView {
   uint32_t* ctr;     // [0] cut bin, [1] count above the cut bin
   uint32_t* ccount;  // per chunk block: candidates
   uint32_t* above;   // per chunk block: entries above the cut bin
-  uint32_t* wins;    // per chunk block: candidates kept
 };
 __device__ __forceinline__ SelView sel_view(const IndexerArgs& a, int b) {
   SelView v;
@@ -556,9 +552,8 @@ __device__ __forceinline__ SelView sel_view(const IndexerArgs& a, int b) {
   v.bitmap = reinterpret_cast<uint32_t*>(a.ws + a.lay.bitmap) + (size_t)b * (v.n_pad / 32);
   v.ctr = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + (size_t)b * 4;
   const int gp = v.n_pad / kSelChunk;
-  v.ccount = reinterpret_cast<uint32_t*>(a.ws + a.lay.cand_counts) + (size_t)b * 3 * gp;
+  v.ccount = reinterpret_cast<uint32_t*>(a.ws + a.lay.cand_counts) + (size_t)b * 2 * gp;
   v.above = v.ccount + gp;
-  v.wins = v.ccount + 2 * gp;
   return v;
 }
 
@@ -674,19 +669,34 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(IndexerArgs a
   }
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_resolve_kernel(IndexerArgs a) {
-  const int b = blockIdx.x;
-  const SelView v = sel_view(a, b);
-  const int N = v.N, G = v.G, k = a.k;
-  if (N <= k) return;
-  __shared__ uint32_t tmp[kSelThreads / 64];
-  __shared__ uint32_t h_s[1024];
+// The exact cut from the candidates (cut-bin entries of every chunk block):
+// they are staged in LDS (unless there are more than kCandLds; then every pass
+// reads their regions), two 10-bit radix passes find the exact cut key T, and
+// ties at T keep the lowest indices (index bound X).  Winners: key > T, or
+// key == T and index <= X (all candidates when take_all).  Also counts the
+// winners of every chunk into wc_s.  Runs in every compaction block (the
+// candidates are few, so each block resolving them is cheaper than one more
+// launch); block-wide, every thread gets the result.
+struct SelLds {
+  uint32_t tmp[kSelThreads / 64];
+  uint32_t h_s[1024];
+  uint32_t pre_s[kMaxSelBlocks + 1];
+  uint32_t wc_s[kMaxSelBlocks];
+  uint2 cl_s[kCandLds];
+};
+
+struct CutKey {
+  uint32_t T;
+  int X;
+  bool take_all;
+  bool in_lds;
+  uint32_t nc;
+};
+
+__device__ CutKey resolve_cut(const SelView& v, int k, SelLds& sm) {
+  const int N = v.N, G = v.G;
   const int cut = (int)v.ctr[0];
   const uint32_t above = v.ctr[1];
-  // the candidates of all G chunk blocks are staged in LDS (one batched pass),
-  // unless there are too many, in which case the passes read their regions
-  __shared__ uint32_t pre_s[kMaxSelBlocks + 1];
-  __shared__ uint2 cl_s[kCandLds];
   {
     uint32_t cv = 0;
     const int per = (G + kSelThreads - 1) / kSelThreads;  // counts per thread, contiguous
@@ -698,22 +708,23 @@ __global__ __launch_bounds__(kSelThreads) void select_resolve_kernel(IndexerArgs
       cv += loc[u];
     }
     uint32_t tot;
-    uint32_t run = block_excl_scan(cv, tmp, tot);
+    uint32_t run = block_excl_scan(cv, sm.tmp, tot);
 #pragma unroll
     for (int u = 0; u < kMaxSelBlocks / kSelThreads; ++u) {
       const int j = threadIdx.x * per + u;
-      if (u < per && j < G) pre_s[j] = run;
+      if (u < per && j < G) sm.pre_s[j] = run;
       run += loc[u];
     }
-    if (threadIdx.x == 0) pre_s[G] = tot;
+    if (threadIdx.x == 0) sm.pre_s[G] = tot;
     __syncthreads();
   }
-  const uint32_t nc = pre_s[G];
-  const bool in_lds = nc <= (uint32_t)kCandLds;
-  if (in_lds) {
+  CutKey r;
+  r.nc = sm.pre_s[G];
+  r.in_lds = r.nc <= (uint32_t)kCandLds;
+  if (r.in_lds) {
     // flat candidate i lives in region j with pre_s[j] <= i < pre_s[j+1]
     constexpr int U = 8;
-    for (uint32_t i0 = threadIdx.x; i0 < nc; i0 += U * kSelThreads) {
+    for (uint32_t i0 = threadIdx.x; i0 < r.nc; i0 += U * kSelThreads) {
       uint2 cv[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -721,29 +732,28 @@ __global__ __launch_bounds__(kSelThreads) void select_resolve_kernel(IndexerArgs
         int lo = 0, hi = G - 1;  // last region with pre_s[j] <= i
         while (lo < hi) {
           const int mid = (lo + hi + 1) >> 1;
-          if (pre_s[mid] <= i) lo = mid; else hi = mid - 1;
+          if (sm.pre_s[mid] <= i) lo = mid; else hi = mid - 1;
         }
-        cv[u] = i < nc ? v.cand[(size_t)lo * kSelChunk + (i - pre_s[lo])] : make_uint2(0u, 0u);
+        cv[u] = i < r.nc ? v.cand[(size_t)lo * kSelChunk + (i - sm.pre_s[lo])] : make_uint2(0u, 0u);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t i = i0 + u * kSelThreads;
-        if (i < nc) cl_s[i] = cv[u];
+        if (i < r.nc) sm.cl_s[i] = cv[u];
       }
     }
     __syncthreads();
   }
-  // visit every candidate: f(key, index)
   auto for_cands = [&](auto&& f) {
-    if (in_lds) {
-      for (uint32_t i = threadIdx.x; i < nc; i += kSelThreads) {
-        const uint2 cd = cl_s[i];
+    if (r.in_lds) {
+      for (uint32_t i = threadIdx.x; i < r.nc; i += kSelThreads) {
+        const uint2 cd = sm.cl_s[i];
         f(cd.x, cd.y);
       }
     } else {
       for (int j = 0; j < G; ++j) {
         const uint2* cb = v.cand + (size_t)j * kSelChunk;
-        const uint32_t n = pre_s[j + 1] - pre_s[j];
+        const uint32_t n = sm.pre_s[j + 1] - sm.pre_s[j];
         for (uint32_t i = threadIdx.x; i < n; i += kSelThreads) {
           const uint2 cd = cb[i];
           f(cd.x, cd.y);
@@ -752,52 +762,48 @@ __global__ __launch_bounds__(kSelThreads) void select_resolve_kernel(IndexerArgs
     }
   };
   uint32_t need = (uint32_t)k - above;  // 1 .. nc
-  const bool take_all = need >= nc;
-  uint32_t T = 0u;  // when !take_all: selected = key > T, or key == T and index <= X
-  int X = 0x7FFFFFFF;
-  if (!take_all) {
+  r.take_all = need >= r.nc;
+  r.T = 0u;
+  r.X = 0x7FFFFFFF;
+  if (!r.take_all) {
     uint32_t prefix = (uint32_t)cut << 20, mask = 0xFFF00000u;
     for (int shift = 10; shift >= 0; shift -= 10) {
-      for (int i = threadIdx.x; i < 1024; i += kSelThreads) h_s[i] = 0;
+      for (int i = threadIdx.x; i < 1024; i += kSelThreads) sm.h_s[i] = 0;
       __syncthreads();
       for_cands([&](uint32_t key, uint32_t) {
-        if ((key & mask) == prefix) atomicAdd(&h_s[(key >> shift) & 1023u], 1u);
+        if ((key & mask) == prefix) atomicAdd(&sm.h_s[(key >> shift) & 1023u], 1u);
       });
       __syncthreads();
       int c2;
       uint32_t ab2;
-      find_cut(h_s, 1024, need, tmp, c2, ab2);
+      find_cut(sm.h_s, 1024, need, sm.tmp, c2, ab2);
       need -= ab2;
       prefix |= (uint32_t)c2 << shift;
       mask |= 1023u << shift;
     }
-    T = prefix;  // exact cut key; `need` of the entries with key == T are taken
-    const uint32_t ties = h_s[T & 1023u];
+    r.T = prefix;  // exact cut key; `need` of the entries with key == T are taken
+    const uint32_t ties = sm.h_s[r.T & 1023u];
     if (need < ties) {
       // keep the `need` lowest indices among the ties (binary search on the index bound)
       int lo = 0, hi = N - 1;
       while (lo < hi) {
         const int mid = lo + (hi - lo) / 2;
         uint32_t cnt = 0;
-        for_cands([&](uint32_t key, uint32_t e) { cnt += (key == T && (int)e <= mid) ? 1u : 0u; });
+        for_cands([&](uint32_t key, uint32_t e) { cnt += (key == r.T && (int)e <= mid) ? 1u : 0u; });
         uint32_t tot;
-        (void)block_excl_scan(cnt, tmp, tot);
+        (void)block_excl_scan(cnt, sm.tmp, tot);
         if (tot >= need) hi = mid; else lo = mid + 1;
       }
-      X = lo;
+      r.X = lo;
     }
   }
-  __shared__ uint32_t wc_s[kMaxSelBlocks];
-  for (int j = threadIdx.x; j < G; j += kSelThreads) wc_s[j] = 0u;
+  for (int j = threadIdx.x; j < G; j += kSelThreads) sm.wc_s[j] = 0u;
   __syncthreads();
   for_cands([&](uint32_t key, uint32_t e) {
-    if (take_all || key > T || (key == T && (int)e <= X)) {
-      atomicOr(&v.bitmap[e >> 5], 1u << (e & 31));
-      atomicAdd(&wc_s[e / kSelChunk], 1u);
-    }
+    if (r.take_all || key > r.T || (key == r.T && (int)e <= r.X)) atomicAdd(&sm.wc_s[e / kSelChunk], 1u);
   });
   __syncthreads();
-  for (int j = threadIdx.x; j < G; j += kSelThreads) v.wins[j] = wc_s[j];
+  return r;
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_compact_kernel(IndexerArgs a) {
@@ -809,21 +815,36 @@ __global__ __launch_bounds__(kSelThreads) void select_compact_kernel(IndexerArgs
   if (N <= k || j >= G) return;
   int32_t* out = a.out_idx + (int64_t)b * k;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ uint32_t tmp[kSelThreads / 64];
+  __shared__ SelLds sm;
+  __shared__ uint32_t wbits_s[kSelChunk / 32];
+  // this chunk's bitmap words (entries above the cut bin), loaded up front
+  const int W = (N + 31) / 32;
+  const int w = j * (kSelChunk / 32) + lane;
+  const uint32_t bits_above = (wave == 0 && w < W) ? v.bitmap[w] : 0u;
+  if (wave == 0) wbits_s[lane] = bits_above;
+  const CutKey ck = resolve_cut(v, k, sm);
+  // this chunk's winning candidates join its words
+  {
+    const uint32_t c0 = sm.pre_s[j], c1 = sm.pre_s[j + 1];
+    const uint2* cb = v.cand + (size_t)j * kSelChunk;
+    for (uint32_t i = c0 + threadIdx.x; i < c1; i += kSelThreads) {
+      const uint2 cd = ck.in_lds ? sm.cl_s[i] : cb[i - c0];
+      if (ck.take_all || cd.x > ck.T || (cd.x == ck.T && (int)cd.y <= ck.X))
+        atomicOr(&wbits_s[(cd.y >> 5) - j * (kSelChunk / 32)], 1u << (cd.y & 31));
+    }
+  }
   uint32_t before = 0, all = 0;
   for (int i = threadIdx.x; i < G; i += kSelThreads) {
-    const uint32_t c = v.above[i] + v.wins[i];
+    const uint32_t c = v.above[i] + sm.wc_s[i];
     all += c;
     before += i < j ? c : 0u;
   }
   uint32_t tot_before, total;
-  (void)block_excl_scan(before, tmp, tot_before);
-  (void)block_excl_scan(all, tmp, total);
-  // chunk j holds words [64 j, 64 j + 64) of the bitmap: one word per lane of wave 0
+  (void)block_excl_scan(before, sm.tmp, tot_before);
+  (void)block_excl_scan(all, sm.tmp, total);  // its barriers also publish wbits_s
+  // one word per lane of wave 0
   if (wave == 0) {
-    const int W = (N + 31) / 32;
-    const int w = j * (kSelChunk / 32) + lane;
-    const uint32_t bits0 = w < W ? v.bitmap[w] : 0u;
+    const uint32_t bits0 = w < W ? wbits_s[lane] : 0u;
     const uint32_t pc = (uint32_t)__popc(bits0);
     uint32_t incl = pc;
 #pragma unroll
@@ -893,7 +914,6 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
   const int gsel = n_max > 0 ? (n_max + kSelChunk - 1) / kSelChunk : 1;
   const int gk = (a.k + kSelChunk - 1) / kSelChunk;
   hipLaunchKernelGGL(select_chunk_kernel, dim3(gsel > gk ? gsel : gk, a.B), dim3(kSelThreads), 0, s, a);
-  hipLaunchKernelGGL(select_resolve_kernel, dim3(a.B), dim3(kSelThreads), 0, s, a);
   hipLaunchKernelGGL(select_compact_kernel, dim3(gsel, a.B), dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
 }
