@@ -33,7 +33,7 @@ constexpr int kScoreChunk = 1024;  // entries per score block (256 per wave)
 constexpr int kSelThreads = 256;
 constexpr int kSelChunk = 2048;    // entries per select block (8 per thread)
 constexpr int kMaxSelBlocks = 1024;  // select blocks per sequence (N <= 2M entries)
-constexpr int kCandLds = 4096;      // candidates the last block stages in LDS
+constexpr int kCandLds = 4096;      // candidates a compaction block stages in LDS
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
