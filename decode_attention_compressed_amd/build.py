@@ -29,9 +29,13 @@ FLAGS = [
 ]
 
 
-# per-source extra flags: the indexer keeps MFMA results in VGPRs (its
-# accumulators are small), saving the AGPR-to-VGPR copies on every tile
-EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source extra flags: the indexer and the attention keep MFMA results in
+# VGPRs.  The indexer's accumulators are small, and this saves AGPR-to-VGPR
+# copies on every tile.  The attention's output accumulator is rescaled by
+# VALU code and carried around the tile loop; in AGPRs it was copied out and
+# back on every tile.
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):

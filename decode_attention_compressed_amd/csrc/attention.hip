@@ -4,35 +4,39 @@
 // by inverse RoPE; section 2.3: every layer keeps a raw window; vLLM-0.7.2
 // page, section 2.3: only window blocks are read).
 //
-// Work split: block = (split of the sequence's row list, sequence, 64-head
-// group); wave w owns 16 query heads.  A split is at most kMaxTiles tiles of
-// 32 rows, and the block issues the gathers of ALL its tiles before it waits
-// for any of them (random 512-byte rows cost a full HBM round trip each, so
-// the bytes in flight, not the arithmetic, set the pace); splits are sized so
-// that all blocks are resident at once.  The rows are
-// gathered through the block table with 16-byte loads (8 lanes cover 128
-// contiguous bytes of 8 rows) and written to LDS row-major as f16.
+// Work split: block = (split of the sequence's row list, sequence, group of
+// 16 query heads); the four waves of a block take the split's 32-row tiles in
+// turn, each with its own online softmax, and merge their states through LDS
+// at the end, so the main loop has no block-wide barrier.  A split is sized so
+// that the grid fills the chip once: its partial output (16 heads x d fp32) is
+// then written once per many rows instead of once per tile.  A wave issues
+// its next tile's gather as soon as the current tile is in registers.
 //
 // fp8 rows are converted without their page scale (every E4M3 value is exact
 // in f16, so no overflow or rounding whatever the scale); the scale is applied
 // per row in fp32: to the logit after the QK product, and to the probability
-// before the PV product as scale/sigma (sigma = the split's largest scale,
-// folded back into the partial output).  The rotated query is multiplied by a
-// power of two per head so that its f16 copy is exact in range.
+// before the PV product as scale/sigma.  sigma is the largest page scale the
+// wave has met so far; like the softmax max it only grows, and O is rescaled
+// when it grows by more than kSigmaSlack, so P x scale/sigma stays within f16
+// range and precision; it is folded back into the partial output.  The
+// rotated query is multiplied by a power of two per head so that its f16 copy
+// is exact in range.
 //
 // Both MFMA contractions are v_mfma_f32_16x16x32_f16:
-//   S^T[rows x heads] = K[rows x d] . Q~^T          (wave w: its 16 heads, all d)
-//   O[heads x d]     += P[heads x rows] . V[rows x d]  (wave w: all 64 heads, d/4 dims)
-// Each wave's P goes through LDS to the other three, so a V fragment read
-// from LDS feeds four MFMAs instead of one.
-// The V operand (8 rows of one dim per lane) is read from the same row-major
-// copy with ds_read_b64_tr_b16: within each 16-lane group, output lane i gets
-// element i%4 of the 8-byte runs addressed by source lanes i/4, i/4+4, i/4+8,
-// i/4+12, so source lane j addresses row R(j/4) at dims 4(j%4).. and lane i
-// receives rows R(0..3) at dim i.
+//   S^T[rows x heads] = K[rows x d] . Q~^T          (K operand straight from the gather)
+//   O[heads x d]     += P[heads x rows] . V[rows x d]  (V operand through LDS)
+// The QK product takes its K operand from the registers the rows were gathered
+// into: lane (row r, group g) loads 16 bytes at byte 64u + 16g of row r, and
+// the k-slots of each k-step are mapped to those dims (the sum over d does not
+// depend on the order of its terms); the query fragments use the same map.
+// The same converted f16 values are written to the wave's LDS tile, from which
+// the V operand (8 rows of one dim per lane) is read with ds_read_b64_tr_b16:
+// within each 16-lane group, output lane i gets element i%4 of the 8-byte runs
+// addressed by source lanes i/4, i/4+4, i/4+8, i/4+12, so source lane j
+// addresses row R(j/4) at dims 4(j%4).. and lane i receives rows R(0..3) at dim i.
 // The S^T accumulator of a lane is exactly its P operand for the PV step when
 // the PV k-slot (g, j) is mapped to row 4g+j (j < 4) / 16+4g+j-4 (j >= 4), so
-// P is shared lane for lane.  The online softmax works in base 2 (log2(e) is
+// P needs no exchange.  The online softmax works in base 2 (log2(e) is
 // folded into the logit factor, so P = 2^(x - m) is one v_exp_f32); it keeps a
 // running max per head and rescales the O accumulator only when the tile max
 // exceeds it by more than 8 (P <= 2^8 in f16), which makes the rescale rare.
@@ -45,15 +49,17 @@
 namespace hca {
 
 constexpr int kAttnThreads = 256;
+constexpr int kAttnWaves = kAttnThreads / 64;
 constexpr int kTileRows = 32;
-constexpr int kHeadsPerBlock = 64;
-constexpr float kRescaleSlack = 8.0f;
-constexpr int kMaxTiles = 8;  // tiles of one split, all in flight at once
-constexpr int kMaxRowsPerSplit = kTileRows * kMaxTiles;
-// A one-tile split keeps two blocks on a CU (<= 256 VGPRs); longer splits hold
-// their tiles in registers and run one block per CU.  Splits are sized so that
-// every block is resident at once: each then pays one HBM round trip.
+constexpr int kHeadsPerBlock = 16;
+constexpr float kRescaleSlack = 8.0f;   // base-2 logit growth before O is rescaled
+constexpr float kSigmaSlack = 16.0f;    // page-scale growth before O is rescaled
+constexpr int kMaxSplitTiles = 32;  // tiles of one split (row addresses staged in LDS)
+constexpr int kMaxSplitRows = kTileRows * kMaxSplitTiles;
+// One block per CU (the waves hold a 16-head x d accumulator and two tiles of
+// gathers each); the grid is sized to fill the chip once.
 constexpr int kCUs = 256;
+constexpr int kXcds = 8;
 constexpr int kMaxSplits = kAttnMaxSplits;
 
 static inline size_t align256a(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -65,18 +71,19 @@ AttnPlan attn_plan(int B, int H, int d, int max_seq_len, int m, int window, int 
   const int win = window < max_seq_len ? window : max_seq_len;
   p.rows_max = ent + win;
   p.head_blocks = (H + kHeadsPerBlock - 1) / kHeadsPerBlock;
-  // one tile per split if two blocks per CU cover the rows, else the fewest
-  // tiles (1..6, or 8) that fit one block per CU
+  // as many splits as give every CU one block (at least one tile each), and
+  // no split longer than kMaxSplitTiles tiles; then the tiles are spread evenly
   const int64_t units = (int64_t)(B > 0 ? B : 1) * p.head_blocks;
   const int64_t tiles = (p.rows_max + kTileRows - 1) / kTileRows;
-  int64_t tps = 1;
-  if (tiles * units > 2 * kCUs) {
-    tps = (tiles * units + kCUs - 1) / kCUs;
-    tps = tps > 6 ? kMaxTiles : tps;
-  }
+  int64_t splits = kCUs / units;
+  splits = splits < tiles ? splits : tiles;
+  const int64_t need = (tiles + kMaxSplitTiles - 1) / kMaxSplitTiles;
+  splits = splits > need ? splits : need;
+  splits = splits > 1 ? splits : 1;
+  const int64_t tps = tiles > 0 ? (tiles + splits - 1) / splits : 1;
   p.tiles = (int)tps;
   p.rows_per_split = kTileRows * p.tiles;
-  const int64_t splits = p.rows_max > 0 ? (p.rows_max + p.rows_per_split - 1) / p.rows_per_split : 1;
+  splits = p.rows_max > 0 ? (p.rows_max + p.rows_per_split - 1) / p.rows_per_split : 1;
   p.splits = (int)(splits > 2 * (int64_t)kMaxSplits ? 2 * (int64_t)kMaxSplits : splits);  // caller rejects > kMaxSplits
   size_t off = 0;
   p.o_off = off; off = align256a(off + (size_t)B * p.splits * H * d * sizeof(float));
@@ -106,17 +113,19 @@ __device__ __forceinline__ uint64_t resolve_row(const AttnArgs& a, int b, int r,
   if (r < n_sel) {
     const int e = a.sel ? e_sel : r;
     if (e < 0 || e >= N) return 0;
-    epp = a.kv.epp;
-    phys = a.sel ? a.bt[(int64_t)b * a.bts + e / epp] : phys_pre;
-    slot = e % epp;
+    epp = a.kv.epp;  // a power of two, like the window's
+    const int lg = __builtin_ctz(epp);
+    phys = a.sel ? a.bt[(int64_t)b * a.bts + (e >> lg)] : phys_pre;
+    slot = e & (epp - 1);
     np = a.kv.num_pages;
     base = reinterpret_cast<uint64_t>(a.kv.codes);
     in_win = false;
   } else {
     const int t = L - n_win + (r - n_sel);
     epp = a.win.epp;
-    phys = a.wbt[(int64_t)b * a.wbts + t / epp];
-    slot = t % epp;
+    const int lg = __builtin_ctz(epp);
+    phys = a.wbt[(int64_t)b * a.wbts + (t >> lg)];
+    slot = t & (epp - 1);
     np = a.win.num_pages;
     base = reinterpret_cast<uint64_t>(a.win.codes);
     in_win = true;
@@ -129,163 +138,209 @@ __device__ __forceinline__ uint64_t resolve_row(const AttnArgs& a, int b, int r,
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // LDS tile layout.  For D >= 128 a row holds its D halves unpadded and the
-// 16-byte chunk c of row r sits at chunk c ^ swz(r): the 16 rows a QK read
-// touches and the 8 rows x 32 bytes a transposed PV read touches then fall on
-// distinct banks.  D = 64 rows (8 chunks) are padded instead.
+// 16-byte chunk c of row r sits at chunk c ^ swz(r): the 16 rows one tile
+// write touches and the 8 rows x 32 bytes a transposed PV read touches then
+// fall on distinct banks.  D = 64 rows (8 chunks) are padded instead.
 template <int D>
 struct TileLayout {
   static constexpr bool kSwz = D >= 128;
   static constexpr int STR = kSwz ? D : D + 16;  // halves per row
   __device__ static __forceinline__ int swz(int r) { return kSwz ? (((r & 7) << 1) | ((r >> 3) & 1)) : 0; }
-  // half index of chunk c (8 halves) of row r
-  __device__ static __forceinline__ int chunk(int r, int c) { return r * STR + ((c ^ swz(r)) << 3); }
+  // half index of chunk 16 hi + lo (8 halves each, lo < 16) of row r: the
+  // swizzle moves a chunk only within its group of 16, so for a fixed lo the
+  // group hi is a constant offset
+  __device__ static __forceinline__ int at(int r, int lo, int hi) { return r * STR + ((lo ^ swz(r)) << 3) + (hi << 7); }
 };
 typedef short s4 __attribute__((ext_vector_type(4)));
+typedef int i2v __attribute__((ext_vector_type(2)));
 
-// the 4 rows x 16 dims one loader thread gathers per tile (raw bytes).  The
-// gather is unconditional and branch-free: a skipped row, a thread with no
-// chunk, or a tile past the end reads the pool's first row (masked when the
-// tile is decoded), so no wait is forced before the tile is used.
-template <int KVDT>
-struct RowRaw {
-  static constexpr int NV = KVDT == HCA_FP8_E4M3 ? 1 : 2;  // 16-byte loads per row
-  u32x4 w[4][NV];
+// One wave's gather of one tile: lane (col, g) loads rows col and 16 + col of
+// the tile, NL 16-byte pieces of each at bytes off(u, g): lane group g takes
+// runs of P consecutive pieces, so that the f16 chunks it writes to LDS differ
+// from those of the other groups in the low four bits of the chunk index only.
+// Branch-free: a skipped row or a row past the split reads the pool's first
+// row instead (masked when the tile is used), so no wait is forced before the
+// tile is used.
+template <int D, int KVDT>
+struct TileRaw {
+  static constexpr int ROWB = KVDT == HCA_FP8_E4M3 ? D : 2 * D;  // bytes per row
+  static constexpr int NL = ROWB / 64;
+  static constexpr int P = D >= 128 ? (KVDT == HCA_FP8_E4M3 ? 2 : 4) : 1;
+  u32x4 w[2][NL];
 
-  __device__ __forceinline__ void gather(const uint64_t* rowptr, int lr, bool tile_ok, int c16, const uint8_t* safe) {
+  __device__ static __forceinline__ int off(int u, int g) { return 64 * P * (u / P) + 16 * P * g + 16 * (u % P); }
+
+  __device__ __forceinline__ void gather(const uint64_t* rowptr, int lr0, int col, int g, const uint8_t* safe) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint64_t t = rowptr[tile_ok ? lr + i : 0] & (tile_ok ? ~0ull : 0ull);
-      const uint8_t* p = t ? reinterpret_cast<const uint8_t*>(t) + 16 * NV * c16 : safe;
+    for (int h = 0; h < 2; ++h) {
+      const uint64_t t = rowptr[lr0 + 16 * h + col];
+      const uint8_t* p = t ? reinterpret_cast<const uint8_t*>(t) : safe;
 #pragma unroll
-      for (int v = 0; v < NV; ++v) w[i][v] = gload<u32x4>(p + 16 * v);
+      for (int u = 0; u < NL; ++u) w[h][u] = gload<u32x4>(p + off(u, g));
     }
   }
 };
 
-template <int D, int KVDT, int TILES>
-__global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_kernel(AttnArgs a) {
-  constexpr int KS = D / 32;          // k-steps of the S contraction
-  constexpr int NTW = D / 64;         // 16-dim tiles of O per wave (a quarter of the dims)
-  using TL = TileLayout<D>;
-  constexpr int CHUNKS = D / 16;      // 16-dim chunks per row (load phase)
-  constexpr int RPS = kTileRows * TILES;
-  constexpr bool kFp8 = KVDT == HCA_FP8_E4M3;
-  __shared__ _Float16 k_s[kTileRows * TL::STR];
-  __shared__ float2 cs_s[D / 2];
-  __shared__ uint64_t rowptr_s[RPS];
-  __shared__ __attribute__((aligned(16))) float ratio_s[RPS];  // page scale / sigma; -1 marks a skipped row
-  __shared__ float red_s[kAttnThreads / 64];
-  __shared__ f16x8 p_s[4][64];        // each wave's P operand, shared for the PV step
-  __shared__ float al_s[4][16];       // rescale factor of each head this tile
-  __shared__ int rs_s[4];             // did the head group rescale this tile
+// First dim of the 8 k-slots that lane group g holds in k-step t: an fp8 load
+// gives a lane 16 consecutive dims (two k-steps), a bf16 load 8.
+template <int D, int KVDT>
+__device__ __forceinline__ int kslot_dim(int t, int g) {
+  using Raw = TileRaw<D, KVDT>;
+  return KVDT == HCA_FP8_E4M3 ? Raw::off(t >> 1, g) + 8 * (t & 1) : Raw::off(t, g) / 2;
+}
 
-  const int s = blockIdx.x, b = blockIdx.y, hb = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// fp8 rows reach LDS through the load-to-LDS path (global_load_lds_dwordx4:
+// lane l's 16 bytes land at the instruction's LDS base + 16 l), two tiles per
+// wave in flight with no registers held.  A tile is 32 rows x D bytes; the
+// 16-byte chunk c of row r sits at position c ^ f(r) within its group of G
+// chunks, so that the 16 rows one K read touches and the 8 rows x 2 halves a
+// transposing V read touches fall on distinct banks.
+template <int D>
+struct RawTile {
+  static constexpr int CH = D / 16;              // chunks per row
+  static constexpr int G = CH < 16 ? CH : 16;    // swizzle group
+  static constexpr int BYTES = kTileRows * D;
+  static constexpr int INSTR = kTileRows * CH / 64;  // load-to-LDS instructions per tile
+  __device__ static __forceinline__ int f(int r) { return ((r & 15) ^ (((r >> 4) & 1) << 3)) & (G - 1); }
+  // byte offset of chunk c of row r
+  __device__ static __forceinline__ int at(int r, int c) {
+    return 16 * (r * CH + ((c & ~(G - 1)) | ((c & (G - 1)) ^ f(r))));
+  }
+};
+
+// s_waitcnt immediate for "at most n vector memory operations outstanding"
+// (the LDS and export counters left free)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// 16 bytes per lane from global memory to LDS: lane l's bytes land at
+// lds + 16 l (lds is the same for the whole wave).  Issued as inline assembly,
+// so the compiler neither counts it nor makes LDS reads wait for it: the
+// kernel waits for these loads itself (vmcnt), and the compiler's own waits
+// for other loads stay correct, since loads it does not know of only make the
+// outstanding count larger.
+__device__ __forceinline__ void load_to_lds16(const void* src, void* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory", "m0");
+}
+
+template <int D, int KVDT>
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a) {
+  constexpr bool kFp8 = KVDT == HCA_FP8_E4M3;
+  constexpr int KS = D / 32;  // k-steps of the S contraction
+  constexpr int NB = D / 16;  // 16-dim column blocks of O
+  using TL = TileLayout<D>;
+  using Raw = TileRaw<D, KVDT>;
+  using RT = RawTile<D>;
+  constexpr int NL = Raw::NL;
+  constexpr int kPer = kMaxSplitRows / kAttnThreads;  // rows each lane resolves
+  constexpr int TILE_H = kTileRows * TL::STR;         // halves of one wave's f16 tile (bf16 rows)
+  // fp8: two raw tiles per wave, one in each array; bf16: one f16 tile per
+  // wave, waves 0-1 in the first array and 2-3 in the second.  The merge
+  // reuses both.
+  constexpr int kHalfBytes = kFp8 ? kAttnWaves * RT::BYTES : 2 * TILE_H * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t tile0_s[kHalfBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tile1_s[kHalfBytes];
+  __shared__ f16x8 q_s[kFp8 ? 1 : KS][64];  // bf16 rows: rotated query fragments
+  __shared__ float2 cs_s[D / 2];
+  __shared__ uint64_t rowptr_s[kMaxSplitRows];
+  __shared__ __attribute__((aligned(16))) float ps_s[kMaxSplitRows];  // page scale; -1: skipped row
+  __shared__ float2 ml_s[kAttnWaves][kHeadsPerBlock];
+  __shared__ __attribute__((aligned(16))) float wt_s[kAttnWaves][kHeadsPerBlock];
+  static_assert(sizeof(float) * 2 * kHeadsPerBlock * D <= kHalfBytes, "the merge reuses the tiles");
+
+  // The head groups of one (split, sequence) read the same rows, so they run
+  // on one XCD (one L2): workgroups go to the XCDs in turn, so block id i runs
+  // on XCD i % 8; the grid is padded to whole rounds.
+  int s, b, hb;
+  {
+    const int id = blockIdx.x, HB = a.plan.head_blocks;
+    const int j = id / kXcds;
+    const int grp = (j / HB) * kXcds + id % kXcds;  // (split, sequence) pair
+    if (grp >= (int64_t)a.plan.splits * a.B) return;
+    hb = j % HB;
+    s = grp % a.plan.splits;
+    b = grp / a.plan.splits;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, g = lane >> 4;
-  // loaded before the lengths are known: the selected entry of this thread's
-  // row, or (no selection: row r is entry r) the page of that entry
-  int e_sel = 0, phys_pre = 0;
-  if (threadIdx.x < RPS) {
-    const int r = s * a.plan.rows_per_split + (int)threadIdx.x;
-    if (a.sel != nullptr)
-      e_sel = gload<int>(a.sel + (int64_t)b * a.k + min(r, a.k - 1));
-    else
-      phys_pre = gload<int>(a.bt + (int64_t)b * a.bts + min(r / a.kv.epp, a.bts - 1));
+  const int RPS = a.plan.rows_per_split;  // a multiple of 32, <= kMaxSplitRows
+  const int r0 = s * RPS;
+  // A wave owns the split's tiles wave, wave + 4, ... and resolves their rows
+  // itself (lane l: row l % 32 of every other one of them), so nothing but the
+  // RoPE table makes a wave wait for another before the merge.
+  auto row_of = [&](int j) { return kTileRows * (wave + kAttnWaves * (2 * j + (lane >> 5))) + (lane & 31); };
+  // loaded before the lengths are known: the selected entry of each row, or
+  // (no selection: row r is entry r) the page of that entry
+  int pre[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = row_of(j);
+    const int r = r0 + i;
+    pre[j] = 0;
+    if (i < RPS) {
+      if (a.sel != nullptr)
+        pre[j] = gload<int>(a.sel + (int64_t)b * a.k + min(r, a.k - 1));
+      else
+        pre[j] = gload<int>(a.bt + (int64_t)b * a.bts + min(r >> __builtin_ctz(a.kv.epp), a.bts - 1));
+    }
+  }
+  const int H = a.H;
+  const int h0 = hb * kHeadsPerBlock;
+  const int head = h0 + col;  // head of this lane's q / P / m / l
+  // ---- query loads (bf16) in the k-slot map, also before the lengths arrive
+  const bool hv = head < H;
+  u32x4 qraw[KS];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)b * H + (hv ? head : H - 1)) * D;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) qraw[t] = gload<u32x4>(qrow + kslot_dim<D, KVDT>(t, g));
   }
   const int L = clampi(a.lens[b], 0, a.max_len);
   const int N = (L + a.m - 1) / a.m;
   const int n_sel = a.sel ? clampi(a.sel_n[b], 0, a.k) : N;
   const int n_win = min(a.window, L);
   const int rows_b = n_sel + n_win;
-  const int r0 = s * a.plan.rows_per_split;
-  const int r1 = min(rows_b, r0 + a.plan.rows_per_split);
-  const int H = a.H;
-  const int head = hb * kHeadsPerBlock + wave * 16 + col;  // head of this lane's q / P / m / l
+  const int r1 = min(rows_b, r0 + RPS);
   float2* ml = reinterpret_cast<float2*>(a.ws + a.plan.ml_off);
   float* opart = reinterpret_cast<float*>(a.ws + a.plan.o_off);
   const size_t part = ((size_t)b * a.plan.splits + s) * H;
 
   if (r0 >= r1) {  // empty split
-    if (g == 0 && head < H) ml[part + head] = make_float2(-INFINITY, 0.0f);
+    if (threadIdx.x < kHeadsPerBlock && h0 + (int)threadIdx.x < H)
+      ml[part + h0 + threadIdx.x] = make_float2(-INFINITY, 0.0f);
     return;
   }
 
-  // ---- query loads (bf16): in flight while the rows are resolved
-  const bool hv = head < H;
-  u32x4 qraw[KS];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)b * H + (hv ? head : H - 1)) * D;
-#pragma unroll
-    for (int t = 0; t < KS; ++t) qraw[t] = gload<u32x4>(qrow + 32 * t + 8 * g);
-  }
-
-  // ---- row addresses of the split; page scales are loaded now, used later
-  constexpr int row_bytes = kFp8 ? D : 2 * D;
-  float pscale = 0.0f;
-  bool row_ok = false;
-  if (threadIdx.x < RPS) {
-    const int r = r0 + threadIdx.x;
-    uint64_t rp = 0;
-    bool in_win = false;
-    int sidx = 0;
-    if (r < r1) rp = resolve_row(a, b, r, e_sel, phys_pre, n_sel, N, L, n_win, row_bytes, in_win, sidx);
-    rowptr_s[threadIdx.x] = rp;
-    row_ok = rp != 0;
-    if constexpr (kFp8) {
-      const float* sc = reinterpret_cast<const float*>(in_win ? a.win.scales : a.kv.scales);
-      pscale = gload<float>(sc + (rp ? sidx : 0));
-      if (rp == 0) pscale = 0.0f;
-    } else {
-      pscale = rp ? 1.0f : 0.0f;
-    }
-  }
-  lds_barrier();
-
-  // ---- every tile's gather, issued before anything waits for one
-  const int q4 = threadIdx.x & 7;
-  const int c16 = threadIdx.x >> 3;
-  const bool loader = c16 < CHUNKS;
-  const uint8_t* safe = reinterpret_cast<const uint8_t*>(a.kv.codes);
-  const int c16e = loader ? c16 : 0;
-  RowRaw<KVDT> raw[TILES];
-#pragma unroll
-  for (int t = 0; t < TILES; ++t) raw[t].gather(rowptr_s, kTileRows * t + 4 * q4, r0 + kTileRows * t < r1, c16e, safe);
-
-  // ---- meanwhile: RoPE table at the query position L-1, sigma, row ratios
+  // ---- RoPE table at the query position L-1: the one block-wide wait
   for (int i = threadIdx.x; i < D / 2; i += kAttnThreads) {
     float c, sn;
     rope_cs((double)(L - 1), rope_inv_freq(i, D, a.theta), c, sn);
     cs_s[i] = make_float2(c, sn);
   }
-  {
-    const float wm = wave_max(pscale);
-    if (lane == 0) red_s[wave] = wm;
-  }
   lds_barrier();
-  float sigma = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
-  sigma = sigma > 0.0f ? sigma : 1.0f;
-  if (threadIdx.x < RPS) ratio_s[threadIdx.x] = row_ok ? pscale / sigma : -1.0f;
 
-  // ---- rotated query fragments: lane holds Q~[head][32t + 8g + j] x qs, j < 8,
-  // with qs a power of two that puts the head's largest |value| in [2^13, 2^14)
-  f16x8 qf[KS];
-  float hfac;  // base-2 logit = S x ratio x hfac
+  // ---- rotated query fragments: lane holds Q~[head][kslot_dim(t, g) + j] x qs,
+  // j < 8, with qs a power of two that puts the head's largest |value| in
+  // [2^13, 2^14).  fp8 rows keep them in registers; for bf16 rows (whose
+  // gathers need the registers) every wave stores the same values to LDS.
+  float hfac;  // base-2 logit = S x page scale x hfac
+  f16x8 qf[kFp8 ? KS : 1];
   {
-    // pass 1: largest |component| of the rotated head; pass 2: rotate again, scale, round
-    auto rot = [&](int t, int p, float& y0, float& y1) {
-      const float x0 = u2f(qraw[t][p] << 16), x1 = u2f(qraw[t][p] & 0xFFFF0000u);
-      const float2 cs = cs_s[(32 * t + 8 * g) / 2 + p];
-      y0 = x0 * cs.x - x1 * cs.y;
-      y1 = x0 * cs.y + x1 * cs.x;
-    };
+    // one pass: all table reads are issued together, the rotated values are
+    // kept (nothing else is live yet), then scaled and rounded
+    float y[KS][8];
     float amax = 0.0f;
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        float y0, y1;
-        rot(t, p, y0, y1);
-        amax = fmaxf(amax, fmaxf(fabsf(y0), fabsf(y1)));
+        const float x0 = u2f(qraw[t][p] << 16), x1 = u2f(qraw[t][p] & 0xFFFF0000u);
+        const float2 cs = cs_s[kslot_dim<D, KVDT>(t, g) / 2 + p];
+        y[t][2 * p] = x0 * cs.x - x1 * cs.y;
+        y[t][2 * p + 1] = x0 * cs.y + x1 * cs.x;
+        amax = fmaxf(amax, fmaxf(fabsf(y[t][2 * p]), fabsf(y[t][2 * p + 1])));
       }
     }
     amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
@@ -293,127 +348,190 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
     int e = 0;
     if (amax > 0.0f) (void)frexpf(amax, &e);  // amax < 2^e
     const float qs = ldexpf(1.0f, min(14 - e, 126));
-    hfac = a.scale * sigma / qs * 1.4426950408889634f;  // logits in base 2: p = 2^(x - m)
+    hfac = a.scale / qs * 1.4426950408889634f;  // logits in base 2: p = 2^(x - m)
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
       f16x8 v;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        float y0, y1;
-        rot(t, p, y0, y1);
-        v[2 * p] = (_Float16)(y0 * qs);
-        v[2 * p + 1] = (_Float16)(y1 * qs);
-      }
-      qf[t] = v;
+      for (int c = 0; c < 8; ++c) v[c] = (_Float16)(y[t][c] * qs);
+      if constexpr (kFp8)
+        qf[t] = v;
+      else
+        q_s[t][lane] = v;
     }
   }
 
-  // O for all 64 heads (head group hg, rows 4g + i) over this wave's dims
-  // 16 (wave * NTW + n) + col
-  f32x4 oacc[4][NTW];
+  // ---- this wave's rows: addresses and page scales, for this wave only.
+  // Every row slot of the wave's tiles is written, rows outside the split as
+  // skipped, so the loads below need no guard.
+  constexpr int row_bytes = Raw::ROWB;
+  float ps[kPer];
 #pragma unroll
-  for (int hg = 0; hg < 4; ++hg)
-#pragma unroll
-    for (int n = 0; n < NTW; ++n) oacc[hg][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;  // for head `head` (replicated over g)
+  for (int j = 0; j < kPer; ++j) {
+    const int i = row_of(j);
+    const int r = r0 + i;
+    uint64_t rp = 0;
+    bool in_win = false;
+    int sidx = 0;
+    if (i < RPS && r < r1) rp = resolve_row(a, b, r, pre[j], pre[j], n_sel, N, L, n_win, row_bytes, in_win, sidx);
+    rowptr_s[i] = rp;
+    if constexpr (kFp8) {
+      const float* sc = reinterpret_cast<const float*>(in_win ? a.win.scales : a.kv.scales);
+      ps[j] = rp ? gload<float>(sc + sidx) : -1.0f;
+    } else {
+      ps[j] = rp ? 1.0f : -1.0f;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
 
-#pragma unroll
-  for (int t = 0; t < TILES; ++t) {
-    const int tr0 = r0 + kTileRows * t;
-    if (tr0 >= r1) break;  // uniform over the block
+  const int nt = (r1 - r0 + kTileRows - 1) / kTileRows;
+  const uint8_t* safe = reinterpret_cast<const uint8_t*>(a.kv.codes);
+  // fp8: load tile t of the split into one of this wave's two ring slots
+  // (skipped rows read the pool's first row; their bytes are masked where they
+  // matter)
+  uint8_t* slot0 = tile0_s + wave * RT::BYTES;
+  uint8_t* slot1 = tile1_s + wave * RT::BYTES;
+  auto issue = [&](int t, uint8_t* dst) {
     const int lr0 = kTileRows * t;
-    // ---- write this tile's 32 rows to LDS as f16 (skipped rows as zeros)
-    if (loader) {
-      const f32x4 rok = *reinterpret_cast<const f32x4*>(&ratio_s[lr0 + 4 * q4]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = rok[i] >= 0.0f;
-        f16x8 lo, hi;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        if constexpr (KVDT == HCA_BF16) {
-          const u32x4 w0 = ok ? raw[t].w[i][0] : z, w1 = ok ? raw[t].w[i][1] : z;
+    for (int j = 0; j < RT::INSTR; ++j) {
+      const int pos = 64 * j + lane;  // chunk position this lane fills
+      const int r = pos / RT::CH, p = pos % RT::CH;
+      const int c = (p & ~(RT::G - 1)) | ((p & (RT::G - 1)) ^ RT::f(r));  // the data chunk stored there
+      const uint64_t rp = rowptr_s[lr0 + r];
+      const uint8_t* src = (rp ? reinterpret_cast<const uint8_t*>(rp) : safe) + 16 * c;
+      load_to_lds16(src, dst + 1024 * j);
+    }
+  };
+  Raw ra;  // bf16: register gather
+  if constexpr (kFp8) {
+    if (wave < nt) issue(wave, slot0);
+    if (wave + kAttnWaves < nt) issue(wave + kAttnWaves, slot1);
+  } else {
+    ra.gather(rowptr_s, kTileRows * wave, col, g, safe);
+  }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            lo[2 * q] = (_Float16)u2f(w0[q] << 16);
-            lo[2 * q + 1] = (_Float16)u2f(w0[q] & 0xFFFF0000u);
-            hi[2 * q] = (_Float16)u2f(w1[q] << 16);
-            hi[2 * q + 1] = (_Float16)u2f(w1[q] & 0xFFFF0000u);
-          }
-        } else {
-          const u32x4 w = ok ? raw[t].w[i][0] : z;
+  for (int j = 0; j < kPer; ++j) ps_s[row_of(j)] = ps[j];
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+
+  // O for the block's 16 heads (rows 4g + i) over all dims 16n + col, in units
+  // of sigma: the largest page scale the wave has seen, up to kSigmaSlack
+  f32x4 oacc[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) oacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;  // for head `head` (replicated over g)
+  float sigma = 0.0f, inv_sigma = 0.0f;
+
+  // ---- S^T = K . Q~^T for the tile's two 16-row halves.  fp8: K chunks from
+  // the ring slot; bf16: from the gathered registers, converted to f16 and
+  // also written to the wave's LDS tile for the PV step (skipped rows as zeros)
+  // this wave's f16 tile (bf16 rows)
+  _Float16* ks = reinterpret_cast<_Float16*>((wave < 2 ? tile0_s : tile1_s) + (wave & 1) * TILE_H * 2);
+  auto qk = [&](const Raw& raw, int t, const uint8_t* tile, f32x4 sres[2]) {
+    const int lr0 = kTileRows * t;
+    f32x4 sacc[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) sacc[h][0] = sacc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(tile + RT::at(16 * h + col, Raw::off(u, g) / 16));
+          f16x8 v0, v1;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const f16x2 x = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w[q], 1.0f, false);
             const f16x2 y = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w[q], 1.0f, true);
-            f16x8& dst = q < 2 ? lo : hi;
+            f16x8& dst = q < 2 ? v0 : v1;
             const int o = (q & 1) * 4;
             dst[o + 0] = x[0];
             dst[o + 1] = x[1];
             dst[o + 2] = y[0];
             dst[o + 3] = y[1];
           }
+          sacc[h][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v0, qf[2 * u], sacc[h][0], 0, 0, 0);
+          sacc[h][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v1, qf[2 * u + 1], sacc[h][1], 0, 0, 0);
         }
-        *reinterpret_cast<f16x8*>(&k_s[TL::chunk(4 * q4 + i, 2 * c16)]) = lo;
-        *reinterpret_cast<f16x8*>(&k_s[TL::chunk(4 * q4 + i, 2 * c16 + 1)]) = hi;
+      }
+    } else {
+      bool okr[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) okr[h] = ps_s[lr0 + 16 * h + col] >= 0.0f;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      constexpr int P = Raw::P;
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 w = okr[h] ? raw.w[h][u] : z;
+          f16x8 v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[2 * q] = (_Float16)u2f(w[q] << 16);
+            v[2 * q + 1] = (_Float16)u2f(w[q] & 0xFFFF0000u);
+          }
+          const int cb = 4 * P * (u / P);
+          *reinterpret_cast<f16x8*>(&ks[TL::at(16 * h + col, (cb & 15) + P * g + u % P, cb >> 4)]) = v;
+          sacc[h][u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, q_s[u][lane], sacc[h][u & 1], 0, 0, 0);
+        }
       }
     }
-    lds_barrier();
-
-    // ---- S^T = K . Q~^T for the two 16-row halves: four independent MFMA
-    // chains (half h, k-step parity); lane reads chunk 4kt + g of row 16h + col.
-    // Fragments are read in batches of 8 before their MFMAs issue, so the LDS
-    // latency is paid once per batch rather than once per MFMA.
-    f32x4 sacc[2][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) sacc[h][0] = sacc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int KB = KS < 4 ? KS : 4;  // k-steps per batch
-#pragma unroll
-    for (int kb = 0; kb < KS; kb += KB) {
-      f16x8 kf[KB][2];
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          kf[u][h] = *reinterpret_cast<const f16x8*>(&k_s[TL::chunk(16 * h + col, 4 * (kb + u) + g)]);
-      }
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          sacc[h][u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[u][h], qf[kb + u], sacc[h][u & 1], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 0);  // the LDS reads first,
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KB, 0);  // then the MFMAs
-    }
-    f32x4 sres[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) sres[h] = sacc[h][0] + sacc[h][1];
+  };
+
+  // ---- online softmax and page-scale normalization, then O += P . V.  The V
+  // operand (8 rows of one dim per lane): fp8, one transposing byte read from
+  // the ring slot, skipped rows masked, then converted; bf16, two transposing
+  // 16-bit reads of 4 rows from the wave's f16 tile.
+  auto pv = [&](int t, const uint8_t* tile, const f32x4 sres[2]) {
+    const int lr0 = kTileRows * t;
     // lane: rows 16h + 4g + i, head `head`
-    float x[8], rr[8];
-    float tmax = -INFINITY;
+    float x[8], sc[8];
+    float tmax = -INFINITY, tsig = 0.0f;
+    uint32_t vmask[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const f32x4 rq = *reinterpret_cast<const f32x4*>(&ratio_s[lr0 + 16 * h + 4 * g]);
+      const f32x4 rq = *reinterpret_cast<const f32x4*>(&ps_s[lr0 + 16 * h + 4 * g]);
+      vmask[h] = 0u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool ok = rq[i] >= 0.0f;  // also false past the end of the split
-        rr[4 * h + i] = ok ? rq[i] : 0.0f;
+        vmask[h] |= ok ? 0xFFu << (8 * i) : 0u;
+        sc[4 * h + i] = ok ? rq[i] : 0.0f;
         const float v = ok ? sres[h][i] * rq[i] * hfac : -INFINITY;
         x[4 * h + i] = v;
         tmax = fmaxf(tmax, v);
+        tsig = fmaxf(tsig, sc[4 * h + i]);
       }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tsig = fmaxf(tsig, __shfl_xor(tsig, 16, 64));
+    tsig = fmaxf(tsig, __shfl_xor(tsig, 32, 64));  // the same in every lane
     const bool need = tmax > m_run + kRescaleSlack;
-    float alpha = 1.0f;
-    bool resc = false;
-    if (__any(need)) {
+    const bool grow = tsig > sigma * kSigmaSlack;
+    if (__any(need) || grow) {
       const float m_new = need ? tmax : m_run;
-      alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // 2^-inf = 0 on the first tile
-      resc = __any(m_run != -INFINITY);           // the accumulators hold something to rescale
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // 2^-inf = 0 on the first tile
+      const float fs = grow ? sigma / tsig : 1.0f;
+      if (__any(m_run != -INFINITY)) {  // the accumulators hold something to rescale
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64) * fs;  // factor of head 4g + i
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[n][i] *= al[i];
+        }
+      }
       l_run *= alpha;
       m_run = m_new;
+      if (grow) {
+        sigma = tsig;
+        inv_sigma = 1.0f / tsig;
+      }
     }
     f16x8 pf;
     float psum = 0.0f;
@@ -421,76 +539,145 @@ __global__ __launch_bounds__(kAttnThreads, TILES == 1 ? 2 : 1) void attn_split_k
     for (int j = 0; j < 8; ++j) {
       const float p = x[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[j] - m_run);
       psum += p;
-      pf[j] = (_Float16)(p * rr[j]);
+      pf[j] = (_Float16)(p * (sc[j] * inv_sigma));
     }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
     l_run += psum;
 
-    // ---- share P and the rescale factors: each wave then accumulates O for
-    // all 64 heads over its quarter of the dims, so one V fragment feeds four
-    // MFMAs (one per head group)
-    p_s[wave][lane] = pf;
-    if (g == 0) al_s[wave][col] = alpha;
-    if (lane == 0) rs_s[wave] = resc ? 1 : 0;
-    lds_barrier();
+    constexpr int VB = NB < 8 ? NB : 8;  // column blocks per batch
+    if constexpr (kFp8) {
+      // source lane j of a 16-lane group addresses row R(j / 2) at byte 8 (j % 2)
+      // of the column block; output lane i then holds rows R(0..7) at dim i
+      const int k = col >> 1;
+      const int vrow = k < 4 ? 4 * g + k : 16 + 4 * g + k - 4;
+      const int half = 8 * (col & 1);
 #pragma unroll
-    for (int hg = 0; hg < 4; ++hg) {
-      if (__builtin_amdgcn_readfirstlane(rs_s[hg])) {  // the same for every lane
-        float al[4];
+      for (int n0 = 0; n0 < NB; n0 += VB) {
+        u32x2 raw8[VB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = al_s[hg][4 * g + i];
+        for (int u = 0; u < VB; ++u) {
+          const i2v r8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) i2v*)(tile + RT::at(vrow, n0 + u) + half));
+          raw8[u] = __builtin_bit_cast(u32x2, r8);
+        }
 #pragma unroll
-        for (int n = 0; n < NTW; ++n) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[hg][n][i] *= al[i];
+        for (int u = 0; u < VB; ++u) {
+          const uint32_t lo = raw8[u][0] & vmask[0], hi = raw8[u][1] & vmask[1];
+          const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)lo, 1.0f, false);
+          const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)lo, 1.0f, true);
+          const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)hi, 1.0f, false);
+          const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)hi, 1.0f, true);
+          const f16x8 vf = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+          oacc[n0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, vf, oacc[n0 + u], 0, 0, 0);
         }
       }
-    }
-    f16x8 pa[4];
+    } else {
+      // lane reads row R (and R + 16) at dims 16n + 4(col & 3): chunk 2n + (col & 3) / 2
+      const int vr = 4 * g + (col >> 2);
+      const int c01 = (col & 3) >> 1;
 #pragma unroll
-    for (int hg = 0; hg < 4; ++hg) pa[hg] = p_s[hg][lane];
-
-    // ---- O += P . V  (V operand: two transposing LDS reads of 4 rows each)
-    // lane reads row R (and R + 16) at dims 16nn + 4(col & 3): chunk 2nn + (col & 3) / 2
-    const int vr = 4 * g + (col >> 2);
-    f16x8 vf[NTW];
+      for (int n0 = 0; n0 < NB; n0 += VB) {
+        f16x8 vf[VB];
 #pragma unroll
-    for (int n = 0; n < NTW; ++n) {
-      const int nn = wave * NTW + n;
-      const int vo = TL::chunk(vr, 2 * nn + ((col & 3) >> 1)) + 4 * (col & 1);
-      const s4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(&k_s[vo]));
-      const s4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s4*)(&k_s[vo + 16 * TL::STR]));
-      const u32x4 vv = {__builtin_bit_cast(u32x2, v0)[0], __builtin_bit_cast(u32x2, v0)[1],
-                        __builtin_bit_cast(u32x2, v1)[0], __builtin_bit_cast(u32x2, v1)[1]};
-      vf[n] = __builtin_bit_cast(f16x8, vv);
-    }
+        for (int u = 0; u < VB; ++u) {
+          const int n = n0 + u;
+          const int vo = TL::at(vr, 2 * (n & 7) + c01, n >> 3) + 4 * (col & 1);
+          const s4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(&ks[vo]));
+          const s4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s4*)(&ks[vo + 16 * TL::STR]));
+          const u32x4 vv = {__builtin_bit_cast(u32x2, v0)[0], __builtin_bit_cast(u32x2, v0)[1],
+                            __builtin_bit_cast(u32x2, v1)[0], __builtin_bit_cast(u32x2, v1)[1]};
+          vf[u] = __builtin_bit_cast(f16x8, vv);
+        }
 #pragma unroll
-    for (int n = 0; n < NTW; ++n) {
-#pragma unroll
-      for (int hg = 0; hg < 4; ++hg)
-        oacc[hg][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[hg], vf[n], oacc[hg][n], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NTW + 4, 0);  // the LDS reads first,
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NTW, 0);      // then the MFMAs
-    lds_barrier();
-  }
-
-  // ---- partials: o (unnormalized, relative to m_run, sigma folded back), m, l
-#pragma unroll
-  for (int hg = 0; hg < 4; ++hg) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = hb * kHeadsPerBlock + hg * 16 + 4 * g + i;
-      if (h < H) {
-        float* dst = opart + (part + h) * D + 16 * wave * NTW + col;
-#pragma unroll
-        for (int n = 0; n < NTW; ++n) dst[16 * n] = oacc[hg][n][i] * sigma;
+        for (int u = 0; u < VB; ++u) oacc[n0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, vf[u], oacc[n0 + u], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * VB, 0);  // the LDS reads first,
+        __builtin_amdgcn_sched_group_barrier(0x008, VB, 0);      // then the MFMAs
       }
     }
+  };
+
+  // ---- the wave's tiles wave, wave + 4, ...  fp8: tile t is in ring slot sl
+  // and tile t + 4 may still be loading behind it; a slot is refilled once its
+  // reads are done.  bf16: the next tile's gather is issued as soon as the
+  // current one's registers are converted.  LDS accesses of one wave complete
+  // in issue order, so what qk writes is what pv reads, and pv's reads precede
+  // the next qk's writes.
+  if constexpr (kFp8) {
+    // one ring slot: wait for its tile (the other slot's tile may still be
+    // loading behind it), use it, then refill it
+    auto step = [&](int t, uint8_t* slot) {
+      if (t + kAttnWaves < nt)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(RT::INSTR));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      asm volatile("" ::: "memory");
+      f32x4 sres[2];
+      qk(ra, t, slot, sres);
+      pv(t, slot, sres);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & ~0x0F00);  // lgkmcnt(0): the slot's reads are done
+      asm volatile("" ::: "memory");
+      if (t + 2 * kAttnWaves < nt) issue(t + 2 * kAttnWaves, slot);
+    };
+    int sl = 0;
+    for (int t = wave; t < nt; t += kAttnWaves, sl ^= 1) step(t, sl ? slot1 : slot0);
+  } else {
+    for (int t = wave; t < nt; t += kAttnWaves) {
+      f32x4 sres[2];
+      qk(ra, t, nullptr, sres);
+      if (t + kAttnWaves < nt) ra.gather(rowptr_s, kTileRows * (t + kAttnWaves), col, g, safe);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+      pv(t, nullptr, sres);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+    }
   }
-  if (g == 0 && hv) ml[part + head] = make_float2(m_run * 0.6931471805599453f, l_run);  // m back to base e
+
+  // ---- merge the four waves' states: o (unnormalized, relative to the block
+  // max), m, l.  The tiles' LDS holds each wave's O as [head quad][dim][4 heads].
+  if constexpr (kFp8) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load into the tiles is in flight
+  __syncthreads();  // every wave is done with its LDS tiles
+  // wave w's O: [4 head quads][D][4] floats at (w < 2 ? first : second array) + (w & 1) x 64 D bytes
+  auto o_of = [&](int w) { return reinterpret_cast<float*>((w < 2 ? tile0_s : tile1_s) + (w & 1) * 64 * D); };
+  {
+    float* o_s = o_of(wave);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) *reinterpret_cast<f32x4*>(&o_s[(g * D + 16 * n + col) * 4]) = oacc[n] * sigma;
+  }
+  if (g == 0) ml_s[wave][col] = make_float2(m_run, l_run);
+  __syncthreads();
+  if (threadIdx.x < kHeadsPerBlock) {
+    const int hh = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml_s[w][hh].x);
+    float l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float wt = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml_s[w][hh].x - M);  // 0 for an empty wave
+      wt_s[w][hh] = wt;
+      l += wt * ml_s[w][hh].y;
+    }
+    if (h0 + hh < H)
+      ml[part + h0 + hh] = M == -INFINITY ? make_float2(-INFINITY, 0.0f) : make_float2(M * 0.6931471805599453f, l);
+  }
+  __syncthreads();
+  // thread -> (4 consecutive heads, one dim): consecutive threads store consecutive dims
+  for (int e = threadIdx.x; e < D * (kHeadsPerBlock / 4); e += kAttnThreads) {
+    const int hq = e / D, dim = e - hq * D;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const f32x4 o = *reinterpret_cast<const f32x4*>(&o_of(w)[(hq * D + dim) * 4]);
+      const f32x4 wt = *reinterpret_cast<const f32x4*>(&wt_s[w][4 * hq]);
+      acc += wt * o;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int h = h0 + 4 * hq + k;
+      if (h < H) opart[(part + h) * D + dim] = acc[k];
+    }
+  }
 }
 
 // Merge the splits of one (sequence, head), then inverse RoPE at L-1.  The
@@ -591,26 +778,17 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
 }
 
 template <int D, int KVDT>
-static void launch_split(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.plan.splits, a.B, a.plan.head_blocks);
-  switch (a.plan.tiles) {
-    case 1: hipLaunchKernelGGL((attn_split_kernel<D, KVDT, 1>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_split_kernel<D, KVDT, 2>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((attn_split_kernel<D, KVDT, 3>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_split_kernel<D, KVDT, 4>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((attn_split_kernel<D, KVDT, 5>), grid, dim3(kAttnThreads), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((attn_split_kernel<D, KVDT, 6>), grid, dim3(kAttnThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_split_kernel<D, KVDT, kMaxTiles>), grid, dim3(kAttnThreads), 0, s, a); break;
-  }
+static hipError_t launch_split(const AttnArgs& a, hipStream_t s) {
+  const int64_t groups = (int64_t)a.plan.splits * a.B;
+  const int64_t blocks = (groups + kXcds - 1) / kXcds * kXcds * a.plan.head_blocks;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((attn_split_kernel<D, KVDT>), dim3((unsigned)blocks), dim3(kAttnThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_attn_d(const AttnArgs& a, hipStream_t s) {
-  if (a.kv.dtype == HCA_FP8_E4M3)
-    launch_split<D, HCA_FP8_E4M3>(a, s);
-  else
-    launch_split<D, HCA_BF16>(a, s);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = a.kv.dtype == HCA_FP8_E4M3 ? launch_split<D, HCA_FP8_E4M3>(a, s) : launch_split<D, HCA_BF16>(a, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel<D>, dim3(a.H, a.B), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -66,8 +66,8 @@ struct AttnPlan {
   int rows_max;     // upper bound of rows of any sequence
   int splits;       // splits per sequence
   int rows_per_split;
-  int tiles;        // 32-row tiles per split (all in flight at once)
-  int head_blocks;  // ceil(H / 64)
+  int tiles;        // 32-row tiles per split
+  int head_blocks;  // ceil(H / 16)
   size_t o_off, ml_off, total;
 };
 constexpr int kAttnMaxSplits = 4096;  // splits per sequence the combine kernel handles
