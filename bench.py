@@ -11,10 +11,9 @@ K=V dim 512 in fp8 E4M3 pages with a per-page fp32 scale, 64 query heads, a
 and reported on its own.
 
 A step is one decode step of the whole stack for the batch: per layer the
-decode update (re-fold of the open group and re-quantization of its page, the
-window insert of the new token, the open indexer page), then indexer_topk (c4a)
-and paged_hybrid_decode.  The three update chains are independent and run on
-separate streams that join before the layer's attention; layers stay in
+decode update (re-fold of the open group and its page, the window insert of
+the new token and its page, the open indexer page: one kv_compress_insert_jobs
+launch), then indexer_topk (c4a) and paged_hybrid_decode; layers stay in
 order.  The step is captured once in a HIP graph and replayed; `value` is
 decode tokens/s = B / step time.
 
@@ -114,14 +113,14 @@ def score_bytes(kind, B, L, d_idx=128, h_idx=16):
 
 
 def update_bytes(kind, B, d, d_idx=128):
-    """Bytes moved by the decode update of one layer (open group, open page,
-    window page, open indexer page)."""
+    """Bytes moved by the decode update of one layer while page scales hold
+    (open group, open page, window page, open indexer page)."""
     m, epp = kind.m, 256 // kind.m
     b = m * d * 2 + m * 4 + d * 4  # ring tokens + logits, entry write
-    b += epp * d * 4 + epp * d + 4  # open page: staging read, codes + scale write
-    b += d * 2 + d * 4 + 256 * d * 4 + 256 * d + 4  # window token, its row, window page re-quantization
+    b += (epp - 1) * d * 4 + d + 8  # open page: earlier staging rows (its amax), the row's codes, scale
+    b += d * 2 + 4 + d * 4 + d + 8  # window token + logit, its staging row, its codes, scale
     if kind.topk is not None:
-        b += epp * d_idx * 4 + epp * (d_idx // 2 + d_idx // 32)
+        b += d_idx * 4 + d_idx // 2 + d_idx // 32  # open indexer row: staging, codes, scales
     return B * b
 
 
@@ -169,11 +168,15 @@ def build_state(w, n_layers, torch, hca, gen, log):
         pre_bytes += B * (L * d * 2 + L * 4 + 2 * N * d * 4 + N * d + 4 * (-(-N // epp)))
         # decode-update state: open group ring, open page staging
         g_open = (L - 1) // m
-        lay.ring_x = xi[:, g_open * m: L].contiguous()
-        lay.ring_z = z[:, g_open * m: L].contiguous()
+        nt_open = L - g_open * m
+        lay.ring_x = torch.zeros((B, m, d), dtype=torch.int16, device="cuda")
+        lay.ring_x[:, :nt_open] = xi[:, g_open * m: L]
+        lay.ring_z = torch.zeros((B, m), dtype=torch.float32, device="cuda")
+        lay.ring_z[:, :nt_open] = z[:, g_open * m: L]
         lay.beta = beta
         e_open0 = (g_open // epp) * epp
-        lay.stage = ent[:, e_open0: N].clone()
+        lay.stage = torch.zeros((B, epp, d), dtype=torch.float32, device="cuda")
+        lay.stage[:, : N - e_open0] = ent[:, e_open0: N]
         lay.slot = g_open - e_open0
         lay.pos0 = dev(np.full(B, g_open * m, np.int32))
         lay.ntok = dev(np.full(B, L - g_open * m, np.int32))
@@ -189,7 +192,8 @@ def build_state(w, n_layers, torch, hca, gen, log):
         lay.win = hca.PagedCache.empty(PW, 256, d, w.kv_dtype)
         hca.kv_quantize_page(wrows, dev(np.full(B, t0, np.int32)), dev(np.full(B, nw, np.int32)), nw, wtable, lay.win)
         tw0 = ((L - 1) // 256) * 256
-        lay.wstage = wrows[:, tw0 - t0:].clone()
+        lay.wstage = torch.zeros((B, 256, d), dtype=torch.float32, device="cuda")
+        lay.wstage[:, : L - tw0] = wrows[:, tw0 - t0:]
         lay.wslot = (L - 1) - tw0
         lay.x_last = xi[:, L - 1: L].contiguous()
         lay.z_last = z[:, L - 1: L].contiguous()
@@ -205,7 +209,8 @@ def build_state(w, n_layers, torch, hca, gen, log):
             keys = gen.device_normal((B, N, kind.d_idx), 1.0, (0, w.cid, li, gen.S_IDXK))
             lay.idx = hca.PagedCache.empty(P, epp, kind.d_idx, kind.idx_dtype)
             hca.kv_quantize_page(keys, zeros_b, dev(np.full(B, N, np.int32)), N, table, lay.idx)
-            lay.istage = keys[:, e_open0: N].clone()
+            lay.istage = torch.zeros((B, epp, kind.d_idx), dtype=torch.float32, device="cuda")
+            lay.istage[:, : N - e_open0] = keys[:, e_open0: N]
             del keys
             lay.qi = dev(gen.index_queries(w, li, kind.h_idx, kind.d_idx).view(np.int16))
             lay.wi = dev(gen.index_weights(w, li, kind.h_idx))
@@ -217,49 +222,33 @@ def build_state(w, n_layers, torch, hca, gen, log):
         torch.cuda.synchronize()
         if li % 10 == 0 or li == n_layers - 1:
             log(f"prefilled layer {li + 1}/{n_layers} ({kind.name})")
-    # decode-update workspaces (one per side stream) and the side streams (default priority)
-    wq_main = max(hca.kv_quantize_page_workspace(B, l.stage.shape[1], l.kv) for l in layers)
-    wq_win = max(hca.kv_quantize_page_workspace(B, l.wstage.shape[1], l.win) for l in layers)
-    shared = dict(table=table, wtable=wtable, lens=lens, wsq_main=hca.workspace(wq_main),
-                  wsq_win=hca.workspace(wq_win), streams=(torch.cuda.Stream(), torch.cuda.Stream()))
+    shared = dict(table=table, wtable=wtable, lens=lens)
     return layers, shared, dict(ms=pre_ms, bytes=pre_bytes)
 
 
 def decode_step(w, layers, shared, ws_idx, ws_att, hca, update=True, attend=True):
-    """One decode step of the stack.  Per layer, the three independent parts of
-    the update run on their own streams (window insert; open-group re-fold and
-    its page; the open indexer page, then the indexer, on the main stream) and
-    join before the layer's attention, which the next layer waits for."""
+    """One decode step of the stack.  Per layer, the update is one launch (the
+    window insert with its page, the open group's re-fold with its page and,
+    for c4a, the open indexer page), then the indexer (c4a) and the attention,
+    which the next layer's update waits for."""
     import torch
     L, W = w.L, w.window
     table, wtable, lens = shared["table"], shared["wtable"], shared["lens"]
-    s_main = torch.cuda.current_stream()
-    s_win, s_fold = shared["streams"]
-    wsq_main, wsq_win = shared["wsq_main"], shared["wsq_win"]
     scale = 1.0 / math.sqrt(w.d)
     for lay in layers:
         kind = lay.kind
         m = kind.m
         if update:
-            s_win.wait_stream(s_main)
-            s_fold.wait_stream(s_main)
-            with torch.cuda.stream(s_win):
-                # window insert of the newest token, then its page
-                hca.kv_compress(lay.x_last, lay.z_last, lay.zero1, lay.wpos0, lay.one, 1, w.theta,
-                                lay.wstage[:, lay.wslot:], 1)
-                hca.kv_quantize_page(lay.wstage, lay.we0, lay.wne, lay.wstage.shape[1], wtable, lay.win, ws=wsq_win)
-            with torch.cuda.stream(s_fold):
-                # open group re-fold -> its slot in the open page staging -> re-quantize the open page
-                hca.kv_compress(lay.ring_x, lay.ring_z, lay.beta, lay.pos0, lay.ntok, m, w.theta,
-                                lay.stage[:, lay.slot:], m)
-                hca.kv_quantize_page(lay.stage, lay.e0, lay.ne, lay.stage.shape[1], table, lay.kv, ws=wsq_main)
+            jobs = [hca.insert_job(lay.wstage, lay.wpos0, lay.we0, wtable, lay.win, 1, x=lay.x_last,
+                                   gate_logit=lay.z_last, pos_bias=lay.zero1, ntok=lay.one, rope_theta=w.theta,
+                                   append=True),
+                    hca.insert_job(lay.stage, lay.pos0, lay.e0, table, lay.kv, m, x=lay.ring_x, gate_logit=lay.ring_z,
+                                   pos_bias=lay.beta, ntok=lay.ntok, rope_theta=w.theta, append=True)]
             if kind.topk is not None:
-                hca.kv_quantize_page(lay.istage, lay.e0, lay.ne, lay.istage.shape[1], table, lay.idx)
+                jobs.append(hca.insert_job(lay.istage, lay.pos0, lay.e0, table, lay.idx, m, append=True))
+            hca.kv_compress_insert_jobs(jobs, w.B)
         if attend and kind.topk is not None:
             hca.indexer_topk(lay.qi, lay.wi, lay.idx, table, lens, L, m, kind.topk, lay.sel, lay.sel_n, ws_idx)
-        if update:
-            s_main.wait_stream(s_win)
-            s_main.wait_stream(s_fold)
         if attend:
             if kind.topk is not None:
                 hca.paged_hybrid_decode(lay.q, lay.kv, table, lay.win, wtable, lens, L, m, W, lay.sel, lay.sel_n,

@@ -27,7 +27,9 @@ STATUS = {0: "HCA_OK", 1: "HCA_ERR_INVALID", 2: "HCA_ERR_UNSUPPORTED", 3: "HCA_E
 
 #: every symbol the C headers declare (include/hca.h and include/hca_testing.h)
 EXPORTS = (
-    "hca_status_string", "hca_version", "kv_compress", "kv_quantize_page_workspace", "kv_quantize_page",
+    "hca_status_string", "hca_version", "kv_compress", "kv_compress_insert", "kv_compress_insert_jobs",
+    "kv_quantize_page_workspace",
+    "kv_quantize_page",
     "indexer_topk_workspace",
     "indexer_topk", "paged_hybrid_decode_workspace", "paged_hybrid_decode", "kv_gather",
     "hca_host_e4m3_encode", "hca_host_e2m1_encode", "hca_host_bf16_encode", "hca_probe_decode", "hca_probe_mfma",
@@ -46,6 +48,15 @@ class CPagedCache(ctypes.Structure):
                 ("epp", ctypes.c_int32), ("dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
+class CInsertJob(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("x_stride_b", ctypes.c_int64), ("gate_logit", ctypes.c_void_p),
+                ("z_stride_b", ctypes.c_int64), ("pos_bias", ctypes.c_void_p), ("pos0", ctypes.c_void_p),
+                ("ntok", ctypes.c_void_p), ("m", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("stage", ctypes.c_void_p), ("stage_stride_b", ctypes.c_int64), ("e0", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("bt_stride", ctypes.c_int32), ("dst", CPagedCache),
+                ("append", ctypes.c_int32)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I32, _I64, _F32, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -62,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.hca_status_string.argtypes = [ctypes.c_int]
         L.hca_version.restype = ctypes.c_char_p
         L.kv_compress.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _I64, _P]
+        L.kv_compress_insert.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _F32, _P, _I64, _P, _P, _I32,
+                                         CPagedCache, _I32, _P]
+        L.kv_compress_insert_jobs.argtypes = [ctypes.POINTER(CInsertJob), _I32, _I32, _P]
         L.kv_quantize_page_workspace.argtypes = [_I32, _I32, CPagedCache]
         L.kv_quantize_page_workspace.restype = _SZ
         L.kv_quantize_page.argtypes = [_P, _I64, _P, _P, _I32, _I32, _P, _I32, CPagedCache, _P, _SZ, _P]
@@ -149,6 +163,35 @@ def kv_compress(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, 
     _check(lib().kv_compress(_ptr(x), x.stride(0), _ptr(gate_logit), gate_logit.stride(0), _ptr(pos_bias),
                              _ptr(pos0), _ptr(ntok), B, max_ntok, d, m, rope_theta, _ptr(out), out.stride(0),
                              _stream(stream)), "kv_compress")
+
+
+def kv_compress_insert(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, stage, e0, block_table,
+                       dst: PagedCache, append: bool = False, stream=None):
+    """Decode-step update of one pool in one launch: x bf16 [B, m, d] (the open
+    group's tokens); gate_logit f32 [B, m]; pos_bias f32 [m]; pos0, ntok, e0
+    int32 [B]; stage f32 [B, epp, d] (the open page's staging); block_table
+    int32 [B, nb]."""
+    B = x.shape[0]
+    _check(lib().kv_compress_insert(_ptr(x), x.stride(0), _ptr(gate_logit), gate_logit.stride(0), _ptr(pos_bias),
+                                    _ptr(pos0), _ptr(ntok), B, m, rope_theta, _ptr(stage), stage.stride(0), _ptr(e0),
+                                    _ptr(block_table), block_table.stride(0), dst.c(), 1 if append else 0,
+                                    _stream(stream)), "kv_compress_insert")
+
+
+def insert_job(stage, pos0, e0, block_table, dst: PagedCache, m: int, x=None, gate_logit=None, pos_bias=None,
+               ntok=None, rope_theta: float = 0.0, append: bool = False) -> "CInsertJob":
+    """One job of kv_compress_insert_jobs (x None: the open row is already in stage).
+    The tensors must stay alive until the call that takes the job is enqueued."""
+    return CInsertJob(_ptr(x), 0 if x is None else x.stride(0), _ptr(gate_logit),
+                      0 if gate_logit is None else gate_logit.stride(0), _ptr(pos_bias), _ptr(pos0), _ptr(ntok), m,
+                      rope_theta, _ptr(stage), stage.stride(0), _ptr(e0), _ptr(block_table), block_table.stride(0),
+                      dst.c(), 1 if append else 0)
+
+
+def kv_compress_insert_jobs(jobs, B: int, stream=None):
+    """Several kv_compress_insert calls over the same B sequences in one launch."""
+    arr = (CInsertJob * max(len(jobs), 1))(*jobs)
+    _check(lib().kv_compress_insert_jobs(arr, len(jobs), B, _stream(stream)), "kv_compress_insert_jobs")
 
 
 def kv_quantize_page_workspace(B: int, max_ne: int, dst: PagedCache) -> int:

@@ -64,6 +64,61 @@ hca_status kv_compress(const uint16_t* x, int64_t x_stride_b, const float* gate_
   return from_hip(launch_compress(a, (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+// one job of a fused insert: validated on the host, nothing launched on failure
+hca_status make_insert(const hca_insert_job& j, int32_t B, InsertArgs& out) {
+  if (j.bt_stride < 1 || (j.append != 0 && j.append != 1)) return HCA_ERR_INVALID;
+  if (!valid_m(j.m) || !cache_ok(j.dst) || j.dst.epp != 256 / j.m) return HCA_ERR_INVALID;
+  const int d = j.dst.dim;
+  if (d > 2048) return HCA_ERR_UNSUPPORTED;
+  const bool fold = j.x != nullptr;
+  if (fold && (!(j.rope_theta > 0.0f) || !isfinite(j.rope_theta))) return HCA_ERR_INVALID;
+  if (!j.pos0 || !j.stage || !j.e0 || !j.block_table) return HCA_ERR_INVALID;
+  if (fold && (!j.gate_logit || !j.pos_bias || !j.ntok || !aligned(j.x, 16) || j.x_stride_b % 8 != 0))
+    return HCA_ERR_INVALID;
+  if (!aligned(j.stage, 16) || j.stage_stride_b % 4 != 0) return HCA_ERR_INVALID;
+  if (B > 1 && j.stage_stride_b < (int64_t)j.dst.epp * d) return HCA_ERR_INVALID;
+  if (fold && B > 1 && (j.x_stride_b < (int64_t)j.m * d || j.z_stride_b < j.m)) return HCA_ERR_INVALID;
+  out = InsertArgs{CompressArgs{j.x, j.x_stride_b, j.gate_logit, j.z_stride_b, j.pos_bias, j.pos0, j.ntok, B, j.m, d,
+                                j.m, j.rope_theta, nullptr, 0},
+                   j.stage, j.stage_stride_b, j.e0, j.block_table, j.bt_stride, j.dst, j.append};
+  return HCA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+hca_status kv_compress_insert(const uint16_t* x, int64_t x_stride_b, const float* gate_logit, int64_t z_stride_b,
+                              const float* pos_bias, const int32_t* pos0, const int32_t* ntok, int32_t B, int32_t m,
+                              float rope_theta, float* stage, int64_t stage_stride_b, const int32_t* e0,
+                              const int32_t* block_table, int32_t bt_stride, hca_paged_cache dst, int32_t append,
+                              void* stream) {
+  if (B < 0) return HCA_ERR_INVALID;
+  if (!x) return HCA_ERR_INVALID;  // this entry point always folds
+  const hca_insert_job j{x, x_stride_b, gate_logit, z_stride_b, pos_bias, pos0, ntok, m, rope_theta, stage,
+                         stage_stride_b, e0, block_table, bt_stride, dst, append};
+  InsertJobs jobs{};
+  const hca_status st = make_insert(j, B, jobs.job[0]);
+  if (st != HCA_OK || B == 0) return st;
+  jobs.n = 1;
+  return from_hip(launch_insert(jobs, B, (hipStream_t)stream));
+}
+
+hca_status kv_compress_insert_jobs(const hca_insert_job* jobs, int32_t n_jobs, int32_t B, void* stream) {
+  if (B < 0 || n_jobs < 0 || (n_jobs > 0 && !jobs)) return HCA_ERR_INVALID;
+  if (n_jobs > kMaxInsertJobs) return HCA_ERR_UNSUPPORTED;
+  InsertJobs all{};
+  for (int i = 0; i < n_jobs; ++i) {
+    const hca_status st = make_insert(jobs[i], B, all.job[i]);
+    if (st != HCA_OK) return st;
+  }
+  if (B == 0 || n_jobs == 0) return HCA_OK;
+  all.n = n_jobs;
+  return from_hip(launch_insert(all, B, (hipStream_t)stream));
+}
+
 size_t kv_quantize_page_workspace(int32_t B, int32_t max_ne, hca_paged_cache dst) {
   if (B < 0 || max_ne < 0 || !cache_ok(dst)) return 0;
   return quantize_ws_bytes(B, max_ne, dst);

@@ -684,23 +684,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
 // threads form SG split groups; a group's lanes cover the D dims with 16-byte
 // loads and the group takes every SG-th split.  All partial loads of a round
 // (up to kCombU splits per thread) are issued together with the (m, l) loads
-// of the splits, so a round costs one memory round trip; the groups' sums meet
-// in LDS in a fixed order.
+// of the splits, before the sequence length is read, so a round costs one
+// memory round trip; the groups' sums meet in LDS in a fixed order.
 constexpr int kCombThreads = 256;
-constexpr int kCombU = 36;
+constexpr int kCombU = 16;
 
 template <int D>
 __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) {
   constexpr int TPG = D / 4;                  // threads per split group (one float4 each)
   constexpr int SG = kCombThreads / TPG;      // split groups: 2 (D=512) .. 16 (D=64)
+  constexpr int kPairs = (D / 2 + kCombThreads - 1) / kCombThreads;  // RoPE pairs per thread
   const int h = blockIdx.x, b = blockIdx.y;
   const int H = a.H;
   const int grp = threadIdx.x / TPG, li = threadIdx.x % TPG;
-  const int L = clampi(a.lens[b], 0, a.max_len);
-  const int N = (L + a.m - 1) / a.m;
-  const int n_sel = a.sel ? clampi(a.sel_n[b], 0, a.k) : N;
-  const int rows_b = n_sel + min(a.window, L);
-  const int S = min(a.plan.splits, (rows_b + a.plan.rows_per_split - 1) / a.plan.rows_per_split);
+  const int Smax = a.plan.splits;
   const float2* ml = reinterpret_cast<const float2*>(a.ws + a.plan.ml_off) + (size_t)b * a.plan.splits * H + h;
   const f32x4* opart =
       reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.ws + a.plan.o_off) + ((size_t)b * a.plan.splits * H + h) * D) + li;
@@ -709,16 +706,33 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
   __shared__ float red_s[kCombThreads / 64];
   __shared__ f32x4 acc_s[SG][TPG];
 
-  // first round of partial loads, issued before anything else waits
+  // first round of partial loads and the first kCombThreads (m, l) pairs,
+  // issued before the lengths are known (every split the plan has is in the
+  // workspace; the ones past this sequence's end get weight 0)
   f32x4 o[kCombU];
 #pragma unroll
   for (int u = 0; u < kCombU; ++u) {
     const int s = grp + SG * u;
-    o[u] = opart[(size_t)(s < S ? s : 0) * ostride];
+    o[u] = s < Smax ? opart[(size_t)s * ostride] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float2 ml0 = (int)threadIdx.x < Smax ? ml[(size_t)threadIdx.x * H] : make_float2(-INFINITY, 0.0f);
+  const int L = clampi(a.lens[b], 0, a.max_len);
+  const int N = (L + a.m - 1) / a.m;
+  const int n_sel = a.sel ? clampi(a.sel_n[b], 0, a.k) : N;
+  const int rows_b = n_sel + min(a.window, L);
+  const int S = min(Smax, (rows_b + a.plan.rows_per_split - 1) / a.plan.rows_per_split);
+  // the inverse rotation at L-1, while the loads are in flight
+  float2 cs[kPairs];
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) {
+    const int pi = threadIdx.x + kCombThreads * k;
+    float c = 1.0f, sn = 0.0f;
+    if (pi < D / 2) rope_cs((double)(L - 1), rope_inv_freq(pi, D, a.theta), c, sn);
+    cs[k] = make_float2(c, sn);
   }
   // split maxima -> M; weights w_s = exp(m_s - M) (0 for empty splits); tot = sum w_s l_s
-  float mloc = -INFINITY;
-  for (int s = threadIdx.x; s < S; s += kCombThreads) mloc = fmaxf(mloc, ml[(size_t)s * H].x);
+  float mloc = (int)threadIdx.x < S ? ml0.x : -INFINITY;
+  for (int s = threadIdx.x + kCombThreads; s < S; s += kCombThreads) mloc = fmaxf(mloc, ml[(size_t)s * H].x);
   mloc = wave_max(mloc);
   if ((threadIdx.x & 63) == 0) red_s[threadIdx.x >> 6] = mloc;
   __syncthreads();
@@ -732,7 +746,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
   }
   float tloc = 0.0f;
   for (int s = threadIdx.x; s < S; s += kCombThreads) {
-    const float2 v = ml[(size_t)s * H];
+    const float2 v = s < kCombThreads ? ml0 : ml[(size_t)s * H];
     const float w = v.y > 0.0f ? expf(v.x - M) : 0.0f;
     w_s[s] = w;
     tloc += w * v.y;
@@ -753,13 +767,16 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
 #pragma unroll
     for (int u = 0; u < kCombU; ++u) {  // next round (more than SG * kCombU splits)
       const int s = s0 + SG * (kCombU + u);
-      o[u] = opart[(size_t)(s < S ? s : 0) * ostride];
+      o[u] = s < S ? opart[(size_t)s * ostride] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
   acc_s[grp][li] = acc;
   __syncthreads();
   const float inv_tot = 1.0f / tot;
-  for (int pi = threadIdx.x; pi < D / 2; pi += kCombThreads) {
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) {
+    const int pi = threadIdx.x + kCombThreads * k;
+    if (pi >= D / 2) break;
     float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
     for (int gq = 0; gq < SG; ++gq) {
@@ -769,10 +786,8 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
     }
     o0 *= inv_tot;
     o1 *= inv_tot;
-    float c, sn;
-    rope_cs((double)(L - 1), rope_inv_freq(pi, D, a.theta), c, sn);
-    out[2 * pi] = o0 * c + o1 * sn;       // rotation by -angle
-    out[2 * pi + 1] = -o0 * sn + o1 * c;
+    out[2 * pi] = o0 * cs[k].x + o1 * cs[k].y;  // rotation by -angle
+    out[2 * pi + 1] = -o0 * cs[k].y + o1 * cs[k].x;
   }
   if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)b * H + h] = M + logf(tot);
 }

@@ -6,16 +6,14 @@
 // HBM-bound stream: each thread owns 8 consecutive dims (one 16-byte bf16
 // load per token) so a row of d dims is read by d/8 adjacent lanes in one
 // coalesced sweep.  Small m: a row-group of d/8 threads folds whole entries on
-// its own.  Large m: the 256 threads of a block share one entry (or, when
-// there are few entries, as in a decode step, one 64-dim slice of it), each
-// row-group folding a strided subset of its tokens, reduced through LDS.
+// its own.  Large m: the 256 threads of a block share one entry, each
+// row-group folding a strided subset of its tokens (a batch's loads all in
+// flight before the first is summed), reduced through LDS.
 #include "hca_common.h"
 #include "hca_internal.h"
 
 namespace hca {
 
-constexpr int kCompressThreads = 256;
-constexpr int kSmallM = 16;
 
 __device__ __forceinline__ void load_bf16x8(const uint16_t* p, float v[8]) {
   const u32x4 raw = *reinterpret_cast<const u32x4*>(p);
@@ -26,7 +24,7 @@ __device__ __forceinline__ void load_bf16x8(const uint16_t* p, float v[8]) {
   }
 }
 
-__device__ __forceinline__ void rope_store8(float* dst, const float acc[8], double pos, const double inv[4]) {
+__device__ __forceinline__ void rope_store8(float* dst, float* lds, const float acc[8], double pos, const double inv[4]) {
   float o[8];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
@@ -38,15 +36,23 @@ __device__ __forceinline__ void rope_store8(float* dst, const float acc[8], doub
   f32x4* d4 = reinterpret_cast<f32x4*>(dst);
   d4[0] = f32x4{o[0], o[1], o[2], o[3]};
   d4[1] = f32x4{o[4], o[5], o[6], o[7]};
+  if (lds != nullptr) {
+    f32x4* l4 = reinterpret_cast<f32x4*>(lds);
+    l4[0] = f32x4{o[0], o[1], o[2], o[3]};
+    l4[1] = f32x4{o[4], o[5], o[6], o[7]};
+  }
 }
 
-__global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs a) {
+// The fold of sequence b by one block of kCompressThreads threads, as block bx
+// of gx blocks over the sequence's work.  With a non-null `lds_row` (a fold of
+// a single entry) the entry is also left in that shared array.  The dynamic
+// shared memory of the launch holds kCompressShm bytes.
+__device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int bx, int gx, float* lds_row) {
   const int TD = a.d >> 3;              // threads across the dims of a row
   const int RP = kCompressThreads / TD; // row groups
   const int li = threadIdx.x % TD;
   const int gi = threadIdx.x / TD;
   const bool active = gi < RP;
-  const int b = blockIdx.y;
   const int n = clampi(a.ntok[b], 0, a.max_ntok);
   const int m = a.m;
   const int N = (n + m - 1) / m;
@@ -61,7 +67,7 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
 
   if (m <= kSmallM) {
     if (!active) return;
-    for (int j = blockIdx.x * RP + gi; j < N; j += gridDim.x * RP) {
+    for (int j = bx * RP + gi; j < N; j += gx * RP) {
       const int t0 = j * m;
       const int r = min(m, n - t0);
       float mx = -INFINITY;
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
       const float inv_tot = 1.0f / tot;
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[c] *= inv_tot;
-      rope_store8(ob + (int64_t)j * a.d, acc, (double)p0 + (double)t0, inv);
+      rope_store8(ob + (int64_t)j * a.d, lds_row ? lds_row + li * 8 : nullptr, acc, (double)p0 + (double)t0, inv);
     }
     return;
   }
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
   __shared__ float red_s[kCompressThreads];
   extern __shared__ float acc_s[];     // [RS][DS]
   const uint16_t* xs = a.x + (int64_t)b * a.xs + ls * 8;
-  for (int u = blockIdx.x; u < N * nsl; u += gridDim.x) {
+  for (int u = bx; u < N * nsl; u += gx) {
     const int j = u / nsl;
     const int base = (u % nsl) * DS;
     const int t0 = j * m;
@@ -122,14 +128,29 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
     }
     const float tot = red_s[0];
     if (gs < RS) {
+      // the row group's tokens i = gs, gs + RS, ..., in batches whose loads
+      // are all in flight before the first is summed (same order of sums)
+      constexpr int kBatch = 16;
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 4
-      for (int i = gs; i < r; i += RS) {
-        float v[8];
-        load_bf16x8(xs + (int64_t)(t0 + i) * a.d + base, v);
-        const float wi = w_s[i];
+      for (int i0 = gs; i0 < r; i0 += kBatch * RS) {
+        u32x4 raw[kBatch];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = fmaf(wi, v[c], acc[c]);
+        for (int k = 0; k < kBatch; ++k) {
+          const int i = i0 + k * RS;
+          raw[k] = i < r ? *reinterpret_cast<const u32x4*>(xs + (int64_t)(t0 + i) * a.d + base) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int i = i0 + k * RS;
+          if (i < r) {
+            const float wi = w_s[i];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              acc[2 * q] = fmaf(wi, u2f(raw[k][q] << 16), acc[2 * q]);
+              acc[2 * q + 1] = fmaf(wi, u2f(raw[k][q] & 0xFFFF0000u), acc[2 * q + 1]);
+            }
+          }
+        }
       }
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc_s[gs * DS + ls * 8 + c] = acc[c];
@@ -151,9 +172,22 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
       float* o = a.out + (int64_t)b * a.os + (int64_t)j * a.d + base + 2 * t;
       o[0] = e0 * c - e1 * sn;
       o[1] = e0 * sn + e1 * c;
+      if (lds_row != nullptr) {
+        lds_row[base + 2 * t] = o[0];
+        lds_row[base + 2 * t + 1] = o[1];
+      }
     }
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs a) {
+  compress_block(a, blockIdx.y, blockIdx.x, gridDim.x, nullptr);
+}
+
+int compress_slice(int n_max, int B, int d, int m) {
+  (void)n_max; (void)B; (void)m;
+  return d;  // a block folds whole entries; its row groups' loads are batched
 }
 
 hipError_t launch_compress(CompressArgs a, hipStream_t s) {
@@ -167,13 +201,231 @@ hipError_t launch_compress(CompressArgs a, hipStream_t s) {
     gx = (n_max + RP - 1) / RP;
     gx = gx > 2048 ? 2048 : gx;
   } else {
-    // few entries (a decode step's open group): cut the dims into 64-wide slices
-    if ((int64_t)n_max * a.B < 512 && a.d % 64 == 0) a.ds = 64;
+    a.ds = compress_slice(n_max, a.B, a.d, a.m);
     const int64_t units = (int64_t)n_max * (a.d / a.ds);
     gx = units > 4096 ? 4096 : (int)units;
-    shm = (size_t)(kCompressThreads / (a.ds / 8)) * a.ds * sizeof(float);
+    shm = kCompressShm;
   }
   hipLaunchKernelGGL(compress_kernel, dim3(gx, a.B), dim3(kCompressThreads), shm, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- decode-step insert
+// kv_compress_insert: a decode step's update of one pool in one launch, one
+// block per sequence: the open group's fold (compress_block, so the entry is
+// bit-identical to kv_compress's) into its row of the open page's staging,
+// then the open page quantized (V4 page, section 3.2.1: RoPE, then insertion
+// into the cache; sections 3.1.1 and 3.1.3: the page formats).  The new row is
+// read back from shared memory, older rows from staging.
+//   append = 0: the page is rewritten whole, as kv_quantize_page rewrites it.
+//   append = 1: the page already holds the codes of the rows before the open
+//   one, made with its current scale, so they stand as long as the scale does
+//   and only the open row is encoded.  For a re-folded entry (m > 1) the scale
+//   is recomputed from all rows (held in registers when the page fits).  For
+//   a window insert (m = 1, a new row) it is not: an fp8 page scale is
+//   fl32(amax/448), which is monotonic in amax, so the new scale is
+//   max(old scale, new row's fl32(amax_row/448)) exactly.  The page is
+//   rewritten whole when the scale changes, the page is new (row 0), or, for
+//   m = 1, the old scale is 1.0 (which an all-zero page also has).
+constexpr int kInsertMaxDim = 2048;
+
+__device__ __forceinline__ uint32_t enc4_e4m3(const f32x4 v, float s) {
+  return (uint32_t)e4m3_encode(v[0] / s) | ((uint32_t)e4m3_encode(v[1] / s) << 8) |
+         ((uint32_t)e4m3_encode(v[2] / s) << 16) | ((uint32_t)e4m3_encode(v[3] / s) << 24);
+}
+
+__device__ __forceinline__ float ins_block_max(float v, float* red) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float amax4(const f32x4 v) {
+  return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+}
+
+__device__ __forceinline__ void insert_block(const InsertArgs& a, int b, float* row_s, float* red_s) {
+  const int m = a.c.m, d = a.c.d, epp = a.dst.epp;
+  const bool fold = a.c.x != nullptr;  // else the open row is already in staging
+  const int n = fold ? clampi(a.c.ntok[b], 0, a.c.max_ntok) : 1;
+  if (n == 0) return;  // no open group: nothing to write
+  const int E0 = a.e0[b];
+  const int row = a.c.pos0[b] / m - E0;  // the open entry's row in its page
+  if (row < 0 || row >= epp) return;
+  const int lb = E0 / epp;
+  if (lb < 0 || lb >= a.bts) return;
+  const int phys = a.bt[(int64_t)b * a.bts + lb];  // loaded now, used after the fold
+  const float* st = a.stage + (int64_t)b * a.ss;  // the page's rows in staging
+  const int d4 = d / 4;
+  const f32x4* st4 = reinterpret_cast<const f32x4*>(st);
+  const int old4 = row * d4, new4 = old4 + d4;  // float4 groups before / through the new row
+  // an fp8 page that fits kPageRegs float4 per thread and needs the amax of
+  // all its rows (a rewrite, or a re-folded open entry): its earlier rows are
+  // loaded now, in flight during the fold
+  constexpr int kPageRegs = 32;
+  const bool in_regs = a.dst.dtype == HCA_FP8_E4M3 && (a.append == 0 || m > 1) &&
+                       epp * d4 <= kPageRegs * kCompressThreads;
+  f32x4 pv[kPageRegs];
+  if (in_regs) {
+#pragma unroll
+    for (int k = 0; k < kPageRegs; ++k) {
+      const int i = threadIdx.x + k * kCompressThreads;
+      pv[k] = i < old4 ? st4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  if (fold) {
+    CompressArgs c = a.c;
+    c.out = a.stage + (int64_t)row * d;
+    c.os = a.ss;
+    compress_block(c, b, 0, 1, row_s);
+  } else {
+    for (int i = threadIdx.x; i < d4; i += kCompressThreads)
+      reinterpret_cast<f32x4*>(row_s)[i] = st4[old4 + i];
+  }
+  __syncthreads();
+  if (phys < 0 || phys >= a.dst.num_pages) return;
+  const f32x4* row4 = reinterpret_cast<const f32x4*>(row_s);
+
+  if (in_regs) {
+    float* scales = reinterpret_cast<float*>(a.dst.scales);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.dst.codes) + (int64_t)phys * epp * d);
+    // the new row joins the registers of the threads that hold its slots
+#pragma unroll
+    for (int k = 0; k < kPageRegs; ++k) {
+      const int i = threadIdx.x + k * kCompressThreads;
+      if (i >= old4 && i < new4) pv[k] = row4[i - old4];
+    }
+    float amx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kPageRegs; ++k) amx = fmaxf(amx, amax4(pv[k]));
+    amx = ins_block_max(amx, red_s);
+    const float s = amx > 0.0f ? amx / 448.0f : 1.0f;
+    // append: the earlier rows' codes stand if the page scale is unchanged
+    const bool all = a.append == 0 || row == 0 || scales[phys] != s;
+    if (all) {
+      const int tot4 = epp * d4;
+#pragma unroll
+      for (int k = 0; k < kPageRegs; ++k) {
+        const int i = threadIdx.x + k * kCompressThreads;
+        if (i < tot4) dst[i] = i < new4 ? enc4_e4m3(pv[k], s) : 0u;
+      }
+      if (threadIdx.x == 0) scales[phys] = s;
+    } else {
+      for (int i = threadIdx.x; i < d4; i += kCompressThreads) dst[old4 + i] = enc4_e4m3(row4[i], s);
+    }
+  } else if (a.dst.dtype == HCA_FP8_E4M3) {
+    float* scales = reinterpret_cast<float*>(a.dst.scales);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.dst.codes) + (int64_t)phys * epp * d);
+    float am = 0.0f;
+    for (int i = threadIdx.x; i < d4; i += kCompressThreads) am = fmaxf(am, amax4(row4[i]));
+    am = ins_block_max(am, red_s);
+    bool full = a.append == 0 || row == 0 || m > 1;
+    float s = 1.0f;
+    if (!full) {
+      const float s_old = scales[phys];
+      if (!(s_old > 0.0f) || s_old == 1.0f || am / 448.0f > s_old) full = true;
+      else s = s_old;
+    }
+    if (full) {
+      constexpr int U = 8;
+      float amx = am;
+      for (int i0 = threadIdx.x; i0 < old4; i0 += U * kCompressThreads) {
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * kCompressThreads;
+          v[u] = i < old4 ? st4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) amx = fmaxf(amx, amax4(v[u]));
+      }
+      amx = ins_block_max(amx, red_s);
+      s = amx > 0.0f ? amx / 448.0f : 1.0f;
+      const int tot4 = epp * d4;
+      for (int i0 = threadIdx.x; i0 < tot4; i0 += U * kCompressThreads) {
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * kCompressThreads;
+          v[u] = i < old4 ? st4[i] : (i < new4 ? row4[i - old4] : f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * kCompressThreads;
+          if (i < tot4) dst[i] = i < new4 ? enc4_e4m3(v[u], s) : 0u;
+        }
+      }
+      if (threadIdx.x == 0) scales[phys] = s;
+    } else {
+      for (int i = threadIdx.x; i < d4; i += kCompressThreads) dst[old4 + i] = enc4_e4m3(row4[i], s);
+    }
+  } else if (a.dst.dtype == HCA_FP4_E2M1) {
+    // per-32 scales within a row: four lanes per block of 32, 8 elements each
+    const int nblk = d / 32;
+    uint8_t* pc = reinterpret_cast<uint8_t*>(a.dst.codes) + (int64_t)phys * epp * (d / 2);
+    uint8_t* ps = reinterpret_cast<uint8_t*>(a.dst.scales) + (int64_t)phys * epp * nblk;
+    const int r0 = a.append ? row : 0, r1 = a.append ? row + 1 : epp;
+    const int units = (r1 - r0) * nblk * 4;
+    for (int u0 = 0; u0 < units; u0 += kCompressThreads) {
+      const int u = u0 + threadIdx.x;
+      const bool live = u < units;
+      const int q = u & 3;
+      const int blk = (u >> 2) % nblk;
+      const int r = r0 + (u >> 2) / nblk;
+      float v[8];
+      float amax = 0.0f;
+      if (live && r <= row) {
+        const float* src = r == row ? row_s + blk * 32 + q * 8 : st + (int64_t)r * d + blk * 32 + q * 8;
+        const f32x4 v0 = reinterpret_cast<const f32x4*>(src)[0], v1 = reinterpret_cast<const f32x4*>(src)[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { v[i] = v0[i]; v[4 + i] = v1[i]; }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      if (!live) continue;
+      const uint32_t sc = r <= row ? e4m3_encode(amax / 6.0f) : 0u;
+      const float sdec = e4m3_decode(sc);
+      uint32_t word = 0;
+      if (sdec > 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= e2m1_encode(v[i] / sdec) << (4 * i);
+      }
+      *reinterpret_cast<uint32_t*>(pc + (int64_t)r * (d / 2) + blk * 16 + q * 4) = word;
+      if (q == 0) ps[(int64_t)r * nblk + blk] = (uint8_t)sc;
+    }
+  } else {
+    u32x2* dst = reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.dst.codes) + (int64_t)phys * epp * d);
+    const int i0 = a.append ? old4 : 0, i1 = a.append ? new4 : epp * d4;
+    for (int i = i0 + threadIdx.x; i < i1; i += kCompressThreads) {
+      u32x2 w = {0u, 0u};
+      if (i < new4) {
+        const f32x4 v = i < old4 ? st4[i] : row4[i - old4];
+        w[0] = (uint32_t)bf16_encode(v[0]) | ((uint32_t)bf16_encode(v[1]) << 16);
+        w[1] = (uint32_t)bf16_encode(v[2]) | ((uint32_t)bf16_encode(v[3]) << 16);
+      }
+      dst[i] = w;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kCompressThreads) void insert_kernel(InsertJobs j) {
+  __shared__ __attribute__((aligned(16))) float row_s[kInsertMaxDim];
+  __shared__ float red_s[kCompressThreads / 64];
+  insert_block(j.job[blockIdx.y], blockIdx.x, row_s, red_s);
+}
+
+hipError_t launch_insert(InsertJobs j, int B, hipStream_t s) {
+  if (B == 0 || j.n == 0) return hipSuccess;
+  for (int i = 0; i < j.n; ++i) j.job[i].c.ds = compress_slice(1, B, j.job[i].c.d, j.job[i].c.m);
+  hipLaunchKernelGGL(insert_kernel, dim3(B, j.n), dim3(kCompressThreads), kCompressShm, s, j);
   return hipGetLastError();
 }
 

@@ -19,6 +19,28 @@ struct CompressArgs {
   int ds;  // dims per block slice (set by the launcher)
 };
 hipError_t launch_compress(CompressArgs a, hipStream_t s);
+constexpr int kCompressThreads = 256;
+constexpr int kSmallM = 16;  // groups up to this size are folded by one row group of threads
+constexpr size_t kCompressShm = (size_t)kCompressThreads * 8 * sizeof(float);  // a large-m fold's row-group sums
+// dims per block slice of a large-m fold (64 when there are few entries)
+int compress_slice(int n_max, int B, int d, int m);
+
+// decode-step update of pools: fold each open group into its staging row and
+// quantize the open page, all in one launch (a job per pool)
+struct InsertArgs {
+  CompressArgs c;           // the open group (c.x null: the row is already in staging); c.out, c.os set per sequence
+  float* stage; int64_t ss; // [B][epp][d] f32 staging of the open page
+  const int32_t* e0;        // [B] first entry of the open page
+  const int32_t* bt; int bts;
+  hca_paged_cache dst;
+  int append;
+};
+constexpr int kMaxInsertJobs = 4;
+struct InsertJobs {
+  InsertArgs job[kMaxInsertJobs];
+  int n;
+};
+hipError_t launch_insert(InsertJobs j, int B, hipStream_t s);
 
 struct QuantArgs {
   const float* src; int64_t ss;

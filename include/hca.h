@@ -154,6 +154,76 @@ hca_status kv_quantize_page(const float* src, int64_t src_stride_b, const int32_
                             void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * kv_compress_insert -- a decode step's update of one pool in one launch: the
+ * open group is folded as kv_compress folds it (V4 page, section 2.1; section
+ * 3.1.2: the open group is the rolling residual; section 3.2.1: RoPE, then
+ * insertion into the cache) into its row of the open page's f32 staging, and
+ * the open page is quantized as kv_quantize_page quantizes it (sections 3.1.1
+ * and 3.1.3).  The staging row and the page bytes are identical to those of
+ * kv_compress(max_ntok = m) followed by kv_quantize_page on that page.
+ *
+ * For sequence b the open group has ntok[b] tokens (clamped to [0, m]; 0
+ * writes nothing) starting at position pos0[b] (a multiple of m); its entry
+ * j = pos0[b]/m is row j - e0[b] of the page that starts at entry e0[b] (a
+ * multiple of dst.epp), which must be in [0, dst.epp) (else nothing is
+ * written); rows 0 .. j-e0[b]-1 of stage are the page's earlier entries.
+ *
+ *   x, gate_logit, pos_bias: as kv_compress, with T = m tokens per sequence;
+ *              m = 1 is the window insert of one token (dst.epp = 256)
+ *   stage      float stage[b * stage_stride_b + r * dst.dim + c], r < dst.epp;
+ *              row j - e0[b] is written
+ *   block_table int32 [B][bt_stride]: page of logical block e0[b] / dst.epp
+ *   dst        the pool; dst.epp == 256 / m, dst.dim <= 2048
+ *   append     0: the page is rewritten whole from staging;
+ *              1: the caller guarantees that the page already holds the codes
+ *              of rows 0 .. j-e0[b]-1, made from the same staging rows (as a
+ *              previous call leaves them), and, for m = 1, that row j-e0[b] is
+ *              new or unchanged (a window insert).  Only what changes is then
+ *              written: the earlier rows' codes stand while the fp8 page scale
+ *              does.  For m > 1 (the open entry is re-folded every step) the
+ *              scale is taken over all rows; for m = 1 it is max(old scale,
+ *              the new row's), which is exact because fl32(amax/448) is
+ *              monotonic in amax.  The result equals that of append = 0.
+ * Calls that write the same page or staging must be ordered by the caller.
+ */
+hca_status kv_compress_insert(const uint16_t* x, int64_t x_stride_b, const float* gate_logit, int64_t z_stride_b,
+                              const float* pos_bias, const int32_t* pos0, const int32_t* ntok, int32_t B, int32_t m,
+                              float rope_theta, float* stage, int64_t stage_stride_b, const int32_t* e0,
+                              const int32_t* block_table, int32_t bt_stride, hca_paged_cache dst, int32_t append,
+                              void* stream);
+
+/*
+ * kv_compress_insert_jobs -- several kv_compress_insert calls over the same B
+ * sequences in one launch (a layer's window insert, its open entry and its
+ * open indexer page), so the decode update of a layer costs one launch.
+ * Each job has the arguments of kv_compress_insert; a job whose x is NULL
+ * folds nothing: its open row j - e0[b] is already in stage (gate_logit,
+ * pos_bias, ntok and rope_theta are then unused) and the page is quantized as
+ * described above.  Jobs must write different pages and staging rows.
+ *   n_jobs     0 .. 4 (HCA_ERR_UNSUPPORTED above); every job is validated
+ *              before anything is launched.
+ */
+typedef struct {
+  const uint16_t* x; /* NULL: nothing to fold */
+  int64_t x_stride_b;
+  const float* gate_logit;
+  int64_t z_stride_b;
+  const float* pos_bias;
+  const int32_t* pos0;
+  const int32_t* ntok;
+  int32_t m;
+  float rope_theta;
+  float* stage;
+  int64_t stage_stride_b;
+  const int32_t* e0;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  hca_paged_cache dst;
+  int32_t append;
+} hca_insert_job;
+hca_status kv_compress_insert_jobs(const hca_insert_job* jobs, int32_t n_jobs, int32_t B, void* stream);
+
+/*
  * indexer_topk -- indexer scoring and top-k selection for c4a layers (V4 page,
  * section 2.2: a separate, smaller indexer KV tells the query which compressed
  * entries to look in).

@@ -112,6 +112,51 @@ def test_validation_kv_compress():
     assert call(B=0) == 0 and call(mx=0) == 0  # nothing to do, nothing launched
 
 
+def test_validation_kv_compress_insert():
+    L = hca.lib()
+    ok = dict(x=FAKE, xs=4 * 128, z=FAKE, zs=4, beta=FAKE, pos0=FAKE, ntok=FAKE, B=2, m=4, theta=1e6, st=FAKE,
+              ss=64 * 128, e0=FAKE, bt=FAKE, bts=16, dst=_cache(), app=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.kv_compress_insert(a["x"], a["xs"], a["z"], a["zs"], a["beta"], a["pos0"], a["ntok"], a["B"],
+                                    a["m"], a["theta"], a["st"], a["ss"], a["e0"], a["bt"], a["bts"], a["dst"],
+                                    a["app"], None)
+
+    assert call(m=3) == 1 and call(m=8) == 1  # the pool's epp must be 256 / m
+    assert call(dst=_cache(dim=4096)) == 2
+    assert call(dst=_cache(dtype=7)) == 1 and call(dst=_cache(scales=None)) == 1
+    assert call(app=2) == 1 and call(bts=0) == 1 and call(theta=0.0) == 1
+    assert call(x=None) == 1 and call(st=None) == 1 and call(e0=None) == 1 and call(bt=None) == 1
+    assert call(xs=100) == 1 and call(ss=16) == 1 and call(zs=3) == 1
+    assert call(B=-1) == 1
+    assert call(B=0) == 0  # nothing to do, nothing launched
+
+
+def test_validation_kv_compress_insert_jobs():
+    L = hca.lib()
+
+    def job(**kw):
+        a = dict(x=FAKE.value, xs=4 * 128, z=FAKE.value, zs=4, beta=FAKE.value, pos0=FAKE.value, ntok=FAKE.value,
+                 m=4, theta=1e6, st=FAKE.value, ss=64 * 128, e0=FAKE.value, bt=FAKE.value, bts=16, dst=_cache(),
+                 app=0)
+        a.update(kw)
+        return hca.CInsertJob(a["x"], a["xs"], a["z"], a["zs"], a["beta"], a["pos0"], a["ntok"], a["m"], a["theta"],
+                              a["st"], a["ss"], a["e0"], a["bt"], a["bts"], a["dst"], a["app"])
+
+    def call(jobs, B=2):
+        arr = (hca.CInsertJob * max(len(jobs), 1))(*jobs)
+        return L.kv_compress_insert_jobs(arr, len(jobs), B, None)
+
+    assert call([job(), job(m=3)]) == 1  # every job is checked before anything is launched
+    assert call([job(), job(dst=_cache(dim=4096))]) == 2
+    assert call([job()] * 5) == 2  # at most four jobs
+    assert call([job(x=None, z=None, beta=None, ntok=None, st=None)]) == 1  # no fold, but a staging row is needed
+    assert call([job()], B=-1) == 1
+    assert call([job(), job(app=3)]) == 1
+    assert call([], B=2) == 0 and call([job()], B=0) == 0  # nothing to do, nothing launched
+
+
 def test_validation_quantize_and_gather():
     L = hca.lib()
     assert L.kv_quantize_page(FAKE, 8192, FAKE, FAKE, 2, 64, FAKE, 16, _cache(dtype=7), None, 0, None) == 1

@@ -137,9 +137,9 @@ def test_quantize_open_page_run(use_ws):
 # ----------------------------------------------------------------- kv_compress
 
 
-# groups0 sets the first sequence's full groups: with few entries (groups0 * 4 < 512)
-# and d % 64 == 0 a large-m fold is cut into 64-dim slices, otherwise a block
-# folds whole entries; (64, 136) has no 64-dim slicing at all.
+# groups0 sets the first sequence's full groups; a large-m fold takes its row
+# group's tokens in batches of 16, so m = 256 (64 tokens per row group at d =
+# 128) spans several batches; d = 136 leaves threads of the block idle.
 @pytest.mark.parametrize("m,d,groups0", [(4, 512, 37), (128, 512, 37), (4, 128, 37), (1, 512, 37), (16, 64, 37),
                                          (256, 128, 37), (128, 512, 140), (64, 136, 37), (32, 256, 1)])
 def test_compress_entries(m, d, groups0):
@@ -162,6 +162,164 @@ def test_compress_entries(m, d, groups0):
     for b in range(B):
         ref = compressor.compress(codecs.bf16_decode(xb[b, : T[b]]), z[b, : T[b]], beta, m, 1e6, pos0=int(pos0[b]))
         assert H.rel_err_rows(got[b, : ref.shape[0]], ref) <= H.ENTRY_TOL, b
+
+
+# ----------------------------------------------------------------- kv_compress_insert
+
+
+# Decode steps of one pool: each step adds one token; the fused call must leave
+# the same staging rows and page bytes as kv_compress + kv_quantize_page on the
+# open page, and those must match the oracle (fold within the entry tolerance,
+# page codes bit-exact for the GPU staging rows).  The runs cross a page start
+# (the new page's first row), grow an fp8 page scale with a large token, and
+# start one page from all-zero rows (scale 1.0, which append mode must not
+# trust).
+@pytest.mark.parametrize("m,dtype,d,append", [(1, "fp8", 512, True), (1, "fp8", 512, False), (4, "fp8", 512, False),
+                                               (4, "fp8", 512, True), (128, "fp8", 512, True),
+                                               (128, "fp8", 512, False), (2, "fp8", 136, False), (2, "fp8", 512, True),
+                                               (4, "fp4", 128, False), (1, "fp4", 128, True),
+                                               (4, "bf16", 128, False), (1, "bf16", 64, True)])
+def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append):
+    H.flush(f"compress_insert m={m} {dtype} d={d} append={append}")
+    rng = np.random.default_rng(61 + m)
+    epp = 256 // m
+    B, steps, theta = 3, 7, 1e6
+    # lengths before the first step: seq 0 three tokens before a page start,
+    # seq 1 empty, seq 2 mid-page (its page begins with all-zero rows)
+    L = np.array([256 * 2 - 3, 0, 256 * 5 + 9 * m + 1], np.int64)
+    nb = int(L.max() + steps) // 256 + 2
+    table = rng.permutation(B * nb + 2)[: B * nb].reshape(B, nb).astype(np.int32)
+    P = B * nb + 2
+    beta = (rng.standard_normal(m) * 0.1).astype(np.float32)
+    stage_f = torch.zeros((B, epp, d), dtype=torch.float32, device="cuda")
+    pool_f = hca.PagedCache.empty(P, epp, d, dtype)
+    pool_f.codes.fill_(0)
+    if pool_f.scales is not None:
+        pool_f.scales.fill_(0)
+    # history of each open page: its earlier rows, quantized as they would have been
+    hist = np.zeros((B, epp, d), np.float32)
+    for b in range(B):
+        j = (L[b]) // m if L[b] % m == 0 else L[b] // m  # the next step's entry
+        row = j % epp
+        hist[b, :row] = rng.standard_normal((row, d)).astype(np.float32)
+        if b == 2:
+            hist[b, :row] = 0.0
+        stage_f[b] = H.to_dev(hist[b])
+        if row > 0:
+            e0 = np.array([j - row], np.int32)
+            hca.kv_quantize_page(stage_f[b:b + 1], H.to_dev(e0), H.to_dev(np.array([row], np.int32)), epp,
+                                 H.to_dev(table[b:b + 1]), pool_f)
+    torch.cuda.synchronize()
+    stage_u = stage_f.clone()
+    pool_u = hca.PagedCache(pool_f.codes.clone(), None if pool_f.scales is None else pool_f.scales.clone(), epp, d,
+                            dtype)
+    ring_x = np.zeros((B, m, d), np.float32)
+    ring_z = np.zeros((B, m), np.float32)
+    for step in range(steps):
+        L += 1
+        pos0 = (m * ((L - 1) // m)).astype(np.int32)
+        ntok = (L - pos0).astype(np.int32)
+        for b in range(B):
+            t = int(ntok[b]) - 1
+            if t == 0:
+                ring_x[b] = 0.0
+                ring_z[b] = 0.0
+            scale = 40.0 if (b == 2 and step == 3) else (0.0 if (b == 2 and step == 0) else 1.0)
+            ring_x[b, t] = rng.standard_normal(d) * scale
+            ring_z[b, t] = rng.standard_normal()
+        xb = gen.to_bf16_bits(ring_x)
+        j = pos0 // m
+        e0 = (epp * (j // epp)).astype(np.int32)
+        row = j - e0
+        xd, zd = H.to_dev(xb.view(np.int16)), H.to_dev(ring_z)
+        hca.kv_compress_insert(xd, zd, H.to_dev(beta), H.to_dev(pos0), H.to_dev(ntok), m, theta, stage_f,
+                               H.to_dev(e0), H.to_dev(table), pool_f, append=append)
+        for b in range(B):  # the two-call path, one sequence at a time (rows differ)
+            hca.kv_compress(xd[b:b + 1], zd[b:b + 1], H.to_dev(beta), H.to_dev(pos0[b:b + 1]),
+                            H.to_dev(ntok[b:b + 1]), m, theta, stage_u[b:b + 1, int(row[b]):], m)
+            hca.kv_quantize_page(stage_u[b:b + 1], H.to_dev(e0[b:b + 1]), H.to_dev(row[b:b + 1] + 1), epp,
+                                 H.to_dev(table[b:b + 1]), pool_u)
+        torch.cuda.synchronize()
+        sf, su = stage_f.cpu().numpy(), stage_u.cpu().numpy()
+        ref_pool = paging.Pool(dtype, P, epp, d)
+        got_f = H.download_pool(pool_f, ref_pool)
+        got_u = H.download_pool(pool_u, ref_pool)
+        for b in range(B):
+            r = int(row[b])
+            assert np.array_equal(sf[b, : r + 1].view(np.uint32), su[b, : r + 1].view(np.uint32)), (step, b)
+            ent = compressor.compress(codecs.bf16_decode(xb[b, : ntok[b]]), ring_z[b, : ntok[b]], beta, m, theta,
+                                      pos0=int(pos0[b]))
+            assert H.rel_err_rows(sf[b, r : r + 1], ent[-1:]) <= H.ENTRY_TOL, (step, b)
+            phys = int(table[b, e0[b] // epp])
+            assert np.array_equal(got_f.codes[phys], got_u.codes[phys]), (step, b)
+            if dtype != "bf16":
+                assert np.array_equal(got_f.scales[phys], got_u.scales[phys]), (step, b)
+            paging.write_run(ref_pool, table[b], int(e0[b]), sf[b, : r + 1])
+            assert np.array_equal(got_f.codes[phys, : r + 1], ref_pool.codes[phys, : r + 1]), (step, b)
+            if dtype == "fp8":
+                assert got_f.scales[phys] == ref_pool.scales[phys], (step, b)
+            elif dtype == "fp4":
+                assert np.array_equal(got_f.scales[phys, : r + 1], ref_pool.scales[phys, : r + 1]), (step, b)
+
+
+def test_compress_insert_jobs_one_launch():
+    # a layer's decode update as one launch: window insert (m = 1, fp8), the
+    # open c4a entry (m = 4, fp8) and its open fp4 indexer page (no fold: the
+    # row is in staging); the same as the three single calls
+    H.flush("compress_insert_jobs")
+    rng = np.random.default_rng(71)
+    B, d, di, theta = 3, 512, 128, 1e6
+    L = np.array([1000, 4097, 300], np.int64)
+    nb = int(L.max()) // 256 + 2
+    table = rng.permutation(B * nb).reshape(B, nb).astype(np.int32)
+    wtable = rng.permutation(B * nb).reshape(B, nb).astype(np.int32)
+    pos_w = (L - 1).astype(np.int32)
+    e0_w = (256 * ((L - 1) // 256)).astype(np.int32)
+    pos_c = (4 * ((L - 1) // 4)).astype(np.int32)
+    ntok_c = (L - pos_c).astype(np.int32)
+    e0_c = (64 * ((pos_c // 4) // 64)).astype(np.int32)
+    xw = gen.to_bf16_bits(rng.standard_normal((B, 1, d)).astype(np.float32))
+    zw = rng.standard_normal((B, 1)).astype(np.float32)
+    xc = gen.to_bf16_bits(rng.standard_normal((B, 4, d)).astype(np.float32))
+    zc = rng.standard_normal((B, 4)).astype(np.float32)
+    beta = (rng.standard_normal(4) * 0.1).astype(np.float32)
+    stages = (rng.standard_normal((B, 256, d)).astype(np.float32), rng.standard_normal((B, 64, d)).astype(np.float32),
+              rng.standard_normal((B, 64, di)).astype(np.float32))
+    outs = []
+    for fused in (True, False):
+        wst, cst, ist = (H.to_dev(a) for a in stages)
+        win = hca.PagedCache.empty(B * nb, 256, d, "fp8")
+        kv = hca.PagedCache.empty(B * nb, 64, d, "fp8")
+        idx = hca.PagedCache.empty(B * nb, 64, di, "fp4")
+        xwd, zwd, xcd, zcd = H.to_dev(xw.view(np.int16)), H.to_dev(zw), H.to_dev(xc.view(np.int16)), H.to_dev(zc)
+        args = dict(pos_w=H.to_dev(pos_w), e0_w=H.to_dev(e0_w), pos_c=H.to_dev(pos_c), ntok_c=H.to_dev(ntok_c),
+                    e0_c=H.to_dev(e0_c), one=H.to_dev(np.ones(B, np.int32)), zero1=H.to_dev(np.zeros(1, np.float32)),
+                    beta=H.to_dev(beta), tab=H.to_dev(table), wtab=H.to_dev(wtable))
+        if fused:
+            jobs = [hca.insert_job(wst, args["pos_w"], args["e0_w"], args["wtab"], win, 1, x=xwd, gate_logit=zwd,
+                                   pos_bias=args["zero1"], ntok=args["one"], rope_theta=theta),
+                    hca.insert_job(cst, args["pos_c"], args["e0_c"], args["tab"], kv, 4, x=xcd, gate_logit=zcd,
+                                   pos_bias=args["beta"], ntok=args["ntok_c"], rope_theta=theta),
+                    hca.insert_job(ist, args["pos_c"], args["e0_c"], args["tab"], idx, 4)]
+            hca.kv_compress_insert_jobs(jobs, B)
+        else:
+            hca.kv_compress_insert(xwd, zwd, args["zero1"], args["pos_w"], args["one"], 1, theta, wst, args["e0_w"],
+                                   args["wtab"], win)
+            hca.kv_compress_insert(xcd, zcd, args["beta"], args["pos_c"], args["ntok_c"], 4, theta, cst, args["e0_c"],
+                                   args["tab"], kv)
+            rows = H.to_dev(((pos_c // 4) - e0_c + 1).astype(np.int32))
+            hca.kv_quantize_page(ist, args["e0_c"], rows, 64, args["tab"], idx)
+        torch.cuda.synchronize()
+        outs.append((wst, cst, ist, win, kv, idx))
+    (wf, cf, if_, winf, kvf, idxf), (wu, cu, iu, winu, kvu, idxu) = outs
+    assert torch.equal(wf, wu) and torch.equal(cf, cu) and torch.equal(if_, iu)
+    for b in range(B):
+        pw, pc = int(wtable[b, e0_w[b] // 256]), int(table[b, e0_c[b] // 64])
+        nw, nc = int(pos_w[b] - e0_w[b] + 1), int(pos_c[b] // 4 - e0_c[b] + 1)
+        assert torch.equal(winf.codes[pw, :nw], winu.codes[pw, :nw]) and torch.equal(winf.scales[pw], winu.scales[pw])
+        assert torch.equal(kvf.codes[pc, :nc], kvu.codes[pc, :nc]) and torch.equal(kvf.scales[pc], kvu.scales[pc])
+        assert torch.equal(idxf.codes[pc, :nc], idxu.codes[pc, :nc])
+        assert torch.equal(idxf.scales[pc, :nc], idxu.scales[pc, :nc])
 
 
 # ----------------------------------------------------------------- indexer_topk
