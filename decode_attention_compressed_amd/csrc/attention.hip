@@ -241,7 +241,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
   constexpr int kHalfBytes = kFp8 ? kAttnWaves * RT::BYTES : 2 * TILE_H * 2;
   __shared__ __attribute__((aligned(16))) uint8_t tile0_s[kHalfBytes];
   __shared__ __attribute__((aligned(16))) uint8_t tile1_s[kHalfBytes];
-  __shared__ f16x8 q_s[kFp8 ? 1 : KS][64];  // bf16 rows: rotated query fragments
+  __shared__ f16x8 q_s[KS][64];  // rotated query fragments of the block's heads
+  __shared__ float qam_s[kAttnWaves][kHeadsPerBlock];  // per wave: the heads' largest rotated |q|
   __shared__ float2 cs_s[D / 2];
   __shared__ uint64_t rowptr_s[kMaxSplitRows];
   __shared__ __attribute__((aligned(16))) float ps_s[kMaxSplitRows];  // page scale; -1: skipped row
@@ -289,13 +290,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
   const int H = a.H;
   const int h0 = hb * kHeadsPerBlock;
   const int head = h0 + col;  // head of this lane's q / P / m / l
-  // ---- query loads (bf16) in the k-slot map, also before the lengths arrive
+  // ---- query loads (bf16) in the k-slot map, also before the lengths arrive;
+  // each wave loads and rotates a quarter of the k-steps (the block's query
+  // is 16 x D bf16, read once per block rather than once per wave)
+  constexpr int KSW = KS >= kAttnWaves ? KS / kAttnWaves : 1;
+  const int tq0 = wave * KSW;
   const bool hv = head < H;
-  u32x4 qraw[KS];
+  u32x4 qraw[KSW];
   {
     const uint16_t* qrow = a.q + ((int64_t)b * H + (hv ? head : H - 1)) * D;
 #pragma unroll
-    for (int t = 0; t < KS; ++t) qraw[t] = gload<u32x4>(qrow + kslot_dim<D, KVDT>(t, g));
+    for (int i = 0; i < KSW; ++i)
+      qraw[i] = tq0 + i < KS ? gload<u32x4>(qrow + kslot_dim<D, KVDT>(tq0 + i, g)) : u32x4{0u, 0u, 0u, 0u};
   }
   const int L = clampi(a.lens[b], 0, a.max_len);
   const int N = (L + a.m - 1) / a.m;
@@ -323,41 +329,45 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
 
   // ---- rotated query fragments: lane holds Q~[head][kslot_dim(t, g) + j] x qs,
   // j < 8, with qs a power of two that puts the head's largest |value| in
-  // [2^13, 2^14).  fp8 rows keep them in registers; for bf16 rows (whose
-  // gathers need the registers) every wave stores the same values to LDS.
+  // [2^13, 2^14).  Each wave rotates its quarter of the k-steps, the head
+  // maxima meet in LDS, the scaled fragments go to LDS; fp8 rows then keep
+  // all of them in registers.
   float hfac;  // base-2 logit = S x page scale x hfac
   f16x8 qf[kFp8 ? KS : 1];
   {
-    // one pass: all table reads are issued together, the rotated values are
-    // kept (nothing else is live yet), then scaled and rounded
-    float y[KS][8];
+    float y[KSW][8];
     float amax = 0.0f;
 #pragma unroll
-    for (int t = 0; t < KS; ++t) {
+    for (int i = 0; i < KSW; ++i) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const float x0 = u2f(qraw[t][p] << 16), x1 = u2f(qraw[t][p] & 0xFFFF0000u);
-        const float2 cs = cs_s[kslot_dim<D, KVDT>(t, g) / 2 + p];
-        y[t][2 * p] = x0 * cs.x - x1 * cs.y;
-        y[t][2 * p + 1] = x0 * cs.y + x1 * cs.x;
-        amax = fmaxf(amax, fmaxf(fabsf(y[t][2 * p]), fabsf(y[t][2 * p + 1])));
+        const float x0 = u2f(qraw[i][p] << 16), x1 = u2f(qraw[i][p] & 0xFFFF0000u);
+        const float2 cs = cs_s[(kslot_dim<D, KVDT>(min(tq0 + i, KS - 1), g)) / 2 + p];
+        y[i][2 * p] = x0 * cs.x - x1 * cs.y;
+        y[i][2 * p + 1] = x0 * cs.y + x1 * cs.x;
+        amax = fmaxf(amax, fmaxf(fabsf(y[i][2 * p]), fabsf(y[i][2 * p + 1])));
       }
     }
     amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
     amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    if (g == 0) qam_s[wave][col] = amax;
+    lds_barrier();
+    amax = fmaxf(fmaxf(qam_s[0][col], qam_s[1][col]), fmaxf(qam_s[2][col], qam_s[3][col]));
     int e = 0;
     if (amax > 0.0f) (void)frexpf(amax, &e);  // amax < 2^e
     const float qs = ldexpf(1.0f, min(14 - e, 126));
     hfac = a.scale / qs * 1.4426950408889634f;  // logits in base 2: p = 2^(x - m)
 #pragma unroll
-    for (int t = 0; t < KS; ++t) {
+    for (int i = 0; i < KSW; ++i) {
       f16x8 v;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) v[c] = (_Float16)(y[t][c] * qs);
-      if constexpr (kFp8)
-        qf[t] = v;
-      else
-        q_s[t][lane] = v;
+      for (int c = 0; c < 8; ++c) v[c] = (_Float16)(y[i][c] * qs);
+      if (tq0 + i < KS) q_s[tq0 + i][lane] = v;
+    }
+    lds_barrier();
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int t = 0; t < KS; ++t) qf[t] = q_s[t][lane];
     }
   }
 
@@ -485,12 +495,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
   // operand (8 rows of one dim per lane): fp8, one transposing byte read from
   // the ring slot, skipped rows masked, then converted; bf16, two transposing
   // 16-bit reads of 4 rows from the wave's f16 tile.
-  auto pv = [&](int t, const uint8_t* tile, const f32x4 sres[2]) {
+  auto softmax = [&](int t, const f32x4 sres[2], f16x8& pf, uint32_t vmask[2]) {
     const int lr0 = kTileRows * t;
     // lane: rows 16h + 4g + i, head `head`
     float x[8], sc[8];
     float tmax = -INFINITY, tsig = 0.0f;
-    uint32_t vmask[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const f32x4 rq = *reinterpret_cast<const f32x4*>(&ps_s[lr0 + 16 * h + 4 * g]);
@@ -533,7 +542,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
         inv_sigma = 1.0f / tsig;
       }
     }
-    f16x8 pf;
     float psum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -544,6 +552,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
     l_run += psum;
+  };
+
+  // ---- O += P . V
+  auto pv_mma = [&](const uint8_t* tile, const f16x8& pf, const uint32_t vmask[2]) {
 
     constexpr int VB = NB < 8 ? NB : 8;  // column blocks per batch
     if constexpr (kFp8) {
@@ -615,7 +627,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
       asm volatile("" ::: "memory");
       f32x4 sres[2];
       qk(ra, t, slot, sres);
-      pv(t, slot, sres);
+      f16x8 pf;
+      uint32_t vmask[2];
+      softmax(t, sres, pf, vmask);
+      pv_mma(slot, pf, vmask);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & ~0x0F00);  // lgkmcnt(0): the slot's reads are done
       asm volatile("" ::: "memory");
       if (t + 2 * kAttnWaves < nt) issue(t + 2 * kAttnWaves, slot);
@@ -628,7 +643,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
       qk(ra, t, nullptr, sres);
       if (t + kAttnWaves < nt) ra.gather(rowptr_s, kTileRows * (t + kAttnWaves), col, g, safe);
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
-      pv(t, nullptr, sres);
+      f16x8 pf;
+      uint32_t vmask[2];
+      softmax(t, sres, pf, vmask);
+      pv_mma(nullptr, pf, vmask);
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
     }
   }

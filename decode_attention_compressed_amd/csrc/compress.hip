@@ -46,7 +46,10 @@ __device__ __forceinline__ void rope_store8(float* dst, float* lds, const float 
 // The fold of sequence b by one block of kCompressThreads threads, as block bx
 // of gx blocks over the sequence's work.  With a non-null `lds_row` (a fold of
 // a single entry) the entry is also left in that shared array.  The dynamic
-// shared memory of the launch holds kCompressShm bytes.
+// shared memory of the launch holds kCompressShm bytes.  PATHS selects the
+// code compiled in: 1 small groups only, 2 large groups only, 3 both (a
+// kernel holding only what its groups need keeps its register count down).
+template <int PATHS = 3>
 __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int bx, int gx, float* lds_row) {
   const int TD = a.d >> 3;              // threads across the dims of a row
   const int RP = kCompressThreads / TD; // row groups
@@ -65,7 +68,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
 #pragma unroll
   for (int p = 0; p < 4; ++p) inv[p] = rope_inv_freq(li * 4 + p, a.d, a.theta);
 
-  if (m <= kSmallM) {
+  if ((PATHS & 1) && (!(PATHS & 2) || m <= kSmallM)) {
     if (!active) return;
     for (int j = bx * RP + gi; j < N; j += gx * RP) {
       const int t0 = j * m;
@@ -181,8 +184,9 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
   }
 }
 
+template <int PATHS>
 __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs a) {
-  compress_block(a, blockIdx.y, blockIdx.x, gridDim.x, nullptr);
+  compress_block<PATHS>(a, blockIdx.y, blockIdx.x, gridDim.x, nullptr);
 }
 
 int compress_slice(int n_max, int B, int d, int m) {
@@ -206,7 +210,10 @@ hipError_t launch_compress(CompressArgs a, hipStream_t s) {
     gx = units > 4096 ? 4096 : (int)units;
     shm = kCompressShm;
   }
-  hipLaunchKernelGGL(compress_kernel, dim3(gx, a.B), dim3(kCompressThreads), shm, s, a);
+  if (a.m <= kSmallM)
+    hipLaunchKernelGGL(compress_kernel<1>, dim3(gx, a.B), dim3(kCompressThreads), shm, s, a);
+  else
+    hipLaunchKernelGGL(compress_kernel<2>, dim3(gx, a.B), dim3(kCompressThreads), shm, s, a);
   return hipGetLastError();
 }
 
