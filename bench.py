@@ -43,8 +43,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 # copy_bandwidth() (the summary with the commands is in profiles/).  They hold
 # only for the kernel source they were taken on, identified by the SHA-256 of
 # the indexer source and the headers it includes; otherwise traffic is null.
-SCORE_TRAFFIC = {"source_sha256": "7f483e9b0b63d177e83b2def35d998a622d140e8b109cf6942a2e999a4fea045",
-                 "fetch_bytes": 71809724, "write_bytes": 5527040}
+SCORE_TRAFFIC = {"source_sha256": "a402ee491b26c4a03dd13bcef109fc9fe6bd6b686838fcaef60515554b40502c",
+                 "fetch_bytes": 71809582, "write_bytes": 5525194}
 SCORE_SOURCES = ("decode_attention_compressed_amd/csrc/indexer.hip", "decode_attention_compressed_amd/csrc/hca_common.h",
                  "decode_attention_compressed_amd/csrc/hca_internal.h")
 
