@@ -31,4 +31,4 @@ indexer parameters are not available; the oracle pins the method as stated,
 with synthetic parameters.
 """
 
-from . import codecs, rope, compressor, paging, indexer, attention, pipeline  # noqa: F401
+from . import codecs, rope, norm, compressor, paging, indexer, attention, pipeline  # noqa: F401

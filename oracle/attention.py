@@ -17,6 +17,7 @@ workloads); window = 0 means no window rows.
 
 import numpy as np
 
+from . import codecs
 from .rope import rope
 
 
@@ -44,3 +45,22 @@ def attend(q, rows, L: int, scale: float, theta):
 def window_positions(L: int, window: int) -> np.ndarray:
     """Token positions of the raw window: [max(0, L-W), L)."""
     return np.arange(max(0, L - window), L, dtype=np.int64)
+
+
+def quantize_out_fp8(out):
+    """The attention output's fp8 form for the next projection ([V4-vLLM]
+    3.2.1: inverse RoPE and fp8 quantisation of the attention output are one
+    fused step ahead of the fp8 o_lora GEMM).
+
+    Reading adopted (the pages give no granularity): one scale per output row,
+    i.e. per (token, head) vector of d values, with the same rule as the fp8
+    pages: s = fl32(amax/448) (1 when the row is all zero), codes
+    E4M3(fl32(x/s)).  The row is taken in fp32, the precision the attention
+    output is delivered in.  out: [..., d].  Returns (codes uint8 [..., d],
+    scales float32 [...])."""
+    o32 = np.asarray(out, dtype=np.float64).astype(np.float32)
+    amax = np.abs(o32).max(axis=-1)
+    s = np.where(amax > 0, (amax / np.float32(codecs.E4M3_MAX)).astype(np.float32), np.float32(1))
+    s = s.astype(np.float32)
+    y = (o32 / s[..., None]).astype(np.float32)
+    return codecs.e4m3_encode(y), s

@@ -16,11 +16,15 @@ Readings adopted:
 * a partial last group (r < m tokens) is an entry whose softmax runs over its r
   available slots; this is exactly the state a running (max, sum exp, sum w*x)
   residual holds after r tokens, and equals the full entry once r = m;
-* the entry is rotated at the position of its first token, jm.
+* the entry is rotated at the position of its first token, jm;
+* with a gain gamma, the entry is RMS-normalised before it is rotated
+  ([V4-vLLM] 3.2.1: compressor, then RMSNorm, then RoPE, then insertion); a
+  partial group's entry is normalised as it stands.
 """
 
 import numpy as np
 
+from .norm import rms_norm
 from .rope import rope
 
 
@@ -48,13 +52,15 @@ def group_weights(z, beta, m):
     return e / e.sum(axis=1, keepdims=True)
 
 
-def compress(x, z, beta, m, theta, pos0=0, chunk_groups=1 << 14):
+def compress(x, z, beta, m, theta, pos0=0, chunk_groups=1 << 14, gamma=None, eps=1e-6):
     """Entries of a run of tokens.
 
     x: [T, d] token vectors of positions pos0 .. pos0+T-1 (pos0 a multiple of m),
     z: [T] logits, beta: [m] slot biases.  Returns e [ceil(T/m), d] fp64, entry j
-    rotated at position pos0 + j*m.  Processed in chunks of groups so that long
-    contexts fit in memory; chunking does not change any value."""
+    rotated at position pos0 + j*m.  With ``gamma`` ([d]) each entry is
+    RMS-normalised (gain gamma, offset eps) before the rotation.  Processed in
+    chunks of groups so that long contexts fit in memory; chunking does not
+    change any value."""
     x = np.asarray(x, dtype=np.float64)
     T, d = x.shape
     assert pos0 % m == 0
@@ -67,15 +73,19 @@ def compress(x, z, beta, m, theta, pos0=0, chunk_groups=1 << 14):
         xs = np.zeros(((g1 - g0) * m, d))
         xs[: t1 - t0] = x[t0:t1]
         c = np.einsum("gi,gid->gd", w, xs.reshape(g1 - g0, m, d))
+        if gamma is not None:
+            c = rms_norm(c, gamma, eps)
         pos = pos0 + m * np.arange(g0, g1, dtype=np.float64)
         out[g0:g1] = rope(c, pos, theta)
     return out
 
 
-def window_rows(x_block, first_pos, theta):
+def window_rows(x_block, first_pos, theta, gamma=None, eps=1e-6):
     """Sliding-window rows ([V4-vLLM] 2.3: raw, uncompressed recent tokens, kept in
     every layer): token t is stored as RoPE(x_t, t).  This is the compressor with
-    m = 1 (one slot, weight 1)."""
+    m = 1 (one slot, weight 1), with the same optional RMS normalisation."""
     x_block = np.asarray(x_block, dtype=np.float64)
+    if gamma is not None:
+        x_block = rms_norm(x_block, gamma, eps)
     pos = first_pos + np.arange(x_block.shape[0], dtype=np.float64)
     return rope(x_block, pos, theta)

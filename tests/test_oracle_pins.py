@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention, codecs, compressor, indexer, paging, pipeline
+from oracle import attention, codecs, compressor, indexer, norm, paging, pipeline
 from oracle.rope import rope
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -412,3 +412,82 @@ def test_page_and_slot_addressing():
     paging.write_run(pool2, [0, 2, 4], 2, rows[:3])
     assert np.array_equal(pool2.codes[2, :2], paging.quantize_page(rows[:2], "fp8", 2)[0])
     assert np.array_equal(pool2.codes[4, :1], paging.quantize_page(rows[2:3], "fp8", 2)[0][:1])
+
+
+# ----------------------------------------------------------------- fused epilogues
+
+
+def test_rms_norm_and_out_fp8_hand_examples():
+    gold = json.load(open(os.path.join(GOLDEN, "fused_epilogue_hand_examples.json")))
+    for e in gold["rms_norm"]:
+        y = norm.rms_norm(np.array(e["c"]), np.array(e["gamma"]), e["eps"])
+        assert np.allclose(y, e["y"], rtol=0, atol=1e-14), e["cite"]
+    for e in gold["out_fp8"]:
+        codes, s = attention.quantize_out_fp8(np.array(e["x"]))
+        assert codes.tolist() == e["codes"], e["cite"]
+        if "scale" in e:
+            assert float(s) == e["scale"], e["cite"]
+
+
+def test_compressor_norm_before_rope_closed_form():
+    # one token, one pair, gains (2, 1/2), position 1 (angle 1 rad for pair 0):
+    # the gains act before the rotation, so the rotated pair is R(1) (6, 2) sqrt(2)/5
+    y0, y1 = 6 * math.sqrt(2) / 5, 2 * math.sqrt(2) / 5
+    want = [y0 * math.cos(1.0) - y1 * math.sin(1.0), y0 * math.sin(1.0) + y1 * math.cos(1.0)]
+    for fn in (lambda x: compressor.compress(x, np.zeros(1), np.zeros(1), 1, 1e6, pos0=1, gamma=[2.0, 0.5], eps=0.0),
+               lambda x: compressor.window_rows(x, 1, 1e6, gamma=[2.0, 0.5], eps=0.0)):
+        got = fn(np.array([[3.0, 4.0]]))
+        assert np.allclose(got[0], want, rtol=0, atol=1e-14)
+    # gains applied after the rotation would differ
+    wrong = [2.0 * (3 * math.cos(1.0) - 4 * math.sin(1.0)), 0.5 * (3 * math.sin(1.0) + 4 * math.cos(1.0))]
+    assert not np.allclose(np.array(wrong) / math.sqrt(12.5), want, atol=1e-3)
+
+
+def test_compressor_norm_invariants():
+    g = np.random.default_rng(31)
+    T, d = 43, 16
+    x, z, beta = g.normal(size=(T, d)), g.normal(size=T), g.normal(0, 0.1, 4)
+    ones = np.ones(d)
+    # unit gains, no eps: every entry (partial last one included) has mean square 1
+    # after the rotation, which keeps pair norms
+    e = compressor.compress(x, z, beta, 4, 1e4, gamma=ones, eps=0.0)
+    assert np.allclose(np.mean(e * e, axis=1), 1.0, atol=1e-13)
+    # no eps: invariant to a positive scale of the tokens, odd in their sign
+    assert np.allclose(compressor.compress(7.5 * x, z, beta, 4, 1e4, gamma=ones, eps=0.0), e, atol=1e-13)
+    assert np.allclose(compressor.compress(-x, z, beta, 4, 1e4, gamma=ones, eps=0.0), -e, atol=1e-13)
+    # gains scale the unrotated entry dimension by dimension
+    gam = g.uniform(0.5, 1.5, d)
+    u1 = compressor.compress(x, z, beta, 4, None, gamma=ones, eps=1e-6)
+    ug = compressor.compress(x, z, beta, 4, None, gamma=gam, eps=1e-6)
+    assert np.allclose(ug, u1 * gam, atol=1e-13)
+    # normalising never changes the direction of the unrotated entry
+    raw = compressor.compress(x, z, beta, 4, None)
+    cosang = np.sum(raw * u1, axis=1) / np.linalg.norm(raw, axis=1) / np.linalg.norm(u1, axis=1)
+    assert np.allclose(cosang, 1.0, atol=1e-13)
+    # eps: a row of mean square eps is scaled by 1/sqrt(2)
+    c = np.full((1, d), 1e-3)
+    assert np.allclose(norm.rms_norm(c, ones, 1e-6), c / math.sqrt(2e-6), atol=1e-14)
+
+
+def test_out_fp8_bound_and_saturation():
+    g = np.random.default_rng(32)
+    q, rows = g.normal(size=(8, 64)), g.normal(size=(300, 64))
+    out, _, _ = attention.attend(q, rows, 300, 0.125, 1e6)
+    out[3] = 0.0
+    codes, s = attention.quantize_out_fp8(out)
+    assert codes.shape == out.shape and s.shape == (8,) and s.dtype == np.float32
+    assert s[3] == 1.0 and (codes[3] == 0).all()
+    dec = codecs.e4m3_decode(codes) * s[:, None].astype(np.float64)
+    assert np.isfinite(dec).all()
+    o32 = out.astype(np.float32).astype(np.float64)
+    for h in range(8):
+        if h == 3:
+            continue
+        amax = np.abs(o32[h]).max()
+        assert s[h] == np.float32(np.float32(amax) / np.float32(448.0))
+        # the largest element takes the largest finite code
+        assert (codes[h][np.abs(o32[h]) == amax] & 0x7F == 0x7E).all()
+        # each element within half an E4M3 step (at its binade, subnormal below 2^-6) of x
+        y = np.abs(o32[h]) / s[h]
+        e = np.maximum(np.floor(np.log2(np.maximum(y, 1e-30))), -6)
+        assert (np.abs(dec[h] - o32[h]) <= 0.5 * 2.0 ** (e - 3) * s[h] * (1 + 1e-6) + 1e-300).all()
