@@ -11,10 +11,11 @@ K=V dim 512 in fp8 E4M3 pages with a per-page fp32 scale, 64 query heads, a
 and reported on its own.
 
 A step is one decode step of the whole stack for the batch: per layer the
-decode update (re-fold of the open group and its page, the window insert of
-the new token and its page, the open indexer page: one kv_compress_insert_jobs
-launch), then indexer_topk (c4a) and paged_hybrid_decode; layers stay in
-order.  The step is captured once in a HIP graph and replayed; `value` is
+decode update (re-fold of the open group with its RMSNorm and RoPE and its
+page, the window insert of the new token and its page, the open indexer page:
+one kv_compress_insert_jobs launch), then indexer_topk (c4a) and
+paged_hybrid_decode, whose output is delivered as fp8 rows with a per-row
+scale; layers stay in order.  The step is captured once in a HIP graph and replayed; `value` is
 decode tokens/s = B / step time.
 
 Also reported: the roofline of the dominant kernel (the indexer scoring
@@ -90,7 +91,7 @@ def layer_bytes(kind, B, L, d, H, W, d_idx=128, h_idx=16):
     epp = 256 // m
     win = min(W, L)
     q = H * d * 2
-    out = H * d * 4 + H * 4
+    out = H * d + H * 4 + H * 4  # fp8 output row, its scale, the lse
     win_rows = win * d + 4 * (-(-win // 256) + 1)
     if kind.topk is not None:
         kk = min(kind.topk, N)
@@ -155,12 +156,13 @@ def build_state(w, n_layers, torch, hca, gen, log):
             x[b] = gen.device_normal((L, d), 1.0, (0, w.cid, li, gen.S_TOK, b), dtype=torch.bfloat16)
         z = gen.device_normal((B, L), 1.0, (0, w.cid, li, gen.S_LOGIT))
         beta = dev(gen.slot_bias(w, li, m))
+        lay.gamma = dev(gen.norm_gain(w, li, d))
         ent = torch.empty((B, N, d), dtype=torch.float32, device="cuda")
         lay.kv = hca.PagedCache.empty(P, epp, d, w.kv_dtype)
         xi = x.view(torch.int16)
         torch.cuda.synchronize()
         ev0.record()
-        hca.kv_compress(xi, z, beta, zeros_b, lens, m, w.theta, ent, L)
+        hca.kv_compress(xi, z, beta, zeros_b, lens, m, w.theta, ent, L, norm_gamma=lay.gamma)
         hca.kv_quantize_page(ent, zeros_b, dev(np.full(B, N, np.int32)), N, table, lay.kv)
         ev1.record()
         torch.cuda.synchronize()
@@ -216,7 +218,9 @@ def build_state(w, n_layers, torch, hca, gen, log):
             lay.wi = dev(gen.index_weights(w, li, kind.h_idx))
             lay.sel = torch.zeros((B, kind.topk), dtype=torch.int32, device="cuda")
             lay.sel_n = torch.zeros((B,), dtype=torch.int32, device="cuda")
-        lay.out = torch.zeros((B, H, d), dtype=torch.float32, device="cuda")
+        # the attention output in the fp8 form the next projection takes
+        lay.out8 = torch.zeros((B, H, d), dtype=torch.uint8, device="cuda")
+        lay.out8s = torch.zeros((B, H), dtype=torch.float32, device="cuda")
         lay.lse = torch.zeros((B, H), dtype=torch.float32, device="cuda")
         layers.append(lay)
         torch.cuda.synchronize()
@@ -243,7 +247,8 @@ def decode_step(w, layers, shared, ws_idx, ws_att, hca, update=True, attend=True
                                    gate_logit=lay.z_last, pos_bias=lay.zero1, ntok=lay.one, rope_theta=w.theta,
                                    append=True),
                     hca.insert_job(lay.stage, lay.pos0, lay.e0, table, lay.kv, m, x=lay.ring_x, gate_logit=lay.ring_z,
-                                   pos_bias=lay.beta, ntok=lay.ntok, rope_theta=w.theta, append=True)]
+                                   pos_bias=lay.beta, ntok=lay.ntok, rope_theta=w.theta, append=True,
+                                   norm_gamma=lay.gamma)]
             if kind.topk is not None:
                 jobs.append(hca.insert_job(lay.istage, lay.pos0, lay.e0, table, lay.idx, m, append=True))
             hca.kv_compress_insert_jobs(jobs, w.B)
@@ -252,10 +257,12 @@ def decode_step(w, layers, shared, ws_idx, ws_att, hca, update=True, attend=True
         if attend:
             if kind.topk is not None:
                 hca.paged_hybrid_decode(lay.q, lay.kv, table, lay.win, wtable, lens, L, m, W, lay.sel, lay.sel_n,
-                                        scale, w.theta, lay.out, lay.lse, ws_att[kind.name])
+                                        scale, w.theta, None, lay.lse, ws_att[kind.name], out_fp8=lay.out8,
+                                        out_scale=lay.out8s)
             else:
                 hca.paged_hybrid_decode(lay.q, lay.kv, table, lay.win, wtable, lens, L, m, W, None, None, scale,
-                                        w.theta, lay.out, lay.lse, ws_att[kind.name])
+                                        w.theta, None, lay.lse, ws_att[kind.name], out_fp8=lay.out8,
+                                        out_scale=lay.out8s)
 
 
 def time_graph(torch, fn, steps, warmup):
@@ -333,7 +340,8 @@ def copy_bandwidth(torch, nbytes=1 << 30, reps=5):
 
 
 def cpu_baseline(w, budget_s=20.0):
-    """The oracle's decode step (indexer scores + top-k + gather/decode + attention)
+    """The oracle's decode step (indexer scores + top-k + gather/decode + attention
+    + fp8 output)
     for ONE sequence of one c4a and one c128a layer, on page contents of the
     workload's shape (random codes: the oracle's time does not depend on the
     values); repeated while within budget; scaled to the 61-layer stack."""
@@ -378,7 +386,8 @@ def cpu_baseline(w, budget_s=20.0):
                 sel = np.arange(N)
             rows = paging.decode_rows(kv, table, sel)
             rows = np.concatenate([rows, paging.decode_rows(win, wtable, attention.window_positions(L, W))])
-            attention.attend(q, rows, L, 1.0 / math.sqrt(d), w.theta)
+            o, _, _ = attention.attend(q, rows, L, 1.0 / math.sqrt(d), w.theta)
+            attention.quantize_out_fp8(o)
             times.append(time.perf_counter() - t0)
             if sum(times) > budget_s / len(kinds) or len(times) >= 200:
                 break
@@ -397,7 +406,7 @@ def cpu_baseline(w, budget_s=20.0):
         "unit": "tokens/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle decode step (indexer scores + top-k + row gather/decode + attention) of one "
+        "sample": (f"fp64 NumPy oracle decode step (indexer scores + top-k + row gather/decode + attention + fp8 output) of one "
                    f"sequence at L={L} for one c4a layer ({reps.get('c4a', 0)} runs, median "
                    f"{t_layer.get('c4a', 0):.2f} s) and one c128a layer ({reps.get('c128a', 0)} runs, median "
                    f"{t_layer.get('c128a', 0):.2f} s), scaled by the stack's {n_kind} layers; the batch's "
@@ -483,7 +492,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8 KV / fp4 idx, f16+bf16 MFMA, fp32 acc",
-        "data": "synthetic (seeded N(0,1) tokens, logits, queries, indexer keys; random page permutation)",
+        "data": ("synthetic (seeded N(0,1) tokens, logits, queries, indexer keys; U(0.5, 1.5) RMSNorm gains; "
+                 "random page permutation)"),
         "config": {"workload": w.name, "batch": w.B, "context": w.L, "layers": n_layers,
                    "c4a_layers": sum(1 for l in layers if l.kind.name == "c4a"),
                    "c128a_layers": sum(1 for l in layers if l.kind.name == "c128a"), "d": w.d, "heads": w.H,

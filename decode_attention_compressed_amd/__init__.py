@@ -52,7 +52,7 @@ class CInsertJob(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("x_stride_b", ctypes.c_int64), ("gate_logit", ctypes.c_void_p),
                 ("z_stride_b", ctypes.c_int64), ("pos_bias", ctypes.c_void_p), ("pos0", ctypes.c_void_p),
                 ("ntok", ctypes.c_void_p), ("m", ctypes.c_int32), ("rope_theta", ctypes.c_float),
-                ("stage", ctypes.c_void_p), ("stage_stride_b", ctypes.c_int64), ("e0", ctypes.c_void_p),
+                ("norm_gamma", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("stage", ctypes.c_void_p), ("stage_stride_b", ctypes.c_int64), ("e0", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("bt_stride", ctypes.c_int32), ("dst", CPagedCache),
                 ("append", ctypes.c_int32)]
 
@@ -72,9 +72,10 @@ def lib() -> ctypes.CDLL:
         L.hca_status_string.restype = ctypes.c_char_p
         L.hca_status_string.argtypes = [ctypes.c_int]
         L.hca_version.restype = ctypes.c_char_p
-        L.kv_compress.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _I64, _P]
-        L.kv_compress_insert.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _F32, _P, _I64, _P, _P, _I32,
-                                         CPagedCache, _I32, _P]
+        L.kv_compress.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _F32, _P, _I64,
+                                  _P]
+        L.kv_compress_insert.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _F32, _P, _F32, _P, _I64, _P,
+                                         _P, _I32, CPagedCache, _I32, _P]
         L.kv_compress_insert_jobs.argtypes = [ctypes.POINTER(CInsertJob), _I32, _I32, _P]
         L.kv_quantize_page_workspace.argtypes = [_I32, _I32, CPagedCache]
         L.kv_quantize_page_workspace.restype = _SZ
@@ -85,7 +86,7 @@ def lib() -> ctypes.CDLL:
         L.paged_hybrid_decode_workspace.argtypes = [_I32, _I32, _I32, _I32, _I32, _I32, _I32]
         L.paged_hybrid_decode_workspace.restype = _SZ
         L.paged_hybrid_decode.argtypes = [_P, _I32, CPagedCache, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32,
-                                          _I32, _I32, _P, _P, _I32, _F32, _F32, _P, _P, _P, _SZ, _P]
+                                          _I32, _I32, _P, _P, _I32, _F32, _F32, _P, _P, _P, _P, _P, _SZ, _P]
         L.kv_gather.argtypes = [CPagedCache, _P, _I32, _P, _I32, _I32, _P, _P, _P]
         L.hca_host_e4m3_encode.argtypes = [_P, _P, _I64]
         L.hca_host_e2m1_encode.argtypes = [_P, _P, _I64]
@@ -156,36 +157,39 @@ def version() -> str:
     return lib().hca_version().decode()
 
 
-def kv_compress(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, out, max_ntok: int, stream=None):
+def kv_compress(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, out, max_ntok: int, stream=None,
+                norm_gamma=None, norm_eps: float = 1e-6):
     """x: bf16 [B, T, d] (or int16 bit patterns); gate_logit f32 [B, T]; pos_bias f32 [m];
-    pos0, ntok int32 [B]; out f32 [B, ceil(T/m), d]."""
+    pos0, ntok int32 [B]; out f32 [B, ceil(T/m), d]; norm_gamma f32 [d] or None."""
     B, T, d = x.shape
     _check(lib().kv_compress(_ptr(x), x.stride(0), _ptr(gate_logit), gate_logit.stride(0), _ptr(pos_bias),
-                             _ptr(pos0), _ptr(ntok), B, max_ntok, d, m, rope_theta, _ptr(out), out.stride(0),
-                             _stream(stream)), "kv_compress")
+                             _ptr(pos0), _ptr(ntok), B, max_ntok, d, m, rope_theta, _ptr(norm_gamma), norm_eps,
+                             _ptr(out), out.stride(0), _stream(stream)), "kv_compress")
 
 
 def kv_compress_insert(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, stage, e0, block_table,
-                       dst: PagedCache, append: bool = False, stream=None):
+                       dst: PagedCache, append: bool = False, stream=None, norm_gamma=None, norm_eps: float = 1e-6):
     """Decode-step update of one pool in one launch: x bf16 [B, m, d] (the open
     group's tokens); gate_logit f32 [B, m]; pos_bias f32 [m]; pos0, ntok, e0
     int32 [B]; stage f32 [B, epp, d] (the open page's staging); block_table
-    int32 [B, nb]."""
+    int32 [B, nb]; norm_gamma f32 [d] or None."""
     B = x.shape[0]
     _check(lib().kv_compress_insert(_ptr(x), x.stride(0), _ptr(gate_logit), gate_logit.stride(0), _ptr(pos_bias),
-                                    _ptr(pos0), _ptr(ntok), B, m, rope_theta, _ptr(stage), stage.stride(0), _ptr(e0),
-                                    _ptr(block_table), block_table.stride(0), dst.c(), 1 if append else 0,
-                                    _stream(stream)), "kv_compress_insert")
+                                    _ptr(pos0), _ptr(ntok), B, m, rope_theta, _ptr(norm_gamma), norm_eps,
+                                    _ptr(stage), stage.stride(0), _ptr(e0), _ptr(block_table),
+                                    block_table.stride(0), dst.c(), 1 if append else 0, _stream(stream)),
+           "kv_compress_insert")
 
 
 def insert_job(stage, pos0, e0, block_table, dst: PagedCache, m: int, x=None, gate_logit=None, pos_bias=None,
-               ntok=None, rope_theta: float = 0.0, append: bool = False) -> "CInsertJob":
+               ntok=None, rope_theta: float = 0.0, append: bool = False, norm_gamma=None,
+               norm_eps: float = 1e-6) -> "CInsertJob":
     """One job of kv_compress_insert_jobs (x None: the open row is already in stage).
     The tensors must stay alive until the call that takes the job is enqueued."""
     return CInsertJob(_ptr(x), 0 if x is None else x.stride(0), _ptr(gate_logit),
                       0 if gate_logit is None else gate_logit.stride(0), _ptr(pos_bias), _ptr(pos0), _ptr(ntok), m,
-                      rope_theta, _ptr(stage), stage.stride(0), _ptr(e0), _ptr(block_table), block_table.stride(0),
-                      dst.c(), 1 if append else 0)
+                      rope_theta, _ptr(norm_gamma), norm_eps, _ptr(stage), stage.stride(0), _ptr(e0),
+                      _ptr(block_table), block_table.stride(0), dst.c(), 1 if append else 0)
 
 
 def kv_compress_insert_jobs(jobs, B: int, stream=None):
@@ -237,8 +241,9 @@ def paged_hybrid_decode_workspace(B: int, H: int, d: int, max_seq_len: int, m: i
 
 def paged_hybrid_decode(q, kv: PagedCache, block_table, win: Optional[PagedCache], win_block_table, seq_lens,
                         max_seq_len: int, m: int, window: int, sel_idx, sel_n, softmax_scale: float,
-                        rope_theta: float, out, lse, ws, stream=None):
-    """q bf16 [B, H, d]; sel_idx int32 [B, k] or None (all entries); out f32 [B, H, d]; lse f32 [B, H] or None."""
+                        rope_theta: float, out, lse, ws, stream=None, out_fp8=None, out_scale=None):
+    """q bf16 [B, H, d]; sel_idx int32 [B, k] or None (all entries); out f32 [B, H, d] or None;
+    lse f32 [B, H] or None; out_fp8 uint8 [B, H, d] with out_scale f32 [B, H], or None."""
     B, H, d = q.shape
     k = 0 if sel_idx is None else sel_idx.shape[1]
     wc = win.c() if (win is not None and window > 0) else _null_cache()
@@ -246,7 +251,7 @@ def paged_hybrid_decode(q, kv: PagedCache, block_table, win: Optional[PagedCache
     _check(lib().paged_hybrid_decode(_ptr(q), H, kv.c(), _ptr(block_table), block_table.stride(0), wc, _ptr(wbt),
                                      0 if wbt is None else wbt.stride(0), _ptr(seq_lens), B, max_seq_len, m, window,
                                      _ptr(sel_idx), _ptr(sel_n), k, softmax_scale, rope_theta, _ptr(out), _ptr(lse),
-                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "paged_hybrid_decode")
+                                     _ptr(out_fp8), _ptr(out_scale), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "paged_hybrid_decode")
 
 
 def kv_gather(src: PagedCache, block_table, n_rows, max_rows: int, dst_codes, dst_scales, stream=None):

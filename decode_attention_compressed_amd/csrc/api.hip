@@ -14,6 +14,10 @@ namespace {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 bool valid_m(int m) { return m >= 1 && m <= 256 && (256 % m) == 0; }
+// RMS normalisation arguments: none, or a 16-byte aligned gain vector with a finite eps > 0
+bool norm_ok(const float* gamma, float eps) {
+  return gamma == nullptr || (aligned(gamma, 16) && eps > 0.0f && isfinite(eps));
+}
 
 // a pool descriptor that the kernels can index safely
 bool cache_ok(const hca_paged_cache& c) {
@@ -47,11 +51,13 @@ const char* hca_version(void) { return "hca 0.1.0 gfx950"; }
 
 hca_status kv_compress(const uint16_t* x, int64_t x_stride_b, const float* gate_logit, int64_t z_stride_b,
                        const float* pos_bias, const int32_t* pos0, const int32_t* ntok, int32_t B, int32_t max_ntok,
-                       int32_t d, int32_t m, float rope_theta, float* out, int64_t out_stride_b, void* stream) {
+                       int32_t d, int32_t m, float rope_theta, const float* norm_gamma, float norm_eps, float* out,
+                       int64_t out_stride_b, void* stream) {
   if (B < 0 || max_ntok < 0) return HCA_ERR_INVALID;
   if (!valid_m(m) || d < 8 || (d % 8) != 0) return HCA_ERR_INVALID;
   if (d > 2048) return HCA_ERR_UNSUPPORTED;
   if (!(rope_theta > 0.0f) || !isfinite(rope_theta)) return HCA_ERR_INVALID;
+  if (!norm_ok(norm_gamma, norm_eps)) return HCA_ERR_INVALID;
   if (B == 0 || max_ntok == 0) return HCA_OK;
   if (!x || !gate_logit || !pos_bias || !pos0 || !ntok || !out) return HCA_ERR_INVALID;
   if (!aligned(x, 16) || !aligned(out, 16)) return HCA_ERR_INVALID;
@@ -59,8 +65,8 @@ hca_status kv_compress(const uint16_t* x, int64_t x_stride_b, const float* gate_
   if (x_stride_b % 8 != 0 || out_stride_b % 4 != 0) return HCA_ERR_INVALID;
   if (B > 1 && (x_stride_b < (int64_t)max_ntok * d || z_stride_b < max_ntok || out_stride_b < n_out * d))
     return HCA_ERR_INVALID;
-  CompressArgs a{x, x_stride_b, gate_logit, z_stride_b, pos_bias, pos0, ntok, B, max_ntok, d, m, rope_theta, out,
-                 out_stride_b};
+  CompressArgs a{x, x_stride_b, gate_logit, z_stride_b, pos_bias, pos0, ntok, B, max_ntok, d, m, rope_theta,
+                 norm_gamma, norm_eps, out, out_stride_b};
   return from_hip(launch_compress(a, (hipStream_t)stream));
 }
 
@@ -75,6 +81,7 @@ hca_status make_insert(const hca_insert_job& j, int32_t B, InsertArgs& out) {
   if (d > 2048) return HCA_ERR_UNSUPPORTED;
   const bool fold = j.x != nullptr;
   if (fold && (!(j.rope_theta > 0.0f) || !isfinite(j.rope_theta))) return HCA_ERR_INVALID;
+  if (fold && !norm_ok(j.norm_gamma, j.norm_eps)) return HCA_ERR_INVALID;
   if (!j.pos0 || !j.stage || !j.e0 || !j.block_table) return HCA_ERR_INVALID;
   if (fold && (!j.gate_logit || !j.pos_bias || !j.ntok || !aligned(j.x, 16) || j.x_stride_b % 8 != 0))
     return HCA_ERR_INVALID;
@@ -82,7 +89,7 @@ hca_status make_insert(const hca_insert_job& j, int32_t B, InsertArgs& out) {
   if (B > 1 && j.stage_stride_b < (int64_t)j.dst.epp * d) return HCA_ERR_INVALID;
   if (fold && B > 1 && (j.x_stride_b < (int64_t)j.m * d || j.z_stride_b < j.m)) return HCA_ERR_INVALID;
   out = InsertArgs{CompressArgs{j.x, j.x_stride_b, j.gate_logit, j.z_stride_b, j.pos_bias, j.pos0, j.ntok, B, j.m, d,
-                                j.m, j.rope_theta, nullptr, 0},
+                                j.m, j.rope_theta, j.norm_gamma, j.norm_eps, nullptr, 0},
                    j.stage, j.stage_stride_b, j.e0, j.block_table, j.bt_stride, j.dst, j.append};
   return HCA_OK;
 }
@@ -92,13 +99,13 @@ extern "C" {
 
 hca_status kv_compress_insert(const uint16_t* x, int64_t x_stride_b, const float* gate_logit, int64_t z_stride_b,
                               const float* pos_bias, const int32_t* pos0, const int32_t* ntok, int32_t B, int32_t m,
-                              float rope_theta, float* stage, int64_t stage_stride_b, const int32_t* e0,
-                              const int32_t* block_table, int32_t bt_stride, hca_paged_cache dst, int32_t append,
-                              void* stream) {
+                              float rope_theta, const float* norm_gamma, float norm_eps, float* stage,
+                              int64_t stage_stride_b, const int32_t* e0, const int32_t* block_table, int32_t bt_stride,
+                              hca_paged_cache dst, int32_t append, void* stream) {
   if (B < 0) return HCA_ERR_INVALID;
   if (!x) return HCA_ERR_INVALID;  // this entry point always folds
-  const hca_insert_job j{x, x_stride_b, gate_logit, z_stride_b, pos_bias, pos0, ntok, m, rope_theta, stage,
-                         stage_stride_b, e0, block_table, bt_stride, dst, append};
+  const hca_insert_job j{x, x_stride_b, gate_logit, z_stride_b, pos_bias, pos0, ntok, m, rope_theta, norm_gamma,
+                         norm_eps, stage, stage_stride_b, e0, block_table, bt_stride, dst, append};
   InsertJobs jobs{};
   const hca_status st = make_insert(j, B, jobs.job[0]);
   if (st != HCA_OK || B == 0) return st;
@@ -203,8 +210,8 @@ hca_status paged_hybrid_decode(const uint16_t* q, int32_t H, hca_paged_cache kv,
                                int32_t bt_stride, hca_paged_cache win, const int32_t* win_block_table,
                                int32_t wbt_stride, const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t m,
                                int32_t window, const int32_t* sel_idx, const int32_t* sel_n, int32_t k,
-                               float softmax_scale, float rope_theta, float* out, float* lse, void* ws,
-                               size_t ws_bytes, void* stream) {
+                               float softmax_scale, float rope_theta, float* out, float* lse, uint8_t* out_fp8,
+                               float* out_scale, void* ws, size_t ws_bytes, void* stream) {
   if (B < 0 || max_seq_len < 0 || !valid_m(m) || bt_stride < 1) return HCA_ERR_INVALID;
   if (H < 1) return HCA_ERR_INVALID;
   if (H > 128) return HCA_ERR_UNSUPPORTED;
@@ -222,7 +229,8 @@ hca_status paged_hybrid_decode(const uint16_t* q, int32_t H, hca_paged_cache kv,
   if (sel_idx && (!sel_n || k < 1)) return HCA_ERR_INVALID;
   if (!isfinite(softmax_scale) || !(rope_theta > 0.0f) || !isfinite(rope_theta)) return HCA_ERR_INVALID;
   if (B == 0) return HCA_OK;
-  if (!q || !block_table || !seq_lens || !out) return HCA_ERR_INVALID;
+  if (!q || !block_table || !seq_lens || (!out && !out_fp8)) return HCA_ERR_INVALID;
+  if (out_fp8 && (!out_scale || !aligned(out_fp8, 2))) return HCA_ERR_INVALID;
   if (!aligned(q, 16)) return HCA_ERR_INVALID;
   const AttnPlan plan = attn_plan(B, H, d, max_seq_len, m, window, sel_idx ? k : 0, sel_idx != nullptr);
   if (plan.splits > kAttnMaxSplits) return HCA_ERR_UNSUPPORTED;
@@ -231,7 +239,8 @@ hca_status paged_hybrid_decode(const uint16_t* q, int32_t H, hca_paged_cache kv,
   if (window == 0) { w = kv; w.epp = 256; }  // never read
   AttnArgs a{q, H, kv, block_table, bt_stride, w, window > 0 ? win_block_table : block_table,
              window > 0 ? wbt_stride : bt_stride, seq_lens, B, max_seq_len, m, window, sel_idx, sel_n,
-             sel_idx ? k : 0, softmax_scale, rope_theta, out, lse, reinterpret_cast<unsigned char*>(ws), plan};
+             sel_idx ? k : 0, softmax_scale, rope_theta, out, lse, out_fp8, out_fp8 ? out_scale : nullptr,
+             reinterpret_cast<unsigned char*>(ws), plan};
   return from_hip(launch_attention(a, (hipStream_t)stream));
 }
 

@@ -756,10 +756,17 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
   __syncthreads();
   const float M = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
   __syncthreads();
-  float* out = a.out + ((int64_t)b * H + h) * D;
+  const int64_t row = (int64_t)b * H + h;
+  float* out = a.out ? a.out + row * D : nullptr;
   if (M == -INFINITY) {
-    for (int c = threadIdx.x; c < D; c += kCombThreads) out[c] = 0.0f;
-    if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)b * H + h] = -INFINITY;
+    if (out)
+      for (int c = threadIdx.x; c < D; c += kCombThreads) out[c] = 0.0f;
+    if (a.out8)
+      for (int c = threadIdx.x; c < D; c += kCombThreads) a.out8[row * D + c] = 0;
+    if (threadIdx.x == 0) {
+      if (a.lse) a.lse[row] = -INFINITY;
+      if (a.out8) a.out8_scale[row] = 1.0f;
+    }
     return;
   }
   float tloc = 0.0f;
@@ -791,9 +798,12 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
   acc_s[grp][li] = acc;
   __syncthreads();
   const float inv_tot = 1.0f / tot;
+  float2 ov[kPairs];
+  float amax = 0.0f;
 #pragma unroll
   for (int k = 0; k < kPairs; ++k) {
     const int pi = threadIdx.x + kCombThreads * k;
+    ov[k] = make_float2(0.0f, 0.0f);
     if (pi >= D / 2) break;
     float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
@@ -804,10 +814,31 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
     }
     o0 *= inv_tot;
     o1 *= inv_tot;
-    out[2 * pi] = o0 * cs[k].x + o1 * cs[k].y;  // rotation by -angle
-    out[2 * pi + 1] = -o0 * cs[k].y + o1 * cs[k].x;
+    ov[k] = make_float2(o0 * cs[k].x + o1 * cs[k].y, -o0 * cs[k].y + o1 * cs[k].x);  // rotation by -angle
+    if (out) {
+      out[2 * pi] = ov[k].x;
+      out[2 * pi + 1] = ov[k].y;
+    }
+    amax = fmaxf(amax, fmaxf(fabsf(ov[k].x), fabsf(ov[k].y)));
   }
-  if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)b * H + h] = M + logf(tot);
+  if (threadIdx.x == 0 && a.lse) a.lse[row] = M + logf(tot);
+  if (a.out8) {
+    // fp8 form of the row for the next projection: one scale per (token, head)
+    // row, amax / 448 (1 for an all-zero row), codes E4M3(x / scale)
+    amax = wave_max(amax);
+    if ((threadIdx.x & 63) == 0) red_s[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
+    const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+    uint16_t* o8 = reinterpret_cast<uint16_t*>(a.out8 + row * D);
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
+      const int pi = threadIdx.x + kCombThreads * k;
+      if (pi >= D / 2) break;
+      o8[pi] = (uint16_t)(e4m3_encode(ov[k].x / sc) | (e4m3_encode(ov[k].y / sc) << 8));
+    }
+    if (threadIdx.x == 0) a.out8_scale[row] = sc;
+  }
 }
 
 template <int D, int KVDT>

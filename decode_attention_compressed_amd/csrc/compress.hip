@@ -9,6 +9,12 @@
 // its own.  Large m: the 256 threads of a block share one entry, each
 // row-group folding a strided subset of its tokens (a batch's loads all in
 // flight before the first is summed), reduced through LDS.
+//
+// With a gain vector the folded entry is RMS-normalised before it is rotated
+// (section 3.2.1 lists compressor, RMSNorm, RoPE and insertion as one fused
+// step): the sum of squares of a row is reduced across the threads that hold
+// it in a fixed order, so every thread of the row scales by the same factor
+// and a fold gives the same bits wherever it runs.
 #include "hca_common.h"
 #include "hca_internal.h"
 
@@ -43,6 +49,58 @@ __device__ __forceinline__ void rope_store8(float* dst, float* lds, const float 
   }
 }
 
+// Entry j of a small-m fold, the 8 dims of this thread: softmax over the
+// group's available slots, weighted sum (normalised, not yet rotated).
+__device__ __forceinline__ void small_fold(const CompressArgs& a, const float* zb, const uint16_t* xb, int j, int n,
+                                           float acc[8]) {
+  const int m = a.m;
+  const int t0 = j * m;
+  const int r = min(m, n - t0);
+  float mx = -INFINITY;
+  for (int i = 0; i < r; ++i) mx = fmaxf(mx, zb[t0 + i] + a.beta[i]);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+  float tot = 0.0f;
+  for (int i = 0; i < r; ++i) {
+    const float e = expf(zb[t0 + i] + a.beta[i] - mx);
+    tot += e;
+    float v[8];
+    load_bf16x8(xb + (int64_t)(t0 + i) * a.d, v);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = fmaf(e, v[c], acc[c]);
+  }
+  const float inv_tot = 1.0f / tot;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] *= inv_tot;
+}
+
+// Sum of v over the TD consecutive threads of row group gi (TD = threads per
+// row, RP full groups in the block), the same value in every thread of the
+// group.  Called by every thread of the block (it may synchronize it).
+__device__ __forceinline__ float row_group_sum(float v, int TD, int RP, int gi, float* sq_s) {
+  if ((TD & (TD - 1)) == 0) {
+    // an xor butterfly gives every lane the same sum (each step adds two equal
+    // partial sums in either order)
+    const int w = TD < 64 ? TD : 64;
+    for (int o = 1; o < w; o <<= 1) v += __shfl_xor(v, o, 64);
+    if (TD <= 64) return v;
+    if ((threadIdx.x & 63) == 0) sq_s[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const int nw = TD >> 6;
+    float t = 0.0f;
+    for (int k = 0; k < nw; ++k) t += sq_s[gi * nw + k];
+    __syncthreads();
+    return t;
+  }
+  sq_s[threadIdx.x] = v;
+  __syncthreads();
+  float t = 0.0f;
+  if (gi < RP)
+    for (int k = 0; k < TD; ++k) t += sq_s[gi * TD + k];
+  __syncthreads();
+  return t;
+}
+
 // The fold of sequence b by one block of kCompressThreads threads, as block bx
 // of gx blocks over the sequence's work.  With a non-null `lds_row` (a fold of
 // a single entry) the entry is also left in that shared array.  The dynamic
@@ -64,31 +122,61 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
   const float* zb = a.z + (int64_t)b * a.zs;
   float* ob = a.out + (int64_t)b * a.os + li * 8;
 
+  const bool small = (PATHS & 1) && (!(PATHS & 2) || m <= kSmallM);
+  // the gains are loaded first, so their latency hides behind the fold: a
+  // small-m thread holds its 8 dims, a large-m thread its dim pairs
+  // t = threadIdx.x + kCompressThreads * k (d <= 2048: at most 4)
+  constexpr int kGainPairs = 4;
+  float gam[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float2 gpair[kGainPairs];
+#pragma unroll
+  for (int k = 0; k < kGainPairs; ++k) gpair[k] = make_float2(0.0f, 0.0f);
+  if (a.gamma != nullptr) {
+    if (small) {
+      if (active) {
+        const f32x4* g4 = reinterpret_cast<const f32x4*>(a.gamma + li * 8);
+        const f32x4 g0 = g4[0], g1 = g4[1];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) { gam[c] = g0[c]; gam[4 + c] = g1[c]; }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kGainPairs; ++k) {
+        const int t = threadIdx.x + kCompressThreads * k;
+        if (t < a.d / 2) gpair[k] = reinterpret_cast<const float2*>(a.gamma)[t];
+      }
+    }
+  }
+
   double inv[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) inv[p] = rope_inv_freq(li * 4 + p, a.d, a.theta);
 
-  if ((PATHS & 1) && (!(PATHS & 2) || m <= kSmallM)) {
-    if (!active) return;
-    for (int j = bx * RP + gi; j < N; j += gx * RP) {
-      const int t0 = j * m;
-      const int r = min(m, n - t0);
-      float mx = -INFINITY;
-      for (int i = 0; i < r; ++i) mx = fmaxf(mx, zb[t0 + i] + a.beta[i]);
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      float tot = 0.0f;
-      for (int i = 0; i < r; ++i) {
-        const float e = expf(zb[t0 + i] + a.beta[i] - mx);
-        tot += e;
-        float v[8];
-        load_bf16x8(xb + (int64_t)(t0 + i) * a.d, v);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = fmaf(e, v[c], acc[c]);
+  if (small) {
+    if (a.gamma == nullptr) {
+      if (!active) return;
+      for (int j = bx * RP + gi; j < N; j += gx * RP) {
+        float acc[8];
+        small_fold(a, zb, xb, j, n, acc);
+        rope_store8(ob + (int64_t)j * a.d, lds_row ? lds_row + li * 8 : nullptr, acc, (double)p0 + (double)(j * m), inv);
       }
-      const float inv_tot = 1.0f / tot;
+      return;
+    }
+    // normalised: every thread runs every round (the row sum may synchronize)
+    __shared__ float sq_s[kCompressThreads];
+    for (int j0 = bx * RP; j0 < N; j0 += gx * RP) {
+      const int j = j0 + gi;
+      const bool live = active && j < N;
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (live) small_fold(a, zb, xb, j, n, acc);
+      float ss = 0.0f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] *= inv_tot;
-      rope_store8(ob + (int64_t)j * a.d, lds_row ? lds_row + li * 8 : nullptr, acc, (double)p0 + (double)t0, inv);
+      for (int c = 0; c < 8; ++c) ss = fmaf(acc[c], acc[c], ss);
+      const float rs = 1.0f / sqrtf(row_group_sum(ss, TD, RP, gi, sq_s) / (float)a.d + a.eps);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = acc[c] * rs * gam[c];
+      if (live)
+        rope_store8(ob + (int64_t)j * a.d, lds_row ? lds_row + li * 8 : nullptr, acc, (double)p0 + (double)(j * m), inv);
     }
     return;
   }
@@ -162,14 +250,47 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
     // one thread per dim pair of the slice: sum the row groups, normalise, rotate
     const float inv_tot = 1.0f / tot;
     const double pos = (double)p0 + (double)t0;
-    for (int t = threadIdx.x; t < DS / 2; t += kCompressThreads) {
-      float e0 = 0.0f, e1 = 0.0f;
-      for (int g = 0; g < RS; ++g) {
-        e0 += acc_s[g * DS + 2 * t];
-        e1 += acc_s[g * DS + 2 * t + 1];
+    float rs = 1.0f;
+    if (a.gamma != nullptr) {
+      // the entry's sum of squares (the slice is the whole row, DS = d): the
+      // pair sums are left in row group 0 of acc_s (each thread reads and
+      // writes only its own pairs' columns), then reduced over the block
+      float ss = 0.0f;
+      for (int t = threadIdx.x; t < DS / 2; t += kCompressThreads) {
+        float e0 = 0.0f, e1 = 0.0f;
+        for (int g = 0; g < RS; ++g) {
+          e0 += acc_s[g * DS + 2 * t];
+          e1 += acc_s[g * DS + 2 * t + 1];
+        }
+        e0 *= inv_tot;
+        e1 *= inv_tot;
+        acc_s[2 * t] = e0;
+        acc_s[2 * t + 1] = e1;
+        ss = fmaf(e0, e0, ss);
+        ss = fmaf(e1, e1, ss);
       }
-      e0 *= inv_tot;
-      e1 *= inv_tot;
+      ss = wave_sum(ss);
+      if ((threadIdx.x & 63) == 0) red_s[threadIdx.x >> 6] = ss;
+      __syncthreads();
+      ss = (red_s[0] + red_s[1]) + (red_s[2] + red_s[3]);
+      rs = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+    }
+#pragma unroll
+    for (int k = 0; k < kGainPairs; ++k) {
+      const int t = threadIdx.x + kCompressThreads * k;
+      if (t >= DS / 2) break;
+      float e0 = 0.0f, e1 = 0.0f;
+      if (a.gamma != nullptr) {  // the slice is the whole row (base = 0)
+        e0 = acc_s[2 * t] * rs * gpair[k].x;
+        e1 = acc_s[2 * t + 1] * rs * gpair[k].y;
+      } else {
+        for (int g = 0; g < RS; ++g) {
+          e0 += acc_s[g * DS + 2 * t];
+          e1 += acc_s[g * DS + 2 * t + 1];
+        }
+        e0 *= inv_tot;
+        e1 *= inv_tot;
+      }
       float c, sn;
       rope_cs(pos, rope_inv_freq(base / 2 + t, a.d, a.theta), c, sn);
       float* o = a.out + (int64_t)b * a.os + (int64_t)j * a.d + base + 2 * t;

@@ -15,6 +15,7 @@ struct CompressArgs {
   const int32_t* pos0; const int32_t* ntok;
   int B, max_ntok, d, m;
   float theta;
+  const float* gamma; float eps;  // RMS normalisation of each entry before its rotation (gamma null: none)
   float* out; int64_t os;
   int ds;  // dims per block slice (set by the launcher)
 };
@@ -103,6 +104,7 @@ struct AttnArgs {
   const int32_t* sel; const int32_t* sel_n; int k;
   float scale, theta;
   float* out; float* lse;
+  uint8_t* out8; float* out8_scale;  // fp8 form of the output (null: none)
   unsigned char* ws; AttnPlan plan;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);

@@ -104,12 +104,16 @@ const char* hca_version(void);
  * slots i < r = min(m, ntok[b] - j*m):
  *     w_i = softmax_i(gate_logit[t] + pos_bias[i]),  t = j*m + i
  *     c   = sum_i w_i x[t]
+ *     c   = c * norm_gamma / sqrt(mean_c(c^2) + norm_eps)   (only if norm_gamma)
  *     out[b][j] = RoPE(c, pos0[b] + j*m)
  * A partial group (r < m) is normalized over its r slots, which is the state of
  * the rolling residual; re-running the call on a decode step's open group
  * (pos0 = m*floor((L-1)/m), ntok = L - pos0) re-emits the open entry.  With
  * m = 1 this is the window insert RoPE(x_t, t).  RoPE rotates adjacent pairs
  * (2i, 2i+1) by angle p * rope_theta^(-2i/d); the angle is reduced in fp64.
+ * The optional RMS normalisation is the RMSNorm that section 3.2.1 fuses
+ * between the compressor and RoPE; it acts on the folded (possibly partial)
+ * entry, before the rotation.
  *
  *   x          bf16  x[b * x_stride_b + t * d + c]
  *   gate_logit float gate_logit[b * z_stride_b + t]
@@ -117,12 +121,15 @@ const char* hca_version(void);
  *   pos0, ntok int32 [B] (device); ntok[b] is clamped to [0, max_ntok]
  *   max_ntok   host bound on ntok (sizes the grid)
  *   d          even, 2 <= d, d % 8 == 0;  m in {1, 2, 4, ..., 256}
+ *   norm_gamma float [d] (16-byte aligned) or NULL (no normalisation);
+ *   norm_eps   finite, > 0 when norm_gamma is given (ignored otherwise)
  *   out        float out[b * out_stride_b + j * d + c]
  */
 hca_status kv_compress(const uint16_t* x, int64_t x_stride_b, const float* gate_logit,
                        int64_t z_stride_b, const float* pos_bias, const int32_t* pos0,
                        const int32_t* ntok, int32_t B, int32_t max_ntok, int32_t d, int32_t m,
-                       float rope_theta, float* out, int64_t out_stride_b, void* stream);
+                       float rope_theta, const float* norm_gamma, float norm_eps, float* out,
+                       int64_t out_stride_b, void* stream);
 
 /*
  * kv_quantize_page -- quantize entries into their pages (V4 page, sections
@@ -168,8 +175,9 @@ hca_status kv_quantize_page(const float* src, int64_t src_stride_b, const int32_
  * multiple of dst.epp), which must be in [0, dst.epp) (else nothing is
  * written); rows 0 .. j-e0[b]-1 of stage are the page's earlier entries.
  *
- *   x, gate_logit, pos_bias: as kv_compress, with T = m tokens per sequence;
- *              m = 1 is the window insert of one token (dst.epp = 256)
+ *   x, gate_logit, pos_bias, norm_gamma, norm_eps: as kv_compress, with
+ *              T = m tokens per sequence; m = 1 is the window insert of one
+ *              token (dst.epp = 256)
  *   stage      float stage[b * stage_stride_b + r * dst.dim + c], r < dst.epp;
  *              row j - e0[b] is written
  *   block_table int32 [B][bt_stride]: page of logical block e0[b] / dst.epp
@@ -188,9 +196,9 @@ hca_status kv_quantize_page(const float* src, int64_t src_stride_b, const int32_
  */
 hca_status kv_compress_insert(const uint16_t* x, int64_t x_stride_b, const float* gate_logit, int64_t z_stride_b,
                               const float* pos_bias, const int32_t* pos0, const int32_t* ntok, int32_t B, int32_t m,
-                              float rope_theta, float* stage, int64_t stage_stride_b, const int32_t* e0,
-                              const int32_t* block_table, int32_t bt_stride, hca_paged_cache dst, int32_t append,
-                              void* stream);
+                              float rope_theta, const float* norm_gamma, float norm_eps, float* stage,
+                              int64_t stage_stride_b, const int32_t* e0, const int32_t* block_table,
+                              int32_t bt_stride, hca_paged_cache dst, int32_t append, void* stream);
 
 /*
  * kv_compress_insert_jobs -- several kv_compress_insert calls over the same B
@@ -198,7 +206,7 @@ hca_status kv_compress_insert(const uint16_t* x, int64_t x_stride_b, const float
  * open indexer page), so the decode update of a layer costs one launch.
  * Each job has the arguments of kv_compress_insert; a job whose x is NULL
  * folds nothing: its open row j - e0[b] is already in stage (gate_logit,
- * pos_bias, ntok and rope_theta are then unused) and the page is quantized as
+ * pos_bias, ntok, rope_theta and the norm arguments are then unused) and the page is quantized as
  * described above.  Jobs must write different pages and staging rows.
  *   n_jobs     0 .. 4 (HCA_ERR_UNSUPPORTED above); every job is validated
  *              before anything is launched.
@@ -213,6 +221,8 @@ typedef struct {
   const int32_t* ntok;
   int32_t m;
   float rope_theta;
+  const float* norm_gamma; /* NULL: no normalisation */
+  float norm_eps;
   float* stage;
   int64_t stage_stride_b;
   const int32_t* e0;
@@ -271,13 +281,20 @@ hca_status indexer_topk(const uint16_t* q_idx, const float* head_w, int32_t HI,
  *     p = softmax(softmax_scale * q~_h . rows),  o = sum p * rows
  *     out[b][h] = RoPE^-1(o, L-1),  lse[b][h] = log sum exp(logits)
  * A sequence with no rows gets out = 0 and lse = -inf.
+ * The output can also be delivered in fp8, as section 3.2.1 fuses inverse RoPE
+ * with the fp8 quantization that feeds the fp8 o_lora GEMM: one scale per
+ * (b, h) row, out_scale[b][h] = amax/448 over the row's d values (1 for an
+ * all-zero row), out_fp8[b][h][c] = E4M3(out[b][h][c] / out_scale[b][h]),
+ * round to nearest even, saturating at +-448 (the fp8 pages' rule).
  *
  *   q          bf16 [B][H][kv.dim], unrotated;  H in 1 .. 128
  *   kv.dim     in {64, 128, 256, 512}; win.dim == kv.dim; win.epp == 256
  *   kv, win    dtype HCA_FP8_E4M3 or HCA_BF16, the same for both pools
  *   sel_idx    int32 [B][k] or NULL;  sel_n int32 [B] (required with sel_idx)
  *   window     0 .. 256 (0: no window; win and win_block_table may be NULL)
- *   out        float [B][H][kv.dim];  lse float [B][H] or NULL
+ *   out        float [B][H][kv.dim] or NULL;  lse float [B][H] or NULL
+ *   out_fp8    uint8 [B][H][kv.dim] (2-byte aligned) or NULL, with
+ *   out_scale  float [B][H]; at least one of out and out_fp8 is required
  *   ws         workspace of paged_hybrid_decode_workspace(B, H, d, max_seq_len,
  *              m, window, k) bytes, with k = 0 when sel_idx will be NULL; its
  *              contents on entry do not matter.
@@ -290,7 +307,8 @@ hca_status paged_hybrid_decode(const uint16_t* q, int32_t H, hca_paged_cache kv,
                                const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t m,
                                int32_t window, const int32_t* sel_idx, const int32_t* sel_n,
                                int32_t k, float softmax_scale, float rope_theta, float* out,
-                               float* lse, void* ws, size_t ws_bytes, void* stream);
+                               float* lse, uint8_t* out_fp8, float* out_scale, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /*
  * kv_gather -- paged -> contiguous copy of rows 0 .. n_rows[b]-1 of every

@@ -31,6 +31,8 @@ class LayerSpec:
     h_idx: int = 16
     theta: float = 1.0e6
     scale: Optional[float] = None  # default 1/sqrt(d)
+    gamma: Optional[np.ndarray] = None  # RMSNorm gain of the entries ([V4-vLLM] 3.2.1), None: no norm
+    eps: float = 1e-6
 
     @property
     def epp(self):
@@ -54,7 +56,7 @@ def window_blocks(L: int, window: int):
 def fill_entries(spec: LayerSpec, pool, table_row, x, z, beta):
     """Compress a whole context and quantize all of its entry pages.  Returns the
     fp64 entries (before quantization)."""
-    e = compressor.compress(x, z, beta, spec.m, spec.theta)
+    e = compressor.compress(x, z, beta, spec.m, spec.theta, gamma=spec.gamma, eps=spec.eps)
     paging.write_run(pool, table_row, 0, e.astype(np.float32))
     return e
 

@@ -4,10 +4,12 @@ Every array comes from its own NumPy PCG64 stream keyed by
 SeedSequence([seed, config, layer, stream, sequence]), so any one sequence of
 any one layer can be drawn without drawing the rest.  Stream ids: 0 block
 table, 1 lengths, 2 tokens, 3 logits, 4 slot bias, 5 queries, 6 indexer keys,
-7 indexer queries, 8 indexer head weights, 9 indexer-key re-draws.
+7 indexer queries, 8 indexer head weights, 9 indexer-key re-draws, 10 the
+entries' RMSNorm gain.
 
 Distributions: tokens, logits, queries, indexer keys and queries and head
 weights ~ N(0, 1); slot biases ~ N(0, 0.1) (0.1 is the standard deviation);
+RMSNorm gains ~ U(0.5, 1.5) (fp32);
 bf16 tensors are fp32 draws rounded to nearest even by torch's CPU cast.
 
 For the largest workloads the benchmark draws tensors on the GPU with torch's
@@ -20,7 +22,7 @@ import numpy as np
 from .configs import Workload
 
 BLOCK = 256
-S_TABLE, S_LEN, S_TOK, S_LOGIT, S_BETA, S_Q, S_IDXK, S_IDXQ, S_IDXW, S_REDRAW = range(10)
+S_TABLE, S_LEN, S_TOK, S_LOGIT, S_BETA, S_Q, S_IDXK, S_IDXQ, S_IDXW, S_REDRAW, S_GAIN = range(11)
 SHARED = 1 << 20  # sub-key of the shared-prefix draws
 
 
@@ -134,6 +136,11 @@ def logits(w: Workload, layer, b, L, members=(), seed=0):
 
 def slot_bias(w: Workload, layer, m, seed=0):
     return _normal(rng(seed, w.cid, layer, S_BETA), (m,), w.beta_std)
+
+
+def norm_gain(w: Workload, layer, d, seed=0):
+    """fp32 [d] gain of the RMSNorm applied to a layer's compressed entries."""
+    return rng(seed, w.cid, layer, S_GAIN).uniform(0.5, 1.5, d).astype(np.float32)
 
 
 def queries(w: Workload, layer, seed=0):

@@ -64,6 +64,56 @@ def download_pool(pc, like: paging.Pool) -> paging.Pool:
     return out
 
 
+# E2M1 magnitudes by code (sign in bit 3): the format's eight values
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_E2M1 = np.concatenate([_E2M1, -_E2M1])
+
+
+def _f8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def decode_page_rows(dtype, codes, scales):
+    """Rows of one page as stored by the GPU, decoded without the oracle (torch's
+    float8_e4m3fn and bfloat16 casts, the E2M1 value list; fp4: element 2c in
+    the low nibble, one E4M3 scale per 32 elements)."""
+    if dtype == "fp8":
+        return _f8(codes) * np.float64(scales)
+    if dtype == "bf16":
+        bits = np.ascontiguousarray(codes).view(np.int16)
+        return torch.from_numpy(bits).view(torch.bfloat16).to(torch.float64).numpy()
+    v = np.empty(codes.shape[:-1] + (2 * codes.shape[-1],))
+    v[..., 0::2] = _E2M1[codes & 0xF]
+    v[..., 1::2] = _E2M1[codes >> 4]
+    return v * np.repeat(_f8(scales), 32, axis=-1)
+
+
+def quantized_rows_close(dtype, codes, scales, ref_rows, tol=ENTRY_TOL):
+    """Stored page rows against fp64 reference rows.  The kernel quantizes its
+    own fp32 rows, which may differ from the reference by tol * (row's max|ref|),
+    so each element may be off by that plus half a code step at the stored
+    scale (fp8: the E4M3 step at its binade, subnormal below 2^-6; fp4: at
+    most one scale unit, the half step between 4 and 6 and the saturation of
+    a rounded block scale; bf16: 2^-8 relative).  An fp8 page scale must be
+    within 2 tol of amax/448 of the reference rows."""
+    ref = np.asarray(ref_rows, np.float64)
+    dec = decode_page_rows(dtype, codes, scales)
+    dev = tol * np.abs(ref).max(axis=-1, keepdims=True)
+    if dtype == "fp8":
+        s = float(scales)
+        amax = float(np.abs(ref).max())
+        if amax > 0 and abs(s - amax / 448.0) > 2 * tol * amax / 448.0:
+            return False
+        y = (np.abs(ref) + dev) / s
+        e = np.maximum(np.floor(np.log2(np.maximum(y, 2.0 ** -12))), -6)
+        half = 0.5 * 2.0 ** (e - 3) * s
+    elif dtype == "fp4":
+        half = np.repeat(_f8(scales), 32, axis=-1)
+    else:
+        half = (np.abs(ref) + dev) * 2.0 ** -8
+    return bool((np.abs(dec - ref) <= (dev + half) * (1 + 1e-9) + 1e-30).all())
+
+
 def bf16_to_f64(bits):
     return codecs.bf16_decode(bits)
 

@@ -96,12 +96,12 @@ def _cache(dtype=1, epp=64, dim=128, pages=4, codes=FAKE, scales=FAKE):
 def test_validation_kv_compress():
     L = hca.lib()
     ok = dict(x=FAKE, xs=4096 * 8, z=FAKE, zs=4096, beta=FAKE, pos0=FAKE, ntok=FAKE, B=2, mx=4096, d=128, m=4,
-              theta=1e6, out=FAKE, os=1024 * 128)
+              theta=1e6, gam=None, eps=1e-6, out=FAKE, os=1024 * 128)
 
     def call(**kw):
         a = dict(ok, **kw)
         return L.kv_compress(a["x"], a["xs"], a["z"], a["zs"], a["beta"], a["pos0"], a["ntok"], a["B"], a["mx"],
-                             a["d"], a["m"], a["theta"], a["out"], a["os"], None)
+                             a["d"], a["m"], a["theta"], a["gam"], a["eps"], a["out"], a["os"], None)
 
     assert call(m=3) == 1 and call(m=512) == 1 and call(m=0) == 1
     assert call(d=12) == 1 and call(d=4096) == 2
@@ -110,18 +110,22 @@ def test_validation_kv_compress():
     assert call(xs=100) == 1 and call(os=16) == 1
     assert call(B=-1) == 1
     assert call(B=0) == 0 and call(mx=0) == 0  # nothing to do, nothing launched
+    # normalisation: an aligned gain vector and a finite eps > 0
+    assert call(gam=FAKE, eps=0.0) == 1 and call(gam=FAKE, eps=float("inf")) == 1
+    assert call(gam=ctypes.c_void_p(0x1004)) == 1
+    assert call(gam=FAKE, B=0) == 0 and call(gam=None, eps=0.0, B=0) == 0
 
 
 def test_validation_kv_compress_insert():
     L = hca.lib()
-    ok = dict(x=FAKE, xs=4 * 128, z=FAKE, zs=4, beta=FAKE, pos0=FAKE, ntok=FAKE, B=2, m=4, theta=1e6, st=FAKE,
-              ss=64 * 128, e0=FAKE, bt=FAKE, bts=16, dst=_cache(), app=0)
+    ok = dict(x=FAKE, xs=4 * 128, z=FAKE, zs=4, beta=FAKE, pos0=FAKE, ntok=FAKE, B=2, m=4, theta=1e6, gam=None,
+              eps=1e-6, st=FAKE, ss=64 * 128, e0=FAKE, bt=FAKE, bts=16, dst=_cache(), app=0)
 
     def call(**kw):
         a = dict(ok, **kw)
         return L.kv_compress_insert(a["x"], a["xs"], a["z"], a["zs"], a["beta"], a["pos0"], a["ntok"], a["B"],
-                                    a["m"], a["theta"], a["st"], a["ss"], a["e0"], a["bt"], a["bts"], a["dst"],
-                                    a["app"], None)
+                                    a["m"], a["theta"], a["gam"], a["eps"], a["st"], a["ss"], a["e0"], a["bt"],
+                                    a["bts"], a["dst"], a["app"], None)
 
     assert call(m=3) == 1 and call(m=8) == 1  # the pool's epp must be 256 / m
     assert call(dst=_cache(dim=4096)) == 2
@@ -130,7 +134,8 @@ def test_validation_kv_compress_insert():
     assert call(x=None) == 1 and call(st=None) == 1 and call(e0=None) == 1 and call(bt=None) == 1
     assert call(xs=100) == 1 and call(ss=16) == 1 and call(zs=3) == 1
     assert call(B=-1) == 1
-    assert call(B=0) == 0  # nothing to do, nothing launched
+    assert call(gam=FAKE, eps=-1.0) == 1 and call(gam=ctypes.c_void_p(0x1008)) == 1
+    assert call(B=0) == 0 and call(gam=FAKE, B=0) == 0  # nothing to do, nothing launched
 
 
 def test_validation_kv_compress_insert_jobs():
@@ -138,11 +143,11 @@ def test_validation_kv_compress_insert_jobs():
 
     def job(**kw):
         a = dict(x=FAKE.value, xs=4 * 128, z=FAKE.value, zs=4, beta=FAKE.value, pos0=FAKE.value, ntok=FAKE.value,
-                 m=4, theta=1e6, st=FAKE.value, ss=64 * 128, e0=FAKE.value, bt=FAKE.value, bts=16, dst=_cache(),
-                 app=0)
+                 m=4, theta=1e6, gam=None, eps=1e-6, st=FAKE.value, ss=64 * 128, e0=FAKE.value, bt=FAKE.value,
+                 bts=16, dst=_cache(), app=0)
         a.update(kw)
         return hca.CInsertJob(a["x"], a["xs"], a["z"], a["zs"], a["beta"], a["pos0"], a["ntok"], a["m"], a["theta"],
-                              a["st"], a["ss"], a["e0"], a["bt"], a["bts"], a["dst"], a["app"])
+                              a["gam"], a["eps"], a["st"], a["ss"], a["e0"], a["bt"], a["bts"], a["dst"], a["app"])
 
     def call(jobs, B=2):
         arr = (hca.CInsertJob * max(len(jobs), 1))(*jobs)
@@ -155,6 +160,9 @@ def test_validation_kv_compress_insert_jobs():
     assert call([job()], B=-1) == 1
     assert call([job(), job(app=3)]) == 1
     assert call([], B=2) == 0 and call([job()], B=0) == 0  # nothing to do, nothing launched
+    assert call([job(), job(gam=FAKE.value, eps=0.0)]) == 1
+    # without a fold the norm arguments are not used
+    assert call([job(x=None, gam=FAKE.value, eps=0.0)], B=0) == 0
 
 
 def test_validation_quantize_and_gather():
@@ -203,11 +211,13 @@ def test_validation_indexer_and_attention():
     def att(**kw):
         a = dict(q=FAKE, H=64, kv=_cache(dtype=1, epp=64, dim=512), bt=FAKE, bts=16,
                  win=_cache(dtype=1, epp=256, dim=512), wbt=FAKE, wbts=16, lens=FAKE, B=2, L=4096, m=4, W=128,
-                 sel=FAKE, seln=FAKE, k=256, scale=0.04, theta=1e6, out=FAKE, lse=None, ws=FAKE, wsb=ws_att)
+                 sel=FAKE, seln=FAKE, k=256, scale=0.04, theta=1e6, out=FAKE, lse=None, o8=None, o8s=None, ws=FAKE,
+                 wsb=ws_att)
         a.update(kw)
         return L.paged_hybrid_decode(a["q"], a["H"], a["kv"], a["bt"], a["bts"], a["win"], a["wbt"], a["wbts"],
                                      a["lens"], a["B"], a["L"], a["m"], a["W"], a["sel"], a["seln"], a["k"],
-                                     a["scale"], a["theta"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+                                     a["scale"], a["theta"], a["out"], a["lse"], a["o8"], a["o8s"], a["ws"], a["wsb"],
+                                     None)
 
     assert att(H=129) == 2 and att(H=0) == 1
     assert att(kv=_cache(dtype=1, epp=64, dim=384)) == 2
@@ -218,4 +228,7 @@ def test_validation_indexer_and_attention():
     assert att(scale=float("inf")) == 1
     assert att(wsb=ws_att - 1) == 3
     assert att(m=5) == 1
+    # the fp8 output needs its scales and 2-byte alignment; one of the two outputs is required
+    assert att(out=None) == 1 and att(o8=FAKE) == 1 and att(out=None, o8=ctypes.c_void_p(0x1001), o8s=FAKE) == 1
+    assert att(out=None, o8=FAKE, o8s=FAKE, wsb=ws_att - 1) == 3  # valid outputs; only the workspace is short
     assert att(B=0) == 0

@@ -164,6 +164,33 @@ def test_compress_entries(m, d, groups0):
         assert H.rel_err_rows(got[b, : ref.shape[0]], ref) <= H.ENTRY_TOL, b
 
 
+# RMS-normalised entries: the row's sum of squares is reduced by an xor
+# butterfly inside a wave (d <= 512), across waves (d = 1024, 2048), through
+# LDS (d = 136: 17 threads a row), or over the block (m > 16)
+@pytest.mark.parametrize("m,d", [(4, 512), (1, 512), (128, 512), (4, 136), (2, 1024), (16, 2048), (256, 128),
+                                 (64, 136), (4, 64)])
+def test_compress_entries_normalised(m, d):
+    H.flush(f"compress normalised m={m} d={d}")
+    rng = np.random.default_rng(52)
+    T = [m * 37 + (m // 2 + 1 if m > 1 else 0), 3, m * 9, 1]
+    B, Tm = len(T), max(T)
+    x32 = rng.standard_normal((B, Tm, d)).astype(np.float32) * rng.uniform(0.01, 10.0, (B, Tm, 1)).astype(np.float32)
+    xb = gen.to_bf16_bits(x32)
+    z = rng.standard_normal((B, Tm)).astype(np.float32)
+    beta = (rng.standard_normal(m) * 0.1).astype(np.float32)
+    gam = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    pos0 = np.array([0, m * 1000, m * 262143, m * 5], np.int32)
+    ntok = np.array(T, np.int32)
+    out = torch.zeros((B, -(-Tm // m), d), dtype=torch.float32, device="cuda")
+    hca.kv_compress(H.to_dev(xb.view(np.int16)), H.to_dev(z), H.to_dev(beta), H.to_dev(pos0), H.to_dev(ntok), m, 1e6,
+                    out, Tm, norm_gamma=H.to_dev(gam), norm_eps=1e-6)
+    got = out.cpu().numpy()
+    for b in range(B):
+        ref = compressor.compress(codecs.bf16_decode(xb[b, : T[b]]), z[b, : T[b]], beta, m, 1e6, pos0=int(pos0[b]),
+                                  gamma=gam, eps=1e-6)
+        assert H.rel_err_rows(got[b, : ref.shape[0]], ref) <= H.ENTRY_TOL, b
+
+
 # ----------------------------------------------------------------- kv_compress_insert
 
 
@@ -173,15 +200,19 @@ def test_compress_entries(m, d, groups0):
 # page codes bit-exact for the GPU staging rows).  The runs cross a page start
 # (the new page's first row), grow an fp8 page scale with a large token, and
 # start one page from all-zero rows (scale 1.0, which append mode must not
-# trust).
-@pytest.mark.parametrize("m,dtype,d,append", [(1, "fp8", 512, True), (1, "fp8", 512, False), (4, "fp8", 512, False),
-                                               (4, "fp8", 512, True), (128, "fp8", 512, True),
-                                               (128, "fp8", 512, False), (2, "fp8", 136, False), (2, "fp8", 512, True),
-                                               (4, "fp4", 128, False), (1, "fp4", 128, True),
-                                               (4, "bf16", 128, False), (1, "bf16", 64, True)])
-def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append):
-    H.flush(f"compress_insert m={m} {dtype} d={d} append={append}")
+# trust).  With norm, every folded entry is RMS-normalised before its rotation.
+@pytest.mark.parametrize("m,dtype,d,append,norm", [
+    (1, "fp8", 512, True, False), (1, "fp8", 512, False, False), (4, "fp8", 512, False, False),
+    (4, "fp8", 512, True, False), (128, "fp8", 512, True, False), (128, "fp8", 512, False, False),
+    (2, "fp8", 136, False, False), (2, "fp8", 512, True, False), (4, "fp4", 128, False, False),
+    (1, "fp4", 128, True, False), (4, "bf16", 128, False, False), (1, "bf16", 64, True, False),
+    (4, "fp8", 512, True, True), (128, "fp8", 512, True, True), (1, "fp8", 512, True, True),
+    (2, "fp8", 136, False, True), (4, "fp4", 128, True, True)])
+def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append, norm):
+    H.flush(f"compress_insert m={m} {dtype} d={d} append={append} norm={norm}")
     rng = np.random.default_rng(61 + m)
+    gam = rng.uniform(0.5, 1.5, d).astype(np.float32) if norm else None
+    gam_d = H.to_dev(gam) if norm else None
     epp = 256 // m
     B, steps, theta = 3, 7, 1e6
     # lengths before the first step: seq 0 three tokens before a page start,
@@ -210,6 +241,7 @@ def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append):
             hca.kv_quantize_page(stage_f[b:b + 1], H.to_dev(e0), H.to_dev(np.array([row], np.int32)), epp,
                                  H.to_dev(table[b:b + 1]), pool_f)
     torch.cuda.synchronize()
+    ref_rows = hist.astype(np.float64)  # the open pages' rows as the oracle has them
     stage_u = stage_f.clone()
     pool_u = hca.PagedCache(pool_f.codes.clone(), None if pool_f.scales is None else pool_f.scales.clone(), epp, d,
                             dtype)
@@ -233,10 +265,10 @@ def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append):
         row = j - e0
         xd, zd = H.to_dev(xb.view(np.int16)), H.to_dev(ring_z)
         hca.kv_compress_insert(xd, zd, H.to_dev(beta), H.to_dev(pos0), H.to_dev(ntok), m, theta, stage_f,
-                               H.to_dev(e0), H.to_dev(table), pool_f, append=append)
+                               H.to_dev(e0), H.to_dev(table), pool_f, append=append, norm_gamma=gam_d)
         for b in range(B):  # the two-call path, one sequence at a time (rows differ)
             hca.kv_compress(xd[b:b + 1], zd[b:b + 1], H.to_dev(beta), H.to_dev(pos0[b:b + 1]),
-                            H.to_dev(ntok[b:b + 1]), m, theta, stage_u[b:b + 1, int(row[b]):], m)
+                            H.to_dev(ntok[b:b + 1]), m, theta, stage_u[b:b + 1, int(row[b]):], m, norm_gamma=gam_d)
             hca.kv_quantize_page(stage_u[b:b + 1], H.to_dev(e0[b:b + 1]), H.to_dev(row[b:b + 1] + 1), epp,
                                  H.to_dev(table[b:b + 1]), pool_u)
         torch.cuda.synchronize()
@@ -248,18 +280,19 @@ def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append):
             r = int(row[b])
             assert np.array_equal(sf[b, : r + 1].view(np.uint32), su[b, : r + 1].view(np.uint32)), (step, b)
             ent = compressor.compress(codecs.bf16_decode(xb[b, : ntok[b]]), ring_z[b, : ntok[b]], beta, m, theta,
-                                      pos0=int(pos0[b]))
+                                      pos0=int(pos0[b]), gamma=gam, eps=1e-6)
             assert H.rel_err_rows(sf[b, r : r + 1], ent[-1:]) <= H.ENTRY_TOL, (step, b)
+            if r == 0:
+                ref_rows[b] = 0.0  # a new page
+            ref_rows[b, r] = ent[-1]
             phys = int(table[b, e0[b] // epp])
             assert np.array_equal(got_f.codes[phys], got_u.codes[phys]), (step, b)
             if dtype != "bf16":
                 assert np.array_equal(got_f.scales[phys], got_u.scales[phys]), (step, b)
-            paging.write_run(ref_pool, table[b], int(e0[b]), sf[b, : r + 1])
-            assert np.array_equal(got_f.codes[phys, : r + 1], ref_pool.codes[phys, : r + 1]), (step, b)
-            if dtype == "fp8":
-                assert got_f.scales[phys] == ref_pool.scales[phys], (step, b)
-            elif dtype == "fp4":
-                assert np.array_equal(got_f.scales[phys, : r + 1], ref_pool.scales[phys, : r + 1]), (step, b)
+            # the stored page against the oracle's rows (its codes are bit-exact
+            # against the oracle's quantizer in the kv_quantize_page tests)
+            sc = got_f.scales[phys] if dtype == "fp8" else (got_f.scales[phys, : r + 1] if dtype == "fp4" else None)
+            assert H.quantized_rows_close(dtype, got_f.codes[phys, : r + 1], sc, ref_rows[b, : r + 1]), (step, b)
 
 
 def test_compress_insert_jobs_one_launch():
@@ -283,6 +316,7 @@ def test_compress_insert_jobs_one_launch():
     xc = gen.to_bf16_bits(rng.standard_normal((B, 4, d)).astype(np.float32))
     zc = rng.standard_normal((B, 4)).astype(np.float32)
     beta = (rng.standard_normal(4) * 0.1).astype(np.float32)
+    gam = H.to_dev(rng.uniform(0.5, 1.5, d).astype(np.float32))  # the entries are RMS-normalised
     stages = (rng.standard_normal((B, 256, d)).astype(np.float32), rng.standard_normal((B, 64, d)).astype(np.float32),
               rng.standard_normal((B, 64, di)).astype(np.float32))
     outs = []
@@ -299,14 +333,14 @@ def test_compress_insert_jobs_one_launch():
             jobs = [hca.insert_job(wst, args["pos_w"], args["e0_w"], args["wtab"], win, 1, x=xwd, gate_logit=zwd,
                                    pos_bias=args["zero1"], ntok=args["one"], rope_theta=theta),
                     hca.insert_job(cst, args["pos_c"], args["e0_c"], args["tab"], kv, 4, x=xcd, gate_logit=zcd,
-                                   pos_bias=args["beta"], ntok=args["ntok_c"], rope_theta=theta),
+                                   pos_bias=args["beta"], ntok=args["ntok_c"], rope_theta=theta, norm_gamma=gam),
                     hca.insert_job(ist, args["pos_c"], args["e0_c"], args["tab"], idx, 4)]
             hca.kv_compress_insert_jobs(jobs, B)
         else:
             hca.kv_compress_insert(xwd, zwd, args["zero1"], args["pos_w"], args["one"], 1, theta, wst, args["e0_w"],
                                    args["wtab"], win)
             hca.kv_compress_insert(xcd, zcd, args["beta"], args["pos_c"], args["ntok_c"], 4, theta, cst, args["e0_c"],
-                                   args["tab"], kv)
+                                   args["tab"], kv, norm_gamma=gam)
             rows = H.to_dev(((pos_c // 4) - e0_c + 1).astype(np.int32))
             hca.kv_quantize_page(ist, args["e0_c"], rows, 64, args["tab"], idx)
         torch.cuda.synchronize()
@@ -373,7 +407,9 @@ def _attn_workload(kv_dtype, d, Hh, window, kind, B=3):
     return synth.Workload(101, "attn", B, None, d, Hh, window, kv_dtype, [kind])
 
 
-def _run_attn(sd, sel_list, window, ws=None, table=None, wtable=None, kv=None, win=None):
+def _run_attn(sd, sel_list, window, ws=None, table=None, wtable=None, kv=None, win=None, fp8=None):
+    """fp8: None (fp32 output only), "both" (fp32 and fp8 outputs) or "only"
+    (fp8 output alone); with fp8 the fp8 codes and scales are returned too."""
     B, d, Hh = sd.B, sd.w.d, sd.w.H
     Lmax = H.max_len(sd.lens)
     m = sd.kind.m
@@ -388,14 +424,17 @@ def _run_attn(sd, sel_list, window, ws=None, table=None, wtable=None, kv=None, w
         k, sel_d, seln_d = 0, None, None
     if ws is None:
         ws = hca.workspace(hca.paged_hybrid_decode_workspace(B, Hh, d, Lmax, m, window, k))
-    out = torch.zeros((B, Hh, d), dtype=torch.float32, device="cuda")
+    out = torch.zeros((B, Hh, d), dtype=torch.float32, device="cuda") if fp8 != "only" else None
     lse = torch.zeros((B, Hh), dtype=torch.float32, device="cuda")
+    o8 = torch.full((B, Hh, d), 0x55, dtype=torch.uint8, device="cuda") if fp8 else None
+    o8s = torch.full((B, Hh), -1.0, dtype=torch.float32, device="cuda") if fp8 else None
     hca.paged_hybrid_decode(H.to_dev(sd.q.view(np.int16)), kv or H.upload_pool(sd.kv),
                             H.to_dev(sd.table if table is None else table), win or H.upload_pool(sd.win),
                             H.to_dev(sd.wtable if wtable is None else wtable), H.to_dev(sd.lens), Lmax, m, window,
-                            sel_d, seln_d, H.scale_for(d), sd.w.theta, out, lse, ws)
+                            sel_d, seln_d, H.scale_for(d), sd.w.theta, out, lse, ws, out_fp8=o8, out_scale=o8s)
     torch.cuda.synchronize()
-    return out.cpu().numpy(), lse.cpu().numpy()
+    res = (None if out is None else out.cpu().numpy(), lse.cpu().numpy())
+    return res + ((o8.cpu().numpy(), o8s.cpu().numpy()) if fp8 else ())
 
 
 @pytest.mark.parametrize("case", [
@@ -417,7 +456,7 @@ def test_paged_hybrid_decode(case):
         sel = [sd.oracle_select(b) for b in range(sd.B)]
     else:
         sel = None
-    out, lse = _run_attn(sd, sel, case["W"])
+    out, lse, o8, o8s = _run_attn(sd, sel, case["W"], fp8="both")
     for b in range(sd.B):
         s = sel[b] if sel is not None else np.arange(int(compressor.n_entries(int(sd.lens[b]), case["m"])))
         ref_out, ref_lse, p = sd.oracle_attend(b, s)
@@ -425,6 +464,32 @@ def test_paged_hybrid_decode(case):
         err = H.rel_err_rows(out[b], ref_out)
         assert err <= H.ATTN_TOL, (b, err)
         assert np.allclose(lse[b], ref_lse, rtol=0, atol=2e-3), b
+        # the fused fp8 form of the output (inverse RoPE, then per-row E4M3)
+        for h in range(case["H"]):
+            assert H.quantized_rows_close("fp8", o8[b, h], o8s[b, h], ref_out[h], tol=H.ATTN_TOL), (b, h)
+        _check_fp8_rows_of(out[b], o8[b], o8s[b])
+    # the fp8 output alone: the same bytes
+    _, lse2, o8b, o8sb = _run_attn(sd, sel, case["W"], fp8="only")
+    assert np.array_equal(o8b, o8) and np.array_equal(o8sb.view(np.uint32), o8s.view(np.uint32))
+    assert np.array_equal(lse2.view(np.uint32), lse.view(np.uint32))
+
+
+def _check_fp8_rows_of(out32, codes, scales):
+    """The fp8 rows against the same call's fp32 rows: scale = fl32(amax/448)
+    (1 for a zero row), the largest element at code 0x7E, every element within
+    half an E4M3 step (decoded by torch's float8_e4m3fn cast)."""
+    amax = np.abs(out32).max(axis=-1).astype(np.float32)
+    want = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    assert np.array_equal(scales.view(np.uint32), want.view(np.uint32))
+    dec = H.decode_page_rows("fp8", codes, 1.0)
+    y = np.abs(out32.astype(np.float64)) / scales[:, None]
+    e = np.maximum(np.floor(np.log2(np.maximum(y, 2.0 ** -12))), -6)
+    assert (np.abs(dec - out32 / scales[:, None]) <= 0.5 * 2.0 ** (e - 3) * (1 + 1e-6)).all()
+    for h in range(out32.shape[0]):
+        if amax[h] > 0:
+            assert ((codes[h][np.abs(out32[h]) == amax[h]] & 0x7F) == 0x7E).all()
+        else:
+            assert (codes[h] == 0).all()
 
 
 def test_attention_layout_invariance_bitwise():
@@ -473,10 +538,12 @@ def test_attention_skips_invalid_indices_and_empty_sequences():
     sd = H.SeqData(w, 0, [1000, 1])
     good = np.arange(0, 250, 5)
     sel = [np.concatenate([good, [-3, 250, 10 ** 6]]), np.zeros(0, np.int64)]
-    out, lse = _run_attn(sd, sel, 0)
+    out, lse, o8, o8s = _run_attn(sd, sel, 0, fp8="both")
     ref_out, ref_lse, _ = sd.oracle_attend(0, good)
     assert H.rel_err_rows(out[0], ref_out) <= H.ATTN_TOL
     assert not out[1].any() and np.all(np.isneginf(lse[1]))
+    # a sequence with no rows: zero codes and scale 1 in the fp8 output
+    assert not o8[1].any() and (o8s[1] == 1.0).all()
 
 
 # ----------------------------------------------------------------- kv_gather
