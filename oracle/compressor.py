@@ -20,6 +20,15 @@ Readings adopted:
 * with a gain gamma, the entry is RMS-normalised before it is rotated
   ([V4-vLLM] 3.2.1: compressor, then RMSNorm, then RoPE, then insertion); a
   partial group's entry is normalised as it stands.
+
+Overlapping windows ([V4-vLLM] 2.1 describes c4a as folding every 8 tokens
+into one entry at a ratio of 1/4; 3.1.2 gives c4a an 8-token compressor
+state): with an overlap o, entry j folds the o + m tokens of positions
+[jm - o, jm + m), its own group and the last o tokens of the group before; one
+softmax runs over the window's slots i = 0 .. o+m-1 (slot bias beta_i, slot 0
+the oldest token); slots at positions below 0 or at or past the context's end
+are absent.  The entry count stays ceil(L/m) and the entry is still rotated at
+jm.  c4a's window is o = m = 4.
 """
 
 import numpy as np
@@ -89,3 +98,39 @@ def window_rows(x_block, first_pos, theta, gamma=None, eps=1e-6):
         x_block = rms_norm(x_block, gamma, eps)
     pos = first_pos + np.arange(x_block.shape[0], dtype=np.float64)
     return rope(x_block, pos, theta)
+
+
+def compress_overlap(x, z, beta, m, o, theta, pos0=0, x_prev=None, z_prev=None, gamma=None, eps=1e-6):
+    """Entries of a run of tokens with overlapping windows of o + m tokens.
+
+    x: [T, d], z: [T] for positions pos0 .. pos0+T-1 (pos0 a multiple of m);
+    x_prev: [o, d], z_prev: [o] the o tokens before pos0 (ignored, and may be
+    None, where pos0 = 0: those positions do not exist); beta: [o + m].
+    Entry j (j < ceil(T/m)) folds the valid slots of positions
+    [pos0 + jm - o, pos0 + jm + m); returns e [ceil(T/m), d] fp64, entry j
+    rotated at pos0 + jm.  Written entry by entry from the definition."""
+    x = np.asarray(x, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    T, d = x.shape
+    assert pos0 % m == 0 and beta.shape[0] == o + m
+    if o > 0 and pos0 > 0:
+        xr = np.concatenate([np.asarray(x_prev, dtype=np.float64).reshape(o, d), x])
+        zr = np.concatenate([np.asarray(z_prev, dtype=np.float64).reshape(o), z])
+    else:  # rows of the (absent) positions before 0 are never read
+        xr = np.concatenate([np.zeros((o, d)), x])
+        zr = np.concatenate([np.zeros(o), z])
+    N = int(n_entries(T, m))
+    out = np.empty((N, d), dtype=np.float64)
+    for j in range(N):
+        pos = pos0 + j * m - o + np.arange(o + m)  # the window's positions
+        valid = (pos >= 0) & (pos < pos0 + T)
+        rows = j * m + np.arange(o + m)  # their rows in xr / zr
+        a = np.where(valid, zr[np.minimum(rows, o + T - 1)] + beta, -np.inf)
+        w = np.exp(a - a.max())
+        w = w / w.sum()
+        c = w[valid] @ xr[rows[valid]]
+        if gamma is not None:
+            c = rms_norm(c, gamma, eps)
+        out[j] = rope(c, pos0 + j * m, theta)
+    return out

@@ -33,6 +33,7 @@ class LayerSpec:
     scale: Optional[float] = None  # default 1/sqrt(d)
     gamma: Optional[np.ndarray] = None  # RMSNorm gain of the entries ([V4-vLLM] 3.2.1), None: no norm
     eps: float = 1e-6
+    overlap: int = 0  # tokens of the previous group in each entry's window (4 for c4a's 8-token window)
 
     @property
     def epp(self):
@@ -56,7 +57,11 @@ def window_blocks(L: int, window: int):
 def fill_entries(spec: LayerSpec, pool, table_row, x, z, beta):
     """Compress a whole context and quantize all of its entry pages.  Returns the
     fp64 entries (before quantization)."""
-    e = compressor.compress(x, z, beta, spec.m, spec.theta, gamma=spec.gamma, eps=spec.eps)
+    if spec.overlap > 0:
+        e = compressor.compress_overlap(x, z, beta, spec.m, spec.overlap, spec.theta, gamma=spec.gamma,
+                                        eps=spec.eps)
+    else:
+        e = compressor.compress(x, z, beta, spec.m, spec.theta, gamma=spec.gamma, eps=spec.eps)
     paging.write_run(pool, table_row, 0, e.astype(np.float32))
     return e
 

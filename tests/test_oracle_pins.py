@@ -491,3 +491,67 @@ def test_out_fp8_bound_and_saturation():
         y = np.abs(o32[h]) / s[h]
         e = np.maximum(np.floor(np.log2(np.maximum(y, 1e-30))), -6)
         assert (np.abs(dec[h] - o32[h]) <= 0.5 * 2.0 ** (e - 3) * s[h] * (1 + 1e-6) + 1e-300).all()
+
+
+# ----------------------------------------------------------------- overlapping windows
+
+
+def test_overlap_zero_is_the_plain_compressor():
+    # two implementations of one definition: the group-at-a-time fold and the
+    # entry-by-entry window fold with no overlap
+    g = np.random.default_rng(41)
+    for m, T in ((4, 37), (1, 9), (16, 100)):
+        x, z, beta = g.normal(size=(T, 8)), g.normal(size=T), g.normal(0, 0.1, m)
+        a = compressor.compress(x, z, beta, m, 1e4, gamma=np.linspace(0.5, 1.5, 8))
+        b = compressor.compress_overlap(x, z, beta, m, 0, 1e4, gamma=np.linspace(0.5, 1.5, 8))
+        assert np.allclose(a, b, atol=1e-13)
+
+
+def test_overlap_windows_by_pooling_slot_bias_and_dominant_token():
+    g = np.random.default_rng(42)
+    T = 37
+    x = g.normal(size=(T, 8))
+    # uniform weights: entry j is the mean of positions [4j-4, 4j+4) within [0, T)
+    e = compressor.compress_overlap(x, np.zeros(T), np.zeros(8), 4, 4, None)
+    assert e.shape == (10, 8)
+    assert np.allclose(e[0], x[0:4].mean(axis=0), atol=1e-14)
+    for j in range(1, 9):
+        assert np.allclose(e[j], x[4 * j - 4: 4 * j + 4].mean(axis=0), atol=1e-14)
+    assert np.allclose(e[9], x[32:37].mean(axis=0), atol=1e-14)  # partial: 32..36
+    # slot 0 (the oldest token of the window) dominant: entry j >= 1 is x[4j-4];
+    # entry 0's slots 0..3 lie before position 0, so it falls back to its own group
+    beta = np.zeros(8)
+    beta[0] = 1e4
+    e = compressor.compress_overlap(x, np.zeros(T), beta, 4, 4, None)
+    assert np.allclose(e[0], x[0:4].mean(axis=0), atol=1e-14)
+    for j in range(1, 10):
+        assert np.allclose(e[j], x[4 * j - 4], atol=1e-12)
+    # a dominant token at t is the whole of the two entries whose windows hold it
+    z = g.normal(size=T)
+    z[13] = 1e4
+    e = compressor.compress_overlap(x, z, g.normal(0, 0.1, 8), 4, 4, None)
+    hit = [j for j in range(10) if np.allclose(e[j], x[13], atol=1e-12)]
+    assert hit == [3, 4]
+
+
+def test_overlap_runs_split_anywhere_and_decode_refold():
+    # a run that starts at pos0 > 0 with the o tokens before it equals the same
+    # entries of one run from 0; re-folding the open group every step from the
+    # last o + m tokens gives the one-shot entries (the 8-token compressor state)
+    g = np.random.default_rng(43)
+    T, d = 203, 16
+    x, z, beta = g.normal(size=(T, d)), g.normal(size=T), g.normal(0, 0.1, 8)
+    gam = g.uniform(0.5, 1.5, d)
+    full = compressor.compress_overlap(x, z, beta, 4, 4, 1e6, gamma=gam)
+    for p0 in (4, 64, 200):
+        part = compressor.compress_overlap(x[p0:], z[p0:], beta, 4, 4, 1e6, pos0=p0, x_prev=x[p0 - 4: p0],
+                                           z_prev=z[p0 - 4: p0], gamma=gam)
+        assert np.allclose(part, full[p0 // 4:], atol=1e-12)
+    for L in range(1, T + 1):
+        j = (L - 1) // 4
+        p0 = 4 * j
+        open_e = compressor.compress_overlap(x[p0:L], z[p0:L], beta, 4, 4, 1e6, pos0=p0,
+                                             x_prev=x[max(0, p0 - 4): p0], z_prev=z[max(0, p0 - 4): p0], gamma=gam)
+        ref = compressor.compress_overlap(x[:L], z[:L], beta, 4, 4, 1e6, gamma=gam)
+        assert np.allclose(open_e[0], ref[j], atol=1e-12)
+    assert compressor.compress_overlap(x[:1], z[:1], beta, 4, 4, None).shape == (1, d)
