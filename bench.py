@@ -11,8 +11,8 @@ K=V dim 512 in fp8 E4M3 pages with a per-page fp32 scale, 64 query heads, a
 and reported on its own.
 
 A step is one decode step of the whole stack for the batch: per layer the
-decode update (re-fold of the open group with its RMSNorm and RoPE and its
-page, the window insert of the new token and its page, the open indexer page:
+decode update (re-fold of the open group's window -- 8 tokens at stride 4 for
+c4a, the 128-token group for c128a -- with its RMSNorm and RoPE, and its page, the window insert of the new token and its page, the open indexer page:
 one kv_compress_insert_jobs launch), then indexer_topk (c4a) and
 paged_hybrid_decode, whose output is delivered as fp8 rows with a per-row
 scale; layers stay in order.  The step is captured once in a HIP graph and replayed; `value` is
@@ -116,8 +116,8 @@ def score_bytes(kind, B, L, d_idx=128, h_idx=16):
 def update_bytes(kind, B, d, d_idx=128):
     """Bytes moved by the decode update of one layer while page scales hold
     (open group, open page, window page, open indexer page)."""
-    m, epp = kind.m, 256 // kind.m
-    b = m * d * 2 + m * 4 + d * 4  # ring tokens + logits, entry write
+    m, epp, s = kind.m, 256 // kind.m, kind.slots
+    b = s * d * 2 + s * 4 + d * 4  # the window's ring tokens + logits, entry write
     b += (epp - 1) * d * 4 + d + 8  # open page: earlier staging rows (its amax), the row's codes, scale
     b += d * 2 + 4 + d * 4 + d + 8  # window token + logit, its staging row, its codes, scale
     if kind.topk is not None:
@@ -155,26 +155,30 @@ def build_state(w, n_layers, torch, hca, gen, log):
         for b in range(B):
             x[b] = gen.device_normal((L, d), 1.0, (0, w.cid, li, gen.S_TOK, b), dtype=torch.bfloat16)
         z = gen.device_normal((B, L), 1.0, (0, w.cid, li, gen.S_LOGIT))
-        beta = dev(gen.slot_bias(w, li, m))
+        o = kind.overlap
+        beta = dev(gen.slot_bias(w, li, kind.slots))
         lay.gamma = dev(gen.norm_gain(w, li, d))
         ent = torch.empty((B, N, d), dtype=torch.float32, device="cuda")
         lay.kv = hca.PagedCache.empty(P, epp, d, w.kv_dtype)
         xi = x.view(torch.int16)
         torch.cuda.synchronize()
         ev0.record()
-        hca.kv_compress(xi, z, beta, zeros_b, lens, m, w.theta, ent, L, norm_gamma=lay.gamma)
+        hca.kv_compress(xi, z, beta, zeros_b, lens, m, w.theta, ent, L, norm_gamma=lay.gamma, overlap=o)
         hca.kv_quantize_page(ent, zeros_b, dev(np.full(B, N, np.int32)), N, table, lay.kv)
         ev1.record()
         torch.cuda.synchronize()
         pre_ms += ev0.elapsed_time(ev1)
         pre_bytes += B * (L * d * 2 + L * 4 + 2 * N * d * 4 + N * d + 4 * (-(-N // epp)))
-        # decode-update state: open group ring, open page staging
+        # decode-update state: the ring of the open group's window (the overlap's
+        # tokens of the group before, then the open group), open page staging
         g_open = (L - 1) // m
         nt_open = L - g_open * m
-        lay.ring_x = torch.zeros((B, m, d), dtype=torch.int16, device="cuda")
-        lay.ring_x[:, :nt_open] = xi[:, g_open * m: L]
-        lay.ring_z = torch.zeros((B, m), dtype=torch.float32, device="cuda")
-        lay.ring_z[:, :nt_open] = z[:, g_open * m: L]
+        p_lo = max(0, g_open * m - o)
+        lay.ring_x = torch.zeros((B, o + m, d), dtype=torch.int16, device="cuda")
+        lay.ring_x[:, o - (g_open * m - p_lo): o + nt_open] = xi[:, p_lo: L]
+        lay.ring_z = torch.zeros((B, o + m), dtype=torch.float32, device="cuda")
+        lay.ring_z[:, o - (g_open * m - p_lo): o + nt_open] = z[:, p_lo: L]
+        lay.x_open, lay.z_open = lay.ring_x[:, o:], lay.ring_z[:, o:]  # rows -o .. -1: the overlap
         lay.beta = beta
         e_open0 = (g_open // epp) * epp
         lay.stage = torch.zeros((B, epp, d), dtype=torch.float32, device="cuda")
@@ -246,9 +250,9 @@ def decode_step(w, layers, shared, ws_idx, ws_att, hca, update=True, attend=True
             jobs = [hca.insert_job(lay.wstage, lay.wpos0, lay.we0, wtable, lay.win, 1, x=lay.x_last,
                                    gate_logit=lay.z_last, pos_bias=lay.zero1, ntok=lay.one, rope_theta=w.theta,
                                    append=True),
-                    hca.insert_job(lay.stage, lay.pos0, lay.e0, table, lay.kv, m, x=lay.ring_x, gate_logit=lay.ring_z,
+                    hca.insert_job(lay.stage, lay.pos0, lay.e0, table, lay.kv, m, x=lay.x_open, gate_logit=lay.z_open,
                                    pos_bias=lay.beta, ntok=lay.ntok, rope_theta=w.theta, append=True,
-                                   norm_gamma=lay.gamma)]
+                                   norm_gamma=lay.gamma, overlap=kind.overlap)]
             if kind.topk is not None:
                 jobs.append(hca.insert_job(lay.istage, lay.pos0, lay.e0, table, lay.idx, m, append=True))
             hca.kv_compress_insert_jobs(jobs, w.B)

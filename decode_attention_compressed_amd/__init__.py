@@ -51,7 +51,8 @@ class CPagedCache(ctypes.Structure):
 class CInsertJob(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("x_stride_b", ctypes.c_int64), ("gate_logit", ctypes.c_void_p),
                 ("z_stride_b", ctypes.c_int64), ("pos_bias", ctypes.c_void_p), ("pos0", ctypes.c_void_p),
-                ("ntok", ctypes.c_void_p), ("m", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("ntok", ctypes.c_void_p), ("m", ctypes.c_int32), ("overlap", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float),
                 ("norm_gamma", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("stage", ctypes.c_void_p), ("stage_stride_b", ctypes.c_int64), ("e0", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("bt_stride", ctypes.c_int32), ("dst", CPagedCache),
                 ("append", ctypes.c_int32)]
@@ -72,10 +73,10 @@ def lib() -> ctypes.CDLL:
         L.hca_status_string.restype = ctypes.c_char_p
         L.hca_status_string.argtypes = [ctypes.c_int]
         L.hca_version.restype = ctypes.c_char_p
-        L.kv_compress.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _F32, _P, _I64,
-                                  _P]
-        L.kv_compress_insert.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _F32, _P, _F32, _P, _I64, _P,
-                                         _P, _I32, CPagedCache, _I32, _P]
+        L.kv_compress.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F32, _P, _F32, _P,
+                                  _I64, _P]
+        L.kv_compress_insert.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _F32, _P, _F32, _P, _I64,
+                                         _P, _P, _I32, CPagedCache, _I32, _P]
         L.kv_compress_insert_jobs.argtypes = [ctypes.POINTER(CInsertJob), _I32, _I32, _P]
         L.kv_quantize_page_workspace.argtypes = [_I32, _I32, CPagedCache]
         L.kv_quantize_page_workspace.restype = _SZ
@@ -158,24 +159,27 @@ def version() -> str:
 
 
 def kv_compress(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, out, max_ntok: int, stream=None,
-                norm_gamma=None, norm_eps: float = 1e-6):
-    """x: bf16 [B, T, d] (or int16 bit patterns); gate_logit f32 [B, T]; pos_bias f32 [m];
-    pos0, ntok int32 [B]; out f32 [B, ceil(T/m), d]; norm_gamma f32 [d] or None."""
+                norm_gamma=None, norm_eps: float = 1e-6, overlap: int = 0):
+    """x: bf16 [B, T, d] (or int16 bit patterns); gate_logit f32 [B, T]; pos_bias f32 [m + overlap];
+    pos0, ntok int32 [B]; out f32 [B, ceil(T/m), d]; norm_gamma f32 [d] or None.  With an
+    overlap, x and gate_logit are views whose rows -overlap .. -1 hold the tokens before pos0."""
     B, T, d = x.shape
     _check(lib().kv_compress(_ptr(x), x.stride(0), _ptr(gate_logit), gate_logit.stride(0), _ptr(pos_bias),
-                             _ptr(pos0), _ptr(ntok), B, max_ntok, d, m, rope_theta, _ptr(norm_gamma), norm_eps,
-                             _ptr(out), out.stride(0), _stream(stream)), "kv_compress")
+                             _ptr(pos0), _ptr(ntok), B, max_ntok, d, m, overlap, rope_theta, _ptr(norm_gamma),
+                             norm_eps, _ptr(out), out.stride(0), _stream(stream)), "kv_compress")
 
 
 def kv_compress_insert(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, stage, e0, block_table,
-                       dst: PagedCache, append: bool = False, stream=None, norm_gamma=None, norm_eps: float = 1e-6):
+                       dst: PagedCache, append: bool = False, stream=None, norm_gamma=None, norm_eps: float = 1e-6,
+                       overlap: int = 0):
     """Decode-step update of one pool in one launch: x bf16 [B, m, d] (the open
     group's tokens); gate_logit f32 [B, m]; pos_bias f32 [m]; pos0, ntok, e0
     int32 [B]; stage f32 [B, epp, d] (the open page's staging); block_table
-    int32 [B, nb]; norm_gamma f32 [d] or None."""
+    int32 [B, nb]; norm_gamma f32 [d] or None; with an overlap, x and gate_logit
+    point at row `overlap` of rings of overlap + m rows."""
     B = x.shape[0]
     _check(lib().kv_compress_insert(_ptr(x), x.stride(0), _ptr(gate_logit), gate_logit.stride(0), _ptr(pos_bias),
-                                    _ptr(pos0), _ptr(ntok), B, m, rope_theta, _ptr(norm_gamma), norm_eps,
+                                    _ptr(pos0), _ptr(ntok), B, m, overlap, rope_theta, _ptr(norm_gamma), norm_eps,
                                     _ptr(stage), stage.stride(0), _ptr(e0), _ptr(block_table),
                                     block_table.stride(0), dst.c(), 1 if append else 0, _stream(stream)),
            "kv_compress_insert")
@@ -183,12 +187,12 @@ def kv_compress_insert(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: 
 
 def insert_job(stage, pos0, e0, block_table, dst: PagedCache, m: int, x=None, gate_logit=None, pos_bias=None,
                ntok=None, rope_theta: float = 0.0, append: bool = False, norm_gamma=None,
-               norm_eps: float = 1e-6) -> "CInsertJob":
+               norm_eps: float = 1e-6, overlap: int = 0) -> "CInsertJob":
     """One job of kv_compress_insert_jobs (x None: the open row is already in stage).
     The tensors must stay alive until the call that takes the job is enqueued."""
     return CInsertJob(_ptr(x), 0 if x is None else x.stride(0), _ptr(gate_logit),
                       0 if gate_logit is None else gate_logit.stride(0), _ptr(pos_bias), _ptr(pos0), _ptr(ntok), m,
-                      rope_theta, _ptr(norm_gamma), norm_eps, _ptr(stage), stage.stride(0), _ptr(e0),
+                      overlap, rope_theta, _ptr(norm_gamma), norm_eps, _ptr(stage), stage.stride(0), _ptr(e0),
                       _ptr(block_table), block_table.stride(0), dst.c(), 1 if append else 0)
 
 

@@ -14,6 +14,12 @@ namespace {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 bool valid_m(int m) { return m >= 1 && m <= 256 && (256 % m) == 0; }
+// overlapping windows: 0 <= overlap <= m, and only for groups the small-group fold takes
+hca_status overlap_ok(int m, int overlap) {
+  if (overlap < 0 || overlap > m) return HCA_ERR_INVALID;
+  if (overlap > 0 && m > kSmallM) return HCA_ERR_UNSUPPORTED;
+  return HCA_OK;
+}
 // RMS normalisation arguments: none, or a 16-byte aligned gain vector with a finite eps > 0
 bool norm_ok(const float* gamma, float eps) {
   return gamma == nullptr || (aligned(gamma, 16) && eps > 0.0f && isfinite(eps));
@@ -51,11 +57,13 @@ const char* hca_version(void) { return "hca 0.1.0 gfx950"; }
 
 hca_status kv_compress(const uint16_t* x, int64_t x_stride_b, const float* gate_logit, int64_t z_stride_b,
                        const float* pos_bias, const int32_t* pos0, const int32_t* ntok, int32_t B, int32_t max_ntok,
-                       int32_t d, int32_t m, float rope_theta, const float* norm_gamma, float norm_eps, float* out,
-                       int64_t out_stride_b, void* stream) {
+                       int32_t d, int32_t m, int32_t overlap, float rope_theta, const float* norm_gamma,
+                       float norm_eps, float* out, int64_t out_stride_b, void* stream) {
   if (B < 0 || max_ntok < 0) return HCA_ERR_INVALID;
   if (!valid_m(m) || d < 8 || (d % 8) != 0) return HCA_ERR_INVALID;
   if (d > 2048) return HCA_ERR_UNSUPPORTED;
+  const hca_status ov = overlap_ok(m, overlap);
+  if (ov != HCA_OK) return ov;
   if (!(rope_theta > 0.0f) || !isfinite(rope_theta)) return HCA_ERR_INVALID;
   if (!norm_ok(norm_gamma, norm_eps)) return HCA_ERR_INVALID;
   if (B == 0 || max_ntok == 0) return HCA_OK;
@@ -65,8 +73,8 @@ hca_status kv_compress(const uint16_t* x, int64_t x_stride_b, const float* gate_
   if (x_stride_b % 8 != 0 || out_stride_b % 4 != 0) return HCA_ERR_INVALID;
   if (B > 1 && (x_stride_b < (int64_t)max_ntok * d || z_stride_b < max_ntok || out_stride_b < n_out * d))
     return HCA_ERR_INVALID;
-  CompressArgs a{x, x_stride_b, gate_logit, z_stride_b, pos_bias, pos0, ntok, B, max_ntok, d, m, rope_theta,
-                 norm_gamma, norm_eps, out, out_stride_b};
+  CompressArgs a{x, x_stride_b, gate_logit, z_stride_b, pos_bias, pos0, ntok, B, max_ntok, d, m, overlap,
+                 rope_theta, norm_gamma, norm_eps, out, out_stride_b};
   return from_hip(launch_compress(a, (hipStream_t)stream));
 }
 
@@ -82,6 +90,7 @@ hca_status make_insert(const hca_insert_job& j, int32_t B, InsertArgs& out) {
   const bool fold = j.x != nullptr;
   if (fold && (!(j.rope_theta > 0.0f) || !isfinite(j.rope_theta))) return HCA_ERR_INVALID;
   if (fold && !norm_ok(j.norm_gamma, j.norm_eps)) return HCA_ERR_INVALID;
+  if (fold && overlap_ok(j.m, j.overlap) != HCA_OK) return overlap_ok(j.m, j.overlap);
   if (!j.pos0 || !j.stage || !j.e0 || !j.block_table) return HCA_ERR_INVALID;
   if (fold && (!j.gate_logit || !j.pos_bias || !j.ntok || !aligned(j.x, 16) || j.x_stride_b % 8 != 0))
     return HCA_ERR_INVALID;
@@ -89,7 +98,7 @@ hca_status make_insert(const hca_insert_job& j, int32_t B, InsertArgs& out) {
   if (B > 1 && j.stage_stride_b < (int64_t)j.dst.epp * d) return HCA_ERR_INVALID;
   if (fold && B > 1 && (j.x_stride_b < (int64_t)j.m * d || j.z_stride_b < j.m)) return HCA_ERR_INVALID;
   out = InsertArgs{CompressArgs{j.x, j.x_stride_b, j.gate_logit, j.z_stride_b, j.pos_bias, j.pos0, j.ntok, B, j.m, d,
-                                j.m, j.rope_theta, j.norm_gamma, j.norm_eps, nullptr, 0},
+                                j.m, fold ? j.overlap : 0, j.rope_theta, j.norm_gamma, j.norm_eps, nullptr, 0},
                    j.stage, j.stage_stride_b, j.e0, j.block_table, j.bt_stride, j.dst, j.append};
   return HCA_OK;
 }
@@ -99,13 +108,15 @@ extern "C" {
 
 hca_status kv_compress_insert(const uint16_t* x, int64_t x_stride_b, const float* gate_logit, int64_t z_stride_b,
                               const float* pos_bias, const int32_t* pos0, const int32_t* ntok, int32_t B, int32_t m,
-                              float rope_theta, const float* norm_gamma, float norm_eps, float* stage,
+                              int32_t overlap, float rope_theta, const float* norm_gamma, float norm_eps, float* stage,
                               int64_t stage_stride_b, const int32_t* e0, const int32_t* block_table, int32_t bt_stride,
                               hca_paged_cache dst, int32_t append, void* stream) {
   if (B < 0) return HCA_ERR_INVALID;
   if (!x) return HCA_ERR_INVALID;  // this entry point always folds
-  const hca_insert_job j{x, x_stride_b, gate_logit, z_stride_b, pos_bias, pos0, ntok, m, rope_theta, norm_gamma,
-                         norm_eps, stage, stage_stride_b, e0, block_table, bt_stride, dst, append};
+  const hca_insert_job j{x,        x_stride_b,     gate_logit, z_stride_b,  pos_bias,  pos0,
+                         ntok,     m,              overlap,    rope_theta,  norm_gamma, norm_eps,
+                         stage,    stage_stride_b, e0,         block_table, bt_stride, dst,
+                         append};
   InsertJobs jobs{};
   const hca_status st = make_insert(j, B, jobs.job[0]);
   if (st != HCA_OK || B == 0) return st;

@@ -3,6 +3,11 @@
 // (V4 page, section 2.1 compressor; section 3.1.2 rolling residual;
 // section 3.2.1 RoPE before cache insertion).
 //
+// Overlapping windows (section 2.1 folds every 8 tokens into one c4a entry at
+// a ratio of 1/4; section 3.1.2 keeps an 8-token state): with an overlap o,
+// entry j also folds the o tokens before its group, read at negative rows
+// relative to the run's first token (small groups only).
+//
 // HBM-bound stream: each thread owns 8 consecutive dims (one 16-byte bf16
 // load per token) so a row of d dims is read by d/8 adjacent lanes in one
 // coalesced sweep.  Small m: a row-group of d/8 threads folds whole entries on
@@ -50,18 +55,21 @@ __device__ __forceinline__ void rope_store8(float* dst, float* lds, const float 
 }
 
 // Entry j of a small-m fold, the 8 dims of this thread: softmax over the
-// group's available slots, weighted sum (normalised, not yet rotated).
+// window's available slots, weighted sum (normalised, not yet rotated).  The
+// window is the group's m tokens and, with an overlap o, the o tokens before
+// it (rows -o .. -1 relative to the group); slots at positions below 0 or at
+// or past the n tokens of the run are absent.
 __device__ __forceinline__ void small_fold(const CompressArgs& a, const float* zb, const uint16_t* xb, int j, int n,
-                                           float acc[8]) {
-  const int m = a.m;
-  const int t0 = j * m;
-  const int r = min(m, n - t0);
+                                           int p0, float acc[8]) {
+  const int t0 = j * a.m - a.ov;                // row of the window's first slot
+  const int lo = max(0, -(p0 + t0));            // first slot at a position >= 0
+  const int hi = min(a.m + a.ov, n - t0);       // one past the last token of the run
   float mx = -INFINITY;
-  for (int i = 0; i < r; ++i) mx = fmaxf(mx, zb[t0 + i] + a.beta[i]);
+  for (int i = lo; i < hi; ++i) mx = fmaxf(mx, zb[t0 + i] + a.beta[i]);
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
   float tot = 0.0f;
-  for (int i = 0; i < r; ++i) {
+  for (int i = lo; i < hi; ++i) {
     const float e = expf(zb[t0 + i] + a.beta[i] - mx);
     tot += e;
     float v[8];
@@ -69,7 +77,7 @@ __device__ __forceinline__ void small_fold(const CompressArgs& a, const float* z
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = fmaf(e, v[c], acc[c]);
   }
-  const float inv_tot = 1.0f / tot;
+  const float inv_tot = tot > 0.0f ? 1.0f / tot : 0.0f;  // no slot: a negative pos0
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] *= inv_tot;
 }
@@ -157,7 +165,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
       if (!active) return;
       for (int j = bx * RP + gi; j < N; j += gx * RP) {
         float acc[8];
-        small_fold(a, zb, xb, j, n, acc);
+        small_fold(a, zb, xb, j, n, p0, acc);
         rope_store8(ob + (int64_t)j * a.d, lds_row ? lds_row + li * 8 : nullptr, acc, (double)p0 + (double)(j * m), inv);
       }
       return;
@@ -168,7 +176,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
       const int j = j0 + gi;
       const bool live = active && j < N;
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (live) small_fold(a, zb, xb, j, n, acc);
+      if (live) small_fold(a, zb, xb, j, n, p0, acc);
       float ss = 0.0f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) ss = fmaf(acc[c], acc[c], ss);

@@ -14,6 +14,7 @@ struct CompressArgs {
   const float* beta;
   const int32_t* pos0; const int32_t* ntok;
   int B, max_ntok, d, m;
+  int ov;  // overlap: tokens of the previous group in each window (rows -ov .. -1), m <= kSmallM when > 0
   float theta;
   const float* gamma; float eps;  // RMS normalisation of each entry before its rotation (gamma null: none)
   float* out; int64_t os;

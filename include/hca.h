@@ -101,8 +101,9 @@ const char* hca_version(void);
  *
  * For sequence b, tokens t = 0 .. ntok[b]-1 are the raw vectors of positions
  * pos0[b] + t (pos0[b] a multiple of m).  Entry j (j < ceil(ntok[b]/m)) folds
- * slots i < r = min(m, ntok[b] - j*m):
- *     w_i = softmax_i(gate_logit[t] + pos_bias[i]),  t = j*m + i
+ * the slots i < m + overlap of its window, t = j*m - overlap + i, that lie at
+ * positions >= 0 and below pos0[b] + ntok[b]:
+ *     w_i = softmax_i(gate_logit[t] + pos_bias[i])   (over those slots)
  *     c   = sum_i w_i x[t]
  *     c   = c * norm_gamma / sqrt(mean_c(c^2) + norm_eps)   (only if norm_gamma)
  *     out[b][j] = RoPE(c, pos0[b] + j*m)
@@ -111,16 +112,25 @@ const char* hca_version(void);
  * (pos0 = m*floor((L-1)/m), ntok = L - pos0) re-emits the open entry.  With
  * m = 1 this is the window insert RoPE(x_t, t).  RoPE rotates adjacent pairs
  * (2i, 2i+1) by angle p * rope_theta^(-2i/d); the angle is reduced in fp64.
+ * With overlap = 0 a window is the entry's own m tokens; c4a's window (section
+ * 2.1 folds every 8 tokens into one entry at a ratio of 1/4, section 3.1.2
+ * keeps an 8-token state) is m = 4, overlap = 4: tokens [4j-4, 4j+4).  The
+ * overlap's tokens are read at rows t = -overlap .. -1 before the run's first
+ * row (x and gate_logit), so for pos0[b] > 0 the caller keeps the previous
+ * group's last tokens there (as a ring of overlap + m rows does, or a buffer
+ * of the whole context); rows at positions below 0 are never read.
  * The optional RMS normalisation is the RMSNorm that section 3.2.1 fuses
  * between the compressor and RoPE; it acts on the folded (possibly partial)
  * entry, before the rotation.
  *
  *   x          bf16  x[b * x_stride_b + t * d + c]
  *   gate_logit float gate_logit[b * z_stride_b + t]
- *   pos_bias   float [m]
+ *   pos_bias   float [m + overlap]
  *   pos0, ntok int32 [B] (device); ntok[b] is clamped to [0, max_ntok]
  *   max_ntok   host bound on ntok (sizes the grid)
  *   d          even, 2 <= d, d % 8 == 0;  m in {1, 2, 4, ..., 256}
+ *   overlap    0 .. m (HCA_ERR_INVALID otherwise); > 0 needs m <= 16
+ *              (HCA_ERR_UNSUPPORTED)
  *   norm_gamma float [d] (16-byte aligned) or NULL (no normalisation);
  *   norm_eps   finite, > 0 when norm_gamma is given (ignored otherwise)
  *   out        float out[b * out_stride_b + j * d + c]
@@ -128,8 +138,8 @@ const char* hca_version(void);
 hca_status kv_compress(const uint16_t* x, int64_t x_stride_b, const float* gate_logit,
                        int64_t z_stride_b, const float* pos_bias, const int32_t* pos0,
                        const int32_t* ntok, int32_t B, int32_t max_ntok, int32_t d, int32_t m,
-                       float rope_theta, const float* norm_gamma, float norm_eps, float* out,
-                       int64_t out_stride_b, void* stream);
+                       int32_t overlap, float rope_theta, const float* norm_gamma, float norm_eps,
+                       float* out, int64_t out_stride_b, void* stream);
 
 /*
  * kv_quantize_page -- quantize entries into their pages (V4 page, sections
@@ -175,9 +185,10 @@ hca_status kv_quantize_page(const float* src, int64_t src_stride_b, const int32_
  * multiple of dst.epp), which must be in [0, dst.epp) (else nothing is
  * written); rows 0 .. j-e0[b]-1 of stage are the page's earlier entries.
  *
- *   x, gate_logit, pos_bias, norm_gamma, norm_eps: as kv_compress, with
- *              T = m tokens per sequence; m = 1 is the window insert of one
- *              token (dst.epp = 256)
+ *   x, gate_logit, pos_bias, overlap, norm_gamma, norm_eps: as kv_compress,
+ *              with T = m tokens per sequence after the overlap's rows (a
+ *              ring of overlap + m rows, x pointing at row overlap); m = 1 is
+ *              the window insert of one token (dst.epp = 256)
  *   stage      float stage[b * stage_stride_b + r * dst.dim + c], r < dst.epp;
  *              row j - e0[b] is written
  *   block_table int32 [B][bt_stride]: page of logical block e0[b] / dst.epp
@@ -196,7 +207,7 @@ hca_status kv_quantize_page(const float* src, int64_t src_stride_b, const int32_
  */
 hca_status kv_compress_insert(const uint16_t* x, int64_t x_stride_b, const float* gate_logit, int64_t z_stride_b,
                               const float* pos_bias, const int32_t* pos0, const int32_t* ntok, int32_t B, int32_t m,
-                              float rope_theta, const float* norm_gamma, float norm_eps, float* stage,
+                              int32_t overlap, float rope_theta, const float* norm_gamma, float norm_eps, float* stage,
                               int64_t stage_stride_b, const int32_t* e0, const int32_t* block_table,
                               int32_t bt_stride, hca_paged_cache dst, int32_t append, void* stream);
 
@@ -206,7 +217,7 @@ hca_status kv_compress_insert(const uint16_t* x, int64_t x_stride_b, const float
  * open indexer page), so the decode update of a layer costs one launch.
  * Each job has the arguments of kv_compress_insert; a job whose x is NULL
  * folds nothing: its open row j - e0[b] is already in stage (gate_logit,
- * pos_bias, ntok, rope_theta and the norm arguments are then unused) and the page is quantized as
+ * pos_bias, ntok, overlap, rope_theta and the norm arguments are then unused) and the page is quantized as
  * described above.  Jobs must write different pages and staging rows.
  *   n_jobs     0 .. 4 (HCA_ERR_UNSUPPORTED above); every job is validated
  *              before anything is launched.
@@ -220,6 +231,7 @@ typedef struct {
   const int32_t* pos0;
   const int32_t* ntok;
   int32_t m;
+  int32_t overlap;
   float rope_theta;
   const float* norm_gamma; /* NULL: no normalisation */
   float norm_eps;

@@ -2,8 +2,9 @@
 
 Shapes follow the problem statement of this build (tiny c4a, 64K c128a, 128K
 c4a with indexer, mixed paged batch, 1M 61-layer stack) and the pages' model
-description ([V4-vLLM] 2.1: 61 layers, the first 30 c4a and the last 31 c128a;
-2.3: a 128-token window; 3.1.1: 256-token logical blocks).
+description ([V4-vLLM] 2.1: 61 layers, the first 30 c4a and the last 31 c128a,
+a c4a entry folding an 8-token window at stride 4; 2.3: a 128-token window;
+3.1.1: 256-token logical blocks).
 """
 
 from dataclasses import dataclass, field
@@ -18,6 +19,12 @@ class LayerKind:
     idx_dtype: Optional[str] = None  # indexer key storage for c4a
     d_idx: int = 0
     h_idx: int = 16
+    overlap: int = 0  # tokens of the previous group in each entry's window (c4a: 4, an 8-token window)
+
+    @property
+    def slots(self) -> int:
+        """Slots of a compressor window (the length of its slot biases)."""
+        return self.m + self.overlap
 
 
 @dataclass
@@ -41,9 +48,9 @@ class Workload:
     extra: dict = field(default_factory=dict)
 
 
-C4A_TINY = LayerKind("c4a", 4, 256, "bf16", 64, 16)
-C4A_FP8 = LayerKind("c4a", 4, 2048, "fp8", 128, 16)
-C4A_FP4 = LayerKind("c4a", 4, 2048, "fp4", 128, 16)
+C4A_TINY = LayerKind("c4a", 4, 256, "bf16", 64, 16, overlap=4)
+C4A_FP8 = LayerKind("c4a", 4, 2048, "fp8", 128, 16, overlap=4)
+C4A_FP4 = LayerKind("c4a", 4, 2048, "fp4", 128, 16, overlap=4)
 C128A = LayerKind("c128a", 128, None)
 
 CONFIGS = {

@@ -132,10 +132,10 @@ class SeqData:
         self.table, self.num_pages, self.wtable, self.num_wpages = gen.block_tables(w, self.lens, seed)
         self.spec = pipeline.LayerSpec(m=self.kind.m, d=w.d, H=w.H, window=w.window, topk=self.kind.topk,
                                        kv_dtype=w.kv_dtype, idx_dtype=self.kind.idx_dtype, d_idx=self.kind.d_idx,
-                                       h_idx=self.kind.h_idx, theta=w.theta)
+                                       h_idx=self.kind.h_idx, theta=w.theta, overlap=self.kind.overlap)
         self.x = [gen.tokens(w, layer_idx, b, int(L), self.members, seed) for b, L in enumerate(self.lens)]
         self.z = [gen.logits(w, layer_idx, b, int(L), self.members, seed) for b, L in enumerate(self.lens)]
-        self.beta = gen.slot_bias(w, layer_idx, self.kind.m, seed)
+        self.beta = gen.slot_bias(w, layer_idx, self.kind.slots, seed)
         self.q = gen.queries(w, layer_idx, seed)[: self.B]
         self.entries = None
         if self.kind.topk is not None:
@@ -154,9 +154,8 @@ class SeqData:
         done_shared = False
         for b in range(self.B):
             xb = bf16_to_f64(self.x[b])
-            e = compressor.compress(xb, self.z[b], self.beta, s.m, s.theta)
+            e = pipeline.fill_entries(s, self.kv, self.table[b], xb, self.z[b], self.beta)
             self.entries.append(e)
-            paging.write_run(self.kv, self.table[b], 0, e.astype(np.float32))
             pipeline.fill_window(s, self.win, self.wtable[b], xb, int(self.lens[b]))
         if self.kind.topk is not None:
             self.idx = paging.Pool(self.kind.idx_dtype, self.num_pages, s.epp, self.kind.d_idx)

@@ -96,12 +96,12 @@ def _cache(dtype=1, epp=64, dim=128, pages=4, codes=FAKE, scales=FAKE):
 def test_validation_kv_compress():
     L = hca.lib()
     ok = dict(x=FAKE, xs=4096 * 8, z=FAKE, zs=4096, beta=FAKE, pos0=FAKE, ntok=FAKE, B=2, mx=4096, d=128, m=4,
-              theta=1e6, gam=None, eps=1e-6, out=FAKE, os=1024 * 128)
+              ov=0, theta=1e6, gam=None, eps=1e-6, out=FAKE, os=1024 * 128)
 
     def call(**kw):
         a = dict(ok, **kw)
         return L.kv_compress(a["x"], a["xs"], a["z"], a["zs"], a["beta"], a["pos0"], a["ntok"], a["B"], a["mx"],
-                             a["d"], a["m"], a["theta"], a["gam"], a["eps"], a["out"], a["os"], None)
+                             a["d"], a["m"], a["ov"], a["theta"], a["gam"], a["eps"], a["out"], a["os"], None)
 
     assert call(m=3) == 1 and call(m=512) == 1 and call(m=0) == 1
     assert call(d=12) == 1 and call(d=4096) == 2
@@ -114,18 +114,21 @@ def test_validation_kv_compress():
     assert call(gam=FAKE, eps=0.0) == 1 and call(gam=FAKE, eps=float("inf")) == 1
     assert call(gam=ctypes.c_void_p(0x1004)) == 1
     assert call(gam=FAKE, B=0) == 0 and call(gam=None, eps=0.0, B=0) == 0
+    # overlapping windows: 0 .. m, and only for groups of at most 16
+    assert call(ov=-1) == 1 and call(ov=5) == 1 and call(m=32, ov=4) == 2
+    assert call(ov=4, B=0) == 0 and call(m=16, ov=16, B=0) == 0
 
 
 def test_validation_kv_compress_insert():
     L = hca.lib()
-    ok = dict(x=FAKE, xs=4 * 128, z=FAKE, zs=4, beta=FAKE, pos0=FAKE, ntok=FAKE, B=2, m=4, theta=1e6, gam=None,
-              eps=1e-6, st=FAKE, ss=64 * 128, e0=FAKE, bt=FAKE, bts=16, dst=_cache(), app=0)
+    ok = dict(x=FAKE, xs=4 * 128, z=FAKE, zs=4, beta=FAKE, pos0=FAKE, ntok=FAKE, B=2, m=4, ov=0, theta=1e6,
+              gam=None, eps=1e-6, st=FAKE, ss=64 * 128, e0=FAKE, bt=FAKE, bts=16, dst=_cache(), app=0)
 
     def call(**kw):
         a = dict(ok, **kw)
         return L.kv_compress_insert(a["x"], a["xs"], a["z"], a["zs"], a["beta"], a["pos0"], a["ntok"], a["B"],
-                                    a["m"], a["theta"], a["gam"], a["eps"], a["st"], a["ss"], a["e0"], a["bt"],
-                                    a["bts"], a["dst"], a["app"], None)
+                                    a["m"], a["ov"], a["theta"], a["gam"], a["eps"], a["st"], a["ss"], a["e0"],
+                                    a["bt"], a["bts"], a["dst"], a["app"], None)
 
     assert call(m=3) == 1 and call(m=8) == 1  # the pool's epp must be 256 / m
     assert call(dst=_cache(dim=4096)) == 2
@@ -135,6 +138,7 @@ def test_validation_kv_compress_insert():
     assert call(xs=100) == 1 and call(ss=16) == 1 and call(zs=3) == 1
     assert call(B=-1) == 1
     assert call(gam=FAKE, eps=-1.0) == 1 and call(gam=ctypes.c_void_p(0x1008)) == 1
+    assert call(ov=8) == 1 and call(ov=-2) == 1
     assert call(B=0) == 0 and call(gam=FAKE, B=0) == 0  # nothing to do, nothing launched
 
 
@@ -143,11 +147,11 @@ def test_validation_kv_compress_insert_jobs():
 
     def job(**kw):
         a = dict(x=FAKE.value, xs=4 * 128, z=FAKE.value, zs=4, beta=FAKE.value, pos0=FAKE.value, ntok=FAKE.value,
-                 m=4, theta=1e6, gam=None, eps=1e-6, st=FAKE.value, ss=64 * 128, e0=FAKE.value, bt=FAKE.value,
-                 bts=16, dst=_cache(), app=0)
+                 m=4, ov=0, theta=1e6, gam=None, eps=1e-6, st=FAKE.value, ss=64 * 128, e0=FAKE.value,
+                 bt=FAKE.value, bts=16, dst=_cache(), app=0)
         a.update(kw)
-        return hca.CInsertJob(a["x"], a["xs"], a["z"], a["zs"], a["beta"], a["pos0"], a["ntok"], a["m"], a["theta"],
-                              a["gam"], a["eps"], a["st"], a["ss"], a["e0"], a["bt"], a["bts"], a["dst"], a["app"])
+        return hca.CInsertJob(a["x"], a["xs"], a["z"], a["zs"], a["beta"], a["pos0"], a["ntok"], a["m"], a["ov"],
+                              a["theta"], a["gam"], a["eps"], a["st"], a["ss"], a["e0"], a["bt"], a["bts"], a["dst"], a["app"])
 
     def call(jobs, B=2):
         arr = (hca.CInsertJob * max(len(jobs), 1))(*jobs)
@@ -161,8 +165,9 @@ def test_validation_kv_compress_insert_jobs():
     assert call([job(), job(app=3)]) == 1
     assert call([], B=2) == 0 and call([job()], B=0) == 0  # nothing to do, nothing launched
     assert call([job(), job(gam=FAKE.value, eps=0.0)]) == 1
-    # without a fold the norm arguments are not used
-    assert call([job(x=None, gam=FAKE.value, eps=0.0)], B=0) == 0
+    # without a fold the norm and overlap arguments are not used
+    assert call([job(x=None, gam=FAKE.value, eps=0.0, ov=9)], B=0) == 0
+    assert call([job(), job(ov=5)]) == 1
 
 
 def test_validation_quantize_and_gather():

@@ -191,6 +191,39 @@ def test_compress_entries_normalised(m, d):
         assert H.rel_err_rows(got[b, : ref.shape[0]], ref) <= H.ENTRY_TOL, b
 
 
+# Overlapping windows: each entry also folds the o tokens before its group,
+# read at rows -o .. -1 of the run (the buffer holds them before the view
+# passed in; for pos0 = 0 those rows hold NaNs, which must never be read).
+@pytest.mark.parametrize("m,o,d,norm", [(4, 4, 512, False), (4, 4, 512, True), (4, 4, 136, True), (2, 1, 64, False),
+                                        (16, 16, 128, False), (4, 2, 1024, True), (1, 1, 256, False)])
+def test_compress_entries_overlap(m, o, d, norm):
+    H.flush(f"compress overlap m={m} o={o} d={d} norm={norm}")
+    rng = np.random.default_rng(53)
+    T = [m * 37 + (m // 2 + 1 if m > 1 else 0), 3, m * 9, 1, 2 * m]
+    pos0 = np.array([0, m * 1000, m * 262143, 0, m], np.int32)
+    B, Tm = len(T), max(T)
+    x32 = rng.standard_normal((B, o + Tm, d)).astype(np.float32)
+    xb = gen.to_bf16_bits(x32)
+    z = rng.standard_normal((B, o + Tm)).astype(np.float32)
+    for b in range(B):
+        if pos0[b] == 0:  # positions below 0: never read
+            xb[b, :o] = 0x7FC0
+            z[b, :o] = np.nan
+    beta = (rng.standard_normal(m + o) * 0.1).astype(np.float32)
+    gam = rng.uniform(0.5, 1.5, d).astype(np.float32) if norm else None
+    xd, zd = H.to_dev(xb.view(np.int16)), H.to_dev(z)
+    out = torch.zeros((B, -(-Tm // m), d), dtype=torch.float32, device="cuda")
+    hca.kv_compress(xd[:, o:], zd[:, o:], H.to_dev(beta), H.to_dev(pos0), H.to_dev(np.array(T, np.int32)), m, 1e6,
+                    out, Tm, norm_gamma=None if gam is None else H.to_dev(gam), overlap=o)
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    for b in range(B):
+        xs = codecs.bf16_decode(xb[b, o: o + T[b]])
+        ref = compressor.compress_overlap(xs, z[b, o: o + T[b]], beta, m, o, 1e6, pos0=int(pos0[b]),
+                                          x_prev=codecs.bf16_decode(xb[b, :o]), z_prev=z[b, :o], gamma=gam)
+        assert H.rel_err_rows(got[b, : ref.shape[0]], ref) <= H.ENTRY_TOL, b
+
+
 # ----------------------------------------------------------------- kv_compress_insert
 
 
@@ -201,15 +234,17 @@ def test_compress_entries_normalised(m, d):
 # (the new page's first row), grow an fp8 page scale with a large token, and
 # start one page from all-zero rows (scale 1.0, which append mode must not
 # trust).  With norm, every folded entry is RMS-normalised before its rotation.
-@pytest.mark.parametrize("m,dtype,d,append,norm", [
-    (1, "fp8", 512, True, False), (1, "fp8", 512, False, False), (4, "fp8", 512, False, False),
-    (4, "fp8", 512, True, False), (128, "fp8", 512, True, False), (128, "fp8", 512, False, False),
-    (2, "fp8", 136, False, False), (2, "fp8", 512, True, False), (4, "fp4", 128, False, False),
-    (1, "fp4", 128, True, False), (4, "bf16", 128, False, False), (1, "bf16", 64, True, False),
-    (4, "fp8", 512, True, True), (128, "fp8", 512, True, True), (1, "fp8", 512, True, True),
-    (2, "fp8", 136, False, True), (4, "fp4", 128, True, True)])
-def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append, norm):
-    H.flush(f"compress_insert m={m} {dtype} d={d} append={append} norm={norm}")
+@pytest.mark.parametrize("m,dtype,d,append,norm,o", [
+    (1, "fp8", 512, True, False, 0), (1, "fp8", 512, False, False, 0), (4, "fp8", 512, False, False, 0),
+    (4, "fp8", 512, True, False, 0), (128, "fp8", 512, True, False, 0), (128, "fp8", 512, False, False, 0),
+    (2, "fp8", 136, False, False, 0), (2, "fp8", 512, True, False, 0), (4, "fp4", 128, False, False, 0),
+    (1, "fp4", 128, True, False, 0), (4, "bf16", 128, False, False, 0), (1, "bf16", 64, True, False, 0),
+    (4, "fp8", 512, True, True, 0), (128, "fp8", 512, True, True, 0), (1, "fp8", 512, True, True, 0),
+    (2, "fp8", 136, False, True, 0), (4, "fp4", 128, True, True, 0),
+    (4, "fp8", 512, True, True, 4), (4, "fp8", 512, False, False, 4), (4, "fp4", 128, True, False, 4),
+    (2, "bf16", 64, False, False, 2), (4, "fp8", 136, True, True, 2)])
+def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append, norm, o):
+    H.flush(f"compress_insert m={m} {dtype} d={d} append={append} norm={norm} overlap={o}")
     rng = np.random.default_rng(61 + m)
     gam = rng.uniform(0.5, 1.5, d).astype(np.float32) if norm else None
     gam_d = H.to_dev(gam) if norm else None
@@ -221,7 +256,7 @@ def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append, norm)
     nb = int(L.max() + steps) // 256 + 2
     table = rng.permutation(B * nb + 2)[: B * nb].reshape(B, nb).astype(np.int32)
     P = B * nb + 2
-    beta = (rng.standard_normal(m) * 0.1).astype(np.float32)
+    beta = (rng.standard_normal(m + o) * 0.1).astype(np.float32)
     stage_f = torch.zeros((B, epp, d), dtype=torch.float32, device="cuda")
     pool_f = hca.PagedCache.empty(P, epp, d, dtype)
     pool_f.codes.fill_(0)
@@ -245,8 +280,13 @@ def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append, norm)
     stage_u = stage_f.clone()
     pool_u = hca.PagedCache(pool_f.codes.clone(), None if pool_f.scales is None else pool_f.scales.clone(), epp, d,
                             dtype)
-    ring_x = np.zeros((B, m, d), np.float32)
-    ring_z = np.zeros((B, m), np.float32)
+    # the ring of the open group's window: rows 0 .. o-1 the overlap (the tokens
+    # before the group: drawn for the starting state, then carried), rows o ..
+    # the open group
+    ring_x = np.zeros((B, o + m, d), np.float32)
+    ring_z = np.zeros((B, o + m), np.float32)
+    ring_x[:, :o] = rng.standard_normal((B, o, d))
+    ring_z[:, :o] = rng.standard_normal((B, o))
     for step in range(steps):
         L += 1
         pos0 = (m * ((L - 1) // m)).astype(np.int32)
@@ -254,21 +294,26 @@ def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append, norm)
         for b in range(B):
             t = int(ntok[b]) - 1
             if t == 0:
-                ring_x[b] = 0.0
-                ring_z[b] = 0.0
+                if step > 0 and o > 0:  # the closed group's last o tokens become the overlap
+                    ring_x[b, :o] = ring_x[b, m: m + o].copy()
+                    ring_z[b, :o] = ring_z[b, m: m + o].copy()
+                ring_x[b, o:] = 0.0
+                ring_z[b, o:] = 0.0
             scale = 40.0 if (b == 2 and step == 3) else (0.0 if (b == 2 and step == 0) else 1.0)
-            ring_x[b, t] = rng.standard_normal(d) * scale
-            ring_z[b, t] = rng.standard_normal()
+            ring_x[b, o + t] = rng.standard_normal(d) * scale
+            ring_z[b, o + t] = rng.standard_normal()
         xb = gen.to_bf16_bits(ring_x)
         j = pos0 // m
         e0 = (epp * (j // epp)).astype(np.int32)
         row = j - e0
-        xd, zd = H.to_dev(xb.view(np.int16)), H.to_dev(ring_z)
+        xr, zr = H.to_dev(xb.view(np.int16)), H.to_dev(ring_z)
+        xd, zd = xr[:, o:], zr[:, o:]  # rows -o .. -1: the overlap
         hca.kv_compress_insert(xd, zd, H.to_dev(beta), H.to_dev(pos0), H.to_dev(ntok), m, theta, stage_f,
-                               H.to_dev(e0), H.to_dev(table), pool_f, append=append, norm_gamma=gam_d)
+                               H.to_dev(e0), H.to_dev(table), pool_f, append=append, norm_gamma=gam_d, overlap=o)
         for b in range(B):  # the two-call path, one sequence at a time (rows differ)
             hca.kv_compress(xd[b:b + 1], zd[b:b + 1], H.to_dev(beta), H.to_dev(pos0[b:b + 1]),
-                            H.to_dev(ntok[b:b + 1]), m, theta, stage_u[b:b + 1, int(row[b]):], m, norm_gamma=gam_d)
+                            H.to_dev(ntok[b:b + 1]), m, theta, stage_u[b:b + 1, int(row[b]):], m, norm_gamma=gam_d,
+                            overlap=o)
             hca.kv_quantize_page(stage_u[b:b + 1], H.to_dev(e0[b:b + 1]), H.to_dev(row[b:b + 1] + 1), epp,
                                  H.to_dev(table[b:b + 1]), pool_u)
         torch.cuda.synchronize()
@@ -279,8 +324,14 @@ def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append, norm)
         for b in range(B):
             r = int(row[b])
             assert np.array_equal(sf[b, : r + 1].view(np.uint32), su[b, : r + 1].view(np.uint32)), (step, b)
-            ent = compressor.compress(codecs.bf16_decode(xb[b, : ntok[b]]), ring_z[b, : ntok[b]], beta, m, theta,
-                                      pos0=int(pos0[b]), gamma=gam, eps=1e-6)
+            if o > 0:
+                ent = compressor.compress_overlap(codecs.bf16_decode(xb[b, o: o + ntok[b]]), ring_z[b, o: o + ntok[b]],
+                                                  beta, m, o, theta, pos0=int(pos0[b]),
+                                                  x_prev=codecs.bf16_decode(xb[b, :o]), z_prev=ring_z[b, :o],
+                                                  gamma=gam, eps=1e-6)
+            else:
+                ent = compressor.compress(codecs.bf16_decode(xb[b, : ntok[b]]), ring_z[b, : ntok[b]], beta, m, theta,
+                                          pos0=int(pos0[b]), gamma=gam, eps=1e-6)
             assert H.rel_err_rows(sf[b, r : r + 1], ent[-1:]) <= H.ENTRY_TOL, (step, b)
             if r == 0:
                 ref_rows[b] = 0.0  # a new page
@@ -313,9 +364,9 @@ def test_compress_insert_jobs_one_launch():
     e0_c = (64 * ((pos_c // 4) // 64)).astype(np.int32)
     xw = gen.to_bf16_bits(rng.standard_normal((B, 1, d)).astype(np.float32))
     zw = rng.standard_normal((B, 1)).astype(np.float32)
-    xc = gen.to_bf16_bits(rng.standard_normal((B, 4, d)).astype(np.float32))
-    zc = rng.standard_normal((B, 4)).astype(np.float32)
-    beta = (rng.standard_normal(4) * 0.1).astype(np.float32)
+    xc = gen.to_bf16_bits(rng.standard_normal((B, 8, d)).astype(np.float32))  # the 8-token window's ring
+    zc = rng.standard_normal((B, 8)).astype(np.float32)
+    beta = (rng.standard_normal(8) * 0.1).astype(np.float32)
     gam = H.to_dev(rng.uniform(0.5, 1.5, d).astype(np.float32))  # the entries are RMS-normalised
     stages = (rng.standard_normal((B, 256, d)).astype(np.float32), rng.standard_normal((B, 64, d)).astype(np.float32),
               rng.standard_normal((B, 64, di)).astype(np.float32))
@@ -325,7 +376,8 @@ def test_compress_insert_jobs_one_launch():
         win = hca.PagedCache.empty(B * nb, 256, d, "fp8")
         kv = hca.PagedCache.empty(B * nb, 64, d, "fp8")
         idx = hca.PagedCache.empty(B * nb, 64, di, "fp4")
-        xwd, zwd, xcd, zcd = H.to_dev(xw.view(np.int16)), H.to_dev(zw), H.to_dev(xc.view(np.int16)), H.to_dev(zc)
+        xwd, zwd, xcd, zcd = H.to_dev(xw.view(np.int16)), H.to_dev(zw), H.to_dev(xc.view(np.int16))[:, 4:], \
+            H.to_dev(zc)[:, 4:]
         args = dict(pos_w=H.to_dev(pos_w), e0_w=H.to_dev(e0_w), pos_c=H.to_dev(pos_c), ntok_c=H.to_dev(ntok_c),
                     e0_c=H.to_dev(e0_c), one=H.to_dev(np.ones(B, np.int32)), zero1=H.to_dev(np.zeros(1, np.float32)),
                     beta=H.to_dev(beta), tab=H.to_dev(table), wtab=H.to_dev(wtable))
@@ -333,14 +385,15 @@ def test_compress_insert_jobs_one_launch():
             jobs = [hca.insert_job(wst, args["pos_w"], args["e0_w"], args["wtab"], win, 1, x=xwd, gate_logit=zwd,
                                    pos_bias=args["zero1"], ntok=args["one"], rope_theta=theta),
                     hca.insert_job(cst, args["pos_c"], args["e0_c"], args["tab"], kv, 4, x=xcd, gate_logit=zcd,
-                                   pos_bias=args["beta"], ntok=args["ntok_c"], rope_theta=theta, norm_gamma=gam),
+                                   pos_bias=args["beta"], ntok=args["ntok_c"], rope_theta=theta, norm_gamma=gam,
+                                   overlap=4),
                     hca.insert_job(ist, args["pos_c"], args["e0_c"], args["tab"], idx, 4)]
             hca.kv_compress_insert_jobs(jobs, B)
         else:
             hca.kv_compress_insert(xwd, zwd, args["zero1"], args["pos_w"], args["one"], 1, theta, wst, args["e0_w"],
                                    args["wtab"], win)
             hca.kv_compress_insert(xcd, zcd, args["beta"], args["pos_c"], args["ntok_c"], 4, theta, cst, args["e0_c"],
-                                   args["tab"], kv, norm_gamma=gam)
+                                   args["tab"], kv, norm_gamma=gam, overlap=4)
             rows = H.to_dev(((pos_c // 4) - e0_c + 1).astype(np.int32))
             hca.kv_quantize_page(ist, args["e0_c"], rows, 64, args["tab"], idx)
         torch.cuda.synchronize()

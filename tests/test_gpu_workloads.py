@@ -68,13 +68,13 @@ class FullLayer:
         for b in range(B):
             self.x[b] = gen.device_normal((L, d), 1.0, (0, w.cid, li, gen.S_TOK, b), dtype=torch.bfloat16)
         self.z = gen.device_normal((B, L), 1.0, (0, w.cid, li, gen.S_LOGIT))
-        self.beta_np = gen.slot_bias(w, li, m)
+        self.beta_np = gen.slot_bias(w, li, kind.slots)
         self.gamma_np = gen.norm_gain(w, li, d)
         xi = self.x.view(torch.int16)
         # prefill: entries, their pages
         self.ent = torch.empty((B, self.N, d), dtype=torch.float32, device="cuda")
         hca.kv_compress(xi, self.z, _dev(self.beta_np), zeros, self.lens, m, w.theta, self.ent, L,
-                        norm_gamma=_dev(self.gamma_np), norm_eps=1e-6)
+                        norm_gamma=_dev(self.gamma_np), norm_eps=1e-6, overlap=kind.overlap)
         self.kv = hca.PagedCache.empty(self.P, self.epp, d, w.kv_dtype)
         hca.kv_quantize_page(self.ent, zeros, _dev(np.full(B, self.N, np.int32)), self.N, _dev(self.table), self.kv)
         # window pages: every token of the blocks that overlap [L-W, L)
@@ -101,7 +101,7 @@ class FullLayer:
         w, k = self.w, self.kind
         return pipeline.LayerSpec(m=k.m, d=w.d, H=w.H, window=w.window, topk=k.topk, kv_dtype=w.kv_dtype,
                                   idx_dtype=k.idx_dtype, d_idx=k.d_idx, h_idx=k.h_idx, theta=w.theta,
-                                  gamma=self.gamma_np, eps=1e-6)
+                                  gamma=self.gamma_np, eps=1e-6, overlap=k.overlap)
 
     def gpu_page(self, pc, phys):
         """Codes and scale(s) of one physical page of a GPU pool, on the host."""
@@ -140,8 +140,15 @@ class OracleSeq:
             k += 1
             e0, e1 = p0 * lay.epp, min(lay.N, p1 * lay.epp)
             t0, t1 = e0 * lay.m, min(w.L, e1 * lay.m)
-            e = compressor.compress(codecs.bf16_decode(self.x[t0:t1]), self.z[t0:t1], lay.beta_np, lay.m, w.theta,
-                                    pos0=t0, gamma=lay.gamma_np, eps=1e-6)
+            o = lay.kind.overlap
+            if o > 0:
+                e = compressor.compress_overlap(codecs.bf16_decode(self.x[t0:t1]), self.z[t0:t1], lay.beta_np,
+                                                lay.m, o, w.theta, pos0=t0,
+                                                x_prev=codecs.bf16_decode(self.x[max(0, t0 - o): t0]),
+                                                z_prev=self.z[max(0, t0 - o): t0], gamma=lay.gamma_np, eps=1e-6)
+            else:
+                e = compressor.compress(codecs.bf16_decode(self.x[t0:t1]), self.z[t0:t1], lay.beta_np, lay.m,
+                                        w.theta, pos0=t0, gamma=lay.gamma_np, eps=1e-6)
             paging.write_run(self.kv, lay.table[self.b], e0, e.astype(np.float32))
             for p in range(p0, p1):
                 self.rows[p] = e[(p - p0) * lay.epp: (p - p0 + 1) * lay.epp]
