@@ -44,10 +44,10 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 # copy_bandwidth() (the summary with the commands is in profiles/).  They hold
 # only for the kernel source they were taken on, identified by the SHA-256 of
 # the indexer source and the headers it includes; otherwise traffic is null.
-SCORE_TRAFFIC = {"source_sha256": "a402ee491b26c4a03dd13bcef109fc9fe6bd6b686838fcaef60515554b40502c",
-                 "fetch_bytes": 71809582, "write_bytes": 5525194}
+SCORE_TRAFFIC = {"source_sha256": "ac7539f94f70c8ec8442a172328fec5a368c6f839a9f2a4d2fbce75ecf2b1c4d",
+                 "fetch_bytes": 71811323, "write_bytes": 5526188}
 SCORE_SOURCES = ("decode_attention_compressed_amd/csrc/indexer.hip", "decode_attention_compressed_amd/csrc/hca_common.h",
-                 "decode_attention_compressed_amd/csrc/hca_internal.h")
+                 "decode_attention_compressed_amd/csrc/indexer_internal.h")
 
 
 def score_source_sha256():

@@ -74,7 +74,7 @@ hca_status kv_compress(const uint16_t* x, int64_t x_stride_b, const float* gate_
   if (B > 1 && (x_stride_b < (int64_t)max_ntok * d || z_stride_b < max_ntok || out_stride_b < n_out * d))
     return HCA_ERR_INVALID;
   CompressArgs a{x, x_stride_b, gate_logit, z_stride_b, pos_bias, pos0, ntok, B, max_ntok, d, m, overlap,
-                 rope_theta, norm_gamma, norm_eps, out, out_stride_b};
+                 rope_theta, 0.0, norm_gamma, norm_eps, out, out_stride_b};
   return from_hip(launch_compress(a, (hipStream_t)stream));
 }
 
@@ -98,7 +98,7 @@ hca_status make_insert(const hca_insert_job& j, int32_t B, InsertArgs& out) {
   if (B > 1 && j.stage_stride_b < (int64_t)j.dst.epp * d) return HCA_ERR_INVALID;
   if (fold && B > 1 && (j.x_stride_b < (int64_t)j.m * d || j.z_stride_b < j.m)) return HCA_ERR_INVALID;
   out = InsertArgs{CompressArgs{j.x, j.x_stride_b, j.gate_logit, j.z_stride_b, j.pos_bias, j.pos0, j.ntok, B, j.m, d,
-                                j.m, fold ? j.overlap : 0, j.rope_theta, j.norm_gamma, j.norm_eps, nullptr, 0},
+                                j.m, fold ? j.overlap : 0, j.rope_theta, 0.0, j.norm_gamma, j.norm_eps, nullptr, 0},
                    j.stage, j.stage_stride_b, j.e0, j.block_table, j.bt_stride, j.dst, j.append};
   return HCA_OK;
 }
@@ -250,7 +250,7 @@ hca_status paged_hybrid_decode(const uint16_t* q, int32_t H, hca_paged_cache kv,
   if (window == 0) { w = kv; w.epp = 256; }  // never read
   AttnArgs a{q, H, kv, block_table, bt_stride, w, window > 0 ? win_block_table : block_table,
              window > 0 ? wbt_stride : bt_stride, seq_lens, B, max_seq_len, m, window, sel_idx, sel_n,
-             sel_idx ? k : 0, softmax_scale, rope_theta, out, lse, out_fp8, out_fp8 ? out_scale : nullptr,
+             sel_idx ? k : 0, softmax_scale, rope_theta, 0.0, out, lse, out_fp8, out_fp8 ? out_scale : nullptr,
              reinterpret_cast<unsigned char*>(ws), plan};
   return from_hip(launch_attention(a, (hipStream_t)stream));
 }

@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
   // ---- RoPE table at the query position L-1: the one block-wide wait
   for (int i = threadIdx.x; i < D / 2; i += kAttnThreads) {
     float c, sn;
-    rope_cs((double)(L - 1), rope_inv_freq(i, D, a.theta), c, sn);
+    rope_cs((double)(L - 1), rope_inv_freq(i, a.rope_r), c, sn);
     cs_s[i] = make_float2(c, sn);
   }
   lds_barrier();
@@ -745,7 +745,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
   for (int k = 0; k < kPairs; ++k) {
     const int pi = threadIdx.x + kCombThreads * k;
     float c = 1.0f, sn = 0.0f;
-    if (pi < D / 2) rope_cs((double)(L - 1), rope_inv_freq(pi, D, a.theta), c, sn);
+    if (pi < D / 2) rope_cs((double)(L - 1), rope_inv_freq(pi, a.rope_r), c, sn);
     cs[k] = make_float2(c, sn);
   }
   // split maxima -> M; weights w_s = exp(m_s - M) (0 for empty splits); tot = sum w_s l_s
@@ -858,8 +858,10 @@ static hipError_t launch_attn_d(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  if (a.B == 0) return hipSuccess;
+hipError_t launch_attention(const AttnArgs& args, hipStream_t s) {
+  if (args.B == 0) return hipSuccess;
+  AttnArgs a = args;
+  a.rope_r = pow((double)a.theta, -2.0 / (double)a.kv.dim);
   switch (a.kv.dim) {
     case 64: return launch_attn_d<64>(a, s);
     case 128: return launch_attn_d<128>(a, s);

@@ -59,23 +59,72 @@ __device__ __forceinline__ void rope_store8(float* dst, float* lds, const float 
 // window is the group's m tokens and, with an overlap o, the o tokens before
 // it (rows -o .. -1 relative to the group); slots at positions below 0 or at
 // or past the n tokens of the run are absent.
+//
+// Every load of a batch is issued before any of it is used, and the sums run
+// in slot order.  The first batch's token rows and logits are loaded, then
+// `mid()` runs (the insert issues its page loads there: they stay in flight
+// while the fold computes, since its own loads were issued first), then the
+// window of up to 2 * kSmallM slots is folded.
+__device__ __forceinline__ void fold_batch(int ns, float mx, int k0, const u32x4 raw[], const float av[], float acc[8],
+                                           float& tot) {
+  constexpr int kFoldBatch = 8;
+#pragma unroll
+  for (int k = 0; k < kFoldBatch; ++k) {
+    if (k0 + k < ns) {
+      const float e = expf(av[k] - mx);
+      tot += e;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(e, u2f(raw[k][q] << 16), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(e, u2f(raw[k][q] & 0xFFFF0000u), acc[2 * q + 1]);
+      }
+    }
+  }
+}
+
+template <typename Mid>
 __device__ __forceinline__ void small_fold(const CompressArgs& a, const float* zb, const uint16_t* xb, int j, int n,
-                                           int p0, float acc[8]) {
+                                           int p0, bool live, float acc[8], Mid&& mid) {
+  constexpr int kFoldBatch = 8;
+  constexpr int kMaxSlots = 2 * kSmallM;        // m + overlap, overlap <= m <= kSmallM
   const int t0 = j * a.m - a.ov;                // row of the window's first slot
   const int lo = max(0, -(p0 + t0));            // first slot at a position >= 0
-  const int hi = min(a.m + a.ov, n - t0);       // one past the last token of the run
+  const int ns = live ? min(a.m + a.ov, n - t0) - lo : 0;  // slots present
+  u32x4 raw[kFoldBatch];
+  float zv[kFoldBatch], bv[kFoldBatch];
+#pragma unroll
+  for (int k = 0; k < kFoldBatch; ++k) {
+    const bool on = k < ns;
+    raw[k] = on ? *reinterpret_cast<const u32x4*>(xb + (int64_t)(t0 + lo + k) * a.d) : u32x4{0u, 0u, 0u, 0u};
+    zv[k] = on ? zb[t0 + lo + k] : 0.0f;
+    bv[k] = on ? a.beta[lo + k] : 0.0f;
+  }
+  mid();
+  float av[kFoldBatch];
   float mx = -INFINITY;
-  for (int i = lo; i < hi; ++i) mx = fmaxf(mx, zb[t0 + i] + a.beta[i]);
+#pragma unroll
+  for (int k = 0; k < kFoldBatch; ++k) {
+    av[k] = zv[k] + bv[k];
+    if (k < ns) mx = fmaxf(mx, av[k]);
+  }
+#pragma unroll
+  for (int k = kFoldBatch; k < kMaxSlots; ++k)
+    if (k < ns) mx = fmaxf(mx, zb[t0 + lo + k] + a.beta[lo + k]);
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
   float tot = 0.0f;
-  for (int i = lo; i < hi; ++i) {
-    const float e = expf(zb[t0 + i] + a.beta[i] - mx);
-    tot += e;
-    float v[8];
-    load_bf16x8(xb + (int64_t)(t0 + i) * a.d, v);
+  fold_batch(ns, mx, 0, raw, av, acc, tot);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = fmaf(e, v[c], acc[c]);
+  for (int k0 = kFoldBatch; k0 < kMaxSlots; k0 += kFoldBatch) {
+    if (k0 < ns) {
+#pragma unroll
+      for (int k = 0; k < kFoldBatch; ++k) {
+        const bool on = k0 + k < ns;
+        raw[k] = on ? *reinterpret_cast<const u32x4*>(xb + (int64_t)(t0 + lo + k0 + k) * a.d) : u32x4{0u, 0u, 0u, 0u};
+        av[k] = on ? zb[t0 + lo + k0 + k] + a.beta[lo + k0 + k] : 0.0f;
+      }
+      fold_batch(ns, mx, k0, raw, av, acc, tot);
+    }
   }
   const float inv_tot = tot > 0.0f ? 1.0f / tot : 0.0f;  // no slot: a negative pos0
 #pragma unroll
@@ -115,17 +164,24 @@ __device__ __forceinline__ float row_group_sum(float v, int TD, int RP, int gi, 
 // shared memory of the launch holds kCompressShm bytes.  PATHS selects the
 // code compiled in: 1 small groups only, 2 large groups only, 3 both (a
 // kernel holding only what its groups need keeps its register count down).
-template <int PATHS = 3>
-__device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int bx, int gx, float* lds_row) {
+//
+// n and p0 are sequence b's token count (clamped) and first position; `mid()`
+// is called by every thread once per round of entries, after the round's
+// first loads are issued (a no-op for a plain fold).
+struct NoMid {
+  __device__ void operator()() const {}
+};
+
+template <int PATHS = 3, typename Mid = NoMid>
+__device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int bx, int gx, float* lds_row, int n,
+                                               int p0, Mid&& mid) {
   const int TD = a.d >> 3;              // threads across the dims of a row
   const int RP = kCompressThreads / TD; // row groups
   const int li = threadIdx.x % TD;
   const int gi = threadIdx.x / TD;
   const bool active = gi < RP;
-  const int n = clampi(a.ntok[b], 0, a.max_ntok);
   const int m = a.m;
   const int N = (n + m - 1) / m;
-  const int p0 = a.pos0[b];
   const uint16_t* xb = a.x + (int64_t)b * a.xs + li * 8;
   const float* zb = a.z + (int64_t)b * a.zs;
   float* ob = a.out + (int64_t)b * a.os + li * 8;
@@ -158,25 +214,23 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
 
   double inv[4];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) inv[p] = rope_inv_freq(li * 4 + p, a.d, a.theta);
+  for (int p = 0; p < 4; ++p) inv[p] = rope_inv_freq(li * 4 + p, a.rope_r);
 
   if (small) {
-    if (a.gamma == nullptr) {
-      if (!active) return;
-      for (int j = bx * RP + gi; j < N; j += gx * RP) {
-        float acc[8];
-        small_fold(a, zb, xb, j, n, p0, acc);
-        rope_store8(ob + (int64_t)j * a.d, lds_row ? lds_row + li * 8 : nullptr, acc, (double)p0 + (double)(j * m), inv);
-      }
-      return;
-    }
-    // normalised: every thread runs every round (the row sum may synchronize)
+    // every thread runs every round (mid() and the row sum of the
+    // normalisation are block-wide)
     __shared__ float sq_s[kCompressThreads];
     for (int j0 = bx * RP; j0 < N; j0 += gx * RP) {
       const int j = j0 + gi;
       const bool live = active && j < N;
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (live) small_fold(a, zb, xb, j, n, p0, acc);
+      float acc[8];
+      small_fold(a, zb, xb, j, n, p0, live, acc, mid);
+      if (a.gamma == nullptr) {
+        if (live)
+          rope_store8(ob + (int64_t)j * a.d, lds_row ? lds_row + li * 8 : nullptr, acc, (double)p0 + (double)(j * m),
+                      inv);
+        continue;
+      }
       float ss = 0.0f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) ss = fmaf(acc[c], acc[c], ss);
@@ -206,37 +260,43 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
     const int base = (u % nsl) * DS;
     const int t0 = j * m;
     const int r = min(m, n - t0);
-    // softmax weights of the group's r slots
-    float a_i = -INFINITY;
-    if (threadIdx.x < r) a_i = zb[t0 + threadIdx.x] + a.beta[threadIdx.x];
-    red_s[threadIdx.x] = a_i;
-    __syncthreads();
-    for (int o = kCompressThreads / 2; o > 0; o >>= 1) {
-      if (threadIdx.x < o) red_s[threadIdx.x] = fmaxf(red_s[threadIdx.x], red_s[threadIdx.x + o]);
-      __syncthreads();
+    // the row group's first batch of token rows is in flight while the
+    // softmax weights of the group's r slots are reduced (wave reductions,
+    // then the four wave partials in a fixed order)
+    constexpr int kBatch = 16;
+    u32x4 raw[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = gs + k * RS;
+      raw[k] = gs < RS && i < r ? *reinterpret_cast<const u32x4*>(xs + (int64_t)(t0 + i) * a.d + base)
+                                : u32x4{0u, 0u, 0u, 0u};
     }
-    const float mx = red_s[0];
+    const float zi = (int)threadIdx.x < r ? zb[t0 + threadIdx.x] : 0.0f;
+    const float bi = (int)threadIdx.x < r ? a.beta[threadIdx.x] : 0.0f;
+    mid();
+    const float a_i = (int)threadIdx.x < r ? zi + bi : -INFINITY;
+    const float wm = wave_max(a_i);
+    if ((threadIdx.x & 63) == 0) red_s[threadIdx.x >> 6] = wm;
     __syncthreads();
+    const float mx = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
     const float e = threadIdx.x < r ? expf(a_i - mx) : 0.0f;
-    red_s[threadIdx.x] = e;
     w_s[threadIdx.x] = e;
+    const float ws = wave_sum(e);
+    if ((threadIdx.x & 63) == 0) red_s[4 + (threadIdx.x >> 6)] = ws;
     __syncthreads();
-    for (int o = kCompressThreads / 2; o > 0; o >>= 1) {
-      if (threadIdx.x < o) red_s[threadIdx.x] += red_s[threadIdx.x + o];
-      __syncthreads();
-    }
-    const float tot = red_s[0];
+    const float tot = (red_s[4] + red_s[5]) + (red_s[6] + red_s[7]);
     if (gs < RS) {
       // the row group's tokens i = gs, gs + RS, ..., in batches whose loads
       // are all in flight before the first is summed (same order of sums)
-      constexpr int kBatch = 16;
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int i0 = gs; i0 < r; i0 += kBatch * RS) {
-        u32x4 raw[kBatch];
+        if (i0 != gs) {
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          const int i = i0 + k * RS;
-          raw[k] = i < r ? *reinterpret_cast<const u32x4*>(xs + (int64_t)(t0 + i) * a.d + base) : u32x4{0u, 0u, 0u, 0u};
+          for (int k = 0; k < kBatch; ++k) {
+            const int i = i0 + k * RS;
+            raw[k] = i < r ? *reinterpret_cast<const u32x4*>(xs + (int64_t)(t0 + i) * a.d + base)
+                           : u32x4{0u, 0u, 0u, 0u};
+          }
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
@@ -300,7 +360,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
         e1 *= inv_tot;
       }
       float c, sn;
-      rope_cs(pos, rope_inv_freq(base / 2 + t, a.d, a.theta), c, sn);
+      rope_cs(pos, rope_inv_freq(base / 2 + t, a.rope_r), c, sn);
       float* o = a.out + (int64_t)b * a.os + (int64_t)j * a.d + base + 2 * t;
       o[0] = e0 * c - e1 * sn;
       o[1] = e0 * sn + e1 * c;
@@ -315,7 +375,8 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
 
 template <int PATHS>
 __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs a) {
-  compress_block<PATHS>(a, blockIdx.y, blockIdx.x, gridDim.x, nullptr);
+  const int b = blockIdx.y;
+  compress_block<PATHS>(a, b, blockIdx.x, gridDim.x, nullptr, clampi(a.ntok[b], 0, a.max_ntok), a.pos0[b], NoMid{});
 }
 
 int compress_slice(int n_max, int B, int d, int m) {
@@ -329,6 +390,7 @@ hipError_t launch_compress(CompressArgs a, hipStream_t s) {
   int gx;
   size_t shm = 0;
   a.ds = a.d;
+  a.rope_r = pow((double)a.theta, -2.0 / (double)a.d);
   if (a.m <= kSmallM) {
     const int RP = kCompressThreads / (a.d / 8);
     gx = (n_max + RP - 1) / RP;
@@ -389,40 +451,48 @@ __device__ __forceinline__ void insert_block(const InsertArgs& a, int b, float* 
   const int n = fold ? clampi(a.c.ntok[b], 0, a.c.max_ntok) : 1;
   if (n == 0) return;  // no open group: nothing to write
   const int E0 = a.e0[b];
-  const int row = a.c.pos0[b] / m - E0;  // the open entry's row in its page
+  const int p0 = a.c.pos0[b];
+  const int row = p0 / m - E0;  // the open entry's row in its page
   if (row < 0 || row >= epp) return;
   const int lb = E0 / epp;
   if (lb < 0 || lb >= a.bts) return;
   const int phys = a.bt[(int64_t)b * a.bts + lb];  // loaded now, used after the fold
+  const bool page_ok = phys >= 0 && phys < a.dst.num_pages;
+  // an fp8 page's current scale, in flight during the fold
+  const float s_prev = a.dst.dtype == HCA_FP8_E4M3 && page_ok ? reinterpret_cast<const float*>(a.dst.scales)[phys] : 1.0f;
   const float* st = a.stage + (int64_t)b * a.ss;  // the page's rows in staging
   const int d4 = d / 4;
   const f32x4* st4 = reinterpret_cast<const f32x4*>(st);
   const int old4 = row * d4, new4 = old4 + d4;  // float4 groups before / through the new row
   // an fp8 page that fits kPageRegs float4 per thread and needs the amax of
   // all its rows (a rewrite, or a re-folded open entry): its earlier rows are
-  // loaded now, in flight during the fold
+  // loaded into registers right after the fold's own loads are issued, and
+  // stay in flight while the fold computes
   constexpr int kPageRegs = 32;
   const bool in_regs = a.dst.dtype == HCA_FP8_E4M3 && (a.append == 0 || m > 1) &&
                        epp * d4 <= kPageRegs * kCompressThreads;
   f32x4 pv[kPageRegs];
-  if (in_regs) {
+  auto load_page = [&]() {
+    if (in_regs) {
 #pragma unroll
-    for (int k = 0; k < kPageRegs; ++k) {
-      const int i = threadIdx.x + k * kCompressThreads;
-      pv[k] = i < old4 ? st4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < kPageRegs; ++k) {
+        const int i = threadIdx.x + k * kCompressThreads;
+        pv[k] = i < old4 ? st4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
-  }
+  };
   if (fold) {
     CompressArgs c = a.c;
     c.out = a.stage + (int64_t)row * d;
     c.os = a.ss;
-    compress_block(c, b, 0, 1, row_s);
+    compress_block(c, b, 0, 1, row_s, n, p0, load_page);
   } else {
+    load_page();
     for (int i = threadIdx.x; i < d4; i += kCompressThreads)
       reinterpret_cast<f32x4*>(row_s)[i] = st4[old4 + i];
   }
   __syncthreads();
-  if (phys < 0 || phys >= a.dst.num_pages) return;
+  if (!page_ok) return;
   const f32x4* row4 = reinterpret_cast<const f32x4*>(row_s);
 
   if (in_regs) {
@@ -440,7 +510,7 @@ __device__ __forceinline__ void insert_block(const InsertArgs& a, int b, float* 
     amx = ins_block_max(amx, red_s);
     const float s = amx > 0.0f ? amx / 448.0f : 1.0f;
     // append: the earlier rows' codes stand if the page scale is unchanged
-    const bool all = a.append == 0 || row == 0 || scales[phys] != s;
+    const bool all = a.append == 0 || row == 0 || s_prev != s;
     if (all) {
       const int tot4 = epp * d4;
 #pragma unroll
@@ -461,7 +531,7 @@ __device__ __forceinline__ void insert_block(const InsertArgs& a, int b, float* 
     bool full = a.append == 0 || row == 0 || m > 1;
     float s = 1.0f;
     if (!full) {
-      const float s_old = scales[phys];
+      const float s_old = s_prev;
       if (!(s_old > 0.0f) || s_old == 1.0f || am / 448.0f > s_old) full = true;
       else s = s_old;
     }
@@ -560,7 +630,10 @@ __global__ __launch_bounds__(kCompressThreads) void insert_kernel(InsertJobs j) 
 
 hipError_t launch_insert(InsertJobs j, int B, hipStream_t s) {
   if (B == 0 || j.n == 0) return hipSuccess;
-  for (int i = 0; i < j.n; ++i) j.job[i].c.ds = compress_slice(1, B, j.job[i].c.d, j.job[i].c.m);
+  for (int i = 0; i < j.n; ++i) {
+    j.job[i].c.ds = compress_slice(1, B, j.job[i].c.d, j.job[i].c.m);
+    j.job[i].c.rope_r = pow((double)j.job[i].c.theta, -2.0 / (double)j.job[i].c.d);
+  }
   hipLaunchKernelGGL(insert_kernel, dim3(B, j.n), dim3(kCompressThreads), kCompressShm, s, j);
   return hipGetLastError();
 }

@@ -88,9 +88,17 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // RoPE of pair i (dims 2i, 2i+1) at integer position pos: angle pos * theta^(-2i/d),
 // reduced modulo 2*pi in fp64 before the fp32 sine/cosine (positions reach 2^20,
-// where an fp32 angle would be off by ~0.06 rad).
-__device__ __forceinline__ double rope_inv_freq(int i, int d, float theta) {
-  return pow((double)theta, -2.0 * (double)i / (double)d);
+// where an fp32 angle would be off by ~0.06 rad).  theta^(-2i/d) is r^i with
+// r = theta^(-2/d) taken once on the host in fp64, raised by binary powering
+// (at most 22 fp64 multiplies for i < 2048; relative error about i ulp of r,
+// which moves an angle at position 2^20 by well under 1e-6 rad).
+__device__ __forceinline__ double rope_inv_freq(int i, double r) {
+  double acc = 1.0, p = r;
+  for (int k = i; k > 0; k >>= 1) {
+    acc *= (k & 1) ? p : 1.0;
+    p *= p;
+  }
+  return acc;
 }
 __device__ __forceinline__ void rope_cs(double pos, double inv_freq, float& c, float& s) {
   const double twopi_hi = 6.283185307179586232;

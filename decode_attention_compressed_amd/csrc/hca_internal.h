@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "hca.h"
+#include "indexer_internal.h"
 
 namespace hca {
 
@@ -16,6 +17,7 @@ struct CompressArgs {
   int B, max_ntok, d, m;
   int ov;  // overlap: tokens of the previous group in each window (rows -ov .. -1), m <= kSmallM when > 0
   float theta;
+  double rope_r;  // theta^(-2/d) in fp64 (set by the launcher)
   const float* gamma; float eps;  // RMS normalisation of each entry before its rotation (gamma null: none)
   float* out; int64_t os;
   int ds;  // dims per block slice (set by the launcher)
@@ -64,26 +66,8 @@ struct GatherArgs {
 };
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 
-// indexer workspace layout (all offsets 256-byte aligned)
-struct IndexerWs {
-  size_t scores, hist, cand, bitmap, counters, cand_counts, total;
-  int n_max;  // max entries per sequence
-};
-IndexerWs indexer_ws_layout(int B, int max_seq_len, int m, int k);
-constexpr int kHistBins = 4096;  // top 12 bits of the score key
-constexpr int kHistCopies = 16;  // per-sequence histogram copies the score blocks spread over
-
-struct IndexerArgs {
-  const uint16_t* q; const float* w; int HI;
-  hca_paged_cache keys;
-  const int32_t* bt; int bts;
-  const int32_t* lens;
-  int B, max_len, m, k;
-  int32_t* out_idx; int32_t* out_n;
-  unsigned char* ws; IndexerWs lay;
-};
-hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
-hipError_t launch_indexer_score(const IndexerArgs& a, hipStream_t s);
+// the indexer's arguments and launchers (their own header: the indexer
+// source depends on nothing else here)
 
 // attention workspace: per (sequence, split, head) partial (m, l) and o[d]
 struct AttnPlan {
@@ -104,6 +88,7 @@ struct AttnArgs {
   const int32_t* lens; int B, max_len, m, window;
   const int32_t* sel; const int32_t* sel_n; int k;
   float scale, theta;
+  double rope_r;  // theta^(-2/d) in fp64 (set by the launcher)
   float* out; float* lse;
   uint8_t* out8; float* out8_scale;  // fp8 form of the output (null: none)
   unsigned char* ws; AttnPlan plan;

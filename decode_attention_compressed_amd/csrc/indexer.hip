@@ -24,7 +24,7 @@
 // writes its chunk's kept indices in ascending order.  The histogram copies are left zeroed for the next call; every
 // other part of the workspace is overwritten before it is read.
 #include "hca_common.h"
-#include "hca_internal.h"
+#include "indexer_internal.h"
 
 namespace hca {
 

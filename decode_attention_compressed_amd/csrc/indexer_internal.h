@@ -1,0 +1,33 @@
+// Arguments, workspace layout and launchers of the indexer kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "hca.h"
+
+namespace hca {
+
+// indexer workspace layout (all offsets 256-byte aligned)
+struct IndexerWs {
+  size_t scores, hist, cand, bitmap, counters, cand_counts, total;
+  int n_max;  // max entries per sequence
+};
+IndexerWs indexer_ws_layout(int B, int max_seq_len, int m, int k);
+constexpr int kHistBins = 4096;  // top 12 bits of the score key
+constexpr int kHistCopies = 16;  // per-sequence histogram copies the score blocks spread over
+
+struct IndexerArgs {
+  const uint16_t* q; const float* w; int HI;
+  hca_paged_cache keys;
+  const int32_t* bt; int bts;
+  const int32_t* lens;
+  int B, max_len, m, k;
+  int32_t* out_idx; int32_t* out_n;
+  unsigned char* ws; IndexerWs lay;
+};
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
+hipError_t launch_indexer_score(const IndexerArgs& a, hipStream_t s);
+
+}  // namespace hca
