@@ -11,8 +11,9 @@ K=V dim 512 in fp8 E4M3 pages with a per-page fp32 scale, 64 query heads, a
 and reported on its own.
 
 A step is one decode step of the whole stack for the batch: per layer the
-decode update (re-fold of the open group's window -- 8 tokens at stride 4 for
-c4a, the 128-token group for c128a -- with its RMSNorm and RoPE, and its page, the window insert of the new token and its page, the open indexer page:
+decode update (the open group's entry -- c4a: re-folded over its 8-token
+window at stride 4; c128a: the newest token folded into the group's running
+fold state -- with its RMSNorm and RoPE, and its page, the window insert of the new token and its page, the open indexer page:
 one kv_compress_insert_jobs launch), then indexer_topk (c4a) and
 paged_hybrid_decode, whose output is delivered as fp8 rows with a per-row
 scale; layers stay in order.  The step is captured once in a HIP graph and replayed; `value` is
@@ -117,8 +118,11 @@ def update_bytes(kind, B, d, d_idx=128):
     """Bytes moved by the decode update of one layer while page scales hold
     (open group, open page, window page, open indexer page)."""
     m, epp, s = kind.m, 256 // kind.m, kind.slots
-    b = s * d * 2 + s * 4 + d * 4  # the window's ring tokens + logits, entry write
-    b += (epp - 1) * d * 4 + d + 8  # open page: earlier staging rows (its amax), the row's codes, scale
+    if m > 16:  # the newest token + logit, the running fold state read and written, entry write
+        b = d * 2 + 4 + 2 * (4 + d) * 4 + d * 4
+    else:  # the window's ring tokens + logits, entry write
+        b = s * d * 2 + s * 4 + d * 4
+    b += 16 + d + 8  # open page: its header (amax of the closed rows), the row's codes, scale
     b += d * 2 + 4 + d * 4 + d + 8  # window token + logit, its staging row, its codes, scale
     if kind.topk is not None:
         b += d_idx * 4 + d_idx // 2 + d_idx // 32  # open indexer row: staging, codes, scales
@@ -187,6 +191,18 @@ def build_state(w, n_layers, torch, hca, gen, log):
         lay.pos0 = dev(np.full(B, g_open * m, np.int32))
         lay.ntok = dev(np.full(B, L - g_open * m, np.int32))
         lay.e0 = dev(np.full(B, e_open0, np.int32))
+        # the entries' update state: the open page's header (the amax of its
+        # closed rows) and, for groups of more than 16 tokens, a running fold
+        # state, so an update folds only the newest token; that one is brought
+        # to the state after the open group's tokens but the newest (what the
+        # previous step left) by an update call with one token fewer
+        lay.fstate = torch.zeros((B, 4 + (2 * (4 + d) if m > 16 else 0)), dtype=torch.float32, device="cuda")
+        if m > 16:
+            if L - g_open * m >= 2:
+                hca.kv_compress_insert(lay.ring_x[:, o:], lay.ring_z[:, o:], beta, lay.pos0,
+                                       dev(np.full(B, L - g_open * m - 1, np.int32)), m, w.theta, lay.stage, lay.e0,
+                                       table, lay.kv, append=False, norm_gamma=lay.gamma, overlap=o,
+                                       fold_state=lay.fstate)
         lay.ne = dev(np.full(B, N - e_open0, np.int32))
         del ent
         # window pages: rows of the blocks that overlap [L-W, L)
@@ -252,7 +268,7 @@ def decode_step(w, layers, shared, ws_idx, ws_att, hca, update=True, attend=True
                                    append=True),
                     hca.insert_job(lay.stage, lay.pos0, lay.e0, table, lay.kv, m, x=lay.x_open, gate_logit=lay.z_open,
                                    pos_bias=lay.beta, ntok=lay.ntok, rope_theta=w.theta, append=True,
-                                   norm_gamma=lay.gamma, overlap=kind.overlap)]
+                                   norm_gamma=lay.gamma, overlap=kind.overlap, fold_state=lay.fstate)]
             if kind.topk is not None:
                 jobs.append(hca.insert_job(lay.istage, lay.pos0, lay.e0, table, lay.idx, m, append=True))
             hca.kv_compress_insert_jobs(jobs, w.B)

@@ -55,7 +55,7 @@ class CInsertJob(ctypes.Structure):
                 ("rope_theta", ctypes.c_float),
                 ("norm_gamma", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("stage", ctypes.c_void_p), ("stage_stride_b", ctypes.c_int64), ("e0", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("bt_stride", ctypes.c_int32), ("dst", CPagedCache),
-                ("append", ctypes.c_int32)]
+                ("append", ctypes.c_int32), ("fold_state", ctypes.c_void_p), ("fold_state_stride_b", ctypes.c_int64)]
 
 
 _lib = None
@@ -76,7 +76,7 @@ def lib() -> ctypes.CDLL:
         L.kv_compress.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F32, _P, _F32, _P,
                                   _I64, _P]
         L.kv_compress_insert.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _F32, _P, _F32, _P, _I64,
-                                         _P, _P, _I32, CPagedCache, _I32, _P]
+                                         _P, _P, _I32, CPagedCache, _I32, _P, _I64, _P]
         L.kv_compress_insert_jobs.argtypes = [ctypes.POINTER(CInsertJob), _I32, _I32, _P]
         L.kv_quantize_page_workspace.argtypes = [_I32, _I32, CPagedCache]
         L.kv_quantize_page_workspace.restype = _SZ
@@ -171,29 +171,32 @@ def kv_compress(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, 
 
 def kv_compress_insert(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, stage, e0, block_table,
                        dst: PagedCache, append: bool = False, stream=None, norm_gamma=None, norm_eps: float = 1e-6,
-                       overlap: int = 0):
+                       overlap: int = 0, fold_state=None):
     """Decode-step update of one pool in one launch: x bf16 [B, m, d] (the open
     group's tokens); gate_logit f32 [B, m]; pos_bias f32 [m]; pos0, ntok, e0
     int32 [B]; stage f32 [B, epp, d] (the open page's staging); block_table
     int32 [B, nb]; norm_gamma f32 [d] or None; with an overlap, x and gate_logit
-    point at row `overlap` of rings of overlap + m rows."""
+    point at row `overlap` of rings of overlap + m rows; fold_state f32 [B, S] or None, the update
+    state (S >= 4: the open page's closed-rows amax; + 2 * (4 + d) running fold states for m > 16)."""
     B = x.shape[0]
     _check(lib().kv_compress_insert(_ptr(x), x.stride(0), _ptr(gate_logit), gate_logit.stride(0), _ptr(pos_bias),
                                     _ptr(pos0), _ptr(ntok), B, m, overlap, rope_theta, _ptr(norm_gamma), norm_eps,
                                     _ptr(stage), stage.stride(0), _ptr(e0), _ptr(block_table),
-                                    block_table.stride(0), dst.c(), 1 if append else 0, _stream(stream)),
+                                    block_table.stride(0), dst.c(), 1 if append else 0, _ptr(fold_state),
+                                    0 if fold_state is None else fold_state.stride(0), _stream(stream)),
            "kv_compress_insert")
 
 
 def insert_job(stage, pos0, e0, block_table, dst: PagedCache, m: int, x=None, gate_logit=None, pos_bias=None,
                ntok=None, rope_theta: float = 0.0, append: bool = False, norm_gamma=None,
-               norm_eps: float = 1e-6, overlap: int = 0) -> "CInsertJob":
+               norm_eps: float = 1e-6, overlap: int = 0, fold_state=None) -> "CInsertJob":
     """One job of kv_compress_insert_jobs (x None: the open row is already in stage).
     The tensors must stay alive until the call that takes the job is enqueued."""
     return CInsertJob(_ptr(x), 0 if x is None else x.stride(0), _ptr(gate_logit),
                       0 if gate_logit is None else gate_logit.stride(0), _ptr(pos_bias), _ptr(pos0), _ptr(ntok), m,
                       overlap, rope_theta, _ptr(norm_gamma), norm_eps, _ptr(stage), stage.stride(0), _ptr(e0),
-                      _ptr(block_table), block_table.stride(0), dst.c(), 1 if append else 0)
+                      _ptr(block_table), block_table.stride(0), dst.c(), 1 if append else 0, _ptr(fold_state),
+                      0 if fold_state is None else fold_state.stride(0))
 
 
 def kv_compress_insert_jobs(jobs, B: int, stream=None):

@@ -97,9 +97,14 @@ hca_status make_insert(const hca_insert_job& j, int32_t B, InsertArgs& out) {
   if (!aligned(j.stage, 16) || j.stage_stride_b % 4 != 0) return HCA_ERR_INVALID;
   if (B > 1 && j.stage_stride_b < (int64_t)j.dst.epp * d) return HCA_ERR_INVALID;
   if (fold && B > 1 && (j.x_stride_b < (int64_t)j.m * d || j.z_stride_b < j.m)) return HCA_ERR_INVALID;
+  const bool state = fold && j.fold_state != nullptr;
+  const int64_t state_floats = kPageHead + (j.m > kSmallM ? 2 * (int64_t)(kFoldStateHead + d) : 0);
+  if (state && (!aligned(j.fold_state, 16) || j.fold_state_stride_b % 4 != 0)) return HCA_ERR_INVALID;
+  if (state && B > 1 && j.fold_state_stride_b < state_floats) return HCA_ERR_INVALID;
   out = InsertArgs{CompressArgs{j.x, j.x_stride_b, j.gate_logit, j.z_stride_b, j.pos_bias, j.pos0, j.ntok, B, j.m, d,
                                 j.m, fold ? j.overlap : 0, j.rope_theta, 0.0, j.norm_gamma, j.norm_eps, nullptr, 0},
-                   j.stage, j.stage_stride_b, j.e0, j.block_table, j.bt_stride, j.dst, j.append};
+                   j.stage, j.stage_stride_b, j.e0, j.block_table, j.bt_stride, j.dst, j.append,
+                   state ? j.fold_state : nullptr, j.fold_state_stride_b};
   return HCA_OK;
 }
 }  // namespace
@@ -110,13 +115,14 @@ hca_status kv_compress_insert(const uint16_t* x, int64_t x_stride_b, const float
                               const float* pos_bias, const int32_t* pos0, const int32_t* ntok, int32_t B, int32_t m,
                               int32_t overlap, float rope_theta, const float* norm_gamma, float norm_eps, float* stage,
                               int64_t stage_stride_b, const int32_t* e0, const int32_t* block_table, int32_t bt_stride,
-                              hca_paged_cache dst, int32_t append, void* stream) {
+                              hca_paged_cache dst, int32_t append, float* fold_state, int64_t fold_state_stride_b,
+                              void* stream) {
   if (B < 0) return HCA_ERR_INVALID;
   if (!x) return HCA_ERR_INVALID;  // this entry point always folds
-  const hca_insert_job j{x,        x_stride_b,     gate_logit, z_stride_b,  pos_bias,  pos0,
+  const hca_insert_job j{x,        x_stride_b,     gate_logit, z_stride_b,  pos_bias,   pos0,
                          ntok,     m,              overlap,    rope_theta,  norm_gamma, norm_eps,
-                         stage,    stage_stride_b, e0,         block_table, bt_stride, dst,
-                         append};
+                         stage,    stage_stride_b, e0,         block_table, bt_stride,  dst,
+                         append,   fold_state,     fold_state_stride_b};
   InsertJobs jobs{};
   const hca_status st = make_insert(j, B, jobs.job[0]);
   if (st != HCA_OK || B == 0) return st;

@@ -174,7 +174,7 @@ struct NoMid {
 
 template <int PATHS = 3, typename Mid = NoMid>
 __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int bx, int gx, float* lds_row, int n,
-                                               int p0, Mid&& mid) {
+                                               int p0, Mid&& mid, float* state_out = nullptr) {
   const int TD = a.d >> 3;              // threads across the dims of a row
   const int RP = kCompressThreads / TD; // row groups
   const int li = threadIdx.x % TD;
@@ -315,28 +315,40 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
       for (int c = 0; c < 8; ++c) acc_s[gs * DS + ls * 8 + c] = acc[c];
     }
     __syncthreads();
-    // one thread per dim pair of the slice: sum the row groups, normalise, rotate
+    // one thread per dim pair of the slice: sum the row groups (the fold's
+    // weighted sums, which a fold state keeps as they are), normalise, rotate.
+    // A pair's normalised values are left in row group 0 of acc_s: each
+    // thread reads and writes only its own pairs' columns.
     const float inv_tot = 1.0f / tot;
     const double pos = (double)p0 + (double)t0;
-    float rs = 1.0f;
-    if (a.gamma != nullptr) {
-      // the entry's sum of squares (the slice is the whole row, DS = d): the
-      // pair sums are left in row group 0 of acc_s (each thread reads and
-      // writes only its own pairs' columns), then reduced over the block
-      float ss = 0.0f;
-      for (int t = threadIdx.x; t < DS / 2; t += kCompressThreads) {
-        float e0 = 0.0f, e1 = 0.0f;
-        for (int g = 0; g < RS; ++g) {
-          e0 += acc_s[g * DS + 2 * t];
-          e1 += acc_s[g * DS + 2 * t + 1];
-        }
-        e0 *= inv_tot;
-        e1 *= inv_tot;
-        acc_s[2 * t] = e0;
-        acc_s[2 * t + 1] = e1;
-        ss = fmaf(e0, e0, ss);
-        ss = fmaf(e1, e1, ss);
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kGainPairs; ++k) {
+      const int t = threadIdx.x + kCompressThreads * k;
+      if (t >= DS / 2) break;
+      float e0 = 0.0f, e1 = 0.0f;
+      for (int g = 0; g < RS; ++g) {
+        e0 += acc_s[g * DS + 2 * t];
+        e1 += acc_s[g * DS + 2 * t + 1];
       }
+      if (state_out != nullptr) {
+        state_out[kFoldStateHead + base + 2 * t] = e0;
+        state_out[kFoldStateHead + base + 2 * t + 1] = e1;
+      }
+      e0 *= inv_tot;
+      e1 *= inv_tot;
+      acc_s[2 * t] = e0;
+      acc_s[2 * t + 1] = e1;
+      ss = fmaf(e0, e0, ss);
+      ss = fmaf(e1, e1, ss);
+    }
+    if (state_out != nullptr && threadIdx.x == 0) {
+      state_out[0] = (float)r;
+      state_out[1] = mx;
+      state_out[2] = tot;
+    }
+    float rs = 1.0f;
+    if (a.gamma != nullptr) {  // the entry's sum of squares (the slice is the whole row, DS = d)
       ss = wave_sum(ss);
       if ((threadIdx.x & 63) == 0) red_s[threadIdx.x >> 6] = ss;
       __syncthreads();
@@ -347,17 +359,10 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
     for (int k = 0; k < kGainPairs; ++k) {
       const int t = threadIdx.x + kCompressThreads * k;
       if (t >= DS / 2) break;
-      float e0 = 0.0f, e1 = 0.0f;
-      if (a.gamma != nullptr) {  // the slice is the whole row (base = 0)
-        e0 = acc_s[2 * t] * rs * gpair[k].x;
-        e1 = acc_s[2 * t + 1] * rs * gpair[k].y;
-      } else {
-        for (int g = 0; g < RS; ++g) {
-          e0 += acc_s[g * DS + 2 * t];
-          e1 += acc_s[g * DS + 2 * t + 1];
-        }
-        e0 *= inv_tot;
-        e1 *= inv_tot;
+      float e0 = acc_s[2 * t], e1 = acc_s[2 * t + 1];
+      if (a.gamma != nullptr) {  // base = 0
+        e0 *= rs * gpair[k].x;
+        e1 *= rs * gpair[k].y;
       }
       float c, sn;
       rope_cs(pos, rope_inv_freq(base / 2 + t, a.rope_r), c, sn);
@@ -445,6 +450,85 @@ __device__ __forceinline__ float amax4(const f32x4 v) {
   return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 }
 
+// One more token into a running fold state (groups of more than kSmallM
+// tokens, whose re-fold reads the whole group): `prev` holds the state after
+// tokens 0 .. n-2 of the open group, `next` receives it after token n-1, and
+// the entry (weighted sums over the sum of weights, then the normalisation and
+// rotation of every fold) goes to the staging row and row_s.  If `prev` is not
+// the state after n-1 tokens (a group's first token, or a state the caller has
+// not kept), the group is re-folded whole and `next` written from that fold.
+// One row group does the row; every thread calls mid() once.
+template <typename Mid>
+__device__ __forceinline__ void state_fold(const CompressArgs& a, int b, int n, int p0, const float* prev, float* next,
+                                           float* row_s, Mid&& mid) {
+  const int TD = a.d >> 3;
+  const int RP = kCompressThreads / TD;
+  const int li = threadIdx.x % TD;
+  const int gi = threadIdx.x / TD;
+  const bool live = gi == 0;
+  const int t = n - 1;  // the newest token
+  // the newest token, its logit and the previous state are loaded first
+  const u32x4 raw = live && t >= 0 ? *reinterpret_cast<const u32x4*>(a.x + (int64_t)b * a.xs + (int64_t)t * a.d + li * 8)
+                                   : u32x4{0u, 0u, 0u, 0u};
+  const float zt = t >= 0 ? a.z[(int64_t)b * a.zs + t] : 0.0f;
+  const float bt = t >= 0 ? a.beta[t] : 0.0f;
+  f32x4 A0 = {0.f, 0.f, 0.f, 0.f}, A1 = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    A0 = reinterpret_cast<const f32x4*>(prev + kFoldStateHead + li * 8)[0];
+    A1 = reinterpret_cast<const f32x4*>(prev + kFoldStateHead + li * 8)[1];
+  }
+  const float cnt = prev[0], M = prev[1], S = prev[2];
+  float gam[8] = {1, 1, 1, 1, 1, 1, 1, 1};
+  if (a.gamma != nullptr && live) {
+    const f32x4 g0 = reinterpret_cast<const f32x4*>(a.gamma + li * 8)[0];
+    const f32x4 g1 = reinterpret_cast<const f32x4*>(a.gamma + li * 8)[1];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) { gam[c] = g0[c]; gam[4 + c] = g1[c]; }
+  }
+  if (!(n >= 2 && cnt == (float)(n - 1) && S > 0.0f)) {
+    CompressArgs c = a;
+    compress_block(c, b, 0, 1, row_s, n, p0, mid, next);
+    return;
+  }
+  mid();
+  double inv[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) inv[p] = rope_inv_freq(li * 4 + p, a.rope_r);
+  const float at = zt + bt;
+  const float M2 = fmaxf(M, at);
+  const float co = expf(M - M2), cn = expf(at - M2);
+  const float S2 = fmaf(S, co, cn);
+  float A[8] = {A0[0], A0[1], A0[2], A0[3], A1[0], A1[1], A1[2], A1[3]};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    A[2 * q] = fmaf(A[2 * q], co, cn * u2f(raw[q] << 16));
+    A[2 * q + 1] = fmaf(A[2 * q + 1], co, cn * u2f(raw[q] & 0xFFFF0000u));
+  }
+  if (live) {
+    reinterpret_cast<f32x4*>(next + kFoldStateHead + li * 8)[0] = f32x4{A[0], A[1], A[2], A[3]};
+    reinterpret_cast<f32x4*>(next + kFoldStateHead + li * 8)[1] = f32x4{A[4], A[5], A[6], A[7]};
+  }
+  if (threadIdx.x == 0) {
+    next[0] = (float)n;
+    next[1] = M2;
+    next[2] = S2;
+  }
+  const float inv_tot = 1.0f / S2;
+  float e[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) e[c] = A[c] * inv_tot;
+  if (a.gamma != nullptr) {
+    __shared__ float sq_s[kCompressThreads];
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ss = fmaf(e[c], e[c], ss);
+    const float rs = 1.0f / sqrtf(row_group_sum(live ? ss : 0.0f, TD, RP, gi, sq_s) / (float)a.d + a.eps);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) e[c] *= rs * gam[c];
+  }
+  if (live) rope_store8(a.out + (int64_t)b * a.os + li * 8, row_s + li * 8, e, (double)p0, inv);
+}
+
 __device__ __forceinline__ void insert_block(const InsertArgs& a, int b, float* row_s, float* red_s) {
   const int m = a.c.m, d = a.c.d, epp = a.dst.epp;
   const bool fold = a.c.x != nullptr;  // else the open row is already in staging
@@ -464,30 +548,26 @@ __device__ __forceinline__ void insert_block(const InsertArgs& a, int b, float* 
   const int d4 = d / 4;
   const f32x4* st4 = reinterpret_cast<const f32x4*>(st);
   const int old4 = row * d4, new4 = old4 + d4;  // float4 groups before / through the new row
-  // an fp8 page that fits kPageRegs float4 per thread and needs the amax of
-  // all its rows (a rewrite, or a re-folded open entry): its earlier rows are
-  // loaded into registers right after the fold's own loads are issued, and
-  // stay in flight while the fold computes
-  constexpr int kPageRegs = 32;
-  const bool in_regs = a.dst.dtype == HCA_FP8_E4M3 && (a.append == 0 || m > 1) &&
-                       epp * d4 <= kPageRegs * kCompressThreads;
-  f32x4 pv[kPageRegs];
-  auto load_page = [&]() {
-    if (in_regs) {
-#pragma unroll
-      for (int k = 0; k < kPageRegs; ++k) {
-        const int i = threadIdx.x + k * kCompressThreads;
-        pv[k] = i < old4 ? st4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  };
+  // the update state: a page header (how many of the open page's rows, and
+  // the amax of those rows, which no longer change once their groups are
+  // complete) read now, in flight during the fold; then, for groups of more
+  // than kSmallM tokens, the two running fold states
+  const bool refold8 = a.dst.dtype == HCA_FP8_E4M3 && a.append != 0 && m > 1;
+  float* hdr = a.state != nullptr ? a.state + (int64_t)b * a.sts : nullptr;
+  const float hc = refold8 && hdr != nullptr ? hdr[0] : -1.0f;
+  const float ha = refold8 && hdr != nullptr ? hdr[1] : 0.0f;
   if (fold) {
     CompressArgs c = a.c;
     c.out = a.stage + (int64_t)row * d;
     c.os = a.ss;
-    compress_block(c, b, 0, 1, row_s, n, p0, load_page);
+    if (m > kSmallM && hdr != nullptr) {
+      float* sb = hdr + kPageHead;
+      const int sl = kFoldStateHead + d;
+      state_fold(c, b, n, p0, sb + ((n - 1) & 1) * sl, sb + (n & 1) * sl, row_s, NoMid{});
+    } else {
+      compress_block(c, b, 0, 1, row_s, n, p0, NoMid{});
+    }
   } else {
-    load_page();
     for (int i = threadIdx.x; i < d4; i += kCompressThreads)
       reinterpret_cast<f32x4*>(row_s)[i] = st4[old4 + i];
   }
@@ -495,48 +575,53 @@ __device__ __forceinline__ void insert_block(const InsertArgs& a, int b, float* 
   if (!page_ok) return;
   const f32x4* row4 = reinterpret_cast<const f32x4*>(row_s);
 
-  if (in_regs) {
+  if (a.dst.dtype == HCA_FP8_E4M3) {
     float* scales = reinterpret_cast<float*>(a.dst.scales);
     uint32_t* dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.dst.codes) + (int64_t)phys * epp * d);
-    // the new row joins the registers of the threads that hold its slots
-#pragma unroll
-    for (int k = 0; k < kPageRegs; ++k) {
-      const int i = threadIdx.x + k * kCompressThreads;
-      if (i >= old4 && i < new4) pv[k] = row4[i - old4];
-    }
-    float amx = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kPageRegs; ++k) amx = fmaxf(amx, amax4(pv[k]));
-    amx = ins_block_max(amx, red_s);
-    const float s = amx > 0.0f ? amx / 448.0f : 1.0f;
-    // append: the earlier rows' codes stand if the page scale is unchanged
-    const bool all = a.append == 0 || row == 0 || s_prev != s;
-    if (all) {
-      const int tot4 = epp * d4;
-#pragma unroll
-      for (int k = 0; k < kPageRegs; ++k) {
-        const int i = threadIdx.x + k * kCompressThreads;
-        if (i < tot4) dst[i] = i < new4 ? enc4_e4m3(pv[k], s) : 0u;
-      }
-      if (threadIdx.x == 0) scales[phys] = s;
-    } else {
-      for (int i = threadIdx.x; i < d4; i += kCompressThreads) dst[old4 + i] = enc4_e4m3(row4[i], s);
-    }
-  } else if (a.dst.dtype == HCA_FP8_E4M3) {
-    float* scales = reinterpret_cast<float*>(a.dst.scales);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.dst.codes) + (int64_t)phys * epp * d);
+    constexpr int U = 8;
     float am = 0.0f;
     for (int i = threadIdx.x; i < d4; i += kCompressThreads) am = fmaxf(am, amax4(row4[i]));
     am = ins_block_max(am, red_s);
-    bool full = a.append == 0 || row == 0 || m > 1;
+    bool full = a.append == 0 || row == 0;
     float s = 1.0f;
-    if (!full) {
-      const float s_old = s_prev;
-      if (!(s_old > 0.0f) || s_old == 1.0f || am / 448.0f > s_old) full = true;
-      else s = s_old;
+    if (!full && m == 1) {
+      // a window insert: the new row's scale joins the page's by max
+      if (!(s_prev > 0.0f) || s_prev == 1.0f || am / 448.0f > s_prev) full = true;
+      else s = s_prev;
+    } else if (!full) {
+      // a re-folded open entry: the page max is the closed rows' (from the
+      // header when it holds them, or all but the row that closed when this
+      // group began) joined with the open row's
+      float closed;
+      if (hc == (float)row) {
+        closed = ha;
+      } else if (hc == (float)(row - 1)) {
+        float v = 0.0f;
+        for (int i = threadIdx.x; i < d4; i += kCompressThreads) v = fmaxf(v, amax4(st4[old4 - d4 + i]));
+        closed = fmaxf(ha, ins_block_max(v, red_s));
+      } else {
+        float v = 0.0f;
+        for (int i0 = threadIdx.x; i0 < old4; i0 += U * kCompressThreads) {
+          f32x4 w[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * kCompressThreads;
+            w[u] = i < old4 ? st4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) v = fmaxf(v, amax4(w[u]));
+        }
+        closed = ins_block_max(v, red_s);
+      }
+      if (hdr != nullptr && threadIdx.x == 0) {
+        hdr[0] = (float)row;
+        hdr[1] = closed;
+      }
+      const float amx = fmaxf(closed, am);
+      s = amx > 0.0f ? amx / 448.0f : 1.0f;
+      full = s != s_prev;  // the earlier rows' codes stand while the page scale does
     }
     if (full) {
-      constexpr int U = 8;
       float amx = am;
       for (int i0 = threadIdx.x; i0 < old4; i0 += U * kCompressThreads) {
         f32x4 v[U];
@@ -550,6 +635,10 @@ __device__ __forceinline__ void insert_block(const InsertArgs& a, int b, float* 
       }
       amx = ins_block_max(amx, red_s);
       s = amx > 0.0f ? amx / 448.0f : 1.0f;
+      if (refold8 && hdr != nullptr && threadIdx.x == 0 && row == 0) {
+        hdr[0] = 0.0f;  // a new page: no closed rows yet
+        hdr[1] = 0.0f;
+      }
       const int tot4 = epp * d4;
       for (int i0 = threadIdx.x; i0 < tot4; i0 += U * kCompressThreads) {
         f32x4 v[U];

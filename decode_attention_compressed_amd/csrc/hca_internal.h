@@ -38,7 +38,15 @@ struct InsertArgs {
   const int32_t* bt; int bts;
   hca_paged_cache dst;
   int append;
+  float* state; int64_t sts;  // [B][kPageHead (+ 2 (kFoldStateHead + d) for m > kSmallM)] update states, or null
 };
+// an update state: the open page's header, [0] how many of its rows and [1]
+// their amax (fp8 pages of re-folded entries), [2], [3] unused; then, for
+// groups of more than kSmallM tokens, two running fold states:
+// [0] tokens folded, [1] running max of the logits, [2] running sum of
+// exp(logit - max), [3] unused, then the d running sums of exp(logit - max) * token
+constexpr int kPageHead = 4;
+constexpr int kFoldStateHead = 4;
 constexpr int kMaxInsertJobs = 4;
 struct InsertJobs {
   InsertArgs job[kMaxInsertJobs];

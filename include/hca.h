@@ -176,8 +176,10 @@ hca_status kv_quantize_page(const float* src, int64_t src_stride_b, const int32_
  * 3.1.2: the open group is the rolling residual; section 3.2.1: RoPE, then
  * insertion into the cache) into its row of the open page's f32 staging, and
  * the open page is quantized as kv_quantize_page quantizes it (sections 3.1.1
- * and 3.1.3).  The staging row and the page bytes are identical to those of
- * kv_compress(max_ntok = m) followed by kv_quantize_page on that page.
+ * and 3.1.3).  Without a fold state, the staging row and the page bytes are
+ * identical to those of kv_compress(max_ntok = m) followed by kv_quantize_page
+ * on that page; with one (below), the page bytes are those of kv_quantize_page
+ * on the staging rows.
  *
  * For sequence b the open group has ntok[b] tokens (clamped to [0, m]; 0
  * writes nothing) starting at position pos0[b] (a multiple of m); its entry
@@ -203,13 +205,35 @@ hca_status kv_quantize_page(const float* src, int64_t src_stride_b, const int32_
  *              scale is taken over all rows; for m = 1 it is max(old scale,
  *              the new row's), which is exact because fl32(amax/448) is
  *              monotonic in amax.  The result equals that of append = 0.
+ *   fold_state float [B][S] (16-byte aligned, S % 4 == 0) or NULL: the
+ *              pool's update state per sequence, S >= 4, and S >= 4 + 2 *
+ *              (4 + dst.dim) when m > 16.  Zero-filled is a valid state; the
+ *              caller keeps it with its ring and page (re-zero it when either
+ *              is rewritten otherwise).  Floats 0..3, for fp8 pages in append
+ *              mode with m > 1: how many of the open page's rows, and their
+ *              amax (rows before the open one no longer change), so a call
+ *              reads no earlier staging row while the page scale holds; a
+ *              header that holds the rows before the open one but the last
+ *              is completed from that row, any other is rebuilt from staging.
+ *              Then, for m > 16 (a re-fold reads the whole open group), two
+ *              running fold states of 4 + dim floats (token count, max logit,
+ *              sum of exp(logit - max), unused, exp-weighted token sums): a
+ *              call with ntok = n reads slot (n-1) % 2 and writes slot n % 2,
+ *              folding only the newest token (a repeated call gives the same
+ *              result); where the slot does not hold the state after n-1
+ *              tokens (a new group, a zero-filled state), the group is
+ *              re-folded whole and the state rewritten.  With fold states the
+ *              entry is the same fold up to rounding (the running sums rescale
+ *              as the maximum grows), so it need not match kv_compress bit for
+ *              bit.  Page bytes are the same with or without a state.
  * Calls that write the same page or staging must be ordered by the caller.
  */
 hca_status kv_compress_insert(const uint16_t* x, int64_t x_stride_b, const float* gate_logit, int64_t z_stride_b,
                               const float* pos_bias, const int32_t* pos0, const int32_t* ntok, int32_t B, int32_t m,
                               int32_t overlap, float rope_theta, const float* norm_gamma, float norm_eps, float* stage,
                               int64_t stage_stride_b, const int32_t* e0, const int32_t* block_table,
-                              int32_t bt_stride, hca_paged_cache dst, int32_t append, void* stream);
+                              int32_t bt_stride, hca_paged_cache dst, int32_t append, float* fold_state,
+                              int64_t fold_state_stride_b, void* stream);
 
 /*
  * kv_compress_insert_jobs -- several kv_compress_insert calls over the same B
@@ -242,6 +266,8 @@ typedef struct {
   int32_t bt_stride;
   hca_paged_cache dst;
   int32_t append;
+  float* fold_state; /* NULL: the open group is re-folded whole */
+  int64_t fold_state_stride_b;
 } hca_insert_job;
 hca_status kv_compress_insert_jobs(const hca_insert_job* jobs, int32_t n_jobs, int32_t B, void* stream);
 

@@ -122,13 +122,14 @@ def test_validation_kv_compress():
 def test_validation_kv_compress_insert():
     L = hca.lib()
     ok = dict(x=FAKE, xs=4 * 128, z=FAKE, zs=4, beta=FAKE, pos0=FAKE, ntok=FAKE, B=2, m=4, ov=0, theta=1e6,
-              gam=None, eps=1e-6, st=FAKE, ss=64 * 128, e0=FAKE, bt=FAKE, bts=16, dst=_cache(), app=0)
+              gam=None, eps=1e-6, st=FAKE, ss=64 * 128, e0=FAKE, bt=FAKE, bts=16, dst=_cache(), app=0, fs=None,
+              fss=0)
 
     def call(**kw):
         a = dict(ok, **kw)
         return L.kv_compress_insert(a["x"], a["xs"], a["z"], a["zs"], a["beta"], a["pos0"], a["ntok"], a["B"],
                                     a["m"], a["ov"], a["theta"], a["gam"], a["eps"], a["st"], a["ss"], a["e0"],
-                                    a["bt"], a["bts"], a["dst"], a["app"], None)
+                                    a["bt"], a["bts"], a["dst"], a["app"], a["fs"], a["fss"], None)
 
     assert call(m=3) == 1 and call(m=8) == 1  # the pool's epp must be 256 / m
     assert call(dst=_cache(dim=4096)) == 2
@@ -139,6 +140,13 @@ def test_validation_kv_compress_insert():
     assert call(B=-1) == 1
     assert call(gam=FAKE, eps=-1.0) == 1 and call(gam=ctypes.c_void_p(0x1008)) == 1
     assert call(ov=8) == 1 and call(ov=-2) == 1
+    # update states: aligned, a page header of 4 floats, + two fold states of 4 + d floats when m > 16
+    c128 = dict(m=128, xs=128 * 128, zs=128, ss=2 * 128, dst=_cache(epp=2))
+    assert call(fs=ctypes.c_void_p(0x1004), fss=4 + 2 * 132, **c128) == 1
+    assert call(fs=FAKE, fss=2 * 132, **c128) == 1 and call(fs=FAKE, fss=4 + 2 * 132 + 2, **c128) == 1
+    assert call(fs=FAKE, fss=4 + 2 * 132, B=0, **c128) == 0
+    assert call(fs=FAKE, fss=2) == 1 and call(fs=ctypes.c_void_p(0x1004), fss=4) == 1  # m = 4: the header
+    assert call(fs=FAKE, fss=4, B=0) == 0
     assert call(B=0) == 0 and call(gam=FAKE, B=0) == 0  # nothing to do, nothing launched
 
 

@@ -277,6 +277,8 @@ def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append, norm,
                                  H.to_dev(table[b:b + 1]), pool_f)
     torch.cuda.synchronize()
     ref_rows = hist.astype(np.float64)  # the open pages' rows as the oracle has them
+    # append runs keep an update state (the page header: its closed rows' amax)
+    state = torch.zeros((B, 4 + (2 * (4 + d) if m > 16 else 0)), dtype=torch.float32, device="cuda") if append else None
     stage_u = stage_f.clone()
     pool_u = hca.PagedCache(pool_f.codes.clone(), None if pool_f.scales is None else pool_f.scales.clone(), epp, d,
                             dtype)
@@ -309,7 +311,8 @@ def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append, norm,
         xr, zr = H.to_dev(xb.view(np.int16)), H.to_dev(ring_z)
         xd, zd = xr[:, o:], zr[:, o:]  # rows -o .. -1: the overlap
         hca.kv_compress_insert(xd, zd, H.to_dev(beta), H.to_dev(pos0), H.to_dev(ntok), m, theta, stage_f,
-                               H.to_dev(e0), H.to_dev(table), pool_f, append=append, norm_gamma=gam_d, overlap=o)
+                               H.to_dev(e0), H.to_dev(table), pool_f, append=append, norm_gamma=gam_d, overlap=o,
+                               fold_state=state if m <= 16 else None)
         for b in range(B):  # the two-call path, one sequence at a time (rows differ)
             hca.kv_compress(xd[b:b + 1], zd[b:b + 1], H.to_dev(beta), H.to_dev(pos0[b:b + 1]),
                             H.to_dev(ntok[b:b + 1]), m, theta, stage_u[b:b + 1, int(row[b]):], m, norm_gamma=gam_d,
@@ -344,6 +347,108 @@ def test_compress_insert_matches_two_calls_and_oracle(m, dtype, d, append, norm,
             # against the oracle's quantizer in the kv_quantize_page tests)
             sc = got_f.scales[phys] if dtype == "fp8" else (got_f.scales[phys, : r + 1] if dtype == "fp4" else None)
             assert H.quantized_rows_close(dtype, got_f.codes[phys, : r + 1], sc, ref_rows[b, : r + 1]), (step, b)
+
+
+# Running fold states (groups of more than 16 tokens): each call folds only the
+# newest token into the state it reads and writes the next state; a group's
+# first token, a zero-filled state, or a state the caller did not keep make
+# it re-fold the whole group.  The staging row must match the oracle's entry,
+# the page bytes must be kv_quantize_page's on the same staging rows, and a
+# repeated call must change nothing.
+@pytest.mark.parametrize("m,dtype,d,norm", [(128, "fp8", 512, True), (128, "fp8", 512, False), (32, "bf16", 136, True),
+                                            (64, "fp4", 128, False), (256, "fp8", 256, True)])
+def test_compress_insert_fold_state(m, dtype, d, norm):
+    H.flush(f"compress_insert fold state m={m} {dtype} d={d} norm={norm}")
+    rng = np.random.default_rng(81 + m)
+    epp = 256 // m
+    B, steps, theta = 3, 12, 1e6
+    # seq 0 crosses a group start at its 6th step; seq 1 starts empty; seq 2 mid-group
+    L = np.array([m * 40 - 5, 0, m * 7 + 3], np.int64)
+    nb = int(L.max() + steps) // 256 + 2
+    P = B * nb + 2
+    table = rng.permutation(P)[: B * nb].reshape(B, nb).astype(np.int32)
+    beta = (rng.standard_normal(m) * 0.1).astype(np.float32)
+    gam = rng.uniform(0.5, 1.5, d).astype(np.float32) if norm else None
+    gam_d = H.to_dev(gam) if norm else None
+    stage = torch.zeros((B, epp, d), dtype=torch.float32, device="cuda")
+    pool = hca.PagedCache.empty(P, epp, d, dtype)
+    pool.codes.fill_(0)
+    if pool.scales is not None:
+        pool.scales.fill_(0)
+    state = torch.zeros((B, 4 + 2 * (4 + d)), dtype=torch.float32, device="cuda")  # page header, two fold states
+    # the open groups' tokens so far (their earlier tokens drawn for the starting state)
+    grp_x = [list(rng.standard_normal((int(L[b]) % m, d)).astype(np.float32)) for b in range(B)]
+    grp_z = [list(rng.standard_normal(int(L[b]) % m).astype(np.float32)) for b in range(B)]
+    # earlier rows of each open page: drawn, in staging and quantized into the page
+    ref_rows = np.zeros((B, epp, d))
+    for b in range(B):
+        row = (int(L[b]) // m) % epp
+        if row > 0:
+            h = rng.standard_normal((row, d)).astype(np.float32)
+            ref_rows[b, :row] = h
+            stage[b, :row] = H.to_dev(h)
+            hca.kv_quantize_page(stage[b:b + 1], H.to_dev(np.array([int(L[b]) // m - row], np.int32)),
+                                 H.to_dev(np.array([row], np.int32)), epp, H.to_dev(table[b:b + 1]), pool)
+    check = hca.PagedCache.empty(P, epp, d, dtype)
+    for step in range(steps):
+        L += 1
+        pos0 = (m * ((L - 1) // m)).astype(np.int32)
+        ntok = (L - pos0).astype(np.int32)
+        for b in range(B):
+            if ntok[b] == 1:
+                grp_x[b], grp_z[b] = [], []
+            grp_x[b].append(rng.standard_normal(d).astype(np.float32) * (30.0 if step == 4 else 1.0))
+            grp_z[b].append(np.float32(rng.standard_normal() + (4.0 if step == 9 else 0.0)))  # a new running max
+        ring = np.zeros((B, m, d), np.float32)
+        ring_z = np.zeros((B, m), np.float32)
+        for b in range(B):
+            ring[b, : ntok[b]] = np.stack(grp_x[b])
+            ring_z[b, : ntok[b]] = np.array(grp_z[b])
+        xb = gen.to_bf16_bits(ring)
+        j = pos0 // m
+        e0 = (epp * (j // epp)).astype(np.int32)
+        row = j - e0
+        args = (H.to_dev(xb.view(np.int16)), H.to_dev(ring_z), H.to_dev(beta), H.to_dev(pos0), H.to_dev(ntok), m, theta,
+                stage, H.to_dev(e0), H.to_dev(table), pool)
+        hca.kv_compress_insert(*args, append=True, norm_gamma=gam_d, fold_state=state)
+        torch.cuda.synchronize()
+        if step == 7:  # the same call again: nothing changes
+            snap = (stage.clone(), pool.codes.clone(), None if pool.scales is None else pool.scales.clone(),
+                    state.clone())
+            hca.kv_compress_insert(*args, append=True, norm_gamma=gam_d, fold_state=state)
+            torch.cuda.synchronize()
+            assert torch.equal(stage, snap[0]) and torch.equal(pool.codes, snap[1]) and torch.equal(state, snap[3])
+            if pool.scales is not None:
+                assert torch.equal(pool.scales, snap[2])
+        # kv_quantize_page on the same staging rows gives the same page bytes
+        hca.kv_quantize_page(stage, H.to_dev(e0), H.to_dev((row + 1).astype(np.int32)), epp, H.to_dev(table), check)
+        torch.cuda.synchronize()
+        sf = stage.cpu().numpy()
+        ref_pool = paging.Pool(dtype, P, epp, d)
+        got = H.download_pool(pool, ref_pool)
+        want = H.download_pool(check, ref_pool)
+        for b in range(B):
+            r = int(row[b])
+            ent = compressor.compress(codecs.bf16_decode(xb[b, : ntok[b]]), ring_z[b, : ntok[b]], beta, m, theta,
+                                      pos0=int(pos0[b]), gamma=gam, eps=1e-6)
+            assert H.rel_err_rows(sf[b, r: r + 1], ent[-1:]) <= H.ENTRY_TOL, (step, b)
+            if r == 0:
+                ref_rows[b] = 0.0
+            ref_rows[b, r] = ent[-1]
+            phys = int(table[b, e0[b] // epp])
+            assert np.array_equal(got.codes[phys, : r + 1], want.codes[phys, : r + 1]), (step, b)
+            sc = None
+            if dtype == "fp8":
+                assert got.scales[phys] == want.scales[phys], (step, b)
+                sc = got.scales[phys]
+            elif dtype == "fp4":
+                assert np.array_equal(got.scales[phys, : r + 1], want.scales[phys, : r + 1]), (step, b)
+                sc = got.scales[phys, : r + 1]
+            assert H.quantized_rows_close(dtype, got.codes[phys, : r + 1], sc, ref_rows[b, : r + 1]), (step, b)
+        # the state holds the open groups' token counts
+        st = state.cpu().numpy()
+        for b in range(B):
+            assert st[b, 4 + (int(ntok[b]) % 2) * (4 + d)] == ntok[b], (step, b)
 
 
 def test_compress_insert_jobs_one_launch():
