@@ -436,6 +436,53 @@ def cpu_baseline(w, budget_s=20.0):
     return out
 
 
+# ----------------------------------------------------------------- page-pool packing
+
+
+def pool_packing(w, hca):
+    """The stack's KV kinds packed into size buckets of one arena (host
+    bookkeeping only): buckets, arena bytes, and the host time to give every
+    sequence of every layer its pages (one allocation per layer, kind and
+    sequence, the shared-prefix pages found by key), then release them."""
+    kinds, count = [], []
+    nb = -(-w.L // 256)
+    for k in w.layers:
+        main = (k.m, w.d, w.kv_dtype)
+        if main not in kinds:
+            kinds.append(main)
+            count.append(0)
+        count[kinds.index(main)] += nb
+        if k.topk is not None:
+            ik = (k.m, k.d_idx, k.idx_dtype)
+            if ik not in kinds:
+                kinds.append(ik)
+                count.append(0)
+            count[kinds.index(ik)] += nb
+    win = (1, w.d, w.kv_dtype)
+    kinds.append(win)
+    count.append(2 * len(w.layers))  # the blocks that overlap the window
+    probe = hca.PagePool(kinds, [1] * len(kinds))
+    cap = [0] * probe.n_buckets
+    for i, c in enumerate(count):
+        cap[probe.bucket_of(i)] += c * w.B
+    pool = hca.PagePool(kinds, cap)
+    t0 = time.perf_counter()
+    held = []
+    for _ in range(w.B):
+        for i, c in enumerate(count):
+            b = pool.bucket_of(i)
+            held.append((b, pool.alloc(b, c)))
+    t1 = time.perf_counter()
+    for b, pages in held:
+        pool.release(b, pages)
+    t2 = time.perf_counter()
+    pages = sum(len(p) for _, p in held)
+    return {"kinds": [f"m={m} d={d} {t}" for m, d, t in kinds], "buckets": probe.n_buckets,
+            "arena_GiB": round(pool.arena_bytes / 2 ** 30, 3),
+            "arena_GiB_per_sequence": round(pool.arena_bytes / 2 ** 30 / w.B, 3),
+            "pages": pages, "alloc_ms": round((t1 - t0) * 1e3, 3), "release_ms": round((t2 - t1) * 1e3, 3)}
+
+
 # ----------------------------------------------------------------- main
 
 
@@ -534,6 +581,7 @@ def main():
         "prefill": {"ms_all_layers": round(pre["ms"], 3), "bytes": int(pre["bytes"]),
                     "GBps": round(pre["bytes"] / (pre["ms"] * 1e-3) / 1e9, 1) if pre["ms"] > 0 else None,
                     "what": "kv_compress + kv_quantize_page over the whole context of every layer"},
+        "page_pool": pool_packing(w, hca),
     }
     print(json.dumps(res))
 

@@ -34,6 +34,8 @@ EXPORTS = (
     "indexer_topk", "paged_hybrid_decode_workspace", "paged_hybrid_decode", "kv_gather",
     "hca_host_e4m3_encode", "hca_host_e2m1_encode", "hca_host_bf16_encode", "hca_probe_decode", "hca_probe_mfma",
     "hca_indexer_score",
+    "hca_page_bytes", "hca_pool_plan", "hca_pool_create", "hca_pool_destroy", "hca_pool_view", "hca_pool_bucket",
+    "hca_pool_alloc", "hca_pool_share", "hca_pool_release", "hca_pool_publish", "hca_pool_lookup", "hca_pool_stats",
 )
 
 
@@ -46,6 +48,10 @@ class HcaError(RuntimeError):
 class CPagedCache(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("num_pages", ctypes.c_int32),
                 ("epp", ctypes.c_int32), ("dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class CKvKind(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int32), ("dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class CInsertJob(ctypes.Structure):
@@ -95,9 +101,22 @@ def lib() -> ctypes.CDLL:
         L.hca_probe_decode.argtypes = [_P, _P, _I32, _I32, _P]
         L.hca_probe_mfma.argtypes = [_P, _P, _P, _I32, _P]
         L.hca_indexer_score.argtypes = [_P, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P]
+        L.hca_page_bytes.argtypes = [CKvKind, _P, _P]
+        L.hca_pool_plan.argtypes = [_P, _I32, _P, _P]
+        L.hca_pool_create.argtypes = [_P, _I32, _P, _P, _P]
+        L.hca_pool_destroy.argtypes = [_P]
+        L.hca_pool_destroy.restype = None
+        L.hca_pool_view.argtypes = [_P, _I32, _P, ctypes.POINTER(CPagedCache)]
+        L.hca_pool_bucket.argtypes = [_P, _I32]
+        L.hca_pool_alloc.argtypes = [_P, _I32, _I32, _P]
+        L.hca_pool_share.argtypes = [_P, _I32, _P, _I32]
+        L.hca_pool_release.argtypes = [_P, _I32, _P, _I32]
+        L.hca_pool_publish.argtypes = [_P, _I32, _I32, ctypes.c_uint64]
+        L.hca_pool_lookup.argtypes = [_P, _I32, ctypes.c_uint64, _P]
+        L.hca_pool_stats.argtypes = [_P, _I32, _P, _P, _P, _P, _P]
         for name in EXPORTS:
             if name not in ("hca_status_string", "hca_version", "indexer_topk_workspace",
-                            "paged_hybrid_decode_workspace", "kv_quantize_page_workspace"):
+                            "paged_hybrid_decode_workspace", "kv_quantize_page_workspace", "hca_pool_destroy"):
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -274,3 +293,102 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+# ----------------------------------------------------------------- page-pool packing
+
+
+def page_bytes(m: int, dim: int, dtype: str):
+    """(code bytes, scale bytes) of one page of a KV kind."""
+    c, sc = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib().hca_page_bytes(CKvKind(m, dim, DTYPES[dtype]), ctypes.byref(c), ctypes.byref(sc)), "hca_page_bytes")
+    return c.value, sc.value
+
+
+class PagePool:
+    """Size buckets of fixed-size pages for several KV kinds in one device arena.
+
+    kinds: [(m, dim, dtype)]; capacity: pages per bucket (bucket_of(kind) maps
+    a kind to its bucket).  `arena_bytes` is what the caller allocates;
+    `view(kind, arena)` is the PagedCache of a kind inside it."""
+
+    def __init__(self, kinds, capacity):
+        self.kinds = list(kinds)
+        arr = (CKvKind * len(self.kinds))(*[CKvKind(m, d, DTYPES[t]) for m, d, t in self.kinds])
+        self._karr = arr
+        kb = (ctypes.c_int32 * len(self.kinds))()
+        nb = ctypes.c_int32(0)
+        _check(lib().hca_pool_plan(arr, len(self.kinds), kb, ctypes.byref(nb)), "hca_pool_plan")
+        self.kind_bucket = list(kb)
+        self.n_buckets = nb.value
+        cap = list(capacity) if hasattr(capacity, "__len__") else [int(capacity)] * self.n_buckets
+        carr = (ctypes.c_int32 * max(1, self.n_buckets))(*cap)
+        ab = ctypes.c_size_t(0)
+        h = ctypes.c_void_p(0)
+        _check(lib().hca_pool_create(arr, len(self.kinds), carr, ctypes.byref(ab), ctypes.byref(h)), "hca_pool_create")
+        self._h = h
+        self.arena_bytes = ab.value
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            try:
+                _lib.hca_pool_destroy(h)
+            except Exception:  # interpreter shutdown
+                pass
+            self._h = None
+
+    def bucket_of(self, kind: int) -> int:
+        return self.kind_bucket[kind]
+
+    def view(self, kind: int, arena) -> "PagedCache":
+        c = CPagedCache()
+        _check(lib().hca_pool_view(self._h, kind, _ptr(arena), ctypes.byref(c)), "hca_pool_view")
+        import torch
+
+        m, d, t = self.kinds[kind]
+        epp = 256 // m
+        cb, sb = page_bytes(m, d, t)
+        base = arena.data_ptr()
+        n = c.num_pages
+        off_c = c.codes - base
+        codes = arena[off_c: off_c + n * cb]
+        if t == "bf16":
+            codes = codes.view(torch.int16).view(n, epp, d)
+            scales = None
+        elif t == "fp8":
+            codes = codes.view(n, epp, d)
+            off_s = c.scales - base
+            scales = arena[off_s: off_s + n * sb].view(torch.float32)
+        else:
+            codes = codes.view(n, epp, d // 2)
+            off_s = c.scales - base
+            scales = arena[off_s: off_s + n * sb].view(n, epp, d // 32)
+        return PagedCache(codes, scales, epp, d, t)
+
+    def alloc(self, bucket: int, n: int):
+        out = (ctypes.c_int32 * max(1, n))()
+        _check(lib().hca_pool_alloc(self._h, bucket, n, out), "hca_pool_alloc")
+        return list(out)[:n]
+
+    def share(self, bucket: int, pages):
+        arr = (ctypes.c_int32 * max(1, len(pages)))(*pages)
+        _check(lib().hca_pool_share(self._h, bucket, arr, len(pages)), "hca_pool_share")
+
+    def release(self, bucket: int, pages):
+        arr = (ctypes.c_int32 * max(1, len(pages)))(*pages)
+        _check(lib().hca_pool_release(self._h, bucket, arr, len(pages)), "hca_pool_release")
+
+    def publish(self, bucket: int, page: int, key: int):
+        _check(lib().hca_pool_publish(self._h, bucket, page, key), "hca_pool_publish")
+
+    def lookup(self, bucket: int, key: int) -> int:
+        p = ctypes.c_int32(-1)
+        _check(lib().hca_pool_lookup(self._h, bucket, key, ctypes.byref(p)), "hca_pool_lookup")
+        return p.value
+
+    def stats(self, bucket: int):
+        """(free, cached, held) pages and the codes and scales offsets in the arena."""
+        v = [ctypes.c_int64(0) for _ in range(3)] + [ctypes.c_size_t(0) for _ in range(2)]
+        _check(lib().hca_pool_stats(self._h, bucket, *[ctypes.byref(x) for x in v]), "hca_pool_stats")
+        return tuple(x.value for x in v)

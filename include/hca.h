@@ -364,6 +364,70 @@ hca_status kv_gather(hca_paged_cache src, const int32_t* block_table, int32_t bt
                      const int32_t* n_rows, int32_t B, int32_t max_rows, void* dst_codes,
                      void* dst_scales, void* stream);
 
+/*
+ * Page-pool packing (V4 page, section 3.1.3: the page of a KV kind is block
+ * size x compress ratio x bytes per element, and the pools of all KV kinds
+ * are packed into a few buckets by page size, each a pool of fixed-size
+ * pages; section 3.1.1: one 256-token logical block; vLLM-0.7.2 page, section
+ * 2.1: block tables name physical pages, and sequences with a common prefix
+ * name the same ones).  Host-side bookkeeping over one device arena that the
+ * caller allocates; nothing here touches the device.
+ *
+ * A kind is (m, dim, dtype): m = 1 for the raw window, 4 or 128 for the
+ * compressed entries, and the indexer keys' (4, d_I, fp8 or fp4).
+ *   hca_page_bytes   code bytes of one page, 256/m rows of dim elements
+ *                    (fp8 1 byte, fp4 half a byte, bf16 2 bytes), and its
+ *                    scale bytes (fp8: one float per page; fp4: one E4M3 byte
+ *                    per 32 elements of a row; bf16: none).
+ *   hca_pool_plan    kinds with equal (code, scale) bytes share a bucket:
+ *                    kind_bucket[n_kinds], *n_buckets.
+ *   hca_pool_create  capacity[b] pages for each bucket; *arena_bytes is the
+ *                    device arena the pools need (256-byte aligned regions:
+ *                    per bucket its pages' codes, then their scales).  The
+ *                    pool object is the caller's until hca_pool_destroy.
+ *   hca_pool_view    the hca_paged_cache of a kind inside an arena (256-byte
+ *                    aligned): the kernels take it as they take any pool;
+ *                    kinds of one bucket share its pages' memory and ids.
+ *   hca_pool_alloc   n pages of a bucket, each with one reference (all or
+ *                    nothing; HCA_ERR_UNSUPPORTED when the bucket has fewer
+ *                    free pages).  Pages are taken from the free pages first,
+ *                    then from the released pages that kept a key, oldest
+ *                    released first (their keys are dropped).
+ *   hca_pool_share   one more reference to held pages (a shared prefix).
+ *   hca_pool_release drop one reference per listed page (a page may be
+ *                    listed as often as it is held); at zero a page is free,
+ *                    or cached if it was published.
+ *   hca_pool_publish a held page's contents are the block named by `key`
+ *                    (say, a hash of the prefix through that block); a key
+ *                    names one page at a time.
+ *   hca_pool_lookup  the page published under `key` with one more reference
+ *                    (brought back if it was cached), or -1.
+ *   hca_pool_stats   free, cached and held pages of a bucket, and the arena
+ *                    offsets of its codes and scales.
+ * Invalid arguments return HCA_ERR_INVALID and change nothing.  Calls on one
+ * pool must not overlap in time.
+ */
+typedef struct {
+  int32_t m;
+  int32_t dim;
+  int32_t dtype; /* hca_dtype */
+} hca_kv_kind;
+typedef struct hca_page_pool hca_page_pool;
+hca_status hca_page_bytes(hca_kv_kind kind, size_t* code_bytes, size_t* scale_bytes);
+hca_status hca_pool_plan(const hca_kv_kind* kinds, int32_t n_kinds, int32_t* kind_bucket, int32_t* n_buckets);
+hca_status hca_pool_create(const hca_kv_kind* kinds, int32_t n_kinds, const int32_t* capacity,
+                           size_t* arena_bytes, hca_page_pool** out);
+void hca_pool_destroy(hca_page_pool* pool);
+hca_status hca_pool_view(const hca_page_pool* pool, int32_t kind, void* arena, hca_paged_cache* out);
+int32_t hca_pool_bucket(const hca_page_pool* pool, int32_t kind);
+hca_status hca_pool_alloc(hca_page_pool* pool, int32_t bucket, int32_t n, int32_t* pages);
+hca_status hca_pool_share(hca_page_pool* pool, int32_t bucket, const int32_t* pages, int32_t n);
+hca_status hca_pool_release(hca_page_pool* pool, int32_t bucket, const int32_t* pages, int32_t n);
+hca_status hca_pool_publish(hca_page_pool* pool, int32_t bucket, int32_t page, uint64_t key);
+hca_status hca_pool_lookup(hca_page_pool* pool, int32_t bucket, uint64_t key, int32_t* page);
+hca_status hca_pool_stats(const hca_page_pool* pool, int32_t bucket, int64_t* free_pages, int64_t* cached_pages,
+                          int64_t* held_pages, size_t* codes_offset, size_t* scales_offset);
+
 #ifdef __cplusplus
 }
 #endif

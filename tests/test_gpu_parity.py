@@ -732,3 +732,91 @@ def test_gather_bit_exact(dtype, epp, dim):
         assert np.array_equal(gc[b, : nrows[b]], rc.view(np.uint8).reshape(nrows[b], rb))
         if dtype != "bf16":
             assert np.array_equal(scales.cpu().numpy()[b, : nrows[b]], rs)
+
+
+# ----------------------------------------------------------------- page-pool packing
+
+
+def test_indexer_and_attention_over_pool_pages():
+    # the pools of one c4a layer (entries, window, indexer keys) live in one
+    # device arena cut by PagePool into size buckets; the block tables are the
+    # allocator's pages, two sequences naming the same prefix pages (found by
+    # key), and the top-k sets and attention equal the oracle's and are
+    # bit-identical to the same contents in plain per-kind pools
+    H.flush("indexer + attention over pool pages")
+    kind = synth.LayerKind("c4a", 4, 512, "fp8", 128)
+    w = synth.Workload(103, "pool", 3, None, 512, 64, 128, "fp8", [kind], shared_prefix_seqs=2,
+                       shared_prefix_blocks=8)
+    sd = H.SeqData(w, 0, [6000, 4100, 2500])
+    assert len(sd.members) == 2
+    sd.idx = paging.Pool("fp8", sd.num_pages, 64, 128)
+    for b in range(sd.B):
+        paging.write_run(sd.idx, sd.table[b], 0, sd.keys[b])
+    sd.enforce_margin()
+    kinds = [(4, 512, "fp8"), (1, 512, "fp8"), (4, 128, "fp8")]
+    nblk = [-(-int(L) // 256) for L in sd.lens]
+    pool = hca.PagePool(kinds, [sum(nblk) + 3, 2 * sd.B + 3, sum(nblk) + 3])
+    arena = torch.zeros(pool.arena_bytes, dtype=torch.uint8, device="cuda")
+    kv, win, idx = (pool.view(i, arena) for i in range(3))
+    bkv, bwin, bidx = (pool.bucket_of(i) for i in range(3))
+    T = np.full(sd.table.shape, -1, np.int32)
+    TI = np.full(sd.table.shape, -1, np.int32)
+    TW = np.full(sd.wtable.shape, -1, np.int32)
+    first = int(sd.members[0])
+    for b in range(sd.B):
+        lb0 = 0
+        if b in sd.members.tolist() and b != first:  # the prefix pages come from the first member, by key
+            for lb in range(8):
+                T[b, lb] = pool.lookup(bkv, 1000 + lb)
+                TI[b, lb] = pool.lookup(bidx, 1000 + lb)
+            assert (T[b, :8] == T[first, :8]).all() and (TI[b, :8] == TI[first, :8]).all()
+            lb0 = 8
+        T[b, lb0: nblk[b]] = pool.alloc(bkv, nblk[b] - lb0)
+        TI[b, lb0: nblk[b]] = pool.alloc(bidx, nblk[b] - lb0)
+        if b == first:
+            for lb in range(8):
+                pool.publish(bkv, int(T[b, lb]), 1000 + lb)
+                pool.publish(bidx, int(TI[b, lb]), 1000 + lb)
+        wl = np.nonzero(sd.wtable[b] >= 0)[0]
+        TW[b, wl] = pool.alloc(bwin, len(wl))
+    assert pool.stats(bkv)[2] == sum(nblk) - 8  # the prefix pages are held once, by two sequences
+    # the oracle's page contents, placed where the allocator put them
+    for b in range(sd.B):
+        for lb in range(nblk[b]):
+            for src, dst, tt in ((sd.kv, kv, T), (sd.idx, idx, TI)):
+                dst.codes[int(tt[b, lb])] = H.to_dev(src.codes[int(sd.table[b, lb])])
+                dst.scales[int(tt[b, lb])] = float(src.scales[int(sd.table[b, lb])])
+        for lb in np.nonzero(sd.wtable[b] >= 0)[0]:
+            win.codes[int(TW[b, lb])] = H.to_dev(sd.win.codes[int(sd.wtable[b, lb])])
+            win.scales[int(TW[b, lb])] = float(sd.win.scales[int(sd.wtable[b, lb])])
+    torch.cuda.synchronize()
+    Lmax, k = H.max_len(sd.lens), kind.topk
+    res = []
+    for (kvp, winp, idxp, t, ti, tw) in ((kv, win, idx, T, TI, TW),
+                                         (H.upload_pool(sd.kv), H.upload_pool(sd.win), H.upload_pool(sd.idx),
+                                          sd.table, sd.table, sd.wtable)):
+        ws = hca.workspace(hca.indexer_topk_workspace(sd.B, Lmax, 4, k))
+        sel = torch.full((sd.B, k), -7, dtype=torch.int32, device="cuda")
+        sel_n = torch.zeros(sd.B, dtype=torch.int32, device="cuda")
+        hca.indexer_topk(H.to_dev(sd.qi.view(np.int16)), H.to_dev(sd.wi), idxp, H.to_dev(ti), H.to_dev(sd.lens), Lmax, 4,
+                         k, sel, sel_n, ws)
+        wsa = hca.workspace(hca.paged_hybrid_decode_workspace(sd.B, w.H, w.d, Lmax, 4, 128, k))
+        out = torch.zeros((sd.B, w.H, w.d), dtype=torch.float32, device="cuda")
+        lse = torch.zeros((sd.B, w.H), dtype=torch.float32, device="cuda")
+        hca.paged_hybrid_decode(H.to_dev(sd.q.view(np.int16)), kvp, H.to_dev(t), winp, H.to_dev(tw), H.to_dev(sd.lens),
+                                Lmax, 4, 128, sel, sel_n, H.scale_for(w.d), w.theta, out, lse, wsa)
+        torch.cuda.synchronize()
+        res.append((sel.cpu().numpy(), sel_n.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()))
+    (sel_p, n_p, out_p, lse_p), (sel_u, n_u, out_u, lse_u) = res
+    assert np.array_equal(sel_p, sel_u) and np.array_equal(n_p, n_u)
+    assert np.array_equal(out_p.view(np.uint32), out_u.view(np.uint32))
+    assert np.array_equal(lse_p.view(np.uint32), lse_u.view(np.uint32))
+    for b in range(sd.B):
+        want = sd.oracle_select(b)
+        assert n_p[b] == len(want) and np.array_equal(sel_p[b, : n_p[b]], want), b
+        ref_out, ref_lse, _ = sd.oracle_attend(b, want)
+        assert H.rel_err_rows(out_p[b], ref_out) <= H.ATTN_TOL, b
+    # the second member lets go: its prefix pages stay held by the first
+    second = int(sd.members[1])
+    pool.release(bkv, [int(p) for p in T[second, : nblk[second]]])
+    assert pool.stats(bkv)[2] == sum(nblk) - 8 - (nblk[second] - 8)
