@@ -210,12 +210,15 @@ def insert_job(stage, pos0, e0, block_table, dst: PagedCache, m: int, x=None, ga
                ntok=None, rope_theta: float = 0.0, append: bool = False, norm_gamma=None,
                norm_eps: float = 1e-6, overlap: int = 0, fold_state=None) -> "CInsertJob":
     """One job of kv_compress_insert_jobs (x None: the open row is already in stage).
-    The tensors must stay alive until the call that takes the job is enqueued."""
-    return CInsertJob(_ptr(x), 0 if x is None else x.stride(0), _ptr(gate_logit),
+    The job holds references to the tensors it names, so they stay alive as
+    long as the job does."""
+    job = CInsertJob(_ptr(x), 0 if x is None else x.stride(0), _ptr(gate_logit),
                       0 if gate_logit is None else gate_logit.stride(0), _ptr(pos_bias), _ptr(pos0), _ptr(ntok), m,
                       overlap, rope_theta, _ptr(norm_gamma), norm_eps, _ptr(stage), stage.stride(0), _ptr(e0),
                       _ptr(block_table), block_table.stride(0), dst.c(), 1 if append else 0, _ptr(fold_state),
                       0 if fold_state is None else fold_state.stride(0))
+    job._keep = (stage, pos0, e0, block_table, dst, x, gate_logit, pos_bias, ntok, norm_gamma, fold_state)
+    return job
 
 
 def kv_compress_insert_jobs(jobs, B: int, stream=None):
