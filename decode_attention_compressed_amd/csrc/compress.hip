@@ -243,11 +243,10 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
     return;
   }
 
-  // large m: a block folds one (entry, dim slice) at a time; its row groups
-  // take strided subsets of the group's tokens and are summed through LDS
-  const int DS = a.ds;                 // dims of a slice (divides d, multiple of 8)
-  const int nsl = a.d / DS;
-  const int TS = DS >> 3;              // threads across the slice
+  // large m: a block folds one entry at a time; its row groups take strided
+  // subsets of the group's tokens and are summed through LDS
+  const int DS = a.d;                  // dims of a row (a multiple of 8, <= 2048)
+  const int TS = DS >> 3;              // threads across the row
   const int RS = kCompressThreads / TS;
   const int ls = threadIdx.x % TS;
   const int gs = threadIdx.x / TS;
@@ -255,9 +254,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
   __shared__ float red_s[kCompressThreads];
   extern __shared__ float acc_s[];     // [RS][DS]
   const uint16_t* xs = a.x + (int64_t)b * a.xs + ls * 8;
-  for (int u = bx; u < N * nsl; u += gx) {
-    const int j = u / nsl;
-    const int base = (u % nsl) * DS;
+  for (int j = bx; j < N; j += gx) {
     const int t0 = j * m;
     const int r = min(m, n - t0);
     // the row group's first batch of token rows is in flight while the
@@ -268,7 +265,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int i = gs + k * RS;
-      raw[k] = gs < RS && i < r ? *reinterpret_cast<const u32x4*>(xs + (int64_t)(t0 + i) * a.d + base)
+      raw[k] = gs < RS && i < r ? *reinterpret_cast<const u32x4*>(xs + (int64_t)(t0 + i) * a.d)
                                 : u32x4{0u, 0u, 0u, 0u};
     }
     const float zi = (int)threadIdx.x < r ? zb[t0 + threadIdx.x] : 0.0f;
@@ -294,7 +291,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
 #pragma unroll
           for (int k = 0; k < kBatch; ++k) {
             const int i = i0 + k * RS;
-            raw[k] = i < r ? *reinterpret_cast<const u32x4*>(xs + (int64_t)(t0 + i) * a.d + base)
+            raw[k] = i < r ? *reinterpret_cast<const u32x4*>(xs + (int64_t)(t0 + i) * a.d)
                            : u32x4{0u, 0u, 0u, 0u};
           }
         }
@@ -332,8 +329,8 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
         e1 += acc_s[g * DS + 2 * t + 1];
       }
       if (state_out != nullptr) {
-        state_out[kFoldStateHead + base + 2 * t] = e0;
-        state_out[kFoldStateHead + base + 2 * t + 1] = e1;
+        state_out[kFoldStateHead + 2 * t] = e0;
+        state_out[kFoldStateHead + 2 * t + 1] = e1;
       }
       e0 *= inv_tot;
       e1 *= inv_tot;
@@ -348,7 +345,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
       state_out[2] = tot;
     }
     float rs = 1.0f;
-    if (a.gamma != nullptr) {  // the entry's sum of squares (the slice is the whole row, DS = d)
+    if (a.gamma != nullptr) {  // the entry's sum of squares
       ss = wave_sum(ss);
       if ((threadIdx.x & 63) == 0) red_s[threadIdx.x >> 6] = ss;
       __syncthreads();
@@ -360,18 +357,18 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
       const int t = threadIdx.x + kCompressThreads * k;
       if (t >= DS / 2) break;
       float e0 = acc_s[2 * t], e1 = acc_s[2 * t + 1];
-      if (a.gamma != nullptr) {  // base = 0
+      if (a.gamma != nullptr) {
         e0 *= rs * gpair[k].x;
         e1 *= rs * gpair[k].y;
       }
       float c, sn;
-      rope_cs(pos, rope_inv_freq(base / 2 + t, a.rope_r), c, sn);
-      float* o = a.out + (int64_t)b * a.os + (int64_t)j * a.d + base + 2 * t;
+      rope_cs(pos, rope_inv_freq(t, a.rope_r), c, sn);
+      float* o = a.out + (int64_t)b * a.os + (int64_t)j * a.d + 2 * t;
       o[0] = e0 * c - e1 * sn;
       o[1] = e0 * sn + e1 * c;
       if (lds_row != nullptr) {
-        lds_row[base + 2 * t] = o[0];
-        lds_row[base + 2 * t + 1] = o[1];
+        lds_row[2 * t] = o[0];
+        lds_row[2 * t + 1] = o[1];
       }
     }
     __syncthreads();
@@ -384,26 +381,19 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
   compress_block<PATHS>(a, b, blockIdx.x, gridDim.x, nullptr, clampi(a.ntok[b], 0, a.max_ntok), a.pos0[b], NoMid{});
 }
 
-int compress_slice(int n_max, int B, int d, int m) {
-  (void)n_max; (void)B; (void)m;
-  return d;  // a block folds whole entries; its row groups' loads are batched
-}
 
 hipError_t launch_compress(CompressArgs a, hipStream_t s) {
   const int n_max = (a.max_ntok + a.m - 1) / a.m;
   if (a.B == 0 || n_max == 0) return hipSuccess;
   int gx;
   size_t shm = 0;
-  a.ds = a.d;
   a.rope_r = pow((double)a.theta, -2.0 / (double)a.d);
   if (a.m <= kSmallM) {
     const int RP = kCompressThreads / (a.d / 8);
     gx = (n_max + RP - 1) / RP;
     gx = gx > 2048 ? 2048 : gx;
   } else {
-    a.ds = compress_slice(n_max, a.B, a.d, a.m);
-    const int64_t units = (int64_t)n_max * (a.d / a.ds);
-    gx = units > 4096 ? 4096 : (int)units;
+    gx = n_max > 4096 ? 4096 : n_max;
     shm = kCompressShm;
   }
   if (a.m <= kSmallM)
@@ -720,7 +710,6 @@ __global__ __launch_bounds__(kCompressThreads) void insert_kernel(InsertJobs j) 
 hipError_t launch_insert(InsertJobs j, int B, hipStream_t s) {
   if (B == 0 || j.n == 0) return hipSuccess;
   for (int i = 0; i < j.n; ++i) {
-    j.job[i].c.ds = compress_slice(1, B, j.job[i].c.d, j.job[i].c.m);
     j.job[i].c.rope_r = pow((double)j.job[i].c.theta, -2.0 / (double)j.job[i].c.d);
   }
   hipLaunchKernelGGL(insert_kernel, dim3(B, j.n), dim3(kCompressThreads), kCompressShm, s, j);

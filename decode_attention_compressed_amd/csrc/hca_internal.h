@@ -20,14 +20,11 @@ struct CompressArgs {
   double rope_r;  // theta^(-2/d) in fp64 (set by the launcher)
   const float* gamma; float eps;  // RMS normalisation of each entry before its rotation (gamma null: none)
   float* out; int64_t os;
-  int ds;  // dims per block slice (set by the launcher)
 };
 hipError_t launch_compress(CompressArgs a, hipStream_t s);
 constexpr int kCompressThreads = 256;
 constexpr int kSmallM = 16;  // groups up to this size are folded by one row group of threads
 constexpr size_t kCompressShm = (size_t)kCompressThreads * 8 * sizeof(float);  // a large-m fold's row-group sums
-// dims per block slice of a large-m fold (64 when there are few entries)
-int compress_slice(int n_max, int B, int d, int m);
 
 // decode-step update of pools: fold each open group into its staging row and
 // quantize the open page, all in one launch (a job per pool)
