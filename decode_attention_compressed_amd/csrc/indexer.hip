@@ -278,9 +278,8 @@ struct PageTiles {
   uint32_t raw[KDT == HCA_FP4_E2M1 ? 4 * KS : 1];
   uint32_t rsc[KDT == HCA_FP4_E2M1 ? SW : 1];
 
-  __device__ __forceinline__ void load(const IndexerArgs& a, const int32_t* btrow, int p, bool p_ok, int N, int col,
-                                       int g) {
-    const int phys = btrow[p_ok ? p : 0];
+  // `phys` is the page's table entry, read ahead of the sequence length
+  __device__ __forceinline__ void load(const IndexerArgs& a, int phys, int p, bool p_ok, int N, int col, int g) {
     const bool live = p_ok && phys >= 0 && phys < a.keys.num_pages;
     const int rows = live ? min(64, N - 64 * p) : 0;
     const int pg = live ? phys : 0;
@@ -379,30 +378,40 @@ struct PageTiles {
 template <int KDT, int DI>
 __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(IndexerArgs a) {
   const int b = blockIdx.y;
-  const int L = clampi(a.lens[b], 0, a.max_len);
-  const int N = (L + a.m - 1) / a.m;
-  const int NP = (N + 63) / 64;
   const int page0 = blockIdx.x * kPagesPerScoreBlock;
-  if (page0 >= NP) return;
   __shared__ uint32_t hist_s[kHistBins];
-  ScoreCtx c;
-  c.want_hist = a.k < N;
-  c.hist_s = hist_s;
-  c.scores = score_row(a, b);
-  if (c.want_hist) {
-    for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) hist_s[i] = 0;
-    __syncthreads();
-  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar page math
   const int col = lane & 15, g = lane >> 4;
+  constexpr int PPW = kPagesPerScoreWave;
+  auto page_of = [&](int i) { return page0 + wave + 4 * i; };
+  // Nothing below waits for the sequence length before its loads are issued:
+  // the length, the query and the table entries of the wave's pages go out
+  // together (entries past the table's width are not read), so the page loads
+  // follow one round trip after the start instead of two.
+  const int len_raw = a.lens[b];
+  const int32_t* btrow = a.bt + (int64_t)b * a.bts;
+  int phys[PPW];
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) phys[i] = btrow[min(page_of(i), a.bts - 1)];
+  ScoreCtx c;
   bf16x8 qa[DI / 32];
   load_query<KDT, DI>(a, b, col, g, qa, c.wgt);
-  const int32_t* btrow = a.bt + (int64_t)b * a.bts;
+  // the histogram is cleared whatever k is; the barrier orders LDS only and
+  // leaves the loads above in flight
+  for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) hist_s[i] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  const int L = clampi(len_raw, 0, a.max_len);
+  const int N = (L + a.m - 1) / a.m;
+  const int NP = (N + 63) / 64;
+  if (page0 >= NP) return;
+  c.want_hist = a.k < N;
+  c.hist_s = hist_s;
+  c.scores = score_row(a, b);
   const int p_end = min(NP, page0 + kPagesPerScoreBlock);
-  constexpr int PPW = kPagesPerScoreWave;
   PageTiles<KDT, DI> pa, pb;
-  auto page_of = [&](int i) { return page0 + wave + 4 * i; };
   auto consume = [&](PageTiles<KDT, DI>& t, int i) {
     t.prepare();
     const int p = page_of(i);
@@ -412,15 +421,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(IndexerArgs 
       finish_tile(c, t.dots(tt, qa), e, p < p_end && e < N, g);
     }
   };
-  pa.load(a, btrow, page_of(0), page_of(0) < p_end, N, col, g);
-  pb.load(a, btrow, page_of(1), page_of(1) < p_end, N, col, g);
-#pragma unroll
-  for (int i = 0; i < PPW; i += 2) {
-    consume(pa, i);
-    if (i + 2 < PPW) pa.load(a, btrow, page_of(i + 2), page_of(i + 2) < p_end, N, col, g);
-    consume(pb, i + 1);
-    if (i + 3 < PPW) pb.load(a, btrow, page_of(i + 3), page_of(i + 3) < p_end, N, col, g);
-  }
+  static_assert(PPW == 2, "two pages per wave, both loaded up front");
+  pa.load(a, phys[0], page_of(0), page_of(0) < p_end, N, col, g);
+  pb.load(a, phys[1], page_of(1), page_of(1) < p_end, N, col, g);
+  // every load of both pages is issued before the first page is used (left to
+  // itself the scheduler holds part of the second page back behind the first)
+  __builtin_amdgcn_sched_barrier(0);
+  consume(pa, 0);
+  consume(pb, 1);
   if (c.want_hist) hist_flush(a, b, hist_s);
 }
 
@@ -540,11 +548,13 @@ struct SelView {
   uint32_t* ccount;  // per chunk block: candidates
   uint32_t* above;   // per chunk block: entries above the cut bin
 };
+// Pointers only: nothing here waits for the sequence length, so the loads a
+// kernel issues from them can be in flight while the length arrives
+// (set_len then gives N and G).
 __device__ __forceinline__ SelView sel_view(const IndexerArgs& a, int b) {
   SelView v;
-  const int L = clampi(a.lens[b], 0, a.max_len);
-  v.N = (L + a.m - 1) / a.m;
-  v.G = (v.N + kSelChunk - 1) / kSelChunk;
+  v.N = 0;
+  v.G = 0;
   v.n_pad = ((a.lay.n_max + kSelChunk - 1) / kSelChunk) * kSelChunk;
   v.scores = reinterpret_cast<const float*>(a.ws + a.lay.scores) + (size_t)b * v.n_pad;
   v.hist = reinterpret_cast<uint32_t*>(a.ws + a.lay.hist) + (size_t)b * kHistCopies * kHistBins;
@@ -556,23 +566,36 @@ __device__ __forceinline__ SelView sel_view(const IndexerArgs& a, int b) {
   v.above = v.ccount + gp;
   return v;
 }
+__device__ __forceinline__ void set_len(SelView& v, const IndexerArgs& a, int len_raw) {
+  const int L = clampi(len_raw, 0, a.max_len);
+  v.N = (L + a.m - 1) / a.m;
+  v.G = (v.N + kSelChunk - 1) / kSelChunk;
+}
 
 // The cut bin (where the count from the top reaches `need`) and the count
 // strictly above it, from the histogram copies: the bins are summed 256 at a
 // time from the top, usually once, since the k highest scores sit in the top
 // bins.  Every thread of the block gets the result.
-__device__ void find_cut_copies(const uint32_t* hist, uint32_t need, uint32_t* tmp, int& cut, uint32_t& above) {
+// The top slice's per-thread sums (`first`) are loaded by the caller, ahead of
+// the sequence length.
+__device__ __forceinline__ uint32_t hist_slice_sum(const uint32_t* hist, int top) {
+  const int bin = top - (int)threadIdx.x;  // descending with the thread index
+  uint32_t c[kHistCopies];
+#pragma unroll
+  for (int r = 0; r < kHistCopies; ++r) c[r] = bin >= 0 ? hist[(size_t)r * kHistBins + bin] : 0u;
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int r = 0; r < kHistCopies; ++r) cnt += c[r];
+  return cnt;
+}
+__device__ void find_cut_copies(const uint32_t* hist, uint32_t first, uint32_t need, uint32_t* tmp, int& cut,
+                                uint32_t& above) {
   __shared__ int cut_s;
   __shared__ uint32_t above_s;
   uint32_t run = 0;  // entries in the bins already passed
   for (int top = kHistBins - 1; top >= 0; top -= kSelThreads) {
-    const int bin = top - (int)threadIdx.x;  // descending with the thread index
-    uint32_t c[kHistCopies];
-#pragma unroll
-    for (int r = 0; r < kHistCopies; ++r) c[r] = bin >= 0 ? hist[(size_t)r * kHistBins + bin] : 0u;
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int r = 0; r < kHistCopies; ++r) cnt += c[r];
+    const int bin = top - (int)threadIdx.x;
+    const uint32_t cnt = top == kHistBins - 1 ? first : hist_slice_sum(hist, top);
     uint32_t total;
     const uint32_t before = run + block_excl_scan(cnt, tmp, total);
     if (run + total >= need) {  // the cut is in this slice
@@ -594,7 +617,21 @@ __device__ void find_cut_copies(const uint32_t* hist, uint32_t need, uint32_t* t
 
 __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(IndexerArgs a) {
   const int b = blockIdx.y;
-  const SelView v = sel_view(a, b);
+  SelView v = sel_view(a, b);
+  const int len_raw = a.lens[b];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // this block's scores and the histogram's top slice are loaded with the
+  // length, unconditionally (a block past the last score chunk, which the grid
+  // has when k exceeds the entries, reads chunk 0 and uses nothing)
+  constexpr int kUnroll = kSelChunk / 256;  // one round of loads per wave
+  const int c0 = blockIdx.x * kSelChunk;
+  const int base0 = (c0 < v.n_pad ? c0 : 0) + wave * 64 * kUnroll;
+  float sc[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) sc[u] = v.scores[base0 + 64 * u + lane];
+  const uint32_t top_cnt = hist_slice_sum(v.hist, kHistBins - 1);
+  __builtin_amdgcn_sched_barrier(0);
+  set_len(v, a, len_raw);
   const int N = v.N, k = a.k;
   int32_t* out = a.out_idx + (int64_t)b * k;
   if (N <= k) {  // every entry is kept
@@ -607,22 +644,11 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(IndexerArgs a
     return;
   }
   if ((int)blockIdx.x >= v.G) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // this block's scores are loaded first: they are in flight while the cut is found
-  const int c0 = blockIdx.x * kSelChunk;
-  const int c1 = min(N, c0 + kSelChunk);
-  constexpr int kUnroll = kSelChunk / 256;  // one round of loads per wave
-  const int base0 = c0 + wave * 64 * kUnroll;
-  float sc[kUnroll];
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int e = base0 + 64 * u + lane;
-    sc[u] = v.scores[e < c1 ? e : c0];
-  }
+  const int c1 = min(N, c0 + kSelChunk);  // scores at c1 and past it are not used
   __shared__ uint32_t tmp[kSelThreads / 64];
   int cut;
   uint32_t above;
-  find_cut_copies(v.hist, (uint32_t)k, tmp, cut, above);
+  find_cut_copies(v.hist, top_cnt, (uint32_t)k, tmp, cut, above);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     v.ctr[0] = (uint32_t)cut;
     v.ctr[1] = above;
@@ -693,24 +719,37 @@ struct CutKey {
   uint32_t nc;
 };
 
-__device__ CutKey resolve_cut(const SelView& v, int k, SelLds& sm) {
+// Per-thread chunk counts, contiguous: thread t holds chunks t*per .. t*per+per-1
+// with per fixed by the padded chunk count, so they can be loaded before the
+// sequence length is known (chunks at G and past it are dropped afterwards).
+constexpr int kSelPer = kMaxSelBlocks / kSelThreads;
+__device__ __forceinline__ int sel_per(const SelView& v) { return (v.n_pad / kSelChunk + kSelThreads - 1) / kSelThreads; }
+__device__ __forceinline__ void load_chunk_counts(const SelView& v, const uint32_t* arr, uint32_t loc[kSelPer]) {
+  const int per = sel_per(v), gp = v.n_pad / kSelChunk;
+#pragma unroll
+  for (int u = 0; u < kSelPer; ++u) {
+    const int j = threadIdx.x * per + u;
+    loc[u] = (u < per && j < gp) ? arr[j] : 0u;
+  }
+}
+
+__device__ CutKey resolve_cut(const SelView& v, int k, SelLds& sm, int cut, uint32_t above,
+                              const uint32_t ccount_pre[kSelPer]) {
   const int N = v.N, G = v.G;
-  const int cut = (int)v.ctr[0];
-  const uint32_t above = v.ctr[1];
   {
     uint32_t cv = 0;
-    const int per = (G + kSelThreads - 1) / kSelThreads;  // counts per thread, contiguous
-    uint32_t loc[kMaxSelBlocks / kSelThreads];
+    const int per = sel_per(v);
+    uint32_t loc[kSelPer];
 #pragma unroll
-    for (int u = 0; u < kMaxSelBlocks / kSelThreads; ++u) {
+    for (int u = 0; u < kSelPer; ++u) {
       const int j = threadIdx.x * per + u;
-      loc[u] = (u < per && j < G) ? v.ccount[j] : 0u;
+      loc[u] = (u < per && j < G) ? ccount_pre[u] : 0u;
       cv += loc[u];
     }
     uint32_t tot;
     uint32_t run = block_excl_scan(cv, sm.tmp, tot);
 #pragma unroll
-    for (int u = 0; u < kMaxSelBlocks / kSelThreads; ++u) {
+    for (int u = 0; u < kSelPer; ++u) {
       const int j = threadIdx.x * per + u;
       if (u < per && j < G) sm.pre_s[j] = run;
       run += loc[u];
@@ -810,19 +849,27 @@ __global__ __launch_bounds__(kSelThreads) void select_compact_kernel(IndexerArgs
   // block j writes the kept entries of chunk j: its output offset is the count
   // kept by chunks 0 .. j-1 (entries above the cut bin plus winning candidates)
   const int b = blockIdx.y, j = blockIdx.x;
-  const SelView v = sel_view(a, b);
+  SelView v = sel_view(a, b);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Loaded with the length, none of them depending on it: the cut, the
+  // per-chunk candidate and above-cut counts, and this chunk's bitmap words
+  // (entries above the cut bin; words at N and past it are dropped below).
+  const int w = j * (kSelChunk / 32) + lane;
+  const uint32_t bits_pre = wave == 0 ? v.bitmap[w] : 0u;
+  const int cut_pre = (int)v.ctr[0];
+  const uint32_t above_pre = v.ctr[1];
+  uint32_t cc_pre[kSelPer], ab_pre[kSelPer];
+  load_chunk_counts(v, v.ccount, cc_pre);
+  load_chunk_counts(v, v.above, ab_pre);
+  set_len(v, a, a.lens[b]);
   const int N = v.N, G = v.G, k = a.k;
   if (N <= k || j >= G) return;
   int32_t* out = a.out_idx + (int64_t)b * k;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ SelLds sm;
   __shared__ uint32_t wbits_s[kSelChunk / 32];
-  // this chunk's bitmap words (entries above the cut bin), loaded up front
   const int W = (N + 31) / 32;
-  const int w = j * (kSelChunk / 32) + lane;
-  const uint32_t bits_above = (wave == 0 && w < W) ? v.bitmap[w] : 0u;
-  if (wave == 0) wbits_s[lane] = bits_above;
-  const CutKey ck = resolve_cut(v, k, sm);
+  if (wave == 0) wbits_s[lane] = w < W ? bits_pre : 0u;
+  const CutKey ck = resolve_cut(v, k, sm, cut_pre, above_pre, cc_pre);
   // this chunk's winning candidates join its words
   {
     const uint32_t c0 = sm.pre_s[j], c1 = sm.pre_s[j + 1];
@@ -834,10 +881,17 @@ __global__ __launch_bounds__(kSelThreads) void select_compact_kernel(IndexerArgs
     }
   }
   uint32_t before = 0, all = 0;
-  for (int i = threadIdx.x; i < G; i += kSelThreads) {
-    const uint32_t c = v.above[i] + sm.wc_s[i];
-    all += c;
-    before += i < j ? c : 0u;
+  {
+    const int per = sel_per(v);
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+      const int i = threadIdx.x * per + u;
+      if (u < per && i < G) {
+        const uint32_t c = ab_pre[u] + sm.wc_s[i];
+        all += c;
+        before += i < j ? c : 0u;
+      }
+    }
   }
   uint32_t tot_before, total;
   (void)block_excl_scan(before, sm.tmp, tot_before);
