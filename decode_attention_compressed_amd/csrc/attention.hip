@@ -137,24 +137,6 @@ __device__ __forceinline__ uint64_t resolve_row(const AttnArgs& a, int b, int r,
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48),
-// every lane getting the result.  Row swaps on the VALU: with both operands x,
-// v_permlane32_swap returns (x, x from the other half) split over its two
-// results, so the pair holds x[l] and x[l^32] in every lane; v_permlane16_swap
-// does the same for x[l] and x[l^16].  Partners combine the same two values,
-// so the sum is identical in all four lanes.
-__device__ __forceinline__ float rows_max4(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
-  v = fmaxf(u2f(a[0]), u2f(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
-  return fmaxf(u2f(b[0]), u2f(b[1]));
-}
-__device__ __forceinline__ float rows_sum4(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
-  v = u2f(a[0]) + u2f(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
-  return u2f(b[0]) + u2f(b[1]);
-}
 
 // LDS tile layout.  For D >= 128 a row holds its D halves unpadded and the
 // 16-byte chunk c of row r sits at chunk c ^ swz(r): the 16 rows one tile

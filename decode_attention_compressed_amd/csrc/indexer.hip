@@ -82,6 +82,8 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // 8 fp4 codes (one dword, element 2c in the low nibble of byte c) -> 8 exact bf16
+// (the block scale is applied after the product, in fp32: the conversion's
+// scale operand does not reproduce the exact product for E4M3 scales)
 __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w) {
   u32x4 r;
   r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0));
@@ -189,8 +191,7 @@ __device__ __forceinline__ void finish_tile(const ScoreCtx& c, f32x4 acc, int e,
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) s = fmaf(c.wgt[i], fmaxf(acc[i], 0.0f), s);
-  s += __shfl_xor(s, 16, 64);
-  s += __shfl_xor(s, 32, 64);
+  s = rows_sum4(s);
   if (g == 0 && valid) {
     c.scores[e] = s;
     if (c.want_hist) atomicAdd(&c.hist_s[order_key(s) >> 20], 1u);
@@ -240,8 +241,9 @@ __device__ __forceinline__ float* score_row(const IndexerArgs& a, int b) {
 // hardware, so the loads need no masks, no branches and only 32-bit offsets.
 // Pages are double-buffered (the loads of page i+2 are issued right after page
 // i is consumed), fully unrolled so that the waits count down in order.
-constexpr int kPagesPerScoreBlock = 8;
+constexpr int kPagesPerScoreBlock = 32;
 constexpr int kPagesPerScoreWave = kPagesPerScoreBlock / 4;
+constexpr int kScoreBufs = 3;  // pages a wave has in flight
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -411,7 +413,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(IndexerArgs 
   c.hist_s = hist_s;
   c.scores = score_row(a, b);
   const int p_end = min(NP, page0 + kPagesPerScoreBlock);
-  PageTiles<KDT, DI> pa, pb;
+  // a ring of kScoreBufs page buffers per wave: the first kScoreBufs pages are
+  // loaded up front, page i + kScoreBufs as soon as page i is consumed
+  PageTiles<KDT, DI> pt[kScoreBufs];
   auto consume = [&](PageTiles<KDT, DI>& t, int i) {
     t.prepare();
     const int p = page_of(i);
@@ -421,14 +425,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(IndexerArgs 
       finish_tile(c, t.dots(tt, qa), e, p < p_end && e < N, g);
     }
   };
-  static_assert(PPW == 2, "two pages per wave, both loaded up front");
-  pa.load(a, phys[0], page_of(0), page_of(0) < p_end, N, col, g);
-  pb.load(a, phys[1], page_of(1), page_of(1) < p_end, N, col, g);
-  // every load of both pages is issued before the first page is used (left to
-  // itself the scheduler holds part of the second page back behind the first)
+#pragma unroll
+  for (int i = 0; i < kScoreBufs; ++i) pt[i].load(a, phys[i], page_of(i), page_of(i) < p_end, N, col, g);
+  // every load of the first pages is issued before the first page is used
+  // (left to itself the scheduler holds some back behind the first page)
   __builtin_amdgcn_sched_barrier(0);
-  consume(pa, 0);
-  consume(pb, 1);
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    consume(pt[i % kScoreBufs], i);
+    const int n = i + kScoreBufs;
+    if (n < PPW) pt[i % kScoreBufs].load(a, phys[n], page_of(n), page_of(n) < p_end, N, col, g);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if (c.want_hist) hist_flush(a, b, hist_s);
 }
 
