@@ -45,8 +45,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 # copy_bandwidth() (the summary with the commands is in profiles/).  They hold
 # only for the kernel source they were taken on, identified by the SHA-256 of
 # the indexer source and the headers it includes; otherwise traffic is null.
-SCORE_TRAFFIC = {"source_sha256": "ac7539f94f70c8ec8442a172328fec5a368c6f839a9f2a4d2fbce75ecf2b1c4d",
-                 "fetch_bytes": 71811323, "write_bytes": 5526188}
+SCORE_TRAFFIC = {"source_sha256": "49fa57889b87d368f32ff58e5e31cedd882ef050078739a4b0ee8cab0608e212",
+                 "fetch_bytes": 71889905, "write_bytes": 4599286}
 SCORE_SOURCES = ("decode_attention_compressed_amd/csrc/indexer.hip", "decode_attention_compressed_amd/csrc/hca_common.h",
                  "decode_attention_compressed_amd/csrc/indexer_internal.h")
 
