@@ -696,6 +696,425 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
   }
 }
 
+// ---- fp8 rows of 512 dims: pairs of waves split each tile's dims.
+// Block of 8 waves = 4 pairs (one block per CU, two waves per SIMD); pair p
+// takes the split's tiles p, p + 4, ... as a wave of the 4-wave kernel does.
+// Wave half hf of a pair loads, converts and multiplies only dims
+// [256 hf, 256 hf + 256) of every row of the pair's tiles: its QK product is
+// the partial S over those dims, the two partials are added through LDS (both
+// waves then hold the same S and run the same softmax), and its PV product is
+// O for those dims.  A wave's tile bytes are its own loads, so it waits for
+// nothing of its partner's but the partial S.  Per wave and tile this is half
+// the conversions and MFMAs of the 4-wave kernel, and half its accumulator
+// and query registers, which leaves room for two waves per SIMD.
+constexpr int kPairThreads = 512;
+constexpr int kPairWaves = kPairThreads / 64;
+constexpr int kPairs = kPairWaves / 2;
+constexpr int kPairD = 512;
+
+// One tile in LDS: half hf holds dims [256 hf, +256) of the 32 rows, 16
+// chunks of 16 bytes per row, chunk cc of row r at position cc ^ f(r): the 16
+// rows one K read touches and the 8 rows a transposing V read touches fall on
+// distinct banks.  A half is filled by its wave's own loads.
+struct PairTile {
+  static constexpr int CHH = kPairD / 2 / 16;                // chunks per half row: 16
+  static constexpr int HALF_BYTES = kTileRows * kPairD / 2;  // 8 KB
+  static constexpr int BYTES = 2 * HALF_BYTES;
+  static constexpr int INSTR = HALF_BYTES / 1024;            // load-to-LDS instructions per half: 8
+  __device__ static __forceinline__ int f(int r) { return (r & 15) ^ (((r >> 4) & 1) << 3); }
+  __device__ static __forceinline__ int at(int hf, int r, int cc) {
+    return hf * HALF_BYTES + 16 * (r * CHH + (cc ^ f(r)));
+  }
+};
+
+// k-step t (of 16, 32 dims each) of the QK product, lane group g: 8 dims from
+// this first dim.  Steps 0-7 are half 0's, 8-15 half 1's; within a half,
+// steps 2u and 2u + 1 are the two 8-dim halves of chunk 4u + g.
+__device__ __forceinline__ int pair_kdim(int t, int g) {
+  return 256 * (t >> 3) + 16 * (4 * ((t & 7) >> 1) + g) + 8 * (t & 1);
+}
+
+__global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) {
+  constexpr int D = kPairD;
+  constexpr int KS = D / 32;     // k-steps of the whole S contraction
+  constexpr int KSH = KS / 2;    // k-steps of a half
+  constexpr int NBH = D / 2 / 16;  // 16-dim column blocks of a half's O
+  using PT = PairTile;
+  constexpr int kPer = kMaxSplitRows / kPairThreads;  // rows each lane resolves: 2
+  __shared__ __attribute__((aligned(16))) uint8_t tile0_s[kPairs * PT::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t tile1_s[kPairs * PT::BYTES];
+  // rotated query fragments; once every wave holds its half in registers, the
+  // same memory carries the partial S of each wave to its partner
+  __shared__ __attribute__((aligned(16))) f16x8 q_s[KS][64];
+  __shared__ float qam_s[kPairWaves][kHeadsPerBlock];
+  __shared__ float2 cs_s[D / 2];
+  __shared__ uint64_t rowptr_s[kMaxSplitRows];
+  __shared__ __attribute__((aligned(16))) float ps_s[kMaxSplitRows];  // page scale; -1: skipped row
+  __shared__ float2 ml_s[kPairs][kHeadsPerBlock];
+  __shared__ __attribute__((aligned(16))) float wt_s[kPairs][kHeadsPerBlock];
+  static_assert(sizeof(q_s) == (size_t)kPairWaves * 2 * 64 * sizeof(f32x4), "partial S exchange area");
+  static_assert(2 * sizeof(float) * kHeadsPerBlock * D <= kPairs * PT::BYTES, "the merge reuses the tiles");
+
+  int s, b, hb;
+  {
+    const int id = blockIdx.x, HB = a.plan.head_blocks;
+    const int j = id / kXcds;
+    const int grp = (j / HB) * kXcds + id % kXcds;  // (split, sequence) pair
+    if (grp >= (int64_t)a.plan.splits * a.B) return;
+    hb = j % HB;
+    s = grp % a.plan.splits;
+    b = grp / a.plan.splits;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pair = wave >> 1, hf = wave & 1;
+  const int col = lane & 15, g = lane >> 4;
+  const int RPS = a.plan.rows_per_split;
+  const int r0 = s * RPS;
+  // rows of the pair's tiles, split over its two waves: lane l of wave
+  // (pair, hf) resolves row l % 32 of the pair's tiles 4j + 2hf + l / 32
+  auto row_of = [&](int j) { return kTileRows * (pair + kPairs * (4 * j + 2 * hf + (lane >> 5))) + (lane & 31); };
+  int pre[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = row_of(j);
+    const int r = r0 + i;
+    pre[j] = 0;
+    if (i < RPS) {
+      if (a.sel != nullptr)
+        pre[j] = gload<int>(a.sel + (int64_t)b * a.k + min(r, a.k - 1));
+      else
+        pre[j] = gload<int>(a.bt + (int64_t)b * a.bts + min(r >> __builtin_ctz(a.kv.epp), a.bts - 1));
+    }
+  }
+  const int H = a.H;
+  const int h0 = hb * kHeadsPerBlock;
+  const int head = h0 + col;
+  // query: each wave loads and rotates 2 of the 16 k-steps
+  constexpr int KSW = KS / kPairWaves;
+  const int tq0 = wave * KSW;
+  const bool hv = head < H;
+  u32x4 qraw[KSW];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)b * H + (hv ? head : H - 1)) * D;
+#pragma unroll
+    for (int i = 0; i < KSW; ++i) qraw[i] = gload<u32x4>(qrow + pair_kdim(tq0 + i, g));
+  }
+  const int L = clampi(a.lens[b], 0, a.max_len);
+  const int N = (L + a.m - 1) / a.m;
+  const int n_sel = a.sel ? clampi(a.sel_n[b], 0, a.k) : N;
+  const int n_win = min(a.window, L);
+  const int rows_b = n_sel + n_win;
+  const int r1 = min(rows_b, r0 + RPS);
+  float2* ml = reinterpret_cast<float2*>(a.ws + a.plan.ml_off);
+  float* opart = reinterpret_cast<float*>(a.ws + a.plan.o_off);
+  const size_t part = ((size_t)b * a.plan.splits + s) * H;
+
+  if (r0 >= r1) {  // empty split (the whole block returns)
+    if (threadIdx.x < kHeadsPerBlock && h0 + (int)threadIdx.x < H)
+      ml[part + h0 + threadIdx.x] = make_float2(-INFINITY, 0.0f);
+    return;
+  }
+
+  // ---- RoPE table at the query position L-1
+  for (int i = threadIdx.x; i < D / 2; i += kPairThreads) {
+    float c, sn;
+    rope_cs((double)(L - 1), rope_inv_freq(i, a.rope_r), c, sn);
+    cs_s[i] = make_float2(c, sn);
+  }
+  lds_barrier();
+
+  // ---- rotated query fragments, scaled per head by a power of two that puts
+  // the head's largest |value| in [2^13, 2^14) (exact in f16); each wave then
+  // keeps its half's 8 k-steps in registers
+  float hfac;
+  f16x8 qf[KSH];
+  {
+    float y[KSW][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < KSW; ++i) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float x0 = u2f(qraw[i][p] << 16), x1 = u2f(qraw[i][p] & 0xFFFF0000u);
+        const float2 cs = cs_s[pair_kdim(tq0 + i, g) / 2 + p];
+        y[i][2 * p] = x0 * cs.x - x1 * cs.y;
+        y[i][2 * p + 1] = x0 * cs.y + x1 * cs.x;
+        amax = fmaxf(amax, fmaxf(fabsf(y[i][2 * p]), fabsf(y[i][2 * p + 1])));
+      }
+    }
+    amax = rows_max4(amax);
+    if (g == 0) qam_s[wave][col] = amax;
+    lds_barrier();
+    amax = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kPairWaves; ++w) amax = fmaxf(amax, qam_s[w][col]);
+    int e = 0;
+    if (amax > 0.0f) (void)frexpf(amax, &e);  // amax < 2^e
+    const float qs = ldexpf(1.0f, min(14 - e, 126));
+    hfac = a.scale / qs * 1.4426950408889634f;  // logits in base 2: p = 2^(x - m)
+#pragma unroll
+    for (int i = 0; i < KSW; ++i) {
+      f16x8 v;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[c] = (_Float16)(y[i][c] * qs);
+      q_s[tq0 + i][lane] = v;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int t = 0; t < KSH; ++t) qf[t] = q_s[KSH * hf + t][lane];
+  }
+
+  // ---- rows: addresses and page scales
+  float ps[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = row_of(j);
+    const int r = r0 + i;
+    uint64_t rp = 0;
+    bool in_win = false;
+    int sidx = 0;
+    if (i < RPS && r < r1) rp = resolve_row(a, b, r, pre[j], pre[j], n_sel, N, L, n_win, D, in_win, sidx);
+    if (i < RPS) rowptr_s[i] = rp;
+    const float* sc = reinterpret_cast<const float*>(in_win ? a.win.scales : a.kv.scales);
+    ps[j] = rp ? gload<float>(sc + sidx) : -1.0f;
+  }
+  // the partner's row addresses are needed for this wave's loads, and every
+  // wave is done reading the query fragments before they are overwritten by
+  // partial S (LDS only: the scale loads stay in flight)
+  lds_barrier();
+
+  const int nt = (r1 - r0 + kTileRows - 1) / kTileRows;
+  const uint8_t* safe = reinterpret_cast<const uint8_t*>(a.kv.codes);
+  uint8_t* slot0 = tile0_s + pair * PT::BYTES;
+  uint8_t* slot1 = tile1_s + pair * PT::BYTES;
+  // this wave's half of tile t into a slot (skipped rows read the pool's
+  // first row; their bytes are masked where they matter)
+  // (the row addresses are read from LDS first, all of them: the loads are
+  // inline assembly that the compiler does not move LDS reads across)
+  auto issue = [&](int t, uint8_t* dst) {
+    const int lr0 = kTileRows * t;
+    uint64_t rp[PT::INSTR];
+#pragma unroll
+    for (int j = 0; j < PT::INSTR; ++j) rp[j] = rowptr_s[lr0 + (64 * j + lane) / PT::CHH];
+#pragma unroll
+    for (int j = 0; j < PT::INSTR; ++j) {
+      const int pos = 64 * j + lane;  // chunk position this lane fills in the half
+      const int r = pos / PT::CHH, p = pos % PT::CHH;
+      const int cc = p ^ PT::f(r);  // the data chunk stored there
+      const uint8_t* src = (rp[j] ? reinterpret_cast<const uint8_t*>(rp[j]) : safe) + (D / 2) * hf + 16 * cc;
+      load_to_lds16(src, dst + PT::HALF_BYTES * hf + 1024 * j);
+    }
+  };
+  if (pair < nt) issue(pair, slot0);
+  if (pair + kPairs < nt) issue(pair + kPairs, slot1);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (row_of(j) < RPS) ps_s[row_of(j)] = ps[j];
+  lds_barrier();  // every row's page scale is visible to both waves of its pair
+
+  f32x4 oacc[NBH];  // O for the 16 heads (rows 4g + i) over dims 256 hf + 16n + col, in units of sigma
+#pragma unroll
+  for (int n = 0; n < NBH; ++n) oacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;  // the same in both waves of a pair
+  float sigma = 0.0f, inv_sigma = 0.0f;
+  f32x4* xs = reinterpret_cast<f32x4*>(&q_s[0][0]);  // [wave][h][lane]: partial S
+
+  // ---- this wave's partial S^T = K[:, half] . Q~[:, half]^T for the tile's two 16-row halves
+  auto qk_half = [&](const uint8_t* tile, f32x4 sres[2]) {
+    f32x4 sacc[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) sacc[h][0] = sacc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < KSH / 2; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(tile + PT::at(hf, 16 * h + col, 4 * u + g));
+        f16x8 v0, v1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f16x2 x = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w[q], 1.0f, false);
+          const f16x2 y = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w[q], 1.0f, true);
+          f16x8& dst = q < 2 ? v0 : v1;
+          const int o = (q & 1) * 4;
+          dst[o + 0] = x[0];
+          dst[o + 1] = x[1];
+          dst[o + 2] = y[0];
+          dst[o + 3] = y[1];
+        }
+        sacc[h][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v0, qf[2 * u], sacc[h][0], 0, 0, 0);
+        sacc[h][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v1, qf[2 * u + 1], sacc[h][1], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) sres[h] = sacc[h][0] + sacc[h][1];
+  };
+
+  // ---- online softmax and page-scale normalization (as in the 4-wave kernel)
+  auto softmax = [&](int t, const f32x4 sres[2], f16x8& pf, uint32_t vmask[2]) {
+    const int lr0 = kTileRows * t;
+    float x[8], sc[8];
+    float tmax = -INFINITY, tsig = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 rq = *reinterpret_cast<const f32x4*>(&ps_s[lr0 + 16 * h + 4 * g]);
+      vmask[h] = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = rq[i] >= 0.0f;  // also false past the end of the split
+        vmask[h] |= ok ? 0xFFu << (8 * i) : 0u;
+        sc[4 * h + i] = ok ? rq[i] : 0.0f;
+        const float v = ok ? sres[h][i] * rq[i] * hfac : -INFINITY;
+        x[4 * h + i] = v;
+        tmax = fmaxf(tmax, v);
+        tsig = fmaxf(tsig, sc[4 * h + i]);
+      }
+    }
+    tmax = rows_max4(tmax);
+    tsig = rows_max4(tsig);
+    const bool need = tmax > m_run + kRescaleSlack;
+    const bool grow = tsig > sigma * kSigmaSlack;
+    if (__any(need) || grow) {
+      const float m_new = need ? tmax : m_run;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      const float fs = grow ? sigma / tsig : 1.0f;
+      if (__any(m_run != -INFINITY)) {
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64) * fs;  // factor of head 4g + i
+#pragma unroll
+        for (int n = 0; n < NBH; ++n) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[n][i] *= al[i];
+        }
+      }
+      l_run *= alpha;
+      m_run = m_new;
+      if (grow) {
+        sigma = tsig;
+        inv_sigma = 1.0f / tsig;
+      }
+    }
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = x[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[j] - m_run);
+      psum += p;
+      pf[j] = (_Float16)(p * (sc[j] * inv_sigma));
+    }
+    l_run += rows_sum4(psum);
+  };
+
+  // ---- O[:, half] += P . V[:, half]
+  auto pv_half = [&](const uint8_t* tile, const f16x8& pf, const uint32_t vmask[2]) {
+    const int k = col >> 1;
+    const int vrow = k < 4 ? 4 * g + k : 16 + 4 * g + k - 4;
+    const int half8 = 8 * (col & 1);
+    u32x2 raw8[NBH];
+#pragma unroll
+    for (int n = 0; n < NBH; ++n) {
+      const i2v r8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) i2v*)(tile + PT::at(hf, vrow, n) + half8));
+      raw8[n] = __builtin_bit_cast(u32x2, r8);
+    }
+#pragma unroll
+    for (int n = 0; n < NBH; ++n) {
+      const uint32_t lo = raw8[n][0] & vmask[0], hi = raw8[n][1] & vmask[1];
+      const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)lo, 1.0f, false);
+      const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)lo, 1.0f, true);
+      const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)hi, 1.0f, false);
+      const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)hi, 1.0f, true);
+      const f16x8 vf = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+      oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, vf, oacc[n], 0, 0, 0);
+    }
+  };
+
+  // ---- the pair's tiles pair, pair + 4, ...: every wave runs the same number
+  // of steps (the block's barriers are not inside any condition); a pair with
+  // fewer tiles idles through its last step.  Tile t is in ring slot st & 1 and
+  // tile t + 4 may still be loading behind it; a slot is refilled with tile
+  // t + 8 once this wave's reads of its half are done.
+  const int nsteps = (nt + kPairs - 1) / kPairs;
+  for (int st = 0; st < nsteps; ++st) {
+    const int t = pair + kPairs * st;
+    const bool act = t < nt;
+    uint8_t* slot = (st & 1) ? slot1 : slot0;
+    f32x4 sres[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if (act) {
+      if (t + kPairs < nt)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PT::INSTR));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      asm volatile("" ::: "memory");
+      qk_half(slot, sres);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) xs[(wave * 2 + h) * 64 + lane] = sres[h];
+    }
+    lds_barrier();  // partial S of both waves of every pair in LDS
+    if (act) {
+      // the full S: half 0's partial plus half 1's, the same sum in both waves
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 o = xs[((wave ^ 1) * 2 + h) * 64 + lane];
+        sres[h] = hf == 0 ? sres[h] + o : o + sres[h];
+      }
+      f16x8 pf;
+      uint32_t vmask[2];
+      softmax(t, sres, pf, vmask);
+      pv_half(slot, pf, vmask);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & ~0x0F00);  // lgkmcnt(0): the slot's reads are done
+      asm volatile("" ::: "memory");
+      if (t + 2 * kPairs < nt) issue(t + 2 * kPairs, slot);
+    }
+    lds_barrier();  // the partner has read this wave's partial before the next one is written
+  }
+
+  // ---- merge the four pairs' states
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load into the tiles is in flight
+  __syncthreads();
+  // pair p's O: [4 head quads][D][4 heads] floats in the tile memory, dims of half hf from its wave
+  auto o_of = [&](int p) { return reinterpret_cast<float*>((p < 2 ? tile0_s : tile1_s) + (p & 1) * 64 * D); };
+  {
+    float* o_s = o_of(pair);
+#pragma unroll
+    for (int n = 0; n < NBH; ++n)
+      *reinterpret_cast<f32x4*>(&o_s[(g * D + (D / 2) * hf + 16 * n + col) * 4]) = oacc[n] * sigma;
+  }
+  if (hf == 0 && g == 0) ml_s[pair][col] = make_float2(m_run, l_run);
+  __syncthreads();
+  if (threadIdx.x < kHeadsPerBlock) {
+    const int hh = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < kPairs; ++p) M = fmaxf(M, ml_s[p][hh].x);
+    float l = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kPairs; ++p) {
+      const float wt = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml_s[p][hh].x - M);  // 0 for an idle pair
+      wt_s[p][hh] = wt;
+      l += wt * ml_s[p][hh].y;
+    }
+    if (h0 + hh < H)
+      ml[part + h0 + hh] = M == -INFINITY ? make_float2(-INFINITY, 0.0f) : make_float2(M * 0.6931471805599453f, l);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < D * (kHeadsPerBlock / 4); e += kPairThreads) {
+    const int hq = e / D, dim = e - hq * D;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < kPairs; ++p) {
+      const f32x4 o = *reinterpret_cast<const f32x4*>(&o_of(p)[(hq * D + dim) * 4]);
+      const f32x4 wt = *reinterpret_cast<const f32x4*>(&wt_s[p][4 * hq]);
+      acc += wt * o;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int h = h0 + 4 * hq + k;
+      if (h < H) opart[(part + h) * D + dim] = acc[k];
+    }
+  }
+}
+
 // Merge the splits of one (sequence, head), then inverse RoPE at L-1.  The
 // threads form SG split groups; a group's lanes cover the D dims with 16-byte
 // loads and the group takes every SG-th split.  All partial loads of a round
@@ -844,7 +1263,10 @@ static hipError_t launch_split(const AttnArgs& a, hipStream_t s) {
   const int64_t groups = (int64_t)a.plan.splits * a.B;
   const int64_t blocks = (groups + kXcds - 1) / kXcds * kXcds * a.plan.head_blocks;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_split_kernel<D, KVDT>), dim3((unsigned)blocks), dim3(kAttnThreads), 0, s, a);
+  if constexpr (D == kPairD && KVDT == HCA_FP8_E4M3)
+    hipLaunchKernelGGL(attn_pair_kernel, dim3((unsigned)blocks), dim3(kPairThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<D, KVDT>), dim3((unsigned)blocks), dim3(kAttnThreads), 0, s, a);
   return hipGetLastError();
 }
 

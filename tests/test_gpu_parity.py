@@ -689,10 +689,11 @@ def test_attention_layout_invariance_bitwise():
         assert np.array_equal(out, base_out) and np.array_equal(lse, base_lse), trial
 
 
-def test_attention_skips_invalid_indices_and_empty_sequences():
-    H.flush("attention invalid / empty")
+@pytest.mark.parametrize("d", [128, 512])
+def test_attention_skips_invalid_indices_and_empty_sequences(d):
+    H.flush(f"attention invalid / empty d={d}")
     kind = synth.LayerKind("c4a", 4, 64, "fp8", 128)
-    w = _attn_workload("fp8", 128, 16, 0, kind, 2)
+    w = _attn_workload("fp8", d, 16, 0, kind, 2)
     sd = H.SeqData(w, 0, [1000, 1])
     good = np.arange(0, 250, 5)
     sel = [np.concatenate([good, [-3, 250, 10 ** 6]]), np.zeros(0, np.int64)]
