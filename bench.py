@@ -76,7 +76,10 @@ def parse():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=0, help="debug only: first N layers (result is not the workload)")
-    ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated per step (0: auto)")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="copies of a single-layer workload's caches, one per timed step in turn, so that one "
+                         "step's pages are not still in the Infinity Cache from the step before (0: 4 for a "
+                         "single-layer workload, 1 otherwise)")
     return ap.parse_args()
 
 
@@ -136,9 +139,11 @@ class Layer:
     pass
 
 
-def build_state(w, n_layers, torch, hca, gen, log):
+def build_state(w, n_layers, torch, hca, gen, log, replicas=1):
     """Fill every layer's pools with a GPU prefill pass; keep the decode-update
-    state.  Returns (layers, prefill stats)."""
+    state.  With replicas > 1 every layer is built that many times over (own
+    pools and inputs: layer index li takes the kind of layer li % n_layers).
+    Returns (layers, prefill stats)."""
     B, L, d, H, W = w.B, w.L, w.d, w.H, w.window
     lens_np = np.full((B,), L, np.int32)
     table_np, P, wtable_np, PW = gen.block_tables(w, lens_np)
@@ -148,8 +153,8 @@ def build_state(w, n_layers, torch, hca, gen, log):
     layers = []
     pre_ms, pre_bytes = 0.0, 0.0
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for li in range(n_layers):
-        kind = w.layers[li]
+    for li in range(n_layers * replicas):
+        kind = w.layers[li % n_layers]
         m, epp = kind.m, 256 // kind.m
         N = -(-L // m)
         lay = Layer()
@@ -486,6 +491,10 @@ def pool_packing(w, hca):
 # ----------------------------------------------------------------- main
 
 
+METRIC_WORKLOAD = {4: "1M-token 61-layer stack", 2: "128K-token c4a layer, batch 16",
+                   1: "64K-token c128a layer, batch 8", 0: "4K-token c4a layer, batch 1"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -508,8 +517,9 @@ def main():
         print("bench.py times fixed-length workloads (configs 0, 1, 2, 4)", file=sys.stderr)
         sys.exit(2)
     n_layers = len(w.layers) if args.layers <= 0 else min(args.layers, len(w.layers))
-    log(f"workload {w.name}: B={w.B} L={w.L} layers={n_layers}")
-    layers, shared, pre = build_state(w, n_layers, torch, hca, gen, log)
+    R = args.replicas if args.replicas > 0 else (4 if n_layers == 1 else 1)
+    log(f"workload {w.name}: B={w.B} L={w.L} layers={n_layers} replicas={R}")
+    layers, shared, pre = build_state(w, n_layers, torch, hca, gen, log, replicas=R)
     # workspaces (one per kind; the indexer one must start zeroed and is left zeroed)
     kinds = {l.kind.name: l.kind for l in layers}
     ws_idx = None
@@ -523,15 +533,18 @@ def main():
     log("capturing decode step")
     t_step, wall, _g = time_graph(torch, lambda: decode_step(w, layers, shared, ws_idx, ws_att, hca), args.steps,
                                   args.warmup)
+    t_step /= R
     log(f"step {t_step:.3f} ms")
     t_attn, _, _g2 = time_graph(torch, lambda: decode_step(w, layers, shared, ws_idx, ws_att, hca, update=False),
                                 args.steps, args.warmup)
     t_upd, _, _g3 = time_graph(torch, lambda: decode_step(w, layers, shared, ws_idx, ws_att, hca, attend=False),
                                args.steps, args.warmup)
+    t_attn /= R
+    t_upd /= R
     dom = time_dominant(torch, hca, w, layers, shared)
     copy_gbs = copy_bandwidth(torch)
-    alg = sum(layer_bytes(l.kind, w.B, w.L, w.d, w.H, w.window) for l in layers)
-    upd = sum(update_bytes(l.kind, w.B, w.d) for l in layers)
+    alg = sum(layer_bytes(l.kind, w.B, w.L, w.d, w.H, w.window) for l in layers) / R
+    upd = sum(update_bytes(l.kind, w.B, w.d) for l in layers) / R
     roofline = None
     if dom is not None:
         kind = [l.kind for l in layers if l.kind.topk is not None][0]
@@ -540,7 +553,7 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_of(kind),
                     "frac_of_measured_copy": round(achieved / copy_gbs, 4), "measured_copy_GBps": round(copy_gbs, 1),
-                    "kernel": "score_kernel<fp4,128> (indexer scoring)", "bytes_per_launch": int(sb),
+                    "kernel": f"score_kernel<{kind.idx_dtype},128> (indexer scoring)", "bytes_per_launch": int(sb),
                     "avg_launch_ms": round(dom[0], 5), "median_of_batches_ms": round(dom[1], 5), "launches": dom[2]}
     cpu = None
     if not args.no_cpu_baseline and n_layers == len(w.layers):
@@ -548,7 +561,7 @@ def main():
         cpu = cpu_baseline(w)
     value = w.B / (t_step * 1e-3)
     res = {
-        "metric": "decode-attn tokens/sec per GPU (1M-token 61-layer stack)",
+        "metric": f"decode-attn tokens/sec per GPU ({METRIC_WORKLOAD.get(args.config, w.name)})",
         "value": round(value, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -558,13 +571,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8 KV / fp4 idx, f16+bf16 MFMA, fp32 acc",
+        "dtype": (f"{w.kv_dtype} KV" + "".join(sorted({f" / {l.kind.idx_dtype} idx" for l in layers if l.kind.idx_dtype}))
+                  + ", f16+bf16 MFMA, fp32 acc"),
         "data": ("synthetic (seeded N(0,1) tokens, logits, queries, indexer keys; U(0.5, 1.5) RMSNorm gains; "
                  "random page permutation)"),
         "config": {"workload": w.name, "batch": w.B, "context": w.L, "layers": n_layers,
-                   "c4a_layers": sum(1 for l in layers if l.kind.name == "c4a"),
-                   "c128a_layers": sum(1 for l in layers if l.kind.name == "c128a"), "d": w.d, "heads": w.H,
-                   "window": w.window, "topk": 2048, "parallelism": "single GPU"},
+                   "c4a_layers": sum(1 for l in layers if l.kind.name == "c4a") // R,
+                   "c128a_layers": sum(1 for l in layers if l.kind.name == "c128a") // R, "d": w.d, "heads": w.H,
+                   "window": w.window, "topk": max([l.kind.topk or 0 for l in layers]) or None,
+                   "cache_replicas": R, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "step_breakdown": {
@@ -578,7 +593,7 @@ def main():
             "update_only_ms": round(t_upd, 4),
             "wall_s_timed_region": round(wall, 4),
         },
-        "prefill": {"ms_all_layers": round(pre["ms"], 3), "bytes": int(pre["bytes"]),
+        "prefill": {"ms_all_layers": round(pre["ms"] / R, 3), "bytes": int(pre["bytes"] / R),
                     "GBps": round(pre["bytes"] / (pre["ms"] * 1e-3) / 1e9, 1) if pre["ms"] > 0 else None,
                     "what": "kv_compress + kv_quantize_page over the whole context of every layer"},
         "page_pool": pool_packing(w, hca),
