@@ -48,7 +48,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 SCORE_TRAFFIC = {"source_sha256": "49fa57889b87d368f32ff58e5e31cedd882ef050078739a4b0ee8cab0608e212",
                  "fetch_bytes": 71889905, "write_bytes": 4599286}
 SCORE_SOURCES = ("decode_attention_compressed_amd/csrc/indexer.hip", "decode_attention_compressed_amd/csrc/hca_common.h",
-                 "decode_attention_compressed_amd/csrc/indexer_internal.h")
+                 "decode_attention_compressed_amd/csrc/indexer_internal.h",
+                 "decode_attention_compressed_amd/csrc/indexer_score.h")
 
 
 def score_source_sha256():
@@ -256,10 +257,14 @@ def build_state(w, n_layers, torch, hca, gen, log, replicas=1):
 
 
 def decode_step(w, layers, shared, ws_idx, ws_att, hca, update=True, attend=True):
-    """One decode step of the stack.  Per layer, the update is one launch (the
-    window insert with its page, the open group's re-fold with its page and,
-    for c4a, the open indexer page), then the indexer (c4a) and the attention,
-    which the next layer's update waits for."""
+    """One decode step of the stack.  Per layer: the update (the window insert
+    with its page, the open group's re-fold with its page and, for c4a, the
+    open indexer page), the indexer (c4a) and the attention, which the next
+    layer's update waits for.  c128a: the update is one launch.  c4a: the open
+    indexer page is one small launch, and the window insert and the open entry
+    run as extra blocks of the indexer's last select launch
+    (indexer_topk_with_updates).
+    The attend-only and update-only variants make the calls separately."""
     import torch
     L, W = w.L, w.window
     table, wtable, lens = shared["table"], shared["wtable"], shared["lens"]
@@ -267,18 +272,25 @@ def decode_step(w, layers, shared, ws_idx, ws_att, hca, update=True, attend=True
     for lay in layers:
         kind = lay.kind
         m = kind.m
-        if update:
-            jobs = [hca.insert_job(lay.wstage, lay.wpos0, lay.we0, wtable, lay.win, 1, x=lay.x_last,
-                                   gate_logit=lay.z_last, pos_bias=lay.zero1, ntok=lay.one, rope_theta=w.theta,
-                                   append=True),
-                    hca.insert_job(lay.stage, lay.pos0, lay.e0, table, lay.kv, m, x=lay.x_open, gate_logit=lay.z_open,
-                                   pos_bias=lay.beta, ntok=lay.ntok, rope_theta=w.theta, append=True,
-                                   norm_gamma=lay.gamma, overlap=kind.overlap, fold_state=lay.fstate)]
-            if kind.topk is not None:
-                jobs.append(hca.insert_job(lay.istage, lay.pos0, lay.e0, table, lay.idx, m, append=True))
-            hca.kv_compress_insert_jobs(jobs, w.B)
-        if attend and kind.topk is not None:
-            hca.indexer_topk(lay.qi, lay.wi, lay.idx, table, lens, L, m, kind.topk, lay.sel, lay.sel_n, ws_idx)
+        jobs = [hca.insert_job(lay.wstage, lay.wpos0, lay.we0, wtable, lay.win, 1, x=lay.x_last,
+                               gate_logit=lay.z_last, pos_bias=lay.zero1, ntok=lay.one, rope_theta=w.theta,
+                               append=True),
+                hca.insert_job(lay.stage, lay.pos0, lay.e0, table, lay.kv, m, x=lay.x_open, gate_logit=lay.z_open,
+                               pos_bias=lay.beta, ntok=lay.ntok, rope_theta=w.theta, append=True,
+                               norm_gamma=lay.gamma, overlap=kind.overlap, fold_state=lay.fstate)]
+        idx_job = (hca.insert_job(lay.istage, lay.pos0, lay.e0, table, lay.idx, m, append=True)
+                   if kind.topk is not None else None)
+        if update and attend and kind.topk is not None:
+            # the open indexer page first (the score reads it), then the
+            # indexer with the window insert and the open entry's update beside it
+            hca.kv_compress_insert_jobs([idx_job], w.B)
+            hca.indexer_topk_with_updates(lay.qi, lay.wi, lay.idx, table, lens, L, m, kind.topk, lay.sel, lay.sel_n,
+                                          ws_idx, jobs)
+        else:
+            if update:
+                hca.kv_compress_insert_jobs(jobs + ([idx_job] if idx_job is not None else []), w.B)
+            if attend and kind.topk is not None:
+                hca.indexer_topk(lay.qi, lay.wi, lay.idx, table, lens, L, m, kind.topk, lay.sel, lay.sel_n, ws_idx)
         if attend:
             if kind.topk is not None:
                 hca.paged_hybrid_decode(lay.q, lay.kv, table, lay.win, wtable, lens, L, m, W, lay.sel, lay.sel_n,

@@ -31,7 +31,7 @@ EXPORTS = (
     "kv_quantize_page_workspace",
     "kv_quantize_page",
     "indexer_topk_workspace",
-    "indexer_topk", "paged_hybrid_decode_workspace", "paged_hybrid_decode", "kv_gather",
+    "indexer_topk", "indexer_topk_with_updates", "paged_hybrid_decode_workspace", "paged_hybrid_decode", "kv_gather",
     "hca_host_e4m3_encode", "hca_host_e2m1_encode", "hca_host_bf16_encode", "hca_probe_decode", "hca_probe_mfma",
     "hca_indexer_score",
     "hca_page_bytes", "hca_pool_plan", "hca_pool_create", "hca_pool_destroy", "hca_pool_view", "hca_pool_bucket",
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.indexer_topk_workspace.argtypes = [_I32, _I32, _I32, _I32]
         L.indexer_topk_workspace.restype = _SZ
         L.indexer_topk.argtypes = [_P, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]
+        L.indexer_topk_with_updates.argtypes = [_P, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P,
+                                                _P, _SZ, ctypes.POINTER(CInsertJob), _I32, _P]
         L.paged_hybrid_decode_workspace.argtypes = [_I32, _I32, _I32, _I32, _I32, _I32, _I32]
         L.paged_hybrid_decode_workspace.restype = _SZ
         L.paged_hybrid_decode.argtypes = [_P, _I32, CPagedCache, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32,
@@ -252,6 +254,18 @@ def indexer_topk(q_idx, head_w, idx_keys: PagedCache, block_table, seq_lens, max
     _check(lib().indexer_topk(_ptr(q_idx), _ptr(head_w), HI, idx_keys.c(), _ptr(block_table),
                               block_table.stride(0), _ptr(seq_lens), B, max_seq_len, m, k, _ptr(out_idx),
                               _ptr(out_n), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "indexer_topk")
+
+
+def indexer_topk_with_updates(q_idx, head_w, idx_keys: PagedCache, block_table, seq_lens, max_seq_len: int, m: int,
+                              k: int, out_idx, out_n, ws, jobs, stream=None):
+    """indexer_topk with update jobs (insert_job(...) descriptors, none writing idx_keys) run beside its score pass;
+    the same results as kv_compress_insert_jobs(jobs, B) then indexer_topk(...)."""
+    B, HI, _ = q_idx.shape
+    arr = (CInsertJob * max(len(jobs), 1))(*jobs)
+    _check(lib().indexer_topk_with_updates(_ptr(q_idx), _ptr(head_w), HI, idx_keys.c(), _ptr(block_table),
+                                           block_table.stride(0), _ptr(seq_lens), B, max_seq_len, m, k, _ptr(out_idx),
+                                           _ptr(out_n), _ptr(ws), ws.numel() * ws.element_size(), arr, len(jobs),
+                                           _stream(stream)), "indexer_topk_with_updates")
 
 
 def indexer_score(q_idx, head_w, idx_keys: PagedCache, block_table, seq_lens, max_seq_len: int, m: int, k: int, ws,

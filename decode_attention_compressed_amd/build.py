@@ -35,6 +35,7 @@ FLAGS = [
 # VALU code and carried around the tile loop; in AGPRs it was copied out and
 # back on every tile.
 EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "compress.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

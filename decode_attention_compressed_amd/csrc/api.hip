@@ -207,6 +207,32 @@ hca_status indexer_topk(const uint16_t* q_idx, const float* head_w, int32_t HI, 
   return from_hip(launch_indexer(a, (hipStream_t)stream));
 }
 
+hca_status indexer_topk_with_updates(const uint16_t* q_idx, const float* head_w, int32_t HI,
+                                     hca_paged_cache idx_keys, const int32_t* block_table, int32_t bt_stride,
+                                     const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t m, int32_t k,
+                                     int32_t* out_idx, int32_t* out_n, void* ws, size_t ws_bytes,
+                                     const hca_insert_job* jobs, int32_t n_jobs, void* stream) {
+  IndexerArgs a{};
+  const hca_status st = indexer_prepare(q_idx, head_w, HI, idx_keys, block_table, bt_stride, seq_lens, B, max_seq_len,
+                                        m, k, out_idx, out_n, true, ws, ws_bytes, a);
+  if (st != HCA_OK) return st;
+  if (n_jobs < 0 || (n_jobs > 0 && !jobs)) return HCA_ERR_INVALID;
+  if (n_jobs > kMaxInsertJobs) return HCA_ERR_UNSUPPORTED;
+  InsertJobs all{};
+  for (int i = 0; i < n_jobs; ++i) {
+    if (jobs[i].dst.codes == idx_keys.codes) return HCA_ERR_INVALID;  // would race with the score reads
+    const hca_status sj = make_insert(jobs[i], B, all.job[i]);
+    if (sj != HCA_OK) return sj;
+  }
+  all.n = n_jobs;
+  if (B == 0) return HCA_OK;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_indexer_score(a, s);
+  if (e == hipSuccess) e = launch_select_chunk(a, s);
+  if (e == hipSuccess) e = launch_compact_insert(a, all, s);
+  return from_hip(e);
+}
+
 hca_status hca_indexer_score(const uint16_t* q_idx, const float* head_w, int32_t HI, hca_paged_cache idx_keys,
                              const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens, int32_t B,
                              int32_t max_seq_len, int32_t m, int32_t k, void* ws, size_t ws_bytes, void* stream) {

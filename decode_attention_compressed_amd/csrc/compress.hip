@@ -22,6 +22,8 @@
 // and a fold gives the same bits wherever it runs.
 #include "hca_common.h"
 #include "hca_internal.h"
+#include "indexer_internal.h"
+#include "indexer_select.h"
 
 namespace hca {
 
@@ -713,6 +715,38 @@ hipError_t launch_insert(InsertJobs j, int B, hipStream_t s) {
     j.job[i].c.rope_r = pow((double)j.job[i].c.theta, -2.0 / (double)j.job[i].c.d);
   }
   hipLaunchKernelGGL(insert_kernel, dim3(B, j.n), dim3(kCompressThreads), kCompressShm, s, j);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------- select with the updates
+// V4 page, section 3.2.2: the indexer runs beside the main-KV compression and
+// the window insert.  Here the updates are extra blocks of the select's
+// compaction launch: block i < n_jobs of row y runs update job i for sequence
+// y, block n_jobs + x of row y compacts chunks 2x and 2x + 1 of sequence y.
+// The blocks are independent (the jobs write no indexer data), and the
+// compaction, like the updates, is a short chain of dependent loads with
+// little traffic, so the updates run in its shadow.  The kernel's register
+// count is the update path's (two blocks per CU); with two chunks per
+// compaction block every block of the launch is resident at once.
+static_assert(kCompressThreads == kSelThreads, "one block size for both kinds of block");
+
+__global__ __launch_bounds__(kCompressThreads) void compact_insert_kernel(IndexerArgs a, InsertJobs j) {
+  __shared__ SelLds sm;
+  __shared__ uint32_t wbits_s[kCompactChunks * kSelChunk / 32];
+  __shared__ __attribute__((aligned(16))) float row_s[kInsertMaxDim];
+  __shared__ float red_s[kCompressThreads / 64];
+  if ((int)blockIdx.x < j.n)
+    insert_block(j.job[blockIdx.x], blockIdx.y, row_s, red_s);
+  else
+    select_compact_block(a, blockIdx.x - j.n, blockIdx.y, sm, wbits_s);
+}
+
+hipError_t launch_compact_insert(const IndexerArgs& a, const InsertJobs& jobs, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  InsertJobs j = jobs;
+  for (int i = 0; i < j.n; ++i) j.job[i].c.rope_r = pow((double)j.job[i].c.theta, -2.0 / (double)j.job[i].c.d);
+  hipLaunchKernelGGL(compact_insert_kernel, dim3(j.n + compact_blocks(a), a.B), dim3(kCompressThreads), kCompressShm,
+                     s, a, j);
   return hipGetLastError();
 }
 

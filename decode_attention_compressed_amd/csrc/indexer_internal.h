@@ -29,5 +29,14 @@ struct IndexerArgs {
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
 hipError_t launch_indexer_score(const IndexerArgs& a, hipStream_t s);
+// the select launches that follow a score pass (cut and bitmap, then the
+// ascending compaction), and the first of them alone
+hipError_t launch_select(const IndexerArgs& a, hipStream_t s);
+hipError_t launch_select_chunk(const IndexerArgs& a, hipStream_t s);
+struct InsertJobs;
+// the compaction launch of the select with a decode step's cache updates as
+// extra blocks of the same launch (after launch_select_chunk); the jobs must
+// not write the indexer keys
+hipError_t launch_compact_insert(const IndexerArgs& a, const InsertJobs& j, hipStream_t s);
 
 }  // namespace hca

@@ -303,6 +303,27 @@ hca_status indexer_topk(const uint16_t* q_idx, const float* head_w, int32_t HI,
                         void* stream);
 
 /*
+ * indexer_topk_with_updates -- indexer_topk with a decode step's cache updates
+ * run beside its score pass (V4 page, section 3.2.2: the indexer overlaps the
+ * main-KV compression and the window insert).  The result is that of
+ * kv_compress_insert_jobs(jobs, n_jobs, B) followed by indexer_topk(...): the
+ * same bytes in every output and page.  The updates run as extra blocks of
+ * the select's last launch, after the score pass has read the keys.
+ *
+ * The jobs must therefore not write the indexer keys being scored (a job whose
+ * dst.codes is idx_keys.codes is rejected with HCA_ERR_INVALID): a step's
+ * indexer-page update goes before this call (kv_compress_insert_jobs), the
+ * other updates into it.  Jobs are validated as for kv_compress_insert_jobs,
+ * the indexer arguments as for indexer_topk; nothing is launched on any
+ * error.
+ */
+hca_status indexer_topk_with_updates(const uint16_t* q_idx, const float* head_w, int32_t HI,
+                                     hca_paged_cache idx_keys, const int32_t* block_table, int32_t bt_stride,
+                                     const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t m,
+                                     int32_t k, int32_t* out_idx, int32_t* out_n, void* ws, size_t ws_bytes,
+                                     const hca_insert_job* jobs, int32_t n_jobs, void* stream);
+
+/*
  * paged_hybrid_decode -- attention of the decode query over the selected
  * compressed entries plus the raw window (V4 page, section 2.1: shared K=V,
  * RoPE on the key use, inverse RoPE on the output; c128a attends to all of its

@@ -245,3 +245,28 @@ def test_validation_indexer_and_attention():
     assert att(out=None) == 1 and att(o8=FAKE) == 1 and att(out=None, o8=ctypes.c_void_p(0x1001), o8s=FAKE) == 1
     assert att(out=None, o8=FAKE, o8s=FAKE, wsb=ws_att - 1) == 3  # valid outputs; only the workspace is short
     assert att(B=0) == 0
+
+
+def test_validation_indexer_topk_with_updates():
+    L = hca.lib()
+    ws_need = L.indexer_topk_workspace(2, 4096, 4, 256)
+    OTHER = ctypes.c_void_p(0x2000)
+
+    def job(dst):
+        return hca.CInsertJob(FAKE.value, 4 * 128, FAKE.value, 4, FAKE.value, FAKE.value, FAKE.value, 4, 0, 1e6, None,
+                              1e-6, FAKE.value, 64 * 128, FAKE.value, FAKE.value, 16, dst, 0)
+
+    def call(jobs, B=2, HI=16, keys=None):
+        keys = keys or _cache(dtype=2, epp=64, dim=128, codes=FAKE)
+        arr = (hca.CInsertJob * max(len(jobs), 1))(*jobs)
+        return L.indexer_topk_with_updates(FAKE, FAKE, HI, keys, FAKE, 16, FAKE, B, 4096, 4, 256, FAKE, FAKE, FAKE,
+                                           ws_need, arr, len(jobs), None)
+
+    ok = job(_cache(dtype=1, epp=64, dim=128, codes=OTHER))
+    assert call([ok], B=0) == 0  # valid, nothing to do
+    # a job writing the keys being scored would race with the score pass
+    assert call([ok, job(_cache(dtype=1, epp=64, dim=128, codes=FAKE))], B=0) == 1
+    assert call([ok] * 5, B=0) == 2  # at most four jobs
+    assert call([ok, job(_cache(dtype=1, epp=3, dim=128, codes=OTHER))]) == 1  # every job checked, nothing launched
+    assert call([ok], HI=17) == 2 and call([ok], B=-1) == 1  # the indexer arguments as for indexer_topk
+    assert call([], B=0) == 0

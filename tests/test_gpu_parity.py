@@ -558,6 +558,82 @@ def test_indexer_topk_sets(dtype, d_idx, k, lens):
             assert (got[b, n[b]:] == -1).all()
 
 
+@pytest.mark.parametrize("dtype,d_idx,k,lens", [
+    ("fp4", 128, 2048, [70001, 8193, 9000]),
+    ("fp8", 32, 300, [1200, 1201, 1199]),  # N = 300 ~ k
+])
+def test_indexer_topk_with_updates_matches_two_calls(dtype, d_idx, k, lens):
+    # a c4a layer's window insert and open-entry update run beside the score
+    # pass: the same selection (the oracle's), and the same bytes in every
+    # staging row and page the jobs write, as the update call then the indexer
+    H.flush(f"indexer with updates {dtype} dI={d_idx} k={k} lens={lens}")
+    w = _idx_workload(dtype, d_idx, k, len(lens))
+    sd = H.SeqData(w, 0, lens, build_pools=False)
+    sd.idx = paging.Pool(dtype, sd.num_pages, 64, d_idx)
+    for b in range(sd.B):
+        paging.write_run(sd.idx, sd.table[b], 0, sd.keys[b])
+    assert min(sd.enforce_margin()) >= H.MARGIN
+    Lmax = H.max_len(lens)
+    B, d, theta = sd.B, 512, 1e6
+    rng = np.random.default_rng(73)
+    L = np.array(lens, np.int64)
+    nb = int(L.max()) // 256 + 2
+    table = rng.permutation(B * nb).reshape(B, nb).astype(np.int32)
+    wtable = rng.permutation(B * nb).reshape(B, nb).astype(np.int32)
+    pos_w = (L - 1).astype(np.int32)
+    e0_w = (256 * ((L - 1) // 256)).astype(np.int32)
+    pos_c = (4 * ((L - 1) // 4)).astype(np.int32)
+    ntok_c = (L - pos_c).astype(np.int32)
+    e0_c = (64 * ((pos_c // 4) // 64)).astype(np.int32)
+    xw = gen.to_bf16_bits(rng.standard_normal((B, 1, d)).astype(np.float32))
+    zw = rng.standard_normal((B, 1)).astype(np.float32)
+    xc = gen.to_bf16_bits(rng.standard_normal((B, 8, d)).astype(np.float32))
+    zc = rng.standard_normal((B, 8)).astype(np.float32)
+    beta = (rng.standard_normal(8) * 0.1).astype(np.float32)
+    gam = H.to_dev(rng.uniform(0.5, 1.5, d).astype(np.float32))
+    stages = (rng.standard_normal((B, 256, d)).astype(np.float32), rng.standard_normal((B, 64, d)).astype(np.float32))
+    dev = {n: H.to_dev(v) for n, v in dict(pos_w=pos_w, e0_w=e0_w, pos_c=pos_c, ntok_c=ntok_c, e0_c=e0_c,
+                                            one=np.ones(B, np.int32), zero1=np.zeros(1, np.float32), beta=beta,
+                                            tab=table, wtab=wtable).items()}
+    keys = H.upload_pool(sd.idx)
+    qi, wi = H.to_dev(sd.qi.view(np.int16)), H.to_dev(sd.wi)
+    ws = hca.workspace(hca.indexer_topk_workspace(B, Lmax, 4, k))
+    outs = []
+    for fused in (True, False):
+        wst, cst = (H.to_dev(a) for a in stages)
+        win = hca.PagedCache.empty(B * nb, 256, d, "fp8")
+        kv = hca.PagedCache.empty(B * nb, 64, d, "fp8")
+        xwd, zwd = H.to_dev(xw.view(np.int16)), H.to_dev(zw)
+        xcd, zcd = H.to_dev(xc.view(np.int16))[:, 4:], H.to_dev(zc)[:, 4:]
+        jobs = [hca.insert_job(wst, dev["pos_w"], dev["e0_w"], dev["wtab"], win, 1, x=xwd, gate_logit=zwd,
+                               pos_bias=dev["zero1"], ntok=dev["one"], rope_theta=theta),
+                hca.insert_job(cst, dev["pos_c"], dev["e0_c"], dev["tab"], kv, 4, x=xcd, gate_logit=zcd,
+                               pos_bias=dev["beta"], ntok=dev["ntok_c"], rope_theta=theta, norm_gamma=gam,
+                               overlap=4)]
+        out_idx = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+        out_n = torch.zeros(B, dtype=torch.int32, device="cuda")
+        if fused:
+            hca.indexer_topk_with_updates(qi, wi, keys, H.to_dev(sd.table), H.to_dev(sd.lens), Lmax, 4, k, out_idx,
+                                          out_n, ws, jobs)
+        else:
+            hca.kv_compress_insert_jobs(jobs, B)
+            hca.indexer_topk(qi, wi, keys, H.to_dev(sd.table), H.to_dev(sd.lens), Lmax, 4, k, out_idx, out_n, ws)
+        torch.cuda.synchronize()
+        outs.append((out_idx, out_n, wst, cst, win, kv))
+    (of, nf, wf, cf, winf, kvf), (ou, nu, wu, cu, winu, kvu) = outs
+    assert torch.equal(of, ou) and torch.equal(nf, nu)
+    got, n = of.cpu().numpy(), nf.cpu().numpy()
+    for b in range(B):
+        want = sd.oracle_select(b)
+        assert n[b] == len(want) and np.array_equal(got[b, : n[b]], want), b
+    assert torch.equal(wf, wu) and torch.equal(cf, cu)
+    for b in range(B):
+        pw, pc = int(wtable[b, e0_w[b] // 256]), int(table[b, e0_c[b] // 64])
+        nw, nc = int(pos_w[b] - e0_w[b] + 1), int(pos_c[b] // 4 - e0_c[b] + 1)
+        assert torch.equal(winf.codes[pw, :nw], winu.codes[pw, :nw]) and torch.equal(winf.scales[pw], winu.scales[pw])
+        assert torch.equal(kvf.codes[pc, :nc], kvu.codes[pc, :nc]) and torch.equal(kvf.scales[pc], kvu.scales[pc])
+
+
 # ----------------------------------------------------------------- paged_hybrid_decode
 
 
