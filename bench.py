@@ -45,8 +45,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 # copy_bandwidth() (the summary with the commands is in profiles/).  They hold
 # only for the kernel source they were taken on, identified by the SHA-256 of
 # the indexer source and the headers it includes; otherwise traffic is null.
-SCORE_TRAFFIC = {"source_sha256": "49fa57889b87d368f32ff58e5e31cedd882ef050078739a4b0ee8cab0608e212",
-                 "fetch_bytes": 71889905, "write_bytes": 4599286}
+SCORE_TRAFFIC = {"source_sha256": "2df40d91157895c6ee8661d6e3e196791cf9ca15f8f8d8be85bbb8e5ab6ddfd6",
+                 "fetch_bytes": 71890336, "write_bytes": 4599894}
 SCORE_SOURCES = ("decode_attention_compressed_amd/csrc/indexer.hip", "decode_attention_compressed_amd/csrc/hca_common.h",
                  "decode_attention_compressed_amd/csrc/indexer_internal.h",
                  "decode_attention_compressed_amd/csrc/indexer_score.h")
