@@ -1144,13 +1144,14 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
   // first round of partial loads and the first kCombThreads (m, l) pairs,
   // issued before the lengths are known (every split the plan has is in the
   // workspace; the ones past this sequence's end get weight 0)
+  // ((m, l) first: loads complete in issue order, and the split maximum needs
+  // only these)
+  const float2 ml0 = (int)threadIdx.x < Smax ? ml[(size_t)threadIdx.x * H] : make_float2(-INFINITY, 0.0f);
+  // (unguarded, the split index clamped into the plan's: guarded loads are
+  // branches, across which the loads' waits are no longer counted exactly)
   f32x4 o[kCombU];
 #pragma unroll
-  for (int u = 0; u < kCombU; ++u) {
-    const int s = grp + SG * u;
-    o[u] = s < Smax ? opart[(size_t)s * ostride] : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const float2 ml0 = (int)threadIdx.x < Smax ? ml[(size_t)threadIdx.x * H] : make_float2(-INFINITY, 0.0f);
+  for (int u = 0; u < kCombU; ++u) o[u] = opart[(size_t)min(grp + SG * u, Smax - 1) * ostride];
   const int L = clampi(a.lens[b], 0, a.max_len);
   const int N = (L + a.m - 1) / a.m;
   const int n_sel = a.sel ? clampi(a.sel_n[b], 0, a.k) : N;
@@ -1187,8 +1188,13 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
     return;
   }
   float tloc = 0.0f;
-  for (int s = threadIdx.x; s < S; s += kCombThreads) {
-    const float2 v = s < kCombThreads ? ml0 : ml[(size_t)s * H];
+  if ((int)threadIdx.x < S) {  // the first round from the registers (a select between them and a load
+    const float w = ml0.y > 0.0f ? expf(ml0.x - M) : 0.0f;  // put ml0 on the stack)
+    w_s[threadIdx.x] = w;
+    tloc += w * ml0.y;
+  }
+  for (int s = threadIdx.x + kCombThreads; s < S; s += kCombThreads) {
+    const float2 v = ml[(size_t)s * H];
     const float w = v.y > 0.0f ? expf(v.x - M) : 0.0f;
     w_s[s] = w;
     tloc += w * v.y;
@@ -1202,14 +1208,15 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
 #pragma unroll
     for (int u = 0; u < kCombU; ++u) {
       const int s = s0 + SG * u;
-      const float w = s < S ? w_s[s] : 0.0f;
-      acc += w * o[u];
+      // splits at S and past it hold no partial of this sequence (whatever
+      // the workspace holds there, it is not added, not even times 0)
+      if (s < S) acc += w_s[s] * o[u];
     }
     if (s0 + SG * kCombU >= S) break;
 #pragma unroll
     for (int u = 0; u < kCombU; ++u) {  // next round (more than SG * kCombU splits)
       const int s = s0 + SG * (kCombU + u);
-      o[u] = s < S ? opart[(size_t)s * ostride] : f32x4{0.f, 0.f, 0.f, 0.f};
+      o[u] = opart[(size_t)min(s, Smax - 1) * ostride];
     }
   }
   acc_s[grp][li] = acc;
