@@ -260,10 +260,10 @@ def decode_step(w, layers, shared, ws_idx, ws_att, hca, update=True, attend=True
     """One decode step of the stack.  Per layer: the update (the window insert
     with its page, the open group's re-fold with its page and, for c4a, the
     open indexer page), the indexer (c4a) and the attention, which the next
-    layer's update waits for.  c128a: the update is one launch.  c4a: the open
-    indexer page is one small launch, and the window insert and the open entry
-    run as extra blocks of the indexer's last select launch
-    (indexer_topk_with_updates).
+    layer's update waits for.  c128a: the update is one launch.  c4a: the
+    update runs inside the indexer call (indexer_topk_with_updates): the open
+    indexer row by the score pass, the window insert and the open entry as
+    extra blocks of the select's last launch.
     The attend-only and update-only variants make the calls separately."""
     import torch
     L, W = w.L, w.window
@@ -281,11 +281,11 @@ def decode_step(w, layers, shared, ws_idx, ws_att, hca, update=True, attend=True
         idx_job = (hca.insert_job(lay.istage, lay.pos0, lay.e0, table, lay.idx, m, append=True)
                    if kind.topk is not None else None)
         if update and attend and kind.topk is not None:
-            # the open indexer page first (the score reads it), then the
-            # indexer with the window insert and the open entry's update beside it
-            hca.kv_compress_insert_jobs([idx_job], w.B)
+            # the indexer with the updates: the open indexer row written by the
+            # score pass, the window insert and the open entry's update beside
+            # the select's compaction
             hca.indexer_topk_with_updates(lay.qi, lay.wi, lay.idx, table, lens, L, m, kind.topk, lay.sel, lay.sel_n,
-                                          ws_idx, jobs)
+                                          ws_idx, jobs + [idx_job])
         else:
             if update:
                 hca.kv_compress_insert_jobs(jobs + ([idx_job] if idx_job is not None else []), w.B)

@@ -218,18 +218,35 @@ hca_status indexer_topk_with_updates(const uint16_t* q_idx, const float* head_w,
   if (st != HCA_OK) return st;
   if (n_jobs < 0 || (n_jobs > 0 && !jobs)) return HCA_ERR_INVALID;
   if (n_jobs > kMaxInsertJobs) return HCA_ERR_UNSUPPORTED;
-  InsertJobs all{};
+  // jobs that write the keys go before the score pass: the open indexer row
+  // (fp4 keys of 128 dims, one staged row appended, same block table) inside
+  // it, any other as a launch of its own; the rest beside the compaction
+  InsertJobs pre{}, side{};
+  IndexerOpen open{};
   for (int i = 0; i < n_jobs; ++i) {
-    if (jobs[i].dst.codes == idx_keys.codes) return HCA_ERR_INVALID;  // would race with the score reads
-    const hca_status sj = make_insert(jobs[i], B, all.job[i]);
+    const hca_insert_job& j = jobs[i];
+    InsertArgs ins{};
+    const hca_status sj = make_insert(j, B, ins);
     if (sj != HCA_OK) return sj;
+    if (j.dst.codes != idx_keys.codes) {
+      side.job[side.n++] = ins;
+    } else if (open.stage == nullptr && j.x == nullptr && j.append == 1 && j.m == m &&
+               idx_keys.dtype == HCA_FP4_E2M1 && idx_keys.dim == 128 && idx_keys.epp == 64 &&
+               j.dst.dtype == idx_keys.dtype && j.dst.dim == idx_keys.dim && j.dst.epp == idx_keys.epp &&
+               j.dst.scales == idx_keys.scales && j.dst.num_pages == idx_keys.num_pages &&
+               j.block_table == block_table && j.bt_stride == bt_stride) {
+      open = IndexerOpen{j.stage, j.stage_stride_b, j.pos0, j.e0};
+    } else {
+      pre.job[pre.n++] = ins;
+    }
   }
-  all.n = n_jobs;
   if (B == 0) return HCA_OK;
+  a.open = open;
   const hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_indexer_score(a, s);
+  hipError_t e = pre.n > 0 ? launch_insert(pre, B, s) : hipSuccess;
+  if (e == hipSuccess) e = launch_indexer_score(a, s);
   if (e == hipSuccess) e = launch_select_chunk(a, s);
-  if (e == hipSuccess) e = launch_compact_insert(a, all, s);
+  if (e == hipSuccess) e = launch_compact_insert(a, side, s);
   return from_hip(e);
 }
 

@@ -18,6 +18,14 @@ IndexerWs indexer_ws_layout(int B, int max_seq_len, int m, int k);
 constexpr int kHistBins = 4096;  // top 12 bits of the score key
 constexpr int kHistCopies = 16;  // per-sequence histogram copies the score blocks spread over
 
+// A decode step's open indexer row, written by the score pass itself: the key
+// of the open entry, row p0/m - e0 of page table[e0/64] of the keys, from f32
+// staging [B][64][128] (fp4 keys of 128 dims, 64 entries per page; the other
+// rows of the page keep their codes).  stage null: none.
+struct IndexerOpen {
+  const float* stage; int64_t ss;
+  const int32_t* pos0; const int32_t* e0;
+};
 struct IndexerArgs {
   const uint16_t* q; const float* w; int HI;
   hca_paged_cache keys;
@@ -26,6 +34,7 @@ struct IndexerArgs {
   int B, max_len, m, k;
   int32_t* out_idx; int32_t* out_n;
   unsigned char* ws; IndexerWs lay;
+  IndexerOpen open;
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
 hipError_t launch_indexer_score(const IndexerArgs& a, hipStream_t s);

@@ -346,6 +346,63 @@ struct PageTiles {
   }
 };
 
+// The open indexer row of a decode step (fp4 keys, 128 dims, 64 entries per
+// page), encoded by the wave that scores its page: lane l holds dims 2l and
+// 2l + 1, so the 16 lanes of a 32-element block find its amax by xor shuffles;
+// scale code E4M3(amax / 6), codes E2M1(x / decoded scale), all codes 0 for a
+// zero scale, element 2l in the low nibble of byte l: the update kernel's
+// encoding, operation for operation.  The row goes to the page (for the steps
+// after this one) and, through LDS, into the registers of the lane that holds
+// that entry of the loaded page.
+struct OpenRow {
+  int page = -1;       // page index of the open row in the sequence, -1: not this wave's
+  int row = 0;         // its row in the page
+  uint32_t byte = 0;   // this lane's code byte
+  uint32_t sc = 0;     // the scale code of this lane's 32-element block
+  __device__ __forceinline__ void prepare(const IndexerArgs& a, int b, int page0, int wave, int lane) {
+    if (a.open.stage == nullptr) return;
+    const int E0 = a.open.e0[b];
+    const int r = a.open.pos0[b] / a.m - E0;
+    const int lb = E0 >> 6;
+    if (r < 0 || r >= 64 || E0 < 0 || lb >= a.bts) return;
+    if (lb < page0 || lb >= page0 + kPagesPerScoreBlock || ((lb - page0) & 3) != wave) return;
+    const float2 v = reinterpret_cast<const float2*>(a.open.stage + (int64_t)b * a.open.ss + (int64_t)r * 128)[lane];
+    float amax = fmaxf(fabsf(v.x), fabsf(v.y));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    sc = e4m3_encode(amax / 6.0f);
+    const float sdec = e4m3_decode(sc);
+    byte = sdec > 0.0f ? (e2m1_encode(v.x / sdec) | (e2m1_encode(v.y / sdec) << 4)) : 0u;
+    const int phys = a.bt[(int64_t)b * a.bts + lb];
+    if (phys < 0 || phys >= a.keys.num_pages) return;  // an unmapped page: nothing written, nothing patched
+    uint8_t* codes = reinterpret_cast<uint8_t*>(a.keys.codes) + ((int64_t)phys * 64 + r) * 64;
+    uint8_t* scales = reinterpret_cast<uint8_t*>(a.keys.scales) + ((int64_t)phys * 64 + r) * 4;
+    codes[lane] = (uint8_t)byte;
+    if ((lane & 15) == 0) scales[lane >> 4] = (uint8_t)sc;
+    page = lb;
+    row = r;
+  }
+  // with the page's loads in: the open row's lane takes the new bytes
+  __device__ __forceinline__ void patch(uint32_t* raw, uint32_t* rsc, int p, int lane) const {
+    if (p != page) return;
+    // the row's 16 code words and its scale word, gathered from the lanes
+    uint32_t w[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t b0 = __shfl(byte, 4 * k, 64), b1 = __shfl(byte, 4 * k + 1, 64);
+      const uint32_t b2 = __shfl(byte, 4 * k + 2, 64), b3 = __shfl(byte, 4 * k + 3, 64);
+      w[k] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    }
+    const uint32_t s4 = __shfl(sc, 0, 64) | (__shfl(sc, 16, 64) << 8) | (__shfl(sc, 32, 64) << 16) |
+                        (__shfl(sc, 48, 64) << 24);
+    if (lane == row) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) raw[k] = w[k];
+      rsc[0] = s4;
+    }
+  }
+};
+
 // One score block of the page path: block bx of sequence b, with the block's
 // LDS histogram (kHistBins words).  Called by every thread of a block of
 // kScoreThreads threads.
@@ -383,10 +440,16 @@ __device__ __forceinline__ void score_pages_block(const IndexerArgs& a, int bx, 
   c.hist_s = hist_s;
   c.scores = score_row(a, b);
   const int p_end = min(NP, page0 + kPagesPerScoreBlock);
+  // the open indexer row (fp4 keys of 128 dims): its wave encodes it from
+  // staging, writes it to the page and scores it in place of the page's old
+  // bytes for that row
+  OpenRow orow;
+  if constexpr (KDT == HCA_FP4_E2M1 && DI == 128) orow.prepare(a, b, page0, wave, lane);
   // a ring of kScoreBufs page buffers per wave: the first kScoreBufs pages are
   // loaded up front, page i + kScoreBufs as soon as page i is consumed
   PageTiles<KDT, DI> pt[kScoreBufs];
   auto consume = [&](PageTiles<KDT, DI>& t, int i) {
+    if constexpr (KDT == HCA_FP4_E2M1 && DI == 128) orow.patch(t.raw, t.rsc, page_of(i), lane);
     t.prepare();
     const int p = page_of(i);
 #pragma unroll

@@ -307,13 +307,12 @@ hca_status indexer_topk(const uint16_t* q_idx, const float* head_w, int32_t HI,
  * run beside its score pass (V4 page, section 3.2.2: the indexer overlaps the
  * main-KV compression and the window insert).  The result is that of
  * kv_compress_insert_jobs(jobs, n_jobs, B) followed by indexer_topk(...): the
- * same bytes in every output and page.  The updates run as extra blocks of
- * the select's last launch, after the score pass has read the keys.
- *
- * The jobs must therefore not write the indexer keys being scored (a job whose
- * dst.codes is idx_keys.codes is rejected with HCA_ERR_INVALID): a step's
- * indexer-page update goes before this call (kv_compress_insert_jobs), the
- * other updates into it.  Jobs are validated as for kv_compress_insert_jobs,
+ * same bytes in every output and page.  Jobs that write other pools run as
+ * extra blocks of the select's last launch.  A job that writes the indexer
+ * keys runs before the score pass: the open indexer row of a decode step (no
+ * fold, append, fp4 keys of dim 128 with 64 entries per page, the indexer's
+ * block table) inside it, encoded by the score blocks of its page; any other
+ * as a launch of its own.  Jobs are validated as for kv_compress_insert_jobs,
  * the indexer arguments as for indexer_topk; nothing is launched on any
  * error.
  */

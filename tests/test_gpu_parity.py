@@ -563,9 +563,10 @@ def test_indexer_topk_sets(dtype, d_idx, k, lens):
     ("fp8", 32, 300, [1200, 1201, 1199]),  # N = 300 ~ k
 ])
 def test_indexer_topk_with_updates_matches_two_calls(dtype, d_idx, k, lens):
-    # a c4a layer's window insert and open-entry update run beside the score
-    # pass: the same selection (the oracle's), and the same bytes in every
-    # staging row and page the jobs write, as the update call then the indexer
+    # a c4a layer's window insert, open-entry update and open indexer row with
+    # the indexer: the same selection (the oracle's, the open row's key left as
+    # the oracle has it), and the same bytes in every staging row and page the
+    # jobs write, as the update call then the indexer
     H.flush(f"indexer with updates {dtype} dI={d_idx} k={k} lens={lens}")
     w = _idx_workload(dtype, d_idx, k, len(lens))
     sd = H.SeqData(w, 0, lens, build_pools=False)
@@ -595,11 +596,20 @@ def test_indexer_topk_with_updates_matches_two_calls(dtype, d_idx, k, lens):
     dev = {n: H.to_dev(v) for n, v in dict(pos_w=pos_w, e0_w=e0_w, pos_c=pos_c, ntok_c=ntok_c, e0_c=e0_c,
                                             one=np.ones(B, np.int32), zero1=np.zeros(1, np.float32), beta=beta,
                                             tab=table, wtab=wtable).items()}
-    keys = H.upload_pool(sd.idx)
     qi, wi = H.to_dev(sd.qi.view(np.int16)), H.to_dev(sd.wi)
     ws = hca.workspace(hca.indexer_topk_workspace(B, Lmax, 4, k))
+    # the open indexer row: the open entry N-1 of each sequence, staged in f32
+    # as the oracle's key (so re-encoding it gives the pool's bytes), with the
+    # rest of its page staged too
+    N = -(-L // 4)
+    pos_i, e0_i = (4 * (N - 1)).astype(np.int32), (64 * ((N - 1) // 64)).astype(np.int32)
+    istage = np.zeros((B, 64, d_idx), np.float32)
+    for bb in range(B):
+        istage[bb, : N[bb] - e0_i[bb]] = sd.keys[bb][e0_i[bb]: N[bb]]
     outs = []
     for fused in (True, False):
+        keys = H.upload_pool(sd.idx)
+        ist = H.to_dev(istage)
         wst, cst = (H.to_dev(a) for a in stages)
         win = hca.PagedCache.empty(B * nb, 256, d, "fp8")
         kv = hca.PagedCache.empty(B * nb, 64, d, "fp8")
@@ -609,7 +619,8 @@ def test_indexer_topk_with_updates_matches_two_calls(dtype, d_idx, k, lens):
                                pos_bias=dev["zero1"], ntok=dev["one"], rope_theta=theta),
                 hca.insert_job(cst, dev["pos_c"], dev["e0_c"], dev["tab"], kv, 4, x=xcd, gate_logit=zcd,
                                pos_bias=dev["beta"], ntok=dev["ntok_c"], rope_theta=theta, norm_gamma=gam,
-                               overlap=4)]
+                               overlap=4),
+                hca.insert_job(ist, H.to_dev(pos_i), H.to_dev(e0_i), H.to_dev(sd.table), keys, 4, append=True)]
         out_idx = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
         out_n = torch.zeros(B, dtype=torch.int32, device="cuda")
         if fused:
@@ -619,9 +630,10 @@ def test_indexer_topk_with_updates_matches_two_calls(dtype, d_idx, k, lens):
             hca.kv_compress_insert_jobs(jobs, B)
             hca.indexer_topk(qi, wi, keys, H.to_dev(sd.table), H.to_dev(sd.lens), Lmax, 4, k, out_idx, out_n, ws)
         torch.cuda.synchronize()
-        outs.append((out_idx, out_n, wst, cst, win, kv))
-    (of, nf, wf, cf, winf, kvf), (ou, nu, wu, cu, winu, kvu) = outs
+        outs.append((out_idx, out_n, wst, cst, win, kv, keys))
+    (of, nf, wf, cf, winf, kvf, kf), (ou, nu, wu, cu, winu, kvu, ku) = outs
     assert torch.equal(of, ou) and torch.equal(nf, nu)
+    assert torch.equal(kf.codes, ku.codes) and torch.equal(kf.scales, ku.scales)  # the whole indexer pool
     got, n = of.cpu().numpy(), nf.cpu().numpy()
     for b in range(B):
         want = sd.oracle_select(b)
