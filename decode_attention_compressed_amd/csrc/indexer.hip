@@ -31,7 +31,7 @@ IndexerWs indexer_ws_layout(int B, int max_seq_len, int m, int k) {
   const int n_pad = ((n_max + kSelChunk - 1) / kSelChunk) * kSelChunk;
   size_t off = 0;
   w.scores = off; off = align256(off + (size_t)B * n_pad * sizeof(float));
-  w.hist = off; off = align256(off + (size_t)B * kHistCopies * kHistBins * sizeof(uint32_t));
+  w.hist = off; off = align256(off + (size_t)B * kHistWords * sizeof(uint32_t));
   w.cand = off; off = align256(off + (size_t)B * n_pad * sizeof(uint2));
   w.bitmap = off; off = align256(off + (size_t)B * (n_pad / 32) * sizeof(uint32_t));
   w.counters = off; off = align256(off + (size_t)B * 4 * sizeof(uint32_t));
@@ -42,7 +42,7 @@ IndexerWs indexer_ws_layout(int B, int max_seq_len, int m, int k) {
 
 template <int KDT, int DI>
 __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(IndexerArgs a) {
-  __shared__ uint32_t hist_s[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist_s[kHistBins];
   score_pages_block<KDT, DI>(a, blockIdx.x, blockIdx.y, hist_s);
 }
 
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs a) {
   const int N = (L + a.m - 1) / a.m;
   const int chunk0 = blockIdx.x * kScoreChunk;
   if (chunk0 >= N) return;
-  __shared__ uint32_t hist_s[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist_s[kHistBins];
   ScoreCtx c;
   c.want_hist = a.k < N;
   c.hist_s = hist_s;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(IndexerArgs a
   SelView v = sel_view(a, b);
   const int len_raw = a.lens[b];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // this block's scores and the histogram's top slice are loaded with the
+  // this block's scores and the coarse histogram are loaded with the
   // length, unconditionally (a block past the last score chunk, which the grid
   // has when k exceeds the entries, reads chunk 0 and uses nothing)
   constexpr int kUnroll = kSelChunk / 256;  // one round of loads per wave
@@ -102,7 +102,9 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(IndexerArgs a
   float sc[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) sc[u] = v.scores[base0 + 64 * u + lane];
-  const uint32_t top_cnt = hist_slice_sum(v.hist, kHistBins - 1);
+  // copy t / 16, coarse bin t % 16 of the coarse histogram
+  static_assert(kSelThreads == kHistCopies * kCoarseBins, "one coarse count per thread");
+  const uint32_t coarse = v.hist[kHistCopies * kHistBins + threadIdx.x];
   __builtin_amdgcn_sched_barrier(0);
   set_len(v, a, len_raw);
   const int N = v.N, k = a.k;
@@ -119,9 +121,25 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(IndexerArgs a
   if ((int)blockIdx.x >= v.G) return;
   const int c1 = min(N, c0 + kSelChunk);  // scores at c1 and past it are not used
   __shared__ uint32_t tmp[kSelThreads / 64];
+  // the coarse bin that holds the cut, and the entries above it: its 256-bin
+  // slice is then the only one summed
+  __shared__ uint32_t coarse_s[kCoarseBins];
+  if (threadIdx.x < kCoarseBins) coarse_s[threadIdx.x] = 0u;
+  __syncthreads();
+  if (coarse) atomicAdd(&coarse_s[threadIdx.x % kCoarseBins], coarse);
+  __syncthreads();
+  int cb = kCoarseBins - 1;
+  uint32_t run = 0;
+  for (; cb > 0; --cb) {
+    const uint32_t x = coarse_s[cb];
+    if (run + x >= (uint32_t)k) break;
+    run += x;
+  }
+  const int top0 = 256 * cb + 255;
+  const uint32_t first = hist_slice_sum(v.hist, top0);
   int cut;
   uint32_t above;
-  find_cut_copies(v.hist, top_cnt, (uint32_t)k, tmp, cut, above);
+  find_cut_copies(v.hist, top0, first, run, (uint32_t)k, tmp, cut, above);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     v.ctr[0] = (uint32_t)cut;
     v.ctr[1] = above;

@@ -17,6 +17,10 @@ struct IndexerWs {
 IndexerWs indexer_ws_layout(int B, int max_seq_len, int m, int k);
 constexpr int kHistBins = 4096;  // top 12 bits of the score key
 constexpr int kHistCopies = 16;  // per-sequence histogram copies the score blocks spread over
+constexpr int kCoarseBins = 16;  // coarse bins of 256 fine bins each, kept beside the fine ones
+// words per sequence: kHistCopies fine histograms, then kHistCopies coarse ones
+constexpr int kHistWords = kHistCopies * (kHistBins + kCoarseBins);
+static_assert(kHistBins == 256 * kCoarseBins && kHistWords % 4 == 0, "coarse bins of 256, zeroed as 16-byte words");
 
 // A decode step's open indexer row, written by the score pass itself: the key
 // of the open entry, row p0/m - e0 of page table[e0/64] of the keys, from f32

@@ -187,14 +187,39 @@ __device__ __forceinline__ void load_query(const IndexerArgs& a, int b, int col,
 }
 
 // The block's histogram is added to one of kHistCopies copies (by block index),
-// so that the blocks of a sequence do not all queue on the same hot bins.
+// so that the blocks of a sequence do not all queue on the same hot bins, and
+// its sums over 256-bin ranges to the same copy of the coarse histogram (which
+// tells the select which 256-bin slice holds its cut without scanning down to
+// it).  Round r of the loop holds the bins of coarse bin r, so each wave adds
+// its share of a coarse bin with one atomic, and only where it has counts;
+// the wave sum is register-to-register (DPP row rotations inside each 16-lane
+// row, then the two permlane swaps across rows).
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);  // row_ror:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false);  // row_ror:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false);  // row_ror:1
+  const auto x = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = x[0] + x[1];
+  const auto y = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return y[0] + y[1];
+}
 __device__ __forceinline__ void hist_flush(const IndexerArgs& a, int b, int bx, const uint32_t* hist_s) {
+  static_assert(kScoreThreads * kCoarseBins == kHistBins, "one coarse bin per round");
   __syncthreads();
-  uint32_t* gh = reinterpret_cast<uint32_t*>(a.ws + a.lay.hist) +
-                 ((size_t)b * kHistCopies + bx % kHistCopies) * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) {
+  uint32_t* base = reinterpret_cast<uint32_t*>(a.ws + a.lay.hist) + (size_t)b * kHistWords;
+  const int copy = bx % kHistCopies;
+  uint32_t* gh = base + copy * kHistBins;
+  uint32_t* gc = base + kHistCopies * kHistBins + copy * kCoarseBins;
+#pragma unroll
+  for (int r = 0; r < kCoarseBins; ++r) {
+    const int i = (int)threadIdx.x + r * kScoreThreads;
     const uint32_t c = hist_s[i];
     if (c) atomicAdd(&gh[i], c);
+    if (__ballot(c != 0u)) {
+      const uint32_t s = wave_sum_u32(c);
+      if ((threadIdx.x & 63) == 0) atomicAdd(&gc[r], s);
+    }
   }
 }
 
@@ -208,8 +233,9 @@ __device__ __forceinline__ float* score_row(const IndexerArgs& a, int b) {
 // gets a buffer resource of its own whose size is the page's valid bytes: a
 // lane past the last valid entry, or a whole page that is unmapped, reads 0 in
 // hardware, so the loads need no masks, no branches and only 32-bit offsets.
-// Pages are double-buffered (the loads of page i+2 are issued right after page
-// i is consumed), fully unrolled so that the waits count down in order.
+// A wave's pages go through a ring of kScoreBufs buffers (the loads of page
+// i + kScoreBufs are issued right after page i is consumed), fully unrolled so
+// that the waits count down in order.
 constexpr int kPagesPerScoreBlock = 32;
 constexpr int kPagesPerScoreWave = kPagesPerScoreBlock / 4;
 constexpr int kScoreBufs = 3;  // pages a wave has in flight

@@ -101,7 +101,7 @@ __device__ __forceinline__ SelView sel_view(const IndexerArgs& a, int b) {
   v.G = 0;
   v.n_pad = ((a.lay.n_max + kSelChunk - 1) / kSelChunk) * kSelChunk;
   v.scores = reinterpret_cast<const float*>(a.ws + a.lay.scores) + (size_t)b * v.n_pad;
-  v.hist = reinterpret_cast<uint32_t*>(a.ws + a.lay.hist) + (size_t)b * kHistCopies * kHistBins;
+  v.hist = reinterpret_cast<uint32_t*>(a.ws + a.lay.hist) + (size_t)b * kHistWords;
   v.cand = reinterpret_cast<uint2*>(a.ws + a.lay.cand) + (size_t)b * v.n_pad;
   v.bitmap = reinterpret_cast<uint32_t*>(a.ws + a.lay.bitmap) + (size_t)b * (v.n_pad / 32);
   v.ctr = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + (size_t)b * 4;
@@ -118,10 +118,10 @@ __device__ __forceinline__ void set_len(SelView& v, const IndexerArgs& a, int le
 
 // The cut bin (where the count from the top reaches `need`) and the count
 // strictly above it, from the histogram copies: the bins are summed 256 at a
-// time from the top, usually once, since the k highest scores sit in the top
-// bins.  Every thread of the block gets the result.
-// The top slice's per-thread sums (`first`) are loaded by the caller, ahead of
-// the sequence length.
+// time from slice top0 down, starting with `run` entries above it; the caller
+// starts at the slice the coarse histogram names, so this is one slice.
+// Every thread of the block gets the result.  The first slice's per-thread
+// sums (`first`) come from the caller.
 __device__ __forceinline__ uint32_t hist_slice_sum(const uint32_t* hist, int top) {
   const int bin = top - (int)threadIdx.x;  // descending with the thread index
   uint32_t c[kHistCopies];
@@ -132,14 +132,14 @@ __device__ __forceinline__ uint32_t hist_slice_sum(const uint32_t* hist, int top
   for (int r = 0; r < kHistCopies; ++r) cnt += c[r];
   return cnt;
 }
-__device__ void find_cut_copies(const uint32_t* hist, uint32_t first, uint32_t need, uint32_t* tmp, int& cut,
-                                uint32_t& above) {
+__device__ void find_cut_copies(const uint32_t* hist, int top0, uint32_t first, uint32_t run, uint32_t need,
+                                uint32_t* tmp, int& cut, uint32_t& above) {
   __shared__ int cut_s;
   __shared__ uint32_t above_s;
-  uint32_t run = 0;  // entries in the bins already passed
-  for (int top = kHistBins - 1; top >= 0; top -= kSelThreads) {
+  // run: entries in the bins already passed
+  for (int top = top0; top >= 0; top -= kSelThreads) {
     const int bin = top - (int)threadIdx.x;
-    const uint32_t cnt = top == kHistBins - 1 ? first : hist_slice_sum(hist, top);
+    const uint32_t cnt = top == top0 ? first : hist_slice_sum(hist, top);
     uint32_t total;
     const uint32_t before = run + block_excl_scan(cnt, tmp, total);
     if (run + total >= need) {  // the cut is in this slice
@@ -407,7 +407,7 @@ __device__ __forceinline__ void select_compact_block(const IndexerArgs& a, int x
   }
   // leave the histogram copies zeroed for the next call: each block a slice
   {
-    constexpr int kWords4 = kHistCopies * kHistBins / 4;
+    constexpr int kWords4 = kHistWords / 4;
     const int nb = (G + kCompactChunks - 1) / kCompactChunks;
     const int per = (kWords4 + nb - 1) / nb;
     u32x4* h4 = reinterpret_cast<u32x4*>(v.hist);
