@@ -45,8 +45,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 # copy_bandwidth() (the summary with the commands is in profiles/).  They hold
 # only for the kernel source they were taken on, identified by the SHA-256 of
 # the indexer source and the headers it includes; otherwise traffic is null.
-SCORE_TRAFFIC = {"source_sha256": "d64c1a261a5b5a4a87ce621a91ba7998c9dac4852dd3f59e423ad542783f7e8f",
-                 "fetch_bytes": 72019213, "write_bytes": 4599480}
+SCORE_TRAFFIC = {"source_sha256": "27475ce318c5781463f87d33311f670bd7d76570ff0046bf4fc387a5a086d253",
+                 "fetch_bytes": 72065010, "write_bytes": 4671982}
 SCORE_SOURCES = ("decode_attention_compressed_amd/csrc/indexer.hip", "decode_attention_compressed_amd/csrc/hca_common.h",
                  "decode_attention_compressed_amd/csrc/indexer_internal.h",
                  "decode_attention_compressed_amd/csrc/indexer_score.h")
