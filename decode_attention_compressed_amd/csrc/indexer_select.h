@@ -19,15 +19,25 @@ inline int select_chunks(const IndexerArgs& a) {
 }
 
 // ------------------------------------------------------------------ select
+// inclusive scan over the 64 lanes of a wave, register to register: DPP row
+// shifts scan each 16-lane row, then every lane adds the totals of the rows
+// below its own (read from the rows' last lanes)
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
 // exclusive block scan of one uint per thread (kSelThreads threads)
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
   uint32_t base = 0, tot = 0;
@@ -170,6 +180,8 @@ __device__ void find_cut_copies(const uint32_t* hist, int top0, uint32_t first, 
 // launch); block-wide, every thread gets the result.
 struct SelLds {
   uint32_t tmp[kSelThreads / 64];
+  uint32_t tot3[3][kSelThreads / 64];
+  uint32_t spec_over;  // a chunk has more candidates than its speculative slots
   uint32_t h_s[1024];
   uint32_t pre_s[kMaxSelBlocks + 1];
   uint32_t wc_s[kMaxSelBlocks];
@@ -198,9 +210,25 @@ __device__ __forceinline__ void load_chunk_counts(const SelView& v, const uint32
   }
 }
 
+// Speculative candidates: the two threads t of chunk t / 2 load one half each
+// of the first kSpecSlots slots of its candidate region, before the counts are
+// known; when there are at most kSelThreads / 2 chunks and
+// none has more than kSpecSlots candidates, these are all of them and no
+// second round trip gathers them.
+constexpr int kSpecSlots = 32;
+constexpr int kSpecU = kSpecSlots / 2 / 2;  // 16-byte loads per thread (two candidates each)
+__device__ __forceinline__ void load_spec(const SelView& v, uint4 spec[kSpecU]) {
+  const int gp = v.n_pad / kSelChunk;
+  const int j = min((int)threadIdx.x >> 1, gp - 1);
+  const uint4* p = reinterpret_cast<const uint4*>(v.cand + (size_t)j * kSelChunk + (threadIdx.x & 1) * (kSpecSlots / 2));
+#pragma unroll
+  for (int u = 0; u < kSpecU; ++u) spec[u] = p[u];
+}
+
 __device__ CutKey resolve_cut(const SelView& v, int k, SelLds& sm, int cut, uint32_t above,
-                              const uint32_t ccount_pre[kSelPer]) {
+                              const uint32_t ccount_pre[kSelPer], const uint4 spec[kSpecU]) {
   const int N = v.N, G = v.G;
+  if (threadIdx.x == 0) sm.spec_over = 0u;  // set below, after the scan's barriers
   {
     uint32_t cv = 0;
     const int per = sel_per(v);
@@ -218,6 +246,7 @@ __device__ CutKey resolve_cut(const SelView& v, int k, SelLds& sm, int cut, uint
       const int j = threadIdx.x * per + u;
       if (u < per && j < G) sm.pre_s[j] = run;
       run += loc[u];
+      if (loc[u] > (uint32_t)kSpecSlots) sm.spec_over = 1u;
     }
     if (threadIdx.x == 0) sm.pre_s[G] = tot;
     __syncthreads();
@@ -225,7 +254,21 @@ __device__ CutKey resolve_cut(const SelView& v, int k, SelLds& sm, int cut, uint
   CutKey r;
   r.nc = sm.pre_s[G];
   r.in_lds = r.nc <= (uint32_t)kCandLds;
-  if (r.in_lds) {
+  if (r.in_lds && G <= kSelThreads / 2 && sm.spec_over == 0u) {
+    // every candidate is in the speculative slots: chunk t / 2's go to LDS
+    const int j = threadIdx.x >> 1;
+    if (j < G) {
+      const uint32_t p0 = sm.pre_s[j], n = sm.pre_s[j + 1] - p0;
+      const uint32_t s0 = (threadIdx.x & 1) * (kSpecSlots / 2);
+#pragma unroll
+      for (int u = 0; u < kSpecU; ++u) {
+        const uint32_t s = s0 + 2 * u;
+        if (s < n) sm.cl_s[p0 + s] = make_uint2(spec[u].x, spec[u].y);
+        if (s + 1 < n) sm.cl_s[p0 + s + 1] = make_uint2(spec[u].z, spec[u].w);
+      }
+    }
+    __syncthreads();
+  } else if (r.in_lds) {
     // flat candidate i lives in region j with pre_s[j] <= i < pre_s[j+1]
     constexpr int U = 8;
     for (uint32_t i0 = threadIdx.x; i0 < r.nc; i0 += U * kSelThreads) {
@@ -339,6 +382,8 @@ __device__ __forceinline__ void select_compact_block(const IndexerArgs& a, int x
   uint32_t cc_pre[kSelPer], ab_pre[kSelPer];
   load_chunk_counts(v, v.ccount, cc_pre);
   load_chunk_counts(v, v.above, ab_pre);
+  uint4 spec[kSpecU];
+  load_spec(v, spec);
   set_len(v, a, a.lens[b]);
   const int N = v.N, G = v.G, k = a.k;
   if (N <= k || j0 >= G) return;
@@ -346,7 +391,7 @@ __device__ __forceinline__ void select_compact_block(const IndexerArgs& a, int x
   int32_t* out = a.out_idx + (int64_t)b * k;
   const int W = (N + 31) / 32;
   if (wave < kCompactChunks) wbits_s[wave * 64 + lane] = j0 + wave < j1 && w < W ? bits_pre : 0u;
-  const CutKey ck = resolve_cut(v, k, sm, cut_pre, above_pre, cc_pre);
+  const CutKey ck = resolve_cut(v, k, sm, cut_pre, above_pre, cc_pre, spec);
   // the chunks' winning candidates join their words
   {
     const uint32_t c0 = sm.pre_s[j0], c1 = sm.pre_s[j1];
@@ -378,20 +423,29 @@ __device__ __forceinline__ void select_compact_block(const IndexerArgs& a, int x
       }
     }
   }
+  // block totals of the three (one barrier, which also publishes wbits_s)
   uint32_t tot_before, tot_first, total;
-  (void)block_excl_scan(before, sm.tmp, tot_before);
-  (void)block_excl_scan(first, sm.tmp, tot_first);
-  (void)block_excl_scan(all, sm.tmp, total);  // its barriers also publish wbits_s
+  {
+    const uint32_t sb = wave_incl_scan(before), sf = wave_incl_scan(first), sa = wave_incl_scan(all);
+    if (lane == 63) {
+      sm.tot3[0][wave] = sb;
+      sm.tot3[1][wave] = sf;
+      sm.tot3[2][wave] = sa;
+    }
+    __syncthreads();
+    tot_before = tot_first = total = 0u;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+      tot_before += sm.tot3[0][w];
+      tot_first += sm.tot3[1][w];
+      total += sm.tot3[2][w];
+    }
+  }
   // wave c compacts chunk j0 + c, one word per lane
   if (wave < kCompactChunks && j0 + wave < j1) {
     const uint32_t bits0 = w < W ? wbits_s[wave * 64 + lane] : 0u;
     const uint32_t pc = (uint32_t)__popc(bits0);
-    uint32_t incl = pc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
+    const uint32_t incl = wave_incl_scan(pc);
     uint32_t pos = tot_before + (wave == 1 ? tot_first : 0u) + incl - pc;
     uint32_t bits = bits0;
     while (bits) {
