@@ -312,7 +312,10 @@ hca_status indexer_topk(const uint16_t* q_idx, const float* head_w, int32_t HI,
  * keys runs before the score pass: the open indexer row of a decode step (no
  * fold, append, fp4 keys of dim 128 with 64 entries per page, the indexer's
  * block table) inside it, encoded by the score blocks of its page; any other
- * as a launch of its own.  Jobs are validated as for kv_compress_insert_jobs,
+ * as a launch of its own.  The open row is written there when it lies inside
+ * the sequence's ceil(seq_lens[b] / m) entries, as a decode step's open entry
+ * does (an open row past them, from lengths that disagree with the job's
+ * positions, is left unwritten, where the two-call form would write it).  Jobs are validated as for kv_compress_insert_jobs,
  * the indexer arguments as for indexer_topk; nothing is launched on any
  * error.
  */
