@@ -148,6 +148,86 @@ def test_fp4_key_quantization_block_scales():
     assert codecs.E2M1_TABLE[lo] * sc[0, 0] == dec[0, 0]
 
 
+def _fraction(s):
+    if "/" in s:
+        n, d = s.split("/")
+        return float(n) / float(d)
+    return float(s)
+
+
+def test_fp4_key_block_hand_example():
+    # tests/golden: two 32-element blocks worked by hand from the bit fields
+    # (scale code, the divided values, the nibbles, the packed bytes, the
+    # decoded values); the second block is the first halved
+    with open(os.path.join(GOLDEN, "fp4_key_block_hand_example.json")) as f:
+        g = json.load(f)
+    b0, b1 = g["blocks"]
+    x = np.array(b0["x"], np.float32)
+    row = np.concatenate([x, x * np.float32(0.5)])[None, :]
+    assert np.abs(row[0, 32:]).max() == b1["amax"]
+    assert np.float32(np.float32(b0["amax"]) / np.float32(6)) == np.float32(b0["amax_over_6"])
+    assert np.float32(np.float32(b1["amax"]) / np.float32(6)) == np.float32(b1["amax_over_6"])
+    codes, scales = paging.quantize_page(row, "fp4", 64)
+    assert list(scales[0]) == [b0["scale_code"], b1["scale_code"]]
+    assert codecs.E4M3_TABLE[b0["scale_code"]] == b0["scale"] and codecs.E4M3_TABLE[b1["scale_code"]] == b1["scale"]
+    # the divided values as the hand computation states them
+    y = x / np.float32(b0["scale"])
+    assert np.allclose(y, [_fraction(s) for s in b0["y"]], rtol=0, atol=5e-5)
+    assert list(codes[0, :16]) == b0["bytes"] and list(codes[0, 16:32]) == b0["bytes"]
+    assert not codes[1:].any() and not scales[1:].any()  # slots past the valid rows
+    nib = np.empty(64, np.int64)
+    nib[0::2], nib[1::2] = codes[0] & 0xF, codes[0] >> 4
+    assert list(nib[:32]) == b0["codes"]
+    pool = paging.Pool("fp4", 1, 64, 64)
+    pool.codes[0], pool.scales[0] = codes, scales
+    dec = paging.decode_rows(pool, [0], [0])[0]
+    want = np.array(b0["decoded"], np.float64)
+    assert np.array_equal(dec[:32], want) and np.array_equal(dec[32:], want * 0.5)
+    assert np.array_equal(np.signbit(dec[:32]), np.signbit(want))  # -0.25 rounds to a signed zero
+
+
+def _e2m1_half_step(a):
+    # half the E2M1 spacing around magnitude a (a <= 6): 0.25 below 2, 0.5 below 4, 1 up to 6
+    return np.where(a < 2.0, 0.25, np.where(a < 4.0, 0.5, 1.0))
+
+
+def test_fp4_key_quantization_half_step_bound():
+    # every decoded element lies within half an E2M1 step (at the magnitude of
+    # x / decoded scale) of x, times the decoded scale; the block's largest
+    # element maps into [4, 6] times the scale.  Dividing by the unrounded
+    # amax/6 instead of the decoded scale breaks this bound.
+    g = np.random.default_rng(41)
+    for spread in (1e-3, 4e-3, 1.0, 37.0):
+        rows = (g.standard_normal((64, 128)) * spread).astype(np.float32)
+        rows[5, :32] *= 1e-3  # one block much smaller than its neighbours
+        codes, scales = paging.quantize_page(rows, "fp4", 64)
+        pool = paging.Pool("fp4", 1, 64, 128)
+        pool.codes[0], pool.scales[0] = codes, scales
+        dec = paging.decode_rows(pool, [0], np.arange(64))
+        sdec = np.repeat(codecs.e4m3_decode(scales), 32, axis=1)
+        x = rows.astype(np.float64)
+        zero = sdec == 0  # amax/6 below half the smallest E4M3 subnormal 2^-9: every code 0
+        assert np.all(dec[zero] == 0) and np.all(np.abs(x[zero]) <= 6 * 2.0 ** -10 * (1 + 1e-6))
+        s = np.where(zero, 1.0, sdec)
+        a = np.abs(x) / s
+        normal = ~zero & (sdec >= 2.0 ** -6)
+        assert np.all(a[normal] <= 6.0 * (1 + 2.0 ** -4) * (1 + 1e-6))  # sc = amax/6 up to one E4M3 rounding
+        err = np.abs(dec - x)
+        inside = ~zero & (a <= 6.0)
+        assert np.all(err[inside] <= (_e2m1_half_step(a) * s)[inside] * (1 + 1e-6))
+        sat = ~zero & (a > 6.0)  # saturated: coded as +-6 with x's sign
+        assert np.all(dec[sat] == np.sign(x[sat]) * 6.0 * sdec[sat])
+        # with a normal scale the block's largest element is coded at 4 or 6 times it
+        sc4 = codecs.e4m3_decode(scales)
+        top = np.abs(dec.reshape(64, 4, 32)).max(axis=2) / np.where(sc4 > 0, sc4, 1.0)
+        assert np.all((top >= 4.0) | (sc4 < 2.0 ** -6))
+    # the plausible mistake the bound catches: codes from x / fl32(amax/6)
+    x = np.array([6.5, 2.75] + [0.0] * 30, np.float32)
+    sc = codecs.e4m3_decode(codecs.e4m3_encode(np.float32(6.5) / np.float32(6)))
+    wrong = codecs.e2m1_decode(codecs.e2m1_encode(x / (np.float32(6.5) / np.float32(6)))) * sc
+    assert abs(wrong[1] - 2.75) > _e2m1_half_step(2.75 / sc) * sc
+
+
 def test_paged_equals_contiguous_under_permutation_and_aliasing():
     # the same logical rows through three different tables read back bit-identically
     g = np.random.default_rng(5)
