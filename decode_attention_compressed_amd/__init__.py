@@ -27,13 +27,15 @@ STATUS = {0: "HCA_OK", 1: "HCA_ERR_INVALID", 2: "HCA_ERR_UNSUPPORTED", 3: "HCA_E
 
 #: every symbol the C headers declare (include/hca.h and include/hca_testing.h)
 EXPORTS = (
-    "hca_status_string", "hca_version", "kv_compress", "kv_compress_insert", "kv_compress_insert_jobs",
+    "hca_status_string", "hca_version", "kv_compress", "kv_prefill_pages", "kv_compress_insert",
+    "kv_compress_insert_jobs",
     "kv_quantize_page_workspace",
     "kv_quantize_page",
     "indexer_topk_workspace",
-    "indexer_topk", "indexer_topk_with_updates", "paged_hybrid_decode_workspace", "paged_hybrid_decode", "kv_gather",
+    "indexer_topk", "indexer_topk_with_updates", "paged_hybrid_decode_workspace", "paged_hybrid_decode",
+    "kv_gather",
     "hca_host_e4m3_encode", "hca_host_e2m1_encode", "hca_host_bf16_encode", "hca_probe_decode", "hca_probe_mfma",
-    "hca_indexer_score",
+    "hca_indexer_score", "hca_attention_split",
     "hca_page_bytes", "hca_pool_plan", "hca_pool_create", "hca_pool_destroy", "hca_pool_view", "hca_pool_bucket",
     "hca_pool_alloc", "hca_pool_share", "hca_pool_release", "hca_pool_publish", "hca_pool_lookup", "hca_pool_stats",
 )
@@ -81,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.hca_version.restype = ctypes.c_char_p
         L.kv_compress.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F32, _P, _F32, _P,
                                   _I64, _P]
+        L.kv_prefill_pages.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _F32, _P,
+                                       _I32, CPagedCache, _P]
         L.kv_compress_insert.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _F32, _P, _F32, _P, _I64,
                                          _P, _P, _I32, CPagedCache, _I32, _P, _I64, _P]
         L.kv_compress_insert_jobs.argtypes = [ctypes.POINTER(CInsertJob), _I32, _I32, _P]
@@ -103,6 +107,8 @@ def lib() -> ctypes.CDLL:
         L.hca_probe_decode.argtypes = [_P, _P, _I32, _I32, _P]
         L.hca_probe_mfma.argtypes = [_P, _P, _P, _I32, _P]
         L.hca_indexer_score.argtypes = [_P, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P]
+        L.hca_attention_split.argtypes = [_P, _I32, CPagedCache, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32, _I32,
+                                          _I32, _P, _P, _I32, _F32, _F32, _P, _SZ, _P]
         L.hca_page_bytes.argtypes = [CKvKind, _P, _P]
         L.hca_pool_plan.argtypes = [_P, _I32, _P, _P]
         L.hca_pool_create.argtypes = [_P, _I32, _P, _P, _P]
@@ -190,6 +196,18 @@ def kv_compress(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, 
                              norm_eps, _ptr(out), out.stride(0), _stream(stream)), "kv_compress")
 
 
+def kv_prefill_pages(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, max_ntok: int, block_table,
+                     dst: "PagedCache", stream=None, norm_gamma=None, norm_eps: float = 1e-6, overlap: int = 0):
+    """The fused prefill of one pool: kv_compress + kv_quantize_page in one launch, no fp32 entries.
+    x: bf16 [B, T, d] (or int16 bit patterns); gate_logit f32 [B, T]; pos0 (multiples of 256), ntok int32 [B];
+    block_table int32 [B, nb]; with an overlap, rows -overlap .. -1 of x and gate_logit hold the tokens before pos0."""
+    B = x.shape[0]
+    _check(lib().kv_prefill_pages(_ptr(x), x.stride(0), _ptr(gate_logit), gate_logit.stride(0), _ptr(pos_bias),
+                                  _ptr(pos0), _ptr(ntok), B, max_ntok, m, overlap, rope_theta, _ptr(norm_gamma),
+                                  norm_eps, _ptr(block_table), block_table.stride(0), dst.c(), _stream(stream)),
+           "kv_prefill_pages")
+
+
 def kv_compress_insert(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, stage, e0, block_table,
                        dst: PagedCache, append: bool = False, stream=None, norm_gamma=None, norm_eps: float = 1e-6,
                        overlap: int = 0, fold_state=None):
@@ -275,6 +293,20 @@ def indexer_score(q_idx, head_w, idx_keys: PagedCache, block_table, seq_lens, ma
     _check(lib().hca_indexer_score(_ptr(q_idx), _ptr(head_w), HI, idx_keys.c(), _ptr(block_table),
                                    block_table.stride(0), _ptr(seq_lens), B, max_seq_len, m, k, _ptr(ws),
                                    ws.numel() * ws.element_size(), _stream(stream)), "hca_indexer_score")
+
+
+def attention_split(q, kv: PagedCache, block_table, win: Optional[PagedCache], win_block_table, seq_lens,
+                    max_seq_len: int, m: int, window: int, sel_idx, sel_n, softmax_scale: float, rope_theta: float, ws,
+                    stream=None):
+    """Measurement hook: the split kernel of paged_hybrid_decode alone (partials into ws, no output)."""
+    B, H, d = q.shape
+    k = 0 if sel_idx is None else sel_idx.shape[1]
+    wc = win.c() if (win is not None and window > 0) else _null_cache()
+    wbt = win_block_table if window > 0 else None
+    _check(lib().hca_attention_split(_ptr(q), H, kv.c(), _ptr(block_table), block_table.stride(0), wc, _ptr(wbt),
+                                     0 if wbt is None else wbt.stride(0), _ptr(seq_lens), B, max_seq_len, m, window,
+                                     _ptr(sel_idx), _ptr(sel_n), k, softmax_scale, rope_theta, _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)), "hca_attention_split")
 
 
 def paged_hybrid_decode_workspace(B: int, H: int, d: int, max_seq_len: int, m: int, window: int, k: int) -> int:

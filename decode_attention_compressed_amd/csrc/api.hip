@@ -143,6 +143,30 @@ hca_status kv_compress_insert_jobs(const hca_insert_job* jobs, int32_t n_jobs, i
   return from_hip(launch_insert(all, B, (hipStream_t)stream));
 }
 
+hca_status kv_prefill_pages(const uint16_t* x, int64_t x_stride_b, const float* gate_logit, int64_t z_stride_b,
+                            const float* pos_bias, const int32_t* pos0, const int32_t* ntok, int32_t B,
+                            int32_t max_ntok, int32_t m, int32_t overlap, float rope_theta, const float* norm_gamma,
+                            float norm_eps, const int32_t* block_table, int32_t bt_stride, hca_paged_cache dst,
+                            void* stream) {
+  if (B < 0 || max_ntok < 0 || bt_stride < 1) return HCA_ERR_INVALID;
+  if (!valid_m(m) || !cache_ok(dst) || dst.epp != 256 / m) return HCA_ERR_INVALID;
+  const int d = dst.dim;
+  if (d > 2048) return HCA_ERR_UNSUPPORTED;
+  const hca_status ov = overlap_ok(m, overlap);
+  if (ov != HCA_OK) return ov;
+  if (!(rope_theta > 0.0f) || !isfinite(rope_theta)) return HCA_ERR_INVALID;
+  if (!norm_ok(norm_gamma, norm_eps)) return HCA_ERR_INVALID;
+  if (!prefill_supported(m, d, dst.epp, dst.dtype)) return HCA_ERR_UNSUPPORTED;
+  if (B == 0 || max_ntok == 0) return HCA_OK;
+  if (!x || !gate_logit || !pos_bias || !pos0 || !ntok || !block_table) return HCA_ERR_INVALID;
+  if (!aligned(x, 16) || x_stride_b % 8 != 0) return HCA_ERR_INVALID;
+  if (B > 1 && (x_stride_b < (int64_t)max_ntok * d || z_stride_b < max_ntok)) return HCA_ERR_INVALID;
+  PrefillArgs p{CompressArgs{x, x_stride_b, gate_logit, z_stride_b, pos_bias, pos0, ntok, B, max_ntok, d, m, overlap,
+                             rope_theta, 0.0, norm_gamma, norm_eps, nullptr, 0},
+                block_table, bt_stride, dst};
+  return from_hip(launch_prefill(p, (hipStream_t)stream));
+}
+
 size_t kv_quantize_page_workspace(int32_t B, int32_t max_ne, hca_paged_cache dst) {
   if (B < 0 || max_ne < 0 || !cache_ok(dst)) return 0;
   return quantize_ws_bytes(B, max_ne, dst);
@@ -266,12 +290,18 @@ size_t paged_hybrid_decode_workspace(int32_t B, int32_t H, int32_t d, int32_t ma
   return attn_plan(B, H, d, max_seq_len, m, window, k, k > 0).total;
 }
 
-hca_status paged_hybrid_decode(const uint16_t* q, int32_t H, hca_paged_cache kv, const int32_t* block_table,
-                               int32_t bt_stride, hca_paged_cache win, const int32_t* win_block_table,
-                               int32_t wbt_stride, const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t m,
-                               int32_t window, const int32_t* sel_idx, const int32_t* sel_n, int32_t k,
-                               float softmax_scale, float rope_theta, float* out, float* lse, uint8_t* out_fp8,
-                               float* out_scale, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// paged_hybrid_decode's host validation and launch arguments (the workspace
+// pointer left null); HCA_OK when a launch may follow (B > 0)
+hca_status attn_prepare(const uint16_t* q, int32_t H, hca_paged_cache kv, const int32_t* block_table,
+                        int32_t bt_stride, hca_paged_cache win, const int32_t* win_block_table, int32_t wbt_stride,
+                        const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t m, int32_t window,
+                        const int32_t* sel_idx, const int32_t* sel_n, int32_t k, float softmax_scale,
+                        float rope_theta, float* out, float* lse, uint8_t* out_fp8, float* out_scale, AttnArgs& a,
+                        bool& empty) {
+  empty = false;
   if (B < 0 || max_seq_len < 0 || !valid_m(m) || bt_stride < 1) return HCA_ERR_INVALID;
   if (H < 1) return HCA_ERR_INVALID;
   if (H > 128) return HCA_ERR_UNSUPPORTED;
@@ -288,20 +318,61 @@ hca_status paged_hybrid_decode(const uint16_t* q, int32_t H, hca_paged_cache kv,
   if ((int64_t)bt_stride * 256 < max_seq_len) return HCA_ERR_INVALID;
   if (sel_idx && (!sel_n || k < 1)) return HCA_ERR_INVALID;
   if (!isfinite(softmax_scale) || !(rope_theta > 0.0f) || !isfinite(rope_theta)) return HCA_ERR_INVALID;
-  if (B == 0) return HCA_OK;
+  if (B == 0) {
+    empty = true;
+    return HCA_OK;
+  }
   if (!q || !block_table || !seq_lens || (!out && !out_fp8)) return HCA_ERR_INVALID;
   if (out_fp8 && (!out_scale || !aligned(out_fp8, 2))) return HCA_ERR_INVALID;
   if (!aligned(q, 16)) return HCA_ERR_INVALID;
   const AttnPlan plan = attn_plan(B, H, d, max_seq_len, m, window, sel_idx ? k : 0, sel_idx != nullptr);
-  if (plan.splits > kAttnMaxSplits) return HCA_ERR_UNSUPPORTED;
-  if (!ws || ws_bytes < plan.total || !aligned(ws, 256)) return HCA_ERR_WORKSPACE;
+  if (plan.items - B + 1 > kAttnMaxSplits) return HCA_ERR_UNSUPPORTED;  // splits of one sequence
   hca_paged_cache w = win;
   if (window == 0) { w = kv; w.epp = 256; }  // never read
-  AttnArgs a{q, H, kv, block_table, bt_stride, w, window > 0 ? win_block_table : block_table,
-             window > 0 ? wbt_stride : bt_stride, seq_lens, B, max_seq_len, m, window, sel_idx, sel_n,
-             sel_idx ? k : 0, softmax_scale, rope_theta, 0.0, out, lse, out_fp8, out_fp8 ? out_scale : nullptr,
-             reinterpret_cast<unsigned char*>(ws), plan};
+  a = AttnArgs{q, H, kv, block_table, bt_stride, w, window > 0 ? win_block_table : block_table,
+               window > 0 ? wbt_stride : bt_stride, seq_lens, B, max_seq_len, m, window, sel_idx, sel_n,
+               sel_idx ? k : 0, softmax_scale, rope_theta, 0.0, out, lse, out_fp8, out_fp8 ? out_scale : nullptr,
+               nullptr, plan};
+  return HCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hca_status paged_hybrid_decode(const uint16_t* q, int32_t H, hca_paged_cache kv, const int32_t* block_table,
+                               int32_t bt_stride, hca_paged_cache win, const int32_t* win_block_table,
+                               int32_t wbt_stride, const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t m,
+                               int32_t window, const int32_t* sel_idx, const int32_t* sel_n, int32_t k,
+                               float softmax_scale, float rope_theta, float* out, float* lse, uint8_t* out_fp8,
+                               float* out_scale, void* ws, size_t ws_bytes, void* stream) {
+  AttnArgs a{};
+  bool empty = false;
+  const hca_status st = attn_prepare(q, H, kv, block_table, bt_stride, win, win_block_table, wbt_stride, seq_lens, B,
+                                     max_seq_len, m, window, sel_idx, sel_n, k, softmax_scale, rope_theta, out, lse,
+                                     out_fp8, out_scale, a, empty);
+  if (st != HCA_OK || empty) return st;
+  if (!ws || ws_bytes < a.plan.total || !aligned(ws, 256)) return HCA_ERR_WORKSPACE;
+  a.ws = reinterpret_cast<unsigned char*>(ws);
   return from_hip(launch_attention(a, (hipStream_t)stream));
+}
+
+hca_status hca_attention_split(const uint16_t* q, int32_t H, hca_paged_cache kv, const int32_t* block_table,
+                               int32_t bt_stride, hca_paged_cache win, const int32_t* win_block_table,
+                               int32_t wbt_stride, const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t m,
+                               int32_t window, const int32_t* sel_idx, const int32_t* sel_n, int32_t k,
+                               float softmax_scale, float rope_theta, void* ws, size_t ws_bytes, void* stream) {
+  AttnArgs a{};
+  bool empty = false;
+  float dummy_out = 0.0f;  // never written: the combine is not launched
+  const hca_status st = attn_prepare(q, H, kv, block_table, bt_stride, win, win_block_table, wbt_stride, seq_lens, B,
+                                     max_seq_len, m, window, sel_idx, sel_n, k, softmax_scale, rope_theta, &dummy_out,
+                                     nullptr, nullptr, nullptr, a, empty);
+  if (st != HCA_OK || empty) return st;
+  if (!ws || ws_bytes < a.plan.total || !aligned(ws, 256)) return HCA_ERR_WORKSPACE;
+  a.ws = reinterpret_cast<unsigned char*>(ws);
+  a.out = nullptr;
+  return from_hip(launch_attention(a, (hipStream_t)stream, true));
 }
 
 hca_status kv_gather(hca_paged_cache src, const int32_t* block_table, int32_t bt_stride, const int32_t* n_rows,

@@ -69,28 +69,121 @@ AttnPlan attn_plan(int B, int H, int d, int max_seq_len, int m, int window, int 
   const int n_max = (max_seq_len + m - 1) / m;
   const int ent = has_sel ? (k < n_max ? k : n_max) : n_max;
   const int win = window < max_seq_len ? window : max_seq_len;
-  p.rows_max = ent + win;
+  p.tiles_max = (ent + win + kTileRows - 1) / kTileRows;
   p.head_blocks = (H + kHeadsPerBlock - 1) / kHeadsPerBlock;
-  // as many splits as give every CU one block (at least one tile each), and
-  // no split longer than kMaxSplitTiles tiles; then the tiles are spread evenly
-  const int64_t units = (int64_t)(B > 0 ? B : 1) * p.head_blocks;
-  const int64_t tiles = (p.rows_max + kTileRows - 1) / kTileRows;
-  int64_t splits = kCUs / units;
-  splits = splits < tiles ? splits : tiles;
-  const int64_t need = (tiles + kMaxSplitTiles - 1) / kMaxSplitTiles;
-  splits = splits > need ? splits : need;
-  splits = splits > 1 ? splits : 1;
-  const int64_t tps = tiles > 0 ? (tiles + splits - 1) / splits : 1;
-  p.tiles = (int)tps;
-  p.rows_per_split = kTileRows * p.tiles;
-  splits = p.rows_max > 0 ? (p.rows_max + p.rows_per_split - 1) / p.rows_per_split : 1;
-  p.splits = (int)(splits > 2 * (int64_t)kMaxSplits ? 2 * (int64_t)kMaxSplits : splits);  // caller rejects > kMaxSplits
+  // as many items as give every CU one block, unless splits of kMaxSplitTiles
+  // tiles need more
+  const int64_t bb = B > 0 ? B : 1;
+  const int64_t target = kCUs / p.head_blocks > 0 ? kCUs / p.head_blocks : 1;
+  const int64_t need = (bb * p.tiles_max + kMaxSplitTiles - 1) / kMaxSplitTiles;
+  // splits sized to fill `target` items; when the splits of kMaxSplitTiles
+  // tiles are fewer than that, the grid still holds all of them
+  const int64_t cap = (target > need ? target : need) + bb;
+  p.spread = (int)target;
+  p.items = (int)(cap > 1 << 25 ? 1 << 25 : cap);
+  // the work list when every sequence has max_seq_len tokens (the device's
+  // formula with those lengths): T tiles a split, S splits a sequence
+  const int64_t tot = bb * p.tiles_max;
+  int64_t tu = (tot + p.spread - 1) / p.spread;
+  tu = tu < 1 ? 1 : (tu > kMaxSplitTiles ? kMaxSplitTiles : tu);
+  p.t_uni = (int)tu;
+  p.s_uni = (int)((p.tiles_max + tu - 1) / tu);
+  p.s_uni = p.s_uni > 0 ? p.s_uni : 1;
   size_t off = 0;
-  p.o_off = off; off = align256a(off + (size_t)B * p.splits * H * d * sizeof(float));
-  p.ml_off = off; off = align256a(off + (size_t)B * p.splits * H * 2 * sizeof(float));
+  p.o_off = off; off = align256a(off + (size_t)p.items * H * d * sizeof(float));
+  p.ml_off = off; off = align256a(off + (size_t)p.items * H * 2 * sizeof(float));
   p.total = off;
   return p;
 }
+
+// ---- the work list, derived by every wave from the lengths alone
+// Tiles of sequence b as the plan counts them: an upper bound of its rows from
+// its length (min(k, N) selected entries, or all N; then min(W, L) window rows).
+__device__ __forceinline__ int plan_tiles(const AttnArgs& a, int L) {
+  const int N = (L + a.m - 1) / a.m;
+  const int n = a.sel ? min(a.k, N) : N;
+  return (n + min(a.window, L) + kTileRows - 1) / kTileRows;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    v += lane >= o ? t : 0;
+  }
+  return v;
+}
+
+struct Work {
+  int b;  // sequence (-1: past the work list)
+  int s;  // split of b (find by item), or b's first item (find by sequence)
+  int T;  // tiles per split
+  int S;  // splits of b
+  int L;  // b's length, clamped
+};
+
+// The first 64 lengths, one per lane: loaded by a kernel before anything
+// else, so that waiting for them (vector loads complete in issue order) waits
+// for nothing issued after them.
+__device__ __forceinline__ int attn_lens0(const AttnArgs& a) {
+  const int lane = threadIdx.x & 63;
+  return lane < a.B ? a.lens[lane] : 0;
+}
+
+// Every sequence's tiles are cut into splits of T tiles, with T = ceil(total /
+// spread) clamped to [1, kMaxSplitTiles], so the splits number at most spread
+// + B, or total / kMaxSplitTiles + B when T is clamped (a sequence of t tiles
+// has ceil(t / T) <= t / T + 1 of them); items are numbered sequence by
+// sequence.  by_item: the split that is item `key`; otherwise the splits of
+// sequence `key`.  lens0 is attn_lens0(a).  Called by a whole wave, all lanes
+// get the result; every wave of every block of a launch finds the same list.
+__device__ Work attn_work(const AttnArgs& a, int key, bool by_item, int lens0) {
+  const int lane = threadIdx.x & 63;
+  int total = 0;
+  const int L0 = clampi(lens0, 0, a.max_len);
+  for (int c0 = 0; c0 < a.B; c0 += 64) {
+    const int i = c0 + lane;
+    const int L = c0 == 0 ? L0 : (i < a.B ? clampi(a.lens[i], 0, a.max_len) : 0);
+    total += wave_sum_i(i < a.B ? plan_tiles(a, L) : 0);
+  }
+  const int T = clampi((total + a.plan.spread - 1) / a.plan.spread, 1, kMaxSplitTiles);
+  Work w{-1, 0, T, 0, 0};
+  int off = 0;
+  for (int c0 = 0; c0 < a.B; c0 += 64) {
+    const int i = c0 + lane;
+    const int L = c0 == 0 ? L0 : (i < a.B ? clampi(a.lens[i], 0, a.max_len) : 0);
+    const int S = i < a.B ? (plan_tiles(a, L) + T - 1) / T : 0;
+    const int incl = off + wave_incl_scan(S, lane);
+    const int excl = incl - S;
+    const bool hit = by_item ? (i < a.B && excl <= key && key < incl) : i == key;
+    const uint64_t bal = __ballot(hit);
+    if (bal != 0) {
+      const int src = __builtin_ctzll(bal);
+      w.b = c0 + src;
+      w.S = __shfl(S, src, 64);
+      w.s = by_item ? key - __shfl(excl, src, 64) : __shfl(excl, src, 64);
+      w.L = __shfl(L, src, 64);
+      break;
+    }
+    off = __shfl(incl, 63, 64);
+  }
+  return w;
+}
+
+// Block -> (work item, head group): the head groups of one item run on one XCD
+// (one L2: they read the same rows).  Workgroups go to the XCDs in turn, so
+// block id i runs on XCD i % 8; the grid is padded to whole rounds.
+__device__ __forceinline__ int attn_item_of_block(const AttnArgs& a) {
+  const int id = blockIdx.x, HB = a.plan.head_blocks;
+  const int item = (id / kXcds / HB) * kXcds + id % kXcds;
+  return item < a.plan.items ? item : -1;
+}
+__device__ __forceinline__ int attn_hb_of_block(const AttnArgs& a) { return (blockIdx.x / kXcds) % a.plan.head_blocks; }
 
 // LDS-only barrier: orders the block's LDS accesses without waiting for its
 // outstanding global loads (a full __syncthreads also drains those).
@@ -251,60 +344,60 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
   __shared__ __attribute__((aligned(16))) float wt_s[kAttnWaves][kHeadsPerBlock];
   static_assert(sizeof(float) * 2 * kHeadsPerBlock * D <= kHalfBytes, "the merge reuses the tiles");
 
-  // The head groups of one (split, sequence) read the same rows, so they run
-  // on one XCD (one L2): workgroups go to the XCDs in turn, so block id i runs
-  // on XCD i % 8; the grid is padded to whole rounds.
-  int s, b, hb;
-  {
-    const int id = blockIdx.x, HB = a.plan.head_blocks;
-    const int j = id / kXcds;
-    const int grp = (j / HB) * kXcds + id % kXcds;  // (split, sequence) pair
-    if (grp >= (int64_t)a.plan.splits * a.B) return;
-    hb = j % HB;
-    s = grp % a.plan.splits;
-    b = grp / a.plan.splits;
-  }
+  const int item = attn_item_of_block(a);
+  if (item < 0) return;
+  const int lens0 = attn_lens0(a);
+  const int hb = attn_hb_of_block(a);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, g = lane >> 4;
-  const int RPS = a.plan.rows_per_split;  // a multiple of 32, <= kMaxSplitRows
-  const int r0 = s * RPS;
   // A wave owns the split's tiles wave, wave + 4, ... and resolves their rows
   // itself (lane l: row l % 32 of every other one of them), so nothing but the
   // RoPE table makes a wave wait for another before the merge.
   auto row_of = [&](int j) { return kTileRows * (wave + kAttnWaves * (2 * j + (lane >> 5))) + (lane & 31); };
-  // loaded before the lengths are known: the selected entry of each row, or
-  // (no selection: row r is entry r) the page of that entry
-  int pre[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = row_of(j);
-    const int r = r0 + i;
-    pre[j] = 0;
-    if (i < RPS) {
-      if (a.sel != nullptr)
-        pre[j] = gload<int>(a.sel + (int64_t)b * a.k + min(r, a.k - 1));
-      else
-        pre[j] = gload<int>(a.bt + (int64_t)b * a.bts + min(r >> __builtin_ctz(a.kv.epp), a.bts - 1));
-    }
-  }
   const int H = a.H;
   const int h0 = hb * kHeadsPerBlock;
   const int head = h0 + col;  // head of this lane's q / P / m / l
-  // ---- query loads (bf16) in the k-slot map, also before the lengths arrive;
-  // each wave loads and rotates a quarter of the k-steps (the block's query
-  // is 16 x D bf16, read once per block rather than once per wave)
+  // each wave loads and rotates a quarter of the query's k-steps (the block's
+  // query is 16 x D bf16, read once per block rather than once per wave)
   constexpr int KSW = KS >= kAttnWaves ? KS / kAttnWaves : 1;
   const int tq0 = wave * KSW;
   const bool hv = head < H;
+  // the first loads of a work item (sequence bb, split ss of tt tiles): the
+  // selected entry of each row, or (no selection: row r is entry r) the page
+  // of that entry, and the query (bf16) in the k-slot map
+  int pre[kPer];
   u32x4 qraw[KSW];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)b * H + (hv ? head : H - 1)) * D;
+  auto first_loads = [&](int bb, int ss, int tt) {
+    const int rps = kTileRows * tt, rr0 = ss * rps;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = row_of(j);
+      const int r = rr0 + i;
+      pre[j] = 0;
+      if (i < rps) {
+        if (a.sel != nullptr)
+          pre[j] = gload<int>(a.sel + (int64_t)bb * a.k + min(r, a.k - 1));
+        else
+          pre[j] = gload<int>(a.bt + (int64_t)bb * a.bts + min(r >> __builtin_ctz(a.kv.epp), a.bts - 1));
+      }
+    }
+    const uint16_t* qrow = a.q + ((int64_t)bb * H + (hv ? head : H - 1)) * D;
 #pragma unroll
     for (int i = 0; i < KSW; ++i)
       qraw[i] = tq0 + i < KS ? gload<u32x4>(qrow + kslot_dim<D, KVDT>(tq0 + i, g)) : u32x4{0u, 0u, 0u, 0u};
-  }
-  const int L = clampi(a.lens[b], 0, a.max_len);
+  };
+  // issued before the lengths are known, for the work list of equal lengths
+  // (max_seq_len each); another list's item gets them again
+  const int su = a.plan.s_uni, tu = a.plan.t_uni;
+  if (item / su < a.B) first_loads(item / su, item % su, tu);
+  const Work wk = attn_work(a, item, true, lens0);
+  if (wk.b < 0) return;  // past the work list
+  if (wk.b != item / su || wk.s != item % su || wk.T != tu) first_loads(wk.b, wk.s, wk.T);
+  const int b = wk.b, s = wk.s;
+  const int RPS = kTileRows * wk.T;  // <= kMaxSplitRows
+  const int r0 = s * RPS;
+  const int L = wk.L;
   const int N = (L + a.m - 1) / a.m;
   const int n_sel = a.sel ? clampi(a.sel_n[b], 0, a.k) : N;
   const int n_win = min(a.window, L);
@@ -312,7 +405,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
   const int r1 = min(rows_b, r0 + RPS);
   float2* ml = reinterpret_cast<float2*>(a.ws + a.plan.ml_off);
   float* opart = reinterpret_cast<float*>(a.ws + a.plan.o_off);
-  const size_t part = ((size_t)b * a.plan.splits + s) * H;
+  const size_t part = (size_t)item * H;
 
   if (r0 >= r1) {  // empty split
     if (threadIdx.x < kHeadsPerBlock && h0 + (int)threadIdx.x < H)
@@ -755,38 +848,17 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
   static_assert(sizeof(q_s) == (size_t)kPairWaves * 2 * 64 * sizeof(f32x4), "partial S exchange area");
   static_assert(2 * sizeof(float) * kHeadsPerBlock * D <= kPairs * PT::BYTES, "the merge reuses the tiles");
 
-  int s, b, hb;
-  {
-    const int id = blockIdx.x, HB = a.plan.head_blocks;
-    const int j = id / kXcds;
-    const int grp = (j / HB) * kXcds + id % kXcds;  // (split, sequence) pair
-    if (grp >= (int64_t)a.plan.splits * a.B) return;
-    hb = j % HB;
-    s = grp % a.plan.splits;
-    b = grp / a.plan.splits;
-  }
+  const int item = attn_item_of_block(a);
+  if (item < 0) return;
+  const int lens0 = attn_lens0(a);
+  const int hb = attn_hb_of_block(a);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int pair = wave >> 1, hf = wave & 1;
   const int col = lane & 15, g = lane >> 4;
-  const int RPS = a.plan.rows_per_split;
-  const int r0 = s * RPS;
   // rows of the pair's tiles, split over its two waves: lane l of wave
   // (pair, hf) resolves row l % 32 of the pair's tiles 4j + 2hf + l / 32
   auto row_of = [&](int j) { return kTileRows * (pair + kPairs * (4 * j + 2 * hf + (lane >> 5))) + (lane & 31); };
-  int pre[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = row_of(j);
-    const int r = r0 + i;
-    pre[j] = 0;
-    if (i < RPS) {
-      if (a.sel != nullptr)
-        pre[j] = gload<int>(a.sel + (int64_t)b * a.k + min(r, a.k - 1));
-      else
-        pre[j] = gload<int>(a.bt + (int64_t)b * a.bts + min(r >> __builtin_ctz(a.kv.epp), a.bts - 1));
-    }
-  }
   const int H = a.H;
   const int h0 = hb * kHeadsPerBlock;
   const int head = h0 + col;
@@ -794,13 +866,39 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
   constexpr int KSW = KS / kPairWaves;
   const int tq0 = wave * KSW;
   const bool hv = head < H;
+  // the first loads of a work item (sequence bb, split ss of tt tiles): the
+  // selected entry or the page of each row, and the query
+  int pre[kPer];
   u32x4 qraw[KSW];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)b * H + (hv ? head : H - 1)) * D;
+  auto first_loads = [&](int bb, int ss, int tt) {
+    const int rps = kTileRows * tt, rr0 = ss * rps;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = row_of(j);
+      const int r = rr0 + i;
+      pre[j] = 0;
+      if (i < rps) {
+        if (a.sel != nullptr)
+          pre[j] = gload<int>(a.sel + (int64_t)bb * a.k + min(r, a.k - 1));
+        else
+          pre[j] = gload<int>(a.bt + (int64_t)bb * a.bts + min(r >> __builtin_ctz(a.kv.epp), a.bts - 1));
+      }
+    }
+    const uint16_t* qrow = a.q + ((int64_t)bb * H + (hv ? head : H - 1)) * D;
 #pragma unroll
     for (int i = 0; i < KSW; ++i) qraw[i] = gload<u32x4>(qrow + pair_kdim(tq0 + i, g));
-  }
-  const int L = clampi(a.lens[b], 0, a.max_len);
+  };
+  // issued before the lengths are known, for the work list of equal lengths
+  // (max_seq_len each); another list's item gets them again
+  const int su = a.plan.s_uni, tu = a.plan.t_uni;
+  if (item / su < a.B) first_loads(item / su, item % su, tu);
+  const Work wk = attn_work(a, item, true, lens0);
+  if (wk.b < 0) return;  // past the work list
+  if (wk.b != item / su || wk.s != item % su || wk.T != tu) first_loads(wk.b, wk.s, wk.T);
+  const int b = wk.b, s = wk.s;
+  const int RPS = kTileRows * wk.T;  // <= kMaxSplitRows
+  const int r0 = s * RPS;
+  const int L = wk.L;
   const int N = (L + a.m - 1) / a.m;
   const int n_sel = a.sel ? clampi(a.sel_n[b], 0, a.k) : N;
   const int n_win = min(a.window, L);
@@ -808,7 +906,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
   const int r1 = min(rows_b, r0 + RPS);
   float2* ml = reinterpret_cast<float2*>(a.ws + a.plan.ml_off);
   float* opart = reinterpret_cast<float*>(a.ws + a.plan.o_off);
-  const size_t part = ((size_t)b * a.plan.splits + s) * H;
+  const size_t part = (size_t)item * H;
 
   if (r0 >= r1) {  // empty split (the whole block returns)
     if (threadIdx.x < kHeadsPerBlock && h0 + (int)threadIdx.x < H)
@@ -1132,31 +1230,43 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
   const int h = blockIdx.x, b = blockIdx.y;
   const int H = a.H;
   const int grp = threadIdx.x / TPG, li = threadIdx.x % TPG;
-  const int Smax = a.plan.splits;
-  const float2* ml = reinterpret_cast<const float2*>(a.ws + a.plan.ml_off) + (size_t)b * a.plan.splits * H + h;
-  const f32x4* opart =
-      reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.ws + a.plan.o_off) + ((size_t)b * a.plan.splits * H + h) * D) + li;
-  const size_t ostride = (size_t)H * D / 4;  // f32x4 between consecutive splits
+  const float2* ml = reinterpret_cast<const float2*>(a.ws + a.plan.ml_off) + h;
+  const f32x4* opart = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.ws + a.plan.o_off) + (size_t)h * D) + li;
+  const size_t ostride = (size_t)H * D / 4;  // f32x4 between consecutive items
   __shared__ float w_s[kMaxSplits];
   __shared__ float red_s[kCombThreads / 64];
   __shared__ f32x4 acc_s[SG][TPG];
-
-  // first round of partial loads and the first kCombThreads (m, l) pairs,
-  // issued before the lengths are known (every split the plan has is in the
-  // workspace; the ones past this sequence's end get weight 0)
-  // ((m, l) first: loads complete in issue order, and the split maximum needs
-  // only these)
-  const float2 ml0 = (int)threadIdx.x < Smax ? ml[(size_t)threadIdx.x * H] : make_float2(-INFINITY, 0.0f);
-  // (unguarded, the split index clamped into the plan's: guarded loads are
-  // branches, across which the loads' waits are no longer counted exactly)
+  // this sequence's splits are items off .. off + Sp - 1.  The first round of
+  // partial loads and the first kCombThreads (m, l) pairs are issued before the
+  // lengths are known, for the work list of equal lengths (max_seq_len each),
+  // and again if the lengths give another list ((m, l) first: loads complete
+  // in issue order, and the split maximum needs only these; unguarded, the
+  // split index clamped into the sequence's, item 0 if it has none: guarded
+  // loads are branches, across which the loads' waits are no longer counted
+  // exactly)
+  const int lens0 = attn_lens0(a);
+  int off = b * a.plan.s_uni, Sp = a.plan.s_uni;
+  auto item_of = [&](int s) { return Sp > 0 ? off + min(s, Sp - 1) : 0; };
+  float2 ml0;
   f32x4 o[kCombU];
+  auto first_loads = [&]() {
+    ml0 = (int)threadIdx.x < Sp ? ml[(size_t)(off + threadIdx.x) * H] : make_float2(-INFINITY, 0.0f);
 #pragma unroll
-  for (int u = 0; u < kCombU; ++u) o[u] = opart[(size_t)min(grp + SG * u, Smax - 1) * ostride];
-  const int L = clampi(a.lens[b], 0, a.max_len);
+    for (int u = 0; u < kCombU; ++u) o[u] = opart[(size_t)item_of(grp + SG * u) * ostride];
+  };
+  first_loads();
+  const Work wk = attn_work(a, b, false, lens0);
+  if (wk.s != off || wk.S != Sp) {
+    off = wk.s;
+    Sp = wk.S;
+    first_loads();
+  }
+  const int L = wk.L;
   const int N = (L + a.m - 1) / a.m;
   const int n_sel = a.sel ? clampi(a.sel_n[b], 0, a.k) : N;
   const int rows_b = n_sel + min(a.window, L);
-  const int S = min(Smax, (rows_b + a.plan.rows_per_split - 1) / a.plan.rows_per_split);
+  const int RPS = kTileRows * wk.T;
+  const int S = min(Sp, (rows_b + RPS - 1) / RPS);
   // the inverse rotation at L-1, while the loads are in flight
   float2 cs[kPairs];
 #pragma unroll
@@ -1168,7 +1278,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
   }
   // split maxima -> M; weights w_s = exp(m_s - M) (0 for empty splits); tot = sum w_s l_s
   float mloc = (int)threadIdx.x < S ? ml0.x : -INFINITY;
-  for (int s = threadIdx.x + kCombThreads; s < S; s += kCombThreads) mloc = fmaxf(mloc, ml[(size_t)s * H].x);
+  for (int s = threadIdx.x + kCombThreads; s < S; s += kCombThreads) mloc = fmaxf(mloc, ml[(size_t)(off + s) * H].x);
   mloc = wave_max(mloc);
   if ((threadIdx.x & 63) == 0) red_s[threadIdx.x >> 6] = mloc;
   __syncthreads();
@@ -1194,7 +1304,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
     tloc += w * ml0.y;
   }
   for (int s = threadIdx.x + kCombThreads; s < S; s += kCombThreads) {
-    const float2 v = ml[(size_t)s * H];
+    const float2 v = ml[(size_t)(off + s) * H];
     const float w = v.y > 0.0f ? expf(v.x - M) : 0.0f;
     w_s[s] = w;
     tloc += w * v.y;
@@ -1216,7 +1326,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
 #pragma unroll
     for (int u = 0; u < kCombU; ++u) {  // next round (more than SG * kCombU splits)
       const int s = s0 + SG * (kCombU + u);
-      o[u] = opart[(size_t)min(s, Smax - 1) * ostride];
+      o[u] = opart[(size_t)item_of(s) * ostride];
     }
   }
   acc_s[grp][li] = acc;
@@ -1267,8 +1377,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
 
 template <int D, int KVDT>
 static hipError_t launch_split(const AttnArgs& a, hipStream_t s) {
-  const int64_t groups = (int64_t)a.plan.splits * a.B;
-  const int64_t blocks = (groups + kXcds - 1) / kXcds * kXcds * a.plan.head_blocks;
+  const int64_t blocks = ((int64_t)a.plan.items + kXcds - 1) / kXcds * kXcds * a.plan.head_blocks;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if constexpr (D == kPairD && KVDT == HCA_FP8_E4M3)
     hipLaunchKernelGGL(attn_pair_kernel, dim3((unsigned)blocks), dim3(kPairThreads), 0, s, a);
@@ -1285,10 +1394,19 @@ static hipError_t launch_attn_d(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs& args, hipStream_t s) {
+hipError_t launch_attention(const AttnArgs& args, hipStream_t s, bool split_only) {
   if (args.B == 0) return hipSuccess;
   AttnArgs a = args;
   a.rope_r = pow((double)a.theta, -2.0 / (double)a.kv.dim);
+  if (split_only) {
+    const bool f8 = a.kv.dtype == HCA_FP8_E4M3;
+    switch (a.kv.dim) {
+      case 64: return f8 ? launch_split<64, HCA_FP8_E4M3>(a, s) : launch_split<64, HCA_BF16>(a, s);
+      case 128: return f8 ? launch_split<128, HCA_FP8_E4M3>(a, s) : launch_split<128, HCA_BF16>(a, s);
+      case 256: return f8 ? launch_split<256, HCA_FP8_E4M3>(a, s) : launch_split<256, HCA_BF16>(a, s);
+      default: return f8 ? launch_split<512, HCA_FP8_E4M3>(a, s) : launch_split<512, HCA_BF16>(a, s);
+    }
+  }
   switch (a.kv.dim) {
     case 64: return launch_attn_d<64>(a, s);
     case 128: return launch_attn_d<128>(a, s);

@@ -174,9 +174,13 @@ struct NoMid {
   __device__ void operator()() const {}
 };
 
+// A large-m fold may also keep every entry it folds in shared memory:
+// lds_stride > 0 puts entry j at lds_row + (j - lds_j0) * lds_stride (the
+// fused prefill's page); a null a.out then skips the global write.
 template <int PATHS = 3, typename Mid = NoMid>
 __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int bx, int gx, float* lds_row, int n,
-                                               int p0, Mid&& mid, float* state_out = nullptr) {
+                                               int p0, Mid&& mid, float* state_out = nullptr, int lds_j0 = 0,
+                                               int lds_stride = 0) {
   const int TD = a.d >> 3;              // threads across the dims of a row
   const int RP = kCompressThreads / TD; // row groups
   const int li = threadIdx.x % TD;
@@ -365,12 +369,16 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
       }
       float c, sn;
       rope_cs(pos, rope_inv_freq(t, a.rope_r), c, sn);
-      float* o = a.out + (int64_t)b * a.os + (int64_t)j * a.d + 2 * t;
-      o[0] = e0 * c - e1 * sn;
-      o[1] = e0 * sn + e1 * c;
+      const float o0 = e0 * c - e1 * sn, o1 = e0 * sn + e1 * c;
+      if (a.out != nullptr) {
+        float* o = a.out + (int64_t)b * a.os + (int64_t)j * a.d + 2 * t;
+        o[0] = o0;
+        o[1] = o1;
+      }
       if (lds_row != nullptr) {
-        lds_row[2 * t] = o[0];
-        lds_row[2 * t + 1] = o[1];
+        float* l = lds_row + (int64_t)(j - lds_j0) * lds_stride;
+        l[2 * t] = o0;
+        l[2 * t + 1] = o1;
       }
     }
     __syncthreads();
@@ -405,6 +413,204 @@ hipError_t launch_compress(CompressArgs a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------- fused prefill
+// kv_prefill_pages: compressor + RMSNorm + RoPE + insertion of a whole run in
+// one launch (V4 page, section 3.2.1 lists them as one fused step; sections
+// 3.1.1 and 3.1.3: the page formats), one block per page: the block folds the
+// page's entries exactly as kv_compress folds them (the same per-entry
+// arithmetic in the same order), keeps them on chip, takes the page's amax and
+// writes its codes and scale exactly as kv_quantize_page does.  The fp32
+// entries never reach HBM.
+//
+// Small groups: a block of kPrefillThreads threads, row groups of d/8 threads
+// folding one entry each per round, the rotated rows held in registers (at
+// most kPrefillRounds rounds).  Large groups: a block of kCompressThreads
+// threads folds the page's entries one after the other (compress_block's
+// large path, so the same sums) into shared memory.
+constexpr int kPrefillThreads = 512;
+constexpr int kPrefillRounds = 8;
+
+// four fp8 codes of x / s (an fp8 page's encoding), packed little-endian
+__device__ __forceinline__ uint32_t enc4_e4m3(const f32x4 v, float s) {
+  return (uint32_t)e4m3_encode(v[0] / s) | ((uint32_t)e4m3_encode(v[1] / s) << 8) |
+         ((uint32_t)e4m3_encode(v[2] / s) << 16) | ((uint32_t)e4m3_encode(v[3] / s) << 24);
+}
+
+__device__ __forceinline__ void rope8(const float acc[8], double pos, const double inv[4], float o[8]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    float c, s;
+    rope_cs(pos, inv[p], c, s);
+    o[2 * p] = acc[2 * p] * c - acc[2 * p + 1] * s;
+    o[2 * p + 1] = acc[2 * p] * s + acc[2 * p + 1] * c;
+  }
+}
+
+__device__ __forceinline__ float block_max_n(float v, float* red, int nwaves) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < nwaves; ++i) r = fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+// the page of block (pg, b): its physical page and valid rows, or -1
+__device__ __forceinline__ int prefill_page(const PrefillArgs& p, int b, int pg, int n, int p0, int& rows) {
+  const int m = p.c.m, epp = p.dst.epp;
+  const int N = (n + m - 1) / m;
+  rows = min(epp, N - pg * epp);
+  if (rows <= 0) return -1;
+  const int lb = p0 / m / epp + pg;
+  if (lb < 0 || lb >= p.bts) return -1;
+  const int phys = p.bt[(int64_t)b * p.bts + lb];
+  return phys >= 0 && phys < p.dst.num_pages ? phys : -1;
+}
+
+__global__ __launch_bounds__(kPrefillThreads) void prefill_small_kernel(PrefillArgs p) {
+  const CompressArgs& a = p.c;
+  const int b = blockIdx.y, pg = blockIdx.x;
+  const int n = clampi(a.ntok[b], 0, a.max_ntok);
+  const int p0 = a.pos0[b];
+  int rows;
+  const int phys = prefill_page(p, b, pg, n, p0, rows);
+  if (phys < 0) return;  // uniform over the block
+  const int m = a.m, d = a.d, epp = p.dst.epp;
+  const int TD = d >> 3, RP = kPrefillThreads / TD;
+  const int li = threadIdx.x % TD, gi = threadIdx.x / TD;
+  const bool active = gi < RP;
+  const uint16_t* xb = a.x + (int64_t)b * a.xs + li * 8;
+  const float* zb = a.z + (int64_t)b * a.zs;
+  float gam[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (a.gamma != nullptr && active) {
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(a.gamma + li * 8);
+    const f32x4 g0 = g4[0], g1 = g4[1];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) { gam[c] = g0[c]; gam[4 + c] = g1[c]; }
+  }
+  double inv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) inv[q] = rope_inv_freq(li * 4 + q, a.rope_r);
+  __shared__ float sq_s[kPrefillThreads];
+  __shared__ float red_s[kPrefillThreads / 64];
+  float v[kPrefillRounds][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < kPrefillRounds; ++r) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[r][c] = 0.0f;
+    if (r * RP >= epp) continue;  // uniform
+    const int row = r * RP + gi;
+    const int j = pg * epp + row;
+    const bool live = active && row < rows;
+    float acc[8];
+    small_fold(a, zb, xb, j, n, p0, live, acc, NoMid{});
+    if (a.gamma != nullptr) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ss = fmaf(acc[c], acc[c], ss);
+      const float rs = 1.0f / sqrtf(row_group_sum(ss, TD, RP, gi, sq_s) / (float)d + a.eps);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = acc[c] * rs * gam[c];
+    }
+    if (live) {
+      rope8(acc, (double)p0 + (double)(j * m), inv, v[r]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(v[r][c]));
+    }
+  }
+  // the page: codes of the valid rows, zeros past them, and the scale
+  if (p.dst.dtype == HCA_FP8_E4M3) {
+    amax = block_max_n(amax, red_s, kPrefillThreads / 64);
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    uint8_t* codes = reinterpret_cast<uint8_t*>(p.dst.codes) + (int64_t)phys * epp * d;
+#pragma unroll
+    for (int r = 0; r < kPrefillRounds; ++r) {
+      const int row = r * RP + gi;
+      if (r * RP >= epp || !active || row >= epp) continue;
+      u32x2 w = {0u, 0u};
+      if (row < rows) {
+        w[0] = enc4_e4m3(f32x4{v[r][0], v[r][1], v[r][2], v[r][3]}, s);
+        w[1] = enc4_e4m3(f32x4{v[r][4], v[r][5], v[r][6], v[r][7]}, s);
+      }
+      *reinterpret_cast<u32x2*>(codes + (int64_t)row * d + li * 8) = w;
+    }
+    if (threadIdx.x == 0) reinterpret_cast<float*>(p.dst.scales)[phys] = s;
+  } else {  // bf16
+    uint16_t* codes = reinterpret_cast<uint16_t*>(p.dst.codes) + (int64_t)phys * epp * d;
+#pragma unroll
+    for (int r = 0; r < kPrefillRounds; ++r) {
+      const int row = r * RP + gi;
+      if (r * RP >= epp || !active || row >= epp) continue;
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (row < rows) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = (uint32_t)bf16_encode(v[r][2 * q]) | ((uint32_t)bf16_encode(v[r][2 * q + 1]) << 16);
+      }
+      *reinterpret_cast<u32x4*>(codes + (int64_t)row * d + li * 8) = w;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kCompressThreads) void prefill_large_kernel(PrefillArgs p) {
+  const CompressArgs& a = p.c;
+  const int b = blockIdx.y, pg = blockIdx.x;
+  const int n = clampi(a.ntok[b], 0, a.max_ntok);
+  const int p0 = a.pos0[b];
+  int rows;
+  const int phys = prefill_page(p, b, pg, n, p0, rows);
+  if (phys < 0) return;  // uniform over the block
+  const int m = a.m, d = a.d, epp = p.dst.epp;
+  extern __shared__ float dyn_s[];  // compress_block's row-group sums, then the page's rows
+  float* page_s = dyn_s + kCompressShm / sizeof(float);
+  // the page's entries, folded as kv_compress folds them, into page_s
+  const int j0 = pg * epp;
+  const int n_page = min(n, (j0 + epp) * m);
+  CompressArgs c = a;
+  c.out = nullptr;
+  compress_block<2>(c, b, j0, 1, page_s, n_page, p0, NoMid{}, nullptr, j0, d);
+  const int nv = rows * d;
+  if (p.dst.dtype == HCA_FP8_E4M3) {
+    __shared__ float red_s[kCompressThreads / 64];
+    float amax = 0.0f;
+    for (int i = threadIdx.x; i < nv; i += kCompressThreads) amax = fmaxf(amax, fabsf(page_s[i]));
+    amax = block_max_n(amax, red_s, kCompressThreads / 64);
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    uint32_t* codes = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.dst.codes) + (int64_t)phys * epp * d);
+    const f32x4* v4 = reinterpret_cast<const f32x4*>(page_s);
+    for (int i = threadIdx.x; i < epp * d / 4; i += kCompressThreads) codes[i] = i < nv / 4 ? enc4_e4m3(v4[i], s) : 0u;
+    if (threadIdx.x == 0) reinterpret_cast<float*>(p.dst.scales)[phys] = s;
+  } else {  // bf16
+    uint32_t* codes = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.dst.codes) + (int64_t)phys * epp * d);
+    for (int i = threadIdx.x; i < epp * d / 2; i += kCompressThreads)
+      codes[i] = i < nv / 2 ? (uint32_t)bf16_encode(page_s[2 * i]) | ((uint32_t)bf16_encode(page_s[2 * i + 1]) << 16)
+                            : 0u;
+  }
+}
+
+bool prefill_supported(int m, int d, int epp, int dtype) {
+  if (dtype != HCA_FP8_E4M3 && dtype != HCA_BF16) return false;
+  if (m <= kSmallM) return epp <= kPrefillRounds * (kPrefillThreads / (d / 8));
+  return (size_t)epp * d * sizeof(float) + kCompressShm <= (size_t)64 * 1024;
+}
+
+hipError_t launch_prefill(PrefillArgs p, hipStream_t s) {
+  CompressArgs& a = p.c;
+  const int n_max = (a.max_ntok + a.m - 1) / a.m;
+  if (a.B == 0 || n_max == 0) return hipSuccess;
+  a.rope_r = pow((double)a.theta, -2.0 / (double)a.d);
+  const int pages = (n_max + p.dst.epp - 1) / p.dst.epp;
+  if (a.m <= kSmallM) {
+    hipLaunchKernelGGL(prefill_small_kernel, dim3(pages, a.B), dim3(kPrefillThreads), 0, s, p);
+  } else {
+    const size_t shm = kCompressShm + (size_t)p.dst.epp * a.d * sizeof(float);
+    hipLaunchKernelGGL(prefill_large_kernel, dim3(pages, a.B), dim3(kCompressThreads), shm, s, p);
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------- decode-step insert
 // kv_compress_insert: a decode step's update of one pool in one launch, one
 // block per sequence: the open group's fold (compress_block, so the entry is
@@ -424,10 +630,6 @@ hipError_t launch_compress(CompressArgs a, hipStream_t s) {
 //   m = 1, the old scale is 1.0 (which an all-zero page also has).
 constexpr int kInsertMaxDim = 2048;
 
-__device__ __forceinline__ uint32_t enc4_e4m3(const f32x4 v, float s) {
-  return (uint32_t)e4m3_encode(v[0] / s) | ((uint32_t)e4m3_encode(v[1] / s) << 8) |
-         ((uint32_t)e4m3_encode(v[2] / s) << 16) | ((uint32_t)e4m3_encode(v[3] / s) << 24);
-}
 
 __device__ __forceinline__ float ins_block_max(float v, float* red) {
   v = wave_max(v);

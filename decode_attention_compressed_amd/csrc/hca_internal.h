@@ -26,6 +26,17 @@ constexpr int kCompressThreads = 256;
 constexpr int kSmallM = 16;  // groups up to this size are folded by one row group of threads
 constexpr size_t kCompressShm = (size_t)kCompressThreads * 8 * sizeof(float);  // a large-m fold's row-group sums
 
+// the fused prefill of one pool: fold, normalise, rotate and quantize a run's
+// pages in one launch, a block per page (the run starts a page)
+struct PrefillArgs {
+  CompressArgs c;
+  const int32_t* bt;
+  int bts;
+  hca_paged_cache dst;
+};
+bool prefill_supported(int m, int d, int epp, int dtype);
+hipError_t launch_prefill(PrefillArgs p, hipStream_t s);
+
 // decode-step update of pools: fold each open group into its staging row and
 // quantize the open page, all in one launch (a job per pool)
 struct InsertArgs {
@@ -74,13 +85,18 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 // the indexer's arguments and launchers (their own header: the indexer
 // source depends on nothing else here)
 
-// attention workspace: per (sequence, split, head) partial (m, l) and o[d]
+// attention launch plan.  The work list itself (which sequence and split a
+// block takes) is derived on the device from the lengths; the host bounds it:
+// every sequence's 32-row tiles are cut into splits of T tiles, T sized so that
+// the splits of all sequences fill `spread` work items (at most kMaxSplitTiles
+// tiles a split, which may take more), so at most `items` items exist.  The
+// workspace holds a partial (m, l) and o[d] per (item, head).
 struct AttnPlan {
-  int rows_max;     // upper bound of rows of any sequence
-  int splits;       // splits per sequence
-  int rows_per_split;
-  int tiles;        // 32-row tiles per split
+  int tiles_max;    // upper bound of 32-row tiles of any sequence
   int head_blocks;  // ceil(H / 16)
+  int spread;       // items the splits are sized to fill
+  int items;        // work items the grid holds: max(spread, B x tiles_max / kMaxSplitTiles) + B
+  int t_uni, s_uni; // tiles a split and splits a sequence when every sequence has max_seq_len tokens
   size_t o_off, ml_off, total;
 };
 constexpr int kAttnMaxSplits = 4096;  // splits per sequence the combine kernel handles
@@ -98,6 +114,7 @@ struct AttnArgs {
   uint8_t* out8; float* out8_scale;  // fp8 form of the output (null: none)
   unsigned char* ws; AttnPlan plan;
 };
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// split_only: the split kernel alone (partials in the workspace, no output), for timing
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s, bool split_only = false);
 
 }  // namespace hca

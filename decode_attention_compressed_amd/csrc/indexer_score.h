@@ -458,6 +458,13 @@ __device__ __forceinline__ void score_pages_block(const IndexerArgs& a, int bx, 
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  // the open indexer row (fp4 keys of 128 dims): its wave encodes it from
+  // staging, writes it to the page and scores it in place of the page's old
+  // bytes for that row.  Written before the length check, so that a row whose
+  // page lies inside the launch's pages is written even where it lies past
+  // the sequence's entries (nothing scores it then)
+  OpenRow orow;
+  if constexpr (KDT == HCA_FP4_E2M1 && DI == 128) orow.prepare(a, b, page0, wave, lane);
   const int L = clampi(len_raw, 0, a.max_len);
   const int N = (L + a.m - 1) / a.m;
   const int NP = (N + 63) / 64;
@@ -466,11 +473,6 @@ __device__ __forceinline__ void score_pages_block(const IndexerArgs& a, int bx, 
   c.hist_s = hist_s;
   c.scores = score_row(a, b);
   const int p_end = min(NP, page0 + kPagesPerScoreBlock);
-  // the open indexer row (fp4 keys of 128 dims): its wave encodes it from
-  // staging, writes it to the page and scores it in place of the page's old
-  // bytes for that row
-  OpenRow orow;
-  if constexpr (KDT == HCA_FP4_E2M1 && DI == 128) orow.prepare(a, b, page0, wave, lane);
   // a ring of kScoreBufs page buffers per wave: the first kScoreBufs pages are
   // loaded up front, page i + kScoreBufs as soon as page i is consumed
   PageTiles<KDT, DI> pt[kScoreBufs];

@@ -171,6 +171,34 @@ hca_status kv_quantize_page(const float* src, int64_t src_stride_b, const int32_
                             void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * kv_prefill_pages -- the prefill of one pool in one launch: the compressor,
+ * its RMSNorm, RoPE and the insertion into the cache fused (V4 page, section
+ * 3.2.1 lists compressor, RMSNorm, RoPE and cache insertion as one fused
+ * step; sections 3.1.1 and 3.1.3: the page formats).  The result is that of
+ * kv_compress(...) followed by kv_quantize_page(e0 = pos0[b] / m, ne =
+ * ceil(ntok[b] / m)) on its output: the same bytes in every page written,
+ * without the fp32 entries passing through memory.  Each page is folded,
+ * normalised, rotated and quantized by one block of the launch.
+ *
+ *   x, gate_logit, pos_bias, pos0, ntok, max_ntok, m, overlap, rope_theta,
+ *   norm_gamma, norm_eps: as kv_compress (d = dst.dim); pos0[b] must be a
+ *              multiple of 256 (the run starts a page; another value writes
+ *              the wrong pages, never out of bounds)
+ *   block_table int32 [B][bt_stride]: the page of logical block
+ *              pos0[b] / 256 + i holds the run's entries [i * epp, i * epp + epp)
+ *   dst        the pool; dst.epp == 256 / m; dtype HCA_FP8_E4M3 or HCA_BF16;
+ *              a page must fit one block: for m <= 16, dst.epp * d <= 32768
+ *              (d = 512: m >= 4; d = 128: any m), for m > 16,
+ *              dst.epp * d <= 14336 (HCA_ERR_UNSUPPORTED otherwise, nothing
+ *              launched: use kv_compress + kv_quantize_page)
+ */
+hca_status kv_prefill_pages(const uint16_t* x, int64_t x_stride_b, const float* gate_logit, int64_t z_stride_b,
+                            const float* pos_bias, const int32_t* pos0, const int32_t* ntok, int32_t B,
+                            int32_t max_ntok, int32_t m, int32_t overlap, float rope_theta, const float* norm_gamma,
+                            float norm_eps, const int32_t* block_table, int32_t bt_stride, hca_paged_cache dst,
+                            void* stream);
+
+/*
  * kv_compress_insert -- a decode step's update of one pool in one launch: the
  * open group is folded as kv_compress folds it (V4 page, section 2.1; section
  * 3.1.2: the open group is the rolling residual; section 3.2.1: RoPE, then
@@ -312,10 +340,12 @@ hca_status indexer_topk(const uint16_t* q_idx, const float* head_w, int32_t HI,
  * keys runs before the score pass: the open indexer row of a decode step (no
  * fold, append, fp4 keys of dim 128 with 64 entries per page, the indexer's
  * block table) inside it, encoded by the score blocks of its page; any other
- * as a launch of its own.  The open row is written there when it lies inside
- * the sequence's ceil(seq_lens[b] / m) entries, as a decode step's open entry
- * does (an open row past them, from lengths that disagree with the job's
- * positions, is left unwritten, where the two-call form would write it).  Jobs are validated as for kv_compress_insert_jobs,
+ * as a launch of its own.  The open row is written whenever it lies within
+ * the first ceil(max_seq_len / m) entries, the pages the score launch covers
+ * (it is scored only when it also lies within the sequence's
+ * ceil(seq_lens[b] / m) entries); an open row past that bound, from
+ * positions that disagree with max_seq_len, may be left unwritten, where the
+ * two-call form would write it.  Jobs are validated as for kv_compress_insert_jobs,
  * the indexer arguments as for indexer_topk; nothing is launched on any
  * error.
  */

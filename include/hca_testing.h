@@ -45,6 +45,16 @@ hca_status hca_indexer_score(const uint16_t* q_idx, const float* head_w, int32_t
                              const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens, int32_t B,
                              int32_t max_seq_len, int32_t m, int32_t k, void* ws, size_t ws_bytes, void* stream);
 
+/* Measurement: the split kernel of paged_hybrid_decode alone, with the same
+ * arguments (outputs omitted), launch configuration and workspace; it writes
+ * only the per-split partials in the workspace, so a workspace reserved for it
+ * is needed when paged_hybrid_decode's results must stay untouched. */
+hca_status hca_attention_split(const uint16_t* q, int32_t H, hca_paged_cache kv, const int32_t* block_table,
+                               int32_t bt_stride, hca_paged_cache win, const int32_t* win_block_table,
+                               int32_t wbt_stride, const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t m,
+                               int32_t window, const int32_t* sel_idx, const int32_t* sel_n, int32_t k,
+                               float softmax_scale, float rope_theta, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

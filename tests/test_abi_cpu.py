@@ -119,6 +119,30 @@ def test_validation_kv_compress():
     assert call(ov=4, B=0) == 0 and call(m=16, ov=16, B=0) == 0
 
 
+def test_validation_kv_prefill_pages():
+    L = hca.lib()
+    ok = dict(x=FAKE, xs=4096 * 128, z=FAKE, zs=4096, beta=FAKE, pos0=FAKE, ntok=FAKE, B=2, mx=4096, m=4, ov=0,
+              theta=1e6, gam=None, eps=1e-6, bt=FAKE, bts=16, dst=_cache())
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.kv_prefill_pages(a["x"], a["xs"], a["z"], a["zs"], a["beta"], a["pos0"], a["ntok"], a["B"], a["mx"],
+                                  a["m"], a["ov"], a["theta"], a["gam"], a["eps"], a["bt"], a["bts"], a["dst"], None)
+
+    assert call(B=0) == 0 and call(mx=0) == 0  # nothing to do, nothing launched
+    assert call(m=3) == 1 and call(m=8) == 1  # m = 8 does not match the pool's 64 entries a page
+    assert call(bts=0) == 1 and call(B=-1) == 1
+    assert call(theta=0.0) == 1 and call(gam=FAKE, eps=0.0) == 1
+    assert call(ov=5) == 1 and call(ov=4, B=0) == 0
+    assert call(x=None) == 1 and call(bt=None) == 1 and call(ntok=None) == 1
+    assert call(xs=100) == 1
+    # page formats the fused kernels write, and pages that fit one block
+    assert call(dst=_cache(dtype=2)) == 2  # fp4
+    assert call(m=1, dst=_cache(epp=256, dim=512)) == 2  # 256 rows of 512 dims
+    assert call(m=4, dst=_cache(epp=64, dim=512), B=0) == 0
+    assert call(m=128, dst=_cache(epp=2, dim=2048), B=0) == 0 and call(m=32, dst=_cache(epp=8, dim=2048)) == 2
+
+
 def test_validation_kv_compress_insert():
     L = hca.lib()
     ok = dict(x=FAKE, xs=4 * 128, z=FAKE, zs=4, beta=FAKE, pos0=FAKE, ntok=FAKE, B=2, m=4, ov=0, theta=1e6,

@@ -224,6 +224,93 @@ def test_compress_entries_overlap(m, o, d, norm):
         assert H.rel_err_rows(got[b, : ref.shape[0]], ref) <= H.ENTRY_TOL, b
 
 
+# ----------------------------------------------------------------- kv_prefill_pages
+
+
+# The fused prefill against kv_compress + kv_quantize_page on the same inputs
+# (identical bytes in every page written) and against the oracle.  Runs start
+# at a page (pos0 a multiple of 256, some > 0 with the overlap's tokens before
+# them), end mid-page or mid-group, and one is empty.  The shapes take the
+# small-group path with a row sum by xor butterfly (d = 128, 256, 512), across
+# the LDS (d = 136) and the large-group path (m = 64, 128, 256).
+@pytest.mark.parametrize("m,o,d,dtype,norm", [
+    (4, 4, 512, "fp8", True), (128, 0, 512, "fp8", True), (4, 0, 128, "bf16", False), (16, 16, 128, "fp8", False),
+    (4, 2, 136, "fp8", True), (2, 1, 256, "fp8", False), (64, 0, 136, "fp8", True), (256, 0, 128, "bf16", False),
+    (4, 4, 512, "bf16", True)])
+def test_prefill_pages_matches_two_calls_and_oracle(m, o, d, dtype, norm):
+    H.flush(f"prefill pages m={m} o={o} d={d} {dtype} norm={norm}")
+    rng = np.random.default_rng(71 + m + d)
+    epp = 256 // m
+    T = [256 * 3 + 5 * m + (m // 2 + 1 if m > 1 else 0), 256 - 1, 0, 256 * 2, 37]
+    pos0 = np.array([0, 256 * 7, 256, 256 * 4000, 0], np.int32)
+    B, Tm = len(T), max(T)
+    ntok = np.array(T, np.int32)
+    x32 = rng.standard_normal((B, o + Tm, d)).astype(np.float32) * rng.uniform(0.1, 4, (B, 1, 1)).astype(np.float32)
+    xb = gen.to_bf16_bits(x32)
+    z = rng.standard_normal((B, o + Tm)).astype(np.float32)
+    beta = (rng.standard_normal(m + o) * 0.1).astype(np.float32)
+    gam = rng.uniform(0.5, 1.5, d).astype(np.float32) if norm else None
+    nb = int((pos0.astype(np.int64) + Tm).max()) // 256 + 2
+    P = B * nb
+    table = rng.permutation(P).reshape(B, nb).astype(np.int32)
+    xd, zd = H.to_dev(xb.view(np.int16)), H.to_dev(z)
+    gd = None if gam is None else H.to_dev(gam)
+    args = dict(norm_gamma=gd, overlap=o)
+    fused = hca.PagedCache.empty(P, epp, d, dtype)
+    fused.codes.fill_(0x5A)  # slots past the valid rows must come back zeroed
+    hca.kv_prefill_pages(xd[:, o:], zd[:, o:], H.to_dev(beta), H.to_dev(pos0), H.to_dev(ntok), m, 1e6, Tm,
+                         H.to_dev(table), fused, **args)
+    n_out = -(-Tm // m)
+    ent = torch.zeros((B, n_out, d), dtype=torch.float32, device="cuda")
+    hca.kv_compress(xd[:, o:], zd[:, o:], H.to_dev(beta), H.to_dev(pos0), H.to_dev(ntok), m, 1e6, ent, Tm, **args)
+    two = hca.PagedCache.empty(P, epp, d, dtype)
+    ne = (-(-ntok // m)).astype(np.int32)
+    hca.kv_quantize_page(ent, H.to_dev((pos0 // m).astype(np.int32)), H.to_dev(ne), n_out, H.to_dev(table), two)
+    torch.cuda.synchronize()
+    got_e = ent.cpu().numpy()
+    for b in range(B):
+        lb0 = int(pos0[b]) // 256
+        for p in range(-(-int(ne[b]) // epp)):
+            phys = int(table[b, lb0 + p])
+            nv = min(epp, int(ne[b]) - p * epp)
+            assert torch.equal(fused.codes[phys, :nv], two.codes[phys, :nv]), (b, p)
+            assert not fused.codes[phys, nv:].any(), (b, p)
+            if dtype == "fp8":
+                assert torch.equal(fused.scales[phys], two.scales[phys]), (b, p)
+        if ne[b] == 0:
+            continue
+        # the oracle's entries, and the fused pages decoded against them
+        xs = codecs.bf16_decode(xb[b, o: o + T[b]])
+        if o > 0:
+            ref = compressor.compress_overlap(xs, z[b, o: o + T[b]], beta, m, o, 1e6, pos0=int(pos0[b]),
+                                              x_prev=codecs.bf16_decode(xb[b, :o]), z_prev=z[b, :o], gamma=gam)
+        else:
+            ref = compressor.compress(xs, z[b, : T[b]], beta, m, 1e6, pos0=int(pos0[b]), gamma=gam)
+        assert H.rel_err_rows(got_e[b, : ref.shape[0]], ref) <= H.ENTRY_TOL, b
+        for p in range(-(-int(ne[b]) // epp)):
+            phys = int(table[b, lb0 + p])
+            rows = ref[p * epp: (p + 1) * epp]
+            codes = fused.codes[phys, : rows.shape[0]].cpu().numpy()
+            sc = fused.scales[phys].item() if dtype == "fp8" else None
+            assert H.quantized_rows_close(dtype, codes.view(np.uint16) if dtype == "bf16" else codes, sc, rows), (b, p)
+
+
+def test_prefill_pages_rejects_unsupported_shapes():
+    kv = hca.PagedCache.empty(4, 256, 512, "fp8")  # m = 1, 512 dims: a page is more rows than a block holds
+    x = torch.zeros((1, 256, 512), dtype=torch.int16, device="cuda")
+    z = torch.zeros((1, 256), dtype=torch.float32, device="cuda")
+    one = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(hca.HcaError) as e:
+        hca.kv_prefill_pages(x, z, torch.zeros(1, device="cuda"), one, one + 256, 1, 1e6, 256,
+                             torch.zeros((1, 1), dtype=torch.int32, device="cuda"), kv)
+    assert e.value.status == 2  # HCA_ERR_UNSUPPORTED
+    fp4 = hca.PagedCache.empty(4, 64, 128, "fp4")
+    with pytest.raises(hca.HcaError) as e:
+        hca.kv_prefill_pages(x[:, :, :128].contiguous(), z, torch.zeros(4, device="cuda"), one, one + 256, 4, 1e6,
+                             256, torch.zeros((1, 1), dtype=torch.int32, device="cuda"), fp4)
+    assert e.value.status == 2
+
+
 # ----------------------------------------------------------------- kv_compress_insert
 
 
@@ -558,26 +645,43 @@ def test_indexer_topk_sets(dtype, d_idx, k, lens):
             assert (got[b, n[b]:] == -1).all()
 
 
-@pytest.mark.parametrize("dtype,d_idx,k,lens", [
-    ("fp4", 128, 2048, [70001, 8193, 9000]),
-    ("fp8", 32, 300, [1200, 1201, 1199]),  # N = 300 ~ k
+@pytest.mark.parametrize("dtype,d_idx,k,lens,back", [
+    ("fp4", 128, 2048, [70001, 8193, 9000], 0),
+    ("fp4", 128, 2048, [70001, 8193, 9000], 1),  # the staged row is not its page's last valid row
+    ("fp8", 32, 300, [1200, 1201, 1199], 0),  # N = 300 ~ k
 ])
-def test_indexer_topk_with_updates_matches_two_calls(dtype, d_idx, k, lens):
-    # a c4a layer's window insert, open-entry update and open indexer row with
-    # the indexer: the same selection (the oracle's, the open row's key left as
-    # the oracle has it), and the same bytes in every staging row and page the
-    # jobs write, as the update call then the indexer
-    H.flush(f"indexer with updates {dtype} dI={d_idx} k={k} lens={lens}")
+def test_indexer_topk_with_updates_matches_two_calls(dtype, d_idx, k, lens, back):
+    # a c4a layer's window insert, open-entry update and the re-encoding of one
+    # indexer row (entry N-1-back) with the indexer.  The row's staged key is a
+    # fresh draw, and the uploaded pool holds zeros in its place, so the update
+    # must write it and the score pass must score the new bytes: the selection
+    # is the oracle's over the new keys, the indexer pool equals the oracle's,
+    # and every staging row and page the jobs write has the same bytes as the
+    # update call followed by the indexer
+    H.flush(f"indexer with updates {dtype} dI={d_idx} k={k} lens={lens} back={back}")
     w = _idx_workload(dtype, d_idx, k, len(lens))
     sd = H.SeqData(w, 0, lens, build_pools=False)
+    L = np.array(lens, np.int64)
+    N = -(-L // 4)
+    e_open = N - 1 - back
+    fresh = np.random.default_rng(91).standard_normal((sd.B, d_idx)).astype(np.float32)
+    for b in range(sd.B):
+        sd.keys[b][e_open[b]] = fresh[b]
     sd.idx = paging.Pool(dtype, sd.num_pages, 64, d_idx)
     for b in range(sd.B):
         paging.write_run(sd.idx, sd.table[b], 0, sd.keys[b])
     assert min(sd.enforce_margin()) >= H.MARGIN
+    stale = paging.Pool(dtype, sd.num_pages, 64, d_idx)
+    stale.codes, stale.scales = sd.idx.codes.copy(), sd.idx.scales.copy()
+    for b in range(sd.B):
+        ph, sl = int(sd.table[b][e_open[b] // 64]), int(e_open[b] % 64)
+        stale.codes[ph, sl] = 0
+        if dtype == "fp4":  # per-row block scales (fp8: one scale per page, left as it is)
+            stale.scales[ph, sl] = 0
+        assert not np.array_equal(stale.codes[ph], sd.idx.codes[ph])
     Lmax = H.max_len(lens)
     B, d, theta = sd.B, 512, 1e6
     rng = np.random.default_rng(73)
-    L = np.array(lens, np.int64)
     nb = int(L.max()) // 256 + 2
     table = rng.permutation(B * nb).reshape(B, nb).astype(np.int32)
     wtable = rng.permutation(B * nb).reshape(B, nb).astype(np.int32)
@@ -598,17 +702,16 @@ def test_indexer_topk_with_updates_matches_two_calls(dtype, d_idx, k, lens):
                                             tab=table, wtab=wtable).items()}
     qi, wi = H.to_dev(sd.qi.view(np.int16)), H.to_dev(sd.wi)
     ws = hca.workspace(hca.indexer_topk_workspace(B, Lmax, 4, k))
-    # the open indexer row: the open entry N-1 of each sequence, staged in f32
-    # as the oracle's key (so re-encoding it gives the pool's bytes), with the
-    # rest of its page staged too
-    N = -(-L // 4)
-    pos_i, e0_i = (4 * (N - 1)).astype(np.int32), (64 * ((N - 1) // 64)).astype(np.int32)
+    # the re-encoded indexer row: entry e_open of each sequence, staged in f32
+    # as the oracle's (new) key, with the rest of its page staged too
+    pos_i, e0_i = (4 * e_open).astype(np.int32), (64 * (e_open // 64)).astype(np.int32)
     istage = np.zeros((B, 64, d_idx), np.float32)
     for bb in range(B):
-        istage[bb, : N[bb] - e0_i[bb]] = sd.keys[bb][e0_i[bb]: N[bb]]
+        e1 = min(N[bb], e0_i[bb] + 64)  # the page's valid rows
+        istage[bb, : e1 - e0_i[bb]] = sd.keys[bb][e0_i[bb]: e1]
     outs = []
     for fused in (True, False):
-        keys = H.upload_pool(sd.idx)
+        keys = H.upload_pool(stale)
         ist = H.to_dev(istage)
         wst, cst = (H.to_dev(a) for a in stages)
         win = hca.PagedCache.empty(B * nb, 256, d, "fp8")
@@ -634,6 +737,15 @@ def test_indexer_topk_with_updates_matches_two_calls(dtype, d_idx, k, lens):
     (of, nf, wf, cf, winf, kvf, kf), (ou, nu, wu, cu, winu, kvu, ku) = outs
     assert torch.equal(of, ou) and torch.equal(nf, nu)
     assert torch.equal(kf.codes, ku.codes) and torch.equal(kf.scales, ku.scales)  # the whole indexer pool
+    if dtype == "fp4":  # one row re-encoded: the pool is the oracle's, byte for byte
+        assert np.array_equal(kf.codes.cpu().numpy(), sd.idx.codes)
+        assert np.array_equal(kf.scales.cpu().numpy(), sd.idx.scales)
+    else:  # the open page is re-quantized whole (one scale per page): compare its valid rows
+        for b in range(B):
+            ph = int(sd.table[b][e_open[b] // 64])
+            nv = int(min(64, N[b] - 64 * (e_open[b] // 64)))
+            assert np.array_equal(kf.codes[ph, :nv].cpu().numpy(), sd.idx.codes[ph, :nv])
+            assert kf.scales[ph].item() == sd.idx.scales[ph]
     got, n = of.cpu().numpy(), nf.cpu().numpy()
     for b in range(B):
         want = sd.oracle_select(b)
