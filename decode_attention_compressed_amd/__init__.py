@@ -33,7 +33,7 @@ EXPORTS = (
     "kv_quantize_page",
     "indexer_topk_workspace",
     "indexer_topk", "indexer_topk_with_updates", "paged_hybrid_decode_workspace", "paged_hybrid_decode",
-    "kv_gather",
+    "paged_hybrid_decode_noalloc_max_bytes", "paged_hybrid_decode_noalloc", "kv_gather",
     "hca_host_e4m3_encode", "hca_host_e2m1_encode", "hca_host_bf16_encode", "hca_probe_decode", "hca_probe_mfma",
     "hca_indexer_score", "hca_attention_split",
     "hca_page_bytes", "hca_pool_plan", "hca_pool_create", "hca_pool_destroy", "hca_pool_view", "hca_pool_bucket",
@@ -100,6 +100,10 @@ def lib() -> ctypes.CDLL:
         L.paged_hybrid_decode_workspace.restype = _SZ
         L.paged_hybrid_decode.argtypes = [_P, _I32, CPagedCache, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32,
                                           _I32, _I32, _P, _P, _I32, _F32, _F32, _P, _P, _P, _P, _P, _SZ, _P]
+        L.paged_hybrid_decode_noalloc_max_bytes.argtypes = []
+        L.paged_hybrid_decode_noalloc_max_bytes.restype = _SZ
+        L.paged_hybrid_decode_noalloc.argtypes = [_P, _I32, CPagedCache, _P, _I32, CPagedCache, _P, _I32, _P, _I32,
+                                                  _I32, _I32, _I32, _P, _P, _I32, _F32, _F32, _P, _P, _P, _P, _P]
         L.kv_gather.argtypes = [CPagedCache, _P, _I32, _P, _I32, _I32, _P, _P, _P]
         L.hca_host_e4m3_encode.argtypes = [_P, _P, _I64]
         L.hca_host_e2m1_encode.argtypes = [_P, _P, _I64]
@@ -124,7 +128,8 @@ def lib() -> ctypes.CDLL:
         L.hca_pool_stats.argtypes = [_P, _I32, _P, _P, _P, _P, _P]
         for name in EXPORTS:
             if name not in ("hca_status_string", "hca_version", "indexer_topk_workspace",
-                            "paged_hybrid_decode_workspace", "kv_quantize_page_workspace", "hca_pool_destroy"):
+                            "paged_hybrid_decode_workspace", "kv_quantize_page_workspace", "hca_pool_destroy",
+                            "paged_hybrid_decode_noalloc_max_bytes"):
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -327,6 +332,26 @@ def paged_hybrid_decode(q, kv: PagedCache, block_table, win: Optional[PagedCache
                                      0 if wbt is None else wbt.stride(0), _ptr(seq_lens), B, max_seq_len, m, window,
                                      _ptr(sel_idx), _ptr(sel_n), k, softmax_scale, rope_theta, _ptr(out), _ptr(lse),
                                      _ptr(out_fp8), _ptr(out_scale), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "paged_hybrid_decode")
+
+
+def paged_hybrid_decode_noalloc_max_bytes() -> int:
+    return int(lib().paged_hybrid_decode_noalloc_max_bytes())
+
+
+def paged_hybrid_decode_noalloc(q, kv: PagedCache, block_table, win: Optional[PagedCache], win_block_table, seq_lens,
+                                max_seq_len: int, m: int, window: int, sel_idx, sel_n, softmax_scale: float,
+                                rope_theta: float, out, lse, stream=None, out_fp8=None, out_scale=None):
+    """paged_hybrid_decode with the library's static per-GPU scratch instead of a workspace
+    (allocates nothing; calls that overlap in time on one GPU race)."""
+    B, H, d = q.shape
+    k = 0 if sel_idx is None else sel_idx.shape[1]
+    wc = win.c() if (win is not None and window > 0) else _null_cache()
+    wbt = win_block_table if window > 0 else None
+    _check(lib().paged_hybrid_decode_noalloc(_ptr(q), H, kv.c(), _ptr(block_table), block_table.stride(0), wc,
+                                             _ptr(wbt), 0 if wbt is None else wbt.stride(0), _ptr(seq_lens), B,
+                                             max_seq_len, m, window, _ptr(sel_idx), _ptr(sel_n), k, softmax_scale,
+                                             rope_theta, _ptr(out), _ptr(lse), _ptr(out_fp8), _ptr(out_scale),
+                                             _stream(stream)), "paged_hybrid_decode_noalloc")
 
 
 def kv_gather(src: PagedCache, block_table, n_rows, max_rows: int, dst_codes, dst_scales, stream=None):

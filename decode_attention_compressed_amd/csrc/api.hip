@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "hca.h"
 #include "hca_common.h"
 #include "hca_internal.h"
@@ -336,6 +338,30 @@ hca_status attn_prepare(const uint16_t* q, int32_t H, hca_paged_cache kv, const 
   return HCA_OK;
 }
 
+// The allocation-free variant's scratch: one array per device, in the code
+// object, held until the process ends.  Host code never uses its name as an
+// address: the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the device address of the current device's scratch (looked up on its first use)
+hca_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return HCA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return HCA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return HCA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HCA_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -373,6 +399,28 @@ hca_status hca_attention_split(const uint16_t* q, int32_t H, hca_paged_cache kv,
   a.ws = reinterpret_cast<unsigned char*>(ws);
   a.out = nullptr;
   return from_hip(launch_attention(a, (hipStream_t)stream, true));
+}
+
+size_t paged_hybrid_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+hca_status paged_hybrid_decode_noalloc(const uint16_t* q, int32_t H, hca_paged_cache kv, const int32_t* block_table,
+                                       int32_t bt_stride, hca_paged_cache win, const int32_t* win_block_table,
+                                       int32_t wbt_stride, const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
+                                       int32_t m, int32_t window, const int32_t* sel_idx, const int32_t* sel_n,
+                                       int32_t k, float softmax_scale, float rope_theta, float* out, float* lse,
+                                       uint8_t* out_fp8, float* out_scale, void* stream) {
+  AttnArgs a{};
+  bool empty = false;
+  const hca_status st = attn_prepare(q, H, kv, block_table, bt_stride, win, win_block_table, wbt_stride, seq_lens, B,
+                                     max_seq_len, m, window, sel_idx, sel_n, k, softmax_scale, rope_theta, out, lse,
+                                     out_fp8, out_scale, a, empty);
+  if (st != HCA_OK || empty) return st;
+  if (a.plan.total > kNoAllocScratchBytes) return HCA_ERR_WORKSPACE;
+  void* p = nullptr;
+  const hca_status sp = scratch_of_current_device(&p);
+  if (sp != HCA_OK) return sp;
+  a.ws = static_cast<unsigned char*>(p);
+  return from_hip(launch_attention(a, (hipStream_t)stream));
 }
 
 hca_status kv_gather(hca_paged_cache src, const int32_t* block_table, int32_t bt_stride, const int32_t* n_rows,

@@ -402,6 +402,30 @@ hca_status paged_hybrid_decode(const uint16_t* q, int32_t H, hca_paged_cache kv,
                                size_t ws_bytes, void* stream);
 
 /*
+ * paged_hybrid_decode_noalloc -- paged_hybrid_decode without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, results and errors as paged_hybrid_decode, with the same
+ * kernels; the scratch its kernels need (per-split partial outputs) is a
+ * static array of paged_hybrid_decode_noalloc_max_bytes() bytes (32 MiB) in
+ * the library's code object, one per GPU, held until the process ends.  The
+ * call allocates nothing.  A shape whose scratch,
+ * paged_hybrid_decode_workspace(B, H, d, max_seq_len, m, window, k), exceeds
+ * that size returns HCA_ERR_WORKSPACE and launches nothing.  Every call on a
+ * GPU shares that GPU's scratch: calls that may overlap in time on one GPU
+ * (different streams, other threads) race and must be ordered by the caller.
+ * The scratch needs no initial contents.
+ */
+size_t paged_hybrid_decode_noalloc_max_bytes(void);
+hca_status paged_hybrid_decode_noalloc(const uint16_t* q, int32_t H, hca_paged_cache kv,
+                                       const int32_t* block_table, int32_t bt_stride, hca_paged_cache win,
+                                       const int32_t* win_block_table, int32_t wbt_stride,
+                                       const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t m,
+                                       int32_t window, const int32_t* sel_idx, const int32_t* sel_n,
+                                       int32_t k, float softmax_scale, float rope_theta, float* out,
+                                       float* lse, uint8_t* out_fp8, float* out_scale, void* stream);
+
+/*
  * kv_gather -- paged -> contiguous copy of rows 0 .. n_rows[b]-1 of every
  * sequence (vLLM-0.7.2 page, section 2.1: logical blocks map to physical
  * pages).  A layout check: the bytes must not depend on where pages live.
