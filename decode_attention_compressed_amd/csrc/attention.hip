@@ -105,19 +105,22 @@ __device__ __forceinline__ int plan_tiles(const AttnArgs& a, int L) {
   return (n + min(a.window, L) + kTileRows - 1) / kTileRows;
 }
 
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
+// Inclusive prefix sum over the wave, on the VALU: Hillis-Steele steps by DPP
+// row shifts inside each row of 16 lanes (lanes shifted in from outside the
+// row add 0), then the totals of the rows before, read from lanes 15, 31, 47.
+// (A lane shuffle is an LDS round trip; a dozen of them in a row would be a
+// microsecond before any work.)
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(v, o, 64);
-    v += lane >= o ? t : 0;
-  }
-  return v;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
 }
+// the wave's sum, uniform (every lane gets it)
+__device__ __forceinline__ int wave_sum_i(int v, int lane) { return __builtin_amdgcn_readlane(wave_incl_scan(v, lane), 63); }
 
 struct Work {
   int b;  // sequence (-1: past the work list)
@@ -132,7 +135,8 @@ struct Work {
 // for nothing issued after them.
 __device__ __forceinline__ int attn_lens0(const AttnArgs& a) {
   const int lane = threadIdx.x & 63;
-  return lane < a.B ? a.lens[lane] : 0;
+  const int v = a.lens[min(lane, a.B - 1)];  // unguarded (a.B >= 1): no branch around the load
+  return lane < a.B ? v : 0;
 }
 
 // Every sequence's tiles are cut into splits of T tiles, with T = ceil(total /
@@ -149,7 +153,7 @@ __device__ Work attn_work(const AttnArgs& a, int key, bool by_item, int lens0) {
   for (int c0 = 0; c0 < a.B; c0 += 64) {
     const int i = c0 + lane;
     const int L = c0 == 0 ? L0 : (i < a.B ? clampi(a.lens[i], 0, a.max_len) : 0);
-    total += wave_sum_i(i < a.B ? plan_tiles(a, L) : 0);
+    total += wave_sum_i(i < a.B ? plan_tiles(a, L) : 0, lane);
   }
   const int T = clampi((total + a.plan.spread - 1) / a.plan.spread, 1, kMaxSplitTiles);
   Work w{-1, 0, T, 0, 0};
@@ -163,14 +167,15 @@ __device__ Work attn_work(const AttnArgs& a, int key, bool by_item, int lens0) {
     const bool hit = by_item ? (i < a.B && excl <= key && key < incl) : i == key;
     const uint64_t bal = __ballot(hit);
     if (bal != 0) {
-      const int src = __builtin_ctzll(bal);
+      const int src = __builtin_ctzll(bal);  // uniform: read the hit lane's values with readlane
       w.b = c0 + src;
-      w.S = __shfl(S, src, 64);
-      w.s = by_item ? key - __shfl(excl, src, 64) : __shfl(excl, src, 64);
-      w.L = __shfl(L, src, 64);
+      w.S = __builtin_amdgcn_readlane(S, src);
+      const int ex = __builtin_amdgcn_readlane(excl, src);
+      w.s = by_item ? key - ex : ex;
+      w.L = __builtin_amdgcn_readlane(L, src);
       break;
     }
-    off = __shfl(incl, 63, 64);
+    off = __builtin_amdgcn_readlane(incl, 63);
   }
   return w;
 }
@@ -373,14 +378,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int i = row_of(j);
-      const int r = rr0 + i;
-      pre[j] = 0;
-      if (i < rps) {
-        if (a.sel != nullptr)
-          pre[j] = gload<int>(a.sel + (int64_t)bb * a.k + min(r, a.k - 1));
-        else
-          pre[j] = gload<int>(a.bt + (int64_t)bb * a.bts + min(r >> __builtin_ctz(a.kv.epp), a.bts - 1));
-      }
+      const int r = rr0 + min(i, rps - 1);  // loaded unguarded, masked after
+      const int v = a.sel != nullptr ? gload<int>(a.sel + (int64_t)bb * a.k + min(r, a.k - 1))
+                                     : gload<int>(a.bt + (int64_t)bb * a.bts + min(r >> __builtin_ctz(a.kv.epp), a.bts - 1));
+      pre[j] = i < rps ? v : 0;
     }
     const uint16_t* qrow = a.q + ((int64_t)bb * H + (hv ? head : H - 1)) * D;
 #pragma unroll
@@ -390,7 +391,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
   // issued before the lengths are known, for the work list of equal lengths
   // (max_seq_len each); another list's item gets them again
   const int su = a.plan.s_uni, tu = a.plan.t_uni;
-  if (item / su < a.B) first_loads(item / su, item % su, tu);
+  first_loads(min(item / su, a.B - 1), item % su, tu);  // a guess past the batch loads from its last sequence
   const Work wk = attn_work(a, item, true, lens0);
   if (wk.b < 0) return;  // past the work list
   if (wk.b != item / su || wk.s != item % su || wk.T != tu) first_loads(wk.b, wk.s, wk.T);
@@ -875,14 +876,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int i = row_of(j);
-      const int r = rr0 + i;
-      pre[j] = 0;
-      if (i < rps) {
-        if (a.sel != nullptr)
-          pre[j] = gload<int>(a.sel + (int64_t)bb * a.k + min(r, a.k - 1));
-        else
-          pre[j] = gload<int>(a.bt + (int64_t)bb * a.bts + min(r >> __builtin_ctz(a.kv.epp), a.bts - 1));
-      }
+      const int r = rr0 + min(i, rps - 1);  // loaded unguarded, masked after
+      const int v = a.sel != nullptr ? gload<int>(a.sel + (int64_t)bb * a.k + min(r, a.k - 1))
+                                     : gload<int>(a.bt + (int64_t)bb * a.bts + min(r >> __builtin_ctz(a.kv.epp), a.bts - 1));
+      pre[j] = i < rps ? v : 0;
     }
     const uint16_t* qrow = a.q + ((int64_t)bb * H + (hv ? head : H - 1)) * D;
 #pragma unroll
@@ -891,7 +888,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
   // issued before the lengths are known, for the work list of equal lengths
   // (max_seq_len each); another list's item gets them again
   const int su = a.plan.s_uni, tu = a.plan.t_uni;
-  if (item / su < a.B) first_loads(item / su, item % su, tu);
+  first_loads(min(item / su, a.B - 1), item % su, tu);  // a guess past the batch loads from its last sequence
   const Work wk = attn_work(a, item, true, lens0);
   if (wk.b < 0) return;  // past the work list
   if (wk.b != item / su || wk.s != item % su || wk.T != tu) first_loads(wk.b, wk.s, wk.T);
@@ -1250,7 +1247,8 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
   float2 ml0;
   f32x4 o[kCombU];
   auto first_loads = [&]() {
-    ml0 = (int)threadIdx.x < Sp ? ml[(size_t)(off + threadIdx.x) * H] : make_float2(-INFINITY, 0.0f);
+    const float2 v = ml[(size_t)item_of(threadIdx.x) * H];
+    ml0 = (int)threadIdx.x < Sp ? v : make_float2(-INFINITY, 0.0f);
 #pragma unroll
     for (int u = 0; u < kCombU; ++u) o[u] = opart[(size_t)item_of(grp + SG * u) * ostride];
   };
