@@ -91,7 +91,7 @@ AttnPlan attn_plan(int B, int H, int d, int max_seq_len, int m, int window, int 
   p.s_uni = p.s_uni > 0 ? p.s_uni : 1;
   size_t off = 0;
   p.o_off = off; off = align256a(off + (size_t)p.items * H * d * sizeof(float));
-  p.ml_off = off; off = align256a(off + (size_t)p.items * H * 2 * sizeof(float));
+  p.ml_off = off; off = align256a(off + (size_t)p.items * H * 4 * sizeof(float));
   p.total = off;
   return p;
 }
@@ -404,13 +404,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
   const int n_win = min(a.window, L);
   const int rows_b = n_sel + n_win;
   const int r1 = min(rows_b, r0 + RPS);
-  float2* ml = reinterpret_cast<float2*>(a.ws + a.plan.ml_off);
+  f32x4* ml = reinterpret_cast<f32x4*>(a.ws + a.plan.ml_off);
   float* opart = reinterpret_cast<float*>(a.ws + a.plan.o_off);
   const size_t part = (size_t)item * H;
 
   if (r0 >= r1) {  // empty split
     if (threadIdx.x < kHeadsPerBlock && h0 + (int)threadIdx.x < H)
-      ml[part + h0 + threadIdx.x] = make_float2(-INFINITY, 0.0f);
+      ml[part + h0 + threadIdx.x] = f32x4{-INFINITY, 0.0f, 0.0f, 0.0f};
     return;
   }
 
@@ -768,8 +768,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
       wt_s[w][hh] = wt;
       l += wt * ml_s[w][hh].y;
     }
+    // fp32 partials are unnormalized: their weight factor is 1
     if (h0 + hh < H)
-      ml[part + h0 + hh] = M == -INFINITY ? make_float2(-INFINITY, 0.0f) : make_float2(M * 0.6931471805599453f, l);
+      ml[part + h0 + hh] = M == -INFINITY ? f32x4{-INFINITY, 0.0f, 0.0f, 0.0f} : f32x4{M * 0.6931471805599453f, l, 1.0f, 0.0f};
   }
   __syncthreads();
   // thread -> (4 consecutive heads, one dim): consecutive threads store consecutive dims
@@ -845,6 +846,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
   __shared__ uint64_t rowptr_s[kMaxSplitRows];
   __shared__ __attribute__((aligned(16))) float ps_s[kMaxSplitRows];  // page scale; -1: skipped row
   __shared__ float2 ml_s[kPairs][kHeadsPerBlock];
+  __shared__ float sg_s[kPairs];
   __shared__ __attribute__((aligned(16))) float wt_s[kPairs][kHeadsPerBlock];
   static_assert(sizeof(q_s) == (size_t)kPairWaves * 2 * 64 * sizeof(f32x4), "partial S exchange area");
   static_assert(2 * sizeof(float) * kHeadsPerBlock * D <= kPairs * PT::BYTES, "the merge reuses the tiles");
@@ -901,13 +903,13 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
   const int n_win = min(a.window, L);
   const int rows_b = n_sel + n_win;
   const int r1 = min(rows_b, r0 + RPS);
-  float2* ml = reinterpret_cast<float2*>(a.ws + a.plan.ml_off);
-  float* opart = reinterpret_cast<float*>(a.ws + a.plan.o_off);
+  f32x4* ml = reinterpret_cast<f32x4*>(a.ws + a.plan.ml_off);
+  _Float16* opart = reinterpret_cast<_Float16*>(a.ws + a.plan.o_off);
   const size_t part = (size_t)item * H;
 
   if (r0 >= r1) {  // empty split (the whole block returns)
     if (threadIdx.x < kHeadsPerBlock && h0 + (int)threadIdx.x < H)
-      ml[part + h0 + threadIdx.x] = make_float2(-INFINITY, 0.0f);
+      ml[part + h0 + threadIdx.x] = f32x4{-INFINITY, 0.0f, 0.0f, 0.0f};
     return;
   }
 
@@ -1176,21 +1178,32 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
       *reinterpret_cast<f32x4*>(&o_s[(g * D + (D / 2) * hf + 16 * n + col) * 4]) = oacc[n] * sigma;
   }
   if (hf == 0 && g == 0) ml_s[pair][col] = make_float2(m_run, l_run);
+  if (threadIdx.x == (unsigned)(2 * pair * 64)) sg_s[pair] = sigma;
   __syncthreads();
   if (threadIdx.x < kHeadsPerBlock) {
     const int hh = threadIdx.x;
-    float M = -INFINITY;
-#pragma unroll
-    for (int p = 0; p < kPairs; ++p) M = fmaxf(M, ml_s[p][hh].x);
-    float l = 0.0f;
+    float M = -INFINITY, sg = 0.0f;
 #pragma unroll
     for (int p = 0; p < kPairs; ++p) {
-      const float wt = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml_s[p][hh].x - M);  // 0 for an idle pair
-      wt_s[p][hh] = wt;
-      l += wt * ml_s[p][hh].y;
+      M = fmaxf(M, ml_s[p][hh].x);
+      sg = fmaxf(sg, sg_s[p]);
     }
+    float l = 0.0f, wt[kPairs];
+#pragma unroll
+    for (int p = 0; p < kPairs; ++p) {
+      wt[p] = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml_s[p][hh].x - M);  // 0 for an idle pair
+      l += wt[p] * ml_s[p][hh].y;
+    }
+    // The f16 partial is O / c with c = l * sg: every row's value is a code
+    // (|code| <= 448) times its page scale, which is at most kSigmaSlack * sg
+    // (sigma grows lazily), so |O / c| <= 448 * kSigmaSlack, well inside f16,
+    // whatever the data's magnitude.
+    const float c = l * sg;
+    const float inv = c > 0.0f ? 1.0f / c : 0.0f;
+#pragma unroll
+    for (int p = 0; p < kPairs; ++p) wt_s[p][hh] = wt[p] * inv;
     if (h0 + hh < H)
-      ml[part + h0 + hh] = M == -INFINITY ? make_float2(-INFINITY, 0.0f) : make_float2(M * 0.6931471805599453f, l);
+      ml[part + h0 + hh] = M == -INFINITY ? f32x4{-INFINITY, 0.0f, 0.0f, 0.0f} : f32x4{M * 0.6931471805599453f, l, c, 0.0f};
   }
   __syncthreads();
   for (int e = threadIdx.x; e < D * (kHeadsPerBlock / 4); e += kPairThreads) {
@@ -1205,7 +1218,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int h = h0 + 4 * hq + k;
-      if (h < H) opart[(part + h) * D + dim] = acc[k];
+      if (h < H) opart[(part + h) * D + dim] = (_Float16)acc[k];
     }
   }
 }
@@ -1219,20 +1232,24 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
 constexpr int kCombThreads = 256;
 constexpr int kCombU = 16;
 
-template <int D>
+// The partials are fp32 (kHalf false: O unnormalized, weight factor c = 1) or
+// f16 (O / c, with c from the split's (m, l, c) entry); either way a thread
+// reads 16 bytes of a split's row: VEC dims.
+template <int D, bool kHalf>
 __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) {
-  constexpr int TPG = D / 4;                  // threads per split group (one float4 each)
-  constexpr int SG = kCombThreads / TPG;      // split groups: 2 (D=512) .. 16 (D=64)
+  constexpr int VEC = kHalf ? 8 : 4;          // dims per 16-byte load
+  constexpr int TPG = D / VEC;                // threads per split group
+  constexpr int SG = kCombThreads / TPG;      // split groups: 2 (D=512, fp32) .. 16 (D=64)
   constexpr int kPairs = (D / 2 + kCombThreads - 1) / kCombThreads;  // RoPE pairs per thread
   const int h = blockIdx.x, b = blockIdx.y;
   const int H = a.H;
   const int grp = threadIdx.x / TPG, li = threadIdx.x % TPG;
-  const float2* ml = reinterpret_cast<const float2*>(a.ws + a.plan.ml_off) + h;
-  const f32x4* opart = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.ws + a.plan.o_off) + (size_t)h * D) + li;
-  const size_t ostride = (size_t)H * D / 4;  // f32x4 between consecutive items
+  const f32x4* ml = reinterpret_cast<const f32x4*>(a.ws + a.plan.ml_off) + h;
+  const u32x4* opart = reinterpret_cast<const u32x4*>(a.ws + a.plan.o_off + (size_t)h * D * (kHalf ? 2 : 4)) + li;
+  const size_t ostride = (size_t)H * D / VEC;  // 16-byte units between consecutive items
   __shared__ float w_s[kMaxSplits];
   __shared__ float red_s[kCombThreads / 64];
-  __shared__ f32x4 acc_s[SG][TPG];
+  __shared__ __attribute__((aligned(16))) float acc_s[SG][D];
   // this sequence's splits are items off .. off + Sp - 1.  The first round of
   // partial loads and the first kCombThreads (m, l) pairs are issued before the
   // lengths are known, for the work list of equal lengths (max_seq_len each),
@@ -1244,11 +1261,11 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
   const int lens0 = attn_lens0(a);
   int off = b * a.plan.s_uni, Sp = a.plan.s_uni;
   auto item_of = [&](int s) { return Sp > 0 ? off + min(s, Sp - 1) : 0; };
-  float2 ml0;
-  f32x4 o[kCombU];
+  f32x4 ml0;
+  u32x4 o[kCombU];
   auto first_loads = [&]() {
-    const float2 v = ml[(size_t)item_of(threadIdx.x) * H];
-    ml0 = (int)threadIdx.x < Sp ? v : make_float2(-INFINITY, 0.0f);
+    const f32x4 v = ml[(size_t)item_of(threadIdx.x) * H];
+    ml0 = (int)threadIdx.x < Sp ? v : f32x4{-INFINITY, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int u = 0; u < kCombU; ++u) o[u] = opart[(size_t)item_of(grp + SG * u) * ostride];
   };
@@ -1274,7 +1291,8 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
     if (pi < D / 2) rope_cs((double)(L - 1), rope_inv_freq(pi, a.rope_r), c, sn);
     cs[k] = make_float2(c, sn);
   }
-  // split maxima -> M; weights w_s = exp(m_s - M) (0 for empty splits); tot = sum w_s l_s
+  // split maxima -> M; weights exp(m_s - M) (0 for empty splits); tot = sum
+  // exp(m_s - M) l_s; a partial counts with exp(m_s - M) c_s (w_s)
   float mloc = (int)threadIdx.x < S ? ml0.x : -INFINITY;
   for (int s = threadIdx.x + kCombThreads; s < S; s += kCombThreads) mloc = fmaxf(mloc, ml[(size_t)(off + s) * H].x);
   mloc = wave_max(mloc);
@@ -1298,27 +1316,39 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
   float tloc = 0.0f;
   if ((int)threadIdx.x < S) {  // the first round from the registers (a select between them and a load
     const float w = ml0.y > 0.0f ? expf(ml0.x - M) : 0.0f;  // put ml0 on the stack)
-    w_s[threadIdx.x] = w;
+    w_s[threadIdx.x] = w * ml0.z;
     tloc += w * ml0.y;
   }
   for (int s = threadIdx.x + kCombThreads; s < S; s += kCombThreads) {
-    const float2 v = ml[(size_t)(off + s) * H];
+    const f32x4 v = ml[(size_t)(off + s) * H];
     const float w = v.y > 0.0f ? expf(v.x - M) : 0.0f;
-    w_s[s] = w;
+    w_s[s] = w * v.z;
     tloc += w * v.y;
   }
   tloc = wave_sum(tloc);
   if ((threadIdx.x & 63) == 0) red_s[threadIdx.x >> 6] = tloc;
   __syncthreads();
   const float tot = (red_s[0] + red_s[1]) + (red_s[2] + red_s[3]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
   for (int s0 = grp;; s0 += SG * kCombU) {
 #pragma unroll
     for (int u = 0; u < kCombU; ++u) {
       const int s = s0 + SG * u;
       // splits at S and past it hold no partial of this sequence (whatever
       // the workspace holds there, it is not added, not even times 0)
-      if (s < S) acc += w_s[s] * o[u];
+      if (s < S) {
+        const float w = w_s[s];
+        if constexpr (kHalf) {
+          const f16x8 x = __builtin_bit_cast(f16x8, o[u]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += w * (float)x[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] += w * u2f(o[u][i]);
+        }
+      }
     }
     if (s0 + SG * kCombU >= S) break;
 #pragma unroll
@@ -1327,7 +1357,9 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
       o[u] = opart[(size_t)item_of(s) * ostride];
     }
   }
-  acc_s[grp][li] = acc;
+#pragma unroll
+  for (int i = 0; i < VEC; i += 4)
+    *reinterpret_cast<f32x4*>(&acc_s[grp][VEC * li + i]) = f32x4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
   __syncthreads();
   const float inv_tot = 1.0f / tot;
   float2 ov[kPairs];
@@ -1340,7 +1372,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
     float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
     for (int gq = 0; gq < SG; ++gq) {
-      const float* ag = reinterpret_cast<const float*>(acc_s[gq]);
+      const float* ag = acc_s[gq];
       o0 += ag[2 * pi];
       o1 += ag[2 * pi + 1];
     }
@@ -1388,7 +1420,11 @@ template <int D>
 static hipError_t launch_attn_d(const AttnArgs& a, hipStream_t s) {
   const hipError_t e = a.kv.dtype == HCA_FP8_E4M3 ? launch_split<D, HCA_FP8_E4M3>(a, s) : launch_split<D, HCA_BF16>(a, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<D>, dim3(a.H, a.B), dim3(256), 0, s, a);
+  // the split kernel for 512-dim fp8 rows writes f16 partials
+  if (D == kPairD && a.kv.dtype == HCA_FP8_E4M3)
+    hipLaunchKernelGGL((attn_combine_kernel<D, true>), dim3(a.H, a.B), dim3(kCombThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<D, false>), dim3(a.H, a.B), dim3(kCombThreads), 0, s, a);
   return hipGetLastError();
 }
 
