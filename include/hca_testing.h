@@ -40,7 +40,9 @@ hca_status hca_probe_mfma(const uint16_t* A, const uint16_t* B, float* D, int32_
 /* Measurement: the scoring kernel of indexer_topk alone, same arguments and
  * launch configuration, no selection.  It accumulates into the workspace's
  * score histogram, so use a workspace reserved for it (never one that
- * indexer_topk will use afterwards).  Scores land in the workspace. */
+ * indexer_topk will use afterwards).  The fp32 scores land at the start of the
+ * workspace: sequence b's row of 2048 * ceil(ceil(max_seq_len / m) / 2048)
+ * floats, entry j at j (entries at or past ceil(seq_lens[b] / m) unwritten). */
 hca_status hca_indexer_score(const uint16_t* q_idx, const float* head_w, int32_t HI, hca_paged_cache idx_keys,
                              const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens, int32_t B,
                              int32_t max_seq_len, int32_t m, int32_t k, void* ws, size_t ws_bytes, void* stream);

@@ -150,3 +150,49 @@ def test_decode_loop_matches_one_shot(m, o):
             pw = int(wtable[b, lb])
             if lb >= (Lb - 1) // BLOCK - 1:  # the window blocks the loop kept whole
                 assert H.quantized_rows_close("fp8", wh.codes[pw, : t1 - t0], wh.scales[pw], wrows), (b, lb)
+    if m > 16:
+        return  # c128a: a running fold state; its pages are checked against the oracle above
+    # c4a has no fold state: each entry is refolded from its tokens, so every
+    # page the loop wrote must hold the same bytes as the GPU's one-shot prefill
+    # of the final context, both the two-launch form (kv_compress +
+    # kv_quantize_page) and the fused kv_prefill_pages; the window pages as the
+    # one-shot fold of their tokens (m = 1) quantized whole
+    kv1 = hca.PagedCache.empty(B * nb, epp, d, "fp8")
+    kv2 = hca.PagedCache.empty(B * nb, epp, d, "fp8")
+    win1 = hca.PagedCache.empty(B * nb, BLOCK, d, "fp8")
+    for b in range(B):
+        Lb = int(L[b])
+        N = -(-Lb // m)
+        ent = torch.zeros((1, N, d), dtype=torch.float32, device="cuda")
+        xb, zb = dev(xs[b:b + 1, :Lb].view(np.int16)), dev(zs[b:b + 1, :Lb])
+        z1, n1 = dev(np.zeros(1, np.int32)), dev(np.array([Lb], np.int32))
+        hca.kv_compress(xb, zb, beta_d, z1, n1, m, 1e6, ent, Lb, norm_gamma=gam_d, overlap=o)
+        hca.kv_quantize_page(ent, z1, dev(np.array([N], np.int32)), N, dev(table[b:b + 1]), kv1)
+        hca.kv_prefill_pages(xb, zb, beta_d, z1, n1, m, 1e6, Lb, dev(table[b:b + 1]), kv2, norm_gamma=gam_d, overlap=o)
+        for lb in range((int(L0[b]) - 1) // BLOCK, -(-Lb // BLOCK)):
+            t0, t1 = lb * BLOCK, min(Lb, (lb + 1) * BLOCK)
+            wr = torch.zeros((1, t1 - t0, d), dtype=torch.float32, device="cuda")
+            p0w, nw = dev(np.array([t0], np.int32)), dev(np.array([t1 - t0], np.int32))
+            hca.kv_compress(dev(xs[b:b + 1, t0:t1].view(np.int16)), dev(zs[b:b + 1, t0:t1]), dev(np.zeros(1, np.float32)),
+                            p0w, nw, 1, 1e6, wr, t1 - t0)
+            hca.kv_quantize_page(wr, p0w, nw, t1 - t0, dev(wtable[b:b + 1]), win1)
+    torch.cuda.synchronize()
+    k1 = H.download_pool(kv1, paging.Pool("fp8", B * nb, epp, d))
+    k2 = H.download_pool(kv2, paging.Pool("fp8", B * nb, epp, d))
+    w1 = H.download_pool(win1, paging.Pool("fp8", B * nb, BLOCK, d))
+    for b in range(B):
+        Lb = int(L[b])
+        N = -(-Lb // m)
+        for lb in range(int(L0[b]) // BLOCK, -(-Lb // BLOCK)):
+            r0, r1 = lb * epp, min(N, (lb + 1) * epp)
+            if r1 <= r0:
+                continue
+            ph = int(table[b, lb])
+            for ref, what in ((k1, "kv_compress + kv_quantize_page"), (k2, "kv_prefill_pages")):
+                assert np.array_equal(kvh.codes[ph, : r1 - r0], ref.codes[ph, : r1 - r0]), (b, lb, what)
+                assert kvh.scales[ph] == ref.scales[ph], (b, lb, what)
+        for lb in range((int(L0[b]) - 1) // BLOCK, -(-Lb // BLOCK)):
+            t0, t1 = lb * BLOCK, min(Lb, (lb + 1) * BLOCK)
+            pw = int(wtable[b, lb])
+            assert np.array_equal(wh.codes[pw, : t1 - t0], w1.codes[pw, : t1 - t0]), (b, lb, "window")
+            assert wh.scales[pw] == w1.scales[pw], (b, lb, "window")

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import synth
-from oracle import codecs, compressor, paging
+from oracle import codecs, compressor, indexer, paging
 from synth import gen
 from tests import helpers as H
 
@@ -643,6 +643,52 @@ def test_indexer_topk_sets(dtype, d_idx, k, lens):
             assert n[b] == len(want), (rep, b)
             assert np.array_equal(got[b, : n[b]], want), (rep, b)
             assert (got[b, n[b]:] == -1).all()
+
+
+# Every score of the scoring pass against the oracle's, element by element.
+# The GPU forms q_h . k_j with bf16 MFMA over exactly decoded keys (products
+# exact in fp32, sums rounded in fp32, the fp4 block scale or fp8 page scale
+# applied in fp32), then sum_h w_h max(0, .) in fp32: a forward error of at
+# most about (d_I + H_I + 2) u times the absolute score
+# A_j = sum_h |w_h| sum_i |q_hi k_ji| (u = 2^-24, ReLU is 1-Lipschitz).  The
+# test allows 4 (d_I + H_I) u A_j: a scale error, a dropped block scale, a
+# wrong head weight or a transposed key fails it.
+@pytest.mark.parametrize("dtype,d_idx,lens", [
+    ("fp4", 128, [70001, 8193, 257]),   # the V4 layers' indexer: pages of 64 entries
+    ("fp8", 128, [40000, 4097, 1025]),
+    ("fp4", 64, [30000, 257, 64]),      # two scale blocks per key
+    ("fp4", 256, [20000, 4096, 100]),   # eight scale blocks per key
+    ("bf16", 64, [4096, 1023, 2000]),
+])
+def test_indexer_scores_elementwise(dtype, d_idx, lens):
+    H.flush(f"indexer scores {dtype} dI={d_idx} lens={lens}")
+    k = 256
+    w = _idx_workload(dtype, d_idx, k, len(lens))
+    sd = H.SeqData(w, 0, lens, build_pools=False)
+    sd.idx = paging.Pool(dtype, sd.num_pages, 64, d_idx)
+    for b in range(sd.B):
+        paging.write_run(sd.idx, sd.table[b], 0, sd.keys[b])
+    Lmax = H.max_len(lens)
+    ws = hca.workspace(hca.indexer_topk_workspace(sd.B, Lmax, 4, k))
+    hca.indexer_score(H.to_dev(sd.qi.view(np.int16)), H.to_dev(sd.wi), H.upload_pool(sd.idx), H.to_dev(sd.table),
+                      H.to_dev(sd.lens), Lmax, 4, k, ws)
+    torch.cuda.synchronize()
+    # the scores lie at the workspace's start: a row of 2048 * ceil(n_max / 2048) per sequence
+    n_max = -(-Lmax // 4)
+    n_pad = -(-n_max // 2048) * 2048
+    got = ws[: sd.B * n_pad * 4].view(torch.float32).reshape(sd.B, n_pad).cpu().numpy()
+    u = 2.0 ** -24
+    for b in range(sd.B):
+        N = int(compressor.n_entries(int(sd.lens[b]), 4))
+        keys = paging.decode_rows(sd.idx, sd.table[b], np.arange(N))
+        q = codecs.bf16_decode(sd.qi[b]).astype(np.float64)
+        wgt = sd.wi[b].astype(np.float64)
+        want = indexer.scores(q, wgt, keys)
+        absolute = np.abs(keys) @ np.abs(q).T @ np.abs(wgt)
+        tol = 4 * (d_idx + len(wgt)) * u * absolute
+        err = np.abs(got[b, :N].astype(np.float64) - want)
+        assert (err <= tol).all(), (b, int(np.argmax(err - tol)), float(err.max()))
+        assert np.isfinite(want).all() and (np.abs(want) > 0).mean() > 0.5  # ReLU keeps a score for most entries
 
 
 @pytest.mark.parametrize("dtype,d_idx,k,lens,back", [

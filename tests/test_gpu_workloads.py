@@ -222,22 +222,31 @@ def _enforce_margin(hca, lay, b, keys_b, idx_ref, max_rounds=20):
 
 
 CASES = [
-    # (workload id, layer index, sampled sequences)
-    pytest.param(4, 0, (0, 3), id="stack1m-c4a-fp4"),
-    pytest.param(4, 30, (1, 2), id="stack1m-c128a"),  # the stack lists its 30 c4a layers first
-    pytest.param(2, 0, (0, 9, 15), id="c4a-128k-b16-fp8"),
-    pytest.param(1, 0, (0, 7), id="c128a-64k-b8"),
+    # (workload id, layer index, sampled sequences, compressor overlap: None as the workload)
+    pytest.param(4, 0, (0, 3), None, id="stack1m-c4a-fp4"),
+    pytest.param(4, 30, (1, 2), None, id="stack1m-c128a"),  # the stack lists its 30 c4a layers first
+    pytest.param(2, 0, (0, 9, 15), None, id="c4a-128k-b16-fp8"),
+    pytest.param(1, 0, (0, 7), None, id="c128a-64k-b8"),
+    # the plain c4a compressor: a softmax over the 4 slots of non-overlapping
+    # groups, on the 1M-token stack's c4a layer shape
+    pytest.param(4, 0, (1, 2), 0, id="stack1m-c4a-fp4-no-overlap"),
 ]
 
 
-@pytest.mark.parametrize("cid,li,bs", CASES)
-def test_full_workload_sampled(cid, li, bs):
+@pytest.mark.parametrize("cid,li,bs,overlap", CASES)
+def test_full_workload_sampled(cid, li, bs, overlap):
+    import dataclasses
+
     import decode_attention_compressed_amd as hca
 
     w = synth.workload(cid)
+    if overlap is not None:
+        layers = list(w.layers)
+        layers[li] = dataclasses.replace(layers[li], overlap=overlap)
+        w = dataclasses.replace(w, layers=layers)
     kind = w.layers[li]
     assert kind.name == ("c128a" if "c128a" in w.name or li >= 30 else "c4a")
-    H.flush(f"full workload {w.name} layer {li} ({kind.name}) B={w.B} L={w.L} sampled {bs}")
+    H.flush(f"full workload {w.name} layer {li} ({kind.name}, overlap {kind.overlap}) B={w.B} L={w.L} sampled {bs}")
     rng = np.random.default_rng(1000 + 10 * cid + li)
     lay = FullLayer(hca, w, li)
     B, L, d, W, Hq = w.B, w.L, w.d, w.window, w.H
