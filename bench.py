@@ -648,6 +648,17 @@ def cpu_baseline(w, budget_s=20.0):
     }
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
 # ----------------------------------------------------------------- page-pool packing
 
 
@@ -856,6 +867,16 @@ def main():
     if not args.no_cpu_baseline and r["n_layers"] == len(w.layers) and args.layer_sample <= 0:
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(w)
+        cpu["cpu_model"] = cpu_model()
+        # the two small workloads once more with one BLAS / NumPy thread
+        from threadpoolctl import threadpool_limits
+
+        one = {}
+        with threadpool_limits(limits=1):
+            for cid in (0, 1):
+                w1 = synth.workload(cid)
+                one[w1.name] = cpu_baseline(w1, budget_s=8.0)
+        cpu["one_thread"] = one
     value = w.B / (r["t_step"] * 1e-3)
     lens = r["lens"]
     res = {

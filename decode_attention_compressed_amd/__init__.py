@@ -19,7 +19,7 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhca.so")
+LIB_PATH = os.environ.get("HCA_LIB") or os.path.join(_PKG, "libhca.so")  # HCA_LIB: another build of the library
 
 BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2
 DTYPES = {"bf16": BF16, "fp8": FP8_E4M3, "fp4": FP4_E2M1}
