@@ -51,20 +51,24 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 # taken on, identified by the SHA-256 of the source files; otherwise traffic
 # is null.
 TRAFFIC = {
-    # (layer kind, kernel): sources, their SHA-256, bytes read and written per launch
+    # (layer kind, kernel): sources, their SHA-256, bytes read and written per launch (rocprofv3 FETCH_SIZE and
+    # WRITE_SIZE per dispatch, scaled by what the same counters read for the bench's 1 GiB device copy)
     ("c4a", "score"): {"sources": ("decode_attention_compressed_amd/csrc/indexer.hip",
                                    "decode_attention_compressed_amd/csrc/hca_common.h",
                                    "decode_attention_compressed_amd/csrc/indexer_internal.h",
                                    "decode_attention_compressed_amd/csrc/indexer_score.h"),
-                       "source_sha256": None, "fetch_bytes": None, "write_bytes": None},
+                       "source_sha256": "c5a762b6187a503b6c253c58647420931b07c8722b81cf769a18f0c2e53079dc",
+                       "fetch_bytes": 72078100, "write_bytes": 4662067},
     ("c128a", "attn_split"): {"sources": ("decode_attention_compressed_amd/csrc/attention.hip",
                                           "decode_attention_compressed_amd/csrc/hca_common.h",
                                           "decode_attention_compressed_amd/csrc/hca_internal.h"),
-                              "source_sha256": None, "fetch_bytes": None, "write_bytes": None},
+                              "source_sha256": "cca231f9c11bfbac647caeec8b73b22fa9fc5d9d8572e432718e15727292071d",
+                              "fetch_bytes": 19994104, "write_bytes": 4259840},
     ("c4a", "attn_split"): {"sources": ("decode_attention_compressed_amd/csrc/attention.hip",
                                         "decode_attention_compressed_amd/csrc/hca_common.h",
                                         "decode_attention_compressed_amd/csrc/hca_internal.h"),
-                            "source_sha256": None, "fetch_bytes": None, "write_bytes": None},
+                            "source_sha256": "cca231f9c11bfbac647caeec8b73b22fa9fc5d9d8572e432718e15727292071d",
+                            "fetch_bytes": 7349671, "write_bytes": 3727360},
 }
 
 
