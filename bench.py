@@ -51,20 +51,20 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 # taken on, identified by the SHA-256 of the source files; otherwise traffic
 # is null.
 TRAFFIC = {
-    # (layer kind, kernel): sources, their SHA-256, bytes read and written per launch (rocprofv3 FETCH_SIZE and
+    # (workload, layer kind, kernel): sources, their SHA-256, bytes read and written per launch (rocprofv3 FETCH_SIZE and
     # WRITE_SIZE per dispatch, scaled by what the same counters read for the bench's 1 GiB device copy)
-    ("c4a", "score"): {"sources": ("decode_attention_compressed_amd/csrc/indexer.hip",
+    ("stack-1m-b4-61layers", "c4a", "score"): {"sources": ("decode_attention_compressed_amd/csrc/indexer.hip",
                                    "decode_attention_compressed_amd/csrc/hca_common.h",
                                    "decode_attention_compressed_amd/csrc/indexer_internal.h",
                                    "decode_attention_compressed_amd/csrc/indexer_score.h"),
                        "source_sha256": "c5a762b6187a503b6c253c58647420931b07c8722b81cf769a18f0c2e53079dc",
                        "fetch_bytes": 72078100, "write_bytes": 4662067},
-    ("c128a", "attn_split"): {"sources": ("decode_attention_compressed_amd/csrc/attention.hip",
+    ("stack-1m-b4-61layers", "c128a", "attn_split"): {"sources": ("decode_attention_compressed_amd/csrc/attention.hip",
                                           "decode_attention_compressed_amd/csrc/hca_common.h",
                                           "decode_attention_compressed_amd/csrc/hca_internal.h"),
                               "source_sha256": "cca231f9c11bfbac647caeec8b73b22fa9fc5d9d8572e432718e15727292071d",
                               "fetch_bytes": 19994104, "write_bytes": 4259840},
-    ("c4a", "attn_split"): {"sources": ("decode_attention_compressed_amd/csrc/attention.hip",
+    ("stack-1m-b4-61layers", "c4a", "attn_split"): {"sources": ("decode_attention_compressed_amd/csrc/attention.hip",
                                         "decode_attention_compressed_amd/csrc/hca_common.h",
                                         "decode_attention_compressed_amd/csrc/hca_internal.h"),
                             "source_sha256": "cca231f9c11bfbac647caeec8b73b22fa9fc5d9d8572e432718e15727292071d",
@@ -82,8 +82,10 @@ def source_sha256(files):
     return h.hexdigest()
 
 
-def traffic_of(kind_name, kname):
-    t = TRAFFIC.get((kind_name, kname))
+def traffic_of(workload, kind_name, kname):
+    """Counted HBM bytes per launch of a kernel, for the workload and layer kind the counters were taken on
+    (None for any other shape, or once the kernel's sources have changed)."""
+    t = TRAFFIC.get((workload, kind_name, kname))
     if t is None or t["source_sha256"] is None or source_sha256(t["sources"]) != t["source_sha256"]:
         return None
     return int(t["fetch_bytes"] + t["write_bytes"])
@@ -834,7 +836,7 @@ def roofline_of(r, copy_gbs):
     kind_name, kname = dk.split(":")
     achieved = v["GBps"]
     return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_of(kind_name, kname),
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_of(r["w"].name, kind_name, kname),
             "frac_of_measured_copy": round(achieved / copy_gbs, 4), "measured_copy_GBps": round(copy_gbs, 1),
             "kernel": f"{KERNEL_NAMES[kname]}, {kind_name} layers", "bytes_per_launch": v["bytes_per_launch"],
             "avg_launch_ms": round(v["avg_us"] * 1e-3, 5), "median_of_rounds_ms": round(v["median_of_rounds_us"] * 1e-3, 5),
