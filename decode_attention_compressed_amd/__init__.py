@@ -34,7 +34,7 @@ EXPORTS = (
     "indexer_topk_workspace",
     "indexer_topk", "indexer_topk_with_updates", "paged_hybrid_decode_workspace", "paged_hybrid_decode",
     "paged_hybrid_decode_noalloc_max_bytes", "paged_hybrid_decode_noalloc", "kv_gather",
-    "hca_host_e4m3_encode", "hca_host_e2m1_encode", "hca_host_bf16_encode", "hca_probe_decode", "hca_probe_mfma",
+    "hca_host_e4m3_encode", "hca_host_e2m1_encode", "hca_host_bf16_encode", "hca_probe_decode", "hca_probe_e4m3_sweep", "hca_probe_mfma",
     "hca_indexer_score", "hca_attention_split",
     "hca_page_bytes", "hca_pool_plan", "hca_pool_create", "hca_pool_destroy", "hca_pool_view", "hca_pool_bucket",
     "hca_pool_alloc", "hca_pool_share", "hca_pool_release", "hca_pool_publish", "hca_pool_lookup", "hca_pool_stats",
@@ -109,6 +109,7 @@ def lib() -> ctypes.CDLL:
         L.hca_host_e2m1_encode.argtypes = [_P, _P, _I64]
         L.hca_host_bf16_encode.argtypes = [_P, _P, _I64]
         L.hca_probe_decode.argtypes = [_P, _P, _I32, _I32, _P]
+        L.hca_probe_e4m3_sweep.argtypes = [ctypes.c_uint32, ctypes.c_uint32, _P, _P]
         L.hca_probe_mfma.argtypes = [_P, _P, _P, _I32, _P]
         L.hca_indexer_score.argtypes = [_P, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P]
         L.hca_attention_split.argtypes = [_P, _I32, CPagedCache, _P, _I32, CPagedCache, _P, _I32, _P, _I32, _I32, _I32,

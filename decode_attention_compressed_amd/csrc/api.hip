@@ -502,9 +502,38 @@ __global__ void probe_mfma_kernel(const uint16_t* A, const uint16_t* B, float* D
   for (int i = 0; i < 4; ++i) D[(4 * (l / 16) + i) * 16 + (l % 16)] = acc[i];
 }
 
+// Every binary32 pattern lo .. lo + n - 1 except NaNs through both E4M3
+// encoders; res[0] counts the patterns where they differ, res[1] keeps the
+// largest such pattern (0 if none).
+__global__ void probe_e4m3_sweep_kernel(uint32_t lo, uint32_t n, uint32_t* res) {
+  uint32_t bad = 0, last = 0;
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint32_t bits = lo + i;
+    const float x = u2f(bits);
+    if (x != x) continue;
+    const uint32_t hw = e4m3_encode2_hw<false>(x, 0.0f, 0u) & 0xFFu;
+    if (hw != e4m3_encode(x)) {
+      ++bad;
+      last = bits > last ? bits : last;
+    }
+  }
+  if (bad) {
+    atomicAdd(&res[0], bad);
+    atomicMax(&res[1], last);
+  }
+}
+
 }  // namespace hca
 
 extern "C" {
+
+hca_status hca_probe_e4m3_sweep(uint32_t lo, uint32_t n, uint32_t* res, void* stream) {
+  if (!res) return HCA_ERR_INVALID;
+  if (n == 0) return HCA_OK;
+  hipLaunchKernelGGL(probe_e4m3_sweep_kernel, dim3(4096), dim3(256), 0, (hipStream_t)stream, lo, n, res);
+  return from_hip(hipGetLastError());
+}
 
 hca_status hca_probe_decode(const uint8_t* codes, float* out, int32_t n, int32_t kind, void* stream) {
   if (!codes || !out || n < 0 || (n % 8) != 0 || (kind != 0 && kind != 1)) return HCA_ERR_INVALID;

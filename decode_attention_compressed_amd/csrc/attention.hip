@@ -1399,7 +1399,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a) 
     for (int k = 0; k < kPairs; ++k) {
       const int pi = threadIdx.x + kCombThreads * k;
       if (pi >= D / 2) break;
-      o8[pi] = (uint16_t)(e4m3_encode(ov[k].x / sc) | (e4m3_encode(ov[k].y / sc) << 8));
+      o8[pi] = (uint16_t)e4m3_encode2_hw<false>(ov[k].x / sc, ov[k].y / sc, 0u);
     }
     if (threadIdx.x == 0) a.out8_scale[row] = sc;
   }

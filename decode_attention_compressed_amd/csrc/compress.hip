@@ -427,14 +427,11 @@ hipError_t launch_compress(CompressArgs a, hipStream_t s) {
 // most kPrefillRounds rounds).  Large groups: a block of kCompressThreads
 // threads folds the page's entries one after the other (compress_block's
 // large path, so the same sums) into shared memory.
-constexpr int kPrefillThreads = 512;
-constexpr int kPrefillRounds = 8;
+constexpr int kPrefillThreads = 1024;
+constexpr int kPrefillRounds = 4;
 
 // four fp8 codes of x / s (an fp8 page's encoding), packed little-endian
-__device__ __forceinline__ uint32_t enc4_e4m3(const f32x4 v, float s) {
-  return (uint32_t)e4m3_encode(v[0] / s) | ((uint32_t)e4m3_encode(v[1] / s) << 8) |
-         ((uint32_t)e4m3_encode(v[2] / s) << 16) | ((uint32_t)e4m3_encode(v[3] / s) << 24);
-}
+__device__ __forceinline__ uint32_t enc4_e4m3(const f32x4 v, float s) { return e4m3_encode4_div(v[0], v[1], v[2], v[3], s); }
 
 __device__ __forceinline__ void rope8(const float acc[8], double pos, const double inv[4], float o[8]) {
 #pragma unroll
@@ -494,13 +491,18 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_small_kernel(PrefillA
   for (int q = 0; q < 4; ++q) inv[q] = rope_inv_freq(li * 4 + q, a.rope_r);
   __shared__ float sq_s[kPrefillThreads];
   __shared__ float red_s[kPrefillThreads / 64];
-  float v[kPrefillRounds][8];
+  // the page's rotated rows stay in registers until the page scale is known:
+  // one named vector per round (an array indexed by the round counter would be
+  // placed in scratch memory, whose traffic exceeded the pages' own: the round
+  // loop is too large to unroll)
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  f32x8 v0 = {}, v1 = {}, v2 = {}, v3 = {};
+  static_assert(kPrefillRounds == 4, "one vector per round");
+#define HCA_ROW_OF_ROUND(r) ((r) == 0 ? v0 : (r) == 1 ? v1 : (r) == 2 ? v2 : v3)
   float amax = 0.0f;
-#pragma unroll
+#pragma nounroll
   for (int r = 0; r < kPrefillRounds; ++r) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) v[r][c] = 0.0f;
-    if (r * RP >= epp) continue;  // uniform
+    if (r * RP >= epp) break;  // uniform
     const int row = r * RP + gi;
     const int j = pg * epp + row;
     const bool live = active && row < rows;
@@ -515,9 +517,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_small_kernel(PrefillA
       for (int c = 0; c < 8; ++c) acc[c] = acc[c] * rs * gam[c];
     }
     if (live) {
-      rope8(acc, (double)p0 + (double)(j * m), inv, v[r]);
+      float o[8];
+      rope8(acc, (double)p0 + (double)(j * m), inv, o);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(v[r][c]));
+      for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(o[c]));
+      const f32x8 ov = {o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
+      switch (r) {  // uniform
+        case 0: v0 = ov; break;
+        case 1: v1 = ov; break;
+        case 2: v2 = ov; break;
+        default: v3 = ov; break;
+      }
     }
   }
   // the page: codes of the valid rows, zeros past them, and the scale
@@ -531,8 +541,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_small_kernel(PrefillA
       if (r * RP >= epp || !active || row >= epp) continue;
       u32x2 w = {0u, 0u};
       if (row < rows) {
-        w[0] = enc4_e4m3(f32x4{v[r][0], v[r][1], v[r][2], v[r][3]}, s);
-        w[1] = enc4_e4m3(f32x4{v[r][4], v[r][5], v[r][6], v[r][7]}, s);
+        const f32x8 vr = HCA_ROW_OF_ROUND(r);
+        w[0] = enc4_e4m3(f32x4{vr[0], vr[1], vr[2], vr[3]}, s);
+        w[1] = enc4_e4m3(f32x4{vr[4], vr[5], vr[6], vr[7]}, s);
       }
       *reinterpret_cast<u32x2*>(codes + (int64_t)row * d + li * 8) = w;
     }
@@ -545,14 +556,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_small_kernel(PrefillA
       if (r * RP >= epp || !active || row >= epp) continue;
       u32x4 w = {0u, 0u, 0u, 0u};
       if (row < rows) {
+        const f32x8 vr = HCA_ROW_OF_ROUND(r);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          w[q] = (uint32_t)bf16_encode(v[r][2 * q]) | ((uint32_t)bf16_encode(v[r][2 * q + 1]) << 16);
+          w[q] = (uint32_t)bf16_encode(vr[2 * q]) | ((uint32_t)bf16_encode(vr[2 * q + 1]) << 16);
       }
       *reinterpret_cast<u32x4*>(codes + (int64_t)row * d + li * 8) = w;
     }
   }
 }
+
+#undef HCA_ROW_OF_ROUND
 
 __global__ __launch_bounds__(kCompressThreads) void prefill_large_kernel(PrefillArgs p) {
   const CompressArgs& a = p.c;

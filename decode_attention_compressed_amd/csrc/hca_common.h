@@ -5,7 +5,9 @@
 // 2.1 and 2.2, and the vLLM-0.7.2 page, section 2.2 "fp8_e4m3").  The encoders
 // are written with exact float steps (power-of-two scaling and rintf, which
 // rounds half to even) so that the same source gives the same codes on the
-// host and on the GPU; they are exported to the host for checking.
+// host and on the GPU; they are exported to the host for checking.  The
+// kernels encode E4M3 with the hardware conversion instead, which gives the
+// same codes for every finite binary32 input (an exhaustive GPU probe).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -43,6 +45,21 @@ HCA_HD uint8_t e4m3_encode(float y) {
     code = ((uint32_t)(E + 7) << 3) | (r - 8u);
   }
   return (uint8_t)(code | sign);
+}
+// Two codes by the hardware conversion (v_cvt_pk_fp8_f32: OCP E4M3, round half
+// to even), after a saturating clamp to [-448, 448], placed in the low (kHi =
+// false) or high half of `old`.  Every finite input gives e4m3_encode's codes
+// (checked over all binary32 values by hca_probe_e4m3_sweep).
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3_encode2_hw(float a, float b, uint32_t old) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, kHi);
+}
+// four codes of v / s (an fp8 page's encoding: exact fp32 divisions), packed
+// little-endian
+__device__ __forceinline__ uint32_t e4m3_encode4_div(float v0, float v1, float v2, float v3, float s) {
+  return e4m3_encode2_hw<true>(v2 / s, v3 / s, e4m3_encode2_hw<false>(v0 / s, v1 / s, 0u));
 }
 HCA_HD float e4m3_decode(uint32_t c) {
   const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;

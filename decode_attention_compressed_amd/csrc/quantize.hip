@@ -30,10 +30,7 @@ __device__ __forceinline__ bool page_ok(int phys, int num_pages) { return phys >
 constexpr int kF8Threads = 1024;
 constexpr int kF8Regs = 16;
 
-__device__ __forceinline__ uint32_t encode4_fp8(const f32x4 v, float s) {
-  return (uint32_t)e4m3_encode(v[0] / s) | ((uint32_t)e4m3_encode(v[1] / s) << 8) |
-         ((uint32_t)e4m3_encode(v[2] / s) << 16) | ((uint32_t)e4m3_encode(v[3] / s) << 24);
-}
+__device__ __forceinline__ uint32_t encode4_fp8(const f32x4 v, float s) { return e4m3_encode4_div(v[0], v[1], v[2], v[3], s); }
 
 __device__ __forceinline__ float block_max_1024(float v, float* red) {
   v = wave_max(v);

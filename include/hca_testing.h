@@ -30,6 +30,13 @@ hca_status hca_host_bf16_encode(const float* in, uint16_t* out, int64_t n);
  * codes, out: device; n a multiple of 8. */
 hca_status hca_probe_decode(const uint8_t* codes, float* out, int32_t n, int32_t kind, void* stream);
 
+/* GPU: every binary32 bit pattern lo .. lo + n - 1 (n < 2^32; NaNs skipped)
+ * through the kernels' two E4M3 encoders, the exact-step one (as
+ * hca_host_e4m3_encode) and the hardware conversion after a saturating clamp;
+ * res (device, two words, zeroed by the caller) accumulates the number of
+ * patterns where they differ and the largest such pattern. */
+hca_status hca_probe_e4m3_sweep(uint32_t lo, uint32_t n, uint32_t* res, void* stream);
+
 /* GPU: one wave computes D[16][16] = A[16][32] . B[32][16] with one
  * v_mfma_f32_16x16x32 (kind 0: f16 operands, kind 1: bf16 operands), loading
  * lane l's operands as A[l%16][8(l/16) .. +8] and B[8(l/16) .. +8][l%16] and

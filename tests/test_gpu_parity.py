@@ -68,6 +68,20 @@ def test_probe_hw_decoders_are_exact():
     assert np.array_equal(got4, want)
 
 
+def test_probe_hw_e4m3_encoder_equals_exact_encoder_everywhere():
+    # every binary32 value (NaNs aside) through the hardware E4M3 conversion
+    # after its saturating clamp and through the exact-step encoder, which the
+    # host tests pin against the oracle over the same sweep: the kernels use
+    # the hardware one
+    H.flush("probe e4m3 encoders, all binary32 values")
+    res = torch.zeros(2, dtype=torch.int32, device="cuda")
+    for part in range(4):
+        assert hca.lib().hca_probe_e4m3_sweep(part << 30, 1 << 30, res.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    bad, last = (int(v) & 0xFFFFFFFF for v in res.cpu().numpy())
+    assert bad == 0, (bad, hex(last))
+
+
 # ----------------------------------------------------------------- kv_quantize_page
 
 
