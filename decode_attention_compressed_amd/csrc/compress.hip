@@ -84,9 +84,80 @@ __device__ __forceinline__ void fold_batch(int ns, float mx, int k0, const u32x4
   }
 }
 
+// The same fold when a row group is exactly one wave (d = 512: 64 threads of
+// 8 dims, and row groups start at wave boundaries), so every slot's weight is
+// uniform over the wave: lane k loads slot k's logit and bias and computes its
+// weight once, and the weights reach the other lanes by lane reads, in slot
+// order.  The arithmetic is the row group fold's, value for value (the same
+// maximum, the same expf of the same arguments, the same sums in the same
+// order): the codes it leads to are identical.
+template <typename Mid>
+__device__ __forceinline__ void small_fold_wave(const CompressArgs& a, const float* zb, const uint16_t* xb, int j,
+                                                int n, int p0, bool live, float acc[8], Mid&& mid) {
+  constexpr int kFoldBatch = 8;
+  constexpr int kMaxSlots = 2 * kSmallM;
+  const int lane = threadIdx.x & 63;
+  const int t0 = j * a.m - a.ov;
+  const int lo = max(0, -(p0 + t0));
+  const int ns = live ? min(a.m + a.ov, n - t0) - lo : 0;  // uniform over the wave
+  const bool on = lane < ns;
+  const float zl = on ? zb[t0 + lo + lane] : 0.0f;
+  const float bl = on ? a.beta[lo + lane] : 0.0f;
+  u32x4 raw[kFoldBatch];
+#pragma unroll
+  for (int k = 0; k < kFoldBatch; ++k)
+    raw[k] = k < ns ? *reinterpret_cast<const u32x4*>(xb + (int64_t)(t0 + lo + k) * a.d) : u32x4{0u, 0u, 0u, 0u};
+  mid();
+  const float av = on ? zl + bl : -INFINITY;
+  // the slots' maximum: a max scan by DPP row shifts inside each 16-lane row,
+  // then the last lanes of rows 0 and 1 (slots 0 .. 31)
+  float mx = av;
+#define HCA_DPP_MAX(CTRL) \
+  mx = fmaxf(mx, u2f((uint32_t)__builtin_amdgcn_update_dpp((int)f2u(-INFINITY), (int)f2u(mx), CTRL, 0xF, 0xF, false)))
+  HCA_DPP_MAX(0x111);  // row_shr:1
+  HCA_DPP_MAX(0x112);  // row_shr:2
+  HCA_DPP_MAX(0x114);  // row_shr:4
+  HCA_DPP_MAX(0x118);  // row_shr:8
+#undef HCA_DPP_MAX
+  static_assert(kMaxSlots <= 32, "slots in lane rows 0 and 1");
+  mx = fmaxf(u2f((uint32_t)__builtin_amdgcn_readlane((int)f2u(mx), 15)),
+             u2f((uint32_t)__builtin_amdgcn_readlane((int)f2u(mx), 31)));
+  const float e = on ? expf(av - mx) : 0.0f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+  float tot = 0.0f;
+  for (int k0 = 0; k0 < ns; k0 += kFoldBatch) {
+    if (k0 > 0) {
+#pragma unroll
+      for (int k = 0; k < kFoldBatch; ++k)
+        raw[k] = k0 + k < ns ? *reinterpret_cast<const u32x4*>(xb + (int64_t)(t0 + lo + k0 + k) * a.d)
+                             : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < kFoldBatch; ++k) {
+      if (k0 + k < ns) {
+        const float ek = u2f((uint32_t)__builtin_amdgcn_readlane((int)f2u(e), k0 + k));  // slot k0 + k's weight
+        tot += ek;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(ek, u2f(raw[k][q] << 16), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(ek, u2f(raw[k][q] & 0xFFFF0000u), acc[2 * q + 1]);
+        }
+      }
+    }
+  }
+  const float inv_tot = tot > 0.0f ? 1.0f / tot : 0.0f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] *= inv_tot;
+}
+
 template <typename Mid>
 __device__ __forceinline__ void small_fold(const CompressArgs& a, const float* zb, const uint16_t* xb, int j, int n,
                                            int p0, bool live, float acc[8], Mid&& mid) {
+  if (a.d == 512) {  // uniform
+    small_fold_wave(a, zb, xb, j, n, p0, live, acc, mid);
+    return;
+  }
   constexpr int kFoldBatch = 8;
   constexpr int kMaxSlots = 2 * kSmallM;        // m + overlap, overlap <= m <= kSmallM
   const int t0 = j * a.m - a.ov;                // row of the window's first slot
