@@ -97,9 +97,11 @@ __device__ __forceinline__ void small_fold_wave(const CompressArgs& a, const flo
   constexpr int kFoldBatch = 8;
   constexpr int kMaxSlots = 2 * kSmallM;
   const int lane = threadIdx.x & 63;
-  const int t0 = j * a.m - a.ov;
+  // uniform over the wave (its one row group): read from the first lane, so
+  // that the slot tests below are scalar branches, not lane masks
+  const int t0 = __builtin_amdgcn_readfirstlane(j * a.m - a.ov);
   const int lo = max(0, -(p0 + t0));
-  const int ns = live ? min(a.m + a.ov, n - t0) - lo : 0;  // uniform over the wave
+  const int ns = __builtin_amdgcn_readfirstlane(live ? min(a.m + a.ov, n - t0) - lo : 0);
   const bool on = lane < ns;
   const float zl = on ? zb[t0 + lo + lane] : 0.0f;
   const float bl = on ? a.beta[lo + lane] : 0.0f;
@@ -208,12 +210,32 @@ __device__ __forceinline__ void small_fold(const CompressArgs& a, const float* z
 // row, RP full groups in the block), the same value in every thread of the
 // group.  Called by every thread of the block (it may synchronize it).
 __device__ __forceinline__ float row_group_sum(float v, int TD, int RP, int gi, float* sq_s) {
+  if ((TD & (TD - 1)) == 0 && TD <= 64) {
+    // an xor butterfly over the group's lanes gives every lane the same sum
+    // (each step adds two equal partial sums in either order), here by lane
+    // permutations on the VALU: DPP quad permutations for the partners l^1 and
+    // l^2; then, the quads holding equal values, the half-row mirror (l to
+    // 7 - l, a lane of the other quad) adds what l^4 would, and the row mirror
+    // what l^8 would; the permlane swaps give l^16 and l^32.
+#define HCA_DPP_ADD(CTRL) v += u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), CTRL, 0xF, 0xF, false))
+    if (TD > 1) HCA_DPP_ADD(0xB1);    // quad_perm [1, 0, 3, 2]
+    if (TD > 2) HCA_DPP_ADD(0x4E);    // quad_perm [2, 3, 0, 1]
+    if (TD > 4) HCA_DPP_ADD(0x141);   // row_half_mirror
+    if (TD > 8) HCA_DPP_ADD(0x140);   // row_mirror
+#undef HCA_DPP_ADD
+    if (TD > 16) {
+      const auto p16 = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
+      v = u2f(p16[0]) + u2f(p16[1]);
+    }
+    if (TD > 32) {
+      const auto p32 = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
+      v = u2f(p32[0]) + u2f(p32[1]);
+    }
+    return v;
+  }
   if ((TD & (TD - 1)) == 0) {
-    // an xor butterfly gives every lane the same sum (each step adds two equal
-    // partial sums in either order)
-    const int w = TD < 64 ? TD : 64;
-    for (int o = 1; o < w; o <<= 1) v += __shfl_xor(v, o, 64);
-    if (TD <= 64) return v;
+    // an xor butterfly inside each wave, then the waves' sums in order
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
     if ((threadIdx.x & 63) == 0) sq_s[threadIdx.x >> 6] = v;
     __syncthreads();
     const int nw = TD >> 6;
