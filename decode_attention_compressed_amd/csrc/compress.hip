@@ -558,6 +558,93 @@ __device__ __forceinline__ int prefill_page(const PrefillArgs& p, int b, int pg,
   return phys >= 0 && phys < p.dst.num_pages ? phys : -1;
 }
 
+// The same kernel specialized for 512-dim rows (the c4a pages): one row group
+// per wave, the fold's wave form called directly, the four rounds unrolled
+// (their rows then sit in a register array with constant indices).
+__global__ __launch_bounds__(kPrefillThreads) void prefill_small512_kernel(PrefillArgs p) {
+  const CompressArgs& a = p.c;
+  const int b = blockIdx.y, pg = blockIdx.x;
+  const int n = clampi(a.ntok[b], 0, a.max_ntok);
+  const int p0 = a.pos0[b];
+  int rows;
+  const int phys = prefill_page(p, b, pg, n, p0, rows);
+  if (phys < 0) return;  // uniform over the block
+  constexpr int d = 512, TD = 64, RP = kPrefillThreads / TD;
+  const int m = a.m, epp = p.dst.epp;
+  const int li = threadIdx.x % TD, gi = __builtin_amdgcn_readfirstlane(threadIdx.x / TD);
+  const uint16_t* xb = a.x + (int64_t)b * a.xs + li * 8;
+  const float* zb = a.z + (int64_t)b * a.zs;
+  float gam[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (a.gamma != nullptr) {
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(a.gamma + li * 8);
+    const f32x4 g0 = g4[0], g1 = g4[1];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) { gam[c] = g0[c]; gam[4 + c] = g1[c]; }
+  }
+  double inv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) inv[q] = rope_inv_freq(li * 4 + q, a.rope_r);
+  __shared__ float sq_s[kPrefillThreads];
+  __shared__ float red_s[kPrefillThreads / 64];
+  float v[kPrefillRounds][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < kPrefillRounds; ++r) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[r][c] = 0.0f;
+    if (r * RP >= epp) continue;  // uniform
+    const int row = r * RP + gi;
+    const int j = pg * epp + row;
+    const bool live = row < rows;
+    float acc[8];
+    small_fold_wave(a, zb, xb, j, n, p0, live, acc, NoMid{});
+    if (a.gamma != nullptr) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ss = fmaf(acc[c], acc[c], ss);
+      const float rs = 1.0f / sqrtf(row_group_sum(ss, TD, RP, gi, sq_s) / (float)d + a.eps);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = acc[c] * rs * gam[c];
+    }
+    if (live) {
+      rope8(acc, (double)p0 + (double)(j * m), inv, v[r]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(v[r][c]));
+    }
+  }
+  if (p.dst.dtype == HCA_FP8_E4M3) {
+    amax = block_max_n(amax, red_s, kPrefillThreads / 64);
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    uint8_t* codes = reinterpret_cast<uint8_t*>(p.dst.codes) + (int64_t)phys * epp * d;
+#pragma unroll
+    for (int r = 0; r < kPrefillRounds; ++r) {
+      const int row = r * RP + gi;
+      if (r * RP >= epp || row >= epp) continue;
+      u32x2 w = {0u, 0u};
+      if (row < rows) {
+        w[0] = enc4_e4m3(f32x4{v[r][0], v[r][1], v[r][2], v[r][3]}, s);
+        w[1] = enc4_e4m3(f32x4{v[r][4], v[r][5], v[r][6], v[r][7]}, s);
+      }
+      *reinterpret_cast<u32x2*>(codes + (int64_t)row * d + li * 8) = w;
+    }
+    if (threadIdx.x == 0) reinterpret_cast<float*>(p.dst.scales)[phys] = s;
+  } else {  // bf16
+    uint16_t* codes = reinterpret_cast<uint16_t*>(p.dst.codes) + (int64_t)phys * epp * d;
+#pragma unroll
+    for (int r = 0; r < kPrefillRounds; ++r) {
+      const int row = r * RP + gi;
+      if (r * RP >= epp || row >= epp) continue;
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (row < rows) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = (uint32_t)bf16_encode(v[r][2 * q]) | ((uint32_t)bf16_encode(v[r][2 * q + 1]) << 16);
+      }
+      *reinterpret_cast<u32x4*>(codes + (int64_t)row * d + li * 8) = w;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kPrefillThreads) void prefill_small_kernel(PrefillArgs p) {
   const CompressArgs& a = p.c;
   const int b = blockIdx.y, pg = blockIdx.x;
@@ -710,7 +797,10 @@ hipError_t launch_prefill(PrefillArgs p, hipStream_t s) {
   a.rope_r = pow((double)a.theta, -2.0 / (double)a.d);
   const int pages = (n_max + p.dst.epp - 1) / p.dst.epp;
   if (a.m <= kSmallM) {
-    hipLaunchKernelGGL(prefill_small_kernel, dim3(pages, a.B), dim3(kPrefillThreads), 0, s, p);
+    if (a.d == 512)
+      hipLaunchKernelGGL(prefill_small512_kernel, dim3(pages, a.B), dim3(kPrefillThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(prefill_small_kernel, dim3(pages, a.B), dim3(kPrefillThreads), 0, s, p);
   } else {
     const size_t shm = kCompressShm + (size_t)p.dst.epp * a.d * sizeof(float);
     hipLaunchKernelGGL(prefill_large_kernel, dim3(pages, a.B), dim3(kCompressThreads), shm, s, p);
