@@ -56,10 +56,27 @@ __device__ __forceinline__ uint32_t e4m3_encode2_hw(float a, float b, uint32_t o
   b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, kHi);
 }
-// four codes of v / s (an fp8 page's encoding: exact fp32 divisions), packed
-// little-endian
+// The quotient x / s for the E4M3 encoder: the code of fl32(x / s) is the code
+// of q = x * rs with rs = rcp(s) (within 1 unit in the last place of 1 / s)
+// wherever q is in E4M3's normal range and more than 8 units in the last place
+// away from the points where E4M3's rounding changes (the midpoints between
+// consecutive E4M3 values: the 20 mantissa bits below E4M3's three equal
+// 0x80000).  q is within 4 units of fl32(x / s) (three roundings of 2^-24 and
+// the reciprocal's 2^-23 of |x / s|), so both lie on the same side of every such
+// point, and saturation clamps both alike; everywhere else (zero, E4M3's
+// subnormal range, a non-finite q, near a midpoint) the exact quotient is
+// taken.
+__device__ __forceinline__ float e4m3_quotient(float x, float s, float rs) {
+  float q = x * rs;
+  const uint32_t u = f2u(q) & 0x7FFFFFFFu;
+  if (!(u >= 0x3C800000u && u < 0x7F800000u && ((u & 0xFFFFFu) - 0x7FFF8u) > 16u)) q = x / s;
+  return q;
+}
+// four codes of fl32(v / s) (an fp8 page's encoding), packed little-endian
 __device__ __forceinline__ uint32_t e4m3_encode4_div(float v0, float v1, float v2, float v3, float s) {
-  return e4m3_encode2_hw<true>(v2 / s, v3 / s, e4m3_encode2_hw<false>(v0 / s, v1 / s, 0u));
+  const float rs = __builtin_amdgcn_rcpf(s);
+  return e4m3_encode2_hw<true>(e4m3_quotient(v2, s, rs), e4m3_quotient(v3, s, rs),
+                               e4m3_encode2_hw<false>(e4m3_quotient(v0, s, rs), e4m3_quotient(v1, s, rs), 0u));
 }
 HCA_HD float e4m3_decode(uint32_t c) {
   const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;

@@ -128,6 +128,57 @@ def test_quantize_pages_bit_exact(dtype, epp, dim, use_ws):
 
 
 @pytest.mark.parametrize("use_ws", [False, True])
+def test_quantize_fp8_values_at_rounding_midpoints(use_ws):
+    # the page encoder divides by the page scale through a reciprocal and takes
+    # the exact quotient only near E4M3's rounding points: here every value of
+    # a page is within a few units in the last place of s times an E4M3
+    # midpoint (every midpoint of the normal range, both signs), for scales of
+    # several magnitudes and mantissas, and the codes must equal the oracle's
+    # RNE(fl32(x / s)) bit for bit
+    H.flush(f"quantize fp8 at rounding midpoints ws={use_ws}")
+    rng = np.random.default_rng(43)
+    epp, dim = 64, 512
+    mids = []
+    for e in range(-6, 9):
+        for mant in range(8):
+            lo = 2.0 ** e * (1 + mant / 8)
+            mids.append(lo * (1 + 1 / 16))  # halfway to the next E4M3 value
+    mids = np.array([m for m in mids if m < 448], np.float64)
+    pages = []
+    for amax in [448.0, 1.0, 3.0e-4, 7.77, 1234.5678, 0.1]:
+        s = np.float32(np.float32(amax) / np.float32(448))
+        vals = []
+        for m in mids:
+            for k in range(-10, 11):  # x / s from about 11 units below the midpoint to 11 above, the midpoint itself among them
+                vals.append(np.float32(m) * s * np.float32(1 + k * 2.0 ** -23))
+        vals = np.array(vals, np.float32)
+        vals = vals * rng.choice([-1, 1], vals.shape).astype(np.float32)
+        flat = np.zeros(epp * dim, np.float32)
+        flat[0] = np.float32(amax)  # the page's amax
+        flat[1: 1 + min(len(vals), epp * dim - 1)] = vals[: epp * dim - 1]
+        pages.append(flat.reshape(epp, dim))
+    B = len(pages)
+    src = np.stack(pages)  # [B, epp, dim]: one page per sequence
+    table = np.arange(B, dtype=np.int32).reshape(B, 1)
+    ref = paging.Pool("fp8", B, epp, dim)
+    for b in range(B):
+        paging.write_run(ref, table[b], 0, src[b])
+    assert (np.abs(src).max(axis=(1, 2)) == np.array([448.0, 1.0, 3.0e-4, 7.77, 1234.5678, 0.1], np.float32)).all()
+    dst = hca.PagedCache.empty(B, epp, dim, "fp8")
+    ws = None
+    if use_ws:
+        ws = torch.zeros((max(hca.kv_quantize_page_workspace(B, epp, dst), 1),), dtype=torch.uint8, device="cuda")
+    lens = np.full(B, epp, np.int32)
+    hca.kv_quantize_page(H.to_dev(src), H.to_dev(np.zeros(B, np.int32)), H.to_dev(lens), epp, H.to_dev(table), dst, ws=ws)
+    torch.cuda.synchronize()
+    got = H.download_pool(dst, ref)
+    for b in range(B):
+        assert got.scales[b] == ref.scales[b], b
+        bad = np.nonzero(got.codes[b] != ref.codes[b])
+        assert bad[0].size == 0, (b, bad[0][:5], bad[1][:5])
+
+
+@pytest.mark.parametrize("use_ws", [False, True])
 def test_quantize_open_page_run(use_ws):
     # a run that starts at a later page (the decode update's open page), e0 > 0
     H.flush(f"quantize open page ws={use_ws}")
