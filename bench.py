@@ -57,18 +57,18 @@ TRAFFIC = {
                                    "decode_attention_compressed_amd/csrc/hca_common.h",
                                    "decode_attention_compressed_amd/csrc/indexer_internal.h",
                                    "decode_attention_compressed_amd/csrc/indexer_score.h"),
-                       "source_sha256": "c5a762b6187a503b6c253c58647420931b07c8722b81cf769a18f0c2e53079dc",
+                       "source_sha256": "08fbcbf2a330ace32bfe8ba11a18e0a61ef3d693ef361d134495eed67f2f19a7",
                        "fetch_bytes": 72078100, "write_bytes": 4662067},
     ("stack-1m-b4-61layers", "c128a", "attn_split"): {"sources": ("decode_attention_compressed_amd/csrc/attention.hip",
                                           "decode_attention_compressed_amd/csrc/hca_common.h",
                                           "decode_attention_compressed_amd/csrc/hca_internal.h"),
-                              "source_sha256": "cca231f9c11bfbac647caeec8b73b22fa9fc5d9d8572e432718e15727292071d",
-                              "fetch_bytes": 19994104, "write_bytes": 4259840},
+                              "source_sha256": "dc096a62b8c6102362560fef433987eec427589122e46e8b05885e27e45529d5",
+                              "fetch_bytes": 19994514, "write_bytes": 4259840},
     ("stack-1m-b4-61layers", "c4a", "attn_split"): {"sources": ("decode_attention_compressed_amd/csrc/attention.hip",
                                         "decode_attention_compressed_amd/csrc/hca_common.h",
                                         "decode_attention_compressed_amd/csrc/hca_internal.h"),
-                            "source_sha256": "cca231f9c11bfbac647caeec8b73b22fa9fc5d9d8572e432718e15727292071d",
-                            "fetch_bytes": 7349671, "write_bytes": 3727360},
+                            "source_sha256": "dc096a62b8c6102362560fef433987eec427589122e46e8b05885e27e45529d5",
+                            "fetch_bytes": 7348647, "write_bytes": 3727360},
 }
 
 
