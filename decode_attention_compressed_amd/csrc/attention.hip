@@ -829,6 +829,25 @@ __device__ __forceinline__ int pair_kdim(int t, int g) {
   return 256 * (t >> 3) + 16 * (4 * ((t & 7) >> 1) + g) + 8 * (t & 1);
 }
 
+// The two waves of a pair meet through LDS counters instead of block
+// barriers, so a pair never waits for another pair's loads.  flag[w][0] counts
+// the steps whose partial S wave w has written, flag[w][1] the steps whose
+// partner partial wave w has read.  A wave's LDS operations complete in order
+// and the release waits for them (lgkmcnt), so a counter never runs ahead of
+// the data it announces.  The spin is bounded (a few ms): if a partner never
+// arrives the kernel still ends.
+__device__ __forceinline__ void pair_signal(int* flag, int v) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  if ((threadIdx.x & 63) == 0) __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void pair_wait(const int* flag, int v) {
+  for (int it = 0; it < (1 << 16); ++it) {
+    if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= v) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) {
   constexpr int D = kPairD;
   constexpr int KS = D / 32;     // k-steps of the whole S contraction
@@ -848,6 +867,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
   __shared__ float2 ml_s[kPairs][kHeadsPerBlock];
   __shared__ float sg_s[kPairs];
   __shared__ __attribute__((aligned(16))) float wt_s[kPairs][kHeadsPerBlock];
+  __shared__ int psync_s[kPairWaves][2];
   static_assert(sizeof(q_s) == (size_t)kPairWaves * 2 * 64 * sizeof(f32x4), "partial S exchange area");
   static_assert(2 * sizeof(float) * kHeadsPerBlock * D <= kPairs * PT::BYTES, "the merge reuses the tiles");
 
@@ -1008,6 +1028,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
 #pragma unroll
   for (int j = 0; j < kPer; ++j)
     if (row_of(j) < RPS) ps_s[row_of(j)] = ps[j];
+  if (lane < 2) psync_s[wave][lane] = 0;
   lds_barrier();  // every row's page scale is visible to both waves of its pair
 
   f32x4 oacc[NBH];  // O for the 16 heads (rows 4g + i) over dims 256 hf + 16n + col, in units of sigma
@@ -1126,44 +1147,40 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
     }
   };
 
-  // ---- the pair's tiles pair, pair + 4, ...: every wave runs the same number
-  // of steps (the block's barriers are not inside any condition); a pair with
-  // fewer tiles idles through its last step.  Tile t is in ring slot st & 1 and
-  // tile t + 4 may still be loading behind it; a slot is refilled with tile
-  // t + 8 once this wave's reads of its half are done.
-  const int nsteps = (nt + kPairs - 1) / kPairs;
+  // ---- the pair's tiles pair, pair + 4, ...: both waves of a pair run the
+  // same steps and meet only each other (pair_signal / pair_wait).  Tile t is
+  // in ring slot st & 1 and tile t + 4 may still be loading behind it; a slot
+  // is refilled with tile t + 8 once this wave's reads of its half are done.
+  const int nsteps = nt > pair ? (nt - pair + kPairs - 1) / kPairs : 0;
   for (int st = 0; st < nsteps; ++st) {
     const int t = pair + kPairs * st;
-    const bool act = t < nt;
     uint8_t* slot = (st & 1) ? slot1 : slot0;
-    f32x4 sres[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    if (act) {
-      if (t + kPairs < nt)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PT::INSTR));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      asm volatile("" ::: "memory");
-      qk_half(slot, sres);
+    f32x4 sres[2];
+    if (t + kPairs < nt)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(PT::INSTR));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    asm volatile("" ::: "memory");
+    qk_half(slot, sres);
+    if (st > 0) pair_wait(&psync_s[wave ^ 1][1], st);  // the partner has read this wave's last partial
 #pragma unroll
-      for (int h = 0; h < 2; ++h) xs[(wave * 2 + h) * 64 + lane] = sres[h];
-    }
-    lds_barrier();  // partial S of both waves of every pair in LDS
-    if (act) {
-      // the full S: half 0's partial plus half 1's, the same sum in both waves
+    for (int h = 0; h < 2; ++h) xs[(wave * 2 + h) * 64 + lane] = sres[h];
+    pair_signal(&psync_s[wave][0], st + 1);
+    pair_wait(&psync_s[wave ^ 1][0], st + 1);  // the partner's partial S of this tile is in LDS
+    // the full S: half 0's partial plus half 1's, the same sum in both waves
+    f32x4 o[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const f32x4 o = xs[((wave ^ 1) * 2 + h) * 64 + lane];
-        sres[h] = hf == 0 ? sres[h] + o : o + sres[h];
-      }
-      f16x8 pf;
-      uint32_t vmask[2];
-      softmax(t, sres, pf, vmask);
-      pv_half(slot, pf, vmask);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & ~0x0F00);  // lgkmcnt(0): the slot's reads are done
-      asm volatile("" ::: "memory");
-      if (t + 2 * kPairs < nt) issue(t + 2 * kPairs, slot);
-    }
-    lds_barrier();  // the partner has read this wave's partial before the next one is written
+    for (int h = 0; h < 2; ++h) o[h] = xs[((wave ^ 1) * 2 + h) * 64 + lane];
+    pair_signal(&psync_s[wave][1], st + 1);  // (the release waits for these reads)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) sres[h] = hf == 0 ? sres[h] + o[h] : o[h] + sres[h];
+    f16x8 pf;
+    uint32_t vmask[2];
+    softmax(t, sres, pf, vmask);
+    pv_half(slot, pf, vmask);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & ~0x0F00);  // lgkmcnt(0): the slot's reads are done
+    asm volatile("" ::: "memory");
+    if (t + 2 * kPairs < nt) issue(t + 2 * kPairs, slot);
   }
 
   // ---- merge the four pairs' states
