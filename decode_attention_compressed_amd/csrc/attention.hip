@@ -866,10 +866,9 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
   __shared__ __attribute__((aligned(16))) float ps_s[kMaxSplitRows];  // page scale; -1: skipped row
   __shared__ float2 ml_s[kPairs][kHeadsPerBlock];
   __shared__ float sg_s[kPairs];
-  __shared__ __attribute__((aligned(16))) float wt_s[kPairs][kHeadsPerBlock];
   __shared__ int psync_s[kPairWaves][2];
   static_assert(sizeof(q_s) == (size_t)kPairWaves * 2 * 64 * sizeof(f32x4), "partial S exchange area");
-  static_assert(2 * sizeof(float) * kHeadsPerBlock * D <= kPairs * PT::BYTES, "the merge reuses the tiles");
+  static_assert(sizeof(float) * kHeadsPerBlock * D / 2 == 2 * PT::HALF_BYTES, "a wave's O fills its halves of its pair's slots");
 
   const int item = attn_item_of_block(a);
   if (item < 0) return;
@@ -1183,22 +1182,30 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
     if (t + 2 * kPairs < nt) issue(t + 2 * kPairs, slot);
   }
 
-  // ---- merge the four pairs' states
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load into the tiles is in flight
-  __syncthreads();
-  // pair p's O: [4 head quads][D][4 heads] floats in the tile memory, dims of half hf from its wave
-  auto o_of = [&](int p) { return reinterpret_cast<float*>((p < 2 ? tile0_s : tile1_s) + (p & 1) * 64 * D); };
-  {
-    float* o_s = o_of(pair);
+  // ---- merge the four pairs' states.  A wave's O goes into the LDS that only
+  // its own loads fill (half hf of both of its pair's ring slots: head quads
+  // 0-1, then 2-3), so it is written as soon as the wave's last tile is read,
+  // while other pairs may still be working; one barrier, then every wave
+  // finds the weights of all 4 pairs x 16 heads (one per lane) and the sum
+  // takes them by lane reads.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load of this wave's into the slots is in flight
+  auto o_at = [&](int p, int hfx, int hq, int dh) {  // f32x4 of head quad hq, dim 256 hfx + dh, pair p
+    return reinterpret_cast<f32x4*>((hq < 2 ? tile0_s : tile1_s) + p * PT::BYTES + PT::HALF_BYTES * hfx +
+                                    16 * ((hq & 1) * (D / 2) + dh));
+  };
 #pragma unroll
-    for (int n = 0; n < NBH; ++n)
-      *reinterpret_cast<f32x4*>(&o_s[(g * D + (D / 2) * hf + 16 * n + col) * 4]) = oacc[n] * sigma;
-  }
+  for (int n = 0; n < NBH; ++n) *o_at(pair, hf, g, 16 * n + col) = oacc[n] * sigma;
   if (hf == 0 && g == 0) ml_s[pair][col] = make_float2(m_run, l_run);
   if (threadIdx.x == (unsigned)(2 * pair * 64)) sg_s[pair] = sigma;
   __syncthreads();
-  if (threadIdx.x < kHeadsPerBlock) {
-    const int hh = threadIdx.x;
+  // lane 16 p + h: the weight of pair p's O for head h0 + h.  The f16 partial
+  // is O / c with c = l * sg: every row's value is a code (|code| <= 448) times
+  // its page scale, which is at most kSigmaSlack * sg (sigma grows lazily), so
+  // |O / c| <= 448 * kSigmaSlack, well inside f16, whatever the data's
+  // magnitude.
+  float wl;
+  {
+    const int hh = lane & 15, pl = lane >> 4;
     float M = -INFINITY, sg = 0.0f;
 #pragma unroll
     for (int p = 0; p < kPairs; ++p) {
@@ -1211,31 +1218,31 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
       wt[p] = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml_s[p][hh].x - M);  // 0 for an idle pair
       l += wt[p] * ml_s[p][hh].y;
     }
-    // The f16 partial is O / c with c = l * sg: every row's value is a code
-    // (|code| <= 448) times its page scale, which is at most kSigmaSlack * sg
-    // (sigma grows lazily), so |O / c| <= 448 * kSigmaSlack, well inside f16,
-    // whatever the data's magnitude.
     const float c = l * sg;
     const float inv = c > 0.0f ? 1.0f / c : 0.0f;
-#pragma unroll
-    for (int p = 0; p < kPairs; ++p) wt_s[p][hh] = wt[p] * inv;
-    if (h0 + hh < H)
+    wl = (pl == 0 ? wt[0] : pl == 1 ? wt[1] : pl == 2 ? wt[2] : wt[3]) * inv;
+    if (wave == 0 && lane < kHeadsPerBlock && h0 + hh < H)
       ml[part + h0 + hh] = M == -INFINITY ? f32x4{-INFINITY, 0.0f, 0.0f, 0.0f} : f32x4{M * 0.6931471805599453f, l, c, 0.0f};
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < D * (kHeadsPerBlock / 4); e += kPairThreads) {
-    const int hq = e / D, dim = e - hq * D;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  static_assert(D == kPairThreads, "one dim per thread in the sum");
+  {
+    const int dim = threadIdx.x, hfx = dim / (D / 2), dh = dim % (D / 2);
 #pragma unroll
-    for (int p = 0; p < kPairs; ++p) {
-      const f32x4 o = *reinterpret_cast<const f32x4*>(&o_of(p)[(hq * D + dim) * 4]);
-      const f32x4 wt = *reinterpret_cast<const f32x4*>(&wt_s[p][4 * hq]);
-      acc += wt * o;
-    }
+    for (int hq = 0; hq < kHeadsPerBlock / 4; ++hq) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int h = h0 + 4 * hq + k;
-      if (h < H) opart[(part + h) * D + dim] = (_Float16)acc[k];
+      for (int p = 0; p < kPairs; ++p) {
+        const f32x4 o = *o_at(p, hfx, hq, dh);
+        f32x4 wt;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) wt[k] = u2f((uint32_t)__builtin_amdgcn_readlane((int)f2u(wl), 16 * p + 4 * hq + k));
+        acc += wt * o;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int h = h0 + 4 * hq + k;
+        if (h < H) opart[(part + h) * D + dim] = (_Float16)acc[k];
+      }
     }
   }
 }
