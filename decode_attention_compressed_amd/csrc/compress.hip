@@ -105,10 +105,17 @@ __device__ __forceinline__ void small_fold_wave(const CompressArgs& a, const flo
   const bool on = lane < ns;
   const float zl = on ? zb[t0 + lo + lane] : 0.0f;
   const float bl = on ? a.beta[lo + lane] : 0.0f;
+  // the first batch's rows, loaded without per-slot tests: a slot past the
+  // present ones re-reads the last present row (it is not added)
   u32x4 raw[kFoldBatch];
+  if (ns > 0) {
 #pragma unroll
-  for (int k = 0; k < kFoldBatch; ++k)
-    raw[k] = k < ns ? *reinterpret_cast<const u32x4*>(xb + (int64_t)(t0 + lo + k) * a.d) : u32x4{0u, 0u, 0u, 0u};
+    for (int k = 0; k < kFoldBatch; ++k)
+      raw[k] = *reinterpret_cast<const u32x4*>(xb + (int64_t)(t0 + lo + min(k, ns - 1)) * a.d);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kFoldBatch; ++k) raw[k] = u32x4{0u, 0u, 0u, 0u};
+  }
   mid();
   const float av = on ? zl + bl : -INFINITY;
   // the slots' maximum: a max scan by DPP row shifts inside each 16-lane row,
@@ -312,8 +319,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int
   }
 
   double inv[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) inv[p] = rope_inv_freq(li * 4 + p, a.rope_r);
+  rope_inv_freq4(li, a.rope_r, inv);
 
   if (small) {
     // every thread runs every round (mid() and the row sum of the
@@ -582,8 +588,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_small512_kernel(Prefi
     for (int c = 0; c < 4; ++c) { gam[c] = g0[c]; gam[4 + c] = g1[c]; }
   }
   double inv[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) inv[q] = rope_inv_freq(li * 4 + q, a.rope_r);
+  rope_inv_freq4(li, a.rope_r, inv);
   __shared__ float sq_s[kPrefillThreads];
   __shared__ float red_s[kPrefillThreads / 64];
   float v[kPrefillRounds][8];
@@ -667,8 +672,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_small_kernel(PrefillA
     for (int c = 0; c < 4; ++c) { gam[c] = g0[c]; gam[4 + c] = g1[c]; }
   }
   double inv[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) inv[q] = rope_inv_freq(li * 4 + q, a.rope_r);
+  rope_inv_freq4(li, a.rope_r, inv);
   __shared__ float sq_s[kPrefillThreads];
   __shared__ float red_s[kPrefillThreads / 64];
   // the page's rotated rows stay in registers until the page scale is known:
@@ -883,8 +887,7 @@ __device__ __forceinline__ void state_fold(const CompressArgs& a, int b, int n, 
   }
   mid();
   double inv[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) inv[p] = rope_inv_freq(li * 4 + p, a.rope_r);
+  rope_inv_freq4(li, a.rope_r, inv);
   const float at = zt + bt;
   const float M2 = fmaxf(M, at);
   const float co = expf(M - M2), cn = expf(at - M2);

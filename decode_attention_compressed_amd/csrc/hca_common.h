@@ -134,6 +134,24 @@ __device__ __forceinline__ double rope_inv_freq(int i, double r) {
   }
   return acc;
 }
+// rope_inv_freq(4 j + q, r) for q = 0 .. 3 and 0 <= j < 256, bit for bit: the
+// same squares of r, multiplied into each power in the same order (a factor
+// of 1.0 where a bit is clear, which is exact), but the squares are taken once
+// for the four and the two low bits are known for each q.
+__device__ __forceinline__ void rope_inv_freq4(int j, double r, double inv[4]) {
+  double p = r * r;  // r^2
+  inv[0] = 1.0;
+  inv[1] = r;
+  inv[2] = p;
+  inv[3] = r * p;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    p *= p;  // r^(2^(k + 2))
+    const double f = ((j >> k) & 1) ? p : 1.0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) inv[q] *= f;
+  }
+}
 // cos and sin of pos * inv_freq: the angle in turns (fp64, so that large
 // positions keep their fraction), reduced to [-1/2, 1/2] turn, then the hardware
 // sine and cosine, which take turns (v_sin_f32 / v_cos_f32: within 1.3e-7 of

@@ -211,10 +211,16 @@ __device__ __forceinline__ void hist_flush(const IndexerArgs& a, int b, int bx, 
   const int copy = bx % kHistCopies;
   uint32_t* gh = base + copy * kHistBins;
   uint32_t* gc = base + kHistCopies * kHistBins + copy * kCoarseBins;
+  // all of the thread's bins are read before the first atomic (the compiler
+  // does not move LDS reads across the atomics, so the rounds would each wait
+  // for their own read)
+  uint32_t cv[kCoarseBins];
+#pragma unroll
+  for (int r = 0; r < kCoarseBins; ++r) cv[r] = hist_s[(int)threadIdx.x + r * kScoreThreads];
 #pragma unroll
   for (int r = 0; r < kCoarseBins; ++r) {
     const int i = (int)threadIdx.x + r * kScoreThreads;
-    const uint32_t c = hist_s[i];
+    const uint32_t c = cv[r];
     if (c) atomicAdd(&gh[i], c);
     if (__ballot(c != 0u)) {
       const uint32_t s = wave_sum_u32(c);
@@ -454,7 +460,10 @@ __device__ __forceinline__ void score_pages_block(const IndexerArgs& a, int bx, 
   load_query<KDT, DI>(a, b, col, g, qa, c.wgt);
   // the histogram is cleared whatever k is; the barrier orders LDS only and
   // leaves the loads above in flight
-  for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) hist_s[i] = 0;
+  static_assert(kHistBins % (4 * kScoreThreads) == 0, "the clear writes 16 bytes per thread and round");
+#pragma unroll
+  for (int i = 4 * (int)threadIdx.x; i < kHistBins; i += 4 * kScoreThreads)
+    *reinterpret_cast<u32x4*>(&hist_s[i]) = u32x4{0u, 0u, 0u, 0u};
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
