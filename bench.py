@@ -57,18 +57,18 @@ TRAFFIC = {
                                    "decode_attention_compressed_amd/csrc/hca_common.h",
                                    "decode_attention_compressed_amd/csrc/indexer_internal.h",
                                    "decode_attention_compressed_amd/csrc/indexer_score.h"),
-                       "source_sha256": "08fbcbf2a330ace32bfe8ba11a18e0a61ef3d693ef361d134495eed67f2f19a7",
-                       "fetch_bytes": 72078100, "write_bytes": 4662067},
+                       "source_sha256": "cb379449b7cd71d89b5d3b0eb32be58f9c9b6d0f6d09792219ba2b3903ded5ea",
+                       "fetch_bytes": 72072892, "write_bytes": 4662278},
     ("stack-1m-b4-61layers", "c128a", "attn_split"): {"sources": ("decode_attention_compressed_amd/csrc/attention.hip",
                                           "decode_attention_compressed_amd/csrc/hca_common.h",
                                           "decode_attention_compressed_amd/csrc/hca_internal.h"),
-                              "source_sha256": "dc096a62b8c6102362560fef433987eec427589122e46e8b05885e27e45529d5",
-                              "fetch_bytes": 19994514, "write_bytes": 4259840},
+                              "source_sha256": "e27060a148f93924a07fdb34c9731e7cf29ce6537ac7683befeaeddaea93fc33",
+                              "fetch_bytes": 20031352, "write_bytes": 4259840},
     ("stack-1m-b4-61layers", "c4a", "attn_split"): {"sources": ("decode_attention_compressed_amd/csrc/attention.hip",
                                         "decode_attention_compressed_amd/csrc/hca_common.h",
                                         "decode_attention_compressed_amd/csrc/hca_internal.h"),
-                            "source_sha256": "dc096a62b8c6102362560fef433987eec427589122e46e8b05885e27e45529d5",
-                            "fetch_bytes": 7348647, "write_bytes": 3727360},
+                            "source_sha256": "e27060a148f93924a07fdb34c9731e7cf29ce6537ac7683befeaeddaea93fc33",
+                            "fetch_bytes": 7385429, "write_bytes": 3727360},
 }
 
 
