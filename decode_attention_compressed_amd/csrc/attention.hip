@@ -443,8 +443,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
         amax = fmaxf(amax, fmaxf(fabsf(y[i][2 * p]), fabsf(y[i][2 * p + 1])));
       }
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    amax = rows_max4(amax);
     if (g == 0) qam_s[wave][col] = amax;
     lds_barrier();
     amax = fmaxf(fmaxf(qam_s[0][col], qam_s[1][col]), fmaxf(qam_s[2][col], qam_s[3][col]));

@@ -213,36 +213,39 @@ __device__ __forceinline__ void small_fold(const CompressArgs& a, const float* z
   for (int c = 0; c < 8; ++c) acc[c] *= inv_tot;
 }
 
+// An xor butterfly over aligned groups of TD lanes (TD a power of two <= 64):
+// every lane of a group gets the same sum (each step adds two equal partial
+// sums in either order), by lane permutations on the VALU: DPP quad
+// permutations for the partners l^1 and l^2; then, the quads holding equal
+// values, the half-row mirror (l to 7 - l, a lane of the other quad) adds what
+// l^4 would, and the row mirror what l^8 would; the permlane swaps give l^16
+// and l^32.
+__device__ __forceinline__ float lanes_sum_pow2(float v, int TD) {
+#define HCA_DPP_ADD(CTRL) v += u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), CTRL, 0xF, 0xF, false))
+  if (TD > 1) HCA_DPP_ADD(0xB1);    // quad_perm [1, 0, 3, 2]
+  if (TD > 2) HCA_DPP_ADD(0x4E);    // quad_perm [2, 3, 0, 1]
+  if (TD > 4) HCA_DPP_ADD(0x141);   // row_half_mirror
+  if (TD > 8) HCA_DPP_ADD(0x140);   // row_mirror
+#undef HCA_DPP_ADD
+  if (TD > 16) {
+    const auto p16 = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
+    v = u2f(p16[0]) + u2f(p16[1]);
+  }
+  if (TD > 32) {
+    const auto p32 = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
+    v = u2f(p32[0]) + u2f(p32[1]);
+  }
+  return v;
+}
+
 // Sum of v over the TD consecutive threads of row group gi (TD = threads per
 // row, RP full groups in the block), the same value in every thread of the
 // group.  Called by every thread of the block (it may synchronize it).
 __device__ __forceinline__ float row_group_sum(float v, int TD, int RP, int gi, float* sq_s) {
-  if ((TD & (TD - 1)) == 0 && TD <= 64) {
-    // an xor butterfly over the group's lanes gives every lane the same sum
-    // (each step adds two equal partial sums in either order), here by lane
-    // permutations on the VALU: DPP quad permutations for the partners l^1 and
-    // l^2; then, the quads holding equal values, the half-row mirror (l to
-    // 7 - l, a lane of the other quad) adds what l^4 would, and the row mirror
-    // what l^8 would; the permlane swaps give l^16 and l^32.
-#define HCA_DPP_ADD(CTRL) v += u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), CTRL, 0xF, 0xF, false))
-    if (TD > 1) HCA_DPP_ADD(0xB1);    // quad_perm [1, 0, 3, 2]
-    if (TD > 2) HCA_DPP_ADD(0x4E);    // quad_perm [2, 3, 0, 1]
-    if (TD > 4) HCA_DPP_ADD(0x141);   // row_half_mirror
-    if (TD > 8) HCA_DPP_ADD(0x140);   // row_mirror
-#undef HCA_DPP_ADD
-    if (TD > 16) {
-      const auto p16 = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
-      v = u2f(p16[0]) + u2f(p16[1]);
-    }
-    if (TD > 32) {
-      const auto p32 = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
-      v = u2f(p32[0]) + u2f(p32[1]);
-    }
-    return v;
-  }
+  if ((TD & (TD - 1)) == 0 && TD <= 64) return lanes_sum_pow2(v, TD);
   if ((TD & (TD - 1)) == 0) {
     // an xor butterfly inside each wave, then the waves' sums in order
-    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+    v = lanes_sum_pow2(v, 64);
     if ((threadIdx.x & 63) == 0) sq_s[threadIdx.x >> 6] = v;
     __syncthreads();
     const int nw = TD >> 6;
@@ -1077,8 +1080,7 @@ __device__ __forceinline__ void insert_block(const InsertArgs& a, int b, float* 
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = 0.0f;
       }
-      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      amax = quad_max(amax);
       if (!live) continue;
       const uint32_t sc = r <= row ? e4m3_encode(amax / 6.0f) : 0u;
       const float sdec = e4m3_decode(sc);

@@ -163,17 +163,36 @@ __device__ __forceinline__ void rope_cs(double pos, double inv_freq, float& c, f
   c = __builtin_amdgcn_cosf(t);
 }
 
-// Wave64 reductions (butterfly through ds_swizzle/DPP via __shfl_xor).
+// Wave64 reductions: the xor butterfly with strides 32, 16, 8, 4, 2, 1, every
+// lane getting the result, on the VALU (a lane shuffle is an LDS round trip).
+// Strides 32 and 16 by v_permlane32_swap / v_permlane16_swap (each lane gets
+// its own value and lane l ^ 32, resp. l ^ 16); then rotations by 8, 4, 2, 1
+// inside each 16-lane row (DPP row_ror): after the steps before, the lane a
+// rotation by k reaches holds the value of lane l ^ k, so every step adds the
+// same two values as the butterfly (in either order, which IEEE addition does
+// not see), and the sums equal the shuffle butterfly's bit for bit.
+#define HCA_ROR(v, n) u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), 0x120 + (n), 0xF, 0xF, false))
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  const auto a = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
+  v = fmaxf(u2f(a[0]), u2f(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
+  v = fmaxf(u2f(b[0]), u2f(b[1]));
+  v = fmaxf(v, HCA_ROR(v, 8));
+  v = fmaxf(v, HCA_ROR(v, 4));
+  v = fmaxf(v, HCA_ROR(v, 2));
+  return fmaxf(v, HCA_ROR(v, 1));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  const auto a = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
+  v = u2f(a[0]) + u2f(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
+  v = u2f(b[0]) + u2f(b[1]);
+  v = v + HCA_ROR(v, 8);
+  v = v + HCA_ROR(v, 4);
+  v = v + HCA_ROR(v, 2);
+  return v + HCA_ROR(v, 1);
 }
+#undef HCA_ROR
 
 // Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48),
 // every lane getting the result.  Row swaps on the VALU: with both operands x,
@@ -192,6 +211,19 @@ __device__ __forceinline__ float rows_sum4(float v) {
   v = u2f(a[0]) + u2f(a[1]);
   const auto b = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
   return u2f(b[0]) + u2f(b[1]);
+}
+// max over the four lanes of each quad (DPP quad permutations: partners l ^ 1,
+// then l ^ 2), every lane of the quad getting it
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), 0xB1, 0xF, 0xF, false)));  // [1, 0, 3, 2]
+  return fmaxf(v, u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), 0x4E, 0xF, 0xF, false)));  // [2, 3, 0, 1]
+}
+// max over each 16-lane row: the quads, then the half-row mirror (a lane of the
+// other quad of its half) and the row mirror (a lane of the other half)
+__device__ __forceinline__ float row16_max(float v) {
+  v = quad_max(v);
+  v = fmaxf(v, u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), 0x141, 0xF, 0xF, false)));
+  return fmaxf(v, u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), 0x140, 0xF, 0xF, false)));
 }
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }

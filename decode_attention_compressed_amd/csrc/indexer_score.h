@@ -400,8 +400,7 @@ struct OpenRow {
     if (lb < page0 || lb >= page0 + kPagesPerScoreBlock || ((lb - page0) & 3) != wave) return;
     const float2 v = reinterpret_cast<const float2*>(a.open.stage + (int64_t)b * a.open.ss + (int64_t)r * 128)[lane];
     float amax = fmaxf(fabsf(v.x), fabsf(v.y));
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    amax = row16_max(amax);
     sc = e4m3_encode(amax / 6.0f);
     const float sdec = e4m3_decode(sc);
     byte = sdec > 0.0f ? (e2m1_encode(v.x / sdec) | (e2m1_encode(v.y / sdec) << 4)) : 0u;

@@ -276,8 +276,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_fp4_kernel(QuantArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = 0.0f;
       }
-      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      amax = quad_max(amax);
       const uint32_t sc = row < rows ? e4m3_encode(amax / 6.0f) : 0u;
       const float sdec = e4m3_decode(sc);
       uint32_t word = 0;
