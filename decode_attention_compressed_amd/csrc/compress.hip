@@ -976,9 +976,11 @@ __device__ __forceinline__ void insert_block(const InsertArgs& a, int b, float* 
     float* scales = reinterpret_cast<float*>(a.dst.scales);
     uint32_t* dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.dst.codes) + (int64_t)phys * epp * d);
     constexpr int U = 8;
+    // the new row's max, taken by every wave over the whole row (no block
+    // reduction, no barrier)
     float am = 0.0f;
-    for (int i = threadIdx.x; i < d4; i += kCompressThreads) am = fmaxf(am, amax4(row4[i]));
-    am = ins_block_max(am, red_s);
+    for (int i = threadIdx.x & 63; i < d4; i += 64) am = fmaxf(am, amax4(row4[i]));
+    am = wave_max(am);
     bool full = a.append == 0 || row == 0;
     float s = 1.0f;
     if (!full && m == 1) {
