@@ -27,7 +27,7 @@ STATUS = {0: "HCA_OK", 1: "HCA_ERR_INVALID", 2: "HCA_ERR_UNSUPPORTED", 3: "HCA_E
 
 #: every symbol the C headers declare (include/hca.h and include/hca_testing.h)
 EXPORTS = (
-    "hca_status_string", "hca_version", "kv_compress", "kv_prefill_pages", "kv_compress_insert",
+    "hca_status_string", "hca_version", "hca_debug_status", "kv_compress", "kv_prefill_pages", "kv_compress_insert",
     "kv_compress_insert_jobs",
     "kv_quantize_page_workspace",
     "kv_quantize_page",
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L.hca_status_string.restype = ctypes.c_char_p
         L.hca_status_string.argtypes = [ctypes.c_int]
         L.hca_version.restype = ctypes.c_char_p
+        L.hca_debug_status.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
         L.kv_compress.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F32, _P, _F32, _P,
                                   _I64, _P]
         L.kv_prefill_pages.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _F32, _P,
@@ -189,6 +190,15 @@ def _null_cache() -> CPagedCache:
 
 def version() -> str:
     return lib().hca_version().decode()
+
+
+def debug_status():
+    """The debug build's index checks (hca_debug_status): waits for the device and returns (status, bits), where
+    bits has 1 for a page id outside its pool, 2 for a block-table slot past the table, 4 for a selected entry
+    outside its sequence and 8 for a row outside its page; the release build returns (HCA_ERR_UNSUPPORTED, 0)."""
+    bits = ctypes.c_uint32(0)
+    st = lib().hca_debug_status(ctypes.byref(bits))
+    return int(st), int(bits.value)
 
 
 def kv_compress(x, gate_logit, pos_bias, pos0, ntok, m: int, rope_theta: float, out, max_ntok: int, stream=None,

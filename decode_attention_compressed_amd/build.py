@@ -19,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhca.so")
+DEBUG_LIB = os.path.join(PKG, "libhca_debug.so")  # the same kernels with the index checks (-DHCA_DEBUG)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -47,26 +48,33 @@ def _run(cmd):
     return r.stdout
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 8, verbose: bool = False, debug: bool = False) -> str:
+    """Build libhca.so, or with debug the same kernels with the index checks (-DHCA_DEBUG) as libhca_debug.so."""
+    out_dir = os.path.join(BUILD, "debug") if debug else BUILD
+    lib = DEBUG_LIB if debug else LIB
+    flags = FLAGS + (["-DHCA_DEBUG"] if debug else [])
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    objs = [os.path.join(out_dir, os.path.basename(s)[:-4] + ".o") for s in srcs]
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        outs = list(ex.map(lambda so: _run([HIPCC, *FLAGS, *EXTRA.get(os.path.basename(so[0]), []), "-c", so[0], "-o", so[1]]),
+        outs = list(ex.map(lambda so: _run([HIPCC, *flags, *EXTRA.get(os.path.basename(so[0]), []), "-c", so[0], "-o", so[1]]),
                            zip(srcs, objs)))
     if verbose:
         for o in outs:
             if o.strip():
                 sys.stdout.write(o)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--debug", action="store_true", help="also build libhca_debug.so (the index-checked kernels)")
     args = ap.parse_args()
     print(build(args.jobs, args.verbose))
+    if args.debug:
+        print(build(args.jobs, args.verbose, debug=True))

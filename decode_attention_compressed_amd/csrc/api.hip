@@ -55,7 +55,28 @@ const char* hca_status_string(hca_status s) {
   return "unknown status";
 }
 
-const char* hca_version(void) { return "hca 0.1.0 gfx950"; }
+const char* hca_version(void) {
+#ifdef HCA_DEBUG
+  return "hca 0.1.0 gfx950 debug";
+#else
+  return "hca 0.1.0 gfx950";
+#endif
+}
+
+hca_status hca_debug_status(uint32_t* bits) {
+#ifdef HCA_DEBUG
+  if (bits == nullptr) return HCA_ERR_INVALID;
+  if (hipDeviceSynchronize() != hipSuccess) return HCA_ERR_HIP;
+  const uint32_t v = debug_bits_attention(true) | debug_bits_compress(true) | debug_bits_indexer(true) |
+                     debug_bits_quantize(true);
+  if (v & 0x80000000u) return HCA_ERR_HIP;
+  *bits = v;
+  return v != 0 ? HCA_ERR_INVALID : HCA_OK;
+#else
+  if (bits != nullptr) *bits = 0;
+  return HCA_ERR_UNSUPPORTED;
+#endif
+}
 
 hca_status kv_compress(const uint16_t* x, int64_t x_stride_b, const float* gate_logit, int64_t z_stride_b,
                        const float* pos_bias, const int32_t* pos0, const int32_t* ntok, int32_t B, int32_t max_ntok,

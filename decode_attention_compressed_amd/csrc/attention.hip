@@ -210,6 +210,7 @@ __device__ __forceinline__ uint64_t resolve_row(const AttnArgs& a, int b, int r,
   uint64_t base;
   if (r < n_sel) {
     const int e = a.sel ? e_sel : r;
+    HCA_DBG_CHECK(e >= 0 && e < N, kDbgEntry);
     if (e < 0 || e >= N) return 0;
     epp = a.kv.epp;  // a power of two, like the window's
     const int lg = __builtin_ctz(epp);
@@ -228,6 +229,7 @@ __device__ __forceinline__ uint64_t resolve_row(const AttnArgs& a, int b, int r,
     base = reinterpret_cast<uint64_t>(a.win.codes);
     in_win = true;
   }
+  HCA_DBG_CHECK(phys >= 0 && phys < np, kDbgPage);
   if (phys < 0 || phys >= np) return 0;
   sidx = phys;
   return base + ((uint64_t)phys * epp + slot) * row_bytes;
@@ -1471,5 +1473,9 @@ hipError_t launch_attention(const AttnArgs& args, hipStream_t s, bool split_only
     default: return launch_attn_d<512>(a, s);
   }
 }
+
+#ifdef HCA_DEBUG
+HCA_DBG_ACCESSOR(debug_bits_attention)
+#endif
 
 }  // namespace hca

@@ -562,8 +562,10 @@ __device__ __forceinline__ int prefill_page(const PrefillArgs& p, int b, int pg,
   rows = min(epp, N - pg * epp);
   if (rows <= 0) return -1;
   const int lb = p0 / m / epp + pg;
+  HCA_DBG_CHECK(lb >= 0 && lb < p.bts, kDbgTable);
   if (lb < 0 || lb >= p.bts) return -1;
   const int phys = p.bt[(int64_t)b * p.bts + lb];
+  HCA_DBG_CHECK(phys >= 0 && phys < p.dst.num_pages, kDbgPage);
   return phys >= 0 && phys < p.dst.num_pages ? phys : -1;
 }
 
@@ -934,11 +936,14 @@ __device__ __forceinline__ void insert_block(const InsertArgs& a, int b, float* 
   const int E0 = a.e0[b];
   const int p0 = a.c.pos0[b];
   const int row = p0 / m - E0;  // the open entry's row in its page
+  HCA_DBG_CHECK(row >= 0 && row < epp, kDbgRow);
   if (row < 0 || row >= epp) return;
   const int lb = E0 / epp;
+  HCA_DBG_CHECK(lb >= 0 && lb < a.bts, kDbgTable);
   if (lb < 0 || lb >= a.bts) return;
   const int phys = a.bt[(int64_t)b * a.bts + lb];  // loaded now, used after the fold
   const bool page_ok = phys >= 0 && phys < a.dst.num_pages;
+  HCA_DBG_CHECK(page_ok, kDbgPage);
   // an fp8 page's current scale, in flight during the fold
   const float s_prev = a.dst.dtype == HCA_FP8_E4M3 && page_ok ? reinterpret_cast<const float*>(a.dst.scales)[phys] : 1.0f;
   const float* st = a.stage + (int64_t)b * a.ss;  // the page's rows in staging
@@ -1155,5 +1160,9 @@ hipError_t launch_compact_insert(const IndexerArgs& a, const InsertJobs& jobs, h
                      s, a, j);
   return hipGetLastError();
 }
+
+#ifdef HCA_DEBUG
+HCA_DBG_ACCESSOR(debug_bits_compress)
+#endif
 
 }  // namespace hca

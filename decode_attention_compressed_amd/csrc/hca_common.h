@@ -228,6 +228,38 @@ __device__ __forceinline__ float row16_max(float v) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// Debug build (-DHCA_DEBUG): where a kernel meets an index its inputs should not
+// hold (a page id outside the pool, a block-table slot past the table's width,
+// a selected entry outside its sequence's entries, a row outside its page) the
+// release build skips the row or the page; the debug build also records a bit
+// in this module's device word, which hca_debug_status reads and clears.  The
+// word is written by vector atomics only.  Release builds compile the checks
+// away.
+constexpr uint32_t kDbgPage = 1u, kDbgTable = 2u, kDbgEntry = 4u, kDbgRow = 8u;
+#ifdef HCA_DEBUG
+static __device__ uint32_t g_hca_dbg;  // one per module: each source file has its own
+#define HCA_DBG_CHECK(ok, bit)                        \
+  do {                                                \
+    if (!(ok)) atomicOr(&::hca::g_hca_dbg, (bit));     \
+  } while (0)
+// reads (and clears) this module's word; defined once per module by
+// HCA_DBG_ACCESSOR(name)
+#define HCA_DBG_ACCESSOR(name)                                                                 \
+  uint32_t name(bool clear) {                                                                 \
+    uint32_t v = 0;                                                                           \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(::hca::g_hca_dbg), sizeof(v), 0, hipMemcpyDeviceToHost) != hipSuccess) \
+      return 0x80000000u;                                                                     \
+    if (clear) {                                                                              \
+      const uint32_t z = 0;                                                                   \
+      if (hipMemcpyToSymbol(HIP_SYMBOL(::hca::g_hca_dbg), &z, sizeof(z), 0, hipMemcpyHostToDevice) != hipSuccess) \
+        return 0x80000000u;                                                                   \
+    }                                                                                         \
+    return v;                                                                                 \
+  }
+#else
+#define HCA_DBG_CHECK(ok, bit) ((void)0)
+#endif
+
 // Load through the global address space.  Pointers rebuilt from integers (for
 // example row addresses kept in LDS) are generic; a generic (flat) load also
 // counts against the LDS counter, so every LDS wait would drain it too.

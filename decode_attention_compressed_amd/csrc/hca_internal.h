@@ -117,4 +117,13 @@ struct AttnArgs {
 // split_only: the split kernel alone (partials in the workspace, no output), for timing
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s, bool split_only = false);
 
+#ifdef HCA_DEBUG
+// each module's debug word (kDbg* bits; 0x80000000 when it cannot be read),
+// cleared when `clear`
+uint32_t debug_bits_attention(bool clear);
+uint32_t debug_bits_compress(bool clear);
+uint32_t debug_bits_indexer(bool clear);
+uint32_t debug_bits_quantize(bool clear);
+#endif
+
 }  // namespace hca

@@ -79,6 +79,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs a) {
     int phys = a.bt[(int64_t)b * a.bts + (valid ? e : wave0) / epp];
     const int slot = (valid ? e : wave0) % epp;
     const bool live = valid && phys >= 0 && phys < a.keys.num_pages;
+    HCA_DBG_CHECK(!valid || live, kDbgPage);
     const float pscale = KDT == HCA_FP8_E4M3 ? reinterpret_cast<const float*>(a.keys.scales)[live ? phys : 0] : 0.0f;
     const int64_t r = live ? (int64_t)phys * epp + slot : 0;
     Tile<KDT, DI> t;
@@ -246,5 +247,9 @@ hipError_t launch_select(const IndexerArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(select_compact_kernel, dim3(compact_blocks(a), a.B), dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
 }
+
+#ifdef HCA_DEBUG
+HCA_DBG_ACCESSOR(debug_bits_indexer)
+#endif
 
 }  // namespace hca

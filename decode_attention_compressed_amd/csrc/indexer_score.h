@@ -284,6 +284,7 @@ struct PageTiles {
   // `phys` is the page's table entry, read ahead of the sequence length
   __device__ __forceinline__ void load(const IndexerArgs& a, int phys, int p, bool p_ok, int N, int col, int g) {
     const bool live = p_ok && phys >= 0 && phys < a.keys.num_pages;
+    HCA_DBG_CHECK(!p_ok || live, kDbgPage);
     const int rows = live ? min(64, N - 64 * p) : 0;
     const int pg = live ? phys : 0;
     const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.keys.codes) + (int64_t)pg * 64 * ROW;
@@ -405,6 +406,7 @@ struct OpenRow {
     const float sdec = e4m3_decode(sc);
     byte = sdec > 0.0f ? (e2m1_encode(v.x / sdec) | (e2m1_encode(v.y / sdec) << 4)) : 0u;
     const int phys = a.bt[(int64_t)b * a.bts + lb];
+    HCA_DBG_CHECK(phys >= 0 && phys < a.keys.num_pages, kDbgPage);
     if (phys < 0 || phys >= a.keys.num_pages) return;  // an unmapped page: nothing written, nothing patched
     uint8_t* codes = reinterpret_cast<uint8_t*>(a.keys.codes) + ((int64_t)phys * 64 + r) * 64;
     uint8_t* scales = reinterpret_cast<uint8_t*>(a.keys.scales) + ((int64_t)phys * 64 + r) * 4;

@@ -55,8 +55,10 @@ __global__ __launch_bounds__(kF8Threads) void quantize_fp8_kernel(QuantArgs a) {
   const int tot4 = epp * dim / 4;
   for (int pg = blockIdx.x; pg < npages; pg += gridDim.x) {
     const int lb = E0 / epp + pg;
+    HCA_DBG_CHECK(lb >= 0 && lb < a.bts, kDbgTable);
     if (lb < 0 || lb >= a.bts) continue;
     const int phys = a.bt[(int64_t)b * a.bts + lb];
+    HCA_DBG_CHECK(page_ok(phys, a.dst.num_pages), kDbgPage);
     if (!page_ok(phys, a.dst.num_pages)) continue;  // uniform over the block
     const int rows = min(epp, n - pg * epp);
     const int nv4 = rows * dim / 4;  // valid float4 groups (dim % 4 == 0)
@@ -146,8 +148,10 @@ __device__ __forceinline__ bool chunk_locate(const QuantArgs& a, int b, int n, i
                                              ChunkLoc& loc) {
   const int epp = a.dst.epp;
   const int lb = a.e0[b] / epp + pg;
+  HCA_DBG_CHECK(lb >= 0 && lb < a.bts, kDbgTable);
   if (lb < 0 || lb >= a.bts) return false;
   const int phys = a.bt[(int64_t)b * a.bts + lb];
+  HCA_DBG_CHECK(page_ok(phys, a.dst.num_pages), kDbgPage);
   if (!page_ok(phys, a.dst.num_pages)) return false;
   const int rows = min(epp, n - pg * epp);
   loc.phys = phys;
@@ -251,8 +255,10 @@ __global__ __launch_bounds__(kQThreads) void quantize_fp4_kernel(QuantArgs a) {
   for (int w = blockIdx.x; w < npages * C; w += gridDim.x) {
     const int pg = w / C, row0 = (w % C) * R;
     const int lb = E0 / epp + pg;
+    HCA_DBG_CHECK(lb >= 0 && lb < a.bts, kDbgTable);
     if (lb < 0 || lb >= a.bts) continue;
     const int phys = a.bt[(int64_t)b * a.bts + lb];
+    HCA_DBG_CHECK(page_ok(phys, a.dst.num_pages), kDbgPage);
     if (!page_ok(phys, a.dst.num_pages)) continue;
     const int rows = min(epp, n - pg * epp);
     const float* src = a.src + (int64_t)b * a.ss + (int64_t)pg * epp * dim;
@@ -299,8 +305,10 @@ __global__ __launch_bounds__(kQThreads) void quantize_bf16_kernel(QuantArgs a) {
   uint16_t* codes = reinterpret_cast<uint16_t*>(a.dst.codes);
   for (int pg = blockIdx.x; pg < npages; pg += gridDim.x) {
     const int lb = E0 / epp + pg;
+    HCA_DBG_CHECK(lb >= 0 && lb < a.bts, kDbgTable);
     if (lb < 0 || lb >= a.bts) continue;
     const int phys = a.bt[(int64_t)b * a.bts + lb];
+    HCA_DBG_CHECK(page_ok(phys, a.dst.num_pages), kDbgPage);
     if (!page_ok(phys, a.dst.num_pages)) continue;
     const int rows = min(epp, n - pg * epp);
     const int nv4 = rows * dim / 4;
@@ -385,5 +393,9 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(gather_kernel, dim3(gx, a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
+
+#ifdef HCA_DEBUG
+HCA_DBG_ACCESSOR(debug_bits_quantize)
+#endif
 
 }  // namespace hca

@@ -90,8 +90,26 @@ typedef struct {
 /* Human-readable name of a status (static string). */
 const char* hca_status_string(hca_status s);
 
-/* Library version, e.g. "hca 0.1.0 gfx950". */
+/* Library version, e.g. "hca 0.1.0 gfx950" ("... debug" for the debug build). */
 const char* hca_version(void);
+
+/*
+ * hca_debug_status -- the debug build's record of indices that the inputs
+ * should not hold (a checked build of the same kernels, compiled with
+ * -DHCA_DEBUG into libhca_debug.so; no section of the pages: it checks the
+ * paging contract of the entry points below).  Where a kernel meets a page id
+ * outside its pool, a block-table slot past the table's width, a selected
+ * entry outside its sequence's entries or a row outside its page, the release
+ * build skips that row or page (documented per entry point); the debug build
+ * does the same and also sets a bit in a device word.  This call waits for the
+ * device (hipDeviceSynchronize), reads the bits of every module into *bits
+ * (1 page id, 2 table slot, 4 selected entry, 8 row) and clears them.
+ *   returns    HCA_OK when no bit is set, HCA_ERR_INVALID when some are,
+ *              HCA_ERR_HIP when the device or the read fails, HCA_ERR_INVALID
+ *              for a NULL bits; HCA_ERR_UNSUPPORTED (and *bits = 0) in the
+ *              release build, which records nothing.
+ */
+hca_status hca_debug_status(uint32_t* bits);
 
 /*
  * kv_compress -- the compressor (V4 page, section 2.1: a learned weighted sum

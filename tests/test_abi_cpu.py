@@ -35,6 +35,24 @@ def test_every_declared_symbol_is_exported():
         assert L.hca_status_string(s)
 
 
+def test_debug_build_exports_every_declared_symbol():
+    # libhca_debug.so: the same kernels with index checks (-DHCA_DEBUG); loaded
+    # beside the release library, no device call made
+    path = os.path.join(os.path.dirname(hca.__file__), "libhca_debug.so")
+    assert os.path.exists(path), "build it with `python -m decode_attention_compressed_amd.build --debug`"
+    D = ctypes.CDLL(path)
+    for n in _declared("hca.h") | _declared("hca_testing.h"):
+        assert hasattr(D, n), n
+    D.hca_version.restype = ctypes.c_char_p
+    assert D.hca_version().decode().endswith(" debug")
+
+
+def test_release_build_debug_status_is_unsupported():
+    # the release build records nothing: HCA_ERR_UNSUPPORTED, bits 0, no device call
+    assert hca.debug_status() == (2, 0)
+    assert hca.lib().hca_debug_status(None) == 2
+
+
 def _host_encode(fn, x, out_dtype):
     x = np.ascontiguousarray(x, dtype=np.float32)
     out = np.zeros(x.shape, dtype=out_dtype)
