@@ -1023,8 +1023,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
       load_to_lds16(src, dst + PT::HALF_BYTES * hf + 1024 * j);
     }
   };
-  if (pair < nt) issue(pair, slot0);
-  if (pair + kPairs < nt) issue(pair + kPairs, slot1);
+  if (pair < nt) issue(pair, slot0);  // the pair's second tile goes out once its first has landed
 #pragma unroll
   for (int j = 0; j < kPer; ++j)
     if (row_of(j) < RPS) ps_s[row_of(j)] = ps[j];
@@ -1156,10 +1155,16 @@ __global__ __launch_bounds__(kPairThreads, 1) void attn_pair_kernel(AttnArgs a) 
     const int t = pair + kPairs * st;
     uint8_t* slot = (st & 1) ? slot1 : slot0;
     f32x4 sres[2];
-    if (t + kPairs < nt)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(PT::INSTR));
-    else
+    if (st == 0) {
+      // the first tile alone was in flight: a smaller first burst lands sooner
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      asm volatile("" ::: "memory");
+      if (t + kPairs < nt) issue(t + kPairs, slot1);
+    } else if (t + kPairs < nt) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(PT::INSTR));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
     asm volatile("" ::: "memory");
     qk_half(slot, sres);
     if (st > 0) pair_wait(&psync_s[wave ^ 1][1], st);  // the partner has read this wave's last partial
