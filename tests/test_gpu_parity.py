@@ -913,6 +913,11 @@ def _run_attn(sd, sel_list, window, ws=None, table=None, wtable=None, kv=None, w
     dict(kv="fp8", d=256, H=96, W=0, m=4, topk=64, lens=[3000, 50, 700]),
     dict(kv="fp8", d=64, H=20, W=256, m=128, topk=None, lens=[700, 1, 257]),
     dict(kv="fp8", d=512, H=128, W=128, m=1, topk=None, lens=[100, 33, 1]),
+    # the paired 512-dim kernel with a partial head group (40 = 2 x 16 + 8),
+    # a sequence shorter than the window and top-k above its entry count
+    dict(kv="fp8", d=512, H=40, W=128, m=4, topk=300, lens=[5000, 64, 3333]),
+    # and without a window: every row a compressed entry, one partial tile
+    dict(kv="fp8", d=512, H=16, W=0, m=128, topk=None, lens=[129, 4229]),
 ])
 def test_paged_hybrid_decode(case):
     H.flush(f"attention {case}")
