@@ -84,40 +84,45 @@ __device__ __forceinline__ void fold_batch(int ns, float mx, int k0, const u32x4
   }
 }
 
-// The same fold when a row group is exactly one wave (d = 512: 64 threads of
-// 8 dims, and row groups start at wave boundaries), so every slot's weight is
-// uniform over the wave: lane k loads slot k's logit and bias and computes its
-// weight once, and the weights reach the other lanes by lane reads, in slot
-// order.  The arithmetic is the row group fold's, value for value (the same
-// maximum, the same expf of the same arguments, the same sums in the same
-// order): the codes it leads to are identical.
-template <typename Mid>
-__device__ __forceinline__ void small_fold_wave(const CompressArgs& a, const float* zb, const uint16_t* xb, int j,
-                                                int n, int p0, bool live, float acc[8], Mid&& mid) {
-  constexpr int kFoldBatch = 8;
-  constexpr int kMaxSlots = 2 * kSmallM;
+// The loads of one wave-form fold (its slots' logits and biases, and the
+// first batch of its rows), kept apart from its arithmetic: all of them are
+// issued before the first is used, and a caller's own work (mid) goes
+// between the two.
+struct FoldWaveIn {
+  static constexpr int kBatch = 8;
+  int t0, lo, ns;
+  bool on;
+  float zl, bl;
+  u32x4 raw[kBatch];
+};
+__device__ __forceinline__ void small_fold_wave_load(const CompressArgs& a, const float* zb, const uint16_t* xb, int j,
+                                                     int n, int p0, bool live, FoldWaveIn& f) {
   const int lane = threadIdx.x & 63;
   // uniform over the wave (its one row group): read from the first lane, so
   // that the slot tests below are scalar branches, not lane masks
-  const int t0 = __builtin_amdgcn_readfirstlane(j * a.m - a.ov);
-  const int lo = max(0, -(p0 + t0));
-  const int ns = __builtin_amdgcn_readfirstlane(live ? min(a.m + a.ov, n - t0) - lo : 0);
-  const bool on = lane < ns;
-  const float zl = on ? zb[t0 + lo + lane] : 0.0f;
-  const float bl = on ? a.beta[lo + lane] : 0.0f;
+  f.t0 = __builtin_amdgcn_readfirstlane(j * a.m - a.ov);
+  f.lo = max(0, -(p0 + f.t0));
+  f.ns = __builtin_amdgcn_readfirstlane(live ? min(a.m + a.ov, n - f.t0) - f.lo : 0);
+  f.on = lane < f.ns;
+  f.zl = f.on ? zb[f.t0 + f.lo + lane] : 0.0f;
+  f.bl = f.on ? a.beta[f.lo + lane] : 0.0f;
   // the first batch's rows, loaded without per-slot tests: a slot past the
   // present ones re-reads the last present row (it is not added)
-  u32x4 raw[kFoldBatch];
-  if (ns > 0) {
+  if (f.ns > 0) {
 #pragma unroll
-    for (int k = 0; k < kFoldBatch; ++k)
-      raw[k] = *reinterpret_cast<const u32x4*>(xb + (int64_t)(t0 + lo + min(k, ns - 1)) * a.d);
+    for (int k = 0; k < FoldWaveIn::kBatch; ++k)
+      f.raw[k] = *reinterpret_cast<const u32x4*>(xb + (int64_t)(f.t0 + f.lo + min(k, f.ns - 1)) * a.d);
   } else {
 #pragma unroll
-    for (int k = 0; k < kFoldBatch; ++k) raw[k] = u32x4{0u, 0u, 0u, 0u};
+    for (int k = 0; k < FoldWaveIn::kBatch; ++k) f.raw[k] = u32x4{0u, 0u, 0u, 0u};
   }
-  mid();
-  const float av = on ? zl + bl : -INFINITY;
+}
+__device__ __forceinline__ void small_fold_wave_compute(const CompressArgs& a, const uint16_t* xb, FoldWaveIn& f,
+                                                        float acc[8]) {
+  constexpr int kFoldBatch = FoldWaveIn::kBatch;
+  constexpr int kMaxSlots = 2 * kSmallM;
+  const int ns = f.ns;
+  const float av = f.on ? f.zl + f.bl : -INFINITY;
   // the slots' maximum: a max scan by DPP row shifts inside each 16-lane row,
   // then the last lanes of rows 0 and 1 (slots 0 .. 31)
   float mx = av;
@@ -131,7 +136,7 @@ __device__ __forceinline__ void small_fold_wave(const CompressArgs& a, const flo
   static_assert(kMaxSlots <= 32, "slots in lane rows 0 and 1");
   mx = fmaxf(u2f((uint32_t)__builtin_amdgcn_readlane((int)f2u(mx), 15)),
              u2f((uint32_t)__builtin_amdgcn_readlane((int)f2u(mx), 31)));
-  const float e = on ? expf(av - mx) : 0.0f;
+  const float e = f.on ? expf(av - mx) : 0.0f;
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
   float tot = 0.0f;
@@ -139,8 +144,8 @@ __device__ __forceinline__ void small_fold_wave(const CompressArgs& a, const flo
     if (k0 > 0) {
 #pragma unroll
       for (int k = 0; k < kFoldBatch; ++k)
-        raw[k] = k0 + k < ns ? *reinterpret_cast<const u32x4*>(xb + (int64_t)(t0 + lo + k0 + k) * a.d)
-                             : u32x4{0u, 0u, 0u, 0u};
+        f.raw[k] = k0 + k < ns ? *reinterpret_cast<const u32x4*>(xb + (int64_t)(f.t0 + f.lo + k0 + k) * a.d)
+                               : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int k = 0; k < kFoldBatch; ++k) {
@@ -149,8 +154,8 @@ __device__ __forceinline__ void small_fold_wave(const CompressArgs& a, const flo
         tot += ek;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = fmaf(ek, u2f(raw[k][q] << 16), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(ek, u2f(raw[k][q] & 0xFFFF0000u), acc[2 * q + 1]);
+          acc[2 * q] = fmaf(ek, u2f(f.raw[k][q] << 16), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(ek, u2f(f.raw[k][q] & 0xFFFF0000u), acc[2 * q + 1]);
         }
       }
     }
@@ -158,6 +163,22 @@ __device__ __forceinline__ void small_fold_wave(const CompressArgs& a, const flo
   const float inv_tot = tot > 0.0f ? 1.0f / tot : 0.0f;
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] *= inv_tot;
+}
+
+// The same fold when a row group is exactly one wave (d = 512: 64 threads of
+// 8 dims, and row groups start at wave boundaries), so every slot's weight is
+// uniform over the wave: lane k loads slot k's logit and bias and computes its
+// weight once, and the weights reach the other lanes by lane reads, in slot
+// order.  The arithmetic is the row group fold's, value for value (the same
+// maximum, the same expf of the same arguments, the same sums in the same
+// order): the codes it leads to are identical.
+template <typename Mid>
+__device__ __forceinline__ void small_fold_wave(const CompressArgs& a, const float* zb, const uint16_t* xb, int j,
+                                                int n, int p0, bool live, float acc[8], Mid&& mid) {
+  FoldWaveIn f;
+  small_fold_wave_load(a, zb, xb, j, n, p0, live, f);
+  mid();
+  small_fold_wave_compute(a, xb, f, acc);
 }
 
 template <typename Mid>
