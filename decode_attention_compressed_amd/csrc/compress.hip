@@ -552,6 +552,8 @@ hipError_t launch_compress(CompressArgs a, hipStream_t s) {
 // large path, so the same sums) into shared memory.
 constexpr int kPrefillThreads = 1024;
 constexpr int kPrefillRounds = 4;
+constexpr int kPrefill512Threads = 512;  // 8 waves: two blocks share a CU
+constexpr int kPrefill512Rounds = 8;
 
 // four fp8 codes of x / s (an fp8 page's encoding), packed little-endian
 __device__ __forceinline__ uint32_t enc4_e4m3(const f32x4 v, float s) { return e4m3_encode4_div(v[0], v[1], v[2], v[3], s); }
@@ -591,9 +593,12 @@ __device__ __forceinline__ int prefill_page(const PrefillArgs& p, int b, int pg,
 }
 
 // The same kernel specialized for 512-dim rows (the c4a pages): one row group
-// per wave, the fold's wave form called directly, the four rounds unrolled
-// (their rows then sit in a register array with constant indices).
-__global__ __launch_bounds__(kPrefillThreads) void prefill_small512_kernel(PrefillArgs p) {
+// per wave, the fold's wave form called directly, the rounds unrolled (their
+// rows then sit in a register array with constant indices).  Eight waves and
+// eight rounds per page rather than sixteen and four: at 125 registers two
+// such blocks share a CU, so one block's folds (load-bound) overlap the
+// other's page maximum and encode (a barrier, then VALU work).
+__global__ __launch_bounds__(kPrefill512Threads) void prefill_small512_kernel(PrefillArgs p) {
   const CompressArgs& a = p.c;
   const int b = blockIdx.y, pg = blockIdx.x;
   const int n = clampi(a.ntok[b], 0, a.max_ntok);
@@ -601,7 +606,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_small512_kernel(Prefi
   int rows;
   const int phys = prefill_page(p, b, pg, n, p0, rows);
   if (phys < 0) return;  // uniform over the block
-  constexpr int d = 512, TD = 64, RP = kPrefillThreads / TD;
+  constexpr int d = 512, TD = 64, RP = kPrefill512Threads / TD;
   const int m = a.m, epp = p.dst.epp;
   const int li = threadIdx.x % TD, gi = __builtin_amdgcn_readfirstlane(threadIdx.x / TD);
   const uint16_t* xb = a.x + (int64_t)b * a.xs + li * 8;
@@ -615,12 +620,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_small512_kernel(Prefi
   }
   double inv[4];
   rope_inv_freq4(li, a.rope_r, inv);
-  __shared__ float sq_s[kPrefillThreads];
-  __shared__ float red_s[kPrefillThreads / 64];
-  float v[kPrefillRounds][8];
+  __shared__ float sq_s[kPrefill512Threads];
+  __shared__ float red_s[kPrefill512Threads / 64];
+  float v[kPrefill512Rounds][8];
   float amax = 0.0f;
 #pragma unroll
-  for (int r = 0; r < kPrefillRounds; ++r) {
+  for (int r = 0; r < kPrefill512Rounds; ++r) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) v[r][c] = 0.0f;
     if (r * RP >= epp) continue;  // uniform
@@ -644,11 +649,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_small512_kernel(Prefi
     }
   }
   if (p.dst.dtype == HCA_FP8_E4M3) {
-    amax = block_max_n(amax, red_s, kPrefillThreads / 64);
+    amax = block_max_n(amax, red_s, kPrefill512Threads / 64);
     const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
     uint8_t* codes = reinterpret_cast<uint8_t*>(p.dst.codes) + (int64_t)phys * epp * d;
 #pragma unroll
-    for (int r = 0; r < kPrefillRounds; ++r) {
+    for (int r = 0; r < kPrefill512Rounds; ++r) {
       const int row = r * RP + gi;
       if (r * RP >= epp || row >= epp) continue;
       u32x2 w = {0u, 0u};
@@ -662,7 +667,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_small512_kernel(Prefi
   } else {  // bf16
     uint16_t* codes = reinterpret_cast<uint16_t*>(p.dst.codes) + (int64_t)phys * epp * d;
 #pragma unroll
-    for (int r = 0; r < kPrefillRounds; ++r) {
+    for (int r = 0; r < kPrefill512Rounds; ++r) {
       const int row = r * RP + gi;
       if (r * RP >= epp || row >= epp) continue;
       u32x4 w = {0u, 0u, 0u, 0u};
@@ -816,6 +821,7 @@ __global__ __launch_bounds__(kCompressThreads) void prefill_large_kernel(Prefill
 
 bool prefill_supported(int m, int d, int epp, int dtype) {
   if (dtype != HCA_FP8_E4M3 && dtype != HCA_BF16) return false;
+  if (m <= kSmallM && d == 512) return epp <= kPrefill512Rounds * (kPrefill512Threads / 64);
   if (m <= kSmallM) return epp <= kPrefillRounds * (kPrefillThreads / (d / 8));
   return (size_t)epp * d * sizeof(float) + kCompressShm <= (size_t)64 * 1024;
 }
@@ -828,7 +834,7 @@ hipError_t launch_prefill(PrefillArgs p, hipStream_t s) {
   const int pages = (n_max + p.dst.epp - 1) / p.dst.epp;
   if (a.m <= kSmallM) {
     if (a.d == 512)
-      hipLaunchKernelGGL(prefill_small512_kernel, dim3(pages, a.B), dim3(kPrefillThreads), 0, s, p);
+      hipLaunchKernelGGL(prefill_small512_kernel, dim3(pages, a.B), dim3(kPrefill512Threads), 0, s, p);
     else
       hipLaunchKernelGGL(prefill_small_kernel, dim3(pages, a.B), dim3(kPrefillThreads), 0, s, p);
   } else {
