@@ -58,17 +58,17 @@ TRAFFIC = {
                                    "decode_attention_compressed_amd/csrc/indexer_internal.h",
                                    "decode_attention_compressed_amd/csrc/indexer_score.h"),
                        "source_sha256": "e15c22d671761d4d76830afa22ad947fd58b595f722bb1a7f0b76f65dd1d4706",
-                       "fetch_bytes": 72060605, "write_bytes": 4662218},
+                       "fetch_bytes": 72060575, "write_bytes": 4662247},
     ("stack-1m-b4-61layers", "c128a", "attn_split"): {"sources": ("decode_attention_compressed_amd/csrc/attention.hip",
                                           "decode_attention_compressed_amd/csrc/hca_common.h",
                                           "decode_attention_compressed_amd/csrc/hca_internal.h"),
                               "source_sha256": "89a7dfe9ecfad1bc075885b4bf6d7c36ae379fd66cbc2287bd5114f4f1a922a9",
-                              "fetch_bytes": 20027106, "write_bytes": 4259840},
+                              "fetch_bytes": 20030315, "write_bytes": 4259840},
     ("stack-1m-b4-61layers", "c4a", "attn_split"): {"sources": ("decode_attention_compressed_amd/csrc/attention.hip",
                                         "decode_attention_compressed_amd/csrc/hca_common.h",
                                         "decode_attention_compressed_amd/csrc/hca_internal.h"),
                             "source_sha256": "89a7dfe9ecfad1bc075885b4bf6d7c36ae379fd66cbc2287bd5114f4f1a922a9",
-                            "fetch_bytes": 7384371, "write_bytes": 3727360},
+                            "fetch_bytes": 7384423, "write_bytes": 3727360},
 }
 
 
