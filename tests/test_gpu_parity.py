@@ -683,6 +683,7 @@ def _idx_workload(dtype, d_idx, k, B=3):
     ("fp4", 64, 500, [30000, 257, 64]),     # two scale blocks per key
     ("fp4", 256, 1000, [20000, 4096, 100]),  # eight scale blocks per key
     ("fp8", 32, 300, [2200000, 3000]),      # 550,000 entries: past the LDS bitmap, separate compaction
+    ("fp4", 128, 64, [(i * 1499) % 5000 + 1 for i in range(70)]),  # 70 sequences, some with N < k
 ])
 def test_indexer_topk_sets(dtype, d_idx, k, lens):
     H.flush(f"indexer {dtype} dI={d_idx} k={k} lens={lens}")
@@ -918,6 +919,9 @@ def _run_attn(sd, sel_list, window, ws=None, table=None, wtable=None, kv=None, w
     dict(kv="fp8", d=512, H=40, W=128, m=4, topk=300, lens=[5000, 64, 3333]),
     # and without a window: every row a compressed entry, one partial tile
     dict(kv="fp8", d=512, H=16, W=0, m=128, topk=None, lens=[129, 4229]),
+    # more than 64 sequences: the work list spans two 64-lane chunks of lengths
+    dict(kv="fp8", d=512, H=16, W=128, m=128, topk=None, lens=[(i * 997) % 3000 + 1 for i in range(70)]),
+    dict(kv="fp8", d=512, H=16, W=128, m=4, topk=64, lens=[(i * 1499) % 2500 + 1 for i in range(70)]),
 ])
 def test_paged_hybrid_decode(case):
     H.flush(f"attention {case}")
